@@ -1,0 +1,318 @@
+"""Seeded synthetic compressed KV caches.
+
+This module only draws random data in the storage format of a DKV cache
+(anchor + rank-r joint K|V delta + exact residual rows per 256-token block,
+plus a dense recency window and one decode query per sequence).  It holds
+none of the method's arithmetic: no reconstruction, scoring, routing or
+softmax.  Both the fp64 oracle (through the tests) and the GPU path read the
+identical fp16 arrays produced here.
+
+Storage format (per layer), following the DKV paper page (Zenodo record,
+abstract) and the Differential-KV README ("Core Architecture & Paper
+Overview"): each block of B_s = 256 tokens keeps its first token exact as the
+anchor (a_k, a_v), a rank-r joint delta U in R^{255 x r} with bases V_K, V_V
+in R^{r x d}, and R exact residual rows at recorded in-block positions.
+
+Array shapes (S = pool slots, Hkv = KV heads, d = 128):
+  anchor_k, anchor_v  fp16 [S][Hkv][d]
+  u                   fp16 [S][Hkv][255][r]
+  vk, vv              fp16 [S][Hkv][r][d]
+  resid_k, resid_v    fp16 [S][Hkv][R][d]
+  resid_pos           uint8 [S][Hkv][R], distinct values in 1..255, ascending
+  q                   fp16 [B][Hq][d]
+  win_k, win_v        fp16 [B][Hkv][W][d]
+  block_table         int32 [B][max_blocks], pool slot of each logical block
+  n_blocks            int32 [B]
+  win_len             int32 [B]
+
+Distributions (the workloads' stated recipe): anchors, queries, residual and
+window rows ~ N(0, 1); U[:, j] ~ N(0, sigma_j^2) with sigma_j = s0 * decay^j;
+V_K and V_V have orthonormal rows (transposed Q factor of a d x r Gaussian).
+All values are drawn in float32 and rounded once to fp16 (round to nearest
+even).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import dataclasses
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK_SIZE = 256
+LOWRANK_ROWS = BLOCK_SIZE - 1
+
+
+@dataclasses.dataclass
+class Layer:
+    rank: int
+    anchor_k: np.ndarray
+    anchor_v: np.ndarray
+    u: np.ndarray
+    vk: np.ndarray
+    vv: np.ndarray
+    resid_k: np.ndarray
+    resid_v: np.ndarray
+    resid_pos: np.ndarray
+    q: np.ndarray
+    win_k: np.ndarray
+    win_v: np.ndarray
+
+    def pool(self) -> dict:
+        """The block-store arrays as a plain dict (the oracle's input form)."""
+        return {k: getattr(self, k) for k in
+                ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int
+    n_resid: int
+    top_k: int
+    scale: float
+    block_table: np.ndarray
+    n_blocks: np.ndarray
+    win_len: np.ndarray
+    layers: List[Layer]
+    seed: int
+    notes: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_slots(self) -> int:
+        return int(self.layers[0].anchor_k.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def _f16(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x.astype(np.float16))
+
+
+_CHUNK = 1 << 22          # values per independently seeded chunk of a large draw
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:       # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _chunked(rng: np.random.Generator, shape, fill) -> np.ndarray:
+    """Fill a float32 array of `shape` in fixed chunks along axis 0, each from its
+    own child stream of `rng`, so the result does not depend on the thread count."""
+    out = np.empty(shape, dtype=np.float32)
+    if out.size == 0:
+        return out
+    per = int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
+    rows = max(1, _CHUNK // max(per, 1))
+    starts = list(range(0, shape[0], rows))
+    kids = rng.spawn(len(starts))
+    flat = out.reshape(shape[0], -1)
+
+    def work(i):
+        a = starts[i]
+        b = min(shape[0], a + rows)
+        fill(np.random.Generator(kids[i].bit_generator), flat[a:b])
+
+    if len(starts) == 1:
+        work(0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(len(starts))))
+    return out
+
+
+def _normal(rng: np.random.Generator, shape, std=1.0) -> np.ndarray:
+    def fill(g, view):
+        g.standard_normal(dtype=np.float32, out=view)
+    a = _chunked(rng, tuple(shape), fill)
+    if std != 1.0:
+        a *= np.asarray(std, dtype=np.float32)
+    return a
+
+
+def _orthonormal_rows(rng: np.random.Generator, lead: tuple, r: int, d: int) -> np.ndarray:
+    """[..., r, d] with orthonormal rows: transposed Q factor of a d x r Gaussian."""
+    n = int(np.prod(lead, dtype=np.int64))
+    g = _normal(rng, (n, d, r))
+    out = np.empty((n, r, d), dtype=np.float32)
+    step = 512
+
+    def work(a):
+        qf, _ = np.linalg.qr(g[a:a + step])      # [k, d, r], orthonormal columns
+        out[a:a + step] = np.swapaxes(qf, -1, -2)
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(0, n, step)))
+    return out.reshape(lead + (r, d))
+
+
+def _positions(rng: np.random.Generator, lead: tuple, n_resid: int) -> np.ndarray:
+    """n_resid distinct in-block positions from 1..255, ascending, per entry."""
+    if n_resid == 0:
+        return np.zeros(lead + (0,), dtype=np.uint8)
+    keys = rng.random(size=lead + (LOWRANK_ROWS,))
+    pos = np.argsort(keys, axis=-1, kind="stable")[..., :n_resid] + 1
+    return np.sort(pos, axis=-1).astype(np.uint8)
+
+
+def make_layer(rng: np.random.Generator, *, n_slots: int, batch: int, n_q_heads: int,
+               n_kv_heads: int, window: int, rank: int, n_resid: int,
+               sigma0: float = 0.5, decay: float = 0.9, zero_anchor: bool = False,
+               head_dim: int = HEAD_DIM) -> Layer:
+    """Draw one layer's pool, query and window with child streams in a fixed order."""
+    d = head_dim
+    streams = rng.spawn(9)
+    lead = (n_slots, n_kv_heads)
+    ak = _normal(streams[0], lead + (d,))
+    av = _normal(streams[1], lead + (d,))
+    if zero_anchor:
+        ak[:] = 0.0
+        av[:] = 0.0
+    sig = (sigma0 * decay ** np.arange(rank)).astype(np.float32)
+    u = _normal(streams[2], lead + (LOWRANK_ROWS, rank)) * sig
+    vk = _orthonormal_rows(streams[3], lead, rank, d)
+    vv = _orthonormal_rows(streams[4], lead, rank, d)
+    rk = _normal(streams[5], lead + (n_resid, d))
+    rv = _normal(streams[5], lead + (n_resid, d))
+    pos = _positions(streams[6], lead, n_resid)
+    q = _normal(streams[7], (batch, n_q_heads, d))
+    wk = _normal(streams[8], (batch, n_kv_heads, window, d))
+    wv = _normal(streams[8], (batch, n_kv_heads, window, d))
+    return Layer(rank=rank, anchor_k=_f16(ak), anchor_v=_f16(av), u=_f16(u), vk=_f16(vk),
+                 vv=_f16(vv), resid_k=_f16(rk), resid_v=_f16(rv), resid_pos=pos,
+                 q=_f16(q), win_k=_f16(wk), win_v=_f16(wv))
+
+
+def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                  window: int, n_blocks: Sequence[int], ranks: Sequence[int], n_resid: int,
+                  top_k: int, sigma0: float = 0.5, decay: float = 0.9,
+                  permute_slots: bool = False, zero_anchor: bool = False,
+                  win_len: Optional[Sequence[int]] = None, max_blocks: Optional[int] = None,
+                  head_dim: int = HEAD_DIM, only_layers: Optional[Sequence[int]] = None,
+                  notes: str = "") -> Workload:
+    """Generic seeded workload: one Layer per entry of `ranks`.
+
+    Sequence b owns n_blocks[b] logical blocks; their pool slots are
+    consecutive (b-major) or a seeded permutation of all slots.  Every layer
+    has its own child seed, so `only_layers` (a subset of layer indices)
+    yields exactly the same arrays for those layers as the full stack.
+    """
+    ss = np.random.SeedSequence(seed)
+    top, layer_seq = ss.spawn(2)
+    trng = np.random.Generator(np.random.PCG64(top))
+    nb = np.asarray(n_blocks, dtype=np.int32)
+    assert nb.shape == (batch,)
+    total = int(nb.sum())
+    mb = int(max_blocks if max_blocks is not None else max(1, int(nb.max(initial=0))))
+    slots = np.arange(total, dtype=np.int32)
+    if permute_slots:
+        slots = trng.permutation(total).astype(np.int32)
+    table = np.full((batch, mb), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        table[b, :nb[b]] = slots[off:off + nb[b]]
+        off += int(nb[b])
+    wl = np.full((batch,), window, dtype=np.int32) if win_len is None else np.asarray(win_len, np.int32)
+    layers = []
+    children = layer_seq.spawn(len(ranks))
+    sel = range(len(ranks)) if only_layers is None else list(only_layers)
+    for li in sel:
+        lrng = np.random.Generator(np.random.PCG64(children[li]))
+        layers.append(make_layer(lrng, n_slots=max(total, 1), batch=batch, n_q_heads=n_q_heads,
+                                 n_kv_heads=n_kv_heads, window=window, rank=int(ranks[li]),
+                                 n_resid=n_resid, sigma0=sigma0, decay=decay,
+                                 zero_anchor=zero_anchor, head_dim=head_dim))
+    return Workload(name=name, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                    head_dim=head_dim, window=window, n_resid=n_resid, top_k=top_k,
+                    scale=float(1.0 / np.sqrt(head_dim)), block_table=table, n_blocks=nb,
+                    win_len=wl, layers=layers, seed=seed, notes=notes)
+
+
+def plant_outlier_rows(wl: Workload, logical_block: int, n_rows: int = 8, rms: float = 4.0,
+                       seq: int = 0, layer: int = 0) -> List[int]:
+    """Rescale n_rows residual rows (K and V) of one block, in every KV head, to an
+    l2 norm of rms * sqrt(d).  The rows are a seeded choice among the block's R
+    residual rows.  Returns the chosen residual-row indices."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 77])))
+    L = wl.layers[layer]
+    slot = int(wl.block_table[seq, logical_block])
+    rows = sorted(int(x) for x in rng.choice(wl.n_resid, size=n_rows, replace=False))
+    target = rms * np.sqrt(wl.head_dim)
+    for arr in (L.resid_k, L.resid_v):
+        blk = arr[slot].astype(np.float32)               # [Hkv][R][d]
+        for t in rows:
+            nrm = np.linalg.norm(blk[:, t, :], axis=-1, keepdims=True)
+            blk[:, t, :] = blk[:, t, :] * (target / nrm)
+        arr[slot] = blk.astype(np.float16)
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# The five workloads and the sensitivity variants.  Seeds are 1000 + id.
+# ---------------------------------------------------------------------------
+
+CONFIG_NAMES = {
+    0: "ctx4k_1head_r32_R40",
+    1: "qwen2.5-1.5b_layer_ctx16k",
+    2: "qwen2.5-1.5b_28layers_ctx64k_b4",
+    3: "ragged_b32_ctx8k-32k",
+    4: "llama3-8b_layer_ctx128k_b8",
+}
+
+# Layer-adaptive rank of the 28-layer stack: 0.75r early, 1.5r mid, 0.5r late (r = 32).
+STACK_RANKS = [24] * 9 + [48] * 10 + [16] * 9
+
+
+def ragged_lengths(seed: int, batch: int = 32, lo: int = 8192, hi: int = 32768) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    raw = rng.uniform(lo, hi, size=batch)
+    return (BLOCK_SIZE * np.round(raw / BLOCK_SIZE)).astype(np.int64)
+
+
+def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[int]] = None,
+                variant: str = "") -> Workload:
+    """Build configuration `cfg` (0..4).  `layers` selects a subset of the
+    28-layer stack (config 2) to bound host memory; `variant` is one of
+    "", "S1" (sigma_j = 4 * 0.9^j) or "S2" (zero anchors) for config 0."""
+    seed = 1000 + cfg if seed is None else seed
+    if cfg == 0:
+        sigma0 = 4.0 if variant == "S1" else 0.5
+        return make_workload(CONFIG_NAMES[0] + (("_" + variant) if variant else ""), seed=seed,
+                             batch=1, n_q_heads=1, n_kv_heads=1, window=512, n_blocks=[14],
+                             ranks=[32], n_resid=40, top_k=14, sigma0=sigma0,
+                             zero_anchor=(variant == "S2"))
+    assert variant == ""
+    if cfg == 1:
+        return make_workload(CONFIG_NAMES[1], seed=seed, batch=1, n_q_heads=12, n_kv_heads=2,
+                             window=1024, n_blocks=[60], ranks=[32], n_resid=128, top_k=16)
+    if cfg == 2:
+        return make_workload(CONFIG_NAMES[2], seed=seed, batch=4, n_q_heads=12, n_kv_heads=2,
+                             window=1024, n_blocks=[252] * 4, ranks=STACK_RANKS, n_resid=128,
+                             top_k=32, only_layers=layers)
+    if cfg == 3:
+        lens = ragged_lengths(seed)
+        nb = (lens - 1024) // BLOCK_SIZE
+        return make_workload(CONFIG_NAMES[3], seed=seed, batch=32, n_q_heads=12, n_kv_heads=2,
+                             window=1024, n_blocks=nb.tolist(), ranks=[32], n_resid=128, top_k=32,
+                             permute_slots=True)
+    if cfg == 4:
+        return make_workload(CONFIG_NAMES[4], seed=seed, batch=8, n_q_heads=32, n_kv_heads=8,
+                             window=2048, n_blocks=[504] * 8, ranks=[32], n_resid=128, top_k=64,
+                             decay=0.93)
+    raise ValueError(f"unknown config {cfg}")

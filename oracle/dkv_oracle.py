@@ -1,0 +1,263 @@
+"""fp64 CPU oracle for DKV decode attention over a compressed KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only tests, the package's smoke() check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library and never sees its outputs.
+
+What it computes (sources are the pages on DKV, cited by title and section):
+
+* Block storage -- "DKV: Anchor + Low-Rank Differential KV-Cache Compression
+  for Scalable Long-Context Inference" (Zenodo record, abstract) and the
+  Differential-KV README, "Core Architecture & Paper Overview", items 1-3:
+  a 256-token block keeps its first token exact as the anchor (a_k, a_v); the
+  other 255 tokens are the anchor plus a row of a joint K|V low-rank delta,
+  k_i = a_k + U_i V_K and v_i = a_v + U_i V_V with U in R^{255 x r}; R exact
+  residual tokens are kept uncompressed at recorded in-block positions.
+  Residual rows REPLACE their reconstructed twin (README, "Physical 4-Bit
+  Group-Quantized Residual Buffers": the lossy SVD twin of a residual token is
+  dropped).
+* Decode -- Zenodo abstract and README "Decode & Prefill Innovations": route to
+  the top-K blocks, score in low-rank space (the result equals attention over
+  the reconstructed rows, which is what is written out here), attend residual
+  rows and the dense recency window exactly, and merge the parts with an fp32
+  log-sum-exp ("Flash-Style LSE Combine").
+* Routing -- README "Key Environment Knobs": DKV_TOPK_BLOCKS picks the number of
+  routed blocks; DKV_CB_GQA_ROUTE averages the query heads of one GQA group;
+  DKV_CB_ROUTE_ALL scores every resident block.  The per-block routing key is
+  c = a_k + mean_i(U_i) V_K over all 255 rows of U (the workload statement of
+  the single-layer configuration); ties go to the lowest logical block index.
+
+Readings where the pages are silent (listed in the design notes):
+  the anchor is attended as its own row at position 0; the delta is relative to
+  the anchor with the singular values folded into U; the LSE is the natural log
+  of the sum of exp of scaled scores z = scale * q.k; a sequence with no rows
+  at all gives o = 0 and lse = -inf; routing scores are unscaled (scale does not
+  change the order).
+
+Every function is plain numpy in float64: inputs are upcast exactly from fp16.
+Pins against things other than this code live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK_SIZE = 256
+LOWRANK_ROWS = BLOCK_SIZE - 1
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Block reconstruction (README "Core Architecture & Paper Overview", items 1-3)
+# ---------------------------------------------------------------------------
+
+def route_key(anchor_k, u, vk) -> np.ndarray:
+    """Routing key of one block and KV head: c = a_k + mean over the 255 rows of U,
+    times V_K.  Shapes: a_k [d], U [255, r], V_K [r, d] -> [d]."""
+    return _f64(anchor_k) + _f64(u).mean(axis=0) @ _f64(vk)
+
+
+def reconstruct_block(anchor_k, anchor_v, u, vk, vv, resid_k, resid_v, resid_pos
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """Explicit K, V rows [256, d] of one block and KV head, in position order.
+
+    Position 0 is the anchor; position i in 1..255 is a + U[i-1] V; each residual
+    row t replaces position resid_pos[t].  Positions must be distinct in 1..255."""
+    ak, av = _f64(anchor_k), _f64(anchor_v)
+    U, VK, VV = _f64(u), _f64(vk), _f64(vv)
+    K = np.empty((BLOCK_SIZE, ak.shape[0]))
+    V = np.empty_like(K)
+    K[0], V[0] = ak, av
+    K[1:] = ak[None, :] + U @ VK
+    V[1:] = av[None, :] + U @ VV
+    pos = np.asarray(resid_pos, dtype=np.int64)
+    if pos.size:
+        if pos.min() < 1 or pos.max() > LOWRANK_ROWS or np.unique(pos).size != pos.size:
+            raise ValueError("residual positions must be distinct values in 1..255")
+        K[pos] = _f64(resid_k)
+        V[pos] = _f64(resid_v)
+    return K, V
+
+
+def lowrank_rows(anchor_k, anchor_v, u, vk, vv, resid_pos) -> Tuple[np.ndarray, np.ndarray]:
+    """The anchor row plus the reconstructed rows that are NOT residual positions
+    (the low-rank part of a block), in position order."""
+    ak, av = _f64(anchor_k), _f64(anchor_v)
+    keep = np.ones(BLOCK_SIZE, dtype=bool)
+    keep[np.asarray(resid_pos, dtype=np.int64)] = False
+    K = np.concatenate([ak[None], ak[None] + _f64(u) @ _f64(vk)])
+    V = np.concatenate([av[None], av[None] + _f64(u) @ _f64(vv)])
+    return K[keep], V[keep]
+
+
+# ---------------------------------------------------------------------------
+# Attention and the log-sum-exp combine (README "Flash-Style LSE Combine")
+# ---------------------------------------------------------------------------
+
+def attend(q, k_rows, v_rows, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax attention of query rows q [G, d] over (k_rows, v_rows) [n, d].
+
+    z = scale * q k^T; lse = log sum exp z (natural log); o = softmax(z) v.
+    With n = 0: o = 0 and lse = -inf."""
+    Q = np.atleast_2d(_f64(q))
+    K, V = _f64(k_rows), _f64(v_rows)
+    if K.shape[0] == 0:
+        return np.zeros((Q.shape[0], V.shape[1] if V.ndim == 2 else Q.shape[1])), \
+            np.full(Q.shape[0], -np.inf)
+    z = scale * (Q @ K.T)                          # [G, n]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    s = e.sum(axis=1, keepdims=True)
+    o = (e @ V) / s
+    lse = (m + np.log(s))[:, 0]
+    return o, lse
+
+
+def lse_merge(parts_o: Sequence[np.ndarray], parts_lse: Sequence[np.ndarray]
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge partials (o_j normalised, lse_j) of disjoint row sets.
+
+    lse = M + log sum_j exp(lse_j - M) with M = max_j lse_j;
+    o = sum_j exp(lse_j - lse) o_j.  Parts with lse = -inf carry no weight; if
+    every part is empty the result is o = 0, lse = -inf."""
+    O = np.stack([_f64(o) for o in parts_o])        # [P, ..., d]
+    L = np.stack([_f64(x) for x in parts_lse])      # [P, ...]
+    M = L.max(axis=0)
+    empty = ~np.isfinite(M)
+    Ms = np.where(empty, 0.0, M)
+    w = np.exp(L - Ms[None])
+    s = w.sum(axis=0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, Ms + np.log(np.where(empty, 1.0, s)))
+    o = np.einsum("p...,p...d->...d", w, O) / np.where(empty, 1.0, s)[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Routing (README "Key Environment Knobs": TOPK_BLOCKS, CB_GQA_ROUTE, CB_ROUTE_ALL)
+# ---------------------------------------------------------------------------
+
+def route(q_group, keys, top_k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Route one GQA group.  q_group [G, d], keys [N, d] (logical block order).
+
+    The group's query heads are averaged, every block is scored by q_bar . c_j,
+    and the K_eff = min(top_k, N) highest scores are kept; equal scores go to
+    the lower block index.  Returns (indices ascending, all N scores)."""
+    qbar = _f64(q_group).mean(axis=0)
+    C = _f64(keys)
+    n = C.shape[0]
+    s = C @ qbar if n else np.zeros(0)
+    k_eff = min(int(top_k), n)
+    order = np.lexsort((np.arange(n), -s))         # score descending, then index ascending
+    return np.sort(order[:k_eff]), s
+
+
+# ---------------------------------------------------------------------------
+# Whole decode step for one layer
+# ---------------------------------------------------------------------------
+
+def _slot_entry(pool: Dict[str, np.ndarray], slot: int, h: int) -> Dict[str, np.ndarray]:
+    return {k: pool[k][slot, h] for k in
+            ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+
+
+def route_batch(pool, q, block_table, n_blocks, n_kv_heads: int, top_k: int):
+    """Routing of every (sequence, KV head).  Returns (idx [B][Hkv][top_k] padded
+    with -1, list of per-(b, h) score vectors, list of per-(b, h) key matrices)."""
+    B, Hq, _ = q.shape
+    G = Hq // n_kv_heads
+    idx = np.full((B, n_kv_heads, top_k), -1, dtype=np.int64)
+    scores, keys_all = {}, {}
+    for b in range(B):
+        for h in range(n_kv_heads):
+            nb = int(n_blocks[b])
+            keys = np.stack([route_key(pool["anchor_k"][block_table[b, j], h],
+                                       pool["u"][block_table[b, j], h],
+                                       pool["vk"][block_table[b, j], h]) for j in range(nb)]) \
+                if nb else np.zeros((0, q.shape[-1]))
+            sel, s = route(q[b, h * G:(h + 1) * G], keys, top_k)
+            idx[b, h, :sel.size] = sel
+            scores[(b, h)] = s
+            keys_all[(b, h)] = keys
+    return idx, scores, keys_all
+
+
+def decode(pool, q, win_k, win_v, block_table, n_blocks, win_len, n_kv_heads: int,
+           top_k: int, scale: float, idx: Optional[np.ndarray] = None):
+    """One decode step of one layer.
+
+    For each sequence b and KV head h: route (unless `idx` [B][Hkv][>=K] is given,
+    -1 entries ignored), reconstruct every routed block explicitly, append the
+    first win_len[b] window rows, and attend each of the G query heads over all
+    of these rows.  Returns (out [B][Hq][d], lse [B][Hq], idx used)."""
+    B, Hq, d = q.shape
+    G = Hq // n_kv_heads
+    if idx is None:
+        idx, _, _ = route_batch(pool, q, block_table, n_blocks, n_kv_heads, top_k)
+    out = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(n_kv_heads):
+            Ks: List[np.ndarray] = []
+            Vs: List[np.ndarray] = []
+            for j in idx[b, h]:
+                if j < 0:
+                    continue
+                K, V = reconstruct_block(**_slot_entry(pool, int(block_table[b, j]), h))
+                Ks.append(K)
+                Vs.append(V)
+            w = int(win_len[b])
+            Ks.append(_f64(win_k[b, h, :w]))
+            Vs.append(_f64(win_v[b, h, :w]))
+            o, l = attend(q[b, h * G:(h + 1) * G], np.concatenate(Ks), np.concatenate(Vs), scale)
+            out[b, h * G:(h + 1) * G] = o
+            lse[b, h * G:(h + 1) * G] = l
+    return out, lse, idx
+
+
+# ---------------------------------------------------------------------------
+# Per-part partials (the split used by the library's per-kernel entry points)
+# ---------------------------------------------------------------------------
+
+def block_partials(pool, slot: int, h: int, q_group, scale: float):
+    """(o, lse) of one block's low-rank part (anchor + unmasked reconstructed rows)
+    and of its residual rows, for the query rows q_group [G, d]."""
+    e = _slot_entry(pool, slot, h)
+    Klr, Vlr = lowrank_rows(e["anchor_k"], e["anchor_v"], e["u"], e["vk"], e["vv"], e["resid_pos"])
+    lr = attend(q_group, Klr, Vlr, scale)
+    ex = attend(q_group, e["resid_k"], e["resid_v"], scale)
+    return lr, ex
+
+
+def window_partials(win_k, win_v, win_len, q, n_kv_heads: int, splits: int, scale: float):
+    """Window partials: rows [s * c, min((s+1) * c, win_len)) with c = ceil(W / splits).
+    Returns o [B][Hq][splits][d], lse [B][Hq][splits]."""
+    B, Hq, d = q.shape
+    W = win_k.shape[2]
+    G = Hq // n_kv_heads
+    c = -(-W // splits)
+    o = np.zeros((B, Hq, splits, d))
+    l = np.full((B, Hq, splits), -np.inf)
+    for b in range(B):
+        for h in range(n_kv_heads):
+            for s in range(splits):
+                a, e = s * c, min((s + 1) * c, int(win_len[b]))
+                if e <= a:
+                    continue
+                oo, ll = attend(q[b, h * G:(h + 1) * G], win_k[b, h, a:e], win_v[b, h, a:e], scale)
+                o[b, h * G:(h + 1) * G, s] = oo
+                l[b, h * G:(h + 1) * G, s] = ll
+    return o, l
+
+
+def bytes_per_block(rank: int, n_resid: int, head_dim: int = 128, elem: int = 2) -> int:
+    """Algorithmic bytes one routed block of one KV head streams at decode:
+    anchors (2d), U (255 r), V_K and V_V (2 r d) and residual K, V (2 R d) in
+    fp16, plus one byte per residual position."""
+    return elem * (2 * head_dim + LOWRANK_ROWS * rank + 2 * rank * head_dim
+                   + 2 * n_resid * head_dim) + n_resid

@@ -1,0 +1,449 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test fixes a part of the oracle by brute force on tiny inputs written
+with plain Python loops, a closed form, an exact identity of the SVD, an
+invariant, or a value the pages print.  A plausible mistake anywhere in the
+oracle (a dropped term, a wrong sign or index, the anchor skipped, residual
+rows added instead of replacing, a routing off-by-one) fails at least one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+from compressed_kv_cache_amd import synth
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BS = 256
+
+
+# ---------------------------------------------------------------------------
+# I1: brute force on tiny inputs, pure Python loops
+# ---------------------------------------------------------------------------
+
+def _bf_block_rows(pool, slot, h):
+    ak = [float(x) for x in pool["anchor_k"][slot, h]]
+    av = [float(x) for x in pool["anchor_v"][slot, h]]
+    U = [[float(x) for x in row] for row in pool["u"][slot, h]]
+    VK = [[float(x) for x in row] for row in pool["vk"][slot, h]]
+    VV = [[float(x) for x in row] for row in pool["vv"][slot, h]]
+    d, r = len(ak), len(VK)
+    K = [ak[:]]
+    V = [av[:]]
+    for i in range(1, BS):
+        K.append([ak[c] + sum(U[i - 1][j] * VK[j][c] for j in range(r)) for c in range(d)])
+        V.append([av[c] + sum(U[i - 1][j] * VV[j][c] for j in range(r)) for c in range(d)])
+    for t, p in enumerate(pool["resid_pos"][slot, h]):
+        K[int(p)] = [float(x) for x in pool["resid_k"][slot, h, t]]
+        V[int(p)] = [float(x) for x in pool["resid_v"][slot, h, t]]
+    return K, V
+
+
+def _bf_route_key(pool, slot, h):
+    ak = [float(x) for x in pool["anchor_k"][slot, h]]
+    U = pool["u"][slot, h]
+    VK = pool["vk"][slot, h]
+    r = VK.shape[0]
+    mean = [sum(float(U[i, j]) for i in range(BS - 1)) / (BS - 1) for j in range(r)]
+    return [ak[c] + sum(mean[j] * float(VK[j, c]) for j in range(r)) for c in range(len(ak))]
+
+
+def _bf_attend(q, K, V, scale):
+    z = [scale * sum(a * b for a, b in zip(q, k)) for k in K]
+    m = max(z)
+    e = [math.exp(x - m) for x in z]
+    s = sum(e)
+    o = [sum(e[t] * V[t][c] for t in range(len(V))) / s for c in range(len(V[0]))]
+    return o, m + math.log(s)
+
+
+def _bf_decode(wl, layer=0):
+    L = wl.layers[layer]
+    pool = L.pool()
+    G = wl.group
+    B, Hq, d = L.q.shape
+    out = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    idx = np.full((B, wl.n_kv_heads, wl.top_k), -1)
+    for b in range(B):
+        for h in range(wl.n_kv_heads):
+            qs = [[float(x) for x in L.q[b, h * G + g]] for g in range(G)]
+            qbar = [sum(qs[g][c] for g in range(G)) / G for c in range(d)]
+            nb = int(wl.n_blocks[b])
+            sc = []
+            for j in range(nb):
+                c = _bf_route_key(pool, int(wl.block_table[b, j]), h)
+                sc.append((-sum(a * bb for a, bb in zip(qbar, c)), j))
+            chosen = sorted(j for _, j in sorted(sc)[:min(wl.top_k, nb)])
+            idx[b, h, :len(chosen)] = chosen
+            K, V = [], []
+            for j in chosen:
+                kk, vv = _bf_block_rows(pool, int(wl.block_table[b, j]), h)
+                K += kk
+                V += vv
+            for t in range(int(wl.win_len[b])):
+                K.append([float(x) for x in L.win_k[b, h, t]])
+                V.append([float(x) for x in L.win_v[b, h, t]])
+            for g in range(G):
+                o, l = _bf_attend(qs[g], K, V, wl.scale)
+                out[b, h * G + g] = o
+                lse[b, h * G + g] = l
+    return out, lse, idx
+
+
+def _oracle_decode(wl, layer=0, idx=None):
+    L = wl.layers[layer]
+    return oracle.decode(L.pool(), L.q, L.win_k, L.win_v, wl.block_table, wl.n_blocks,
+                         wl.win_len, wl.n_kv_heads, wl.top_k, wl.scale, idx=idx)
+
+
+@pytest.mark.parametrize("hq,hkv,nblocks,topk,R,r", [
+    (2, 1, [4], 2, 5, 3),
+    (4, 2, [3, 2], 2, 7, 2),
+    (1, 1, [3], 3, 0, 4),
+])
+def test_brute_force_tiny(hq, hkv, nblocks, topk, R, r):
+    wl = synth.make_workload("tiny", seed=11 + hq + R, batch=len(nblocks), n_q_heads=hq,
+                             n_kv_heads=hkv, window=5, n_blocks=nblocks, ranks=[r], n_resid=R,
+                             top_k=topk, head_dim=8, sigma0=1.5, win_len=[5, 3][:len(nblocks)],
+                             permute_slots=True)
+    ref_o, ref_l, ref_i = _bf_decode(wl)
+    o, l, i = _oracle_decode(wl)
+    assert np.array_equal(i, ref_i)
+    assert np.abs(o - ref_o).max() < 1e-12
+    assert np.abs(l - ref_l).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I2: exact SVD identities of the joint K|V delta
+# ---------------------------------------------------------------------------
+
+def _compress_exact(K, V, r):
+    ak, av = K[0], V[0]
+    D = np.concatenate([K[1:] - ak, V[1:] - av], axis=1)      # [255, 2d] joint delta
+    Uf, S, Vt = np.linalg.svd(D, full_matrices=False)
+    d = K.shape[1]
+    return ak, av, (Uf[:, :r] * S[:r]), Vt[:r, :d], Vt[:r, d:]
+
+
+def test_svd_identity_full_joint_rank():
+    rng = np.random.default_rng(5)
+    d = 16
+    K = rng.standard_normal((BS, d))
+    V = rng.standard_normal((BS, d))
+    ak, av, U, VK, VV = _compress_exact(K, V, 2 * d)
+    Kr, Vr = oracle.reconstruct_block(ak, av, U, VK, VV, np.zeros((0, d)), np.zeros((0, d)),
+                                      np.zeros(0, dtype=np.int64))
+    assert np.abs(Kr - K).max() < 1e-12 and np.abs(Vr - V).max() < 1e-12
+    q = rng.standard_normal((3, d))
+    o, l = oracle.attend(q, Kr, Vr, 0.25)
+    z = 0.25 * q @ K.T
+    assert np.abs(o - softmax(z, axis=1) @ V).max() < 1e-12
+    assert np.abs(l - logsumexp(z, axis=1)).max() < 1e-12
+
+
+def test_svd_identity_rank_d_delta():
+    """A joint delta of rank <= d is reproduced exactly at r = d."""
+    rng = np.random.default_rng(6)
+    d = 16
+    A = rng.standard_normal((BS - 1, d))
+    a_k, a_v = rng.standard_normal(d), rng.standard_normal(d)
+    K = np.concatenate([a_k[None], a_k + A @ rng.standard_normal((d, d))])
+    V = np.concatenate([a_v[None], a_v + A @ rng.standard_normal((d, d))])
+    ak, av, U, VK, VV = _compress_exact(K, V, d)
+    Kr, Vr = oracle.reconstruct_block(ak, av, U, VK, VV, np.zeros((0, d)), np.zeros((0, d)),
+                                      np.zeros(0, dtype=np.int64))
+    assert np.abs(Kr - K).max() < 1e-10 and np.abs(Vr - V).max() < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# I3: LSE split invariance
+# ---------------------------------------------------------------------------
+
+def test_lse_split_invariance():
+    rng = np.random.default_rng(7)
+    n, d, G = 300, 16, 3
+    K = rng.standard_normal((n, d)) * 2
+    V = rng.standard_normal((n, d))
+    q = rng.standard_normal((G, d))
+    z = 0.3 * q @ K.T
+    ref_o, ref_l = softmax(z, axis=1) @ V, logsumexp(z, axis=1)
+    for trial in range(20):
+        cuts = np.sort(rng.choice(np.arange(n + 1), size=rng.integers(1, 12), replace=True))
+        bounds = [0] + cuts.tolist() + [n]               # repeated cuts give empty parts
+        perm = rng.permutation(n)
+        parts_o, parts_l = [], []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            sel = perm[a:b]
+            o, l = oracle.attend(q, K[sel], V[sel], 0.3)
+            parts_o.append(o)
+            parts_l.append(l)
+        o, l = oracle.lse_merge(parts_o, parts_l)
+        assert np.abs(o - ref_o).max() < 1e-12
+        assert np.abs(l - ref_l).max() < 1e-12
+    o, l = oracle.lse_merge([np.zeros((G, d))], [np.full(G, -np.inf)])
+    assert np.all(o == 0) and np.all(l == -np.inf)
+
+
+def test_lse_definition_equal_scores():
+    d, n = 8, 37
+    K = np.ones((n, d))
+    V = np.arange(n * d, dtype=np.float64).reshape(n, d)
+    q = np.full((1, d), 0.5)
+    o, l = oracle.attend(q, K, V, 2.0)
+    assert abs(l[0] - (2.0 * 0.5 * d + math.log(n))) < 1e-12
+    assert np.abs(o[0] - V.mean(axis=0)).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I4: residual rows replace their reconstructed twin
+# ---------------------------------------------------------------------------
+
+def test_residual_replaces_not_adds():
+    wl = synth.make_workload("i4", seed=21, batch=1, n_q_heads=2, n_kv_heads=1, window=16,
+                             n_blocks=[3], ranks=[6], n_resid=9, top_k=3, head_dim=16,
+                             sigma0=2.0)
+    L = wl.layers[0]
+    pool = {k: v.astype(np.float64) if v.dtype == np.float16 else v for k, v in L.pool().items()}
+    for s in range(pool["u"].shape[0]):
+        pos = pool["resid_pos"][s, 0].astype(np.int64)
+        pool["resid_k"][s, 0] = pool["anchor_k"][s, 0] + pool["u"][s, 0][pos - 1] @ pool["vk"][s, 0]
+        pool["resid_v"][s, 0] = pool["anchor_v"][s, 0] + pool["u"][s, 0][pos - 1] @ pool["vv"][s, 0]
+    o1, l1, _ = oracle.decode(pool, L.q, L.win_k, L.win_v, wl.block_table, wl.n_blocks,
+                              wl.win_len, 1, 3, wl.scale)
+    nores = dict(pool)
+    nores["resid_k"] = pool["resid_k"][:, :, :0]
+    nores["resid_v"] = pool["resid_v"][:, :, :0]
+    nores["resid_pos"] = pool["resid_pos"][:, :, :0]
+    o2, l2, _ = oracle.decode(nores, L.q, L.win_k, L.win_v, wl.block_table, wl.n_blocks,
+                              wl.win_len, 1, 3, wl.scale)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I5: closed form of a block whose U is zero
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R", [0, 40, 128])
+def test_closed_form_zero_delta(R):
+    wl = synth.make_workload("i5", seed=31 + R, batch=1, n_q_heads=3, n_kv_heads=1, window=4,
+                             n_blocks=[2], ranks=[8], n_resid=R, top_k=2)
+    L = wl.layers[0]
+    pool = L.pool()
+    pool["u"] = np.zeros_like(pool["u"])
+    q = L.q[0].astype(np.float64)
+    (o_lr, l_lr), _ = oracle.block_partials(pool, 1, 0, q, wl.scale)
+    ak = pool["anchor_k"][1, 0].astype(np.float64)
+    av = pool["anchor_v"][1, 0].astype(np.float64)
+    assert np.abs(l_lr - (wl.scale * q @ ak + math.log(BS - R))).max() < 1e-12
+    assert np.abs(o_lr - av[None]).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I6: routing special cases
+# ---------------------------------------------------------------------------
+
+def test_routing_all_blocks_is_identity():
+    rng = np.random.default_rng(1)
+    keys = rng.standard_normal((9, 16))
+    sel, _ = oracle.route(rng.standard_normal((2, 16)), keys, 9)
+    assert sel.tolist() == list(range(9))
+    sel, _ = oracle.route(rng.standard_normal((2, 16)), keys, 50)
+    assert sel.tolist() == list(range(9))
+
+
+def test_routing_ties_go_to_lowest_index():
+    keys = np.tile(np.arange(16, dtype=np.float64), (10, 1))
+    keys[7] *= 0.5                                     # one block scores lower
+    q = np.ones((3, 16))
+    sel, s = oracle.route(q, keys, 4)
+    assert sel.tolist() == [0, 1, 2, 3]
+    keys[8] *= 3.0                                     # one dominant block
+    sel, _ = oracle.route(q, keys, 4)
+    assert sel.tolist() == [0, 1, 2, 8]
+
+
+def test_routing_matches_exhaustive_sort():
+    rng = np.random.default_rng(2)
+    for _ in range(30):
+        n = int(rng.integers(1, 40))
+        keys = np.round(rng.standard_normal((n, 8)), 1)  # coarse values make exact ties
+        q = np.round(rng.standard_normal((2, 8)), 1)
+        k = int(rng.integers(1, 45))
+        sel, s = oracle.route(q, keys, k)
+        qbar = [(q[0, c] + q[1, c]) / 2 for c in range(8)]
+        sc = [sum(qbar[c] * keys[j, c] for c in range(8)) for j in range(n)]
+        ref = sorted(sorted(range(n), key=lambda j: (-sc[j], j))[:min(k, n)])
+        assert sel.tolist() == ref
+
+
+def test_route_key_mean_over_all_rows():
+    rng = np.random.default_rng(3)
+    ak = rng.standard_normal(8)
+    U = np.zeros((BS - 1, 4))
+    U[0, 1] = 255.0                                   # mean over 255 rows gives row 1 of V_K
+    VK = rng.standard_normal((4, 8))
+    assert np.abs(oracle.route_key(ak, U, VK) - (ak + VK[1])).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I7: GQA
+# ---------------------------------------------------------------------------
+
+def test_gqa_identical_heads_identical_outputs():
+    wl = synth.make_workload("i7", seed=41, batch=1, n_q_heads=4, n_kv_heads=2, window=8,
+                             n_blocks=[5], ranks=[4], n_resid=6, top_k=2, head_dim=16)
+    L = wl.layers[0]
+    L.q[0, 1] = L.q[0, 0]
+    L.q[0, 3] = L.q[0, 2]
+    o, l, idx = _oracle_decode(wl)
+    assert np.array_equal(o[0, 0], o[0, 1]) and np.array_equal(o[0, 2], o[0, 3])
+    # a group of identical heads routes exactly like its single head
+    wl1 = synth.make_workload("i7b", seed=41, batch=1, n_q_heads=4, n_kv_heads=2, window=8,
+                              n_blocks=[5], ranks=[4], n_resid=6, top_k=2, head_dim=16)
+    L1 = wl1.layers[0]
+    L1.q[0, 1] = L1.q[0, 0]
+    L1.q[0, 3] = L1.q[0, 2]
+    single = oracle.decode(L1.pool(), L1.q[:, ::2], L1.win_k, L1.win_v, wl1.block_table,
+                           wl1.n_blocks, wl1.win_len, 2, 2, wl1.scale)
+    assert np.array_equal(single[2], idx)
+    assert np.abs(single[0][0] - o[0, ::2]).max() < 1e-12
+
+
+def test_gqa_routes_on_group_mean():
+    rng = np.random.default_rng(4)
+    keys = rng.standard_normal((12, 16))
+    q = rng.standard_normal((3, 16))
+    a, _ = oracle.route(q, keys, 5)
+    b, _ = oracle.route(q.mean(axis=0, keepdims=True), keys, 5)
+    assert a.tolist() == b.tolist()
+
+
+# ---------------------------------------------------------------------------
+# I8: permutation invariances
+# ---------------------------------------------------------------------------
+
+def test_permutation_invariance():
+    wl = synth.make_workload("i8", seed=51, batch=2, n_q_heads=2, n_kv_heads=1, window=8,
+                             n_blocks=[4, 3], ranks=[5], n_resid=10, top_k=3, head_dim=16,
+                             sigma0=2.0)
+    L = wl.layers[0]
+    o0, l0, i0 = _oracle_decode(wl)
+    rng = np.random.default_rng(9)
+    # residual rows permuted together with their positions
+    for s in range(L.resid_k.shape[0]):
+        p = rng.permutation(L.resid_k.shape[2])
+        L.resid_k[s, 0] = L.resid_k[s, 0][p]
+        L.resid_v[s, 0] = L.resid_v[s, 0][p]
+        L.resid_pos[s, 0] = L.resid_pos[s, 0][p]
+    o1, l1, i1 = _oracle_decode(wl)
+    assert np.array_equal(i0, i1)
+    assert np.abs(o1 - o0).max() < 1e-12 and np.abs(l1 - l0).max() < 1e-12
+    # pool slots permuted with a consistent block table
+    S = L.anchor_k.shape[0]
+    perm = rng.permutation(S)                          # new slot of old slot s is perm[s]
+    for name in ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos"):
+        arr = getattr(L, name)
+        new = np.empty_like(arr)
+        new[perm] = arr
+        setattr(L, name, new)
+    wl.block_table = np.where(wl.block_table >= 0, perm[np.maximum(wl.block_table, 0)], -1)
+    o2, l2, i2 = _oracle_decode(wl)
+    assert np.array_equal(i0, i2)
+    assert np.abs(o2 - o0).max() < 1e-12 and np.abs(l2 - l0).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# I9: the self-check configuration with no compression at all
+# ---------------------------------------------------------------------------
+
+def test_self_check_no_compression():
+    wl = synth.make_workload("i9", seed=61, batch=1, n_q_heads=2, n_kv_heads=1, window=12,
+                             n_blocks=[3], ranks=[4], n_resid=255, top_k=3, head_dim=16)
+    L = wl.layers[0]
+    o, l, idx = _oracle_decode(wl)
+    rows_k, rows_v = [], []
+    for j in range(3):
+        s = int(wl.block_table[0, j])
+        rows_k += [L.anchor_k[s, 0]] + list(L.resid_k[s, 0])
+        rows_v += [L.anchor_v[s, 0]] + list(L.resid_v[s, 0])
+    rows_k += list(L.win_k[0, 0])
+    rows_v += list(L.win_v[0, 0])
+    K = np.array(rows_k, dtype=np.float64)
+    V = np.array(rows_v, dtype=np.float64)
+    z = wl.scale * L.q[0].astype(np.float64) @ K.T
+    assert np.abs(o[0] - softmax(z, axis=1) @ V).max() < 1e-12
+    assert np.abs(l[0] - logsumexp(z, axis=1)).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Partials and the split into parts used by the library's per-kernel entries
+# ---------------------------------------------------------------------------
+
+def test_block_partials_merge_to_block():
+    wl = synth.make_workload("pp", seed=71, batch=1, n_q_heads=3, n_kv_heads=1, window=8,
+                             n_blocks=[2], ranks=[6], n_resid=33, top_k=2, head_dim=16,
+                             sigma0=2.0)
+    L = wl.layers[0]
+    pool = L.pool()
+    q = L.q[0].astype(np.float64)
+    (olr, llr), (oex, lex) = oracle.block_partials(pool, 1, 0, q, wl.scale)
+    o, l = oracle.lse_merge([olr, oex], [llr, lex])
+    K, V = _bf_block_rows(pool, 1, 0)
+    for g in range(3):
+        ro, rl = _bf_attend(list(q[g]), K, V, wl.scale)
+        assert np.abs(o[g] - ro).max() < 1e-12 and abs(l[g] - rl) < 1e-12
+
+
+def test_window_partials_merge_to_window():
+    rng = np.random.default_rng(8)
+    B, Hkv, G, W, d = 2, 2, 3, 37, 8
+    wk = rng.standard_normal((B, Hkv, W, d))
+    wv = rng.standard_normal((B, Hkv, W, d))
+    q = rng.standard_normal((B, Hkv * G, d))
+    wlen = np.array([37, 20])
+    o, l = oracle.window_partials(wk, wv, wlen, q, Hkv, 5, 0.4)
+    for b in range(B):
+        for h in range(Hkv):
+            for g in range(G):
+                row = h * G + g
+                mo, ml = oracle.lse_merge(list(o[b, row]), list(l[b, row]))
+                z = 0.4 * wk[b, h, :wlen[b]] @ q[b, row]
+                assert abs(ml - logsumexp(z)) < 1e-12
+                assert np.abs(mo - softmax(z) @ wv[b, h, :wlen[b]]).max() < 1e-12
+
+
+def test_empty_sequence_gives_zero_and_neg_inf():
+    wl = synth.make_workload("empty", seed=81, batch=2, n_q_heads=2, n_kv_heads=1, window=4,
+                             n_blocks=[0, 2], ranks=[4], n_resid=3, top_k=2, head_dim=8,
+                             win_len=[0, 4])
+    o, l, idx = _oracle_decode(wl)
+    assert np.all(o[0] == 0) and np.all(l[0] == -np.inf)
+    assert np.all(idx[0] == -1)
+    assert np.all(np.isfinite(l[1]))
+
+
+# ---------------------------------------------------------------------------
+# Values the pages print: the per-block byte table
+# ---------------------------------------------------------------------------
+
+def test_block_byte_accounting_matches_pages():
+    g = json.load(open(os.path.join(HERE, "golden", "dkv_block_bytes.json")))
+    H, r = g["kv_heads"], g["rank"]
+    rows = g["rows"]
+    full = oracle.bytes_per_block(r, 128)
+    lowrank_only = oracle.bytes_per_block(r, 0)
+    # our per-head block bytes decompose into the pages' rows (per head, fp16)
+    u_bytes = 2 * 255 * r
+    assert H * u_bytes == rows["u_coefficients"]["bytes"]
+    assert H * 2 * 128 * 2 == rows["anchors"]["bytes"]
+    assert H * (full - lowrank_only - 128) == rows["exact_residuals_R128"]["bytes"]
+    assert H * (oracle.bytes_per_block(r, 64) - lowrank_only - 64) == rows["exact_residuals_R64"]["bytes"]
+    assert H * 2 * 256 * 128 * 2 == rows["dense_block"]["bytes"]
+    assert lowrank_only == u_bytes + 2 * 2 * 128 + 2 * 2 * r * 128
