@@ -1,0 +1,280 @@
+"""Thin Python binding of libdkv_attn (argument marshalling only).
+
+Every computation runs in the HIP library; this module only fills the C structs
+from torch tensors (device pointers, element strides), allocates output tensors
+with torch, and passes torch's current HIP stream.  If the built library is
+missing it raises instead of falling back to anything else.
+
+Entry points mirror include/dkv_attn.h: route_keys, route_topk, lowrank_attn,
+exact_attn, lse_merge, decode_workspace_size, decode.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdkv_attn.so")
+
+HEAD_DIM = 128
+BLOCK_SIZE = 256
+
+DKV_OK = 0
+DKV_ERR_INVALID_ARG = 1
+DKV_ERR_UNSUPPORTED = 2
+DKV_ERR_WORKSPACE = 3
+DKV_ERR_HIP = 4
+
+EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route_keys",
+            "dkv_route_topk", "dkv_lowrank_attn", "dkv_exact_attn", "dkv_lse_merge",
+            "dkv_decode_workspace_size", "dkv_decode")
+
+
+class DKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class View(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("slot_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64)]
+
+
+class PoolC(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("n_resid", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("anchor_k", View), ("anchor_v", View), ("u", View), ("vk", View), ("vv", View),
+                ("resid_k", View), ("resid_v", View), ("resid_pos", View), ("route_key", View)]
+
+
+class BatchC(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("block_table", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p),
+                ("win_len", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the built library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(PoolC)
+    Bp = ctypes.POINTER(BatchC)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.dkv_status_string.argtypes = [i32]
+    lib.dkv_status_string.restype = ctypes.c_char_p
+    lib.dkv_last_error.argtypes = []
+    lib.dkv_last_error.restype = ctypes.c_char_p
+    lib.dkv_abi_version.argtypes = []
+    lib.dkv_abi_version.restype = i32
+    lib.dkv_route_keys.argtypes = [P, vp, i32, vp]
+    lib.dkv_route_keys.restype = i32
+    lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
+    lib.dkv_route_topk.restype = i32
+    lib.dkv_lowrank_attn.argtypes = [P, Bp, vp, i32, f32, vp, vp, i32, i32, vp]
+    lib.dkv_lowrank_attn.restype = i32
+    lib.dkv_exact_attn.argtypes = [P, Bp, vp, i32, i32, f32, vp, vp, i32, i32, vp]
+    lib.dkv_exact_attn.restype = i32
+    lib.dkv_lse_merge.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.dkv_lse_merge.restype = i32
+    lib.dkv_decode_workspace_size.argtypes = [P, Bp, i32]
+    lib.dkv_decode_workspace_size.restype = ctypes.c_size_t
+    lib.dkv_decode.argtypes = [P, Bp, i32, f32, vp, ctypes.c_size_t, vp, vp, vp, vp]
+    lib.dkv_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != DKV_OK:
+        lib = load()
+        raise DKVError(status, f"{what}: {lib.dkv_status_string(status).decode()}: "
+                               f"{lib.dkv_last_error().decode()}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _view(t, dims_inside: int) -> View:
+    """View of a tensor shaped [slots][heads][...inside...] (strides in elements)."""
+    if t is None:
+        return View(None, 0, 0)
+    st = t.stride()
+    return View(t.data_ptr(), st[0], st[1])
+
+
+class Pool:
+    """One layer's block pool on the device (torch tensors kept alive here).
+
+    anchor_k, anchor_v fp16 [S][Hkv][128]; u fp16 [S][Hkv][255][r];
+    vk, vv fp16 [S][Hkv][r][128]; resid_k, resid_v fp16 [S][Hkv][R][128];
+    resid_pos uint8 [S][Hkv][R]; route_key fp32 [S][Hkv][128].
+    Inner dimensions must be packed; outer (slot, head) strides are free."""
+
+    def __init__(self, anchor_k, anchor_v, u, vk, vv, resid_k, resid_v, resid_pos, route_key):
+        self.tensors = dict(anchor_k=anchor_k, anchor_v=anchor_v, u=u, vk=vk, vv=vv,
+                            resid_k=resid_k, resid_v=resid_v, resid_pos=resid_pos,
+                            route_key=route_key)
+        S, Hkv = anchor_k.shape[0], anchor_k.shape[1]
+        self.rank = int(u.shape[-1])
+        self.n_resid = int(resid_k.shape[2])
+        self.n_kv_heads = int(Hkv)
+        self.n_slots = int(S)
+        self.c = PoolC(HEAD_DIM, BLOCK_SIZE, self.rank, self.n_resid, self.n_kv_heads, self.n_slots,
+                       _view(anchor_k, 1), _view(anchor_v, 1), _view(u, 2), _view(vk, 2),
+                       _view(vv, 2), _view(resid_k, 2), _view(resid_v, 2), _view(resid_pos, 1),
+                       _view(route_key, 1))
+
+    @classmethod
+    def from_numpy(cls, arrays: dict, device="cuda"):
+        import torch
+        t = {k: torch.from_numpy(arrays[k]).to(device) for k in
+             ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+        S, Hkv, d = arrays["anchor_k"].shape
+        rk = torch.zeros((S, Hkv, d), dtype=torch.float32, device=device)
+        return cls(t["anchor_k"], t["anchor_v"], t["u"], t["vk"], t["vv"], t["resid_k"],
+                   t["resid_v"], t["resid_pos"], rk)
+
+    @property
+    def route_key(self):
+        return self.tensors["route_key"]
+
+
+class Batch:
+    """One decode step's batch on the device.
+
+    q fp16 [B][Hq][128]; win_k, win_v fp16 [B][Hkv][W][128]; block_table int32
+    [B][max_blocks]; n_blocks int32 [B]; win_len int32 [B] or None."""
+
+    def __init__(self, q, win_k, win_v, block_table, n_blocks, win_len=None):
+        self.tensors = dict(q=q, win_k=win_k, win_v=win_v, block_table=block_table,
+                            n_blocks=n_blocks, win_len=win_len)
+        B, Hq = int(q.shape[0]), int(q.shape[1])
+        W = int(win_k.shape[2]) if win_k is not None else 0
+        mb = int(block_table.shape[1]) if block_table is not None else 0
+        self.batch, self.n_q_heads, self.window, self.max_blocks = B, Hq, W, mb
+        self.c = BatchC(B, Hq, W, mb, _ptr(block_table), _ptr(n_blocks), _ptr(win_len), _ptr(q),
+                        _ptr(win_k), _ptr(win_v))
+
+    @classmethod
+    def from_numpy(cls, q, win_k, win_v, block_table, n_blocks, win_len=None, device="cuda"):
+        import torch
+
+        def up(a):
+            return None if a is None else torch.from_numpy(a).to(device)
+        return cls(up(q), up(win_k), up(win_v), up(block_table), up(n_blocks), up(win_len))
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+
+def route_keys(pool: Pool, slots=None, stream=None) -> None:
+    lib = load()
+    n = 0 if slots is None else int(slots.numel())
+    _check(lib.dkv_route_keys(ctypes.byref(pool.c), _ptr(slots), n, _stream(stream)), "dkv_route_keys")
+
+
+def route_topk(pool: Pool, batch: Batch, top_k: int, with_scores: bool = False, stream=None):
+    import torch
+    lib = load()
+    dev = batch.tensors["q"].device
+    idx = torch.empty((batch.batch, pool.n_kv_heads, top_k), dtype=torch.int32, device=dev)
+    sc = torch.empty((batch.batch, pool.n_kv_heads, top_k), dtype=torch.float32, device=dev) \
+        if with_scores else None
+    _check(lib.dkv_route_topk(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, _ptr(idx),
+                              _ptr(sc), _stream(stream)), "dkv_route_topk")
+    return (idx, sc) if with_scores else idx
+
+
+def _parts(batch: Batch, n_parts: int, part_o, part_lse, dev):
+    import torch
+    rows = batch.batch * batch.n_q_heads
+    if part_o is None:
+        part_o = torch.empty((rows, n_parts, HEAD_DIM), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((rows, n_parts), dtype=torch.float32, device=dev)
+    return part_o, part_lse
+
+
+def lowrank_attn(pool: Pool, batch: Batch, idx, top_k: int, scale: float, part_o=None,
+                 part_lse=None, n_parts: Optional[int] = None, part_offset: int = 0, stream=None):
+    lib = load()
+    n_parts = top_k + part_offset if n_parts is None else n_parts
+    part_o, part_lse = _parts(batch, n_parts, part_o, part_lse, batch.tensors["q"].device)
+    _check(lib.dkv_lowrank_attn(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(idx), top_k,
+                                scale, _ptr(part_o), _ptr(part_lse), n_parts, part_offset,
+                                _stream(stream)), "dkv_lowrank_attn")
+    return part_o, part_lse
+
+
+def exact_attn(pool: Pool, batch: Batch, idx, top_k: int, window_splits: int, scale: float,
+               part_o=None, part_lse=None, n_parts: Optional[int] = None, part_offset: int = 0,
+               stream=None):
+    lib = load()
+    n_parts = top_k + window_splits + part_offset if n_parts is None else n_parts
+    part_o, part_lse = _parts(batch, n_parts, part_o, part_lse, batch.tensors["q"].device)
+    _check(lib.dkv_exact_attn(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(idx), top_k,
+                              window_splits, scale, _ptr(part_o), _ptr(part_lse), n_parts,
+                              part_offset, _stream(stream)), "dkv_exact_attn")
+    return part_o, part_lse
+
+
+def lse_merge(part_o, part_lse, stream=None):
+    import torch
+    lib = load()
+    rows, n_parts = int(part_lse.shape[0]), int(part_lse.shape[1])
+    out = torch.empty((rows, HEAD_DIM), dtype=torch.float16, device=part_o.device)
+    lse = torch.empty((rows,), dtype=torch.float32, device=part_o.device)
+    _check(lib.dkv_lse_merge(_ptr(part_o), _ptr(part_lse), n_parts, rows, HEAD_DIM, _ptr(out),
+                             _ptr(lse), _stream(stream)), "dkv_lse_merge")
+    return out, lse
+
+
+def decode_workspace_size(pool: Pool, batch: Batch, top_k: int) -> int:
+    return int(load().dkv_decode_workspace_size(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k))
+
+
+def alloc_workspace(pool: Pool, batch: Batch, top_k: int):
+    import torch
+    n = max(decode_workspace_size(pool, batch, top_k), 256)
+    return torch.empty((n,), dtype=torch.uint8, device=batch.tensors["q"].device)
+
+
+def decode(pool: Pool, batch: Batch, top_k: int, scale: float, workspace=None, out=None,
+           out_lse=None, out_idx=None, return_idx: bool = True, stream=None):
+    """One fused decode step.  Returns (out fp16 [B][Hq][128], lse fp32 [B][Hq], idx or None)."""
+    import torch
+    lib = load()
+    dev = batch.tensors["q"].device
+    if workspace is None:
+        workspace = alloc_workspace(pool, batch, top_k)
+    if out is None:
+        out = torch.empty((batch.batch, batch.n_q_heads, HEAD_DIM), dtype=torch.float16, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((batch.batch, batch.n_q_heads), dtype=torch.float32, device=dev)
+    if out_idx is None and return_idx and top_k > 0:
+        out_idx = torch.empty((batch.batch, pool.n_kv_heads, top_k), dtype=torch.int32, device=dev)
+    _check(lib.dkv_decode(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, scale,
+                          _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                          _ptr(out), _ptr(out_lse), _ptr(out_idx), _stream(stream)), "dkv_decode")
+    return out, out_lse, out_idx

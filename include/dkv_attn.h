@@ -1,0 +1,208 @@
+/*
+ * dkv_attn.h -- C ABI of libdkv_attn: DKV decode attention over a compressed
+ * KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the pages "DKV: Anchor + Low-Rank
+ * Differential KV-Cache Compression for Scalable Long-Context Inference"
+ * (Zenodo record, abstract) and the Differential-KV README ("Core Architecture
+ * & Paper Overview", "Decode & Prefill Innovations", "Key Environment Knobs").
+ *
+ * Storage of one 256-token block, per layer and KV head:
+ *   anchor (a_k, a_v)   the block's first token, exact                 fp16 [d] each
+ *   U                   joint K|V delta coefficients of tokens 1..255  fp16 [255][r]
+ *   V_K, V_V            right bases of the delta                       fp16 [r][d] each
+ *   residual rows       exact K, V rows                                fp16 [R][d] each
+ *   residual positions  in-block position (1..255) of each residual    uint8 [R]
+ *   route key           c = a_k + mean_i(U_i) V_K                      fp32 [d]
+ * Token i (1..255) of a block is k_i = a_k + U_{i-1} V_K, v_i = a_v + U_{i-1} V_V,
+ * except that a residual row replaces the token at its recorded position.
+ *
+ * Decode output for query head g of sequence b is exact softmax attention
+ * over: the 256 rows of each routed block (anchor, reconstructed rows that are
+ * not residual positions, residual rows) and the first win_len[b] rows of the
+ * dense recency window, with scores z = scale * q_g . k.  The library never
+ * materialises reconstructed K or V; scores of reconstructed rows are taken
+ * in the rank-r space, q.a_k + U_i.(V_K q), and their values gathered as
+ * (sum p) a_v + (p^T U) V_V.
+ *
+ * Conventions shared by every entry point
+ *   - head_dim d = 128 and block size 256 are fixed (DKV_ERR_UNSUPPORTED
+ *     otherwise); 1 <= r <= 64; 0 <= R <= 255; G = Hq / Hkv <= 16.
+ *   - All pointers in dkv_pool / dkv_batch and every array argument are DEVICE
+ *     pointers, owned by the caller.  The library allocates nothing, frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return; results are valid after the stream is
+ *     synchronised.  Device-side faults surface at that synchronisation.
+ *   - Scalar arguments, pointer presence and alignment are validated on the
+ *     host before anything is enqueued; on failure the call returns an error
+ *     code, enqueues nothing, and dkv_last_error() describes the problem.
+ *   - Contents of device arrays are preconditions and are not checked on the
+ *     hot path: residual positions distinct in 1..255, finite values.  Block
+ *     table entries outside [0, n_slots) and idx entries outside
+ *     [0, n_blocks[b]) are treated as empty blocks (no rows), never read.
+ *   - Alignment: every fp16 / fp32 array base and every slot / head stride
+ *     (in bytes) must be a multiple of 16, except `u` (a multiple of 8 bytes
+ *     when r is a multiple of 4, else of 2) and `resid_pos` (any alignment).
+ *   - Deterministic: identical inputs give bit-identical outputs (fixed
+ *     reduction orders, no floating-point atomics).
+ *   - lse values are natural logarithms of sums of exp of SCALED scores.
+ *     A part or a sequence with no rows has o = 0 and lse = -inf.
+ *   - fp16 outputs are rounded from fp32 to nearest even.
+ */
+#ifndef DKV_ATTN_H
+#define DKV_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DKV_ABI_VERSION 1
+#define DKV_HEAD_DIM 128
+#define DKV_BLOCK_SIZE 256
+#define DKV_MAX_RANK 64
+#define DKV_MAX_RESID 255
+#define DKV_MAX_GROUP 16
+#define DKV_MAX_ROUTE_BLOCKS 16384
+
+typedef int32_t dkv_status;
+#define DKV_OK 0
+#define DKV_ERR_INVALID_ARG 1  /* null pointer, negative size, bad combination */
+#define DKV_ERR_UNSUPPORTED 2  /* d != 128, block != 256, r > 64, R > 255, G > 16, misalignment */
+#define DKV_ERR_WORKSPACE 3    /* workspace missing or smaller than dkv_decode_workspace_size() */
+#define DKV_ERR_HIP 4          /* a HIP launch failed; see dkv_last_error() */
+
+/* A strided view of one per-(slot, KV head) array of the block pool: the entry of
+ * (slot s, head h) starts at element  ptr + s * slot_stride + h * head_stride
+ * (strides in ELEMENTS of the array's type); inside an entry rows are packed. */
+typedef struct dkv_view {
+  const void* ptr;
+  int64_t slot_stride;
+  int64_t head_stride;
+} dkv_view;
+
+/* One layer's block pool (README "Core Architecture & Paper Overview", items 1-3). */
+typedef struct dkv_pool {
+  int32_t head_dim;    /* d, must be 128 */
+  int32_t block_size;  /* must be 256 */
+  int32_t rank;        /* r, 1..64 */
+  int32_t n_resid;     /* R, 0..255: residual rows stored in every block */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t n_slots;     /* number of blocks the pool holds */
+  dkv_view anchor_k;   /* fp16 [d]      */
+  dkv_view anchor_v;   /* fp16 [d]      */
+  dkv_view u;          /* fp16 [255][r] */
+  dkv_view vk;         /* fp16 [r][d]   */
+  dkv_view vv;         /* fp16 [r][d]   */
+  dkv_view resid_k;    /* fp16 [R][d]   */
+  dkv_view resid_v;    /* fp16 [R][d]   */
+  dkv_view resid_pos;  /* uint8 [R], distinct values in 1..255 */
+  dkv_view route_key;  /* fp32 [d]; written by dkv_route_keys, read by routing */
+} dkv_pool;
+
+/* One decode step's batch: one new query token per sequence. */
+typedef struct dkv_batch {
+  int32_t batch;             /* B >= 0 sequences */
+  int32_t n_q_heads;         /* Hq, a multiple of n_kv_heads with Hq / Hkv <= 16 */
+  int32_t window;            /* W: window rows allocated per (sequence, KV head) */
+  int32_t max_blocks;        /* columns of block_table */
+  const int32_t* block_table;/* int32 [B][max_blocks]: pool slot of logical block j */
+  const int32_t* n_blocks;   /* int32 [B]: compressed blocks of each sequence (<= max_blocks) */
+  const int32_t* win_len;    /* int32 [B]: valid window rows (<= W), or NULL for W everywhere */
+  const void* q;             /* fp16 [B][Hq][d]: the decode queries (post-RoPE) */
+  const void* win_k;         /* fp16 [B][Hkv][W][d]: exact recency window keys */
+  const void* win_v;         /* fp16 [B][Hkv][W][d]: exact recency window values */
+} dkv_batch;
+
+/* Human-readable name of a status code (static string). */
+const char* dkv_status_string(dkv_status status);
+
+/* Detail of the last failing call on this thread (static thread-local buffer). */
+const char* dkv_last_error(void);
+
+/* DKV_ABI_VERSION of the built library. */
+int32_t dkv_abi_version(void);
+
+/* Routing-key precompute, once per sealed block (off the per-query path).
+ * Computes c = a_k + (1/255) sum_{i=1..255} U_i V_K in fp32 for every KV head of
+ * the listed slots and stores it through pool->route_key (which must point to
+ * writable memory).  The routing key is the block's centroid key, the mean of
+ * its anchor-relative reconstructed rows 1..255 (all of them, residual
+ * positions included); the pages keep such per-block router metadata (README,
+ * "Per-Block Memory Breakdown", the decode-router row).
+ *   slots:   int32 [n_list] pool slots to process, or NULL for every slot
+ *            (then n_list is ignored).  Out-of-range slots are skipped. */
+dkv_status dkv_route_keys(const dkv_pool* pool, const int32_t* slots, int32_t n_list,
+                          void* stream);
+
+/* Top-K block routing (README "Key Environment Knobs": DKV_TOPK_BLOCKS,
+ * DKV_CB_GQA_ROUTE head averaging, DKV_CB_ROUTE_ALL scoring of every block).
+ * For each (sequence b, KV head h): q_bar = mean of the group's G query heads
+ * (fp32), s_j = q_bar . c_j over all n_blocks[b] logical blocks, and the
+ * K_eff = min(top_k, n_blocks[b]) largest scores are kept, ties going to the
+ * lower logical block index.
+ *   idx:    int32 [B][Hkv][top_k] out: chosen logical block indices, ascending,
+ *           entries beyond K_eff set to -1.
+ *   scores: fp32 [B][Hkv][top_k] out, or NULL: score of each chosen block in idx
+ *           order (-inf for padding).
+ * top_k >= 1; max_blocks <= DKV_MAX_ROUTE_BLOCKS. */
+dkv_status dkv_route_topk(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k,
+                          int32_t* idx, float* scores, void* stream);
+
+/* Partials layout shared by the attention entry points and dkv_lse_merge:
+ * row r = b * Hq + head, part p:
+ *   part_o  [n_rows][n_parts][d]  fp32, normalised (sum p v / sum p)
+ *   part_lse[n_rows][n_parts]     fp32, log sum exp of the part's scaled scores
+ * An entry point writes parts part_offset .. part_offset + (its count) - 1. */
+
+/* Low-rank part of each routed block (README "Decode & Prefill Innovations":
+ * low-rank space query scoring).  For routed block k of (b, h) it attends the
+ * anchor row and the 255 reconstructed rows minus the residual positions:
+ *   z_0 = scale q.a_k,  z_i = scale (q.a_k + U_i.(V_K q)),
+ *   o = ((sum p) a_v + (p^T U) V_V) / sum p.
+ * Writes top_k parts (k = 0..top_k-1); idx entries of -1 give empty parts.
+ *   idx: int32 [B][Hkv][top_k] logical block indices (as from dkv_route_topk). */
+dkv_status dkv_lowrank_attn(const dkv_pool* pool, const dkv_batch* batch, const int32_t* idx,
+                            int32_t top_k, float scale, float* part_o, float* part_lse,
+                            int32_t n_parts, int32_t part_offset, void* stream);
+
+/* Exact attention (Zenodo abstract: residuals and the dense recency window are
+ * attended exactly).  Writes top_k parts holding the R residual rows of routed
+ * block k (only when idx != NULL; with idx == NULL top_k must be 0), then
+ * window_splits parts: part s covers window rows [s c, min((s+1) c, win_len[b]))
+ * with c = ceil(W / window_splits). */
+dkv_status dkv_exact_attn(const dkv_pool* pool, const dkv_batch* batch, const int32_t* idx,
+                          int32_t top_k, int32_t window_splits, float scale, float* part_o,
+                          float* part_lse, int32_t n_parts, int32_t part_offset, void* stream);
+
+/* Flash-style log-sum-exp combine (README "Decode & Prefill Innovations"):
+ * for each of n_rows rows, M = max_p lse_p, lse = M + log sum_p exp(lse_p - M),
+ * o = sum_p exp(lse_p - lse) o_p, summed in part order.
+ *   out:     fp16 [n_rows][d] out;  out_lse: fp32 [n_rows] out.
+ * head_dim must be 128. */
+dkv_status dkv_lse_merge(const float* part_o, const float* part_lse, int32_t n_parts,
+                         int32_t n_rows, int32_t head_dim, void* out, float* out_lse,
+                         void* stream);
+
+/* Bytes of workspace dkv_decode needs for this pool, batch and top_k (>= 0). */
+size_t dkv_decode_workspace_size(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k);
+
+/* One fused decode step of one layer: routing, low-rank + residual attention of
+ * every routed block, window attention and the LSE combine (the Zenodo abstract's
+ * decode path).  top_k = 0 attends the window only.
+ *   workspace: device memory of >= dkv_decode_workspace_size() bytes, 256-byte
+ *              aligned, owned by the caller, contents need not be initialised.
+ *   out:     fp16 [B][Hq][d] out;  out_lse: fp32 [B][Hq] out.
+ *   out_idx: int32 [B][Hkv][top_k] out (the routed blocks), or NULL. */
+dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
+                      void* workspace, size_t workspace_bytes, void* out, float* out_lse,
+                      int32_t* out_idx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_ATTN_H */

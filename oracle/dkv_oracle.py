@@ -24,8 +24,9 @@ What it computes (sources are the pages on DKV, cited by title and section):
 * Routing -- README "Key Environment Knobs": DKV_TOPK_BLOCKS picks the number of
   routed blocks; DKV_CB_GQA_ROUTE averages the query heads of one GQA group;
   DKV_CB_ROUTE_ALL scores every resident block.  The per-block routing key is
-  c = a_k + mean_i(U_i) V_K over all 255 rows of U (the workload statement of
-  the single-layer configuration); ties go to the lowest logical block index.
+  the block's centroid key c = a_k + mean_i(U_i) V_K over all 255 rows of U
+  (the pages keep per-block decode-router metadata, README "Per-Block Memory
+  Breakdown"); ties go to the lowest logical block index.
 
 Readings where the pages are silent (listed in the design notes):
   the anchor is attended as its own row at position 0; the delta is relative to

@@ -1,0 +1,333 @@
+"""GPU parity: every C-ABI entry point against the fp64 oracle.
+
+Bars (see parity.py): routing identical outside the near-tie band; decode
+max |d out| <= 1e-2 and |d lse| <= 1e-3, compared on the GPU's accepted routed
+set; per-part partials |d lse| <= 1e-3 and relative |d o| <= 1e-3.
+"""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+from compressed_kv_cache_amd import synth
+import oracle
+import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="session")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from compressed_kv_cache_amd import lib as L
+    L.load()                       # raises if the HIP library is not built
+    return L
+
+
+DEV = "cuda:0"
+
+
+@functools.lru_cache(maxsize=None)
+def config(cfg, variant=""):
+    if cfg == 2:
+        return synth.make_config(2, layers=[0, 9, 19, 27])
+    return synth.make_config(cfg, variant=variant)
+
+
+@functools.lru_cache(maxsize=None)
+def planted_config1():
+    """Config 1 with 8 outlier residual rows planted in a block the oracle routes
+    for KV head 0 (planting residual rows does not move routing keys)."""
+    wl = synth.make_config(1)
+    L0 = wl.layers[0]
+    idx, _, _ = oracle.route_batch(L0.pool(), L0.q, wl.block_table, wl.n_blocks, wl.n_kv_heads,
+                                   wl.top_k)
+    blk = int(idx[0, 0, 0])
+    synth.plant_outlier_rows(wl, blk)
+    wl.notes = f"planted block {blk}"
+    wl.planted = blk
+    return wl
+
+
+def upload(L, wl, layer=0):
+    lay = wl.layers[layer]
+    pool = L.Pool.from_numpy(lay.pool(), DEV)
+    batch = L.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                               wl.win_len, device=DEV)
+    L.route_keys(pool)
+    return pool, batch
+
+
+def oracle_routing(wl, layer=0):
+    lay = wl.layers[layer]
+    return oracle.route_batch(lay.pool(), lay.q, wl.block_table, wl.n_blocks, wl.n_kv_heads,
+                              wl.top_k)
+
+
+def check_decode(L, wl, layer=0, label=""):
+    say(f"[decode] {wl.name} {label} layer={layer}")
+    pool, batch = upload(L, wl, layer)
+    out, lse, idx = L.decode(pool, batch, wl.top_k, wl.scale)
+    torch.cuda.synchronize()
+    lay = wl.layers[layer]
+    gidx = idx.cpu().numpy().astype(np.int64) if idx is not None else \
+        np.full((wl.batch, wl.n_kv_heads, 0), -1)
+    if wl.top_k > 0:
+        _, scores, keys = oracle_routing(wl, layer)
+        rc = parity.check_routing(gidx, scores, keys, lay.q, wl.n_kv_heads, wl.top_k)
+        assert rc.ok, rc.message
+    else:
+        rc = parity.RouteCheck(True, 0)
+    ref_o, ref_l, _ = oracle.decode(lay.pool(), lay.q, lay.win_k, lay.win_v, wl.block_table,
+                                    wl.n_blocks, wl.win_len, wl.n_kv_heads, wl.top_k, wl.scale,
+                                    idx=gidx)
+    oc = parity.check_outputs(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l)
+    say(f"   near-ties {rc.near_ties}; max|d out| {oc.max_out:.3e} max|d lse| {oc.max_lse:.3e} "
+        f"rel {oc.rel_l2:.3e}")
+    assert oc.ok, oc.message
+    return gidx, out, lse
+
+
+# ---------------------------------------------------------------------------
+# Routing keys and routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (1, ""), (2, "")])
+def test_route_keys(lib, cfg, variant):
+    wl = config(cfg, variant)
+    say(f"[route_keys] {wl.name} {variant}")
+    pool, _ = upload(lib, wl)
+    got = pool.route_key.cpu().numpy().astype(np.float64)
+    P = wl.layers[0].pool()
+    S, H = got.shape[:2]
+    worst = 0.0
+    for s in range(S):
+        for h in range(H):
+            ref = oracle.route_key(P["anchor_k"][s, h], P["u"][s, h], P["vk"][s, h])
+            worst = max(worst, float(np.abs(got[s, h] - ref).max() / (np.abs(ref).max() + 1.0)))
+    say(f"   max rel err {worst:.2e}")
+    assert worst < 2e-6
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3, 4, 2])
+def test_route_topk(lib, cfg):
+    wl = config(cfg)
+    for layer in range(len(wl.layers)):
+        say(f"[route_topk] {wl.name} layer {layer}")
+        pool, batch = upload(lib, wl, layer)
+        idx, sc = lib.route_topk(pool, batch, wl.top_k, with_scores=True)
+        torch.cuda.synchronize()
+        _, scores, keys = oracle_routing(wl, layer)
+        rc = parity.check_routing(idx.cpu().numpy(), scores, keys, wl.layers[layer].q,
+                                  wl.n_kv_heads, wl.top_k)
+        say(f"   near-ties {rc.near_ties}")
+        assert rc.ok, rc.message
+        g = idx.cpu().numpy()
+        s = sc.cpu().numpy()
+        for (b, h), ref in scores.items():
+            sel = g[b, h][g[b, h] >= 0]
+            assert np.allclose(s[b, h][:sel.size], ref[sel], rtol=1e-4, atol=1e-4)
+            assert np.all(np.isneginf(s[b, h][sel.size:]))
+
+
+def test_route_ties_go_to_lowest_index(lib):
+    wl = synth.make_workload("ties", seed=5, batch=2, n_q_heads=4, n_kv_heads=2, window=16,
+                             n_blocks=[40, 25], ranks=[16], n_resid=8, top_k=10)
+    lay = wl.layers[0]
+    for name in ("anchor_k", "u", "vk"):
+        arr = getattr(lay, name)
+        arr[:] = arr[0:1]                       # every block identical: all scores tie
+    pool, batch = upload(lib, wl)
+    idx = lib.route_topk(pool, batch, 10).cpu().numpy()
+    assert np.array_equal(idx, np.broadcast_to(np.arange(10), idx.shape))
+    # one dominant block is always chosen, the rest of the ties by lowest index
+    G = wl.group
+    for h in range(2):
+        qbar = lay.q[0, h * G:(h + 1) * G].astype(np.float32).mean(axis=0)
+        lay.anchor_k[int(wl.block_table[0, 30]), h] = (10 * qbar).astype(np.float16)
+    pool, batch = upload(lib, wl)
+    idx = lib.route_topk(pool, batch, 10).cpu().numpy()
+    assert 30 in idx[0, 0] and 30 in idx[0, 1]
+
+
+def test_route_more_blocks_than_topk_and_padding(lib):
+    wl = synth.make_workload("pad", seed=6, batch=3, n_q_heads=6, n_kv_heads=2, window=8,
+                             n_blocks=[3, 0, 70], ranks=[8], n_resid=4, top_k=5, max_blocks=80)
+    pool, batch = upload(lib, wl)
+    idx = lib.route_topk(pool, batch, 5).cpu().numpy()
+    _, scores, keys = oracle_routing(wl)
+    rc = parity.check_routing(idx, scores, keys, wl.layers[0].q, 2, 5)
+    assert rc.ok, rc.message
+    assert np.array_equal(idx[0, 0], [0, 1, 2, -1, -1]) and np.all(idx[1] == -1)
+
+
+# ---------------------------------------------------------------------------
+# Per-part entry points (sensitivity variant S3: per-block partials)
+# ---------------------------------------------------------------------------
+
+def _all_blocks_idx(wl):
+    K = int(wl.n_blocks.max())
+    idx = np.full((wl.batch, wl.n_kv_heads, K), -1, dtype=np.int32)
+    for b in range(wl.batch):
+        idx[b, :, :wl.n_blocks[b]] = np.arange(wl.n_blocks[b])
+    return idx
+
+
+@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (1, "")])
+def test_block_partials(lib, cfg, variant):
+    wl = config(cfg, variant)
+    say(f"[block partials] {wl.name} {variant}")
+    pool, batch = upload(lib, wl)
+    idx = _all_blocks_idx(wl)
+    K = idx.shape[-1]
+    gi = torch.from_numpy(idx).to(DEV)
+    lo, ll = lib.lowrank_attn(pool, batch, gi, K, wl.scale)
+    eo, el = lib.exact_attn(pool, batch, gi, K, 0, wl.scale)
+    torch.cuda.synchronize()
+    lo, ll, eo, el = (t.cpu().numpy() for t in (lo, ll, eo, el))
+    lay = wl.layers[0]
+    G = wl.group
+    ref_lo, ref_ll, ref_eo, ref_el = (np.zeros_like(lo, dtype=np.float64), np.zeros_like(ll, dtype=np.float64),
+                                      np.zeros_like(eo, dtype=np.float64), np.zeros_like(el, dtype=np.float64))
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            for k in range(K):
+                j = idx[b, h, k]
+                slot = int(wl.block_table[b, j])
+                (o1, l1), (o2, l2) = oracle.block_partials(lay.pool(), slot, h,
+                                                          lay.q[b, h * G:(h + 1) * G], wl.scale)
+                rows = slice(b * wl.n_q_heads + h * G, b * wl.n_q_heads + (h + 1) * G)
+                ref_lo[rows, k], ref_ll[rows, k] = o1, l1
+                ref_eo[rows, k], ref_el[rows, k] = o2, l2
+    c1 = parity.check_partials(lo, ll, ref_lo, ref_ll)
+    c2 = parity.check_partials(eo, el, ref_eo, ref_el)
+    say(f"   low-rank: rel {c1.rel_l2:.2e} lse {c1.max_lse:.2e}; residual: rel {c2.rel_l2:.2e} "
+        f"lse {c2.max_lse:.2e}")
+    assert c1.ok, c1.message
+    assert c2.ok, c2.message
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 37])
+def test_window_partials(lib, splits):
+    wl = synth.make_workload("win", seed=7, batch=3, n_q_heads=8, n_kv_heads=2, window=300,
+                             n_blocks=[1, 1, 1], ranks=[8], n_resid=4, top_k=1,
+                             win_len=[300, 17, 0])
+    say(f"[window partials] splits={splits}")
+    pool, batch = upload(lib, wl)
+    po, pl = lib.exact_attn(pool, batch, None, 0, splits, wl.scale)
+    torch.cuda.synchronize()
+    lay = wl.layers[0]
+    ro, rl = oracle.window_partials(lay.win_k, lay.win_v, wl.win_len, lay.q, 2, splits, wl.scale)
+    c = parity.check_partials(po.cpu().numpy(), pl.cpu().numpy(),
+                              ro.reshape(po.shape), rl.reshape(pl.shape))
+    assert c.ok, c.message
+
+
+def test_lse_merge(lib):
+    rng = np.random.default_rng(3)
+    rows, parts = 37, 23
+    o = rng.standard_normal((rows, parts, 128)).astype(np.float32)
+    l = (rng.standard_normal((rows, parts)) * 5).astype(np.float32)
+    l[3, :5] = -np.inf
+    o[3, :5] = 0
+    l[7, :] = -np.inf                             # a row with no rows at all
+    o[7, :] = 0
+    out, lse = lib.lse_merge(torch.from_numpy(o).to(DEV), torch.from_numpy(l).to(DEV))
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(list(np.moveaxis(o, 1, 0)), list(np.moveaxis(l, 1, 0)))
+    c = parity.check_outputs(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, tol_out=2e-3, tol_lse=1e-5)
+    assert c.ok, c.message
+    assert np.all(out[7].cpu().numpy() == 0) and np.isneginf(lse[7].item())
+
+
+# ---------------------------------------------------------------------------
+# Fused decode on the five workloads and the sensitivity variants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (3, ""), (4, "")])
+def test_decode_configs(lib, cfg, variant):
+    check_decode(lib, config(cfg, variant), label=variant)
+
+
+def test_decode_config1_planted_outliers(lib):
+    wl = planted_config1()
+    gidx, out, lse = check_decode(lib, wl, label=wl.notes)
+    assert wl.planted in gidx[0, 0]
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_decode_stack_layers(lib, layer):
+    """The 28-layer 64k batch-4 stack, one layer of each rank (24, 48, 16) and the
+    last layer, at full size in the per-layer launch the benchmark times."""
+    check_decode(lib, config(2), layer=layer, label=f"rank {config(2).layers[layer].rank}")
+
+
+EDGE = {
+    "no_residuals": dict(n_resid=0),
+    "rank1": dict(ranks=[1]),
+    "odd_rank7": dict(ranks=[7]),
+    "rank64": dict(ranks=[64]),
+    "rank15_R255": dict(ranks=[15], n_resid=255),
+    "group1": dict(n_q_heads=2, n_kv_heads=2),
+    "group16": dict(n_q_heads=16, n_kv_heads=1),
+    "ragged_window": dict(window=37, win_len=[37, 5, 0, 36]),
+    "empty_sequence": dict(n_blocks=[3, 0, 5, 2], win_len=[64, 0, 64, 64]),
+    "topk_over_n": dict(top_k=9, n_blocks=[3, 7, 1, 8]),
+    "window_only": dict(top_k=0),
+    "permuted_pool": dict(permute_slots=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_decode_edge_cases(lib, case):
+    kw = dict(seed=100 + len(case), batch=4, n_q_heads=6, n_kv_heads=2, window=64,
+              n_blocks=[5, 3, 6, 4], ranks=[12], n_resid=20, top_k=3, sigma0=2.0)
+    kw.update(EDGE[case])
+    wl = synth.make_workload(case, **kw)
+    check_decode(lib, wl, label=case)
+
+
+def test_decode_invalid_table_entries_are_empty(lib):
+    wl = synth.make_workload("badslot", seed=9, batch=2, n_q_heads=4, n_kv_heads=2, window=32,
+                             n_blocks=[4, 4], ranks=[8], n_resid=6, top_k=4)
+    pool, batch = upload(lib, wl)
+    bt = torch.from_numpy(wl.block_table.copy()).to(DEV)
+    bt[0, 2] = -1
+    bt[1, 1] = 10_000
+    batch2 = lib.Batch(batch.tensors["q"], batch.tensors["win_k"], batch.tensors["win_v"], bt,
+                       batch.tensors["n_blocks"], batch.tensors["win_len"])
+    out, lse, idx = lib.decode(pool, batch2, 4, wl.scale)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy().astype(np.int64)
+    lay = wl.layers[0]
+    # reference: the bad blocks contribute no rows
+    pool_np = lay.pool()
+    keep = g.copy()
+    keep[0][keep[0] == 2] = -1
+    keep[1][keep[1] == 1] = -1
+    ro, rl, _ = oracle.decode(pool_np, lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                              wl.win_len, 2, 4, wl.scale, idx=keep)
+    c = parity.check_outputs(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+    assert c.ok, c.message
+
+
+def test_decode_is_deterministic(lib):
+    wl = config(1)
+    pool, batch = upload(lib, wl)
+    ws = lib.alloc_workspace(pool, batch, wl.top_k)
+    a = [t.clone() for t in lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws)]
+    b = [t.clone() for t in lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws)]
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

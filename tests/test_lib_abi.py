@@ -1,0 +1,144 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status codes before
+enqueueing anything.  No call here reaches a kernel launch, so these run
+without a GPU."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_kv_cache_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dkv_attn.h")
+
+
+@pytest.fixture(scope="module")
+def clib():
+    if not os.path.exists(L.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return L.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dkv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(clib):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(clib, n), f"{n} declared in dkv_attn.h but not exported"
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_abi_version_and_status_strings(clib):
+    m = re.search(r"#define DKV_ABI_VERSION (\d+)", open(HEADER).read())
+    assert clib.dkv_abi_version() == int(m.group(1))
+    for code, name in [(0, "DKV_OK"), (1, "DKV_ERR_INVALID_ARG"), (2, "DKV_ERR_UNSUPPORTED"),
+                       (3, "DKV_ERR_WORKSPACE"), (4, "DKV_ERR_HIP")]:
+        assert clib.dkv_status_string(code).decode() == name
+
+
+FAKE = 0x10000  # 64 KiB-aligned dummy address: never dereferenced on the host
+
+
+def _pool(**kw):
+    v = L.View(FAKE, 4096, 1024)
+    p = L.PoolC(128, 256, 32, 16, 2, 10, v, v, L.View(FAKE, 16320, 8160), v, v, v, v,
+                L.View(FAKE, 32, 16), L.View(FAKE, 256, 128))
+    for k, val in kw.items():
+        setattr(p, k, val)
+    return p
+
+
+def _batch(**kw):
+    b = L.BatchC(2, 12, 64, 8, FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    for k, val in kw.items():
+        setattr(b, k, val)
+    return b
+
+
+def _decode(clib, pool, batch, top_k=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
+    return clib.dkv_decode(ctypes.byref(pool) if pool is not None else None,
+                           ctypes.byref(batch) if batch is not None else None, top_k,
+                           0.088, ws, ws_bytes, out, FAKE, None, None)
+
+
+@pytest.mark.parametrize("pool_kw,batch_kw,top_k,code", [
+    ({"head_dim": 64}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"block_size": 128}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"rank": 0}, {}, 4, L.DKV_ERR_INVALID_ARG),
+    ({"rank": 65}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"n_resid": 256}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"n_resid": -1}, {}, 4, L.DKV_ERR_INVALID_ARG),
+    ({"n_kv_heads": 0}, {}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {"n_q_heads": 13}, 4, L.DKV_ERR_INVALID_ARG),
+    ({"n_kv_heads": 1}, {"n_q_heads": 17}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({}, {"window": -1}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {"q": None}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {"q": FAKE + 2}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({}, {"block_table": None}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {"win_k": None}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {"max_blocks": 20000}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"vk": L.View(FAKE + 8, 4096, 1024)}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"vk": L.View(FAKE, 4100, 1024)}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"u": L.View(None, 0, 0)}, {}, 4, L.DKV_ERR_INVALID_ARG),
+    ({}, {}, -1, L.DKV_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_arguments(clib, pool_kw, batch_kw, top_k, code):
+    st = _decode(clib, _pool(**pool_kw), _batch(**batch_kw), top_k=top_k)
+    assert st == code, (st, clib.dkv_last_error().decode())
+    assert clib.dkv_last_error().decode() != ""
+
+
+def test_decode_null_structs_and_workspace(clib):
+    assert _decode(clib, None, _batch()) == L.DKV_ERR_INVALID_ARG
+    assert _decode(clib, _pool(), None) == L.DKV_ERR_INVALID_ARG
+    need = clib.dkv_decode_workspace_size(ctypes.byref(_pool()), ctypes.byref(_batch()), 4)
+    assert _decode(clib, _pool(), _batch(), ws_bytes=need - 1) == L.DKV_ERR_WORKSPACE
+    assert _decode(clib, _pool(), _batch(), ws=None) == L.DKV_ERR_WORKSPACE
+    assert _decode(clib, _pool(), _batch(), ws=FAKE + 16) == L.DKV_ERR_WORKSPACE
+    assert _decode(clib, _pool(), _batch(), out=None) == L.DKV_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(clib):
+    assert _decode(clib, _pool(), _batch(batch=0)) == L.DKV_OK
+    p, b = _pool(), _batch(batch=0)
+    assert clib.dkv_route_topk(ctypes.byref(p), ctypes.byref(b), 4, FAKE, None, None) == L.DKV_OK
+
+
+def test_workspace_size_formula(clib):
+    def a256(x):
+        return (x + 255) // 256 * 256
+    p, b = _pool(), _batch()
+    for top_k in (0, 1, 16, 64):
+        n_parts = top_k + (64 + 127) // 128
+        rows = 2 * 12
+        want = a256(2 * 2 * top_k * 4) + a256(rows * n_parts * 4) + a256(rows * n_parts * 128 * 4)
+        assert clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) == want
+    assert clib.dkv_decode_workspace_size(None, ctypes.byref(b), 4) == 0
+
+
+def test_other_entry_points_validate(clib):
+    p, b = _pool(), _batch()
+    P, B = ctypes.byref(p), ctypes.byref(b)
+    assert clib.dkv_route_topk(P, B, 0, FAKE, None, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_route_topk(P, B, 4, None, None, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_lowrank_attn(P, B, FAKE, 4, 0.1, FAKE, FAKE, 3, 0, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_lowrank_attn(P, B, FAKE, 0, 0.1, FAKE, FAKE, 3, 0, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_exact_attn(P, B, None, 2, 1, 0.1, FAKE, FAKE, 3, 0, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_exact_attn(P, B, FAKE, 2, 2, 0.1, FAKE, FAKE, 3, 0, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_exact_attn(P, B, FAKE, 0, -1, 0.1, FAKE, FAKE, 3, 0, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_lse_merge(FAKE, FAKE, 4, 8, 64, FAKE, FAKE, None) == L.DKV_ERR_UNSUPPORTED
+    assert clib.dkv_lse_merge(FAKE, FAKE, -1, 8, 128, FAKE, FAKE, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_lse_merge(FAKE, FAKE, 4, 0, 128, FAKE, FAKE, None) == L.DKV_OK
+    assert clib.dkv_route_keys(P, FAKE, -1, None) == L.DKV_ERR_INVALID_ARG
+    q = _pool(route_key=L.View(FAKE + 4, 256, 128))
+    assert clib.dkv_route_keys(ctypes.byref(q), None, 0, None) == L.DKV_ERR_UNSUPPORTED
