@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a compressed KV cache on one MI355X.
+
+Workload: the Qwen2.5-1.5B-shaped 28-layer stack at 64k context, batch 4
+(12 query heads over 2 KV heads, d = 128, 252 compressed blocks of 256 tokens
+plus a 1024-token exact window per sequence, 128 residual rows per block, top-K
+= 32 routed blocks, layer ranks 24 / 48 / 16).  Synthetic seeded caches of that
+shape stand in for model-derived KV (no weights or datasets are used).
+
+One step = one decode query for each of the 4 sequences in each of the 28
+layers (112 queries): 28 per-layer dkv_decode calls (routing, block and window
+attention, log-sum-exp merge), with every input resident in HBM.  The step is
+timed eagerly with hipEvents around every decode kernel, and as a captured
+hipGraph replay.  Prints one JSON line.
+
+Roofline: each layer's decode is one kernel, k_decode.  Its algorithmic bytes
+per launch are, for each (sequence, KV head), the fp32 routing keys of all N
+blocks (512 N bytes), K_eff routed blocks of P(r, R) = 2*(2d + 255 r + 2 r d +
+2 R d) + R bytes and 2*2*W*d window bytes, plus the fp16 queries, outputs, lse
+and routed indices; divided by the kernel duration measured with hipEvents
+around it in the same timed (eager) steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+METRIC = "decode attention queries/sec + achieved HBM GB/s over compressed KV at 64k ctx"
+D = 128
+
+
+def bytes_per_block(rank: int, n_resid: int) -> int:
+    """Algorithmic bytes of one routed block of one KV head (fp16, + u8 positions)."""
+    return 2 * (2 * D + 255 * rank + 2 * rank * D + 2 * n_resid * D) + n_resid
+
+
+def layer_bytes(batch, hkv, hq, top_k_eff, rank, n_resid, window, n_blocks):
+    """Per-layer algorithmic bytes by stage: route keys + q (routing), routed
+    blocks + window + q (attention), output (merge)."""
+    route = batch * hkv * n_blocks * D * 4 + batch * hq * D * 2
+    attend = batch * hkv * (top_k_eff * bytes_per_block(rank, n_resid) + 2 * 2 * window * D) \
+        + batch * hq * D * 2
+    merge = batch * hq * (D * 2 + 4) + batch * hkv * top_k_eff * 4
+    return route, attend, merge
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "compressed_kv_cache_amd", "csrc", "dkv_attn.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest: str):
+    """HBM bytes per k_attend launch from the committed rocprofv3 PMC summary, or
+    None when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "k_attend_traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+CPU_SAMPLE_LAYERS = (0, 9, 19, 27)      # one layer of each rank (24, 48, 16) and the last
+
+
+def cpu_baseline(sample: dict, seconds: float, log):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    decode steps of the sample layers (all 4 sequences each), cycled until about
+    `seconds` of CPU time are spent.  sample: {layer index: Workload}."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:                                   # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    runs, spent = 0, 0.0
+    keys = sorted(sample)
+    while spent < seconds:
+        li = keys[runs % len(keys)]
+        wl = sample[li]
+        lay = wl.layers[0]
+        t0 = time.perf_counter()
+        oracle.decode(lay.pool(), lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                      wl.win_len, wl.n_kv_heads, wl.top_k, wl.scale)
+        spent += time.perf_counter() - t0
+        runs += 1
+        if runs % len(keys) == 0:
+            log(f"cpu baseline: {runs} layer decodes, {spent:.1f} s")
+    queries = runs * 4
+    return {"value": queries / spent, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} one-layer decode steps (4 sequences each) cycling over layers "
+                      f"{list(keys)} of the stack: routing over all 252 blocks, explicit "
+                      f"decompression of the 32 routed blocks and dense fp64 softmax; {spent:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=28, help="layers of the stack to use (default all 28)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this size (PMC scaling reference)")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from compressed_kv_cache_amd import lib, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    lib.load()
+
+    if args.copy_probe_mib:
+        # a plain device copy of known size: the reference for HBM counter scaling
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n * 4} bytes read and written per dispatch")
+        del a, b
+
+    hip = Hip()
+    n_layers = max(1, min(28, args.layers))
+    layer_ids = list(range(n_layers))
+    # ---- build the resident cache: one layer at a time on the host
+    pools, batches, wss, outs, lses, idxs = [], [], [], [], [], []
+    meta = None
+    cpu_sample = {}
+    t0 = time.perf_counter()
+    for li in layer_ids:
+        wl = synth.make_config(2, layers=[li])
+        lay = wl.layers[0]
+        pool = lib.Pool.from_numpy(lay.pool(), dev)
+        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                                     wl.win_len, device=dev)
+        lib.route_keys(pool)                      # once per sealed block, not per query
+        pools.append(pool)
+        batches.append(batch)
+        wss.append(lib.alloc_workspace(pool, batch, wl.top_k))
+        outs.append(torch.empty((wl.batch, wl.n_q_heads, D), dtype=torch.float16, device=dev))
+        lses.append(torch.empty((wl.batch, wl.n_q_heads), dtype=torch.float32, device=dev))
+        idxs.append(torch.empty((wl.batch, wl.n_kv_heads, wl.top_k), dtype=torch.int32, device=dev))
+        meta = wl
+        if li in CPU_SAMPLE_LAYERS and not args.no_cpu_baseline:
+            cpu_sample[li] = wl
+        del wl, lay
+        if li % 7 == 6:
+            log(f"uploaded {li + 1} layers ({time.perf_counter() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    wl = meta
+    resident = sum(sum(t.numel() * t.element_size() for t in p.tensors.values()) for p in pools) + \
+        sum(sum(t.numel() * t.element_size() for t in b.tensors.values() if t is not None) for b in batches)
+    log(f"resident cache {resident / 1e9:.2f} GB in {time.perf_counter() - t0:.0f} s")
+
+    B, Hq, Hkv, K, R, W, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.top_k, wl.n_resid, wl.window, 252
+    ranks = [synth.STACK_RANKS[i] for i in layer_ids]
+    per_layer = [layer_bytes(B, Hkv, Hq, min(K, N), r, R, W, N) for r in ranks]
+    step_route = sum(x[0] for x in per_layer)
+    step_attend = sum(x[1] for x in per_layer)
+    step_merge = sum(x[2] for x in per_layer)
+    step_bytes = step_route + step_attend + step_merge
+    queries_per_step = B * n_layers
+
+    def step_eager():
+        for i in range(n_layers):
+            lib.decode(pools[i], batches[i], K, wl.scale, workspace=wss[i], out=outs[i],
+                       out_lse=lses[i], out_idx=idxs[i])
+
+    # ---- eager, with hipEvents around every layer's decode kernel, in the timed steps
+    ev = [[[hip.event() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step_eager()
+    torch.cuda.synchronize()
+    ref_out = [o.clone() for o in outs]
+    ref_lse = [x.clone() for x in lses]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        for i in range(n_layers):
+            lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
+                                ev[s][i], out_idx=idxs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_eager = t_start.elapsed_time(t_end) / args.steps
+    kern = np.array([[hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for i in range(n_layers)]
+                     for s in range(args.steps)])
+    kernel_ms = float(kern.mean())
+    for s in ev:
+        for e2 in s:
+            for e in e2:
+                hip.destroy(e)
+    log(f"eager: {ms_eager:.4f} ms/step; decode kernel {kernel_ms * 1e3:.2f} us per layer "
+        f"(p10 {np.percentile(kern, 10) * 1e3:.2f}, p90 {np.percentile(kern, 90) * 1e3:.2f})")
+    for i in range(n_layers):
+        assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
+            "eager steps are not bit-identical"
+
+    # ---- the same step captured once as a hipGraph
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step_eager()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step_eager()
+        torch.cuda.synchronize()
+        for rep in range(3):                              # every replay equals eager
+            for o in outs:
+                o.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for i in range(n_layers):
+                assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
+                    f"graph replay {rep} differs from eager"
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.steps):
+            g.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        ms_graph = t_start.elapsed_time(t_end) / args.steps
+        log(f"hipGraph: {ms_graph:.4f} ms/step")
+
+    best_ms = ms_eager if ms_graph is None else min(ms_eager, ms_graph)
+    mode = "hipgraph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"
+    qps = queries_per_step / (best_ms * 1e-3)
+    gbps = step_bytes / (best_ms * 1e-3) / 1e9
+    launch_bytes = step_bytes / n_layers                  # one decode kernel per layer
+    kernel_gbps = launch_bytes / (kernel_ms * 1e-3) / 1e9
+    digest = source_digest()
+    traffic = measured_traffic(digest)
+
+    res = {
+        "metric": METRIC,
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": best_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": synth.CONFIG_NAMES[2] if n_layers == 28 else
+                   f"{synth.CONFIG_NAMES[2]}_first{n_layers}layers",
+                   "batch": B, "layers": n_layers, "context": 65536, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "window": W, "blocks_per_seq": N, "block_size": 256, "top_k": K,
+                   "resid_rows": R, "ranks": "24 (layers 0-8), 48 (9-18), 16 (19-27)",
+                   "timed_mode": mode, "accumulate": "f32"},
+        "achieved_GBps": gbps,
+        "hbm_frac": gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "queries_per_step": queries_per_step,
+        "ms_per_step_eager": ms_eager,
+        "ms_per_step_graph": ms_graph,
+        "kernel_us_per_layer": kernel_ms * 1e3,
+        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": kernel_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes,
+                     "avg_launch_us": kernel_ms * 1e3},
+        "resident_cache_GB": resident / 1e9,
+        "kernel_source_sha256_16": digest,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cpu_sample or {layer_ids[0]: meta}, args.cpu_seconds, log)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

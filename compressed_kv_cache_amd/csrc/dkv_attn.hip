@@ -44,12 +44,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kD = 128;            // head dim
-constexpr int kThreads = 256;      // 4 waves of 64
-constexpr int kWaves = 4;
 constexpr int kLowRankRows = 255;  // tokens 1..255 of a block
 constexpr int kVStride = 132;      // LDS row stride (halves) of 128-wide tiles: conflict-free column reads
 constexpr int kWinChunk = 128;     // window rows per part in dkv_decode
-constexpr int kMaxRQ = 80;         // augmented rank r + 1 rounded up to 16, r <= 64
 
 thread_local char g_err[512] = "";
 
@@ -90,6 +87,7 @@ struct BatchArgs {
 
 struct AttnArgs {
   const int32_t* idx;
+  const int32_t* slots;  // [units][top_k] routed pool slots (-1: none), or NULL to look them up
   int top_k;           // row stride of idx
   int n_block_parts;   // parts per unit that are routed blocks (top_k or 0)
   int block_mode;      // bit 0: low-rank rows of a block, bit 1: its residual rows
@@ -122,13 +120,53 @@ __device__ __forceinline__ void split_hl(float x0, float x1, float x2, float x3,
   }
 }
 
+// LDS hand-off between lanes of one wave: LDS operations of a wave complete in
+// order, so waiting for this wave's outstanding LDS operations (lgkmcnt = 0)
+// before reading what other lanes wrote is enough; the empty asm and the wave
+// barrier keep the compiler from moving LDS accesses across this point.
 __device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = 63 (no wait), expcnt = 7, lgkmcnt = 0
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ v8h ld8(const f16* p) { return *reinterpret_cast<const v8h*>(p); }
+
+// Values handed from one workgroup to another inside a launch are written and
+// read with device-scope (agent) relaxed atomics: these go to the device-wide
+// coherence point, so no L2 write-back fence is needed on the hot path.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's stores have completed
+__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Loads are always issued from an in-bounds address and masked afterwards: a
+// guarded load would compile to its own branch, and the branch merge to a full
+// wait for every outstanding load.
+__device__ __forceinline__ v8h ld8_mask(const f16* p, bool keep) {
+  uint4 x = *reinterpret_cast<const uint4*>(p);
+  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  x.x &= m;
+  x.y &= m;
+  x.z &= m;
+  x.w &= m;
+  return __builtin_bit_cast(v8h, x);
+}
+
+__device__ __forceinline__ v4h ld4_mask(const f16* p, bool keep) {
+  uint2 x = *reinterpret_cast<const uint2*>(p);
+  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  x.x &= m;
+  x.y &= m;
+  return __builtin_bit_cast(v4h, x);
+}
 
 __device__ __forceinline__ v4h lo4(v8h x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
 __device__ __forceinline__ v4h hi4(v8h x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
@@ -170,7 +208,8 @@ __device__ __forceinline__ float from_ordered(uint32_t k) {
   return __uint_as_float(u);
 }
 
-// Exclusive count of `flag` over the workgroup in thread order, and the total.
+// Exclusive count of `flag` over the workgroup (NW waves) in thread order, and the total.
+template <int NW>
 __device__ __forceinline__ void block_count(bool flag, int& excl, int& total, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const unsigned long long m = __ballot(flag);
@@ -180,7 +219,7 @@ __device__ __forceinline__ void block_count(bool flag, int& excl, int& total, ui
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const int c = (int)wsum[i];
     off += (i < w) ? c : 0;
     tot += c;
@@ -217,137 +256,283 @@ __global__ __launch_bounds__(128) void k_route_keys(PoolArgs P, const int32_t* s
 }
 
 // ----------------------------------------------------------------------------
-// Top-K routing
+// Top-K routing: one workgroup of 8 waves per (sequence, KV head)
 // ----------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void k_route_topk(PoolArgs P, BatchArgs Bt, int top_k,
-                                                         int32_t* idx, float* scores) {
-  extern __shared__ uint32_t keys[];  // [mb]
-  __shared__ float qbar[kD];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t suf[256];
-  __shared__ uint32_t wsum[kWaves];
-  __shared__ int sh_digit;
-  __shared__ uint32_t sh_above;
+constexpr int kRouteThreads = 512;
 
+template <int NW>
+struct RouteShared {
+  float qbar[kD] __attribute__((aligned(16)));
+  uint32_t hist[256];
+  uint32_t wsum[NW];
+  uint32_t digit, above;
+};
+
+// Route one (sequence, KV head) unit u with a workgroup of NT threads.
+// keys: LDS scratch of at least max_blocks words.
+template <int NT>
+__device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
+                                           float* scores, int32_t* slots_out, uint32_t* keys,
+                                           RouteShared<NT / 64>& sh) {
+  float* qbar = sh.qbar;
+  uint32_t* hist = sh.hist;
+  uint32_t* wsum = sh.wsum;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int u = blockIdx.x;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
   int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
   N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
   const int keff = top_k < N ? top_k : N;
 
+  // GQA mean of the group's query heads (all G loads in flight, summed in head order)
   if (tid < kD) {
+    float v[DKV_MAX_GROUP];
+#pragma unroll
+    for (int g = 0; g < DKV_MAX_GROUP; ++g) {
+      const int gc = g < Bt.G ? g : Bt.G - 1;
+      const float x = (float)Bt.q[((int64_t)b * Bt.Hq + h * Bt.G + gc) * kD + tid];
+      v[g] = (g < Bt.G) ? x : 0.f;
+    }
     float s = 0.f;
-    for (int g = 0; g < Bt.G; ++g) s += (float)Bt.q[((int64_t)b * Bt.Hq + h * Bt.G + g) * kD + tid];
+#pragma unroll
+    for (int g = 0; g < DKV_MAX_GROUP; ++g) s += v[g];
     qbar[tid] = s / (float)Bt.G;
   }
   __syncthreads();
 
-  const float q0 = qbar[2 * lane], q1 = qbar[2 * lane + 1];
-  for (int j = wave; j < N; j += kWaves) {
-    const int slot = Bt.table[(int64_t)b * Bt.mb + j];
-    const bool ok = slot >= 0 && slot < P.n_slots;
-    float part = 0.f;
-    if (ok) {
-      const float2 c = *reinterpret_cast<const float2*>(P.key + slot * P.key_s + h * P.key_h + 2 * lane);
-      part = q0 * c.x + q1 * c.y;
-    }
+  // one thread per block: the whole 512-byte routing key is loaded at once
+  for (int j0 = 0; j0 < N; j0 += NT) {
+    const int j = j0 + tid;
+    const int jc = j < N ? j : N - 1;
+    const int slot_raw = Bt.table[(int64_t)b * Bt.mb + jc];
+    const bool ok = slot_raw >= 0 && slot_raw < P.n_slots;
+    const int slot = ok ? slot_raw : 0;
+    const float4* c = reinterpret_cast<const float4*>(P.key + slot * P.key_s + h * P.key_h);
+    float4 v[kD / 4];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-    if (lane == 0) keys[j] = ordered_key(ok ? part : -INFINITY);
+    for (int i = 0; i < kD / 4; ++i) v[i] = c[i];
+    const float4* qb = reinterpret_cast<const float4*>(qbar);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kD / 4; ++i) {
+      const float4 qq = qb[i];
+      acc += v[i].x * qq.x + v[i].y * qq.y + v[i].z * qq.z + v[i].w * qq.w;
+    }
+    if (j < N) keys[j] = ordered_key(ok ? acc : -INFINITY);
   }
   __syncthreads();
 
   if (keff > 0) {
+    // radix select of the keff-th largest key, 8 bits per pass
     uint32_t prefix = 0u, pmask = 0u;
     uint32_t krem = (uint32_t)keff;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      hist[tid] = 0u;
+      if (tid < 256) hist[tid] = 0u;
       __syncthreads();
-      for (int j = tid; j < N; j += kThreads) {
+      for (int j = tid; j < N; j += NT) {
         const uint32_t k = keys[j];
         if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
       }
       __syncthreads();
-      suf[tid] = hist[tid];
-      __syncthreads();
-      for (int off = 1; off < 256; off <<= 1) {
-        const uint32_t add = (tid + off < 256) ? suf[tid + off] : 0u;
-        __syncthreads();
-        suf[tid] += add;
-        __syncthreads();
+      if (wave == 0) {
+        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        const uint32_t mine = h0 + h1 + h2 + h3;
+        uint32_t incl = mine;  // sum over lanes >= this lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t v = __shfl_down(incl, off, 64);
+          if (lane + off < 64) incl += v;
+        }
+        const uint32_t above = incl - mine;  // bins 4 * lane + 4 and higher
+        const uint32_t s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+        if (s3 >= krem && above < krem) { sh.digit = 4 * lane + 3; sh.above = above; }
+        if (s2 >= krem && s3 < krem) { sh.digit = 4 * lane + 2; sh.above = s3; }
+        if (s1 >= krem && s2 < krem) { sh.digit = 4 * lane + 1; sh.above = s2; }
+        if (s0 >= krem && s1 < krem) { sh.digit = 4 * lane; sh.above = s1; }
       }
-      const uint32_t nxt = (tid < 255) ? suf[tid + 1] : 0u;
-      if (suf[tid] >= krem && nxt < krem) {
-        sh_digit = tid;
-        sh_above = nxt;
-      }
       __syncthreads();
-      prefix |= (uint32_t)sh_digit << shift;
+      prefix |= sh.digit << shift;
       pmask |= 0xFFu << shift;
-      krem -= sh_above;
-      __syncthreads();
+      krem -= sh.above;
     }
+    // keys above the threshold, then the lowest-index keys equal to it
     const uint32_t T = prefix;
     int eq_base = 0, sel_base = 0;
-    for (int c0 = 0; c0 < N; c0 += kThreads) {
+    for (int c0 = 0; c0 < N; c0 += NT) {
       const int j = c0 + tid;
       const bool in = j < N;
       const uint32_t k = in ? keys[j] : 0u;
       const bool eq = in && k == T;
       int eq_rank, eq_tot;
-      block_count(eq, eq_rank, eq_tot, wsum);
+      block_count<(NT / 64)>(eq, eq_rank, eq_tot, wsum);
       const bool sel = in && (k > T || (eq && (uint32_t)(eq_base + eq_rank) < krem));
       int sel_rank, sel_tot;
-      block_count(sel, sel_rank, sel_tot, wsum);
+      block_count<(NT / 64)>(sel, sel_rank, sel_tot, wsum);
       if (sel) {
         const int pos = sel_base + sel_rank;
-        idx[(int64_t)u * top_k + pos] = j;
-        if (scores) scores[(int64_t)u * top_k + pos] = from_ordered(k);
+        st_dev(&idx[(int64_t)u * top_k + pos], j);
+        if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
+        if (slots_out) {
+          const int sl = Bt.table[(int64_t)b * Bt.mb + j];
+          st_dev(&slots_out[(int64_t)u * top_k + pos], (sl >= 0 && sl < P.n_slots) ? sl : -1);
+        }
       }
       eq_base += eq_tot;
       sel_base += sel_tot;
     }
   }
-  for (int pos = keff + tid; pos < top_k; pos += kThreads) {
-    idx[(int64_t)u * top_k + pos] = -1;
-    if (scores) scores[(int64_t)u * top_k + pos] = -INFINITY;
+  for (int pos = keff + tid; pos < top_k; pos += NT) {
+    st_dev(&idx[(int64_t)u * top_k + pos], -1);
+    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], -INFINITY);
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], -1);
   }
 }
 
-// ----------------------------------------------------------------------------
-// Attention over one part: a routed block (low-rank and/or residual rows) or a
-// chunk of window rows.  One workgroup of 4 waves per part.
-// ----------------------------------------------------------------------------
-
-__host__ __device__ inline int wave_region_bytes(int rq) {
-  int a = 16 * kVStride * 2;            // V tile, fp16
-  const int b = 16 * (rq + 4) * 2;      // Ux tile, fp16
-  const int c = 16 * rq * 4;            // W transpose, fp32
-  if (b > a) a = b;
-  if (c > a) a = c;
-  return (a + 15) & ~15;
+__global__ __launch_bounds__(kRouteThreads) void k_route_topk(PoolArgs P, BatchArgs Bt, int top_k,
+                                                              int32_t* idx, float* scores, int32_t* slots_out) {
+  extern __shared__ uint32_t keys[];  // [mb] ordered score keys
+  __shared__ RouteShared<kRouteThreads / 64> sh;
+  route_unit<kRouteThreads>(P, Bt, blockIdx.x, top_k, idx, scores, slots_out, keys, sh);
 }
 
-__host__ __device__ inline int attend_lds_bytes(int rq) {
-  return 16 * rq * 4                    // V_K q (fp32) [16][rq]
-         + rq * kVStride * 2            // VVx staged [rq][132] fp16
-         + 8 * 4                        // residual-position mask
-         + 2 * kWaves * 16 * 4          // per-wave softmax statistics
-         + kWaves * wave_region_bytes(rq);
+// ----------------------------------------------------------------------------
+// Attention over one part: a routed block (its low-rank rows and/or its
+// residual rows) or a chunk of window rows.  One workgroup of 4 waves per part,
+// two workgroups per CU.
+//
+// Wave w takes low-rank tiles w, w+4, w+8, w+12 (16 block positions each) and
+// exact-row tiles w, w+4, ... (16 rows each), with one online-softmax state per
+// query head.  Every load a wave needs is issued before its first use, in the
+// order of use; exact rows beyond the first two tiles are streamed two tiles
+// ahead.  The final phase rescales the four states to the common maximum,
+// sums them in a fixed order and applies V_V once: wave w finishes output
+// columns 16 w .. 16 w + 15 and 64 + 16 w .. 64 + 16 w + 15.
+// ----------------------------------------------------------------------------
+
+constexpr int kAttThreads = 256;
+constexpr int kAttWaves = kAttThreads / 64;
+constexpr int kLRTilesPerWave = 16 / kAttWaves;
+constexpr int kRedStride = 132;  // floats per row of the reduction buffer (conflict-free C-layout access)
+
+__host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
+
+// per-wave scratch: the V tile of an exact tile, or the Ux transpose of a
+// low-rank tile, followed by that wave's residual-position bit mask
+__host__ __device__ inline int att_scratch_bytes(int rq) {
+  const int a = 16 * kVStride * 2;
+  const int b = 16 * (rq + 4) * 2;
+  return round16((a > b ? a : b) + 32);
 }
 
-__global__ __launch_bounds__(kThreads) void k_attend(PoolArgs P, BatchArgs Bt, AttnArgs A) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__host__ __device__ inline int att_region_bytes(int rq) {
+  const int scratch = kAttWaves * att_scratch_bytes(rq);
+  const int red = kAttWaves * 16 * kRedStride * 4 + kAttWaves * 16 * rq * 4;  // O and W of 4 waves
+  return scratch > red ? scratch : red;
+}
+
+__host__ __device__ inline int att_lds_bytes(int rq) {
+  return 16 * rq * 4 + rq * kVStride * 2 + 2 * kAttWaves * 16 * 4 + att_region_bytes(rq);
+}
+
+struct ExState {
+  float m, l;
+  v4f O[8];
+};
+
+template <int NQ>
+__device__ __forceinline__ void rescale_state(ExState& st, v4f (&Wacc)[NQ], float alpha, int q4) {
+  float ae[4];
+  rows_of(alpha, q4, ae);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.O[n][e] *= ae[e];
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Wacc[n][e] *= ae[e];
+  }
+}
+
+// One 16-row tile of exact rows t0..t0+15 (rows >= n_ex masked).
+template <int NQ>
+__device__ __forceinline__ void exact_tile(const v8h (&kx)[4], const v8h (&vx)[4], int t0, int n_ex,
+                                           const v4h (&qf)[4][2], float scale, ExState& st, v4f (&Wacc)[NQ],
+                                           f16* Vt, int l16, int q4) {
+  v4f S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    S = mfma16(lo4(kx[s]), qf[s][0], S);
+    S = mfma16(hi4(kx[s]), qf[s][1], S);
+  }
+  float zz[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) zz[e] = (t0 + 4 * q4 + e < n_ex) ? S[e] * scale : -INFINITY;
+  float alpha, pe[4];
+  softmax_tile(zz, st.m, st.l, alpha, pe);
+  rescale_state<NQ>(st, Wacc, alpha, q4);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4) = lo4(vx[s]);
+    *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4 + 4) = hi4(vx[s]);
+  }
+  wave_sync_lds();
+  v4h ph, pl;
+  split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    v4h bv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bv[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
+    st.O[n] = mfma16(ph, bv, st.O[n]);
+    st.O[n] = mfma16(pl, bv, st.O[n]);
+  }
+  wave_sync_lds();
+}
+
+__device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, int tile, int ntile, int n_ex,
+                                                v8h (&kx)[4], v8h (&vx)[4], int l16, int q4) {
+  // rows past n_ex read row n_ex - 1: their scores are masked to -inf and their
+  // softmax weights are exactly 0, so the (finite) data never contributes
+  const int t = tile * 16 + l16;
+  const int tc = (tile < ntile && t < n_ex) ? t : n_ex - 1;  // n_ex >= 1 here
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kx[s] = ld8(kb + (int64_t)tc * kD + 32 * s + 8 * q4);
+    vx[s] = ld8(vb + (int64_t)tc * kD + 32 * s + 8 * q4);
+  }
+}
+
+// NRQ = number of 16-wide column tiles of the augmented rank r + 1 (0 without
+// low-rank rows), a template parameter so that every loop over them is static.
+template <int NRQ>
+__device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& Bt, const AttnArgs& A, int u, int p,
+                                            unsigned char* smem) {
+  constexpr int NQ = NRQ > 0 ? NRQ : 1;
+  constexpr int RQ = 16 * NRQ;
+  constexpr int kVVChunks = (16 * NQ * 16 + kAttThreads - 1) / kAttThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int item = blockIdx.x;
-  const int u = item / A.items_per_unit, p = item % A.items_per_unit;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
   const int G = Bt.G;
   const int row0 = b * Bt.Hq + h * G;
+
+  // ---- query fragments first (they depend on nothing else): lane holds
+  //      q[g = l16][32 s + 8 q4 + 4 hh + e]; lanes of padded heads g >= G load
+  //      head 0, whose results they never write
+  v4h qf[4][2];
+  {
+    const f16* qrow = Bt.q + (int64_t)(row0 + (l16 < G ? l16 : 0)) * kD + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const v8h x = ld8(qrow + 32 * s);
+      qf[s][0] = lo4(x);
+      qf[s][1] = hi4(x);
+    }
+  }
 
   // ---- what this part covers (uniform over the workgroup)
   bool lr = false;
@@ -356,13 +541,15 @@ __global__ __launch_bounds__(kThreads) void k_attend(PoolArgs P, BatchArgs Bt, A
   const f16* exv = nullptr;
   int slot = -1;
   if (p < A.n_block_parts) {
-    int nb = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
-    nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
-    const int j = A.idx[(int64_t)u * A.top_k + p];
-    if (j >= 0 && j < nb) {
-      const int s = Bt.table[(int64_t)b * Bt.mb + j];
-      if (s >= 0 && s < P.n_slots) slot = s;
+    if (A.slots) {
+      slot = ld_dev(&A.slots[(int64_t)u * A.top_k + p]);  // routed pool slot, or -1
+    } else {
+      int nb = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
+      nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
+      const int j = A.idx[(int64_t)u * A.top_k + p];
+      if (j >= 0 && j < nb) slot = Bt.table[(int64_t)b * Bt.mb + j];
     }
+    if (slot >= P.n_slots) slot = -1;
     if (slot >= 0) {
       lr = (A.block_mode & 1) != 0;
       if ((A.block_mode & 2) && P.n_resid > 0) {
@@ -387,364 +574,536 @@ __global__ __launch_bounds__(kThreads) void k_attend(PoolArgs P, BatchArgs Bt, A
 
   const int part = A.part_offset + p;
   if (!lr && n_ex == 0) {
-    for (int t = tid; t < G * kD; t += kThreads) {
+    for (int t = tid; t < G * kD; t += kAttThreads) {
       const int g = t / kD, d = t % kD;
-      A.part_o[((int64_t)(row0 + g) * A.n_parts + part) * kD + d] = 0.f;
+      st_dev(&A.part_o[((int64_t)(row0 + g) * A.n_parts + part) * kD + d], 0.f);
     }
-    if (tid < G) A.part_lse[(int64_t)(row0 + tid) * A.n_parts + part] = -INFINITY;
+    if (tid < G) st_dev(&A.part_lse[(int64_t)(row0 + tid) * A.n_parts + part], -INFINITY);
     return;
   }
 
   // ---- LDS carve-up
-  const int RQ = A.rq;
-  float* qt = reinterpret_cast<float*>(smem);                       // [16][RQ]
-  f16* vvx = reinterpret_cast<f16*>(qt + 16 * RQ);                  // [RQ][kVStride]
-  uint32_t* mask = reinterpret_cast<uint32_t*>(vvx + RQ * kVStride); // [8]
-  float* wstat = reinterpret_cast<float*>(mask + 8);                 // m [4][16], l [4][16]
-  unsigned char* wreg = reinterpret_cast<unsigned char*>(wstat + 2 * kWaves * 16);
-  const int WREG = wave_region_bytes(RQ);
-  unsigned char* my = wreg + wave * WREG;
-
-  // ---- query fragments: lane holds q[g = l16][32 s + 8 q4 + 4 hh + e]
-  v4h qf[4][2];
-  {
-    const bool ok = l16 < G;
-    const f16* qrow = Bt.q + (int64_t)(row0 + l16) * kD + 8 * q4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v8h x = ok ? ld8(qrow + 32 * s) : (v8h)(f16)0;
-      qf[s][0] = lo4(x);
-      qf[s][1] = hi4(x);
-    }
-  }
-
+  float* qt = reinterpret_cast<float*>(smem);                     // [16][RQ]  V_K q and q.a_k
+  f16* vvx = reinterpret_cast<f16*>(qt + 16 * RQ);                // [RQ][kVStride]  [V_V ; a_v ; *]
+  float* wstat = reinterpret_cast<float*>(vvx + RQ * kVStride);   // m [4][16], l [4][16]
+  unsigned char* region = reinterpret_cast<unsigned char*>(wstat + 2 * kAttWaves * 16);
+  constexpr int TS = RQ + 4;
+  unsigned char* my = region + wave * att_scratch_bytes(RQ);
+  uint32_t* wmask = reinterpret_cast<uint32_t*>(my + att_scratch_bytes(RQ) - 32);
+  const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
-  const int nrq = RQ / 16;
-  v4h qth[5], qtl[5];
+  const float scale = A.scale;
+
+  ExState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-  for (int s = 0; s < 5; ++s) { qth[s] = (v4h)(f16)0; qtl[s] = (v4h)(f16)0; }
+  for (int n = 0; n < 8; ++n) st.O[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v4f Wacc[NQ];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) Wacc[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // ---- issue the loads, in the order of use
+  v4h ua[kLRTilesPerWave][NQ];
+  int ps[4];
+  v8h vvl[kVVChunks];
+  v8h vkx[2][4];
   const f16* U = nullptr;
-  if (lr) {
+  if (NRQ > 0 && lr) {
     const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
     const f16* AV = P.av + slot * P.av_s + h * P.av_h;
     const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
     const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
     U = P.u + slot * P.u_s + h * P.u_h;
-    if (tid < 8) mask[tid] = 0u;
-    // VVx = [V_V ; a_v ; 0] staged in LDS
-    for (int c = tid; c < RQ * 16; c += kThreads) {
-      const int j = c >> 4, col = (c & 15) * 8;
-      v8h x = (v8h)(f16)0;
-      if (j < r) x = ld8(VV + (int64_t)j * kD + col);
-      else if (j == r) x = ld8(AV + col);
-      *reinterpret_cast<v4h*>(vvx + j * kVStride + col) = lo4(x);
-      *reinterpret_cast<v4h*>(vvx + j * kVStride + col + 4) = hi4(x);
-    }
-    // VKx q: rows j of [V_K ; a_k ; 0] against the G queries, C rows j, columns g
-    for (int jt = wave; jt < nrq; jt += kWaves) {
-      const int j = jt * 16 + l16;
-      const f16* src = (j < r) ? VK + (int64_t)j * kD : ((j == r) ? AK : nullptr);
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int nres = P.n_resid;
+      const uint8_t* pp = nres > 0 ? P.rp + slot * P.rp_s + h * P.rp_h : P.rp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8h x = src ? ld8(src + 32 * s + 8 * q4) : (v8h)(f16)0;
-        acc = mfma16(lo4(x), qf[s][0], acc);
-        acc = mfma16(hi4(x), qf[s][1], acc);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qt[l16 * RQ + jt * 16 + 4 * q4 + e] = acc[e];
-    }
-    __syncthreads();
-    const uint8_t* pos = P.rp + slot * P.rp_s + h * P.rp_h;
-    for (int t = tid; t < P.n_resid; t += kThreads) {
-      const int ps = pos[t];
-      if (ps >= 1 && ps <= kLowRankRows) atomicOr(&mask[ps >> 5], 1u << (ps & 31));
-    }
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      if (s < nrq) {
-        const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
-        split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
+      for (int k = 0; k < 4; ++k) {
+        const int t = lane + 64 * k;
+        ps[k] = (nres > 0) ? (int)pp[t < nres ? t : 0] : 0;
       }
     }
-    __syncthreads();
+    // VVx rows: V_V rows j < r, a_v at j = r.  Padding rows j > r read V_V row 0:
+    // their weight in (p^T Ux) is exactly 0 because Ux is zero there.
+#pragma unroll
+    for (int k = 0; k < kVVChunks; ++k) {
+      const int c = tid + kAttThreads * k;
+      const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
+      const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
+      vvl[k] = ld8(src + col);
+    }
+    // VKx rows: V_K rows j < r, a_k at j = r; padding rows read V_K row 0
+    // (they only meet zero columns of Ux)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = (wave + kAttWaves * k) * 16 + l16;
+      const f16* src = (j < r) ? VK + (int64_t)j * kD : ((j == r) ? AK : VK);
+      if (wave + kAttWaves * k < NRQ) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) vkx[k][s] = ld8(src + 32 * s + 8 * q4);
+      }
+    }
+    if ((r & 3) == 0) {
+#pragma unroll
+      for (int k = 0; k < kLRTilesPerWave; ++k) {
+        const int i = (wave + kAttWaves * k) * 16 + l16;  // position in the block; 0 = anchor
+        const f16* row = U + (int64_t)(i > 0 ? i - 1 : 0) * r;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+          const int j0 = 16 * s + 4 * q4;
+          ua[k][s] = *reinterpret_cast<const v4h*>(row + (j0 < r ? j0 : 0));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kLRTilesPerWave; ++k) {
+        const int i = (wave + kAttWaves * k) * 16 + l16;
+        const f16* row = U + (int64_t)(i > 0 ? i - 1 : 0) * r;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * s + 4 * q4 + e;
+            ua[k][s][e] = row[j < r ? j : 0];
+          }
+        }
+      }
+    }
+  }
+  v8h ka[4], va[4], kb[4], vb[4];
+  int ta = wave, tb = wave + kAttWaves;
+  if (n_ex > 0) {
+    load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
+    load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  v4f O[8];
-  v4f Wacc[5];
+  // ---- low-rank set-up: residual-position mask (per wave), VVx, VKx q
+  if (NRQ > 0 && lr) {
+    if (lane < 8) wmask[lane] = 0u;
+    wave_sync_lds();
 #pragma unroll
-  for (int n = 0; n < 8; ++n) O[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 4; ++k)
+      if (ps[k] >= 1 && ps[k] <= kLowRankRows) atomicOr(&wmask[ps[k] >> 5], 1u << (ps[k] & 31));
 #pragma unroll
-  for (int n = 0; n < 5; ++n) Wacc[n] = (v4f){0.f, 0.f, 0.f, 0.f};
-  const float scale = A.scale;
-
-  // ---- low-rank rows: 16 tiles of 16 positions (position 0 is the anchor)
-  if (lr) {
-    const bool uvec = (r & 3) == 0;
-    const int TS = RQ + 4;
-    f16* T = reinterpret_cast<f16*>(my);  // [16][RQ + 4] transpose buffer for Ux
-    for (int tile = wave; tile < 16; tile += kWaves) {
-      const int i0 = tile * 16;
-      const int i = i0 + l16;
-      v4h ua[5];
+    for (int k = 0; k < kVVChunks; ++k) {
+      const int c = tid + kAttThreads * k;
+      if (c < RQ * 16) {
+        const int j = c >> 4, col = (c & 15) * 8;
+        *reinterpret_cast<v4h*>(vvx + j * kVStride + col) = lo4(vvl[k]);
+        *reinterpret_cast<v4h*>(vvx + j * kVStride + col + 4) = hi4(vvl[k]);
+      }
+    }
 #pragma unroll
-      for (int s = 0; s < 5; ++s) {
-        v4h x = (v4h)(f16)0;
-        if (s < nrq) {
-          const int j0 = 16 * s + 4 * q4;
-          if (i > 0) {
-            const f16* row = U + (int64_t)(i - 1) * r;
-            if (uvec) {
-              if (j0 < r) x = *reinterpret_cast<const v4h*>(row + j0);
-            } else {
+    for (int k = 0; k < 2; ++k) {
+      const int jt = wave + kAttWaves * k;
+      if (jt < NRQ) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (j0 + e < r) x[e] = row[j0 + e];
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j0 + e == r) x[e] = (f16)1.0f;
+        for (int s = 0; s < 4; ++s) {
+          acc = mfma16(lo4(vkx[k][s]), qf[s][0], acc);
+          acc = mfma16(hi4(vkx[k][s]), qf[s][1], acc);
         }
-        ua[s] = x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qt[l16 * RQ + jt * 16 + 4 * q4 + e] = acc[e];
+      }
+    }
+    __syncthreads();  // V_K q and VVx complete (uniform: lr is uniform)
+
+    // ---- low-rank tiles: 16 positions each (position 0 is the anchor)
+    v4h qth[NQ], qtl[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
+      split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
+    }
+    f16* T = reinterpret_cast<f16*>(my);
+#pragma unroll
+    for (int k = 0; k < kLRTilesPerWave; ++k) {
+      const int i0 = (wave + kAttWaves * k) * 16;
+      const int i = i0 + l16;
+      // Ux = [U | 1 | 0]; the anchor row has U = 0
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * s + 4 * q4 + e;
+          ua[k][s][e] = (j == r) ? (f16)1.0f : ((i > 0 && j < r) ? ua[k][s][e] : (f16)0.0f);
+        }
       }
       v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 5; ++s) {
-        if (s < nrq) {
-          z = mfma16(ua[s], qth[s], z);
-          z = mfma16(ua[s], qtl[s], z);
-        }
+      for (int s = 0; s < NQ; ++s) {
+        z = mfma16(ua[k][s], qth[s], z);
+        z = mfma16(ua[k][s], qtl[s], z);
       }
       float zz[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = i0 + 4 * q4 + e;
-        const bool masked = ii > 0 && ((mask[ii >> 5] >> (ii & 31)) & 1u);
+        const bool masked = (ii > 0) & (((wmask[ii >> 5] >> (ii & 31)) & 1u) != 0u);
         zz[e] = masked ? -INFINITY : z[e] * scale;
       }
-      float alpha, pe[4], ae[4];
-      softmax_tile(zz, m_run, l_run, alpha, pe);
-      rows_of(alpha, q4, ae);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[n][e] *= ae[e];
-      }
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Wacc[n][e] *= ae[e];
-      }
+      float alpha, pe[4];
+      softmax_tile(zz, st.m, st.l, alpha, pe);
+      rescale_state<NQ>(st, Wacc, alpha, q4);
       v4h ph, pl;
       split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
 #pragma unroll
-      for (int s = 0; s < 5; ++s)
-        if (s < nrq) *reinterpret_cast<v4h*>(T + l16 * TS + 16 * s + 4 * q4) = ua[s];
+      for (int s = 0; s < NQ; ++s) *reinterpret_cast<v4h*>(T + l16 * TS + 16 * s + 4 * q4) = ua[k][s];
       wave_sync_lds();
 #pragma unroll
-      for (int n = 0; n < 5; ++n) {
-        if (n < nrq) {
-          v4h bu;
+      for (int n = 0; n < NQ; ++n) {
+        v4h bu;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bu[e] = T[(4 * q4 + e) * TS + 16 * n + l16];
-          Wacc[n] = mfma16(ph, bu, Wacc[n]);
-          Wacc[n] = mfma16(pl, bu, Wacc[n]);
-        }
+        for (int e = 0; e < 4; ++e) bu[e] = T[(4 * q4 + e) * TS + 16 * n + l16];
+        Wacc[n] = mfma16(ph, bu, Wacc[n]);
+        Wacc[n] = mfma16(pl, bu, Wacc[n]);
       }
       wave_sync_lds();
     }
   }
 
-  // ---- exact rows (residual rows of a block, or window rows): 16-row tiles
+  // ---- exact rows: two 16-row tiles in flight
   if (n_ex > 0) {
-    const int ntile = (n_ex + 15) / 16;
-    f16* Vt = reinterpret_cast<f16*>(my);  // [16][kVStride]
-    for (int tile = wave; tile < ntile; tile += kWaves) {
-      const int t0 = tile * 16;
-      const int t = t0 + l16;
-      const bool valid = t < n_ex;
-      v8h kx[4], vx[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        kx[s] = valid ? ld8(exk + (int64_t)t * kD + 32 * s + 8 * q4) : (v8h)(f16)0;
-        vx[s] = valid ? ld8(exv + (int64_t)t * kD + 32 * s + 8 * q4) : (v8h)(f16)0;
-      }
-      v4f S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        S = mfma16(lo4(kx[s]), qf[s][0], S);
-        S = mfma16(hi4(kx[s]), qf[s][1], S);
-      }
-      float zz[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) zz[e] = (t0 + 4 * q4 + e < n_ex) ? S[e] * scale : -INFINITY;
-      float alpha, pe[4], ae[4];
-      softmax_tile(zz, m_run, l_run, alpha, pe);
-      rows_of(alpha, q4, ae);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[n][e] *= ae[e];
-      }
-#pragma unroll
-      for (int n = 0; n < 5; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Wacc[n][e] *= ae[e];
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4) = lo4(vx[s]);
-        *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4 + 4) = hi4(vx[s]);
-      }
-      wave_sync_lds();
-      v4h ph, pl;
-      split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        v4h bv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
-        O[n] = mfma16(ph, bv, O[n]);
-        O[n] = mfma16(pl, bv, O[n]);
-      }
-      wave_sync_lds();
-    }
-  }
-
-  // ---- low-rank values: O += (p^T Ux) VVx, once per wave
-  if (lr) {
-    float* Wt = reinterpret_cast<float*>(my);  // [16][RQ]
-#pragma unroll
-    for (int n = 0; n < 5; ++n) {
-      if (n < nrq) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Wt[(4 * q4 + e) * RQ + 16 * n + l16] = Wacc[n][e];
-      }
-    }
-    wave_sync_lds();
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      if (s < nrq) {
-        const float4 w = *reinterpret_cast<const float4*>(Wt + l16 * RQ + 16 * s + 4 * q4);
-        v4h wh, wl;
-        split_hl(w.x, w.y, w.z, w.w, wh, wl);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          v4h bv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bv[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
-          O[n] = mfma16(wh, bv, O[n]);
-          O[n] = mfma16(wl, bv, O[n]);
-        }
+    f16* Vt = reinterpret_cast<f16*>(my);
+    while (ta < ntile) {
+      exact_tile<NQ>(ka, va, ta * 16, n_ex, qf, scale, st, Wacc, Vt, l16, q4);
+      ta += 2 * kAttWaves;
+      if (ta < ntile) load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
+      if (tb < ntile) {
+        exact_tile<NQ>(kb, vb, tb * 16, n_ex, qf, scale, st, Wacc, Vt, l16, q4);
+        tb += 2 * kAttWaves;
+        if (tb < ntile) load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
       }
     }
   }
 
-  // ---- combine the 4 waves: common max, rescale, fixed-order sum
+  // ---- final phase: common maximum, fixed-order reduction
   if (q4 == 0) {
-    wstat[wave * 16 + l16] = m_run;
-    wstat[kWaves * 16 + wave * 16 + l16] = l_run;
+    wstat[wave * 16 + l16] = st.m;
+    wstat[kAttWaves * 16 + wave * 16 + l16] = st.l;
   }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wstat[w * 16 + l16]);
+  for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, wstat[w * 16 + l16]);
   float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < kAttWaves; ++w) {
     const float mw = wstat[w * 16 + l16];
-    L += (mw == -INFINITY) ? 0.f : wstat[kWaves * 16 + w * 16 + l16] * __expf(mw - M);
+    L += (mw == -INFINITY) ? 0.f : wstat[kAttWaves * 16 + w * 16 + l16] * __expf(mw - M);
   }
+  float be[4];
+  rows_of((st.m == -INFINITY) ? 0.f : __expf(st.m - M), q4, be);
+  __syncthreads();  // per-wave scratch becomes the reduction buffer
+  float* redO = reinterpret_cast<float*>(region);              // [4][16][kRedStride]
+  float* redW = redO + kAttWaves * 16 * kRedStride;            // [4][16][RQ]
   {
-    const float beta = (m_run == -INFINITY) ? 0.f : __expf(m_run - M);
-    float be[4];
-    rows_of(beta, q4, be);
+    float* dst = redO + wave * 16 * kRedStride;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[n][e] *= be[e];
+      for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * kRedStride + 16 * n + l16] = st.O[n][e] * be[e];
     }
   }
-  __syncthreads();  // wave regions become the reduction buffer
-  float* red = reinterpret_cast<float*>(wreg);  // [2][16][128]
-  if (wave >= 2) {
-    float* dst = red + (wave - 2) * 16 * kD;
+  if (NRQ > 0 && lr) {
+    float* dst = redW + wave * 16 * RQ;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NRQ; ++n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * kD + 16 * n + l16] = O[n][e];
+      for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * RQ + 16 * n + l16] = Wacc[n][e] * be[e];
     }
   }
   __syncthreads();
-  if (wave < 2) {
-    const float* src = red + wave * 16 * kD;
+  v4h wh[NQ], wl[NQ];
+  if (NRQ > 0 && lr) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int s = 0; s < NRQ; ++s) {
+      float4 w = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[n][e] += src[(4 * q4 + e) * kD + 16 * n + l16];
+      for (int lw = 0; lw < kAttWaves; ++lw) {
+        const float4 x = *reinterpret_cast<const float4*>(redW + lw * 16 * RQ + l16 * RQ + 16 * s + 4 * q4);
+        w.x += x.x;
+        w.y += x.y;
+        w.z += x.z;
+        w.w += x.w;
+      }
+      split_hl(w.x, w.y, w.z, w.w, wh[s], wl[s]);
     }
   }
-  __syncthreads();
-  if (wave == 1) {
+  float Le[4];
+  rows_of(L, q4, Le);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+  for (int half = 0; half < 2; ++half) {
+    const int n = wave + kAttWaves * half;  // output columns 16 n .. 16 n + 15
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[(4 * q4 + e) * kD + 16 * n + l16] = O[n][e];
+    for (int w = 0; w < kAttWaves; ++w) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += redO[w * 16 * kRedStride + (4 * q4 + e) * kRedStride + 16 * n + l16];
     }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float Le[4];
-    rows_of(L, q4, Le);
+    if (NRQ > 0 && lr) {
+#pragma unroll
+      for (int s = 0; s < NRQ; ++s) {
+        v4h bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
+        acc = mfma16(wh[s], bv, acc);
+        acc = mfma16(wl[s], bv, acc);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int g = 4 * q4 + e;
-      if (g < G) {
-        float* dst = A.part_o + ((int64_t)(row0 + g) * A.n_parts + part) * kD;
+      if (g < G)
+        st_dev(&A.part_o[((int64_t)(row0 + g) * A.n_parts + part) * kD + 16 * n + l16],
+               (Le[e] > 0.f) ? acc[e] / Le[e] : 0.f);
+    }
+  }
+  if (wave == 0 && q4 == 0 && l16 < G)
+    st_dev(&A.part_lse[(int64_t)(row0 + l16) * A.n_parts + part], (L > 0.f) ? M + __logf(L) : -INFINITY);
+}
+
+template <int NRQ>
+__global__ __launch_bounds__(kAttThreads, 2) void k_attend(PoolArgs P, BatchArgs Bt, AttnArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int item = blockIdx.x;
+  attend_part<NRQ>(P, Bt, A, item / A.items_per_unit, item % A.items_per_unit, smem);
+}
+
+// ----------------------------------------------------------------------------
+// Log-sum-exp combine: one workgroup of 4 waves per query row; wave w takes
+// parts w, w + 4, ... (16 at a time, all loads in flight); fixed-order sums.
+// ----------------------------------------------------------------------------
+
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 16;
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, const float* part_lse,
+                                                        int n_parts, int n_rows, f16* out, float* out_lse) {
+  __shared__ float red[4][kD];
+  __shared__ float redS[4];
+  __shared__ float redM[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const float* L = part_lse + (int64_t)row * n_parts;
+  float M = -INFINITY;
+  for (int p = tid; p < n_parts; p += kMergeThreads) M = fmaxf(M, L[p]);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const float v = O[n][e] + red[g * kD + 16 * n + l16];
-          dst[16 * n + l16] = (Le[e] > 0.f) ? v / Le[e] : 0.f;
-        }
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) redM[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(redM[0], redM[1]), fmaxf(redM[2], redM[3]));
+  float ax = 0.f, ay = 0.f, S = 0.f;
+  if (M != -INFINITY) {
+    for (int p0 = wave; p0 < n_parts; p0 += 4 * kMergeUnroll) {
+      float lp[kMergeUnroll];
+      float2 o[kMergeUnroll];
+#pragma unroll
+      for (int k = 0; k < kMergeUnroll; ++k) {
+        const int p = p0 + 4 * k;
+        const bool in = p < n_parts;
+        const int pc = in ? p : 0;
+        const float l = L[pc];
+        const float2 v = *reinterpret_cast<const float2*>(part_o + ((int64_t)row * n_parts + pc) * kD + 2 * lane);
+        lp[k] = in ? l : -INFINITY;
+        o[k] = in ? v : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeUnroll; ++k) {
+        const float w = (lp[k] == -INFINITY) ? 0.f : __expf(lp[k] - M);
+        S += w;
+        ax += w * o[k].x;
+        ay += w * o[k].y;
       }
     }
-    if (q4 == 0 && l16 < G)
-      A.part_lse[(int64_t)(row0 + l16) * A.n_parts + part] = (L > 0.f) ? M + __logf(L) : -INFINITY;
+  }
+  red[wave][2 * lane] = ax;
+  red[wave][2 * lane + 1] = ay;
+  if (lane == 0) redS[wave] = S;
+  __syncthreads();
+  if (wave == 0) {
+    const float St = ((redS[0] + redS[1]) + redS[2]) + redS[3];
+    const float x = ((red[0][2 * lane] + red[1][2 * lane]) + red[2][2 * lane]) + red[3][2 * lane];
+    const float y = ((red[0][2 * lane + 1] + red[1][2 * lane + 1]) + red[2][2 * lane + 1]) + red[3][2 * lane + 1];
+    const bool any = St > 0.f;
+    f16* dst = out + (int64_t)row * kD + 2 * lane;
+    dst[0] = (f16)(any ? x / St : 0.f);
+    dst[1] = (f16)(any ? y / St : 0.f);
+    if (lane == 0) out_lse[row] = any ? M + __logf(St) : -INFINITY;
   }
 }
 
 // ----------------------------------------------------------------------------
-// Log-sum-exp combine: one wave per query row
+// Log-sum-exp combine of the G query rows of one (sequence, KV head) unit by
+// one workgroup: 8 rows at a time, 32 lanes per row, 4 columns per lane.
 // ----------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void k_merge(const float* part_o, const float* part_lse,
-                                                   int n_parts, int n_rows, f16* out, float* out_lse) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  const float* L = part_lse + (int64_t)row * n_parts;
-  float M = -INFINITY;
-  for (int p = lane; p < n_parts; p += 64) M = fmaxf(M, L[p]);
+__device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0,
+                                           int G, f16* out, float* out_lse) {
+  const int tid = threadIdx.x;
+  const int j = tid & 31;   // lane within the row's 32-lane group
+  const int grp = tid >> 5;
+  for (int g0 = 0; g0 < G; g0 += kAttThreads / 32) {
+    const int g = g0 + grp;
+    const bool valid = g < G;
+    const int row = row0 + (valid ? g : 0);
+    const float* L = part_lse + (int64_t)row * n_parts;
+    float M = -INFINITY;
+    for (int pb = 0; pb < n_parts; pb += 32) {
+      const int pp = pb + j;
+      const float l = L[pp < n_parts ? pp : 0];
+      M = fmaxf(M, pp < n_parts ? l : -INFINITY);
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float ax = 0.f, ay = 0.f, S = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p < n_parts; ++p) {
-      const float lp = L[p];
-      const float w = (lp == -INFINITY) ? 0.f : __expf(lp - M);
-      const float2 o = *reinterpret_cast<const float2*>(part_o + ((int64_t)row * n_parts + p) * kD + 2 * lane);
-      S += w;
-      ax += w * o.x;
-      ay += w * o.y;
+    for (int off = 16; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
+    float S = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != -INFINITY) {
+      for (int pb = 0; pb < n_parts; pb += 32) {
+        const int pp = pb + j;
+        const float l = L[pp < n_parts ? pp : 0];
+        const float w = (pp < n_parts && l != -INFINITY) ? __expf(l - M) : 0.f;
+        float ws = w;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
+        S += ws;
+        const int np = (n_parts - pb) < 32 ? (n_parts - pb) : 32;
+        for (int k0 = 0; k0 < np; k0 += 16) {
+          float wk[16];
+          float4 o[16];
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
+            const int k = k0 + kk;
+            const int kc = k < np ? k : 0;
+            wk[kk] = __shfl(w, kc, 32);
+            o[kk] = *reinterpret_cast<const float4*>(part_o + ((int64_t)row * n_parts + pb + kc) * kD + 4 * j);
+            wk[kk] = k < np ? wk[kk] : 0.f;
+          }
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) {
+            acc.x += wk[kk] * o[kk].x;
+            acc.y += wk[kk] * o[kk].y;
+            acc.z += wk[kk] * o[kk].z;
+            acc.w += wk[kk] * o[kk].w;
+          }
+        }
+      }
+    }
+    if (valid) {
+      const bool any = S > 0.f;
+      v4h h4;
+      h4[0] = (f16)(any ? acc.x / S : 0.f);
+      h4[1] = (f16)(any ? acc.y / S : 0.f);
+      h4[2] = (f16)(any ? acc.z / S : 0.f);
+      h4[3] = (f16)(any ? acc.w / S : 0.f);
+      *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * j) = h4;
+      if (j == 0) out_lse[row] = any ? M + __logf(S) : -INFINITY;
     }
   }
-  const bool any = S > 0.f;
-  f16* dst = out + (int64_t)row * kD + 2 * lane;
-  dst[0] = (f16)(any ? ax / S : 0.f);
-  dst[1] = (f16)(any ? ay / S : 0.f);
-  if (lane == 0) out_lse[row] = any ? M + __logf(S) : -INFINITY;
+}
+
+// ----------------------------------------------------------------------------
+// One decode step of one layer in a single launch.
+//
+// Work items, handed out in ticket order (an atomic counter, so an item is
+// only ever taken by a workgroup that is already running): first the routing
+// of every (sequence, KV head) unit, then per unit its routed blocks and its
+// window chunks.  A block item waits (bounded) until its unit's routing flag
+// is set; routing items precede it in ticket order and are held by running
+// workgroups, so the wait always ends.  The workgroup that completes a unit's
+// last part merges that unit's partials; the workgroup that finishes last
+// leaves the control words zeroed for the next launch.
+// ----------------------------------------------------------------------------
+
+struct DecodeArgs {
+  AttnArgs att;
+  int32_t* idx;          // [units][top_k] routed logical blocks
+  int32_t* slots;        // [units][top_k] routed pool slots
+  uint32_t* ctrl;        // [0] ticket, [1] finished workgroups, [2] sticky wait-timeout flag
+  uint32_t* route_flag;  // [units]
+  uint32_t* unit_done;   // [units]
+  f16* out;
+  float* out_lse;
+  int n_units;
+  int n_route;           // units routed in this launch (0 when top_k == 0)
+  int n_items;           // n_route + n_units * att.items_per_unit: the grid size
+};
+
+constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
+
+template <int NRQ>
+__global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ RouteShared<kAttWaves> rsh;
+  __shared__ uint32_t sh_ticket, sh_flag;
+  const int tid = threadIdx.x;
+  if (tid == 0) sh_ticket = atomicAdd(&D.ctrl[0], 1u);
+  __syncthreads();
+  const int t = (int)sh_ticket;
+  if (t < D.n_route) {
+    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
+    stores_done();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(&D.route_flag[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (t < D.n_items) {
+    const int it = t - D.n_route;
+    const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
+    bool ok = true;
+    if (p < D.att.n_block_parts) {
+      if (tid == 0) {
+        unsigned n = 0;
+        uint32_t f = __hip_atomic_load(&D.route_flag[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (f == 0u && n < kRouteWaitLimit) {
+          __builtin_amdgcn_s_sleep(2);
+          f = __hip_atomic_load(&D.route_flag[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ++n;
+        }
+        sh_flag = f;
+        if (f == 0u) atomicOr(&D.ctrl[2], 1u);
+      }
+      __syncthreads();
+      ok = sh_flag != 0u;  // the routed slots are then read with device-scope loads
+    }
+    if (ok) {
+      attend_part<NRQ>(P, Bt, D.att, u, p, smem);
+    } else {
+      const int b = u / Bt.Hkv, h = u % Bt.Hkv;
+      const int row0 = b * Bt.Hq + h * Bt.G;
+      for (int x = tid; x < Bt.G * kD; x += kAttThreads)
+        st_dev(&D.att.part_o[((int64_t)(row0 + x / kD) * D.att.n_parts + p) * kD + x % kD], 0.f);
+      if (tid < Bt.G) st_dev(&D.att.part_lse[(int64_t)(row0 + tid) * D.att.n_parts + p], -INFINITY);
+    }
+    // count this part once its partial is stored; the unit's last part merges
+    stores_done();
+    __syncthreads();
+    if (tid == 0) sh_flag = (atomicAdd(&D.unit_done[u], 1u) == (uint32_t)(D.att.items_per_unit - 1)) ? 1u : 0u;
+    __syncthreads();
+    if (sh_flag) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale cached copies of the partials
+      const int b = u / Bt.Hkv, h = u % Bt.Hkv;
+      merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse);
+    }
+  }
+  // the last workgroup to finish zeroes the control words for the next launch
+  __syncthreads();
+  if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (sh_flag) {
+    for (int i = tid; i < D.n_units; i += kAttThreads) {
+      D.route_flag[i] = 0u;
+      D.unit_done[i] = 0u;
+    }
+    if (tid == 0) {
+      D.ctrl[0] = 0u;
+      D.ctrl[1] = 0u;
+    }
+  }
+}
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 // ----------------------------------------------------------------------------
@@ -868,29 +1227,63 @@ int rq_of(int rank) { return ((rank + 1 + 15) / 16) * 16; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 dkv_status launch_route(const dkv_pool* P, const dkv_batch* B, int top_k, int32_t* idx, float* scores,
-                        hipStream_t st) {
+                        int32_t* slots, hipStream_t st) {
   const int units = B->batch * P->n_kv_heads;
   if (units == 0) return DKV_OK;
   const size_t shm = (size_t)(B->max_blocks > 0 ? B->max_blocks : 1) * sizeof(uint32_t);
   static bool attr_set = false;
-  if (shm > 48 * 1024 && !attr_set) {
-    hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) !=
+        hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_route_topk) failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_route_topk, dim3(units), dim3(kThreads), shm, st, make_pool_args(P),
-                     make_batch_args(P, B), top_k, idx, scores);
+  hipLaunchKernelGGL(k_route_topk, dim3(units), dim3(kRouteThreads), shm, st, make_pool_args(P),
+                     make_batch_args(P, B), top_k, idx, scores, slots);
   return launched("k_route_topk");
 }
 
-dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* idx, int top_k,
-                         int n_block_parts, int block_mode, int n_win_parts, int win_chunk, float scale,
-                         float* part_o, float* part_lse, int n_parts, int part_offset, hipStream_t st) {
+template <int NRQ>
+dkv_status launch_decode_nrq(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B, const DecodeArgs& D) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    // 160 KB of LDS per workgroup on gfx950, less this kernel's static shared memory
+    if (hipFuncSetAttribute((const void*)k_decode<NRQ>, hipFuncAttributeMaxDynamicSharedMemorySize, 158 * 1024) !=
+        hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_decode) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_decode<NRQ>, dim3((unsigned)D.n_items), dim3(kAttThreads), shm, st, make_pool_args(P),
+                     make_batch_args(P, B), D);
+  return launched("k_decode");
+}
+
+template <int NRQ>
+dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
+                             const AttnArgs& a) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_attend<NRQ>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+        hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_attend) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_attend<NRQ>, dim3((unsigned)items), dim3(kAttThreads), shm, st, make_pool_args(P),
+                     make_batch_args(P, B), a);
+  return launched("k_attend");
+}
+
+dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* idx, const int32_t* slots,
+                         int top_k, int n_block_parts, int block_mode, int n_win_parts, int win_chunk,
+                         float scale, float* part_o, float* part_lse, int n_parts, int part_offset,
+                         hipStream_t st) {
   const int per_unit = n_block_parts + n_win_parts;
   const int64_t items = (int64_t)B->batch * P->n_kv_heads * per_unit;
   if (items == 0) return DKV_OK;
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many attention parts (%lld)", (long long)items);
   AttnArgs a;
   a.idx = idx;
+  a.slots = slots;
   a.top_k = top_k;
   a.n_block_parts = n_block_parts;
   a.block_mode = block_mode;
@@ -903,22 +1296,57 @@ dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* i
   a.part_lse = part_lse;
   a.n_parts = n_parts;
   a.part_offset = part_offset;
-  const size_t shm = (size_t)attend_lds_bytes(a.rq);
-  hipLaunchKernelGGL(k_attend, dim3((unsigned)items), dim3(kThreads), shm, st, make_pool_args(P),
-                     make_batch_args(P, B), a);
-  return launched("k_attend");
+  const size_t shm = (size_t)att_lds_bytes(a.rq);
+  switch (a.rq / 16) {
+    case 0: return launch_attend_nrq<0>(items, shm, st, P, B, a);
+    case 1: return launch_attend_nrq<1>(items, shm, st, P, B, a);
+    case 2: return launch_attend_nrq<2>(items, shm, st, P, B, a);
+    case 3: return launch_attend_nrq<3>(items, shm, st, P, B, a);
+    case 4: return launch_attend_nrq<4>(items, shm, st, P, B, a);
+    case 5: return launch_attend_nrq<5>(items, shm, st, P, B, a);
+    default: return fail(DKV_ERR_UNSUPPORTED, "rank %d", P->rank);
+  }
 }
 
 dkv_status launch_merge(const float* part_o, const float* part_lse, int n_parts, int n_rows, void* out,
                         float* out_lse, hipStream_t st) {
   if (n_rows == 0) return DKV_OK;
-  const unsigned blocks = (unsigned)((n_rows + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(k_merge, dim3(blocks), dim3(kThreads), 0, st, part_o, part_lse, n_parts, n_rows,
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, st, part_o, part_lse, n_parts, n_rows,
                      (f16*)out, out_lse);
   return launched("k_merge");
 }
 
 int win_parts_of(int window) { return (window + kWinChunk - 1) / kWinChunk; }
+
+// dkv_decode gives every unit at least one window part, so that a unit with
+// neither routed blocks nor window rows still produces its (empty) output
+int decode_win_parts(int window) {
+  const int n = win_parts_of(window);
+  return n > 0 ? n : 1;
+}
+
+// Workspace of dkv_decode: a control area (ticket, counters, per-unit flags;
+// zero between calls), then routed indices and slots, then the partials.
+struct WsLayout {
+  size_t ctrl_bytes, route_flag, unit_done, idx, slots, part_lse, part_o, total;
+};
+
+WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
+  WsLayout w;
+  const size_t B = (size_t)batch->batch;
+  const size_t units = B * (size_t)pool->n_kv_heads;
+  const size_t n_parts = (size_t)top_k + (size_t)decode_win_parts(batch->window);
+  const size_t rows = B * (size_t)batch->n_q_heads;
+  w.route_flag = 256;
+  w.unit_done = w.route_flag + align256(units * 4);
+  w.ctrl_bytes = w.unit_done + align256(units * 4);
+  w.idx = w.ctrl_bytes;
+  w.slots = w.idx + align256(units * (size_t)top_k * 4);
+  w.part_lse = w.slots + align256(units * (size_t)top_k * 4);
+  w.part_o = w.part_lse + align256(rows * n_parts * 4);
+  w.total = w.part_o + align256(rows * n_parts * kD * 4);
+  return w;
+}
 
 }  // namespace
 
@@ -969,7 +1397,7 @@ dkv_status dkv_route_topk(const dkv_pool* pool, const dkv_batch* batch, int32_t 
   if (batch->batch == 0) return DKV_OK;
   if (!idx) return fail(DKV_ERR_INVALID_ARG, "idx is NULL");
   if (batch->max_blocks > 0 && (s = check_pool_arrays(pool, 4))) return s;
-  return launch_route(pool, batch, top_k, idx, scores, (hipStream_t)stream);
+  return launch_route(pool, batch, top_k, idx, scores, nullptr, (hipStream_t)stream);
 }
 
 dkv_status dkv_lowrank_attn(const dkv_pool* pool, const dkv_batch* batch, const int32_t* idx, int32_t top_k,
@@ -985,8 +1413,8 @@ dkv_status dkv_lowrank_attn(const dkv_pool* pool, const dkv_batch* batch, const 
   if (batch->batch == 0) return DKV_OK;
   if (!idx || !part_o || !part_lse) return fail(DKV_ERR_INVALID_ARG, "idx / part_o / part_lse is NULL");
   if ((s = check_pool_arrays(pool, 1))) return s;
-  return launch_attend(pool, batch, idx, top_k, top_k, 1, 0, kWinChunk, scale, part_o, part_lse, n_parts,
-                       part_offset, (hipStream_t)stream);
+  return launch_attend(pool, batch, idx, nullptr, top_k, top_k, 1, 0, kWinChunk, scale, part_o, part_lse,
+                       n_parts, part_offset, (hipStream_t)stream);
 }
 
 dkv_status dkv_exact_attn(const dkv_pool* pool, const dkv_batch* batch, const int32_t* idx, int32_t top_k,
@@ -1006,8 +1434,8 @@ dkv_status dkv_exact_attn(const dkv_pool* pool, const dkv_batch* batch, const in
   if (!part_o || !part_lse) return fail(DKV_ERR_INVALID_ARG, "part_o / part_lse is NULL");
   if (top_k > 0 && (s = check_pool_arrays(pool, 2))) return s;
   const int chunk = window_splits > 0 ? (batch->window + window_splits - 1) / window_splits : 1;
-  return launch_attend(pool, batch, idx, top_k, top_k, 2, window_splits, chunk > 0 ? chunk : 1, scale, part_o,
-                       part_lse, n_parts, part_offset, (hipStream_t)stream);
+  return launch_attend(pool, batch, idx, nullptr, top_k, top_k, 2, window_splits, chunk > 0 ? chunk : 1, scale,
+                       part_o, part_lse, n_parts, part_offset, (hipStream_t)stream);
 }
 
 dkv_status dkv_lse_merge(const float* part_o, const float* part_lse, int32_t n_parts, int32_t n_rows,
@@ -1026,15 +1454,30 @@ size_t dkv_decode_workspace_size(const dkv_pool* pool, const dkv_batch* batch, i
   if (!pool || !batch || top_k < 0 || batch->batch < 0 || batch->window < 0 || batch->n_q_heads < 1 ||
       pool->n_kv_heads < 1)
     return 0;
-  const size_t B = (size_t)batch->batch;
-  const size_t n_parts = (size_t)top_k + (size_t)win_parts_of(batch->window);
-  const size_t rows = B * (size_t)batch->n_q_heads;
-  return align256(B * pool->n_kv_heads * (size_t)top_k * sizeof(int32_t)) +
-         align256(rows * n_parts * sizeof(float)) + align256(rows * n_parts * kD * sizeof(float));
+  return decode_layout(pool, batch, top_k).total;
 }
 
-dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale, void* workspace,
-                      size_t workspace_bytes, void* out, float* out_lse, int32_t* out_idx, void* stream) {
+dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  dkv_status s;
+  if ((s = check_pool_shape(pool))) return s;
+  if (top_k < 0) return fail(DKV_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+  if ((s = check_batch(pool, batch, false, false))) return s;
+  const WsLayout w = decode_layout(pool, batch, top_k);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(DKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                w.total);
+  if (!al(workspace, 256)) return fail(DKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int words = (int)(w.ctrl_bytes / 4);
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)workspace, words);
+  return launched("k_zero_words");
+}
+
+static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
+                              void* workspace, size_t workspace_bytes, void* out, float* out_lse, int32_t* out_idx,
+                              void* const* events, void* stream) {
   g_err[0] = 0;
   dkv_status s;
   if ((s = check_pool_shape(pool))) return s;
@@ -1053,25 +1496,74 @@ dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_
   if (top_k > 0 && (s = check_pool_arrays(pool, 1 | 2 | 4))) return s;
 
   const hipStream_t st = (hipStream_t)stream;
-  const int n_win = win_parts_of(batch->window);
+  const WsLayout w = decode_layout(pool, batch, top_k);
+  const int n_win = decode_win_parts(batch->window);
   const int n_parts = top_k + n_win;
-  const size_t B = (size_t)batch->batch;
-  const size_t rows = B * (size_t)batch->n_q_heads;
+  const int units = batch->batch * pool->n_kv_heads;
   unsigned char* ws = (unsigned char*)workspace;
-  int32_t* idx = (int32_t*)ws;
-  float* part_lse = (float*)(ws + align256(B * pool->n_kv_heads * (size_t)top_k * sizeof(int32_t)));
-  float* part_o = (float*)((unsigned char*)part_lse + align256(rows * n_parts * sizeof(float)));
-  if (out_idx) idx = out_idx;
 
-  if (top_k > 0) {
-    if ((s = launch_route(pool, batch, top_k, idx, nullptr, st))) return s;
+  DecodeArgs D;
+  AttnArgs& a = D.att;
+  a.idx = nullptr;
+  a.slots = (int32_t*)(ws + w.slots);
+  a.top_k = top_k;
+  a.n_block_parts = top_k;
+  a.block_mode = 3;
+  a.n_win_parts = n_win;
+  a.win_chunk = kWinChunk;
+  a.items_per_unit = n_parts;
+  a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
+  a.scale = scale;
+  a.part_o = (float*)(ws + w.part_o);
+  a.part_lse = (float*)(ws + w.part_lse);
+  a.n_parts = n_parts;
+  a.part_offset = 0;
+  D.idx = out_idx ? out_idx : (int32_t*)(ws + w.idx);
+  D.slots = (int32_t*)(ws + w.slots);
+  D.ctrl = (uint32_t*)ws;
+  D.route_flag = (uint32_t*)(ws + w.route_flag);
+  D.unit_done = (uint32_t*)(ws + w.unit_done);
+  D.out = (f16*)out;
+  D.out_lse = out_lse;
+  D.n_units = units;
+  D.n_route = top_k > 0 ? units : 0;
+  const int64_t items = (int64_t)D.n_route + (int64_t)units * n_parts;
+  if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
+  D.n_items = (int)items;
+  size_t shm = (size_t)att_lds_bytes(a.rq);
+  const size_t route_shm = (size_t)(batch->max_blocks > 0 ? batch->max_blocks : 1) * 4;
+  if (top_k > 0 && route_shm > shm) shm = route_shm;
+
+  if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)
+    return fail(DKV_ERR_HIP, "hipEventRecord failed");
+  switch (a.rq / 16) {
+    case 0: s = launch_decode_nrq<0>(shm, st, pool, batch, D); break;
+    case 1: s = launch_decode_nrq<1>(shm, st, pool, batch, D); break;
+    case 2: s = launch_decode_nrq<2>(shm, st, pool, batch, D); break;
+    case 3: s = launch_decode_nrq<3>(shm, st, pool, batch, D); break;
+    case 4: s = launch_decode_nrq<4>(shm, st, pool, batch, D); break;
+    case 5: s = launch_decode_nrq<5>(shm, st, pool, batch, D); break;
+    default: return fail(DKV_ERR_UNSUPPORTED, "rank %d", pool->rank);
   }
-  if (n_parts > 0) {
-    if ((s = launch_attend(pool, batch, idx, top_k, top_k, 3, n_win, kWinChunk, scale, part_o, part_lse, n_parts,
-                           0, st)))
-      return s;
+  if (s) return s;
+  if (events && hipEventRecord((hipEvent_t)events[1], st) != hipSuccess)
+    return fail(DKV_ERR_HIP, "hipEventRecord failed");
+  return DKV_OK;
+}
+
+dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale, void* workspace,
+                      size_t workspace_bytes, void* out, float* out_lse, int32_t* out_idx, void* stream) {
+  return decode_impl(pool, batch, top_k, scale, workspace, workspace_bytes, out, out_lse, out_idx, nullptr, stream);
+}
+
+dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
+                               void* workspace, size_t workspace_bytes, void* out, float* out_lse, int32_t* out_idx,
+                               void* const* events, void* stream) {
+  if (!events || !events[0] || !events[1]) {
+    g_err[0] = 0;
+    return fail(DKV_ERR_INVALID_ARG, "events must hold two hipEvent_t handles");
   }
-  return launch_merge(part_o, part_lse, n_parts, (int)rows, out, out_lse, st);
+  return decode_impl(pool, batch, top_k, scale, workspace, workspace_bytes, out, out_lse, out_idx, events, stream);
 }
 
 }  // extern "C"

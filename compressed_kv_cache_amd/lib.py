@@ -28,7 +28,8 @@ DKV_ERR_HIP = 4
 
 EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route_keys",
             "dkv_route_topk", "dkv_lowrank_attn", "dkv_exact_attn", "dkv_lse_merge",
-            "dkv_decode_workspace_size", "dkv_decode")
+            "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
+            "dkv_decode_profiled")
 
 
 class DKVError(RuntimeError):
@@ -90,8 +91,13 @@ def load(path: str = LIB_PATH):
     lib.dkv_lse_merge.restype = i32
     lib.dkv_decode_workspace_size.argtypes = [P, Bp, i32]
     lib.dkv_decode_workspace_size.restype = ctypes.c_size_t
+    lib.dkv_decode_workspace_init.argtypes = [P, Bp, i32, vp, ctypes.c_size_t, vp]
+    lib.dkv_decode_workspace_init.restype = i32
     lib.dkv_decode.argtypes = [P, Bp, i32, f32, vp, ctypes.c_size_t, vp, vp, vp, vp]
     lib.dkv_decode.restype = i32
+    lib.dkv_decode_profiled.argtypes = [P, Bp, i32, f32, vp, ctypes.c_size_t, vp, vp, vp,
+                                        ctypes.POINTER(ctypes.c_void_p), vp]
+    lib.dkv_decode_profiled.restype = i32
     _lib = lib
     return lib
 
@@ -254,10 +260,14 @@ def decode_workspace_size(pool: Pool, batch: Batch, top_k: int) -> int:
     return int(load().dkv_decode_workspace_size(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k))
 
 
-def alloc_workspace(pool: Pool, batch: Batch, top_k: int):
+def alloc_workspace(pool: Pool, batch: Batch, top_k: int, stream=None):
+    """A decode workspace, zero-filled and prepared by dkv_decode_workspace_init."""
     import torch
     n = max(decode_workspace_size(pool, batch, top_k), 256)
-    return torch.empty((n,), dtype=torch.uint8, device=batch.tensors["q"].device)
+    ws = torch.zeros((n,), dtype=torch.uint8, device=batch.tensors["q"].device)
+    _check(load().dkv_decode_workspace_init(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, _ptr(ws), n,
+                                            _stream(stream)), "dkv_decode_workspace_init")
+    return ws
 
 
 def decode(pool: Pool, batch: Batch, top_k: int, scale: float, workspace=None, out=None,
@@ -278,3 +288,14 @@ def decode(pool: Pool, batch: Batch, top_k: int, scale: float, workspace=None, o
                           _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                           _ptr(out), _ptr(out_lse), _ptr(out_idx), _stream(stream)), "dkv_decode")
     return out, out_lse, out_idx
+
+
+def decode_profiled(pool: Pool, batch: Batch, top_k: int, scale: float, workspace, out, out_lse,
+                    events, out_idx=None, stream=None) -> None:
+    """dkv_decode plus two hipEvent_t records around its kernel (raw handles as ints)."""
+    lib = load()
+    arr = (ctypes.c_void_p * 2)(*events)
+    _check(lib.dkv_decode_profiled(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, scale,
+                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                   _ptr(out), _ptr(out_lse), _ptr(out_idx), arr, _stream(stream)),
+           "dkv_decode_profiled")

@@ -190,16 +190,42 @@ dkv_status dkv_lse_merge(const float* part_o, const float* part_lse, int32_t n_p
 /* Bytes of workspace dkv_decode needs for this pool, batch and top_k (>= 0). */
 size_t dkv_decode_workspace_size(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k);
 
-/* One fused decode step of one layer: routing, low-rank + residual attention of
- * every routed block, window attention and the LSE combine (the Zenodo abstract's
- * decode path).  top_k = 0 attends the window only.
+/* Prepare a dkv_decode workspace for first use: zeroes its control area (a few
+ * KB at its start) with a kernel on `stream` (no memset, so it may be captured
+ * in a graph).  Not needed for memory that is already zero-filled.  Every
+ * dkv_decode leaves the control area zeroed again, so a workspace is prepared
+ * once and may then be reused by any number of calls (one at a time). */
+dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step of one layer in a single kernel launch: routing, low-rank +
+ * residual attention of every routed block, window attention and the LSE
+ * combine (the Zenodo abstract's decode path).  top_k = 0 attends the window
+ * only.  Work is handed out in ticket order from a counter in the workspace:
+ * the routing of each (sequence, KV head) first, then its blocks (which wait
+ * for that routing) and window chunks; the workgroup completing a unit's last
+ * part merges it.
  *   workspace: device memory of >= dkv_decode_workspace_size() bytes, 256-byte
- *              aligned, owned by the caller, contents need not be initialised.
+ *              aligned, owned by the caller, whose control area is zero (fresh
+ *              zero-filled memory, dkv_decode_workspace_init, or a previous
+ *              dkv_decode with the same or a larger-or-equal shape).  Calls
+ *              that share a workspace must not overlap.  Word 2 of the
+ *              workspace (uint32 at byte 8) is a sticky flag set if a block
+ *              ever gave up waiting for its routing (never in a correct run).
  *   out:     fp16 [B][Hq][d] out;  out_lse: fp32 [B][Hq] out.
  *   out_idx: int32 [B][Hkv][top_k] out (the routed blocks), or NULL. */
 dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
                       void* workspace, size_t workspace_bytes, void* out, float* out_lse,
                       int32_t* out_idx, void* stream);
+
+/* dkv_decode with timing (the pages' DKV_PROFILE_CB knob, README "Key
+ * Environment Knobs": GPU-kernel latency profiling).  Identical results;
+ * additionally records the two caller-created hipEvent_t handles in `events`
+ * on `stream`, [0] right before and [1] right after the decode kernel. */
+dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k,
+                               float scale, void* workspace, size_t workspace_bytes, void* out,
+                               float* out_lse, int32_t* out_idx, void* const* events,
+                               void* stream);
 
 #ifdef __cplusplus
 }

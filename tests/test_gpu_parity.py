@@ -331,3 +331,60 @@ def test_decode_is_deterministic(lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_decode_graph_replays_match_eager(lib):
+    """A captured decode replays correctly several times, with eager work and
+    synchronisations between the replays (the workspace control words are
+    left zeroed by every launch)."""
+    wl = config(1)
+    pool, batch = upload(lib, wl)
+    ws = lib.alloc_workspace(pool, batch, wl.top_k)
+    out = torch.empty((1, 12, 128), dtype=torch.float16, device=DEV)
+    lse = torch.empty((1, 12), dtype=torch.float32, device=DEV)
+    idx = torch.empty((1, 2, wl.top_k), dtype=torch.int32, device=DEV)
+    lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws, out=out, out_lse=lse, out_idx=idx)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), idx.clone())
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws, out=out, out_lse=lse, out_idx=idx)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws, out=out, out_lse=lse, out_idx=idx)
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]) and torch.equal(idx, ref[2]), rep
+        # eager work between replays
+        lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws, out=out, out_lse=lse, out_idx=idx)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0])
+    assert int(ws[8:12].view(torch.int32).item()) == 0      # no routing wait ever timed out
+
+
+def test_decode_workspace_reused_across_shapes(lib):
+    """One workspace, sized for the larger call, serves calls of different shapes."""
+    big = config(1)
+    small = synth.make_workload("small", seed=17, batch=2, n_q_heads=6, n_kv_heads=2, window=40,
+                                n_blocks=[5, 3], ranks=[8], n_resid=10, top_k=4)
+    pb, bb = upload(lib, big)
+    ps, bs = upload(lib, small)
+    ws = lib.alloc_workspace(pb, bb, big.top_k)
+    for _ in range(2):
+        o1, l1, i1 = lib.decode(pb, bb, big.top_k, big.scale, workspace=ws)
+        o2, l2, i2 = lib.decode(ps, bs, small.top_k, small.scale, workspace=ws)
+        torch.cuda.synchronize()
+        r1, rl1, _ = oracle.decode(big.layers[0].pool(), big.layers[0].q, big.layers[0].win_k,
+                                   big.layers[0].win_v, big.block_table, big.n_blocks, big.win_len, 2,
+                                   big.top_k, big.scale, idx=i1.cpu().numpy().astype(np.int64))
+        r2, rl2, _ = oracle.decode(small.layers[0].pool(), small.layers[0].q, small.layers[0].win_k,
+                                   small.layers[0].win_v, small.block_table, small.n_blocks, small.win_len,
+                                   2, small.top_k, small.scale, idx=i2.cpu().numpy().astype(np.int64))
+        assert parity.check_outputs(o1.cpu().numpy(), l1.cpu().numpy(), r1, rl1).ok
+        assert parity.check_outputs(o2.cpu().numpy(), l2.cpu().numpy(), r2, rl2).ok

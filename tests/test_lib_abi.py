@@ -117,13 +117,28 @@ def test_empty_batch_is_a_no_op(clib):
 def test_workspace_size_formula(clib):
     def a256(x):
         return (x + 255) // 256 * 256
+    p = _pool()
+    for window in (0, 64, 300):
+        b = _batch(window=window)
+        for top_k in (0, 1, 16, 64):
+            n_parts = top_k + max(1, (window + 127) // 128)   # window parts of 128 rows, at least one
+            rows, units = 2 * 12, 2 * 2
+            ctrl = 256 + 2 * a256(units * 4)                   # ticket/counters + two per-unit words
+            want = ctrl + 2 * a256(units * top_k * 4) + a256(rows * n_parts * 4) \
+                + a256(rows * n_parts * 128 * 4)
+            assert clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) == want
+    assert clib.dkv_decode_workspace_size(None, ctypes.byref(_batch()), 4) == 0
+
+
+def test_workspace_init_validates(clib):
     p, b = _pool(), _batch()
-    for top_k in (0, 1, 16, 64):
-        n_parts = top_k + (64 + 127) // 128
-        rows = 2 * 12
-        want = a256(2 * 2 * top_k * 4) + a256(rows * n_parts * 4) + a256(rows * n_parts * 128 * 4)
-        assert clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) == want
-    assert clib.dkv_decode_workspace_size(None, ctypes.byref(b), 4) == 0
+    need = clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), 4)
+    assert clib.dkv_decode_workspace_init(ctypes.byref(p), ctypes.byref(b), 4, FAKE, need - 1, None) \
+        == L.DKV_ERR_WORKSPACE
+    assert clib.dkv_decode_workspace_init(ctypes.byref(p), ctypes.byref(b), 4, None, need, None) \
+        == L.DKV_ERR_WORKSPACE
+    assert clib.dkv_decode_workspace_init(ctypes.byref(p), ctypes.byref(b), -2, FAKE, need, None) \
+        == L.DKV_ERR_INVALID_ARG
 
 
 def test_other_entry_points_validate(clib):
