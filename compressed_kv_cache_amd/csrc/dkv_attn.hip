@@ -87,7 +87,6 @@ struct BatchArgs {
 
 struct AttnArgs {
   const int32_t* idx;
-  const int32_t* slots;  // [units][top_k] routed pool slots (-1: none), or NULL to look them up
   int top_k;           // row stride of idx
   int n_block_parts;   // parts per unit that are routed blocks (top_k or 0)
   int block_mode;      // bit 0: low-rank rows of a block, bit 1: its residual rows
@@ -270,11 +269,23 @@ struct RouteShared {
 };
 
 // Route one (sequence, KV head) unit u with a workgroup of NT threads.
-// keys: LDS scratch of at least max_blocks words.
+// lds: scratch of at least 2 * max_blocks words (ordered score keys, slots).
+//
+// All loads are issued before the first barrier: the G query rows, and for
+// the first NT blocks their pool slot and 512-byte routing key.  Up to 1024
+// blocks, the top-K selection is done by wave 0 alone with a bit-by-bit radix
+// select on wave ballots (no workgroup barriers); beyond that, by a 4-pass
+// 8-bit radix select of the whole workgroup.
+// Routed-slot words of the fused kernel hold pool slot + kSlotCode (1: no block),
+// so that 0, the state of zero-filled memory, means "routing not written yet".
+constexpr int32_t kSlotPending = 0;
+constexpr int32_t kSlotCode = 2;
+
 template <int NT>
 __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
-                                           float* scores, int32_t* slots_out, uint32_t* keys,
+                                           float* scores, int32_t* slots_out, uint32_t* lds,
                                            RouteShared<NT / 64>& sh) {
+  constexpr int NW = NT / 64;
   float* qbar = sh.qbar;
   uint32_t* hist = sh.hist;
   uint32_t* wsum = sh.wsum;
@@ -283,47 +294,128 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
   int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
   N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
   const int keff = top_k < N ? top_k : N;
+  uint32_t* keys = lds;
+  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + (Bt.mb > 0 ? Bt.mb : 1));
 
-  // GQA mean of the group's query heads (all G loads in flight, summed in head order)
+  // ---- issue: query rows, and slot + routing key of block j = tid
+  float qv[DKV_MAX_GROUP];
   if (tid < kD) {
-    float v[DKV_MAX_GROUP];
 #pragma unroll
     for (int g = 0; g < DKV_MAX_GROUP; ++g) {
       const int gc = g < Bt.G ? g : Bt.G - 1;
-      const float x = (float)Bt.q[((int64_t)b * Bt.Hq + h * Bt.G + gc) * kD + tid];
-      v[g] = (g < Bt.G) ? x : 0.f;
+      qv[g] = (float)Bt.q[((int64_t)b * Bt.Hq + h * Bt.G + gc) * kD + tid];
     }
+  }
+  float4 kv[kD / 4];
+  int slot0 = -1;
+  bool ok0 = false;
+  if (N > 0) {
+    const int jc = tid < N ? tid : N - 1;
+    const int sr = Bt.table[(int64_t)b * Bt.mb + jc];
+    ok0 = tid < N && sr >= 0 && sr < P.n_slots;
+    slot0 = ok0 ? sr : -1;
+    const float4* c = reinterpret_cast<const float4*>(P.key + (ok0 ? sr : 0) * P.key_s + h * P.key_h);
+#pragma unroll
+    for (int i = 0; i < kD / 4; ++i) kv[i] = c[i];
+  }
+  if (tid < kD) {
     float s = 0.f;
 #pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) s += v[g];
+    for (int g = 0; g < DKV_MAX_GROUP; ++g) s += (g < Bt.G) ? qv[g] : 0.f;
     qbar[tid] = s / (float)Bt.G;
   }
   __syncthreads();
 
-  // one thread per block: the whole 512-byte routing key is loaded at once
-  for (int j0 = 0; j0 < N; j0 += NT) {
-    const int j = j0 + tid;
-    const int jc = j < N ? j : N - 1;
-    const int slot_raw = Bt.table[(int64_t)b * Bt.mb + jc];
-    const bool ok = slot_raw >= 0 && slot_raw < P.n_slots;
-    const int slot = ok ? slot_raw : 0;
-    const float4* c = reinterpret_cast<const float4*>(P.key + slot * P.key_s + h * P.key_h);
-    float4 v[kD / 4];
-#pragma unroll
-    for (int i = 0; i < kD / 4; ++i) v[i] = c[i];
+  // ---- scores (GQA-mean query against each routing key), as ordered keys
+  if (N > 0) {
     const float4* qb = reinterpret_cast<const float4*>(qbar);
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < kD / 4; ++i) {
       const float4 qq = qb[i];
-      acc += v[i].x * qq.x + v[i].y * qq.y + v[i].z * qq.z + v[i].w * qq.w;
+      acc += kv[i].x * qq.x + kv[i].y * qq.y + kv[i].z * qq.z + kv[i].w * qq.w;
     }
-    if (j < N) keys[j] = ordered_key(ok ? acc : -INFINITY);
+    if (tid < N) {
+      keys[tid] = ordered_key(ok0 ? acc : -INFINITY);
+      slot_of[tid] = slot0;
+    }
+    for (int j0 = NT; j0 < N; j0 += NT) {
+      const int j = j0 + tid;
+      const int jc = j < N ? j : N - 1;
+      const int sr = Bt.table[(int64_t)b * Bt.mb + jc];
+      const bool ok = j < N && sr >= 0 && sr < P.n_slots;
+      const float4* c = reinterpret_cast<const float4*>(P.key + (ok ? sr : 0) * P.key_s + h * P.key_h);
+#pragma unroll
+      for (int i = 0; i < kD / 4; ++i) kv[i] = c[i];
+      float a2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < kD / 4; ++i) {
+        const float4 qq = qb[i];
+        a2 += kv[i].x * qq.x + kv[i].y * qq.y + kv[i].z * qq.z + kv[i].w * qq.w;
+      }
+      if (j < N) {
+        keys[j] = ordered_key(ok ? a2 : -INFINITY);
+        slot_of[j] = ok ? sr : -1;
+      }
+    }
   }
   __syncthreads();
 
-  if (keff > 0) {
-    // radix select of the keff-th largest key, 8 bits per pass
+  auto emit = [&](int pos, int j, uint32_t k) {
+    st_dev(&idx[(int64_t)u * top_k + pos], j);
+    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)slot_of[j] + kSlotCode);
+  };
+
+  if (keff > 0 && N <= 1024) {
+    // ---- wave 0: bit-by-bit radix select of the keff-th largest key
+    if (wave == 0) {
+      constexpr int kPer = 16;
+      const int per = (N + 63) >> 6;
+      uint32_t kk[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int j = lane + 64 * i;
+        kk[i] = (i < per && j < N) ? keys[j] : 0u;
+      }
+      uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)keff;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t bm = 1u << bit;
+        uint32_t cnt = 0u;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if (i < per) {
+            const int j = lane + 64 * i;
+            const bool c = (j < N) && ((kk[i] & mask) == prefix) && (kk[i] & bm);
+            cnt += (uint32_t)__popcll(__ballot(c));
+          }
+        }
+        if (cnt >= krem) prefix |= bm;
+        else krem -= cnt;
+        mask |= bm;
+      }
+      // keys above the threshold T = prefix, then the lowest-index keys equal to it,
+      // emitted in ascending block order
+      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+      uint32_t eq_base = 0u, sel_base = 0u;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (i < per) {
+          const int j = lane + 64 * i;
+          const bool in = j < N;
+          const bool eq = in && kk[i] == prefix;
+          const unsigned long long em = __ballot(eq);
+          const uint32_t er = eq_base + (uint32_t)__popcll(em & lt);
+          const bool sel = in && (kk[i] > prefix || (eq && er < krem));
+          const unsigned long long smk = __ballot(sel);
+          if (sel) emit((int)(sel_base + (uint32_t)__popcll(smk & lt)), j, kk[i]);
+          eq_base += (uint32_t)__popcll(em);
+          sel_base += (uint32_t)__popcll(smk);
+        }
+      }
+    }
+  } else if (keff > 0) {
+    // ---- whole workgroup: 4-pass 8-bit radix select
     uint32_t prefix = 0u, pmask = 0u;
     uint32_t krem = (uint32_t)keff;
     for (int pass = 0; pass < 4; ++pass) {
@@ -357,7 +449,6 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
       pmask |= 0xFFu << shift;
       krem -= sh.above;
     }
-    // keys above the threshold, then the lowest-index keys equal to it
     const uint32_t T = prefix;
     int eq_base = 0, sel_base = 0;
     for (int c0 = 0; c0 < N; c0 += NT) {
@@ -366,19 +457,11 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
       const uint32_t k = in ? keys[j] : 0u;
       const bool eq = in && k == T;
       int eq_rank, eq_tot;
-      block_count<(NT / 64)>(eq, eq_rank, eq_tot, wsum);
+      block_count<NW>(eq, eq_rank, eq_tot, wsum);
       const bool sel = in && (k > T || (eq && (uint32_t)(eq_base + eq_rank) < krem));
       int sel_rank, sel_tot;
-      block_count<(NT / 64)>(sel, sel_rank, sel_tot, wsum);
-      if (sel) {
-        const int pos = sel_base + sel_rank;
-        st_dev(&idx[(int64_t)u * top_k + pos], j);
-        if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
-        if (slots_out) {
-          const int sl = Bt.table[(int64_t)b * Bt.mb + j];
-          st_dev(&slots_out[(int64_t)u * top_k + pos], (sl >= 0 && sl < P.n_slots) ? sl : -1);
-        }
-      }
+      block_count<NW>(sel, sel_rank, sel_tot, wsum);
+      if (sel) emit(sel_base + sel_rank, j, k);
       eq_base += eq_tot;
       sel_base += sel_tot;
     }
@@ -386,15 +469,15 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
   for (int pos = keff + tid; pos < top_k; pos += NT) {
     st_dev(&idx[(int64_t)u * top_k + pos], -1);
     if (scores) st_dev(&scores[(int64_t)u * top_k + pos], -INFINITY);
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], -1);
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], -1 + kSlotCode);
   }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(PoolArgs P, BatchArgs Bt, int top_k,
                                                               int32_t* idx, float* scores, int32_t* slots_out) {
-  extern __shared__ uint32_t keys[];  // [mb] ordered score keys
+  extern __shared__ uint32_t route_lds[];  // [2][mb] ordered score keys, pool slots
   __shared__ RouteShared<kRouteThreads / 64> sh;
-  route_unit<kRouteThreads>(P, Bt, blockIdx.x, top_k, idx, scores, slots_out, keys, sh);
+  route_unit<kRouteThreads>(P, Bt, blockIdx.x, top_k, idx, scores, slots_out, route_lds, sh);
 }
 
 // ----------------------------------------------------------------------------
@@ -508,9 +591,11 @@ __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, in
 
 // NRQ = number of 16-wide column tiles of the augmented rank r + 1 (0 without
 // low-rank rows), a template parameter so that every loop over them is static.
+constexpr int kSlotLookup = -0x7fffffff;  // attend_part: look the slot up from idx and the block table
+
 template <int NRQ>
 __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& Bt, const AttnArgs& A, int u, int p,
-                                            unsigned char* smem) {
+                                            int slot_in, unsigned char* smem) {
   constexpr int NQ = NRQ > 0 ? NRQ : 1;
   constexpr int RQ = 16 * NRQ;
   constexpr int kVVChunks = (16 * NQ * 16 + kAttThreads - 1) / kAttThreads;
@@ -541,8 +626,8 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   const f16* exv = nullptr;
   int slot = -1;
   if (p < A.n_block_parts) {
-    if (A.slots) {
-      slot = ld_dev(&A.slots[(int64_t)u * A.top_k + p]);  // routed pool slot, or -1
+    if (slot_in != kSlotLookup) {
+      slot = slot_in;  // routed pool slot, or -1
     } else {
       int nb = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
       nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
@@ -869,7 +954,7 @@ template <int NRQ>
 __global__ __launch_bounds__(kAttThreads, 2) void k_attend(PoolArgs P, BatchArgs Bt, AttnArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int item = blockIdx.x;
-  attend_part<NRQ>(P, Bt, A, item / A.items_per_unit, item % A.items_per_unit, smem);
+  attend_part<NRQ>(P, Bt, A, item / A.items_per_unit, item % A.items_per_unit, kSlotLookup, smem);
 }
 
 // ----------------------------------------------------------------------------
@@ -942,54 +1027,53 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 
 __device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0,
                                            int G, f16* out, float* out_lse) {
+  constexpr int kChunk = 32;
   const int tid = threadIdx.x;
-  const int j = tid & 31;   // lane within the row's 32-lane group
+  const int j = tid & 31;   // lane within the row's 32-lane group: columns 4 j .. 4 j + 3
   const int grp = tid >> 5;
   for (int g0 = 0; g0 < G; g0 += kAttThreads / 32) {
     const int g = g0 + grp;
     const bool valid = g < G;
     const int row = row0 + (valid ? g : 0);
-    const float* L = part_lse + (int64_t)row * n_parts;
-    float M = -INFINITY;
-    for (int pb = 0; pb < n_parts; pb += 32) {
-      const int pp = pb + j;
-      const float l = L[pp < n_parts ? pp : 0];
-      M = fmaxf(M, pp < n_parts ? l : -INFINITY);
-    }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
-    float S = 0.f;
+    const float* Lrow = part_lse + (int64_t)row * n_parts;
+    const float* Orow = part_o + (int64_t)row * n_parts * kD + 4 * j;
+    float m = -INFINITY, S = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-      for (int pb = 0; pb < n_parts; pb += 32) {
-        const int pp = pb + j;
-        const float l = L[pp < n_parts ? pp : 0];
-        const float w = (pp < n_parts && l != -INFINITY) ? __expf(l - M) : 0.f;
-        float ws = w;
+    for (int pb = 0; pb < n_parts; pb += kChunk) {
+      // every load of the chunk first: its lse values (one per lane) and its partials
+      const int pl = pb + j;
+      const float lj = Lrow[pl < n_parts ? pl : 0];
+      float4 o[kChunk];
 #pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
-        S += ws;
-        const int np = (n_parts - pb) < 32 ? (n_parts - pb) : 32;
-        for (int k0 = 0; k0 < np; k0 += 16) {
-          float wk[16];
-          float4 o[16];
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) {
-            const int k = k0 + kk;
-            const int kc = k < np ? k : 0;
-            wk[kk] = __shfl(w, kc, 32);
-            o[kk] = *reinterpret_cast<const float4*>(part_o + ((int64_t)row * n_parts + pb + kc) * kD + 4 * j);
-            wk[kk] = k < np ? wk[kk] : 0.f;
-          }
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) {
-            acc.x += wk[kk] * o[kk].x;
-            acc.y += wk[kk] * o[kk].y;
-            acc.z += wk[kk] * o[kk].z;
-            acc.w += wk[kk] * o[kk].w;
-          }
-        }
+      for (int k = 0; k < kChunk; ++k) {
+        const int pk = pb + k < n_parts ? pb + k : 0;
+        o[k] = *reinterpret_cast<const float4*>(Orow + (int64_t)pk * kD);
       }
+      const float l = (pl < n_parts) ? lj : -INFINITY;
+      float cm = l;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 32));
+      const float mn = fmaxf(m, cm);
+      if (mn == -INFINITY) continue;   // uniform within the row group
+      const float alpha = (m == -INFINITY) ? 0.f : __expf(m - mn);
+      const float w = (l == -INFINITY) ? 0.f : __expf(l - mn);
+      float ws = w;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
+      S = S * alpha + ws;
+      acc.x *= alpha;
+      acc.y *= alpha;
+      acc.z *= alpha;
+      acc.w *= alpha;
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const float wk = (pb + k < n_parts) ? __shfl(w, k, 32) : 0.f;
+        acc.x += wk * o[k].x;
+        acc.y += wk * o[k].y;
+        acc.z += wk * o[k].z;
+        acc.w += wk * o[k].w;
+      }
+      m = mn;
     }
     if (valid) {
       const bool any = S > 0.f;
@@ -999,7 +1083,7 @@ __device__ __forceinline__ void merge_unit(const float* part_o, const float* par
       h4[2] = (f16)(any ? acc.z / S : 0.f);
       h4[3] = (f16)(any ? acc.w / S : 0.f);
       *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * j) = h4;
-      if (j == 0) out_lse[row] = any ? M + __logf(S) : -INFINITY;
+      if (j == 0) out_lse[row] = any ? m + __logf(S) : -INFINITY;
     }
   }
 }
@@ -1020,10 +1104,9 @@ __device__ __forceinline__ void merge_unit(const float* part_o, const float* par
 struct DecodeArgs {
   AttnArgs att;
   int32_t* idx;          // [units][top_k] routed logical blocks
-  int32_t* slots;        // [units][top_k] routed pool slots
+  int32_t* slots;        // [units][top_k] routed pool slots (-1: none); kSlotPending until routed
   uint32_t* ctrl;        // [0] ticket, [1] finished workgroups, [2] sticky wait-timeout flag
-  uint32_t* route_flag;  // [units]
-  uint32_t* unit_done;   // [units]
+  uint32_t* unit_done;   // [units] parts finished
   f16* out;
   float* out_lse;
   int n_units;
@@ -1038,43 +1121,38 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ RouteShared<kAttWaves> rsh;
   __shared__ uint32_t sh_ticket, sh_flag;
+  __shared__ int32_t sh_slot;
   const int tid = threadIdx.x;
   if (tid == 0) sh_ticket = atomicAdd(&D.ctrl[0], 1u);
   __syncthreads();
   const int t = (int)sh_ticket;
   if (t < D.n_route) {
     route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
-    stores_done();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&D.route_flag[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else if (t < D.n_items) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
-    bool ok = true;
+    int slot = kSlotLookup;
     if (p < D.att.n_block_parts) {
+      // wait (bounded) until the unit's routing has written this part's pool slot
       if (tid == 0) {
+        const int32_t* sp = &D.slots[(int64_t)u * D.att.top_k + p];
         unsigned n = 0;
-        uint32_t f = __hip_atomic_load(&D.route_flag[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        while (f == 0u && n < kRouteWaitLimit) {
-          __builtin_amdgcn_s_sleep(2);
-          f = __hip_atomic_load(&D.route_flag[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int32_t v = ld_dev(sp);
+        while (v == kSlotPending && n < kRouteWaitLimit) {
+          __builtin_amdgcn_s_sleep(1);
+          v = ld_dev(sp);
           ++n;
         }
-        sh_flag = f;
-        if (f == 0u) atomicOr(&D.ctrl[2], 1u);
+        if (v == kSlotPending) {
+          atomicOr(&D.ctrl[2], 1u);
+          v = -1 + kSlotCode;  // give up: an empty part
+        }
+        sh_slot = v - kSlotCode;
       }
       __syncthreads();
-      ok = sh_flag != 0u;  // the routed slots are then read with device-scope loads
+      slot = sh_slot;
     }
-    if (ok) {
-      attend_part<NRQ>(P, Bt, D.att, u, p, smem);
-    } else {
-      const int b = u / Bt.Hkv, h = u % Bt.Hkv;
-      const int row0 = b * Bt.Hq + h * Bt.G;
-      for (int x = tid; x < Bt.G * kD; x += kAttThreads)
-        st_dev(&D.att.part_o[((int64_t)(row0 + x / kD) * D.att.n_parts + p) * kD + x % kD], 0.f);
-      if (tid < Bt.G) st_dev(&D.att.part_lse[(int64_t)(row0 + tid) * D.att.n_parts + p], -INFINITY);
-    }
+    attend_part<NRQ>(P, Bt, D.att, u, p, slot, smem);
     // count this part once its partial is stored; the unit's last part merges
     stores_done();
     __syncthreads();
@@ -1091,10 +1169,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - 1)) ? 1u : 0u;
   __syncthreads();
   if (sh_flag) {
-    for (int i = tid; i < D.n_units; i += kAttThreads) {
-      D.route_flag[i] = 0u;
-      D.unit_done[i] = 0u;
-    }
+    for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
+    for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
     if (tid == 0) {
       D.ctrl[0] = 0u;
       D.ctrl[1] = 0u;
@@ -1224,16 +1300,19 @@ dkv_status launched(const char* what) {
 
 int rq_of(int rank) { return ((rank + 1 + 15) / 16) * 16; }
 
+// routing scratch: an ordered score key and a pool slot per logical block
+size_t route_lds_bytes(int max_blocks) { return (size_t)2 * (max_blocks > 0 ? max_blocks : 1) * sizeof(uint32_t); }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 dkv_status launch_route(const dkv_pool* P, const dkv_batch* B, int top_k, int32_t* idx, float* scores,
                         int32_t* slots, hipStream_t st) {
   const int units = B->batch * P->n_kv_heads;
   if (units == 0) return DKV_OK;
-  const size_t shm = (size_t)(B->max_blocks > 0 ? B->max_blocks : 1) * sizeof(uint32_t);
+  const size_t shm = route_lds_bytes(B->max_blocks);
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) !=
+    if (hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize, 152 * 1024) !=
         hipSuccess)
       return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_route_topk) failed");
     attr_set = true;
@@ -1283,7 +1362,6 @@ dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* i
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many attention parts (%lld)", (long long)items);
   AttnArgs a;
   a.idx = idx;
-  a.slots = slots;
   a.top_k = top_k;
   a.n_block_parts = n_block_parts;
   a.block_mode = block_mode;
@@ -1328,7 +1406,7 @@ int decode_win_parts(int window) {
 // Workspace of dkv_decode: a control area (ticket, counters, per-unit flags;
 // zero between calls), then routed indices and slots, then the partials.
 struct WsLayout {
-  size_t ctrl_bytes, route_flag, unit_done, idx, slots, part_lse, part_o, total;
+  size_t ctrl_bytes, unit_done, slots, idx, part_lse, part_o, total;
 };
 
 WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
@@ -1337,12 +1415,11 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) 
   const size_t units = B * (size_t)pool->n_kv_heads;
   const size_t n_parts = (size_t)top_k + (size_t)decode_win_parts(batch->window);
   const size_t rows = B * (size_t)batch->n_q_heads;
-  w.route_flag = 256;
-  w.unit_done = w.route_flag + align256(units * 4);
-  w.ctrl_bytes = w.unit_done + align256(units * 4);
+  w.unit_done = 256;
+  w.slots = w.unit_done + align256(units * 4);
+  w.ctrl_bytes = w.slots + align256(units * (size_t)top_k * 4);
   w.idx = w.ctrl_bytes;
-  w.slots = w.idx + align256(units * (size_t)top_k * 4);
-  w.part_lse = w.slots + align256(units * (size_t)top_k * 4);
+  w.part_lse = w.idx + align256(units * (size_t)top_k * 4);
   w.part_o = w.part_lse + align256(rows * n_parts * 4);
   w.total = w.part_o + align256(rows * n_parts * kD * 4);
   return w;
@@ -1505,7 +1582,6 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   DecodeArgs D;
   AttnArgs& a = D.att;
   a.idx = nullptr;
-  a.slots = (int32_t*)(ws + w.slots);
   a.top_k = top_k;
   a.n_block_parts = top_k;
   a.block_mode = 3;
@@ -1521,7 +1597,6 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   D.idx = out_idx ? out_idx : (int32_t*)(ws + w.idx);
   D.slots = (int32_t*)(ws + w.slots);
   D.ctrl = (uint32_t*)ws;
-  D.route_flag = (uint32_t*)(ws + w.route_flag);
   D.unit_done = (uint32_t*)(ws + w.unit_done);
   D.out = (f16*)out;
   D.out_lse = out_lse;
@@ -1531,7 +1606,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
   D.n_items = (int)items;
   size_t shm = (size_t)att_lds_bytes(a.rq);
-  const size_t route_shm = (size_t)(batch->max_blocks > 0 ? batch->max_blocks : 1) * 4;
+  const size_t route_shm = route_lds_bytes(batch->max_blocks);
   if (top_k > 0 && route_shm > shm) shm = route_shm;
 
   if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)

@@ -123,8 +123,8 @@ def test_workspace_size_formula(clib):
         for top_k in (0, 1, 16, 64):
             n_parts = top_k + max(1, (window + 127) // 128)   # window parts of 128 rows, at least one
             rows, units = 2 * 12, 2 * 2
-            ctrl = 256 + 2 * a256(units * 4)                   # ticket/counters + two per-unit words
-            want = ctrl + 2 * a256(units * top_k * 4) + a256(rows * n_parts * 4) \
+            ctrl = 256 + a256(units * 4) + a256(units * top_k * 4)  # counters, per-unit, routed slots
+            want = ctrl + a256(units * top_k * 4) + a256(rows * n_parts * 4) \
                 + a256(rows * n_parts * 128 * 4)
             assert clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) == want
     assert clib.dkv_decode_workspace_size(None, ctypes.byref(_batch()), 4) == 0
