@@ -194,6 +194,7 @@ def main() -> int:
         batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
                                      wl.win_len, device=dev)
         lib.route_keys(pool)                      # once per sealed block, not per query
+        lib.gather_route_keys(pool, batch)        # per-sequence key table: refreshed with the block table
         pools.append(pool)
         batches.append(batch)
         wss.append(lib.alloc_workspace(pool, batch, wl.top_k))
@@ -208,8 +209,13 @@ def main() -> int:
             log(f"uploaded {li + 1} layers ({time.perf_counter() - t0:.0f} s)")
     torch.cuda.synchronize()
     wl = meta
-    resident = sum(sum(t.numel() * t.element_size() for t in p.tensors.values()) for p in pools) + \
-        sum(sum(t.numel() * t.element_size() for t in b.tensors.values() if t is not None) for b in batches)
+    storages = {}
+    for holder in pools + batches:
+        for t in holder.tensors.values():
+            if t is not None:
+                st = t.untyped_storage()
+                storages[st.data_ptr()] = st.nbytes()
+    resident = sum(storages.values())
     log(f"resident cache {resident / 1e9:.2f} GB in {time.perf_counter() - t0:.0f} s")
 
     B, Hq, Hkv, K, R, W, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.top_k, wl.n_resid, wl.window, 252

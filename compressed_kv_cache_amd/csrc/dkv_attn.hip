@@ -83,6 +83,7 @@ struct BatchArgs {
   const f16* q;
   const f16* wk;
   const f16* wv;
+  const float* rkeys;  // [B][Hkv][mb][kD] per-sequence routing keys, or NULL
 };
 
 struct AttnArgs {
@@ -127,6 +128,17 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = 63 (no wait), expcnt = 7, lgkmcnt = 0
   asm volatile("" ::: "memory");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier for LDS hand-offs: each wave waits for its own LDS (and
+// scalar) operations, then all waves meet.  Unlike __syncthreads() it does not
+// drain the waves' outstanding global loads, so data requested before it keeps
+// streaming in while the workgroup moves on.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt = 0 only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ v8h ld8(const f16* p) { return *reinterpret_cast<const v8h*>(p); }
@@ -215,7 +227,7 @@ __device__ __forceinline__ void block_count(bool flag, int& excl, int& total, ui
   const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   const int in_wave = __popcll(m & lt);
   if (lane == 0) wsum[w] = (uint32_t)__popcll(m);
-  __syncthreads();
+  lds_barrier();
   int off = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
@@ -223,7 +235,7 @@ __device__ __forceinline__ void block_count(bool flag, int& excl, int& total, ui
     off += (i < w) ? c : 0;
     tot += c;
   }
-  __syncthreads();
+  lds_barrier();
   excl = off + in_wave;
   total = tot;
 }
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(128) void k_route_keys(PoolArgs P, const int32_t* s
     for (int i = 0; i < kLowRankRows; ++i) s += (float)U[(int64_t)i * r + t];
     ubar[t] = s / (float)kLowRankRows;
   }
-  __syncthreads();
+  lds_barrier();
   const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
   const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
   float c = 0.f;
@@ -254,112 +266,189 @@ __global__ __launch_bounds__(128) void k_route_keys(PoolArgs P, const int32_t* s
   P.key[slot * P.key_s + h * P.key_h + t] = (float)AK[t] + c;
 }
 
+// Per-sequence routing-key table: one thread per 16 bytes of out.
+__global__ void k_gather_route_keys(PoolArgs P, BatchArgs Bt, float* out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)Bt.B * Bt.Hkv * Bt.mb * (kD / 4);
+  if (t >= n) return;
+  const int c4 = (int)(t % (kD / 4));
+  const int64_t row = t / (kD / 4);  // (b, h, j)
+  const int j = (int)(row % Bt.mb);
+  const int h = (int)((row / Bt.mb) % Bt.Hkv);
+  const int b = (int)(row / ((int64_t)Bt.mb * Bt.Hkv));
+  int nb = Bt.nblk[b];
+  nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j < nb) {
+    const int sr = Bt.table[(int64_t)b * Bt.mb + j];
+    if (sr >= 0 && sr < P.n_slots) v = *reinterpret_cast<const float4*>(P.key + sr * P.key_s + h * P.key_h + 4 * c4);
+  }
+  *reinterpret_cast<float4*>(out + row * kD + 4 * c4) = v;
+}
+
 // ----------------------------------------------------------------------------
-// Top-K routing: one workgroup of 8 waves per (sequence, KV head)
+// Wave-wide reductions and scans with DPP lane moves (no LDS round trips)
 // ----------------------------------------------------------------------------
 
-constexpr int kRouteThreads = 512;
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// max (MAX = true) or min over the 64 lanes, returned to every lane
+template <bool MAX>
+__device__ __forceinline__ float wave_minmax(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  uint32_t u = __float_as_uint(v);
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0xB1>(u, u))));   // quad_perm 1,0,3,2
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x4E>(u, u))));   // quad_perm 2,3,0,1
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x141>(u, u))));  // row_half_mirror
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x140>(u, u))));  // row_mirror
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x142, 0xa>(u, u))));  // row_bcast:15
+  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x143, 0xc>(u, u))));  // row_bcast:31
+  return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
+}
+
+// inclusive prefix sum over the 64 lanes in lane order
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  uint32_t s = v + dpp_u32<0x111>(0u, v);  // row_shr:1
+  s += dpp_u32<0x112>(0u, v);              // row_shr:2
+  s += dpp_u32<0x113>(0u, v);              // row_shr:3
+  s += dpp_u32<0x114, 0xf, 0xe>(0u, s);    // row_shr:4 into lanes 4..15 of each row
+  s += dpp_u32<0x118, 0xf, 0xc>(0u, s);    // row_shr:8 into lanes 8..15
+  s += dpp_u32<0x142, 0xa>(0u, s);         // row_bcast:15 into rows 1 and 3
+  s += dpp_u32<0x143, 0xc>(0u, s);         // row_bcast:31 into rows 2 and 3
+  return s;
+}
+
+// ----------------------------------------------------------------------------
+// Top-K routing: one workgroup of 4 waves per (sequence, KV head)
+// ----------------------------------------------------------------------------
+
+constexpr int kRouteThreads = 256;
+constexpr int kRedRow = 36;          // floats per row of the per-wave transpose area (conflict-free float4 reads)
 
 template <int NW>
 struct RouteShared {
-  float qbar[kD] __attribute__((aligned(16)));
   uint32_t hist[256];
   uint32_t wsum[NW];
+  float wlo[NW], whi[NW];
   uint32_t digit, above;
 };
 
-// Route one (sequence, KV head) unit u with a workgroup of NT threads.
-// lds: scratch of at least 2 * max_blocks words (ordered score keys, slots).
-//
-// All loads are issued before the first barrier: the G query rows, and for
-// the first NT blocks their pool slot and 512-byte routing key.  Up to 1024
-// blocks, the top-K selection is done by wave 0 alone with a bit-by-bit radix
-// select on wave ballots (no workgroup barriers); beyond that, by a 4-pass
-// 8-bit radix select of the whole workgroup.
+// LDS words route_unit needs for max_blocks blocks and NW waves.
+__host__ __device__ constexpr size_t route_lds_words(int max_blocks, int nw) {
+  return (size_t)2 * (size_t)(((max_blocks > 0 ? max_blocks : 1) + 3) & ~3) + (size_t)nw * 64 * kRedRow;
+}
+
 // Routed-slot words of the fused kernel hold pool slot + kSlotCode (1: no block),
 // so that 0, the state of zero-filled memory, means "routing not written yet".
 constexpr int32_t kSlotPending = 0;
 constexpr int32_t kSlotCode = 2;
 
+// Route one (sequence, KV head) unit u with a workgroup of NT threads.
+// lds: route_lds_words(max_blocks, NT / 64) words: ordered score keys [mb],
+// pool slots [mb] (both rounded up to 4), then a 64 x kRedRow float area per wave.
+//
+// Scores: lane l of a wave holds columns 4 (l % 32) .. +3 of the GQA-mean query;
+// a 512-byte routing key is read by 32 lanes, 16 bytes each, two keys per load
+// instruction (fully coalesced), and the 32 lane partials of a key are summed
+// through LDS.  Selection: block j is routed iff fewer than K blocks beat it
+// (a larger score, or an equal score at a smaller index: the lowest-index-first
+// tie rule), found with a 256-bin histogram of the scores and an exact ranking
+// inside the boundary bin only.  Routed blocks are emitted in ascending block
+// order.
 template <int NT>
 __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
                                            float* scores, int32_t* slots_out, uint32_t* lds,
                                            RouteShared<NT / 64>& sh) {
   constexpr int NW = NT / 64;
-  float* qbar = sh.qbar;
-  uint32_t* hist = sh.hist;
+  static_assert(NT == 256, "route_unit: one histogram bin per thread");
   uint32_t* wsum = sh.wsum;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
   int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
   N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
   const int keff = top_k < N ? top_k : N;
+  const int mbp = ((Bt.mb > 0 ? Bt.mb : 1) + 3) & ~3;
   uint32_t* keys = lds;
-  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + (Bt.mb > 0 ? Bt.mb : 1));
+  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + mbp);
+  float* red = reinterpret_cast<float*>(lds + 2 * mbp) + wave * 64 * kRedRow;
 
-  // ---- issue: query rows, and slot + routing key of block j = tid
-  float qv[DKV_MAX_GROUP];
-  if (tid < kD) {
+  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
+  const int c4 = lane & 31, half = lane >> 5;
+  float4 qb = make_float4(0.f, 0.f, 0.f, 0.f);
+  {
+    const f16* q0 = Bt.q + ((int64_t)b * Bt.Hq + h * Bt.G) * kD + 4 * c4;
+    v4h qh[DKV_MAX_GROUP];
+#pragma unroll
+    for (int g = 0; g < DKV_MAX_GROUP; ++g) qh[g] = *reinterpret_cast<const v4h*>(q0 + (g < Bt.G ? g : Bt.G - 1) * kD);
 #pragma unroll
     for (int g = 0; g < DKV_MAX_GROUP; ++g) {
-      const int gc = g < Bt.G ? g : Bt.G - 1;
-      qv[g] = (float)Bt.q[((int64_t)b * Bt.Hq + h * Bt.G + gc) * kD + tid];
+      if (g < Bt.G) {
+        qb.x += (float)qh[g][0];
+        qb.y += (float)qh[g][1];
+        qb.z += (float)qh[g][2];
+        qb.w += (float)qh[g][3];
+      }
     }
+    const float inv = 1.f / (float)Bt.G;
+    qb.x *= inv;
+    qb.y *= inv;
+    qb.z *= inv;
+    qb.w *= inv;
   }
-  float4 kv[kD / 4];
-  int slot0 = -1;
-  bool ok0 = false;
-  if (N > 0) {
-    const int jc = tid < N ? tid : N - 1;
-    const int sr = Bt.table[(int64_t)b * Bt.mb + jc];
-    ok0 = tid < N && sr >= 0 && sr < P.n_slots;
-    slot0 = ok0 ? sr : -1;
-    const float4* c = reinterpret_cast<const float4*>(P.key + (ok0 ? sr : 0) * P.key_s + h * P.key_h);
-#pragma unroll
-    for (int i = 0; i < kD / 4; ++i) kv[i] = c[i];
-  }
-  if (tid < kD) {
-    float s = 0.f;
-#pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) s += (g < Bt.G) ? qv[g] : 0.f;
-    qbar[tid] = s / (float)Bt.G;
-  }
-  __syncthreads();
 
-  // ---- scores (GQA-mean query against each routing key), as ordered keys
-  if (N > 0) {
-    const float4* qb = reinterpret_cast<const float4*>(qbar);
+  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
+  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
+  const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
+  float4 kv[32];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      int r = g0 + 2 * i + half;
+      r = r < N ? r : N - 1;
+      const float* src;
+      if (seq_keys) {
+        src = seq_keys + (int64_t)r * kD;
+      } else {
+        const int sr = slot_of[r];
+        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
+      }
+      kv[i] = *reinterpret_cast<const float4*>(src);
+    }
+  };
+  // with per-sequence keys the first group does not wait for the block table
+  if (seq_keys && wave * 64 < N) load_group(wave * 64);
+
+  // ---- pool slots of the unit's blocks (coalesced block-table reads)
+  for (int j = tid; j < N; j += NT) {
+    const int sr = Bt.table[(int64_t)b * Bt.mb + j];
+    slot_of[j] = (sr >= 0 && sr < P.n_slots) ? sr : -1;
+  }
+  lds_barrier();
+
+  // ---- scores of 64-block groups, one group per wave at a time
+  for (int g0 = wave * 64; g0 < N; g0 += NT) {
+    if (!seq_keys || g0 != wave * 64) load_group(g0);
+    float part[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) part[i] = (kv[i].x * qb.x + kv[i].y * qb.y) + (kv[i].z * qb.z + kv[i].w * qb.w);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) red[(2 * i + half) * kRedRow + c4] = part[i];
+    wave_sync_lds();
+    const float4* rr = reinterpret_cast<const float4*>(red + lane * kRedRow);
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kD / 4; ++i) {
-      const float4 qq = qb[i];
-      acc += kv[i].x * qq.x + kv[i].y * qq.y + kv[i].z * qq.z + kv[i].w * qq.w;
+    for (int m = 0; m < 8; ++m) {
+      const float4 v = rr[m];
+      acc += (v.x + v.y) + (v.z + v.w);
     }
-    if (tid < N) {
-      keys[tid] = ordered_key(ok0 ? acc : -INFINITY);
-      slot_of[tid] = slot0;
-    }
-    for (int j0 = NT; j0 < N; j0 += NT) {
-      const int j = j0 + tid;
-      const int jc = j < N ? j : N - 1;
-      const int sr = Bt.table[(int64_t)b * Bt.mb + jc];
-      const bool ok = j < N && sr >= 0 && sr < P.n_slots;
-      const float4* c = reinterpret_cast<const float4*>(P.key + (ok ? sr : 0) * P.key_s + h * P.key_h);
-#pragma unroll
-      for (int i = 0; i < kD / 4; ++i) kv[i] = c[i];
-      float a2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < kD / 4; ++i) {
-        const float4 qq = qb[i];
-        a2 += kv[i].x * qq.x + kv[i].y * qq.y + kv[i].z * qq.z + kv[i].w * qq.w;
-      }
-      if (j < N) {
-        keys[j] = ordered_key(ok ? a2 : -INFINITY);
-        slot_of[j] = ok ? sr : -1;
-      }
-    }
+    const int j = g0 + lane;
+    if (j < N) keys[j] = ordered_key(slot_of[j] >= 0 ? acc : -INFINITY);
+    wave_sync_lds();  // the next group reuses the transpose area
   }
-  __syncthreads();
+  lds_barrier();
 
   auto emit = [&](int pos, int j, uint32_t k) {
     st_dev(&idx[(int64_t)u * top_k + pos], j);
@@ -367,102 +456,108 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
     if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)slot_of[j] + kSlotCode);
   };
 
-  if (keff > 0 && N <= 1024) {
-    // ---- wave 0: bit-by-bit radix select of the keff-th largest key
-    if (wave == 0) {
-      constexpr int kPer = 16;
-      const int per = (N + 63) >> 6;
-      uint32_t kk[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int j = lane + 64 * i;
-        kk[i] = (i < per && j < N) ? keys[j] : 0u;
+  if (keff > 0) {
+    // ---- histogram select.  Finite scores are binned linearly between their
+    // minimum and maximum into bins 1..255 (-inf and below into bin 0); the
+    // bin map is monotone, so every block in a bin above the boundary bin b* is
+    // routed and none below it.  Inside b* the blocks are ranked exactly by
+    // (score, lower index first) against the other members of b*.
+    uint32_t* hist = sh.hist;
+    constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // ordered key of -inf
+    float lo = INFINITY, hi = -INFINITY;
+    for (int jj = tid; jj < N; jj += NT) {
+      const float sc = from_ordered(keys[jj]);
+      if (isfinite(sc)) {
+        lo = fminf(lo, sc);
+        hi = fmaxf(hi, sc);
       }
-      uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)keff;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t bm = 1u << bit;
-        uint32_t cnt = 0u;
+    }
+    hist[tid] = 0u;  // NT == 256 bins
+    lo = wave_minmax<false>(lo);
+    hi = wave_minmax<true>(hi);
+    if (lane == 0) {
+      sh.wlo[wave] = lo;
+      sh.whi[wave] = hi;
+    }
+    lds_barrier();
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          if (i < per) {
-            const int j = lane + 64 * i;
-            const bool c = (j < N) && ((kk[i] & mask) == prefix) && (kk[i] & bm);
-            cnt += (uint32_t)__popcll(__ballot(c));
+    for (int w = 0; w < NW; ++w) {
+      lo = fminf(lo, sh.wlo[w]);
+      hi = fmaxf(hi, sh.whi[w]);
+    }
+    const float inv = (hi > lo) ? 254.99f / (hi - lo) : 0.f;
+    auto bin_of = [&](uint32_t k) -> uint32_t {
+      if (k <= kNegInfKey) return 0u;
+      const float sc = from_ordered(k);
+      if (!(sc <= INFINITY)) return 255u;  // +NaN keys order above +inf
+      const float t = (sc - lo) * inv;
+      return 1u + (uint32_t)fminf(fmaxf(t, 0.f), 254.f);
+    };
+    if (tid == 0) {
+      sh.digit = 0u;
+      sh.above = 0u;
+    }
+    for (int jj = tid; jj < N; jj += NT) atomicAdd(&hist[bin_of(keys[jj])], 1u);
+    lds_barrier();
+    // counts of bins >= 255 - tid (a scan of the bins in descending order)
+    const uint32_t hb = hist[255 - tid];
+    uint32_t incl = wave_incl_scan(hb);
+    if (lane == 63) wsum[wave] = incl;
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) incl += (w < wave) ? wsum[w] : 0u;
+    const uint32_t excl = incl - hb;
+    if (excl < (uint32_t)keff && incl >= (uint32_t)keff) {
+      sh.digit = 255u - (uint32_t)tid;
+      sh.above = excl;
+    }
+    lds_barrier();
+    const uint32_t bstar = sh.digit & 255u, need = (uint32_t)keff - sh.above, m = hist[bstar];
+    // members of b* that are routed: all of them, or the `need` best by rank
+    uint64_t* cand = reinterpret_cast<uint64_t*>(lds + 2 * mbp);  // the score transpose area, now free
+    const uint32_t cap = (uint32_t)(NW * 64 * kRedRow / 2 - 2);
+    uint32_t* n_cand = reinterpret_cast<uint32_t*>(cand + cap);
+    const bool rank_members = m > need;
+    const bool listed = m <= cap;
+    if (rank_members && listed) {
+      if (tid == 0) *n_cand = 0u;
+      lds_barrier();
+      for (int jj = tid; jj < N; jj += NT) {
+        const uint32_t k = keys[jj];
+        if (bin_of(k) == bstar) cand[atomicAdd(n_cand, 1u)] = ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)jj);
+      }
+      lds_barrier();
+    }
+    int sel_base = 0;
+    for (int b0 = 0; b0 < N; b0 += NT) {
+      const int jj = b0 + tid;
+      bool sel = false;
+      uint32_t kj = 0u;
+      if (jj < N) {
+        kj = keys[jj];
+        const uint32_t bj = bin_of(kj);
+        sel = bj > bstar;
+        if (bj == bstar) {
+          if (!rank_members) {
+            sel = true;
+          } else {
+            const uint64_t cj = ((uint64_t)kj << 32) | (uint64_t)(~(uint32_t)jj);
+            uint32_t beat = 0u;
+            if (listed) {
+              for (uint32_t t2 = 0; t2 < m; ++t2) beat += (uint32_t)(cand[t2] > cj);
+            } else {
+              for (int t2 = 0; t2 < N; ++t2) {
+                const uint32_t k2 = keys[t2];
+                beat += (uint32_t)(bin_of(k2) == bstar && (((uint64_t)k2 << 32) | (uint64_t)(~(uint32_t)t2)) > cj);
+              }
+            }
+            sel = beat < need;
           }
         }
-        if (cnt >= krem) prefix |= bm;
-        else krem -= cnt;
-        mask |= bm;
       }
-      // keys above the threshold T = prefix, then the lowest-index keys equal to it,
-      // emitted in ascending block order
-      const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-      uint32_t eq_base = 0u, sel_base = 0u;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        if (i < per) {
-          const int j = lane + 64 * i;
-          const bool in = j < N;
-          const bool eq = in && kk[i] == prefix;
-          const unsigned long long em = __ballot(eq);
-          const uint32_t er = eq_base + (uint32_t)__popcll(em & lt);
-          const bool sel = in && (kk[i] > prefix || (eq && er < krem));
-          const unsigned long long smk = __ballot(sel);
-          if (sel) emit((int)(sel_base + (uint32_t)__popcll(smk & lt)), j, kk[i]);
-          eq_base += (uint32_t)__popcll(em);
-          sel_base += (uint32_t)__popcll(smk);
-        }
-      }
-    }
-  } else if (keff > 0) {
-    // ---- whole workgroup: 4-pass 8-bit radix select
-    uint32_t prefix = 0u, pmask = 0u;
-    uint32_t krem = (uint32_t)keff;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();
-      for (int j = tid; j < N; j += NT) {
-        const uint32_t k = keys[j];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
-        const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-        const uint32_t mine = h0 + h1 + h2 + h3;
-        uint32_t incl = mine;  // sum over lanes >= this lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t v = __shfl_down(incl, off, 64);
-          if (lane + off < 64) incl += v;
-        }
-        const uint32_t above = incl - mine;  // bins 4 * lane + 4 and higher
-        const uint32_t s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
-        if (s3 >= krem && above < krem) { sh.digit = 4 * lane + 3; sh.above = above; }
-        if (s2 >= krem && s3 < krem) { sh.digit = 4 * lane + 2; sh.above = s3; }
-        if (s1 >= krem && s2 < krem) { sh.digit = 4 * lane + 1; sh.above = s2; }
-        if (s0 >= krem && s1 < krem) { sh.digit = 4 * lane; sh.above = s1; }
-      }
-      __syncthreads();
-      prefix |= sh.digit << shift;
-      pmask |= 0xFFu << shift;
-      krem -= sh.above;
-    }
-    const uint32_t T = prefix;
-    int eq_base = 0, sel_base = 0;
-    for (int c0 = 0; c0 < N; c0 += NT) {
-      const int j = c0 + tid;
-      const bool in = j < N;
-      const uint32_t k = in ? keys[j] : 0u;
-      const bool eq = in && k == T;
-      int eq_rank, eq_tot;
-      block_count<NW>(eq, eq_rank, eq_tot, wsum);
-      const bool sel = in && (k > T || (eq && (uint32_t)(eq_base + eq_rank) < krem));
       int sel_rank, sel_tot;
       block_count<NW>(sel, sel_rank, sel_tot, wsum);
-      if (sel) emit(sel_base + sel_rank, j, k);
-      eq_base += eq_tot;
+      if (sel) emit(sel_base + sel_rank, jj, kj);
       sel_base += sel_tot;
     }
   }
@@ -475,7 +570,7 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(PoolArgs P, BatchArgs Bt, int top_k,
                                                               int32_t* idx, float* scores, int32_t* slots_out) {
-  extern __shared__ uint32_t route_lds[];  // [2][mb] ordered score keys, pool slots
+  extern __shared__ __attribute__((aligned(16))) uint32_t route_lds[];  // route_lds_words(mb, 4)
   __shared__ RouteShared<kRouteThreads / 64> sh;
   route_unit<kRouteThreads>(P, Bt, blockIdx.x, top_k, idx, scores, slots_out, route_lds, sh);
 }
@@ -793,7 +888,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         for (int e = 0; e < 4; ++e) qt[l16 * RQ + jt * 16 + 4 * q4 + e] = acc[e];
       }
     }
-    __syncthreads();  // V_K q and VVx complete (uniform: lr is uniform)
+    lds_barrier();  // V_K q and VVx complete (uniform: lr is uniform)
 
     // ---- low-rank tiles: 16 positions each (position 0 is the anchor)
     v4h qth[NQ], qtl[NQ];
@@ -869,7 +964,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     wstat[wave * 16 + l16] = st.m;
     wstat[kAttWaves * 16 + wave * 16 + l16] = st.l;
   }
-  __syncthreads();
+  lds_barrier();
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, wstat[w * 16 + l16]);
@@ -881,7 +976,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
   float be[4];
   rows_of((st.m == -INFINITY) ? 0.f : __expf(st.m - M), q4, be);
-  __syncthreads();  // per-wave scratch becomes the reduction buffer
+  lds_barrier();  // per-wave scratch becomes the reduction buffer
   float* redO = reinterpret_cast<float*>(region);              // [4][16][kRedStride]
   float* redW = redO + kAttWaves * 16 * kRedStride;            // [4][16][RQ]
   {
@@ -900,7 +995,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * RQ + 16 * n + l16] = Wacc[n][e] * be[e];
     }
   }
-  __syncthreads();
+  lds_barrier();
   v4h wh[NQ], wl[NQ];
   if (NRQ > 0 && lr) {
 #pragma unroll
@@ -978,7 +1073,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   if (lane == 0) redM[wave] = M;
-  __syncthreads();
+  lds_barrier();
   M = fmaxf(fmaxf(redM[0], redM[1]), fmaxf(redM[2], redM[3]));
   float ax = 0.f, ay = 0.f, S = 0.f;
   if (M != -INFINITY) {
@@ -1007,7 +1102,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
   red[wave][2 * lane] = ax;
   red[wave][2 * lane + 1] = ay;
   if (lane == 0) redS[wave] = S;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const float St = ((redS[0] + redS[1]) + redS[2]) + redS[3];
     const float x = ((red[0][2 * lane] + red[1][2 * lane]) + red[2][2 * lane]) + red[3][2 * lane];
@@ -1022,11 +1117,33 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 
 // ----------------------------------------------------------------------------
 // Log-sum-exp combine of the G query rows of one (sequence, KV head) unit by
-// one workgroup: 8 rows at a time, 32 lanes per row, 4 columns per lane.
+// one workgroup.  merge_chunked: 8 rows at a time, 32 lanes per row, 4 columns
+// per lane, online over chunks of 32 parts.  merge_unit: the G x n_parts
+// partials of the unit are contiguous; each of 8 slots of 32 lanes takes an
+// equal contiguous run of them (at most two rows) and issues every load at
+// once, then the slots' sums are combined through LDS.
 // ----------------------------------------------------------------------------
 
-__device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0,
-                                           int G, f16* out, float* out_lse) {
+constexpr int kMergeRun = 32;  // partials per slot in merge_unit's single-issue path
+
+// Buffer loads at device scope (cache policy sc1): they read the device-coherent
+// copy, so they observe data that other workgroups of the same launch wrote with
+// device-scope stores and then published through a counter, without an
+// invalidation of the whole cache.  Reads outside [base, base + bytes) return 0.
+constexpr int kLoadDeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kLoadDeviceScope);  // 4 x 32 raw bits
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kLoadDeviceScope));
+}
+
+__device__ __forceinline__ void merge_chunked(const float* part_o, const float* part_lse, int n_parts, int row0,
+                                              int G, f16* out, float* out_lse) {
   constexpr int kChunk = 32;
   const int tid = threadIdx.x;
   const int j = tid & 31;   // lane within the row's 32-lane group: columns 4 j .. 4 j + 3
@@ -1088,6 +1205,109 @@ __device__ __forceinline__ void merge_unit(const float* part_o, const float* par
   }
 }
 
+// lds: 8 * 2 * kD + 2 * 8 floats
+__device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0,
+                                           int G, f16* out, float* out_lse, float* lds) {
+  const int total = G * n_parts;
+  const int L = (total + 7) / 8;
+  if (n_parts < 1 || G > 8 || n_parts > 64 || L > kMergeRun) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // plain loads below: drop stale cached copies
+    merge_chunked(part_o, part_lse, n_parts, row0, G, out, out_lse);
+    return;
+  }
+  const int tid = threadIdx.x, c4 = tid & 31, sl = tid >> 5;
+  float* red = lds;              // [8 slots][2 rows][kD]
+  float* ms = lds + 8 * 2 * kD;  // [8 rows][m, S]
+  const int e0 = sl * L;
+  const int e1 = e0 + L < total ? e0 + L : total;  // this slot's partials [e0, e1)
+  const int ra = (e0 / n_parts) < G ? e0 / n_parts : G - 1;
+  const int rb = ra + 1 < G ? ra + 1 : G - 1;
+  const int bnd = (ra + 1) * n_parts;  // partials below bnd belong to row ra
+  const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row0 * n_parts * kD, (uint32_t)total * kD * 4);
+  const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row0 * n_parts, (uint32_t)total * 4);
+  float4 o[kMergeRun];
+#pragma unroll
+  for (int k = 0; k < kMergeRun; ++k) {
+    int e = e0 + k;
+    e = e < e1 ? e : (e1 > 0 ? e1 - 1 : 0);
+    o[k] = ld_coherent4(Ob, (uint32_t)(e * kD + 4 * c4) * 4u);
+  }
+  const int p0 = c4 < n_parts ? c4 : 0, p1 = c4 + 32 < n_parts ? c4 + 32 : 0;
+  float la0 = ld_coherent(Lb, (uint32_t)(ra * n_parts + p0) * 4u), la1 = ld_coherent(Lb, (uint32_t)(ra * n_parts + p1) * 4u);
+  float lb0 = ld_coherent(Lb, (uint32_t)(rb * n_parts + p0) * 4u), lb1 = ld_coherent(Lb, (uint32_t)(rb * n_parts + p1) * 4u);
+  if (c4 >= n_parts) la0 = lb0 = -INFINITY;
+  if (c4 + 32 >= n_parts) la1 = lb1 = -INFINITY;
+  float ma = fmaxf(la0, la1), mb = fmaxf(lb0, lb1);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    ma = fmaxf(ma, __shfl_xor(ma, off, 32));
+    mb = fmaxf(mb, __shfl_xor(mb, off, 32));
+  }
+  const float wa0 = la0 == -INFINITY ? 0.f : __expf(la0 - ma), wa1 = la1 == -INFINITY ? 0.f : __expf(la1 - ma);
+  const float wb0 = lb0 == -INFINITY ? 0.f : __expf(lb0 - mb), wb1 = lb1 == -INFINITY ? 0.f : __expf(lb1 - mb);
+  float Sa = wa0 + wa1, Sb = wb0 + wb1;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    Sa += __shfl_xor(Sa, off, 32);
+    Sb += __shfl_xor(Sb, off, 32);
+  }
+  float4 acca = make_float4(0.f, 0.f, 0.f, 0.f), accb = acca;
+#pragma unroll
+  for (int k = 0; k < kMergeRun; ++k) {
+    const int e = e0 + k;
+    const bool in_a = e < bnd;
+    const int pp = in_a ? e - ra * n_parts : e - rb * n_parts;  // the same in all 32 lanes of the slot
+    const float src = pp < 32 ? (in_a ? wa0 : wb0) : (in_a ? wa1 : wb1);
+    float w = __shfl(src, pp & 31, 32);
+    w = e < e1 ? w : 0.f;
+    const float wa = in_a ? w : 0.f, wb = in_a ? 0.f : w;
+    acca.x += wa * o[k].x;
+    acca.y += wa * o[k].y;
+    acca.z += wa * o[k].z;
+    acca.w += wa * o[k].w;
+    accb.x += wb * o[k].x;
+    accb.y += wb * o[k].y;
+    accb.z += wb * o[k].z;
+    accb.w += wb * o[k].w;
+  }
+  *reinterpret_cast<float4*>(red + (sl * 2 + 0) * kD + 4 * c4) = acca;
+  *reinterpret_cast<float4*>(red + (sl * 2 + 1) * kD + 4 * c4) = accb;
+  if (c4 == 0 && e0 < total) {
+    // the slot holding a row's first partial publishes that row's max and sum
+    if (ra * n_parts >= e0) {
+      ms[2 * ra] = ma;
+      ms[2 * ra + 1] = Sa;
+    }
+    if (rb != ra && bnd < e1) {
+      ms[2 * rb] = mb;
+      ms[2 * rb + 1] = Sb;
+    }
+  }
+  lds_barrier();
+  const int g = sl;
+  if (g < G) {
+    const int s_lo = (g * n_parts) / L, s_hi = ((g + 1) * n_parts - 1) / L;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s2 = s_lo; s2 <= s_hi; ++s2) {
+      const int which = ((s2 * L) / n_parts == g) ? 0 : 1;
+      const float4 v = *reinterpret_cast<const float4*>(red + (s2 * 2 + which) * kD + 4 * c4);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const float m = ms[2 * g], S = ms[2 * g + 1];
+    const bool any = S > 0.f;
+    v4h h4;
+    h4[0] = (f16)(any ? acc.x / S : 0.f);
+    h4[1] = (f16)(any ? acc.y / S : 0.f);
+    h4[2] = (f16)(any ? acc.z / S : 0.f);
+    h4[3] = (f16)(any ? acc.w / S : 0.f);
+    *reinterpret_cast<v4h*>(out + (int64_t)(row0 + g) * kD + 4 * c4) = h4;
+    if (c4 == 0) out_lse[row0 + g] = any ? m + __logf(S) : -INFINITY;
+  }
+}
+
 // ----------------------------------------------------------------------------
 // One decode step of one layer in a single launch.
 //
@@ -1124,9 +1344,10 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   __shared__ int32_t sh_slot;
   const int tid = threadIdx.x;
   if (tid == 0) sh_ticket = atomicAdd(&D.ctrl[0], 1u);
-  __syncthreads();
+  lds_barrier();
   const int t = (int)sh_ticket;
   if (t < D.n_route) {
+    __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
     route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
   } else if (t < D.n_items) {
     const int it = t - D.n_route;
@@ -1149,7 +1370,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
         }
         sh_slot = v - kSlotCode;
       }
-      __syncthreads();
+      lds_barrier();
       slot = sh_slot;
     }
     attend_part<NRQ>(P, Bt, D.att, u, p, slot, smem);
@@ -1157,17 +1378,17 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
     stores_done();
     __syncthreads();
     if (tid == 0) sh_flag = (atomicAdd(&D.unit_done[u], 1u) == (uint32_t)(D.att.items_per_unit - 1)) ? 1u : 0u;
-    __syncthreads();
+    lds_barrier();
     if (sh_flag) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale cached copies of the partials
       const int b = u / Bt.Hkv, h = u % Bt.Hkv;
-      merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse);
+      merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse,
+                 reinterpret_cast<float*>(smem));
     }
   }
   // the last workgroup to finish zeroes the control words for the next launch
   __syncthreads();
   if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - 1)) ? 1u : 0u;
-  __syncthreads();
+  lds_barrier();
   if (sh_flag) {
     for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
     for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
@@ -1249,6 +1470,8 @@ dkv_status check_batch(const dkv_pool* P, const dkv_batch* B, bool need_table, b
     if (!B->block_table) return fail(DKV_ERR_INVALID_ARG, "batch->block_table is NULL");
     if (!B->n_blocks) return fail(DKV_ERR_INVALID_ARG, "batch->n_blocks is NULL");
   }
+  if (B->route_keys && !al(B->route_keys, 16))
+    return fail(DKV_ERR_UNSUPPORTED, "batch->route_keys must be 16-byte aligned");
   if (need_window && B->window > 0) {
     if (!B->win_k || !B->win_v) return fail(DKV_ERR_INVALID_ARG, "batch->win_k / win_v is NULL");
     if (!al(B->win_k, 16) || !al(B->win_v, 16))
@@ -1289,6 +1512,7 @@ BatchArgs make_batch_args(const dkv_pool* P, const dkv_batch* B) {
   a.q = (const f16*)B->q;
   a.wk = (const f16*)B->win_k;
   a.wv = (const f16*)B->win_v;
+  a.rkeys = B->route_keys;
   return a;
 }
 
@@ -1301,7 +1525,7 @@ dkv_status launched(const char* what) {
 int rq_of(int rank) { return ((rank + 1 + 15) / 16) * 16; }
 
 // routing scratch: an ordered score key and a pool slot per logical block
-size_t route_lds_bytes(int max_blocks) { return (size_t)2 * (max_blocks > 0 ? max_blocks : 1) * sizeof(uint32_t); }
+size_t route_lds_bytes(int max_blocks, int nw) { return route_lds_words(max_blocks, nw) * sizeof(uint32_t); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1309,7 +1533,7 @@ dkv_status launch_route(const dkv_pool* P, const dkv_batch* B, int top_k, int32_
                         int32_t* slots, hipStream_t st) {
   const int units = B->batch * P->n_kv_heads;
   if (units == 0) return DKV_OK;
-  const size_t shm = route_lds_bytes(B->max_blocks);
+  const size_t shm = route_lds_bytes(B->max_blocks, kRouteThreads / 64);
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)k_route_topk, hipFuncAttributeMaxDynamicSharedMemorySize, 152 * 1024) !=
@@ -1462,6 +1686,22 @@ dkv_status dkv_route_keys(const dkv_pool* pool, const int32_t* slots, int32_t n_
   return launched("k_route_keys");
 }
 
+dkv_status dkv_gather_route_keys(const dkv_pool* pool, const dkv_batch* batch, float* out, void* stream) {
+  g_err[0] = 0;
+  dkv_status s;
+  if ((s = check_pool_shape(pool))) return s;
+  if ((s = check_batch(pool, batch, true, false))) return s;
+  const int64_t n = (int64_t)batch->batch * pool->n_kv_heads * batch->max_blocks * (DKV_HEAD_DIM / 4);
+  if (n == 0) return DKV_OK;
+  if (!out) return fail(DKV_ERR_INVALID_ARG, "out is NULL");
+  if (!al(out, 16)) return fail(DKV_ERR_UNSUPPORTED, "out must be 16-byte aligned");
+  if ((s = check_pool_arrays(pool, 4))) return s;
+  if ((n + 255) / 256 > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "routing-key table too large");
+  hipLaunchKernelGGL(k_gather_route_keys, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     make_pool_args(pool), make_batch_args(pool, batch), out);
+  return launched("k_gather_route_keys");
+}
+
 dkv_status dkv_route_topk(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, int32_t* idx,
                           float* scores, void* stream) {
   g_err[0] = 0;
@@ -1473,7 +1713,7 @@ dkv_status dkv_route_topk(const dkv_pool* pool, const dkv_batch* batch, int32_t 
     return fail(DKV_ERR_UNSUPPORTED, "max_blocks %d > %d", batch->max_blocks, DKV_MAX_ROUTE_BLOCKS);
   if (batch->batch == 0) return DKV_OK;
   if (!idx) return fail(DKV_ERR_INVALID_ARG, "idx is NULL");
-  if (batch->max_blocks > 0 && (s = check_pool_arrays(pool, 4))) return s;
+  if (batch->max_blocks > 0 && !batch->route_keys && (s = check_pool_arrays(pool, 4))) return s;
   return launch_route(pool, batch, top_k, idx, scores, nullptr, (hipStream_t)stream);
 }
 
@@ -1570,7 +1810,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
     return fail(DKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
                 need);
   if (!al(workspace, 256)) return fail(DKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (top_k > 0 && (s = check_pool_arrays(pool, 1 | 2 | 4))) return s;
+  if (top_k > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) return s;
 
   const hipStream_t st = (hipStream_t)stream;
   const WsLayout w = decode_layout(pool, batch, top_k);
@@ -1606,7 +1846,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
   D.n_items = (int)items;
   size_t shm = (size_t)att_lds_bytes(a.rq);
-  const size_t route_shm = route_lds_bytes(batch->max_blocks);
+  const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
   if (top_k > 0 && route_shm > shm) shm = route_shm;
 
   if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)

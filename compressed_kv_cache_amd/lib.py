@@ -12,6 +12,8 @@ from __future__ import annotations
 
 import ctypes
 import os
+
+import numpy as np
 from typing import Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +31,7 @@ DKV_ERR_HIP = 4
 EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route_keys",
             "dkv_route_topk", "dkv_lowrank_attn", "dkv_exact_attn", "dkv_lse_merge",
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
-            "dkv_decode_profiled")
+            "dkv_decode_profiled", "dkv_gather_route_keys")
 
 
 class DKVError(RuntimeError):
@@ -56,7 +58,8 @@ class BatchC(ctypes.Structure):
                 ("window", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("block_table", ctypes.c_void_p), ("n_blocks", ctypes.c_void_p),
                 ("win_len", ctypes.c_void_p), ("q", ctypes.c_void_p),
-                ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p)]
+                ("win_k", ctypes.c_void_p), ("win_v", ctypes.c_void_p),
+                ("route_keys", ctypes.c_void_p)]
 
 
 _lib = None
@@ -82,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.dkv_route_keys.argtypes = [P, vp, i32, vp]
     lib.dkv_route_keys.restype = i32
     lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
+    lib.dkv_gather_route_keys.argtypes = [P, Bp, vp, vp]
+    lib.dkv_gather_route_keys.restype = i32
     lib.dkv_route_topk.restype = i32
     lib.dkv_lowrank_attn.argtypes = [P, Bp, vp, i32, f32, vp, vp, i32, i32, vp]
     lib.dkv_lowrank_attn.restype = i32
@@ -120,6 +125,20 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
+def _torch_dtypes():
+    import torch
+    return {"<f2": torch.float16, "<f4": torch.float32, "|u1": torch.uint8, "<i4": torch.int32}
+
+
+class _LazyDtypes(dict):
+    def __missing__(self, key):
+        self.update(_torch_dtypes())
+        return dict.__getitem__(self, key)
+
+
+_TORCH_DTYPE = _LazyDtypes()
+
+
 def _view(t, dims_inside: int) -> View:
     """View of a tensor shaped [slots][heads][...inside...] (strides in elements)."""
     if t is None:
@@ -150,15 +169,56 @@ class Pool:
                        _view(vv, 2), _view(resid_k, 2), _view(resid_v, 2), _view(resid_pos, 1),
                        _view(route_key, 1))
 
+    # per-(slot, head) record order: what a block's attention reads first comes first
+    RECORD_ORDER = ("resid_pos", "vv", "anchor_v", "vk", "anchor_k", "u", "resid_k", "resid_v")
+
     @classmethod
-    def from_numpy(cls, arrays: dict, device="cuda"):
+    def from_numpy(cls, arrays: dict, device="cuda", layout: str = "records"):
+        """Upload one layer's pool.
+
+        layout "records": all compressed arrays of one (slot, KV head) share one
+        contiguous record (each piece 256-byte aligned), so a routed block is
+        one contiguous read and one or two address translations.
+        layout "arrays": one dense tensor per array.
+        The routing key is a dense fp32 [S][Hkv][128] array in both layouts
+        (routing reads it for every block of a sequence)."""
         import torch
-        t = {k: torch.from_numpy(arrays[k]).to(device) for k in
-             ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
         S, Hkv, d = arrays["anchor_k"].shape
         rk = torch.zeros((S, Hkv, d), dtype=torch.float32, device=device)
-        return cls(t["anchor_k"], t["anchor_v"], t["u"], t["vk"], t["vv"], t["resid_k"],
+        names = ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")
+        if layout == "arrays":
+            t = {k: torch.from_numpy(arrays[k]).to(device) for k in names}
+        elif layout == "records":
+            offs, rec = {}, 0
+            for k in cls.RECORD_ORDER:
+                offs[k] = rec
+                nbytes = arrays[k][0, 0].nbytes if arrays[k].size else 0
+                rec += (nbytes + 255) // 256 * 256
+            rec = max(rec, 256)
+            host = np.zeros((S, Hkv, rec), dtype=np.uint8)
+            for k in cls.RECORD_ORDER:
+                a = np.ascontiguousarray(arrays[k])
+                nb = a[0, 0].nbytes if a.size else 0
+                if nb:
+                    host[:, :, offs[k]:offs[k] + nb] = a.reshape(S, Hkv, -1).view(np.uint8).reshape(S, Hkv, nb)
+            buf = torch.from_numpy(host).to(device)
+            t = {}
+            for k in names:
+                a = arrays[k]
+                dt = _TORCH_DTYPE[a.dtype.str]
+                nb = a[0, 0].nbytes if a.size else 0
+                if nb == 0:
+                    t[k] = torch.empty(a.shape, dtype=dt, device=device)
+                else:
+                    t[k] = buf[:, :, offs[k]:offs[k] + nb].view(dt).unflatten(2, a.shape[2:])
+            t["_record"] = buf
+        else:
+            raise ValueError(f"unknown pool layout {layout!r}")
+        pool = cls(t["anchor_k"], t["anchor_v"], t["u"], t["vk"], t["vv"], t["resid_k"],
                    t["resid_v"], t["resid_pos"], rk)
+        if "_record" in t:
+            pool.tensors["_record"] = t["_record"]
+        return pool
 
     @property
     def route_key(self):
@@ -171,15 +231,21 @@ class Batch:
     q fp16 [B][Hq][128]; win_k, win_v fp16 [B][Hkv][W][128]; block_table int32
     [B][max_blocks]; n_blocks int32 [B]; win_len int32 [B] or None."""
 
-    def __init__(self, q, win_k, win_v, block_table, n_blocks, win_len=None):
+    def __init__(self, q, win_k, win_v, block_table, n_blocks, win_len=None, route_keys=None):
         self.tensors = dict(q=q, win_k=win_k, win_v=win_v, block_table=block_table,
-                            n_blocks=n_blocks, win_len=win_len)
+                            n_blocks=n_blocks, win_len=win_len, route_keys=route_keys)
         B, Hq = int(q.shape[0]), int(q.shape[1])
         W = int(win_k.shape[2]) if win_k is not None else 0
         mb = int(block_table.shape[1]) if block_table is not None else 0
         self.batch, self.n_q_heads, self.window, self.max_blocks = B, Hq, W, mb
         self.c = BatchC(B, Hq, W, mb, _ptr(block_table), _ptr(n_blocks), _ptr(win_len), _ptr(q),
-                        _ptr(win_k), _ptr(win_v))
+                        _ptr(win_k), _ptr(win_v), _ptr(route_keys))
+
+    def set_route_keys(self, route_keys) -> None:
+        """Attach (or with None detach) the per-sequence routing-key table
+        fp32 [B][Hkv][max_blocks][128]."""
+        self.tensors["route_keys"] = route_keys
+        self.c.route_keys = _ptr(route_keys)
 
     @classmethod
     def from_numpy(cls, q, win_k, win_v, block_table, n_blocks, win_len=None, device="cuda"):
@@ -193,6 +259,27 @@ class Batch:
 # ---------------------------------------------------------------------------
 # Entry points
 # ---------------------------------------------------------------------------
+
+def gather_route_keys(pool: Pool, batch: Batch, out=None, attach: bool = True, stream=None):
+    """Per-sequence routing-key table (dkv_gather_route_keys); attached to the
+    batch unless attach is False.  Returns the fp32 [B][Hkv][max_blocks][128] tensor."""
+    import torch
+    lib = load()
+    if out is None:
+        dev = batch.tensors["q"].device
+        out = torch.empty((batch.batch, pool.n_kv_heads, batch.max_blocks, HEAD_DIM),
+                          dtype=torch.float32, device=dev)
+    saved = batch.c.route_keys
+    batch.c.route_keys = None
+    try:
+        _check(lib.dkv_gather_route_keys(ctypes.byref(pool.c), ctypes.byref(batch.c), _ptr(out),
+                                         _stream(stream)), "dkv_gather_route_keys")
+    finally:
+        batch.c.route_keys = saved
+    if attach:
+        batch.set_route_keys(out)
+    return out
+
 
 def route_keys(pool: Pool, slots=None, stream=None) -> None:
     lib = load()

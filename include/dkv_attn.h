@@ -60,13 +60,13 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 1
+#define DKV_ABI_VERSION 2
 #define DKV_HEAD_DIM 128
 #define DKV_BLOCK_SIZE 256
 #define DKV_MAX_RANK 64
 #define DKV_MAX_RESID 255
 #define DKV_MAX_GROUP 16
-#define DKV_MAX_ROUTE_BLOCKS 16384
+#define DKV_MAX_ROUTE_BLOCKS 12288
 
 typedef int32_t dkv_status;
 #define DKV_OK 0
@@ -115,6 +115,12 @@ typedef struct dkv_batch {
   const void* q;             /* fp16 [B][Hq][d]: the decode queries (post-RoPE) */
   const void* win_k;         /* fp16 [B][Hkv][W][d]: exact recency window keys */
   const void* win_v;         /* fp16 [B][Hkv][W][d]: exact recency window values */
+  const float* route_keys;   /* fp32 [B][Hkv][max_blocks][d]: routing key of logical block j
+                                of each sequence (a copy of pool->route_key in block-table
+                                order, see dkv_gather_route_keys), 16-byte aligned; or NULL to
+                                read pool->route_key through block_table.  Routing then reads
+                                each sequence's keys as one contiguous run, with no wait for
+                                the block table.  Entries of invalid table slots are ignored. */
 } dkv_batch;
 
 /* Human-readable name of a status code (static string). */
@@ -137,6 +143,14 @@ int32_t dkv_abi_version(void);
  *            (then n_list is ignored).  Out-of-range slots are skipped. */
 dkv_status dkv_route_keys(const dkv_pool* pool, const int32_t* slots, int32_t n_list,
                           void* stream);
+
+/* Per-sequence routing-key table for dkv_batch.route_keys:
+ * out[b][h][j] = pool->route_key[block_table[b][j]][h] for j < n_blocks[b] and a
+ * valid slot, zero otherwise.  Refresh a sequence's rows when its block table
+ * changes (once per sealed block), like the block table itself.
+ *   out: fp32 [B][Hkv][max_blocks][d], 16-byte aligned, caller-owned. */
+dkv_status dkv_gather_route_keys(const dkv_pool* pool, const dkv_batch* batch, float* out,
+                                 void* stream);
 
 /* Top-K block routing (README "Key Environment Knobs": DKV_TOPK_BLOCKS,
  * DKV_CB_GQA_ROUTE head averaging, DKV_CB_ROUTE_ALL scoring of every block).

@@ -388,3 +388,56 @@ def test_decode_workspace_reused_across_shapes(lib):
                                    2, small.top_k, small.scale, idx=i2.cpu().numpy().astype(np.int64))
         assert parity.check_outputs(o1.cpu().numpy(), l1.cpu().numpy(), r1, rl1).ok
         assert parity.check_outputs(o2.cpu().numpy(), l2.cpu().numpy(), r2, rl2).ok
+
+
+@pytest.mark.parametrize("cfg,variant", [(1, ""), (0, "S1")])
+def test_decode_pool_layouts(lib, cfg, variant):
+    """The pool views may point into one record per (slot, KV head) or into one
+    dense tensor per array: identical arithmetic, so identical bits."""
+    wl = config(cfg, variant)
+    lay = wl.layers[0]
+    res = {}
+    for layout in ("arrays", "records"):
+        say(f"[decode layout] {wl.name} {variant} {layout}")
+        pool = lib.Pool.from_numpy(lay.pool(), DEV, layout=layout)
+        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                                     wl.win_len, device=DEV)
+        lib.route_keys(pool)
+        out, lse, idx = lib.decode(pool, batch, wl.top_k, wl.scale)
+        torch.cuda.synchronize()
+        res[layout] = (out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy())
+    for a, b in zip(res["arrays"], res["records"]):
+        assert np.array_equal(a, b)
+    gidx = res["records"][2].astype(np.int64)
+    ref_o, ref_l, _ = oracle.decode(lay.pool(), lay.q, lay.win_k, lay.win_v, wl.block_table,
+                                    wl.n_blocks, wl.win_len, wl.n_kv_heads, wl.top_k, wl.scale,
+                                    idx=gidx)
+    oc = parity.check_outputs(res["records"][0], res["records"][1], ref_o, ref_l)
+    assert oc.ok, oc.message
+
+
+@pytest.mark.parametrize("cfg,variant", [(1, ""), (3, ""), (0, "S2")])
+def test_route_key_table(lib, cfg, variant):
+    """dkv_gather_route_keys copies pool keys into block-table order (zero past
+    n_blocks), and routing / decode read through it give the same bits as
+    through the pool."""
+    wl = config(cfg, variant)
+    say(f"[route key table] {wl.name} {variant}")
+    pool, batch = upload(lib, wl)
+    tab = lib.gather_route_keys(pool, batch, attach=False)
+    torch.cuda.synchronize()
+    pk = pool.route_key.cpu().numpy()
+    t = tab.cpu().numpy()
+    want = np.zeros_like(t)
+    for b in range(wl.batch):
+        nb = int(wl.n_blocks[b])
+        want[b, :, :nb] = pk[wl.block_table[b, :nb]].transpose(1, 0, 2)
+    assert np.array_equal(t, want)
+    idx0, sc0 = lib.route_topk(pool, batch, wl.top_k, with_scores=True)
+    out0, lse0, oi0 = lib.decode(pool, batch, wl.top_k, wl.scale)
+    batch.set_route_keys(tab)
+    idx1, sc1 = lib.route_topk(pool, batch, wl.top_k, with_scores=True)
+    out1, lse1, oi1 = lib.decode(pool, batch, wl.top_k, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx1) and torch.equal(sc0, sc1)
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1) and torch.equal(oi0, oi1)

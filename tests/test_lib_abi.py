@@ -157,3 +157,20 @@ def test_other_entry_points_validate(clib):
     assert clib.dkv_route_keys(P, FAKE, -1, None) == L.DKV_ERR_INVALID_ARG
     q = _pool(route_key=L.View(FAKE + 4, 256, 128))
     assert clib.dkv_route_keys(ctypes.byref(q), None, 0, None) == L.DKV_ERR_UNSUPPORTED
+
+
+def test_route_key_table_validates(clib):
+    p, b = _pool(), _batch()
+    P, B = ctypes.byref(p), ctypes.byref(b)
+    assert clib.dkv_gather_route_keys(P, B, None, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_gather_route_keys(P, B, FAKE + 8, None) == L.DKV_ERR_UNSUPPORTED
+    assert clib.dkv_gather_route_keys(P, ctypes.byref(_batch(batch=0)), None, None) == L.DKV_OK
+    q = _pool(route_key=L.View(None, 0, 0))
+    assert clib.dkv_gather_route_keys(ctypes.byref(q), B, FAKE, None) == L.DKV_ERR_INVALID_ARG
+    # a misaligned per-sequence table is refused by routing and decode alike
+    bad = _batch(route_keys=FAKE + 4)
+    assert clib.dkv_route_topk(P, ctypes.byref(bad), 4, FAKE, None, None) == L.DKV_ERR_UNSUPPORTED
+    assert _decode(clib, _pool(), bad) == L.DKV_ERR_UNSUPPORTED
+    # with the table, routing needs no pool routing keys
+    ok = _batch(route_keys=FAKE)
+    assert clib.dkv_decode_workspace_size(ctypes.byref(q), ctypes.byref(ok), 4) > 0
