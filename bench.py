@@ -89,9 +89,10 @@ def source_digest() -> str:
 
 
 def measured_traffic(digest: str):
-    """HBM bytes per k_attend launch from the committed rocprofv3 PMC summary, or
-    None when the kernel source changed since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", "k_attend_traffic.json")
+    """HBM bytes per k_decode launch (read + written, scaled by the copy-kernel
+    calibration) from the committed rocprofv3 PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "k_decode_traffic_stack64k_b4.json")
     try:
         with open(p) as f:
             t = json.load(f)
@@ -170,13 +171,14 @@ def main() -> int:
 
     if args.copy_probe_mib:
         # a plain device copy of known size: the reference for HBM counter scaling
+        # (an elementwise kernel, so that it is a dispatch the counters see)
         n = args.copy_probe_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
-        log(f"copy probe: {n * 4} bytes read and written per dispatch")
+        log(f"copy probe: {n * 4} bytes read and {n * 4} bytes written per dispatch")
         del a, b
 
     hip = Hip()
@@ -295,12 +297,48 @@ def main() -> int:
         ms_graph = t_start.elapsed_time(t_end) / args.steps
         log(f"hipGraph: {ms_graph:.4f} ms/step")
 
+    # ---- kernel durations inside a graph replay: hipEvents recorded as graph nodes
+    #      around every layer's decode kernel (no host launch gaps between kernels)
+    kernel_ms_graph = None
+    if not args.no_graph:
+        try:
+            evg = [[hip.event() for _ in range(2)] for _ in range(n_layers)]
+            gp = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gp):
+                for i in range(n_layers):
+                    lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
+                                        evg[i], out_idx=idxs[i])
+            torch.cuda.synchronize()
+            per = []
+            for rep in range(args.warmup + args.steps):
+                gp.replay()
+                torch.cuda.synchronize()
+                if rep >= args.warmup:
+                    per.append([hip.elapsed_ms(evg[i][0], evg[i][1]) for i in range(n_layers)])
+            per = np.array(per)
+            kernel_ms_graph = float(per.mean())
+            for i in range(n_layers):
+                assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
+                    "profiled graph replay differs from eager"
+            log(f"in-graph decode kernel {kernel_ms_graph * 1e3:.2f} us per layer "
+                f"(p10 {np.percentile(per, 10) * 1e3:.2f}, p90 {np.percentile(per, 90) * 1e3:.2f})")
+            del gp
+            for e2 in evg:
+                for e in e2:
+                    hip.destroy(e)
+        except Exception as e:                            # pragma: no cover
+            log(f"in-graph kernel timing unavailable ({e}); using the eager kernel timing")
+            kernel_ms_graph = None
+
     best_ms = ms_eager if ms_graph is None else min(ms_eager, ms_graph)
     mode = "hipgraph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"
     qps = queries_per_step / (best_ms * 1e-3)
     gbps = step_bytes / (best_ms * 1e-3) / 1e9
     launch_bytes = step_bytes / n_layers                  # one decode kernel per layer
-    kernel_gbps = launch_bytes / (kernel_ms * 1e-3) / 1e9
+    # the roofline uses the kernel duration of the timed mode: in-graph when the
+    # graph replay is the timed mode, else the eager events
+    kern_ms = kernel_ms_graph if (mode == "hipgraph" and kernel_ms_graph is not None) else kernel_ms
+    kernel_gbps = launch_bytes / (kern_ms * 1e-3) / 1e9
     digest = source_digest()
     traffic = measured_traffic(digest)
 
@@ -329,11 +367,13 @@ def main() -> int:
         "queries_per_step": queries_per_step,
         "ms_per_step_eager": ms_eager,
         "ms_per_step_graph": ms_graph,
-        "kernel_us_per_layer": kernel_ms * 1e3,
+        "kernel_us_per_layer": kern_ms * 1e3,
+        "kernel_us_per_layer_eager": kernel_ms * 1e3,
+        "kernel_us_per_layer_in_graph": None if kernel_ms_graph is None else kernel_ms_graph * 1e3,
         "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": kernel_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes,
-                     "avg_launch_us": kernel_ms * 1e3},
+                     "avg_launch_us": kern_ms * 1e3},
         "resident_cache_GB": resident / 1e9,
         "kernel_source_sha256_16": digest,
     }
