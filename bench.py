@@ -243,15 +243,22 @@ def main() -> int:
     ref_lse = [x.clone() for x in lses]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    s_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    s_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start.record()
+    # Each step is enqueued while a spin kernel holds the GPU, so that its 28
+    # kernels then run back to back, as they do in a graph replay: host launch
+    # gaps would otherwise leave the GPU idle between layers.
+    hold = int(2e-3 * 2.4e9)                              # ~2 ms of shader clock
     for s in range(args.steps):
+        torch.cuda._sleep(hold)
+        s_start[s].record()
         for i in range(n_layers):
             lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
                                 ev[s][i], out_idx=idxs[i])
-    t_end.record()
+        s_end[s].record()
     torch.cuda.synchronize()
-    ms_eager = t_start.elapsed_time(t_end) / args.steps
+    ms_eager = float(np.mean([s_start[s].elapsed_time(s_end[s]) for s in range(args.steps)]))
     kern = np.array([[hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for i in range(n_layers)]
                      for s in range(args.steps)])
     kernel_ms = float(kern.mean())
@@ -297,47 +304,14 @@ def main() -> int:
         ms_graph = t_start.elapsed_time(t_end) / args.steps
         log(f"hipGraph: {ms_graph:.4f} ms/step")
 
-    # ---- kernel durations inside a graph replay: hipEvents recorded as graph nodes
-    #      around every layer's decode kernel (no host launch gaps between kernels)
-    kernel_ms_graph = None
-    if not args.no_graph:
-        try:
-            evg = [[hip.event() for _ in range(2)] for _ in range(n_layers)]
-            gp = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gp):
-                for i in range(n_layers):
-                    lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
-                                        evg[i], out_idx=idxs[i])
-            torch.cuda.synchronize()
-            per = []
-            for rep in range(args.warmup + args.steps):
-                gp.replay()
-                torch.cuda.synchronize()
-                if rep >= args.warmup:
-                    per.append([hip.elapsed_ms(evg[i][0], evg[i][1]) for i in range(n_layers)])
-            per = np.array(per)
-            kernel_ms_graph = float(per.mean())
-            for i in range(n_layers):
-                assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
-                    "profiled graph replay differs from eager"
-            log(f"in-graph decode kernel {kernel_ms_graph * 1e3:.2f} us per layer "
-                f"(p10 {np.percentile(per, 10) * 1e3:.2f}, p90 {np.percentile(per, 90) * 1e3:.2f})")
-            del gp
-            for e2 in evg:
-                for e in e2:
-                    hip.destroy(e)
-        except Exception as e:                            # pragma: no cover
-            log(f"in-graph kernel timing unavailable ({e}); using the eager kernel timing")
-            kernel_ms_graph = None
-
     best_ms = ms_eager if ms_graph is None else min(ms_eager, ms_graph)
     mode = "hipgraph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"
     qps = queries_per_step / (best_ms * 1e-3)
     gbps = step_bytes / (best_ms * 1e-3) / 1e9
     launch_bytes = step_bytes / n_layers                  # one decode kernel per layer
-    # the roofline uses the kernel duration of the timed mode: in-graph when the
-    # graph replay is the timed mode, else the eager events
-    kern_ms = kernel_ms_graph if (mode == "hipgraph" and kernel_ms_graph is not None) else kernel_ms
+    # the roofline uses the kernel duration measured with hipEvents around every
+    # decode kernel in the timed eager steps (kernels back to back, as in a replay)
+    kern_ms = kernel_ms
     kernel_gbps = launch_bytes / (kern_ms * 1e-3) / 1e9
     digest = source_digest()
     traffic = measured_traffic(digest)
@@ -368,8 +342,6 @@ def main() -> int:
         "ms_per_step_eager": ms_eager,
         "ms_per_step_graph": ms_graph,
         "kernel_us_per_layer": kern_ms * 1e3,
-        "kernel_us_per_layer_eager": kernel_ms * 1e3,
-        "kernel_us_per_layer_in_graph": None if kernel_ms_graph is None else kernel_ms_graph * 1e3,
         "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": kernel_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes,

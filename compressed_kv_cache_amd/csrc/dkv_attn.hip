@@ -155,8 +155,33 @@ __device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
 __device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // wait until this thread's stores have completed
 __device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Buffer loads at device scope (cache policy sc1): they read the device-coherent
+// copy, so they observe data that other workgroups of the same launch wrote with
+// device-scope stores and then published through a counter, without an
+// invalidation of the whole cache.  Reads outside [base, base + bytes) return 0.
+constexpr int kLoadDeviceScope = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kLoadDeviceScope);  // 4 x 32 raw bits
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float4 v) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u bits = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(bits, r, (int)byte_off, 0, kLoadDeviceScope);
+}
+__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kLoadDeviceScope));
+}
+
 
 // Loads are always issued from an in-bounds address and masked afterwards: a
 // guarded load would compile to its own branch, and the branch merge to a full
@@ -598,15 +623,18 @@ __host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
 
 // per-wave scratch: the V tile of an exact tile, or the Ux transpose of a
 // low-rank tile, followed by that wave's residual-position bit mask
+// per-wave scratch: the wave's four transposed U tiles (low-rank phase) or two
+// V tiles (exact phase), then the 256-bit residual-position mask
 __host__ __device__ inline int att_scratch_bytes(int rq) {
-  const int a = 16 * kVStride * 2;
-  const int b = 16 * (rq + 4) * 2;
+  const int a = kLRTilesPerWave * 16 * (rq + 4) * 2;
+  const int b = 2 * 16 * kVStride * 2;
   return round16((a > b ? a : b) + 32);
 }
 
+// the per-wave scratch areas, later reused for the cross-wave sum of O^T
 __host__ __device__ inline int att_region_bytes(int rq) {
   const int scratch = kAttWaves * att_scratch_bytes(rq);
-  const int red = kAttWaves * 16 * kRedStride * 4 + kAttWaves * 16 * rq * 4;  // O and W of 4 waves
+  const int red = kAttWaves * 16 * kRedStride * 4;
   return scratch > red ? scratch : red;
 }
 
@@ -614,61 +642,62 @@ __host__ __device__ inline int att_lds_bytes(int rq) {
   return 16 * rq * 4 + rq * kVStride * 2 + 2 * kAttWaves * 16 * 4 + att_region_bytes(rq);
 }
 
-struct ExState {
-  float m, l;
-  v4f O[8];
-};
-
-template <int NQ>
-__device__ __forceinline__ void rescale_state(ExState& st, v4f (&Wacc)[NQ], float alpha, int q4) {
-  float ae[4];
-  rows_of(alpha, q4, ae);
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st.O[n][e] *= ae[e];
-  }
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Wacc[n][e] *= ae[e];
-  }
+// Reductions over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (the four
+// row groups of an MFMA accumulator), with gfx950 lane-swap moves; every lane
+// gets the same bits.
+__device__ __forceinline__ float q4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float q4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One 16-row tile of exact rows t0..t0+15 (rows >= n_ex masked).
-template <int NQ>
-__device__ __forceinline__ void exact_tile(const v8h (&kx)[4], const v8h (&vx)[4], int t0, int n_ex,
-                                           const v4h (&qf)[4][2], float scale, ExState& st, v4f (&Wacc)[NQ],
-                                           f16* Vt, int l16, int q4) {
+// Attention state of one wave, transposed: head g = lane % 16 is the MFMA
+// column, so every per-head factor is the lane's own value.
+//   Ot[n]: O^T[d = 16 n + 4 (lane / 16) + e][g]   (sum over rows of p v, unnormalised)
+//   m, l:  running maximum and sum of exp for head g
+struct ExState {
+  float m, l;
+  v4f Ot[8];
+};
+
+// QK^T of one 16-row exact tile: S[row = 4 q4 + e][head l16]
+__device__ __forceinline__ v4f exact_scores(const v8h (&kx)[4], const v4h (&qf)[4][2]) {
   v4f S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     S = mfma16(lo4(kx[s]), qf[s][0], S);
     S = mfma16(hi4(kx[s]), qf[s][1], S);
   }
-  float zz[4];
+  return S;
+}
+
+// O^T += V^T p for one 16-row tile whose V rows sit in LDS at Vt[row][kVStride]
+__device__ __forceinline__ void exact_pv(ExState& st, const f16* Vt, const float (&pe)[4], int l16, int q4) {
+  v4h ph, pl;
+  split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) zz[e] = (t0 + 4 * q4 + e < n_ex) ? S[e] * scale : -INFINITY;
-  float alpha, pe[4];
-  softmax_tile(zz, st.m, st.l, alpha, pe);
-  rescale_state<NQ>(st, Wacc, alpha, q4);
+  for (int n = 0; n < 8; ++n) {
+    v4h av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
+    st.Ot[n] = mfma16(av, ph, st.Ot[n]);
+    st.Ot[n] = mfma16(av, pl, st.Ot[n]);
+  }
+}
+
+__device__ __forceinline__ void stage_v_tile(f16* Vt, const v8h (&vx)[4], int l16, int q4) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4) = lo4(vx[s]);
     *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4 + 4) = hi4(vx[s]);
   }
-  wave_sync_lds();
-  v4h ph, pl;
-  split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    v4h bv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bv[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
-    st.O[n] = mfma16(ph, bv, st.O[n]);
-    st.O[n] = mfma16(pl, bv, st.O[n]);
-  }
-  wave_sync_lds();
 }
 
 __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, int tile, int ntile, int n_ex,
@@ -778,10 +807,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   st.m = -INFINITY;
   st.l = 0.f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) st.O[n] = (v4f){0.f, 0.f, 0.f, 0.f};
-  v4f Wacc[NQ];
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) Wacc[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 8; ++n) st.Ot[n] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // ---- issue the loads, in the order of use
   v4h ua[kLRTilesPerWave][NQ];
@@ -859,6 +885,9 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
 
   // ---- low-rank set-up: residual-position mask (per wave), VVx, VKx q
+  v4f Wt[NQ];  // W^T[j = 16 n + 4 q4 + e][head l16] = sum over positions of Ux[pos][j] p[pos][head]
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) Wt[n] = (v4f){0.f, 0.f, 0.f, 0.f};
   if (NRQ > 0 && lr) {
     if (lane < 8) wmask[lane] = 0u;
     wave_sync_lds();
@@ -890,14 +919,15 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
     lds_barrier();  // V_K q and VVx complete (uniform: lr is uniform)
 
-    // ---- low-rank tiles: 16 positions each (position 0 is the anchor)
+    // ---- the wave's four 16-position tiles as one softmax step (position 0 is the anchor)
     v4h qth[NQ], qtl[NQ];
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
       split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
     }
-    f16* T = reinterpret_cast<f16*>(my);
+    f16* T = reinterpret_cast<f16*>(my);  // [kLRTilesPerWave][16][TS]
+    float zz[kLRTilesPerWave][4];
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
       const int i0 = (wave + kAttWaves * k) * 16;
@@ -910,6 +940,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
           const int j = 16 * s + 4 * q4 + e;
           ua[k][s][e] = (j == r) ? (f16)1.0f : ((i > 0 && j < r) ? ua[k][s][e] : (f16)0.0f);
         }
+        *reinterpret_cast<v4h*>(T + (k * 16 + l16) * TS + 16 * s + 4 * q4) = ua[k][s];
       }
       v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -917,132 +948,158 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         z = mfma16(ua[k][s], qth[s], z);
         z = mfma16(ua[k][s], qtl[s], z);
       }
-      float zz[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ii = i0 + 4 * q4 + e;
         const bool masked = (ii > 0) & (((wmask[ii >> 5] >> (ii & 31)) & 1u) != 0u);
-        zz[e] = masked ? -INFINITY : z[e] * scale;
+        zz[k][e] = masked ? -INFINITY : z[e] * scale;
       }
-      float alpha, pe[4];
-      softmax_tile(zz, st.m, st.l, alpha, pe);
-      rescale_state<NQ>(st, Wacc, alpha, q4);
-      v4h ph, pl;
-      split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
+    }
+    float tm = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) *reinterpret_cast<v4h*>(T + l16 * TS + 16 * s + 4 * q4) = ua[k][s];
-      wave_sync_lds();
+    for (int k = 0; k < kLRTilesPerWave; ++k)
+      tm = fmaxf(tm, fmaxf(fmaxf(zz[k][0], zz[k][1]), fmaxf(zz[k][2], zz[k][3])));
+    tm = q4_max(tm);
+    float pe[kLRTilesPerWave][4];
+    float ps_ = 0.f;
+#pragma unroll
+    for (int k = 0; k < kLRTilesPerWave; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[k][e] = (tm == -INFINITY) ? 0.f : __expf(zz[k][e] - tm);
+        ps_ += pe[k][e];
+      }
+    }
+    st.m = tm;  // the low-rank rows come first: nothing to rescale
+    st.l = q4_sum(ps_);
+    wave_sync_lds();
+#pragma unroll
+    for (int k = 0; k < kLRTilesPerWave; ++k) {
+      v4h ph, pl;
+      split_hl(pe[k][0], pe[k][1], pe[k][2], pe[k][3], ph, pl);
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        v4h bu;
+        v4h au;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bu[e] = T[(4 * q4 + e) * TS + 16 * n + l16];
-        Wacc[n] = mfma16(ph, bu, Wacc[n]);
-        Wacc[n] = mfma16(pl, bu, Wacc[n]);
+        for (int e = 0; e < 4; ++e) au[e] = T[(k * 16 + 4 * q4 + e) * TS + 16 * n + l16];
+        Wt[n] = mfma16(au, ph, Wt[n]);
+        Wt[n] = mfma16(au, pl, Wt[n]);
       }
-      wave_sync_lds();
     }
+    wave_sync_lds();
   }
 
-  // ---- exact rows: two 16-row tiles in flight
+  // ---- exact rows: two 16-row tiles per softmax step
   if (n_ex > 0) {
-    f16* Vt = reinterpret_cast<f16*>(my);
+    f16* Va = reinterpret_cast<f16*>(my);
+    f16* Vb = Va + 16 * kVStride;
     while (ta < ntile) {
-      exact_tile<NQ>(ka, va, ta * 16, n_ex, qf, scale, st, Wacc, Vt, l16, q4);
+      const bool has_b = tb < ntile;  // uniform over the wave
+      const v4f Sa = exact_scores(ka, qf);
+      const v4f Sb = exact_scores(kb, qf);
+      float za[4], zb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        za[e] = (ta * 16 + 4 * q4 + e < n_ex) ? Sa[e] * scale : -INFINITY;
+        zb[e] = (has_b && tb * 16 + 4 * q4 + e < n_ex) ? Sb[e] * scale : -INFINITY;
+      }
+      float tm = fmaxf(fmaxf(fmaxf(za[0], za[1]), fmaxf(za[2], za[3])),
+                       fmaxf(fmaxf(zb[0], zb[1]), fmaxf(zb[2], zb[3])));
+      tm = q4_max(tm);
+      const float mn = fmaxf(st.m, tm);
+      const bool none = (mn == -INFINITY);
+      const float alpha = none ? 1.f : __expf(st.m - mn);
+      float pa[4], pb[4];
+      float ps_ = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pa[e] = none ? 0.f : __expf(za[e] - mn);
+        pb[e] = none ? 0.f : __expf(zb[e] - mn);
+        ps_ += pa[e] + pb[e];
+      }
+      st.l = st.l * alpha + q4_sum(ps_);
+      st.m = mn;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.Ot[n][e] *= alpha;
+      }
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Wt[n][e] *= alpha;
+      }
+      stage_v_tile(Va, va, l16, q4);
+      if (has_b) stage_v_tile(Vb, vb, l16, q4);
+      wave_sync_lds();
+      exact_pv(st, Va, pa, l16, q4);
+      if (has_b) exact_pv(st, Vb, pb, l16, q4);
+      wave_sync_lds();
       ta += 2 * kAttWaves;
+      tb += 2 * kAttWaves;
       if (ta < ntile) load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
-      if (tb < ntile) {
-        exact_tile<NQ>(kb, vb, tb * 16, n_ex, qf, scale, st, Wacc, Vt, l16, q4);
-        tb += 2 * kAttWaves;
-        if (tb < ntile) load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
+      if (tb < ntile) load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
+    }
+  }
+
+  // ---- fold the low-rank values into O^T per wave: O^T += VVx^T W^T (linear)
+  if (NRQ > 0 && lr) {
+    v4h wh[NQ], wl[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) split_hl(Wt[s][0], Wt[s][1], Wt[s][2], Wt[s][3], wh[s], wl[s]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int s = 0; s < NRQ; ++s) {
+        v4h av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
+        st.Ot[n] = mfma16(av, wh[s], st.Ot[n]);
+        st.Ot[n] = mfma16(av, wl[s], st.Ot[n]);
       }
     }
   }
 
-  // ---- final phase: common maximum, fixed-order reduction
+  // ---- final phase: common maximum over the waves, fixed-order sum, stores
   if (q4 == 0) {
     wstat[wave * 16 + l16] = st.m;
     wstat[kAttWaves * 16 + wave * 16 + l16] = st.l;
   }
-  lds_barrier();
+  lds_barrier();  // statistics visible; every wave is done with its scratch
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, wstat[w * 16 + l16]);
-  float L = 0.f;
+  const float be = (st.m == -INFINITY) ? 0.f : __expf(st.m - M);
+  float* red = reinterpret_cast<float*>(region);  // [kAttWaves][16 heads][kRedStride]
 #pragma unroll
-  for (int w = 0; w < kAttWaves; ++w) {
-    const float mw = wstat[w * 16 + l16];
-    L += (mw == -INFINITY) ? 0.f : wstat[kAttWaves * 16 + w * 16 + l16] * __expf(mw - M);
-  }
-  float be[4];
-  rows_of((st.m == -INFINITY) ? 0.f : __expf(st.m - M), q4, be);
-  lds_barrier();  // per-wave scratch becomes the reduction buffer
-  float* redO = reinterpret_cast<float*>(region);              // [4][16][kRedStride]
-  float* redW = redO + kAttWaves * 16 * kRedStride;            // [4][16][RQ]
-  {
-    float* dst = redO + wave * 16 * kRedStride;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * kRedStride + 16 * n + l16] = st.O[n][e] * be[e];
-    }
-  }
-  if (NRQ > 0 && lr) {
-    float* dst = redW + wave * 16 * RQ;
-#pragma unroll
-    for (int n = 0; n < NRQ; ++n) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(4 * q4 + e) * RQ + 16 * n + l16] = Wacc[n][e] * be[e];
-    }
+  for (int n = 0; n < 8; ++n) {
+    const float4 v = make_float4(st.Ot[n][0] * be, st.Ot[n][1] * be, st.Ot[n][2] * be, st.Ot[n][3] * be);
+    *reinterpret_cast<float4*>(red + (wave * 16 + l16) * kRedStride + 16 * n + 4 * q4) = v;
   }
   lds_barrier();
-  v4h wh[NQ], wl[NQ];
-  if (NRQ > 0 && lr) {
+  const __amdgpu_buffer_rsrc_t Po = coherent_rsrc(A.part_o + ((int64_t)row0 * A.n_parts + part) * kD, 0xFFFFFFFFu);
+  for (int t = tid; t < G * (kD / 4); t += kAttThreads) {
+    const int g = t / (kD / 4), c4 = t % (kD / 4);
+    float Mg = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < NRQ; ++s) {
-      float4 w = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int lw = 0; lw < kAttWaves; ++lw) {
-        const float4 x = *reinterpret_cast<const float4*>(redW + lw * 16 * RQ + l16 * RQ + 16 * s + 4 * q4);
-        w.x += x.x;
-        w.y += x.y;
-        w.z += x.z;
-        w.w += x.w;
-      }
-      split_hl(w.x, w.y, w.z, w.w, wh[s], wl[s]);
-    }
-  }
-  float Le[4];
-  rows_of(L, q4, Le);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int n = wave + kAttWaves * half;  // output columns 16 n .. 16 n + 15
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kAttWaves; ++w) Mg = fmaxf(Mg, wstat[w * 16 + g]);
+    float Lg = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kAttWaves; ++w) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += redO[w * 16 * kRedStride + (4 * q4 + e) * kRedStride + 16 * n + l16];
+      const float mw = wstat[w * 16 + g];
+      Lg += (mw == -INFINITY) ? 0.f : wstat[kAttWaves * 16 + w * 16 + g] * __expf(mw - Mg);
+      const float4 x = *reinterpret_cast<const float4*>(red + (w * 16 + g) * kRedStride + 4 * c4);
+      o.x += x.x;
+      o.y += x.y;
+      o.z += x.z;
+      o.w += x.w;
     }
-    if (NRQ > 0 && lr) {
-#pragma unroll
-      for (int s = 0; s < NRQ; ++s) {
-        v4h bv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
-        acc = mfma16(wh[s], bv, acc);
-        acc = mfma16(wl[s], bv, acc);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int g = 4 * q4 + e;
-      if (g < G)
-        st_dev(&A.part_o[((int64_t)(row0 + g) * A.n_parts + part) * kD + 16 * n + l16],
-               (Le[e] > 0.f) ? acc[e] / Le[e] : 0.f);
-    }
+    const float inv = (Lg > 0.f) ? 1.f / Lg : 0.f;
+    st_coherent4(Po, (uint32_t)((g * A.n_parts * kD + 4 * c4) * 4),
+                 make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
+    if (c4 == 0) st_dev(&A.part_lse[(int64_t)(row0 + g) * A.n_parts + part], (Lg > 0.f) ? Mg + __logf(Lg) : -INFINITY);
   }
-  if (wave == 0 && q4 == 0 && l16 < G)
-    st_dev(&A.part_lse[(int64_t)(row0 + l16) * A.n_parts + part], (L > 0.f) ? M + __logf(L) : -INFINITY);
 }
 
 template <int NRQ>
@@ -1116,195 +1173,88 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 }
 
 // ----------------------------------------------------------------------------
-// Log-sum-exp combine of the G query rows of one (sequence, KV head) unit by
-// one workgroup.  merge_chunked: 8 rows at a time, 32 lanes per row, 4 columns
-// per lane, online over chunks of 32 parts.  merge_unit: the G x n_parts
-// partials of the unit are contiguous; each of 8 slots of 32 lanes takes an
-// equal contiguous run of them (at most two rows) and issues every load at
-// once, then the slots' sums are combined through LDS.
+// Log-sum-exp merge of the partials of one decode step, inside the launch
 // ----------------------------------------------------------------------------
 
-constexpr int kMergeRun = 32;  // partials per slot in merge_unit's single-issue path
 
-// Buffer loads at device scope (cache policy sc1): they read the device-coherent
-// copy, so they observe data that other workgroups of the same launch wrote with
-// device-scope stores and then published through a counter, without an
-// invalidation of the whole cache.  Reads outside [base, base + bytes) return 0.
-constexpr int kLoadDeviceScope = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kLoadDeviceScope);  // 4 x 32 raw bits
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-}
-__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kLoadDeviceScope));
-}
-
-__device__ __forceinline__ void merge_chunked(const float* part_o, const float* part_lse, int n_parts, int row0,
-                                              int G, f16* out, float* out_lse) {
-  constexpr int kChunk = 32;
-  const int tid = threadIdx.x;
-  const int j = tid & 31;   // lane within the row's 32-lane group: columns 4 j .. 4 j + 3
-  const int grp = tid >> 5;
-  for (int g0 = 0; g0 < G; g0 += kAttThreads / 32) {
-    const int g = g0 + grp;
-    const bool valid = g < G;
-    const int row = row0 + (valid ? g : 0);
-    const float* Lrow = part_lse + (int64_t)row * n_parts;
-    const float* Orow = part_o + (int64_t)row * n_parts * kD + 4 * j;
-    float m = -INFINITY, S = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int pb = 0; pb < n_parts; pb += kChunk) {
-      // every load of the chunk first: its lse values (one per lane) and its partials
-      const int pl = pb + j;
-      const float lj = Lrow[pl < n_parts ? pl : 0];
-      float4 o[kChunk];
+// Log-sum-exp combine of one query row's n_parts partials by one workgroup:
+// 8 slots of 32 lanes (4 columns per lane), slot s taking parts s, s + 8, ...,
+// every load of a round issued at once; the row maximum comes first so the
+// slots' weighted sums add without rescaling, in a fixed order.
+// lds: 8 * kD + 8 + kAttWaves floats.
+constexpr int kMergeRowChunk = 8;  // parts per slot per round
+__device__ __forceinline__ void merge_row(const float* part_o, const float* part_lse, int n_parts, int row,
+                                          f16* out, float* out_lse, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c4 = tid & 31, sl = tid >> 5;
+  float* red = lds;                   // [8][kD]
+  float* redS = lds + 8 * kD;         // [8]
+  float* redM = redS + 8;             // [kAttWaves]
+  const int np = n_parts > 0 ? n_parts : 1;
+  const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row * n_parts * kD, (uint32_t)n_parts * kD * 4);
+  const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row * n_parts, (uint32_t)n_parts * 4);
+  // first round's partials, then the row maximum over every part
+  float4 o[kMergeRowChunk];
+  float l[kMergeRowChunk];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int pk = pb + k < n_parts ? pb + k : 0;
-        o[k] = *reinterpret_cast<const float4*>(Orow + (int64_t)pk * kD);
-      }
-      const float l = (pl < n_parts) ? lj : -INFINITY;
-      float cm = l;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 32));
-      const float mn = fmaxf(m, cm);
-      if (mn == -INFINITY) continue;   // uniform within the row group
-      const float alpha = (m == -INFINITY) ? 0.f : __expf(m - mn);
-      const float w = (l == -INFINITY) ? 0.f : __expf(l - mn);
-      float ws = w;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 32);
-      S = S * alpha + ws;
-      acc.x *= alpha;
-      acc.y *= alpha;
-      acc.z *= alpha;
-      acc.w *= alpha;
-#pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const float wk = (pb + k < n_parts) ? __shfl(w, k, 32) : 0.f;
-        acc.x += wk * o[k].x;
-        acc.y += wk * o[k].y;
-        acc.z += wk * o[k].z;
-        acc.w += wk * o[k].w;
-      }
-      m = mn;
-    }
-    if (valid) {
-      const bool any = S > 0.f;
-      v4h h4;
-      h4[0] = (f16)(any ? acc.x / S : 0.f);
-      h4[1] = (f16)(any ? acc.y / S : 0.f);
-      h4[2] = (f16)(any ? acc.z / S : 0.f);
-      h4[3] = (f16)(any ? acc.w / S : 0.f);
-      *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * j) = h4;
-      if (j == 0) out_lse[row] = any ? m + __logf(S) : -INFINITY;
-    }
+  for (int k = 0; k < kMergeRowChunk; ++k) {
+    const int pp = sl + 8 * k;
+    const int pc = pp < np ? pp : np - 1;
+    o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
+    l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
   }
-}
-
-// lds: 8 * 2 * kD + 2 * 8 floats
-__device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0,
-                                           int G, f16* out, float* out_lse, float* lds) {
-  const int total = G * n_parts;
-  const int L = (total + 7) / 8;
-  if (n_parts < 1 || G > 8 || n_parts > 64 || L > kMergeRun) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // plain loads below: drop stale cached copies
-    merge_chunked(part_o, part_lse, n_parts, row0, G, out, out_lse);
-    return;
-  }
-  const int tid = threadIdx.x, c4 = tid & 31, sl = tid >> 5;
-  float* red = lds;              // [8 slots][2 rows][kD]
-  float* ms = lds + 8 * 2 * kD;  // [8 rows][m, S]
-  const int e0 = sl * L;
-  const int e1 = e0 + L < total ? e0 + L : total;  // this slot's partials [e0, e1)
-  const int ra = (e0 / n_parts) < G ? e0 / n_parts : G - 1;
-  const int rb = ra + 1 < G ? ra + 1 : G - 1;
-  const int bnd = (ra + 1) * n_parts;  // partials below bnd belong to row ra
-  const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row0 * n_parts * kD, (uint32_t)total * kD * 4);
-  const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row0 * n_parts, (uint32_t)total * 4);
-  float4 o[kMergeRun];
-#pragma unroll
-  for (int k = 0; k < kMergeRun; ++k) {
-    int e = e0 + k;
-    e = e < e1 ? e : (e1 > 0 ? e1 - 1 : 0);
-    o[k] = ld_coherent4(Ob, (uint32_t)(e * kD + 4 * c4) * 4u);
-  }
-  const int p0 = c4 < n_parts ? c4 : 0, p1 = c4 + 32 < n_parts ? c4 + 32 : 0;
-  float la0 = ld_coherent(Lb, (uint32_t)(ra * n_parts + p0) * 4u), la1 = ld_coherent(Lb, (uint32_t)(ra * n_parts + p1) * 4u);
-  float lb0 = ld_coherent(Lb, (uint32_t)(rb * n_parts + p0) * 4u), lb1 = ld_coherent(Lb, (uint32_t)(rb * n_parts + p1) * 4u);
-  if (c4 >= n_parts) la0 = lb0 = -INFINITY;
-  if (c4 + 32 >= n_parts) la1 = lb1 = -INFINITY;
-  float ma = fmaxf(la0, la1), mb = fmaxf(lb0, lb1);
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    ma = fmaxf(ma, __shfl_xor(ma, off, 32));
-    mb = fmaxf(mb, __shfl_xor(mb, off, 32));
-  }
-  const float wa0 = la0 == -INFINITY ? 0.f : __expf(la0 - ma), wa1 = la1 == -INFINITY ? 0.f : __expf(la1 - ma);
-  const float wb0 = lb0 == -INFINITY ? 0.f : __expf(lb0 - mb), wb1 = lb1 == -INFINITY ? 0.f : __expf(lb1 - mb);
-  float Sa = wa0 + wa1, Sb = wb0 + wb1;
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) {
-    Sa += __shfl_xor(Sa, off, 32);
-    Sb += __shfl_xor(Sb, off, 32);
-  }
-  float4 acca = make_float4(0.f, 0.f, 0.f, 0.f), accb = acca;
-#pragma unroll
-  for (int k = 0; k < kMergeRun; ++k) {
-    const int e = e0 + k;
-    const bool in_a = e < bnd;
-    const int pp = in_a ? e - ra * n_parts : e - rb * n_parts;  // the same in all 32 lanes of the slot
-    const float src = pp < 32 ? (in_a ? wa0 : wb0) : (in_a ? wa1 : wb1);
-    float w = __shfl(src, pp & 31, 32);
-    w = e < e1 ? w : 0.f;
-    const float wa = in_a ? w : 0.f, wb = in_a ? 0.f : w;
-    acca.x += wa * o[k].x;
-    acca.y += wa * o[k].y;
-    acca.z += wa * o[k].z;
-    acca.w += wa * o[k].w;
-    accb.x += wb * o[k].x;
-    accb.y += wb * o[k].y;
-    accb.z += wb * o[k].z;
-    accb.w += wb * o[k].w;
-  }
-  *reinterpret_cast<float4*>(red + (sl * 2 + 0) * kD + 4 * c4) = acca;
-  *reinterpret_cast<float4*>(red + (sl * 2 + 1) * kD + 4 * c4) = accb;
-  if (c4 == 0 && e0 < total) {
-    // the slot holding a row's first partial publishes that row's max and sum
-    if (ra * n_parts >= e0) {
-      ms[2 * ra] = ma;
-      ms[2 * ra + 1] = Sa;
-    }
-    if (rb != ra && bnd < e1) {
-      ms[2 * rb] = mb;
-      ms[2 * rb + 1] = Sb;
-    }
-  }
+  float m = -INFINITY;
+  for (int pp = tid; pp < n_parts; pp += kAttThreads) m = fmaxf(m, ld_coherent(Lb, (uint32_t)pp * 4u));
+  m = wave_minmax<true>(m);
+  if (lane == 0) redM[wave] = m;
   lds_barrier();
-  const int g = sl;
-  if (g < G) {
-    const int s_lo = (g * n_parts) / L, s_hi = ((g + 1) * n_parts - 1) / L;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s2 = s_lo; s2 <= s_hi; ++s2) {
-      const int which = ((s2 * L) / n_parts == g) ? 0 : 1;
-      const float4 v = *reinterpret_cast<const float4*>(red + (s2 * 2 + which) * kD + 4 * c4);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+#pragma unroll
+  for (int w = 0; w < kAttWaves; ++w) m = fmaxf(m, redM[w]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float S = 0.f;
+  for (int p0 = 0; p0 < n_parts; p0 += 8 * kMergeRowChunk) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int k = 0; k < kMergeRowChunk; ++k) {
+        const int pp = p0 + sl + 8 * k;
+        const int pc = pp < np ? pp : np - 1;
+        o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
+        l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
+      }
     }
-    const float m = ms[2 * g], S = ms[2 * g + 1];
-    const bool any = S > 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeRowChunk; ++k) {
+      const int pp = p0 + sl + 8 * k;
+      const float w = (pp < n_parts && l[k] != -INFINITY) ? __expf(l[k] - m) : 0.f;
+      S += w;
+      acc.x += w * o[k].x;
+      acc.y += w * o[k].y;
+      acc.z += w * o[k].z;
+      acc.w += w * o[k].w;
+    }
+  }
+  *reinterpret_cast<float4*>(red + sl * kD + 4 * c4) = acc;
+  if (c4 == 0) redS[sl] = S;
+  lds_barrier();
+  if (tid < 32) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float St = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const float4 v = *reinterpret_cast<const float4*>(red + s2 * kD + 4 * c4);
+      t.x += v.x;
+      t.y += v.y;
+      t.z += v.z;
+      t.w += v.w;
+      St += redS[s2];
+    }
+    const bool any = St > 0.f;
     v4h h4;
-    h4[0] = (f16)(any ? acc.x / S : 0.f);
-    h4[1] = (f16)(any ? acc.y / S : 0.f);
-    h4[2] = (f16)(any ? acc.z / S : 0.f);
-    h4[3] = (f16)(any ? acc.w / S : 0.f);
-    *reinterpret_cast<v4h*>(out + (int64_t)(row0 + g) * kD + 4 * c4) = h4;
-    if (c4 == 0) out_lse[row0 + g] = any ? m + __logf(S) : -INFINITY;
+    h4[0] = (f16)(any ? t.x / St : 0.f);
+    h4[1] = (f16)(any ? t.y / St : 0.f);
+    h4[2] = (f16)(any ? t.z / St : 0.f);
+    h4[3] = (f16)(any ? t.w / St : 0.f);
+    *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * c4) = h4;
+    if (tid == 0) out_lse[row] = any ? m + __logf(St) : -INFINITY;
   }
 }
 
@@ -1331,7 +1281,8 @@ struct DecodeArgs {
   float* out_lse;
   int n_units;
   int n_route;           // units routed in this launch (0 when top_k == 0)
-  int n_items;           // n_route + n_units * att.items_per_unit: the grid size
+  int n_part_end;        // n_route + n_units * att.items_per_unit: first merge item
+  int n_items;           // n_part_end + n_units * G merge items (one per query row): the grid size
 };
 
 constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
@@ -1349,7 +1300,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
     route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
-  } else if (t < D.n_items) {
+  } else if (t < D.n_part_end) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
     int slot = kSlotLookup;
@@ -1374,16 +1325,29 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
       slot = sh_slot;
     }
     attend_part<NRQ>(P, Bt, D.att, u, p, slot, smem);
-    // count this part once its partial is stored; the unit's last part merges
+    // count this part once its partial is stored
     stores_done();
     __syncthreads();
-    if (tid == 0) sh_flag = (atomicAdd(&D.unit_done[u], 1u) == (uint32_t)(D.att.items_per_unit - 1)) ? 1u : 0u;
-    lds_barrier();
-    if (sh_flag) {
-      const int b = u / Bt.Hkv, h = u % Bt.Hkv;
-      merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse,
-                 reinterpret_cast<float*>(smem));
+    if (tid == 0) atomicAdd(&D.unit_done[u], 1u);
+  } else if (t < D.n_items) {
+    // merge item: one query row of a unit, once all of the unit's parts are stored
+    const int it = t - D.n_part_end;
+    const int u = it / Bt.G, g = it % Bt.G;
+    if (tid == 0) {
+      const uint32_t want = (uint32_t)D.att.items_per_unit;
+      unsigned n = 0;
+      uint32_t v = ld_dev(&D.unit_done[u]);
+      while (v < want && n < kRouteWaitLimit) {
+        __builtin_amdgcn_s_sleep(2);
+        v = ld_dev(&D.unit_done[u]);
+        ++n;
+      }
+      if (v < want) atomicOr(&D.ctrl[2], 1u);
     }
+    lds_barrier();
+    const int b = u / Bt.Hkv, h = u % Bt.Hkv;
+    merge_row(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G + g, D.out, D.out_lse,
+              reinterpret_cast<float*>(smem));
   }
   // the last workgroup to finish zeroes the control words for the next launch
   __syncthreads();
@@ -1842,8 +1806,10 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   D.out_lse = out_lse;
   D.n_units = units;
   D.n_route = top_k > 0 ? units : 0;
-  const int64_t items = (int64_t)D.n_route + (int64_t)units * n_parts;
+  const int64_t part_end = (int64_t)D.n_route + (int64_t)units * n_parts;
+  const int64_t items = part_end + (int64_t)units * (batch->n_q_heads / pool->n_kv_heads);
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
+  D.n_part_end = (int)part_end;
   D.n_items = (int)items;
   size_t shm = (size_t)att_lds_bytes(a.rq);
   const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
