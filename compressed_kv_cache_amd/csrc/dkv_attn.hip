@@ -93,6 +93,7 @@ struct AttnArgs {
   int block_mode;      // bit 0: low-rank rows of a block, bit 1: its residual rows
   int n_win_parts;
   int win_chunk;
+  int win_tile_stride; // > 0: block part p also attends window tiles p, p + stride, ... (16 rows each)
   int items_per_unit;
   int rq;              // augmented rank rounded up to 16 (0 without low-rank rows)
   float scale;
@@ -388,7 +389,8 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
                                            float* scores, int32_t* slots_out, uint32_t* lds,
                                            RouteShared<NT / 64>& sh) {
   constexpr int NW = NT / 64;
-  static_assert(NT == 256, "route_unit: one histogram bin per thread");
+  static_assert(NT == 256 || NT == 512, "route_unit: 256 histogram bins over the first 4 waves");
+  constexpr int kBinWaves = 256 / 64;
   uint32_t* wsum = sh.wsum;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
@@ -497,7 +499,7 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
         hi = fmaxf(hi, sc);
       }
     }
-    hist[tid] = 0u;  // NT == 256 bins
+    if (tid < 256) hist[tid] = 0u;
     lo = wave_minmax<false>(lo);
     hi = wave_minmax<true>(hi);
     if (lane == 0) {
@@ -525,14 +527,14 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
     for (int jj = tid; jj < N; jj += NT) atomicAdd(&hist[bin_of(keys[jj])], 1u);
     lds_barrier();
     // counts of bins >= 255 - tid (a scan of the bins in descending order)
-    const uint32_t hb = hist[255 - tid];
+    const uint32_t hb = tid < 256 ? hist[255 - tid] : 0u;
     uint32_t incl = wave_incl_scan(hb);
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63 && wave < kBinWaves) wsum[wave] = incl;
     lds_barrier();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) incl += (w < wave) ? wsum[w] : 0u;
+    for (int w = 0; w < kBinWaves; ++w) incl += (w < wave) ? wsum[w] : 0u;
     const uint32_t excl = incl - hb;
-    if (excl < (uint32_t)keff && incl >= (uint32_t)keff) {
+    if (tid < 256 && excl < (uint32_t)keff && incl >= (uint32_t)keff) {
       sh.digit = 255u - (uint32_t)tid;
       sh.above = excl;
     }
@@ -700,6 +702,56 @@ __device__ __forceinline__ void stage_v_tile(f16* Vt, const v8h (&vx)[4], int l1
   }
 }
 
+// One softmax step over two 16-row exact tiles (b optional): scores, a common
+// maximum, the rescale of the state and of the low-rank accumulator, and PV.
+// rows_a / rows_b: valid rows of each tile (the rest are masked out).
+template <int NQ>
+__device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h (&ka)[4], const v8h (&va)[4],
+                                           const v8h (&kb)[4], const v8h (&vb)[4], int rows_a, int rows_b,
+                                           bool has_b, const v4h (&qf)[4][2], float scale, f16* Va, f16* Vb,
+                                           int l16, int q4) {
+  const v4f Sa = exact_scores(ka, qf);
+  const v4f Sb = exact_scores(kb, qf);
+  float za[4], zb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    za[e] = (4 * q4 + e < rows_a) ? Sa[e] * scale : -INFINITY;
+    zb[e] = (has_b && 4 * q4 + e < rows_b) ? Sb[e] * scale : -INFINITY;
+  }
+  float tm = fmaxf(fmaxf(fmaxf(za[0], za[1]), fmaxf(za[2], za[3])),
+                   fmaxf(fmaxf(zb[0], zb[1]), fmaxf(zb[2], zb[3])));
+  tm = q4_max(tm);
+  const float mn = fmaxf(st.m, tm);
+  const bool none = (mn == -INFINITY);
+  const float alpha = none ? 1.f : __expf(st.m - mn);
+  float pa[4], pb[4];
+  float ps_ = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pa[e] = none ? 0.f : __expf(za[e] - mn);
+    pb[e] = none ? 0.f : __expf(zb[e] - mn);
+    ps_ += pa[e] + pb[e];
+  }
+  st.l = st.l * alpha + q4_sum(ps_);
+  st.m = mn;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.Ot[n][e] *= alpha;
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Wt[n][e] *= alpha;
+  }
+  stage_v_tile(Va, va, l16, q4);
+  if (has_b) stage_v_tile(Vb, vb, l16, q4);
+  wave_sync_lds();
+  exact_pv(st, Va, pa, l16, q4);
+  if (has_b) exact_pv(st, Vb, pb, l16, q4);
+  wave_sync_lds();
+}
+
 __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, int tile, int ntile, int n_ex,
                                                 v8h (&kx)[4], v8h (&vx)[4], int l16, int q4) {
   // rows past n_ex read row n_ex - 1: their scores are masked to -inf and their
@@ -715,11 +767,24 @@ __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, in
 
 // NRQ = number of 16-wide column tiles of the augmented rank r + 1 (0 without
 // low-rank rows), a template parameter so that every loop over them is static.
-constexpr int kSlotLookup = -0x7fffffff;  // attend_part: look the slot up from idx and the block table
+// Pool slot of routed block p of unit u from the routed indices and the block
+// table (-1: none); the standalone attention kernels use it.
+__device__ __forceinline__ int lookup_slot(const BatchArgs& Bt, const AttnArgs& A, int u, int p) {
+  const int b = u / Bt.Hkv;
+  int nb = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
+  nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
+  const int j = A.idx[(int64_t)u * A.top_k + p];
+  return (j >= 0 && j < nb) ? Bt.table[(int64_t)b * Bt.mb + j] : -1;
+}
 
-template <int NRQ>
+// One part of a decode step for unit u = (sequence, KV head), by the whole
+// workgroup.  Part p < n_block_parts is routed block p: its low-rank rows and
+// residual rows, and, when win_tile_stride > 0, the window's 16-row tiles p,
+// p + stride, ..., which are attended first, before get_slot() (which may wait
+// for the routing) is called.  Other parts are window chunks of win_chunk rows.
+template <int NRQ, class SlotFn>
 __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& Bt, const AttnArgs& A, int u, int p,
-                                            int slot_in, unsigned char* smem) {
+                                            SlotFn&& get_slot, unsigned char* smem) {
   constexpr int NQ = NRQ > 0 ? NRQ : 1;
   constexpr int RQ = 16 * NRQ;
   constexpr int kVVChunks = (16 * NQ * 16 + kAttThreads - 1) / kAttThreads;
@@ -743,21 +808,59 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
   }
 
-  // ---- what this part covers (uniform over the workgroup)
+  // ---- LDS carve-up
+  float* qt = reinterpret_cast<float*>(smem);                     // [16][RQ]  V_K q and q.a_k
+  f16* vvx = reinterpret_cast<f16*>(qt + 16 * RQ);                // [RQ][kVStride]  [V_V ; a_v ; *]
+  float* wstat = reinterpret_cast<float*>(vvx + RQ * kVStride);   // m [4][16], l [4][16]
+  unsigned char* region = reinterpret_cast<unsigned char*>(wstat + 2 * kAttWaves * 16);
+  constexpr int TS = RQ + 4;
+  unsigned char* my = region + wave * att_scratch_bytes(RQ);
+  uint32_t* wmask = reinterpret_cast<uint32_t*>(my + att_scratch_bytes(RQ) - 32);
+  const float scale = A.scale;
+
+  ExState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.Ot[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v4f Wt[NQ];  // W^T[j = 16 n + 4 q4 + e][head l16] = sum over positions of Ux[pos][j] p[pos][head]
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) Wt[n] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  int wl = Bt.wlen ? Bt.wlen[b] : Bt.W;
+  wl = wl < 0 ? 0 : (wl > Bt.W ? Bt.W : wl);
+  const int64_t win_base = (((int64_t)b * Bt.Hkv + h) * Bt.W) * kD;
+
+  // ---- window tiles owned by a routed-block part: exact rows that do not
+  //      depend on the routing, attended while it may still be running
+  bool any = false;
+  if (p < A.n_block_parts && A.win_tile_stride > 0) {
+    const int n_wt = (wl + 15) >> 4;
+    any = p < n_wt;  // uniform
+    f16* Va = reinterpret_cast<f16*>(my);
+    f16* Vb = Va + 16 * kVStride;
+    v8h ka[4], va[4], kb[4], vb[4];
+    for (int i = wave; p + A.win_tile_stride * i < n_wt; i += 2 * kAttWaves) {
+      const int wa = p + A.win_tile_stride * i, wb = p + A.win_tile_stride * (i + kAttWaves);
+      const bool has_b = wb < n_wt;
+      const int ra = wl - 16 * wa < 16 ? wl - 16 * wa : 16;
+      const int rb = has_b ? (wl - 16 * wb < 16 ? wl - 16 * wb : 16) : 0;
+      load_exact_tile(Bt.wk + win_base + (int64_t)16 * wa * kD, Bt.wv + win_base + (int64_t)16 * wa * kD, 0, 1, ra,
+                      ka, va, l16, q4);
+      load_exact_tile(Bt.wk + win_base + (int64_t)16 * (has_b ? wb : wa) * kD,
+                      Bt.wv + win_base + (int64_t)16 * (has_b ? wb : wa) * kD, 0, 1, has_b ? rb : ra, kb, vb, l16, q4);
+      exact_pair<NQ>(st, Wt, ka, va, kb, vb, ra, rb, has_b, qf, scale, Va, Vb, l16, q4);
+    }
+  }
+
+  // ---- what else this part covers (uniform over the workgroup)
   bool lr = false;
   int n_ex = 0;
   const f16* exk = nullptr;
   const f16* exv = nullptr;
   int slot = -1;
   if (p < A.n_block_parts) {
-    if (slot_in != kSlotLookup) {
-      slot = slot_in;  // routed pool slot, or -1
-    } else {
-      int nb = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
-      nb = nb < 0 ? 0 : (nb > Bt.mb ? Bt.mb : nb);
-      const int j = A.idx[(int64_t)u * A.top_k + p];
-      if (j >= 0 && j < nb) slot = Bt.table[(int64_t)b * Bt.mb + j];
-    }
+    slot = get_slot();  // routed pool slot, or -1
     if (slot >= P.n_slots) slot = -1;
     if (slot >= 0) {
       lr = (A.block_mode & 1) != 0;
@@ -769,20 +872,17 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
   } else {
     const int s = p - A.n_block_parts;
-    int wl = Bt.wlen ? Bt.wlen[b] : Bt.W;
-    wl = wl < 0 ? 0 : (wl > Bt.W ? Bt.W : wl);
     const int start = s * A.win_chunk;
     const int end = (start + A.win_chunk < wl) ? start + A.win_chunk : wl;
     if (end > start) {
       n_ex = end - start;
-      const int64_t base = (((int64_t)b * Bt.Hkv + h) * Bt.W + start) * kD;
-      exk = Bt.wk + base;
-      exv = Bt.wv + base;
+      exk = Bt.wk + win_base + (int64_t)start * kD;
+      exv = Bt.wv + win_base + (int64_t)start * kD;
     }
   }
 
   const int part = A.part_offset + p;
-  if (!lr && n_ex == 0) {
+  if (!lr && n_ex == 0 && !any) {
     for (int t = tid; t < G * kD; t += kAttThreads) {
       const int g = t / kD, d = t % kD;
       st_dev(&A.part_o[((int64_t)(row0 + g) * A.n_parts + part) * kD + d], 0.f);
@@ -790,24 +890,8 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     if (tid < G) st_dev(&A.part_lse[(int64_t)(row0 + tid) * A.n_parts + part], -INFINITY);
     return;
   }
-
-  // ---- LDS carve-up
-  float* qt = reinterpret_cast<float*>(smem);                     // [16][RQ]  V_K q and q.a_k
-  f16* vvx = reinterpret_cast<f16*>(qt + 16 * RQ);                // [RQ][kVStride]  [V_V ; a_v ; *]
-  float* wstat = reinterpret_cast<float*>(vvx + RQ * kVStride);   // m [4][16], l [4][16]
-  unsigned char* region = reinterpret_cast<unsigned char*>(wstat + 2 * kAttWaves * 16);
-  constexpr int TS = RQ + 4;
-  unsigned char* my = region + wave * att_scratch_bytes(RQ);
-  uint32_t* wmask = reinterpret_cast<uint32_t*>(my + att_scratch_bytes(RQ) - 32);
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
-  const float scale = A.scale;
-
-  ExState st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int n = 0; n < 8; ++n) st.Ot[n] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // ---- issue the loads, in the order of use
   v4h ua[kLRTilesPerWave][NQ];
@@ -885,9 +969,6 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
 
   // ---- low-rank set-up: residual-position mask (per wave), VVx, VKx q
-  v4f Wt[NQ];  // W^T[j = 16 n + 4 q4 + e][head l16] = sum over positions of Ux[pos][j] p[pos][head]
-#pragma unroll
-  for (int n = 0; n < NQ; ++n) Wt[n] = (v4f){0.f, 0.f, 0.f, 0.f};
   if (NRQ > 0 && lr) {
     if (lane < 8) wmask[lane] = 0u;
     wave_sync_lds();
@@ -960,18 +1041,26 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     for (int k = 0; k < kLRTilesPerWave; ++k)
       tm = fmaxf(tm, fmaxf(fmaxf(zz[k][0], zz[k][1]), fmaxf(zz[k][2], zz[k][3])));
     tm = q4_max(tm);
+    const float mn = fmaxf(st.m, tm);
+    const bool none = (mn == -INFINITY);
+    const float alpha = none ? 1.f : __expf(st.m - mn);
     float pe[kLRTilesPerWave][4];
     float ps_ = 0.f;
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[k][e] = (tm == -INFINITY) ? 0.f : __expf(zz[k][e] - tm);
+        pe[k][e] = none ? 0.f : __expf(zz[k][e] - mn);
         ps_ += pe[k][e];
       }
     }
-    st.m = tm;  // the low-rank rows come first: nothing to rescale
-    st.l = q4_sum(ps_);
+    st.l = st.l * alpha + q4_sum(ps_);
+    st.m = mn;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.Ot[n][e] *= alpha;  // (W^T is still zero here)
+    }
     wave_sync_lds();
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
@@ -995,46 +1084,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     f16* Vb = Va + 16 * kVStride;
     while (ta < ntile) {
       const bool has_b = tb < ntile;  // uniform over the wave
-      const v4f Sa = exact_scores(ka, qf);
-      const v4f Sb = exact_scores(kb, qf);
-      float za[4], zb[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        za[e] = (ta * 16 + 4 * q4 + e < n_ex) ? Sa[e] * scale : -INFINITY;
-        zb[e] = (has_b && tb * 16 + 4 * q4 + e < n_ex) ? Sb[e] * scale : -INFINITY;
-      }
-      float tm = fmaxf(fmaxf(fmaxf(za[0], za[1]), fmaxf(za[2], za[3])),
-                       fmaxf(fmaxf(zb[0], zb[1]), fmaxf(zb[2], zb[3])));
-      tm = q4_max(tm);
-      const float mn = fmaxf(st.m, tm);
-      const bool none = (mn == -INFINITY);
-      const float alpha = none ? 1.f : __expf(st.m - mn);
-      float pa[4], pb[4];
-      float ps_ = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pa[e] = none ? 0.f : __expf(za[e] - mn);
-        pb[e] = none ? 0.f : __expf(zb[e] - mn);
-        ps_ += pa[e] + pb[e];
-      }
-      st.l = st.l * alpha + q4_sum(ps_);
-      st.m = mn;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.Ot[n][e] *= alpha;
-      }
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Wt[n][e] *= alpha;
-      }
-      stage_v_tile(Va, va, l16, q4);
-      if (has_b) stage_v_tile(Vb, vb, l16, q4);
-      wave_sync_lds();
-      exact_pv(st, Va, pa, l16, q4);
-      if (has_b) exact_pv(st, Vb, pb, l16, q4);
-      wave_sync_lds();
+      exact_pair<NQ>(st, Wt, ka, va, kb, vb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, scale, Va, Vb, l16, q4);
       ta += 2 * kAttWaves;
       tb += 2 * kAttWaves;
       if (ta < ntile) load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
@@ -1106,7 +1156,8 @@ template <int NRQ>
 __global__ __launch_bounds__(kAttThreads, 2) void k_attend(PoolArgs P, BatchArgs Bt, AttnArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int item = blockIdx.x;
-  attend_part<NRQ>(P, Bt, A, item / A.items_per_unit, item % A.items_per_unit, kSlotLookup, smem);
+  const int u = item / A.items_per_unit, p = item % A.items_per_unit;
+  attend_part<NRQ>(P, Bt, A, u, p, [&]() { return lookup_slot(Bt, A, u, p); }, smem);
 }
 
 // ----------------------------------------------------------------------------
@@ -1178,17 +1229,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 
 
 // Log-sum-exp combine of one query row's n_parts partials by one workgroup:
-// 8 slots of 32 lanes (4 columns per lane), slot s taking parts s, s + 8, ...,
-// every load of a round issued at once; the row maximum comes first so the
-// slots' weighted sums add without rescaling, in a fixed order.
-// lds: 8 * kD + 8 + kAttWaves floats.
+// kMergeSlots slots of 32 lanes (4 columns per lane), slot s taking parts s,
+// s + kMergeSlots, ..., every load of a round issued at once; the row maximum
+// comes first so the slots' weighted sums add without rescaling, in a fixed
+// order.  lds: kMergeSlots * (kD + 1) + kAttWaves floats.
+constexpr int kMergeSlots = kAttThreads / 32;
 constexpr int kMergeRowChunk = 8;  // parts per slot per round
 __device__ __forceinline__ void merge_row(const float* part_o, const float* part_lse, int n_parts, int row,
                                           f16* out, float* out_lse, float* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c4 = tid & 31, sl = tid >> 5;
-  float* red = lds;                   // [8][kD]
-  float* redS = lds + 8 * kD;         // [8]
-  float* redM = redS + 8;             // [kAttWaves]
+  float* red = lds;                           // [kMergeSlots][kD]
+  float* redS = lds + kMergeSlots * kD;       // [kMergeSlots]
+  float* redM = redS + kMergeSlots;           // [kAttWaves]
   const int np = n_parts > 0 ? n_parts : 1;
   const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row * n_parts * kD, (uint32_t)n_parts * kD * 4);
   const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row * n_parts, (uint32_t)n_parts * 4);
@@ -1197,7 +1249,7 @@ __device__ __forceinline__ void merge_row(const float* part_o, const float* part
   float l[kMergeRowChunk];
 #pragma unroll
   for (int k = 0; k < kMergeRowChunk; ++k) {
-    const int pp = sl + 8 * k;
+    const int pp = sl + kMergeSlots * k;
     const int pc = pp < np ? pp : np - 1;
     o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
     l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
@@ -1211,11 +1263,11 @@ __device__ __forceinline__ void merge_row(const float* part_o, const float* part
   for (int w = 0; w < kAttWaves; ++w) m = fmaxf(m, redM[w]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float S = 0.f;
-  for (int p0 = 0; p0 < n_parts; p0 += 8 * kMergeRowChunk) {
+  for (int p0 = 0; p0 < n_parts; p0 += kMergeSlots * kMergeRowChunk) {
     if (p0 > 0) {
 #pragma unroll
       for (int k = 0; k < kMergeRowChunk; ++k) {
-        const int pp = p0 + sl + 8 * k;
+        const int pp = p0 + sl + kMergeSlots * k;
         const int pc = pp < np ? pp : np - 1;
         o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
         l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
@@ -1223,7 +1275,7 @@ __device__ __forceinline__ void merge_row(const float* part_o, const float* part
     }
 #pragma unroll
     for (int k = 0; k < kMergeRowChunk; ++k) {
-      const int pp = p0 + sl + 8 * k;
+      const int pp = p0 + sl + kMergeSlots * k;
       const float w = (pp < n_parts && l[k] != -INFINITY) ? __expf(l[k] - m) : 0.f;
       S += w;
       acc.x += w * o[k].x;
@@ -1239,7 +1291,7 @@ __device__ __forceinline__ void merge_row(const float* part_o, const float* part
     float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
     float St = 0.f;
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
+    for (int s2 = 0; s2 < kMergeSlots; ++s2) {
       const float4 v = *reinterpret_cast<const float4*>(red + s2 * kD + 4 * c4);
       t.x += v.x;
       t.y += v.y;
@@ -1275,7 +1327,7 @@ struct DecodeArgs {
   AttnArgs att;
   int32_t* idx;          // [units][top_k] routed logical blocks
   int32_t* slots;        // [units][top_k] routed pool slots (-1: none); kSlotPending until routed
-  uint32_t* ctrl;        // [0] ticket, [1] finished workgroups, [2] sticky wait-timeout flag
+  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, queue counters
   uint32_t* unit_done;   // [units] parts finished
   f16* out;
   float* out_lse;
@@ -1286,6 +1338,10 @@ struct DecodeArgs {
 };
 
 constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
+constexpr int kQueues = 8;                      // one work queue per XCD
+constexpr int kQueueStride = 64;                // words between queue counters (separate 256-byte lines)
+constexpr int kCtrlQueue = 64;                  // first queue counter
+constexpr int kCtrlHeaderBytes = 4096;          // control words: [0..63] misc, then the queue counters
 
 template <int NRQ>
 __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
@@ -1294,18 +1350,50 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   __shared__ uint32_t sh_ticket, sh_flag;
   __shared__ int32_t sh_slot;
   const int tid = threadIdx.x;
-  if (tid == 0) sh_ticket = atomicAdd(&D.ctrl[0], 1u);
+  // Work comes from one queue per XCD (the units u with u % 8 == x go to queue
+  // x), so the queue counters are contended by few workgroups and a unit's
+  // hand-offs tend to stay within one XCD.  A workgroup takes from its own
+  // XCD's queue and, when that is empty, from the next ones.  Each queue holds
+  // its units' routings, then their parts, then their merges: every wait is on
+  // an item that comes earlier in some queue and so is already taken by a
+  // running workgroup.
+  if (tid == 0) {
+    const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
+    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = Bt.G;
+    uint32_t item = 0xFFFFFFFFu;
+    for (int k = 0; k < kQueues && item == 0xFFFFFFFFu; ++k) {
+      const int x = (x0 + k) & (kQueues - 1);
+      const int nx = D.n_units > x ? (D.n_units - x + kQueues - 1) / kQueues : 0;
+      const uint32_t size = (uint32_t)(nx * (R + P + G));
+      if (size == 0u) continue;
+      const uint32_t i = atomicAdd(&D.ctrl[kCtrlQueue + x * kQueueStride], 1u);
+      if (i >= size) continue;
+      // queue position -> launch-wide item index: routes, then parts, then merges
+      if (i < (uint32_t)(R * nx)) {
+        item = (uint32_t)(x + kQueues * (int)i);
+      } else if (i < (uint32_t)(R * nx + nx * P)) {
+        const int j = (int)i - R * nx;
+        item = (uint32_t)(D.n_route + (x + kQueues * (j / P)) * P + j % P);
+      } else {
+        const int j = (int)i - R * nx - nx * P;
+        item = (uint32_t)(D.n_part_end + (x + kQueues * (j / G)) * G + j % G);
+      }
+    }
+    sh_ticket = item;
+  }
   lds_barrier();
   const int t = (int)sh_ticket;
-  if (t < D.n_route) {
+  if (t < 0) {
+    // no item (cannot happen: the launch has exactly one workgroup per item)
+  } else if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
     route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
   } else if (t < D.n_part_end) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
-    int slot = kSlotLookup;
-    if (p < D.att.n_block_parts) {
-      // wait (bounded) until the unit's routing has written this part's pool slot
+    // the routed slot of a block part: wait (bounded) until the unit's routing
+    // has written it; called after the part's window tiles are done
+    auto get_slot = [&]() {
       if (tid == 0) {
         const int32_t* sp = &D.slots[(int64_t)u * D.att.top_k + p];
         unsigned n = 0;
@@ -1322,9 +1410,9 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
         sh_slot = v - kSlotCode;
       }
       lds_barrier();
-      slot = sh_slot;
-    }
-    attend_part<NRQ>(P, Bt, D.att, u, p, slot, smem);
+      return (int)sh_slot;
+    };
+    attend_part<NRQ>(P, Bt, D.att, u, p, get_slot, smem);
     // count this part once its partial is stored
     stores_done();
     __syncthreads();
@@ -1349,16 +1437,18 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
     merge_row(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G + g, D.out, D.out_lse,
               reinterpret_cast<float*>(smem));
   }
-  // the last workgroup to finish zeroes the control words for the next launch
-  __syncthreads();
-  if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - 1)) ? 1u : 0u;
-  lds_barrier();
-  if (sh_flag) {
-    for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
-    for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
-    if (tid == 0) {
-      D.ctrl[0] = 0u;
-      D.ctrl[1] = 0u;
+  // The last merge to finish zeroes the control words for the next launch:
+  // merges start only after all of their unit's parts are stored, and every
+  // part only after its routing, so no other item still uses them.
+  if (t >= D.n_part_end) {
+    __syncthreads();
+    if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - D.n_part_end - 1)) ? 1u : 0u;
+    lds_barrier();
+    if (sh_flag) {
+      for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
+      for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
+      if (tid < kQueues) D.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
+      if (tid == 0) D.ctrl[1] = 0u;
     }
   }
 }
@@ -1554,6 +1644,7 @@ dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* i
   a.n_block_parts = n_block_parts;
   a.block_mode = block_mode;
   a.n_win_parts = n_win_parts;
+  a.win_tile_stride = 0;
   a.win_chunk = win_chunk;
   a.items_per_unit = per_unit;
   a.rq = (n_block_parts > 0 && (block_mode & 1)) ? rq_of(P->rank) : 0;
@@ -1601,9 +1692,9 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) 
   WsLayout w;
   const size_t B = (size_t)batch->batch;
   const size_t units = B * (size_t)pool->n_kv_heads;
-  const size_t n_parts = (size_t)top_k + (size_t)decode_win_parts(batch->window);
+  const size_t n_parts = top_k > 0 ? (size_t)top_k : (size_t)decode_win_parts(batch->window);
   const size_t rows = B * (size_t)batch->n_q_heads;
-  w.unit_done = 256;
+  w.unit_done = kCtrlHeaderBytes;
   w.slots = w.unit_done + align256(units * 4);
   w.ctrl_bytes = w.slots + align256(units * (size_t)top_k * 4);
   w.idx = w.ctrl_bytes;
@@ -1778,7 +1869,9 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
 
   const hipStream_t st = (hipStream_t)stream;
   const WsLayout w = decode_layout(pool, batch, top_k);
-  const int n_win = decode_win_parts(batch->window);
+  // with routing, each routed-block part also takes its share of the window;
+  // without, the window comes in chunks of kWinChunk rows
+  const int n_win = top_k > 0 ? 0 : decode_win_parts(batch->window);
   const int n_parts = top_k + n_win;
   const int units = batch->batch * pool->n_kv_heads;
   unsigned char* ws = (unsigned char*)workspace;
@@ -1791,6 +1884,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   a.block_mode = 3;
   a.n_win_parts = n_win;
   a.win_chunk = kWinChunk;
+  a.win_tile_stride = top_k;
   a.items_per_unit = n_parts;
   a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
   a.scale = scale;
