@@ -88,11 +88,11 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest: str):
-    """HBM bytes per k_decode launch (read + written, scaled by the copy-kernel
-    calibration) from the committed rocprofv3 PMC summary, or None when the
-    kernel source changed since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", "k_decode_traffic_stack64k_b4.json")
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch of `kernel` (read + written, scaled by the
+    copy-kernel calibration) from the committed rocprofv3 PMC summary, or None
+    when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic_stack64k_b4.json")
     try:
         with open(p) as f:
             t = json.load(f)
@@ -145,6 +145,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-layer-batched", action="store_true",
+                    help="skip the mode that runs every layer's decode in one launch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (PMC scaling reference)")
     ap.add_argument("--quiet", action="store_true")
@@ -304,17 +306,78 @@ def main() -> int:
         ms_graph = t_start.elapsed_time(t_end) / args.steps
         log(f"hipGraph: {ms_graph:.4f} ms/step")
 
-    best_ms = ms_eager if ms_graph is None else min(ms_eager, ms_graph)
-    mode = "hipgraph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"
+    # ---- every layer's decode step in ONE layer-batched launch (k_decode_layers)
+    ms_lb = ms_lb_graph = lb_kernel_ms = None
+    if not args.no_layer_batched:
+        run = lib.Layers(pools, batches, K, wl.scale)
+        for _ in range(args.warmup):
+            run.run()
+        torch.cuda.synchronize()
+        for i in range(n_layers):
+            assert torch.equal(run.outs[i], ref_out[i]) and torch.equal(run.lses[i], ref_lse[i]) and \
+                torch.equal(run.idxs[i], idxs[i]), f"layer-batched layer {i} differs from per-layer decode"
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(hold)
+        for s in range(args.steps):
+            e0[s].record()
+            run.run()
+            e1[s].record()
+        torch.cuda.synchronize()
+        lb = np.array([e0[s].elapsed_time(e1[s]) for s in range(args.steps)])
+        lb_kernel_ms = float(lb.mean())
+        ms_lb = float(e0[0].elapsed_time(e1[-1])) / args.steps
+        log(f"layer-batched: {ms_lb:.4f} ms/step; k_decode_layers {lb_kernel_ms * 1e3:.2f} us per launch "
+            f"(p10 {np.percentile(lb, 10) * 1e3:.2f}, p90 {np.percentile(lb, 90) * 1e3:.2f})")
+        assert run.timeout_flag() == 0, "a wait in k_decode_layers timed out"
+        for i in range(n_layers):
+            assert torch.equal(run.outs[i], ref_out[i]), "layer-batched steps are not bit-identical"
+        if not args.no_graph:
+            g2 = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                run.run(cs)
+            torch.cuda.current_stream().wait_stream(cs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g2):
+                run.run(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            for rep in range(3):
+                for o in run.outs:
+                    o.zero_()
+                g2.replay()
+                torch.cuda.synchronize()
+                for i in range(n_layers):
+                    assert torch.equal(run.outs[i], ref_out[i]), f"layer-batched replay {rep} differs"
+            for _ in range(args.warmup):
+                g2.replay()
+            torch.cuda.synchronize()
+            t_start.record()
+            for _ in range(args.steps):
+                g2.replay()
+            t_end.record()
+            torch.cuda.synchronize()
+            ms_lb_graph = t_start.elapsed_time(t_end) / args.steps
+            log(f"layer-batched hipGraph: {ms_lb_graph:.4f} ms/step")
+
+    modes = {"per_layer_eager": ms_eager, "per_layer_hipgraph": ms_graph,
+             "layer_batched_eager": ms_lb, "layer_batched_hipgraph": ms_lb_graph}
+    mode = min((k for k in modes if modes[k] is not None), key=lambda k: modes[k])
+    best_ms = modes[mode]
     qps = queries_per_step / (best_ms * 1e-3)
     gbps = step_bytes / (best_ms * 1e-3) / 1e9
-    launch_bytes = step_bytes / n_layers                  # one decode kernel per layer
-    # the roofline uses the kernel duration measured with hipEvents around every
-    # decode kernel in the timed eager steps (kernels back to back, as in a replay)
-    kern_ms = kernel_ms
-    kernel_gbps = launch_bytes / (kern_ms * 1e-3) / 1e9
     digest = source_digest()
-    traffic = measured_traffic(digest)
+    if mode.startswith("layer_batched"):
+        # one k_decode_layers launch processes the whole step
+        kernel_name, launch_bytes, kern_ms = "k_decode_layers", step_bytes, lb_kernel_ms
+    else:
+        # one k_decode launch per layer; duration from the events around every
+        # decode kernel in the timed eager steps (kernels back to back, as in a replay)
+        kernel_name, launch_bytes, kern_ms = "k_decode", step_bytes / n_layers, kernel_ms
+    kernel_gbps = launch_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(kernel_name, digest)
 
     res = {
         "metric": METRIC,
@@ -339,10 +402,10 @@ def main() -> int:
         "hbm_frac": gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "queries_per_step": queries_per_step,
-        "ms_per_step_eager": ms_eager,
-        "ms_per_step_graph": ms_graph,
-        "kernel_us_per_layer": kern_ms * 1e3,
-        "roofline": {"bound": "hbm", "kernel": "k_decode", "achieved": kernel_gbps,
+        "ms_per_step_by_mode": modes,
+        "k_decode_us_per_layer": kernel_ms * 1e3,
+        "k_decode_layers_us_per_launch": None if lb_kernel_ms is None else lb_kernel_ms * 1e3,
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kernel_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes,
                      "avg_launch_us": kern_ms * 1e3},

@@ -1343,48 +1343,15 @@ constexpr int kQueueStride = 64;                // words between queue counters 
 constexpr int kCtrlQueue = 64;                  // first queue counter
 constexpr int kCtrlHeaderBytes = 4096;          // control words: [0..63] misc, then the queue counters
 
+// One work item of a fused decode step: t < n_route routes unit t; then
+// the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merges
+// (u, g).  sh_slot: a shared word of the calling workgroup.
 template <int NRQ>
-__global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ RouteShared<kAttWaves> rsh;
-  __shared__ uint32_t sh_ticket, sh_flag;
-  __shared__ int32_t sh_slot;
+__device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& Bt, const DecodeArgs& D, int t,
+                                            unsigned char* smem, RouteShared<kAttWaves>& rsh, int32_t& sh_slot) {
   const int tid = threadIdx.x;
-  // Work comes from one queue per XCD (the units u with u % 8 == x go to queue
-  // x), so the queue counters are contended by few workgroups and a unit's
-  // hand-offs tend to stay within one XCD.  A workgroup takes from its own
-  // XCD's queue and, when that is empty, from the next ones.  Each queue holds
-  // its units' routings, then their parts, then their merges: every wait is on
-  // an item that comes earlier in some queue and so is already taken by a
-  // running workgroup.
-  if (tid == 0) {
-    const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
-    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = Bt.G;
-    uint32_t item = 0xFFFFFFFFu;
-    for (int k = 0; k < kQueues && item == 0xFFFFFFFFu; ++k) {
-      const int x = (x0 + k) & (kQueues - 1);
-      const int nx = D.n_units > x ? (D.n_units - x + kQueues - 1) / kQueues : 0;
-      const uint32_t size = (uint32_t)(nx * (R + P + G));
-      if (size == 0u) continue;
-      const uint32_t i = atomicAdd(&D.ctrl[kCtrlQueue + x * kQueueStride], 1u);
-      if (i >= size) continue;
-      // queue position -> launch-wide item index: routes, then parts, then merges
-      if (i < (uint32_t)(R * nx)) {
-        item = (uint32_t)(x + kQueues * (int)i);
-      } else if (i < (uint32_t)(R * nx + nx * P)) {
-        const int j = (int)i - R * nx;
-        item = (uint32_t)(D.n_route + (x + kQueues * (j / P)) * P + j % P);
-      } else {
-        const int j = (int)i - R * nx - nx * P;
-        item = (uint32_t)(D.n_part_end + (x + kQueues * (j / G)) * G + j % G);
-      }
-    }
-    sh_ticket = item;
-  }
-  lds_barrier();
-  const int t = (int)sh_ticket;
   if (t < 0) {
-    // no item (cannot happen: the launch has exactly one workgroup per item)
+    // no item
   } else if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
     route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
@@ -1437,6 +1404,49 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
     merge_row(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G + g, D.out, D.out_lse,
               reinterpret_cast<float*>(smem));
   }
+}
+
+template <int NRQ>
+__global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ RouteShared<kAttWaves> rsh;
+  __shared__ uint32_t sh_ticket, sh_flag;
+  __shared__ int32_t sh_slot;
+  const int tid = threadIdx.x;
+  // Work comes from one queue per XCD (the units u with u % 8 == x go to queue
+  // x), so the queue counters are contended by few workgroups and a unit's
+  // hand-offs tend to stay within one XCD.  A workgroup takes from its own
+  // XCD's queue and, when that is empty, from the next ones.  Each queue holds
+  // its units' routings, then their parts, then their merges: every wait is on
+  // an item that comes earlier in some queue and so is already taken by a
+  // running workgroup.
+  if (tid == 0) {
+    const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
+    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = Bt.G;
+    uint32_t item = 0xFFFFFFFFu;
+    for (int k = 0; k < kQueues && item == 0xFFFFFFFFu; ++k) {
+      const int x = (x0 + k) & (kQueues - 1);
+      const int nx = D.n_units > x ? (D.n_units - x + kQueues - 1) / kQueues : 0;
+      const uint32_t size = (uint32_t)(nx * (R + P + G));
+      if (size == 0u) continue;
+      const uint32_t i = atomicAdd(&D.ctrl[kCtrlQueue + x * kQueueStride], 1u);
+      if (i >= size) continue;
+      // queue position -> launch-wide item index: routes, then parts, then merges
+      if (i < (uint32_t)(R * nx)) {
+        item = (uint32_t)(x + kQueues * (int)i);
+      } else if (i < (uint32_t)(R * nx + nx * P)) {
+        const int j = (int)i - R * nx;
+        item = (uint32_t)(D.n_route + (x + kQueues * (j / P)) * P + j % P);
+      } else {
+        const int j = (int)i - R * nx - nx * P;
+        item = (uint32_t)(D.n_part_end + (x + kQueues * (j / G)) * G + j % G);
+      }
+    }
+    sh_ticket = item;
+  }
+  lds_barrier();
+  const int t = (int)sh_ticket;
+  decode_item<NRQ>(P, Bt, D, t, smem, rsh, sh_slot);
   // The last merge to finish zeroes the control words for the next launch:
   // merges start only after all of their unit's parts are stored, and every
   // part only after its routing, so no other item still uses them.
@@ -1449,6 +1459,108 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
       for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
       if (tid < kQueues) D.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
       if (tid == 0) D.ctrl[1] = 0u;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Layer-batched decode: the fused steps of several layers in one launch
+// ----------------------------------------------------------------------------
+
+struct LayerArgs {
+  PoolArgs P;
+  BatchArgs Bt;
+  DecodeArgs D;  // the layer's workspace region; D.ctrl is the launch-wide control header
+  int nrq;
+};
+
+struct LayersArgs {
+  uint32_t* ctrl;  // [1] merges finished, [2] sticky wait-timeout flag, queue counters
+  int n_layers;
+  int n_units;     // units per layer (the same in every layer)
+  int routes;      // routing items per unit (0 or 1)
+  int parts;       // parts per unit
+  int group;       // merges per unit (query heads per KV head)
+};
+
+// Work items of every layer from the per-XCD queues: a queue holds, for the
+// units u with u % 8 == x of every layer, first all routings, then all parts,
+// then all merges (layer-major), so every wait is on an item taken earlier.
+// NMAX: the largest low-rank tile count of any layer (instances hold only the
+// attention variants up to it, which keeps register use down).
+template <int NMAX>
+__global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArgs* __restrict__ table, LayersArgs L) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ RouteShared<kAttWaves> rsh;
+  __shared__ int32_t sh_item, sh_layer, sh_slot;
+  __shared__ uint32_t sh_flag;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
+    const int R = L.routes, Pp = L.parts, G = L.group, NL = L.n_layers;
+    int item = -1, layer = 0;
+    for (int k = 0; k < kQueues && item < 0; ++k) {
+      const int x = (x0 + k) & (kQueues - 1);
+      const int nx = L.n_units > x ? (L.n_units - x + kQueues - 1) / kQueues : 0;
+      const uint32_t size = (uint32_t)(NL * nx * (R + Pp + G));
+      if (size == 0u) continue;
+      const uint32_t i = atomicAdd(&L.ctrl[kCtrlQueue + x * kQueueStride], 1u);
+      if (i >= size) continue;
+      const uint32_t nr = (uint32_t)(NL * nx * R), np = (uint32_t)(NL * nx * Pp);
+      const int n_route = R * L.n_units, n_part_end = n_route + L.n_units * Pp;
+      if (i < nr) {
+        layer = (int)i / nx;
+        item = x + kQueues * ((int)i % nx);
+      } else if (i < nr + np) {
+        const int j = (int)(i - nr);
+        layer = j / (nx * Pp);
+        const int r = j % (nx * Pp);
+        item = n_route + (x + kQueues * (r / Pp)) * Pp + r % Pp;
+      } else {
+        const int j = (int)(i - nr - np);
+        layer = j / (nx * G);
+        const int r = j % (nx * G);
+        item = n_part_end + (x + kQueues * (r / G)) * G + r % G;
+      }
+    }
+    sh_item = item;
+    sh_layer = layer;
+  }
+  lds_barrier();
+  // the item and its layer are the same in every lane: keep them, and the
+  // layer's arguments, in scalar registers
+  const int t = __builtin_amdgcn_readfirstlane(sh_item);
+  const LayerArgs la = table[__builtin_amdgcn_readfirstlane(sh_layer)];
+  if (t >= 0) {
+    if (la.nrq <= 0 || NMAX == 0)
+      decode_item<0>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+    else if (la.nrq == 1 || NMAX == 1)
+      decode_item<(NMAX < 1 ? NMAX : 1)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+    else if (la.nrq == 2 || NMAX == 2)
+      decode_item<(NMAX < 2 ? NMAX : 2)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+    else if (la.nrq == 3 || NMAX == 3)
+      decode_item<(NMAX < 3 ? NMAX : 3)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+    else if (la.nrq == 4 || NMAX == 4)
+      decode_item<(NMAX < 4 ? NMAX : 4)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+    else
+      decode_item<NMAX>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+  }
+  // The last merge of the launch zeroes every layer's control words and the
+  // queue counters: it finishes after every part, and every part after its
+  // routing, so no other item still uses them.
+  if (t >= la.D.n_part_end) {
+    __syncthreads();
+    if (tid == 0)
+      sh_flag = (atomicAdd(&L.ctrl[1], 1u) == (uint32_t)(L.n_layers * L.n_units * L.group - 1)) ? 1u : 0u;
+    lds_barrier();
+    if (sh_flag) {
+      for (int l = 0; l < L.n_layers; ++l) {
+        const DecodeArgs& D = table[l].D;
+        for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
+        for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
+      }
+      if (tid < kQueues) L.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
+      if (tid == 0) L.ctrl[1] = 0u;
     }
   }
 }
@@ -1704,11 +1816,69 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) 
   return w;
 }
 
+// Arguments of one layer's fused decode over the workspace region ws (laid out
+// by decode_layout); ctrl: the control header the launch uses.
+dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
+                             uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm) {
+  const WsLayout w = decode_layout(pool, batch, top_k);
+  // with routing, each routed-block part also takes its share of the window;
+  // without, the window comes in chunks of kWinChunk rows
+  const int n_win = top_k > 0 ? 0 : decode_win_parts(batch->window);
+  const int n_parts = top_k + n_win;
+  const int units = batch->batch * pool->n_kv_heads;
+  AttnArgs& a = D.att;
+  a.idx = nullptr;
+  a.top_k = top_k;
+  a.n_block_parts = top_k;
+  a.block_mode = 3;
+  a.n_win_parts = n_win;
+  a.win_chunk = kWinChunk;
+  a.win_tile_stride = top_k;
+  a.items_per_unit = n_parts;
+  a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
+  a.scale = scale;
+  a.part_o = (float*)(ws + w.part_o);
+  a.part_lse = (float*)(ws + w.part_lse);
+  a.n_parts = n_parts;
+  a.part_offset = 0;
+  D.idx = out_idx ? out_idx : (int32_t*)(ws + w.idx);
+  D.slots = (int32_t*)(ws + w.slots);
+  D.ctrl = ctrl;
+  D.unit_done = (uint32_t*)(ws + w.unit_done);
+  D.out = (f16*)out;
+  D.out_lse = out_lse;
+  D.n_units = units;
+  D.n_route = top_k > 0 ? units : 0;
+  const int64_t part_end = (int64_t)D.n_route + (int64_t)units * n_parts;
+  const int64_t items = part_end + (int64_t)units * (batch->n_q_heads / pool->n_kv_heads);
+  if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
+  D.n_part_end = (int)part_end;
+  D.n_items = (int)items;
+  shm = (size_t)att_lds_bytes(a.rq);
+  const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
+  if (top_k > 0 && route_shm > shm) shm = route_shm;
+  return DKV_OK;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
 // C ABI
 // ----------------------------------------------------------------------------
+
+template <int NMAX>
+static dkv_status launch_layers(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_decode_layers<NMAX>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            158 * 1024) != hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_decode_layers) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_decode_layers<NMAX>, dim3((unsigned)plan->n_items), dim3(kAttThreads),
+                     (size_t)plan->lds_bytes, st, (const LayerArgs*)plan->table, L);
+  return launched("k_decode_layers");
+}
 
 extern "C" {
 
@@ -1868,46 +2038,12 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   if (top_k > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) return s;
 
   const hipStream_t st = (hipStream_t)stream;
-  const WsLayout w = decode_layout(pool, batch, top_k);
-  // with routing, each routed-block part also takes its share of the window;
-  // without, the window comes in chunks of kWinChunk rows
-  const int n_win = top_k > 0 ? 0 : decode_win_parts(batch->window);
-  const int n_parts = top_k + n_win;
-  const int units = batch->batch * pool->n_kv_heads;
-  unsigned char* ws = (unsigned char*)workspace;
-
   DecodeArgs D;
-  AttnArgs& a = D.att;
-  a.idx = nullptr;
-  a.top_k = top_k;
-  a.n_block_parts = top_k;
-  a.block_mode = 3;
-  a.n_win_parts = n_win;
-  a.win_chunk = kWinChunk;
-  a.win_tile_stride = top_k;
-  a.items_per_unit = n_parts;
-  a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
-  a.scale = scale;
-  a.part_o = (float*)(ws + w.part_o);
-  a.part_lse = (float*)(ws + w.part_lse);
-  a.n_parts = n_parts;
-  a.part_offset = 0;
-  D.idx = out_idx ? out_idx : (int32_t*)(ws + w.idx);
-  D.slots = (int32_t*)(ws + w.slots);
-  D.ctrl = (uint32_t*)ws;
-  D.unit_done = (uint32_t*)(ws + w.unit_done);
-  D.out = (f16*)out;
-  D.out_lse = out_lse;
-  D.n_units = units;
-  D.n_route = top_k > 0 ? units : 0;
-  const int64_t part_end = (int64_t)D.n_route + (int64_t)units * n_parts;
-  const int64_t items = part_end + (int64_t)units * (batch->n_q_heads / pool->n_kv_heads);
-  if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
-  D.n_part_end = (int)part_end;
-  D.n_items = (int)items;
-  size_t shm = (size_t)att_lds_bytes(a.rq);
-  const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
-  if (top_k > 0 && route_shm > shm) shm = route_shm;
+  size_t shm = 0;
+  if ((s = build_decode_args(pool, batch, top_k, scale, (unsigned char*)workspace, (uint32_t*)workspace, out, out_lse,
+                             out_idx, D, shm)))
+    return s;
+  const AttnArgs& a = D.att;
 
   if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)
     return fail(DKV_ERR_HIP, "hipEventRecord failed");
@@ -1939,6 +2075,130 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
     return fail(DKV_ERR_INVALID_ARG, "events must hold two hipEvent_t handles");
   }
   return decode_impl(pool, batch, top_k, scale, workspace, workspace_bytes, out, out_lse, out_idx, events, stream);
+}
+
+// ---- layer-batched decode -------------------------------------------------
+
+size_t dkv_decode_layers_table_size(int32_t n_layers) {
+  return n_layers > 0 ? (size_t)n_layers * sizeof(LayerArgs) : 0;
+}
+
+static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
+  return align256(decode_layout(pool, batch, top_k).total);
+}
+
+size_t dkv_decode_layers_workspace_size(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
+                                        int32_t top_k) {
+  if (!pools || !batches || n_layers < 1 || top_k < 0) return 0;
+  size_t total = kCtrlHeaderBytes;
+  for (int l = 0; l < n_layers; ++l) total += layer_region_bytes(&pools[l], &batches[l], top_k);
+  return total;
+}
+
+dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
+                                     int32_t top_k, float scale, void* const* outs, float* const* out_lses,
+                                     int32_t* const* out_idxs, void* table, size_t table_bytes,
+                                     void* workspace, size_t workspace_bytes, dkv_layers_plan* plan) {
+  g_err[0] = 0;
+  if (!pools || !batches || !plan) return fail(DKV_ERR_INVALID_ARG, "pools / batches / plan is NULL");
+  if (n_layers < 1) return fail(DKV_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (top_k < 0) return fail(DKV_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+  if (!outs || !out_lses) return fail(DKV_ERR_INVALID_ARG, "outs / out_lses is NULL");
+  if (!table || table_bytes < dkv_decode_layers_table_size(n_layers))
+    return fail(DKV_ERR_WORKSPACE, "table of %zu bytes given, %zu needed", table ? table_bytes : 0,
+                dkv_decode_layers_table_size(n_layers));
+  if (!al(table, 16)) return fail(DKV_ERR_WORKSPACE, "table must be 16-byte aligned");
+  const size_t need = dkv_decode_layers_workspace_size(pools, batches, n_layers, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(DKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                need);
+  if (!al(workspace, 256)) return fail(DKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const dkv_pool& p0 = pools[0];
+  const dkv_batch& b0 = batches[0];
+  LayerArgs* host = (LayerArgs*)calloc((size_t)n_layers, sizeof(LayerArgs));
+  if (!host) return fail(DKV_ERR_HIP, "out of host memory");
+  dkv_status s = DKV_OK;
+  size_t shm = 0, off = kCtrlHeaderBytes;
+  unsigned char* ws = (unsigned char*)workspace;
+  for (int l = 0; l < n_layers && s == DKV_OK; ++l) {
+    const dkv_pool* pool = &pools[l];
+    const dkv_batch* batch = &batches[l];
+    if ((s = check_pool_shape(pool))) break;
+    if ((s = check_batch(pool, batch, top_k > 0, true))) break;
+    if (pool->n_kv_heads != p0.n_kv_heads || batch->batch != b0.batch || batch->n_q_heads != b0.n_q_heads ||
+        batch->window != b0.window || batch->max_blocks != b0.max_blocks) {
+      s = fail(DKV_ERR_INVALID_ARG, "layer %d: batch shape or KV heads differ from layer 0", l);
+      break;
+    }
+    if (top_k > 0 && batch->max_blocks > DKV_MAX_ROUTE_BLOCKS) {
+      s = fail(DKV_ERR_UNSUPPORTED, "max_blocks %d > %d", batch->max_blocks, DKV_MAX_ROUTE_BLOCKS);
+      break;
+    }
+    if (b0.batch > 0 && (!outs[l] || !out_lses[l])) {
+      s = fail(DKV_ERR_INVALID_ARG, "layer %d: out / out_lse is NULL", l);
+      break;
+    }
+    if (outs[l] && !al(outs[l], 4)) {
+      s = fail(DKV_ERR_UNSUPPORTED, "layer %d: out must be 4-byte aligned", l);
+      break;
+    }
+    if (top_k > 0 && b0.batch > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) break;
+    size_t shm_l = 0;
+    if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
+                               out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l)))
+      break;
+    host[l].P = make_pool_args(pool);
+    host[l].Bt = make_batch_args(pool, batch);
+    host[l].nrq = host[l].D.att.rq / 16;
+    if (shm_l > shm) shm = shm_l;
+    off += layer_region_bytes(pool, batch, top_k);
+  }
+  if (s == DKV_OK) {
+    if (hipMemcpy(table, host, (size_t)n_layers * sizeof(LayerArgs), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(workspace, 0, need) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      s = fail(DKV_ERR_HIP, "table upload or workspace clear failed");
+  }
+  if (s == DKV_OK) {
+    const int units = b0.batch * p0.n_kv_heads;
+    plan->n_layers = n_layers;
+    plan->n_units = units;
+    plan->routes = top_k > 0 ? 1 : 0;
+    plan->parts = host[0].D.att.items_per_unit;
+    plan->group = b0.n_q_heads / p0.n_kv_heads;
+    const int64_t items = (int64_t)n_layers * units * (plan->routes + plan->parts + plan->group);
+    if (items > 0x7FFFFFFF) s = fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
+    plan->n_items = (int32_t)items;
+    plan->lds_bytes = (int32_t)shm;
+    int nmax = 0;
+    for (int l = 0; l < n_layers; ++l) nmax = host[l].nrq > nmax ? host[l].nrq : nmax;
+    plan->max_tiles = nmax;
+    plan->table = table;
+    plan->workspace = workspace;
+  }
+  free(host);
+  return s;
+}
+
+dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
+  g_err[0] = 0;
+  if (!plan || !plan->table || !plan->workspace) return fail(DKV_ERR_INVALID_ARG, "plan is NULL or not prepared");
+  if (plan->n_items == 0) return DKV_OK;
+  LayersArgs L;
+  L.ctrl = (uint32_t*)plan->workspace;
+  L.n_layers = plan->n_layers;
+  L.n_units = plan->n_units;
+  L.routes = plan->routes;
+  L.parts = plan->parts;
+  L.group = plan->group;
+  switch (plan->max_tiles) {  // the largest low-rank tile count of the layers
+    case 0: return launch_layers<0>(plan, L, (hipStream_t)stream);
+    case 1: return launch_layers<1>(plan, L, (hipStream_t)stream);
+    case 2: return launch_layers<2>(plan, L, (hipStream_t)stream);
+    case 3: return launch_layers<3>(plan, L, (hipStream_t)stream);
+    case 4: return launch_layers<4>(plan, L, (hipStream_t)stream);
+    case 5: return launch_layers<5>(plan, L, (hipStream_t)stream);
+    default: return fail(DKV_ERR_INVALID_ARG, "plan is corrupt (tile count %d)", plan->max_tiles);
+  }
 }
 
 }  // extern "C"

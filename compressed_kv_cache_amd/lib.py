@@ -31,7 +31,8 @@ DKV_ERR_HIP = 4
 EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route_keys",
             "dkv_route_topk", "dkv_lowrank_attn", "dkv_exact_attn", "dkv_lse_merge",
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
-            "dkv_decode_profiled", "dkv_gather_route_keys")
+            "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
+            "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers")
 
 
 class DKVError(RuntimeError):
@@ -62,6 +63,13 @@ class BatchC(ctypes.Structure):
                 ("route_keys", ctypes.c_void_p)]
 
 
+class LayersPlanC(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_units", ctypes.c_int32), ("routes", ctypes.c_int32),
+                ("parts", ctypes.c_int32), ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("table", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -86,6 +94,15 @@ def load(path: str = LIB_PATH):
     lib.dkv_route_keys.restype = i32
     lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
     lib.dkv_gather_route_keys.argtypes = [P, Bp, vp, vp]
+    lib.dkv_decode_layers_table_size.argtypes = [i32]
+    lib.dkv_decode_layers_table_size.restype = ctypes.c_size_t
+    lib.dkv_decode_layers_workspace_size.argtypes = [P, Bp, i32, i32]
+    lib.dkv_decode_layers_workspace_size.restype = ctypes.c_size_t
+    lib.dkv_decode_layers_prepare.argtypes = [P, Bp, i32, i32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                              ctypes.c_size_t, ctypes.POINTER(LayersPlanC)]
+    lib.dkv_decode_layers_prepare.restype = i32
+    lib.dkv_decode_layers.argtypes = [ctypes.POINTER(LayersPlanC), vp]
+    lib.dkv_decode_layers.restype = i32
     lib.dkv_gather_route_keys.restype = i32
     lib.dkv_route_topk.restype = i32
     lib.dkv_lowrank_attn.argtypes = [P, Bp, vp, i32, f32, vp, vp, i32, i32, vp]
@@ -386,3 +403,44 @@ def decode_profiled(pool: Pool, batch: Batch, top_k: int, scale: float, workspac
                                    _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                    _ptr(out), _ptr(out_lse), _ptr(out_idx), arr, _stream(stream)),
            "dkv_decode_profiled")
+
+
+class Layers:
+    """A prepared layer-batched decode (dkv_decode_layers_prepare): the fused
+    decode steps of several layers in one launch per run().  Holds the device
+    argument table, the workspace and the per-layer outputs."""
+
+    def __init__(self, pools: Sequence[Pool], batches: Sequence[Batch], top_k: int, scale: float,
+                 with_idx: bool = True):
+        import torch
+        lib = load()
+        n = len(pools)
+        assert n == len(batches) and n > 0
+        self.pools, self.batches, self.top_k = list(pools), list(batches), top_k
+        dev = batches[0].tensors["q"].device
+        PA = (PoolC * n)(*[p.c for p in pools])
+        BA = (BatchC * n)(*[b.c for b in batches])
+        self.outs = [torch.empty((b.batch, b.n_q_heads, HEAD_DIM), dtype=torch.float16, device=dev)
+                     for b in batches]
+        self.lses = [torch.empty((b.batch, b.n_q_heads), dtype=torch.float32, device=dev) for b in batches]
+        self.idxs = [torch.empty((b.batch, p.n_kv_heads, top_k), dtype=torch.int32, device=dev)
+                     for p, b in zip(pools, batches)] if (with_idx and top_k > 0) else None
+        tsz = lib.dkv_decode_layers_table_size(n)
+        wsz = lib.dkv_decode_layers_workspace_size(PA, BA, n, top_k)
+        self.table = torch.empty((max(tsz, 16),), dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty((max(wsz, 256),), dtype=torch.uint8, device=dev)
+        vpa = ctypes.c_void_p * n
+        outs = vpa(*[o.data_ptr() for o in self.outs])
+        lses = vpa(*[x.data_ptr() for x in self.lses])
+        idxs = vpa(*[x.data_ptr() for x in self.idxs]) if self.idxs is not None else None
+        self.plan = LayersPlanC()
+        _check(lib.dkv_decode_layers_prepare(PA, BA, n, top_k, scale, outs, lses, idxs, _ptr(self.table),
+                                             self.table.numel(), _ptr(self.workspace), self.workspace.numel(),
+                                             ctypes.byref(self.plan)), "dkv_decode_layers_prepare")
+
+    def run(self, stream=None) -> None:
+        _check(load().dkv_decode_layers(ctypes.byref(self.plan), _stream(stream)), "dkv_decode_layers")
+
+    def timeout_flag(self) -> int:
+        """The workspace's sticky wait-timeout word (0 in every correct run)."""
+        return int(self.workspace[8:12].view(__import__("torch").int32).item())

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 2
+#define DKV_ABI_VERSION 3
 #define DKV_HEAD_DIM 128
 #define DKV_BLOCK_SIZE 256
 #define DKV_MAX_RANK 64
@@ -240,6 +240,50 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
                                float scale, void* workspace, size_t workspace_bytes, void* out,
                                float* out_lse, int32_t* out_idx, void* const* events,
                                void* stream);
+
+/* ---- Layer-batched decode -------------------------------------------------
+ * The fused decode step (dkv_decode) of n_layers independent layers in ONE
+ * launch, so that the routing, block-attention and merge phases of different
+ * layers overlap and the launch streams the cache at full bandwidth.  Use it
+ * when several layers' queries are at hand at once: micro-batches in flight at
+ * different layers, or a model's layers evaluated on given queries.  All
+ * layers share head_dim, block size, n_kv_heads and the batch shape (batch,
+ * n_q_heads, window, max_blocks) and top_k; pools may differ in rank, residual
+ * count and slot count.  Results are the same bits as n_layers dkv_decode calls.
+ *
+ * dkv_decode_layers_prepare (once; synchronous, not capturable in a graph)
+ * validates every layer, writes the per-layer argument table into `table`
+ * (device memory of dkv_decode_layers_table_size bytes, caller-owned), zeroes
+ * the control words of `workspace` (device memory of
+ * dkv_decode_layers_workspace_size bytes, 256-byte aligned, caller-owned) and
+ * fills *plan.  dkv_decode_layers (any number of times; asynchronous, may be
+ * captured) runs one step.  The pools, batches, outputs, table and workspace
+ * given to prepare must keep their addresses; their contents (e.g. the
+ * queries) may change between calls.  Calls sharing a workspace must not
+ * overlap.  Word 2 of the workspace is the sticky wait-timeout flag.
+ *   outs[l]: fp16 [B][Hq][d]; out_lses[l]: fp32 [B][Hq];
+ *   out_idxs: NULL, or per layer int32 [B][Hkv][top_k] or NULL. */
+typedef struct dkv_layers_plan {
+  int32_t n_layers;
+  int32_t n_units;        /* (sequence, KV head) units per layer */
+  int32_t routes;         /* routing items per unit (0 or 1) */
+  int32_t parts;          /* parts per unit */
+  int32_t group;          /* merges per unit */
+  int32_t n_items;        /* work items of one launch */
+  int32_t lds_bytes;      /* dynamic LDS per workgroup */
+  int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */
+  const void* table;
+  void* workspace;
+} dkv_layers_plan;
+
+size_t dkv_decode_layers_table_size(int32_t n_layers);
+size_t dkv_decode_layers_workspace_size(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
+                                        int32_t top_k);
+dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
+                                     int32_t top_k, float scale, void* const* outs, float* const* out_lses,
+                                     int32_t* const* out_idxs, void* table, size_t table_bytes,
+                                     void* workspace, size_t workspace_bytes, dkv_layers_plan* plan);
+dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream);
 
 #ifdef __cplusplus
 }

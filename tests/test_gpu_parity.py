@@ -441,3 +441,129 @@ def test_route_key_table(lib, cfg, variant):
     torch.cuda.synchronize()
     assert torch.equal(idx0, idx1) and torch.equal(sc0, sc1)
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1) and torch.equal(oi0, oi1)
+
+
+# ---------------------------------------------------------------------------
+# Layer-batched decode: several layers' fused steps in one launch
+# ---------------------------------------------------------------------------
+
+
+def _upload_layers(L, wl, layers, route_table=True):
+    pools, batches = [], []
+    for l in layers:
+        pool, batch = upload(L, wl, l)
+        if route_table:
+            L.gather_route_keys(pool, batch)
+        pools.append(pool)
+        batches.append(batch)
+    return pools, batches
+
+
+def _check_layers_match_per_layer(L, wl, layers, label):
+    say(f"[decode layers] {label}: layers {list(layers)}")
+    pools, batches = _upload_layers(L, wl, layers)
+    want = []
+    for p, b in zip(pools, batches):
+        o, s, i = L.decode(p, b, wl.top_k, wl.scale)
+        want.append((o, s, i))
+    run = L.Layers(pools, batches, wl.top_k, wl.scale)
+    for rep in range(3):
+        for o in run.outs:
+            o.fill_(7)
+        run.run()
+        torch.cuda.synchronize()
+        for l, (o, s, i) in enumerate(want):
+            assert torch.equal(run.outs[l], o), (rep, l)
+            assert torch.equal(run.lses[l], s), (rep, l)
+            if i is not None:
+                assert torch.equal(run.idxs[l], i), (rep, l)
+    assert run.timeout_flag() == 0
+    return run, want
+
+
+def test_decode_layers_stack_matches_per_layer(lib):
+    """Four layers of the 28-layer 64k batch-4 stack (ranks 24, 48, 16 and the
+    last layer's) in one launch give the same bits as four per-layer launches,
+    on three launches in a row."""
+    wl = config(2)
+    _check_layers_match_per_layer(lib, wl, range(len(wl.layers)), "stack64k")
+
+
+def test_decode_layers_mixed_ranks_and_edges(lib):
+    """Layers of every low-rank tile count (ranks 1..64, 0..255 residual rows),
+    ragged windows and an empty sequence, in one launch."""
+    base = dict(batch=4, n_q_heads=6, n_kv_heads=2, window=48, n_blocks=[5, 0, 6, 3],
+                win_len=[48, 0, 17, 30], top_k=3, sigma0=2.0)
+    specs = [dict(ranks=[1], n_resid=0), dict(ranks=[7], n_resid=20), dict(ranks=[24], n_resid=8),
+             dict(ranks=[40], n_resid=33), dict(ranks=[64], n_resid=4), dict(ranks=[15], n_resid=255)]
+    wls = [synth.make_workload(f"mix{i}", seed=300 + i, **base, **s) for i, s in enumerate(specs)]
+    pools, batches = [], []
+    for w in wls:
+        p, b = upload(lib, w)
+        pools.append(p)
+        batches.append(b)
+    run = lib.Layers(pools, batches, 3, wls[0].scale)
+    assert run.plan.max_tiles >= 4           # rank 64 needs the largest instance
+    for rep in range(2):
+        run.run()
+        torch.cuda.synchronize()
+        for l, w in enumerate(wls):
+            o, s, i = lib.decode(pools[l], batches[l], 3, w.scale)
+            torch.cuda.synchronize()
+            assert torch.equal(run.outs[l], o) and torch.equal(run.lses[l], s) and torch.equal(run.idxs[l], i)
+    # and against the oracle, for one layer of each kind
+    for l in (0, 4, 5):
+        w = wls[l]
+        lay = w.layers[0]
+        gidx = run.idxs[l].cpu().numpy().astype(np.int64)
+        ro, rl, _ = oracle.decode(lay.pool(), lay.q, lay.win_k, lay.win_v, w.block_table, w.n_blocks,
+                                  w.win_len, w.n_kv_heads, 3, w.scale, idx=gidx)
+        c = parity.check_outputs(run.outs[l].cpu().numpy(), run.lses[l].cpu().numpy(), ro, rl)
+        assert c.ok, c.message
+    assert run.timeout_flag() == 0
+
+
+def test_decode_layers_window_only(lib):
+    base = dict(batch=3, n_q_heads=8, n_kv_heads=2, window=300, n_blocks=[2, 1, 2],
+                win_len=[300, 129, 1], top_k=0, ranks=[8], n_resid=4)
+    wls = [synth.make_workload(f"win{i}", seed=400 + i, **base) for i in range(3)]
+    pools, batches = zip(*[upload(lib, w) for w in wls])
+    run = lib.Layers(list(pools), list(batches), 0, wls[0].scale)
+    assert run.idxs is None
+    run.run()
+    torch.cuda.synchronize()
+    for l, w in enumerate(wls):
+        o, s, _ = lib.decode(pools[l], batches[l], 0, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(run.outs[l], o) and torch.equal(run.lses[l], s)
+
+
+def test_decode_layers_graph_replays(lib):
+    """The layer-batched launch captured in a graph replays to the eager bits,
+    with eager launches and synchronisations between replays."""
+    wl = config(1)
+    pools, batches = _upload_layers(lib, wl, [0, 0, 0])
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    run.run()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), s.clone(), i.clone()) for o, s, i in zip(run.outs, run.lses, run.idxs)]
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        run.run(cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run.run(torch.cuda.current_stream())
+    for rep in range(4):
+        for o in run.outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (o, s, i) in enumerate(ref):
+            assert torch.equal(run.outs[l], o) and torch.equal(run.lses[l], s) and torch.equal(run.idxs[l], i)
+        run.run()
+        torch.cuda.synchronize()
+        assert torch.equal(run.outs[0], ref[0][0])
+    assert run.timeout_flag() == 0

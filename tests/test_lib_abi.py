@@ -175,3 +175,31 @@ def test_route_key_table_validates(clib):
     # with the table, routing needs no pool routing keys
     ok = _batch(route_keys=FAKE)
     assert clib.dkv_decode_workspace_size(ctypes.byref(q), ctypes.byref(ok), 4) > 0
+
+
+def test_layer_batched_entry_points_validate(clib):
+    p, b = _pool(), _batch()
+    PA = (L.PoolC * 2)(p, p)
+    BA = (L.BatchC * 2)(b, b)
+    assert clib.dkv_decode_layers_table_size(0) == 0
+    assert clib.dkv_decode_layers_table_size(3) > 0
+    need = clib.dkv_decode_layers_workspace_size(PA, BA, 2, 4)
+    one = clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), 4)
+    assert need >= 2 * one
+    assert clib.dkv_decode_layers_workspace_size(PA, BA, 0, 4) == 0
+    plan = L.LayersPlanC()
+    outs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    tsz = clib.dkv_decode_layers_table_size(2)
+    # bad counts and sizes are refused before anything touches the device
+    assert clib.dkv_decode_layers_prepare(PA, BA, 0, 4, 0.1, outs, outs, None, FAKE, tsz, FAKE, need,
+                                          ctypes.byref(plan)) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_decode_layers_prepare(PA, BA, 2, 4, 0.1, outs, outs, None, FAKE, tsz - 1, FAKE, need,
+                                          ctypes.byref(plan)) == L.DKV_ERR_WORKSPACE
+    assert clib.dkv_decode_layers_prepare(PA, BA, 2, 4, 0.1, outs, outs, None, FAKE, tsz, FAKE, need - 1,
+                                          ctypes.byref(plan)) == L.DKV_ERR_WORKSPACE
+    b2 = _batch(n_q_heads=16)
+    BB = (L.BatchC * 2)(b, b2)
+    need2 = clib.dkv_decode_layers_workspace_size(PA, BB, 2, 4)
+    assert clib.dkv_decode_layers_prepare(PA, BB, 2, 4, 0.1, outs, outs, None, FAKE, tsz, FAKE, need2,
+                                          ctypes.byref(plan)) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_decode_layers(None, None) == L.DKV_ERR_INVALID_ARG
