@@ -313,9 +313,14 @@ def main() -> int:
         for _ in range(args.warmup):
             run.run()
         torch.cuda.synchronize()
+        # the same routing; outputs equal the per-layer ones up to the rounding of
+        # another split of the rows (the window has parts of its own here)
         for i in range(n_layers):
-            assert torch.equal(run.outs[i], ref_out[i]) and torch.equal(run.lses[i], ref_lse[i]) and \
-                torch.equal(run.idxs[i], idxs[i]), f"layer-batched layer {i} differs from per-layer decode"
+            assert torch.equal(run.idxs[i], idxs[i]), f"layer-batched layer {i} routes differently"
+            d_out = (run.outs[i].float() - ref_out[i].float()).abs().max().item()
+            d_lse = (run.lses[i] - ref_lse[i]).abs().max().item()
+            assert d_out <= 2e-3 and d_lse <= 1e-4, f"layer-batched layer {i}: {d_out:.2e} {d_lse:.2e}"
+        lb_ref = [o.clone() for o in run.outs]
         e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -332,7 +337,7 @@ def main() -> int:
             f"(p10 {np.percentile(lb, 10) * 1e3:.2f}, p90 {np.percentile(lb, 90) * 1e3:.2f})")
         assert run.timeout_flag() == 0, "a wait in k_decode_layers timed out"
         for i in range(n_layers):
-            assert torch.equal(run.outs[i], ref_out[i]), "layer-batched steps are not bit-identical"
+            assert torch.equal(run.outs[i], lb_ref[i]), "layer-batched steps are not bit-identical"
         if not args.no_graph:
             g2 = torch.cuda.CUDAGraph()
             cs = torch.cuda.Stream()
@@ -350,7 +355,7 @@ def main() -> int:
                 g2.replay()
                 torch.cuda.synchronize()
                 for i in range(n_layers):
-                    assert torch.equal(run.outs[i], ref_out[i]), f"layer-batched replay {rep} differs"
+                    assert torch.equal(run.outs[i], lb_ref[i]), f"layer-batched replay {rep} differs"
             for _ in range(args.warmup):
                 g2.replay()
             torch.cuda.synchronize()

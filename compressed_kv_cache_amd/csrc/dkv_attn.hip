@@ -40,6 +40,7 @@ typedef _Float16 f16;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -119,6 +120,15 @@ __device__ __forceinline__ void split_hl(float x0, float x1, float x2, float x3,
     hi[e] = h;
     lo[e] = (f16)(x[e] - (float)h);
   }
+}
+
+// Four softmax weights in [0, 1] as an fp16 MFMA operand (round to nearest
+// even: relative error at most 2^-11 per weight; the row sums stay fp32)
+__device__ __forceinline__ v4h to_h4(const float (&x)[4]) {
+  v4h h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
+  return h;
 }
 
 // LDS hand-off between lanes of one wave: LDS operations of a wave complete in
@@ -682,15 +692,13 @@ __device__ __forceinline__ v4f exact_scores(const v8h (&kx)[4], const v4h (&qf)[
 
 // O^T += V^T p for one 16-row tile whose V rows sit in LDS at Vt[row][kVStride]
 __device__ __forceinline__ void exact_pv(ExState& st, const f16* Vt, const float (&pe)[4], int l16, int q4) {
-  v4h ph, pl;
-  split_hl(pe[0], pe[1], pe[2], pe[3], ph, pl);
+  const v4h ph = to_h4(pe);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     v4h av;
 #pragma unroll
     for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
     st.Ot[n] = mfma16(av, ph, st.Ot[n]);
-    st.Ot[n] = mfma16(av, pl, st.Ot[n]);
   }
 }
 
@@ -1009,17 +1017,35 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
     f16* T = reinterpret_cast<f16*>(my);  // [kLRTilesPerWave][16][TS]
     float zz[kLRTilesPerWave][4];
+    // Ux = [U | 1 | 0]; the anchor row has U = 0.  With r % 4 == 0 a lane's four
+    // columns j0 .. j0 + 3 are all below r, or are r, r + 1, .. (then only the
+    // first is 1), or are all padding: two bit masks per 16-column tile.
+    const bool whole4 = (r & 3) == 0;  // uniform
+    uint32_t keep[NQ], one[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int j0 = 16 * s + 4 * q4;
+      keep[s] = j0 < r ? 0xFFFFFFFFu : 0u;
+      one[s] = j0 == r ? 0x3C00u : 0u;  // fp16 1.0 in the low half
+    }
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
       const int i0 = (wave + kAttWaves * k) * 16;
       const int i = i0 + l16;
-      // Ux = [U | 1 | 0]; the anchor row has U = 0
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
+        if (whole4) {
+          const uint32_t kp = i > 0 ? keep[s] : 0u;
+          v2u w = __builtin_bit_cast(v2u, ua[k][s]);
+          w[0] = (w[0] & kp) | one[s];
+          w[1] = w[1] & kp;
+          ua[k][s] = __builtin_bit_cast(v4h, w);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * s + 4 * q4 + e;
-          ua[k][s][e] = (j == r) ? (f16)1.0f : ((i > 0 && j < r) ? ua[k][s][e] : (f16)0.0f);
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * s + 4 * q4 + e;
+            ua[k][s][e] = (j == r) ? (f16)1.0f : ((i > 0 && j < r) ? ua[k][s][e] : (f16)0.0f);
+          }
         }
         *reinterpret_cast<v4h*>(T + (k * 16 + l16) * TS + 16 * s + 4 * q4) = ua[k][s];
       }
@@ -1064,15 +1090,13 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     wave_sync_lds();
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
-      v4h ph, pl;
-      split_hl(pe[k][0], pe[k][1], pe[k][2], pe[k][3], ph, pl);
+      const v4h ph = to_h4(pe[k]);
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
         v4h au;
 #pragma unroll
         for (int e = 0; e < 4; ++e) au[e] = T[(k * 16 + 4 * q4 + e) * TS + 16 * n + l16];
         Wt[n] = mfma16(au, ph, Wt[n]);
-        Wt[n] = mfma16(au, pl, Wt[n]);
       }
     }
     wave_sync_lds();
@@ -1092,25 +1116,9 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
   }
 
-  // ---- fold the low-rank values into O^T per wave: O^T += VVx^T W^T (linear)
-  if (NRQ > 0 && lr) {
-    v4h wh[NQ], wl[NQ];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s) split_hl(Wt[s][0], Wt[s][1], Wt[s][2], Wt[s][3], wh[s], wl[s]);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-#pragma unroll
-      for (int s = 0; s < NRQ; ++s) {
-        v4h av;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) av[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
-        st.Ot[n] = mfma16(av, wh[s], st.Ot[n]);
-        st.Ot[n] = mfma16(av, wl[s], st.Ot[n]);
-      }
-    }
-  }
-
-  // ---- final phase: common maximum over the waves, fixed-order sum, stores
+  // ---- final phase: common maximum over the waves; the low-rank values
+  //      (VVx^T W^T, linear in W) folded once from the waves' summed W^T;
+  //      fixed-order sum over the waves; stores
   if (q4 == 0) {
     wstat[wave * 16 + l16] = st.m;
     wstat[kAttWaves * 16 + wave * 16 + l16] = st.l;
@@ -1121,9 +1129,53 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, wstat[w * 16 + l16]);
   const float be = (st.m == -INFINITY) ? 0.f : __expf(st.m - M);
   float* red = reinterpret_cast<float*>(region);  // [kAttWaves][16 heads][kRedStride]
+  v4f F[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // VVx^T W^T for d tiles 2 wave, 2 wave + 1
+  if (NRQ > 0 && lr) {
+    constexpr int WS = RQ + 4;  // floats per head row of wred
+    float* wred = red;          // [kAttWaves][16 heads][WS]: each wave's W, at the common maximum
+#pragma unroll
+    for (int s = 0; s < NQ; ++s)
+      *reinterpret_cast<float4*>(wred + (wave * 16 + l16) * WS + 16 * s + 4 * q4) =
+          make_float4(Wt[s][0] * be, Wt[s][1] * be, Wt[s][2] * be, Wt[s][3] * be);
+    lds_barrier();
+    v4h wh[NQ], wl[NQ];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int w = 0; w < kAttWaves; ++w) {
+        const float4 y = *reinterpret_cast<const float4*>(wred + (w * 16 + l16) * WS + 16 * s + 4 * q4);
+        x.x += y.x;
+        x.y += y.y;
+        x.z += y.z;
+        x.w += y.w;
+      }
+      split_hl(x.x, x.y, x.z, x.w, wh[s], wl[s]);
+    }
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) {
+      const int n = 2 * wave + nn;
+#pragma unroll
+      for (int s = 0; s < NRQ; ++s) {
+        v4h av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = vvx[(16 * s + 4 * q4 + e) * kVStride + 16 * n + l16];
+        F[nn] = mfma16(av, wh[s], F[nn]);
+        F[nn] = mfma16(av, wl[s], F[nn]);
+      }
+    }
+    lds_barrier();  // every wave has read wred before red overwrites it
+  }
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    const float4 v = make_float4(st.Ot[n][0] * be, st.Ot[n][1] * be, st.Ot[n][2] * be, st.Ot[n][3] * be);
+    float4 v = make_float4(st.Ot[n][0] * be, st.Ot[n][1] * be, st.Ot[n][2] * be, st.Ot[n][3] * be);
+    if ((n >> 1) == wave) {  // uniform
+      const v4f f = F[n & 1];
+      v.x += f[0];
+      v.y += f[1];
+      v.z += f[2];
+      v.w += f[3];
+    }
     *reinterpret_cast<float4*>(red + (wave * 16 + l16) * kRedStride + 16 * n + 4 * q4) = v;
   }
   lds_barrier();
@@ -1478,14 +1530,70 @@ struct LayersArgs {
   uint32_t* ctrl;  // [1] merges finished, [2] sticky wait-timeout flag, queue counters
   int n_layers;
   int n_units;     // units per layer (the same in every layer)
-  int routes;      // routing items per unit (0 or 1)
-  int parts;       // parts per unit
-  int group;       // merges per unit (query heads per KV head)
+  int routes;       // routing items per unit (0 or 1)
+  int block_parts;  // routed-block parts per unit
+  int win_parts;    // window parts per unit
+  int group;        // merges per unit (query heads per KV head)
 };
 
-// Work items of every layer from the per-XCD queues: a queue holds, for the
-// units u with u % 8 == x of every layer, first all routings, then all parts,
-// then all merges (layer-major), so every wait is on an item taken earlier.
+// Position i of XCD queue x (which holds the nx units u = x + 8 j of every
+// layer) -> (layer, item index within that layer's launch).  The queue holds
+// the routings of every layer, then the window parts of every layer (they wait
+// on nothing, and run while the routings finish), then the routed-block parts
+// of layer 0, 1, ..., with the merges of layer l placed after the block parts
+// of layer l + kMergeLag, when its parts are most likely done.  Every wait is
+// on an item earlier in the same queue.  Uniform (scalar) arithmetic.
+constexpr int kMergeLag = 2;
+
+__device__ __forceinline__ void layers_item(int i, int x, int nx, const LayersArgs& L, int& layer, int& item) {
+  const int NL = L.n_layers, NP = L.block_parts, NW = L.win_parts, G = L.group;
+  const int per_unit = NP + NW;
+  const int n_route = L.routes * L.n_units;
+  const int n_part_end = n_route + L.n_units * per_unit;
+  const int nR = nx * L.routes, nW = nx * NW, nP = nx * NP, nM = nx * G;
+  if (i < NL * nR) {
+    layer = i / nR;
+    item = x + kQueues * (i % nR);
+    return;
+  }
+  i -= NL * nR;
+  if (i < NL * nW) {
+    layer = i / nW;
+    const int r = i % nW;
+    item = n_route + (x + kQueues * (r / NW)) * per_unit + NP + r % NW;
+    return;
+  }
+  i -= NL * nW;
+  const int a = NL < kMergeLag ? NL : kMergeLag;
+  int kind = 0, r = 0;  // kind 0: block part of `layer`, 1: merge of `layer`
+  if (i < a * nP) {
+    layer = i / nP;
+    r = i % nP;
+  } else {
+    i -= a * nP;
+    const int pair = nP + nM;
+    if (i < (NL - a) * pair) {
+      const int c = i / pair;
+      r = i % pair;
+      if (r < nP) {
+        layer = a + c;
+      } else {
+        layer = c;
+        r -= nP;
+        kind = 1;
+      }
+    } else {
+      i -= (NL - a) * pair;
+      layer = NL - a + i / nM;
+      r = i % nM;
+      kind = 1;
+    }
+  }
+  item = kind == 0 ? n_route + (x + kQueues * (r / NP)) * per_unit + r % NP
+                   : n_part_end + (x + kQueues * (r / G)) * G + r % G;
+}
+
+// Work items of every layer from the per-XCD queues (see layers_item).
 // NMAX: the largest low-rank tile count of any layer (instances hold only the
 // attention variants up to it, which keeps register use down).
 template <int NMAX>
@@ -1495,36 +1603,27 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArg
   __shared__ int32_t sh_item, sh_layer, sh_slot;
   __shared__ uint32_t sh_flag;
   const int tid = threadIdx.x;
-  if (tid == 0) {
+  // wave 0 takes the ticket: lane 0 does the atomic, the mapping runs on the
+  // scalar unit
+  if (__builtin_amdgcn_readfirstlane(tid >> 6) == 0) {
     const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
-    const int R = L.routes, Pp = L.parts, G = L.group, NL = L.n_layers;
+    const int per_unit = L.routes + L.block_parts + L.win_parts + L.group;
     int item = -1, layer = 0;
     for (int k = 0; k < kQueues && item < 0; ++k) {
       const int x = (x0 + k) & (kQueues - 1);
       const int nx = L.n_units > x ? (L.n_units - x + kQueues - 1) / kQueues : 0;
-      const uint32_t size = (uint32_t)(NL * nx * (R + Pp + G));
+      const uint32_t size = (uint32_t)(L.n_layers * nx * per_unit);
       if (size == 0u) continue;
-      const uint32_t i = atomicAdd(&L.ctrl[kCtrlQueue + x * kQueueStride], 1u);
+      uint32_t i = 0u;
+      if (tid == 0) i = atomicAdd(&L.ctrl[kCtrlQueue + x * kQueueStride], 1u);
+      i = __builtin_amdgcn_readfirstlane(i);
       if (i >= size) continue;
-      const uint32_t nr = (uint32_t)(NL * nx * R), np = (uint32_t)(NL * nx * Pp);
-      const int n_route = R * L.n_units, n_part_end = n_route + L.n_units * Pp;
-      if (i < nr) {
-        layer = (int)i / nx;
-        item = x + kQueues * ((int)i % nx);
-      } else if (i < nr + np) {
-        const int j = (int)(i - nr);
-        layer = j / (nx * Pp);
-        const int r = j % (nx * Pp);
-        item = n_route + (x + kQueues * (r / Pp)) * Pp + r % Pp;
-      } else {
-        const int j = (int)(i - nr - np);
-        layer = j / (nx * G);
-        const int r = j % (nx * G);
-        item = n_part_end + (x + kQueues * (r / G)) * G + r % G;
-      }
+      layers_item((int)i, x, nx, L, layer, item);
     }
-    sh_item = item;
-    sh_layer = layer;
+    if (tid == 0) {
+      sh_item = item;
+      sh_layer = layer;
+    }
   }
   lds_barrier();
   // the item and its layer are the same in every lane: keep them, and the
@@ -1800,11 +1899,14 @@ struct WsLayout {
   size_t ctrl_bytes, unit_done, slots, idx, part_lse, part_o, total;
 };
 
-WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
+// fold: the window's tiles are shared out over the routed-block parts (else
+// the window has parts of its own, of kWinChunk rows)
+WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold = true) {
   WsLayout w;
   const size_t B = (size_t)batch->batch;
   const size_t units = B * (size_t)pool->n_kv_heads;
-  const size_t n_parts = top_k > 0 ? (size_t)top_k : (size_t)decode_win_parts(batch->window);
+  const size_t n_parts = (top_k > 0 && fold) ? (size_t)top_k
+                                             : (size_t)top_k + (size_t)decode_win_parts(batch->window);
   const size_t rows = B * (size_t)batch->n_q_heads;
   w.unit_done = kCtrlHeaderBytes;
   w.slots = w.unit_done + align256(units * 4);
@@ -1819,11 +1921,13 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k) 
 // Arguments of one layer's fused decode over the workspace region ws (laid out
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
-                             uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm) {
-  const WsLayout w = decode_layout(pool, batch, top_k);
-  // with routing, each routed-block part also takes its share of the window;
-  // without, the window comes in chunks of kWinChunk rows
-  const int n_win = top_k > 0 ? 0 : decode_win_parts(batch->window);
+                             uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
+                             bool fold = true) {
+  const WsLayout w = decode_layout(pool, batch, top_k, fold);
+  // folded, each routed-block part also takes its share of the window;
+  // otherwise the window comes in chunks of kWinChunk rows
+  fold = fold && top_k > 0;
+  const int n_win = fold ? 0 : decode_win_parts(batch->window);
   const int n_parts = top_k + n_win;
   const int units = batch->batch * pool->n_kv_heads;
   AttnArgs& a = D.att;
@@ -1833,7 +1937,7 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   a.block_mode = 3;
   a.n_win_parts = n_win;
   a.win_chunk = kWinChunk;
-  a.win_tile_stride = top_k;
+  a.win_tile_stride = fold ? top_k : 0;
   a.items_per_unit = n_parts;
   a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
   a.scale = scale;
@@ -2083,8 +2187,13 @@ size_t dkv_decode_layers_table_size(int32_t n_layers) {
   return n_layers > 0 ? (size_t)n_layers * sizeof(LayerArgs) : 0;
 }
 
+// the layer-batched launch gives the window parts of their own: with many
+// layers in flight no part waits long for its routing, and a part then has
+// one load phase rather than two
+constexpr bool kLayersFoldWindow = false;
+
 static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
-  return align256(decode_layout(pool, batch, top_k).total);
+  return align256(decode_layout(pool, batch, top_k, kLayersFoldWindow).total);
 }
 
 size_t dkv_decode_layers_workspace_size(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
@@ -2145,7 +2254,7 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     if (top_k > 0 && b0.batch > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) break;
     size_t shm_l = 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
-                               out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l)))
+                               out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow)))
       break;
     host[l].P = make_pool_args(pool);
     host[l].Bt = make_batch_args(pool, batch);
@@ -2163,9 +2272,11 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     plan->n_layers = n_layers;
     plan->n_units = units;
     plan->routes = top_k > 0 ? 1 : 0;
-    plan->parts = host[0].D.att.items_per_unit;
+    plan->parts = host[0].D.att.n_block_parts;
+    plan->win_parts = host[0].D.att.n_win_parts;
     plan->group = b0.n_q_heads / p0.n_kv_heads;
-    const int64_t items = (int64_t)n_layers * units * (plan->routes + plan->parts + plan->group);
+    const int64_t items =
+        (int64_t)n_layers * units * (plan->routes + plan->parts + plan->win_parts + plan->group);
     if (items > 0x7FFFFFFF) s = fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
     plan->n_items = (int32_t)items;
     plan->lds_bytes = (int32_t)shm;
@@ -2188,7 +2299,8 @@ dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
   L.n_layers = plan->n_layers;
   L.n_units = plan->n_units;
   L.routes = plan->routes;
-  L.parts = plan->parts;
+  L.block_parts = plan->parts;
+  L.win_parts = plan->win_parts;
   L.group = plan->group;
   switch (plan->max_tiles) {  // the largest low-rank tile count of the layers
     case 0: return launch_layers<0>(plan, L, (hipStream_t)stream);

@@ -65,7 +65,8 @@ class BatchC(ctypes.Structure):
 
 class LayersPlanC(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_units", ctypes.c_int32), ("routes", ctypes.c_int32),
-                ("parts", ctypes.c_int32), ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
+                ("parts", ctypes.c_int32), ("win_parts", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("table", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p)]
 

@@ -249,7 +249,10 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
  * different layers, or a model's layers evaluated on given queries.  All
  * layers share head_dim, block size, n_kv_heads and the batch shape (batch,
  * n_q_heads, window, max_blocks) and top_k; pools may differ in rank, residual
- * count and slot count.  Results are the same bits as n_layers dkv_decode calls.
+ * count and slot count.  The routed blocks are those of n_layers dkv_decode
+ * calls; the window rows are split into parts of their own (rather than shared
+ * out over the routed-block parts), so outputs equal dkv_decode's up to the
+ * rounding of that other split, and repeat bit for bit from launch to launch.
  *
  * dkv_decode_layers_prepare (once; synchronous, not capturable in a graph)
  * validates every layer, writes the per-layer argument table into `table`
@@ -267,7 +270,8 @@ typedef struct dkv_layers_plan {
   int32_t n_layers;
   int32_t n_units;        /* (sequence, KV head) units per layer */
   int32_t routes;         /* routing items per unit (0 or 1) */
-  int32_t parts;          /* parts per unit */
+  int32_t parts;          /* routed-block parts per unit */
+  int32_t win_parts;      /* window parts per unit */
   int32_t group;          /* merges per unit */
   int32_t n_items;        /* work items of one launch */
   int32_t lds_bytes;      /* dynamic LDS per workgroup */
