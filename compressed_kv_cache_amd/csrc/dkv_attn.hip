@@ -36,6 +36,8 @@
 
 #include "dkv_attn.h"
 
+#include <type_traits>
+
 typedef _Float16 f16;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -633,6 +635,7 @@ constexpr int kRedStride = 132;  // floats per row of the reduction buffer (conf
 
 __host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
 
+
 // per-wave scratch: the V tile of an exact tile, or the Ux transpose of a
 // low-rank tile, followed by that wave's residual-position bit mask
 // per-wave scratch: the wave's four transposed U tiles (low-rank phase) or two
@@ -898,6 +901,12 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     if (tid < G) st_dev(&A.part_lse[(int64_t)(row0 + tid) * A.n_parts + part], -INFINITY);
     return;
   }
+  // Everything from here on is straight-line from the issue of the loads to
+  // their uses (with or without the low-rank rows, chosen once), so that the
+  // compiler's wait counts let the first data be used while the rest is still
+  // in flight.
+  auto body = [&](auto lr_tag) {
+  constexpr bool LR = decltype(lr_tag)::value && NRQ > 0;
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
 
@@ -907,19 +916,22 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   v8h vvl[kVVChunks];
   v8h vkx[2][4];
   const f16* U = nullptr;
-  if (NRQ > 0 && lr) {
+  if constexpr (LR) {
     const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
     const f16* AV = P.av + slot * P.av_s + h * P.av_h;
     const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
     const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
     U = P.u + slot * P.u_s + h * P.u_h;
     {
+      // positions 0 (none) for lanes past n_resid; a pool without residual rows
+      // reads (and ignores) the first byte of the block's U
       const int nres = P.n_resid;
-      const uint8_t* pp = nres > 0 ? P.rp + slot * P.rp_s + h * P.rp_h : P.rp;
+      const uint8_t* pp = nres > 0 ? P.rp + slot * P.rp_s + h * P.rp_h : reinterpret_cast<const uint8_t*>(U);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int t = lane + 64 * k;
-        ps[k] = (nres > 0) ? (int)pp[t < nres ? t : 0] : 0;
+        const int v = (int)pp[t < nres ? t : 0];
+        ps[k] = t < nres ? v : 0;
       }
     }
     // VVx rows: V_V rows j < r, a_v at j = r.  Padding rows j > r read V_V row 0:
@@ -935,49 +947,44 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     // (they only meet zero columns of Ux)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int j = (wave + kAttWaves * k) * 16 + l16;
-      const f16* src = (j < r) ? VK + (int64_t)j * kD : ((j == r) ? AK : VK);
-      if (wave + kAttWaves * k < NRQ) {
+      if (kAttWaves * k < NRQ) {  // compile time; every wave loads (tiles past NRQ read V_K row 0, unused)
+        const int j = (wave + kAttWaves * k) * 16 + l16;
+        const f16* src = (j < r) ? VK + (int64_t)j * kD : ((j == r) ? AK : VK);
 #pragma unroll
         for (int s = 0; s < 4; ++s) vkx[k][s] = ld8(src + 32 * s + 8 * q4);
       }
     }
-    if ((r & 3) == 0) {
+    // U: four columns j0 .. j0 + 3 of row i - 1 per lane, as one 8-byte load
+    // (2-byte aligned when r % 4 != 0).  Padding columns read columns 0 .. 3.
+    // A load that would run past the block's last U element starts 1 .. 3
+    // elements earlier and is shifted back into place before use.
 #pragma unroll
-      for (int k = 0; k < kLRTilesPerWave; ++k) {
-        const int i = (wave + kAttWaves * k) * 16 + l16;  // position in the block; 0 = anchor
-        const f16* row = U + (int64_t)(i > 0 ? i - 1 : 0) * r;
+    for (int k = 0; k < kLRTilesPerWave; ++k) {
+      const int i = (wave + kAttWaves * k) * 16 + l16;  // position in the block; 0 = anchor
+      const int row = i > 0 ? i - 1 : 0;
 #pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-          const int j0 = 16 * s + 4 * q4;
-          ua[k][s] = *reinterpret_cast<const v4h*>(row + (j0 < r ? j0 : 0));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kLRTilesPerWave; ++k) {
-        const int i = (wave + kAttWaves * k) * 16 + l16;
-        const f16* row = U + (int64_t)(i > 0 ? i - 1 : 0) * r;
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 16 * s + 4 * q4 + e;
-            ua[k][s][e] = row[j < r ? j : 0];
-          }
-        }
+      for (int s = 0; s < NQ; ++s) {
+        const int j0 = 16 * s + 4 * q4;
+        const int e0 = row * r + (j0 < r ? j0 : 0);
+        const int lim = kLowRankRows * r - 4;
+        __builtin_memcpy(&ua[k][s], U + (e0 < lim ? e0 : (lim > 0 ? lim : 0)), 8);
       }
     }
   }
   v8h ka[4], va[4], kb[4], vb[4];
   int ta = wave, tb = wave + kAttWaves;
-  if (n_ex > 0) {
-    load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
-    load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
+  {
+    // issued in every case (a part without exact rows reads its first query
+    // row, unused), so that no branch separates these loads from the waits for
+    // earlier ones
+    const bool none = n_ex == 0;
+    const f16* qrow0 = Bt.q + (int64_t)row0 * kD;
+    load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, ta, none ? 1 : ntile, none ? 1 : n_ex, ka, va, l16, q4);
+    load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, tb, none ? 1 : ntile, none ? 1 : n_ex, kb, vb, l16, q4);
   }
 
   // ---- low-rank set-up: residual-position mask (per wave), VVx, VKx q
-  if (NRQ > 0 && lr) {
+  if constexpr (LR) {
     if (lane < 8) wmask[lane] = 0u;
     wave_sync_lds();
 #pragma unroll
@@ -1017,36 +1024,31 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
     f16* T = reinterpret_cast<f16*>(my);  // [kLRTilesPerWave][16][TS]
     float zz[kLRTilesPerWave][4];
-    // Ux = [U | 1 | 0]; the anchor row has U = 0.  With r % 4 == 0 a lane's four
-    // columns j0 .. j0 + 3 are all below r, or are r, r + 1, .. (then only the
-    // first is 1), or are all padding: two bit masks per 16-column tile.
-    const bool whole4 = (r & 3) == 0;  // uniform
-    uint32_t keep[NQ], one[NQ];
+    // Ux = [U | 1 | 0]; the anchor row has U = 0.  Per lane and 16-column
+    // tile: a 64-bit mask keeping the columns below r and the fp16 1.0 at
+    // column r (if it is among the lane's four).
+    uint64_t keep[NQ], one[NQ];
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       const int j0 = 16 * s + 4 * q4;
-      keep[s] = j0 < r ? 0xFFFFFFFFu : 0u;
-      one[s] = j0 == r ? 0x3C00u : 0u;  // fp16 1.0 in the low half
+      const int nk = r - j0;  // columns of the four below r
+      keep[s] = nk >= 4 ? ~0ull : (nk <= 0 ? 0ull : ((1ull << (16 * nk)) - 1ull));
+      one[s] = (nk >= 0 && nk < 4) ? (0x3C00ull << (16 * nk)) : 0ull;
     }
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k) {
       const int i0 = (wave + kAttWaves * k) * 16;
       const int i = i0 + l16;
+      const int row = i > 0 ? i - 1 : 0;
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
-        if (whole4) {
-          const uint32_t kp = i > 0 ? keep[s] : 0u;
-          v2u w = __builtin_bit_cast(v2u, ua[k][s]);
-          w[0] = (w[0] & kp) | one[s];
-          w[1] = w[1] & kp;
-          ua[k][s] = __builtin_bit_cast(v4h, w);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 16 * s + 4 * q4 + e;
-            ua[k][s][e] = (j == r) ? (f16)1.0f : ((i > 0 && j < r) ? ua[k][s][e] : (f16)0.0f);
-          }
-        }
+        const int j0 = 16 * s + 4 * q4;
+        const int e0 = row * r + (j0 < r ? j0 : 0);
+        const int lim = kLowRankRows * r - 4;
+        const int back = e0 - (e0 < lim ? e0 : (lim > 0 ? lim : 0));  // 0 .. 3 elements
+        uint64_t w = __builtin_bit_cast(uint64_t, ua[k][s]) >> (16 * back);
+        w = (w & (i > 0 ? keep[s] : 0ull)) | one[s];
+        ua[k][s] = __builtin_bit_cast(v4h, w);
         *reinterpret_cast<v4h*>(T + (k * 16 + l16) * TS + 16 * s + 4 * q4) = ua[k][s];
       }
       v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -1130,7 +1132,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   const float be = (st.m == -INFINITY) ? 0.f : __expf(st.m - M);
   float* red = reinterpret_cast<float*>(region);  // [kAttWaves][16 heads][kRedStride]
   v4f F[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};  // VVx^T W^T for d tiles 2 wave, 2 wave + 1
-  if (NRQ > 0 && lr) {
+  if constexpr (LR) {
     constexpr int WS = RQ + 4;  // floats per head row of wred
     float* wred = red;          // [kAttWaves][16 heads][WS]: each wave's W, at the common maximum
 #pragma unroll
@@ -1202,6 +1204,11 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
                  make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv));
     if (c4 == 0) st_dev(&A.part_lse[(int64_t)(row0 + g) * A.n_parts + part], (Lg > 0.f) ? Mg + __logf(Lg) : -INFINITY);
   }
+  };
+  if (NRQ > 0 && lr)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 template <int NRQ>
