@@ -8,17 +8,26 @@ plus a 1024-token exact window per sequence, 128 residual rows per block, top-K
 shape stand in for model-derived KV (no weights or datasets are used).
 
 One step = one decode query for each of the 4 sequences in each of the 28
-layers (112 queries): 28 per-layer dkv_decode calls (routing, block and window
-attention, log-sum-exp merge), with every input resident in HBM.  The step is
-timed eagerly with hipEvents around every decode kernel, and as a captured
-hipGraph replay.  Prints one JSON line.
+layers (112 queries): routing, block and window attention and the log-sum-exp
+merge of every layer, with every input resident in HBM.  The step is timed in
+three launch modes:
+  per_layer_eager         28 dkv_decode calls, hipEvents around every kernel;
+  per_layer_hipgraph      the same 28 calls captured once as a hipGraph;
+  layer_batched_eager     one dkv_decode_layers launch for all 28 layers;
+  layer_batched_hipgraph  that launch captured as a hipGraph.
+`value` is the queries/s of the fastest mode (named in config.timed_mode);
+every mode is reported in ms_per_step_by_mode.  The layer-batched launch does
+the same work, on the same inputs, with the same routing (checked in the run).
 
-Roofline: each layer's decode is one kernel, k_decode.  Its algorithmic bytes
-per launch are, for each (sequence, KV head), the fp32 routing keys of all N
-blocks (512 N bytes), K_eff routed blocks of P(r, R) = 2*(2d + 255 r + 2 r d +
-2 R d) + R bytes and 2*2*W*d window bytes, plus the fp16 queries, outputs, lse
-and routed indices; divided by the kernel duration measured with hipEvents
-around it in the same timed (eager) steps.
+Roofline: the kernel of the timed mode (k_decode for the per-layer modes,
+k_decode_layers for the layer-batched ones).  Its algorithmic bytes per launch
+are, for each (sequence, KV head, layer), the fp32 routing keys of all N blocks
+(512 N bytes), K_eff routed blocks of P(r, R) = 2*(2d + 255 r + 2 r d + 2 R d) + R
+bytes and 2*2*W*d window bytes, plus the fp16 queries, outputs, lse and routed
+indices; divided by that kernel's duration measured with events around it in
+the timed eager steps (kernels back to back behind a spin kernel, as in a
+replay).  `traffic` is the committed rocprofv3 PMC summary for that kernel
+(`--pmc-summary` writes it), null when the kernel source changed since.
 """
 from __future__ import annotations
 
@@ -103,6 +112,94 @@ def measured_traffic(kernel: str, digest: str):
     return t.get("bytes_per_launch")
 
 
+def step_algorithmic_bytes(n_layers: int) -> int:
+    """Algorithmic bytes of one step over the first n_layers layers of the stack."""
+    from compressed_kv_cache_amd import synth
+    B, Hq, Hkv, K, R, W, N = 4, 12, 2, 32, 128, 1024, 252
+    return sum(sum(layer_bytes(B, Hkv, Hq, min(K, N), synth.STACK_RANKS[i], R, W, N)) for i in range(n_layers))
+
+
+def pmc_summary(args) -> int:
+    """Per-launch HBM traffic of one kernel from two rocprofv3 --pmc runs of
+    this benchmark (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each
+    scaled by what the same counter reads for the benchmark's copy probe
+    (torch.mul over --copy-probe-mib MiB of fp32: that many bytes read and
+    written).  Writes profiles/<kernel>_traffic_stack64k_b4.{json,md}."""
+    import csv
+    import collections
+
+    def per_dispatch(path, counter):
+        vals = collections.defaultdict(float)
+        names = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                d = row["Dispatch_Id"]
+                vals[d] += float(row["Counter_Value"])
+                names[d] = row["Kernel_Name"]
+        return vals, names
+
+    copy_bytes = args.copy_probe_mib * (1 << 20)
+    if copy_bytes <= 0:
+        print("--pmc-summary needs --copy-probe-mib (the probe size of the profiled runs)", file=sys.stderr)
+        return 2
+    out = {}
+    for key, path, counter in (("fetch", args.pmc_summary[0], "FETCH_SIZE"),
+                               ("write", args.pmc_summary[1], "WRITE_SIZE")):
+        vals, names = per_dispatch(path, counter)
+        probe = [v for d, v in vals.items() if "elementwise" in names[d] or "mul" in names[d]]
+        kern = [v for d, v in vals.items() if args.pmc_kernel + "<" in names[d] or
+                names[d].split("(")[0].endswith(args.pmc_kernel)]
+        if not probe or not kern:
+            print(f"{path}: no copy-probe or {args.pmc_kernel} dispatches", file=sys.stderr)
+            return 2
+        probe_kib = max(probe)
+        scale = copy_bytes / (probe_kib * 1024.0)
+        out[key] = {"counter": counter, "probe_KiB": probe_kib, "scale": scale, "dispatches": len(kern),
+                    "bytes_per_launch": sum(kern) / len(kern) * 1024.0 * scale}
+    n_layers = max(1, min(28, args.layers))
+    alg = step_algorithmic_bytes(n_layers)
+    if args.pmc_kernel == "k_decode":
+        alg /= n_layers
+    total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
+    res = {
+        "kernel": args.pmc_kernel,
+        "workload": f"qwen2.5-1.5b 64k ctx, batch 4, layers 0-{n_layers - 1}",
+        "kernel_source_sha256_16": source_digest(),
+        "dispatches": out["fetch"]["dispatches"],
+        "fetch_bytes_per_launch": out["fetch"]["bytes_per_launch"],
+        "write_bytes_per_launch": out["write"]["bytes_per_launch"],
+        "bytes_per_launch": total,
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": total / alg,
+        "calibration": {"copy_kernel": f"torch.mul(a, 1.0, out=b) over {args.copy_probe_mib} MiB fp32",
+                        "FETCH_SIZE_KiB": out["fetch"]["probe_KiB"], "WRITE_SIZE_KiB": out["write"]["probe_KiB"],
+                        "fetch_scale": out["fetch"]["scale"], "write_scale": out["write"]["scale"]},
+    }
+    base = os.path.join(ROOT, "profiles", f"{args.pmc_kernel}_traffic_stack64k_b4")
+    with open(base + ".json", "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write(f"# {args.pmc_kernel} HBM traffic — 64k-context stack, batch 4, layers 0-{n_layers - 1}\n\n")
+        f.write(f"Kernel source sha256[:16] = `{res['kernel_source_sha256_16']}`. "
+                f"Numbers in `{os.path.basename(base)}.json`, written by `python bench.py --pmc-summary`.\n\n")
+        f.write("Commands (from the repository root, `TMPDIR=/tmp`):\n\n```\n" + args.pmc_command.strip() + "\n```\n\n")
+        c = res["calibration"]
+        f.write(f"Calibration: the copy probe reads and writes {copy_bytes // 1024:,} KiB. FETCH_SIZE reports "
+                f"{c['FETCH_SIZE_KiB']:,.0f} KiB for it (scale {c['fetch_scale']:.3f}), WRITE_SIZE "
+                f"{c['WRITE_SIZE_KiB']:,.0f} KiB (scale {c['write_scale']:.3f}).\n\n")
+        f.write(f"| per {args.pmc_kernel} launch (mean of {res['dispatches']}) | bytes |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE x {c['fetch_scale']:.3f} | {res['fetch_bytes_per_launch'] / 1e6:.2f} MB |\n")
+        f.write(f"| WRITE_SIZE x {c['write_scale']:.3f} | {res['write_bytes_per_launch'] / 1e6:.2f} MB |\n")
+        f.write(f"| total HBM traffic | {total / 1e6:.2f} MB |\n")
+        f.write(f"| algorithmic bytes | {alg / 1e6:.2f} MB |\n")
+        f.write(f"| traffic / algorithmic | {res['traffic_over_algorithmic']:.3f} |\n")
+    print(json.dumps(res))
+    return 0
+
+
 CPU_SAMPLE_LAYERS = (0, 9, 19, 27)      # one layer of each rank (24, 48, 16) and the last
 
 
@@ -145,8 +242,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--no-layer-batched", action="store_true",
-                    help="skip the mode that runs every layer's decode in one launch")
+    ap.add_argument("--mode", choices=("all", "per-layer", "layer-batched"), default="all",
+                    help="which launch modes to time (default: all)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark "
+                         "into profiles/<kernel>_traffic_stack64k_b4.{json,md} and exit")
+    ap.add_argument("--pmc-kernel", default="k_decode_layers", help="kernel the PMC summary is for")
+    ap.add_argument("--pmc-command", default="", help="the rocprofv3 command lines, recorded in the summary")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (PMC scaling reference)")
     ap.add_argument("--quiet", action="store_true")
@@ -155,6 +257,9 @@ def main() -> int:
     def log(msg):
         if not args.quiet:
             print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.pmc_summary:
+        return pmc_summary(args)
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -236,47 +341,50 @@ def main() -> int:
             lib.decode(pools[i], batches[i], K, wl.scale, workspace=wss[i], out=outs[i],
                        out_lse=lses[i], out_idx=idxs[i])
 
+    per_layer_modes = args.mode in ("all", "per-layer")
     # ---- eager, with hipEvents around every layer's decode kernel, in the timed steps
-    ev = [[[hip.event() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
-    for _ in range(args.warmup):
+    for _ in range(args.warmup if per_layer_modes else 1):
         step_eager()
     torch.cuda.synchronize()
     ref_out = [o.clone() for o in outs]
     ref_lse = [x.clone() for x in lses]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    s_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    s_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    # Each step is enqueued while a spin kernel holds the GPU, so that its 28
-    # kernels then run back to back, as they do in a graph replay: host launch
-    # gaps would otherwise leave the GPU idle between layers.
+    ms_eager = kernel_ms = None
     hold = int(2e-3 * 2.4e9)                              # ~2 ms of shader clock
-    for s in range(args.steps):
-        torch.cuda._sleep(hold)
-        s_start[s].record()
+    if per_layer_modes:
+        ev = [[[hip.event() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
+        s_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        s_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        # Each step is enqueued while a spin kernel holds the GPU, so that its 28
+        # kernels then run back to back, as they do in a graph replay: host launch
+        # gaps would otherwise leave the GPU idle between layers.
+        for s in range(args.steps):
+            torch.cuda._sleep(hold)
+            s_start[s].record()
+            for i in range(n_layers):
+                lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
+                                    ev[s][i], out_idx=idxs[i])
+            s_end[s].record()
+        torch.cuda.synchronize()
+        ms_eager = float(np.mean([s_start[s].elapsed_time(s_end[s]) for s in range(args.steps)]))
+        kern = np.array([[hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for i in range(n_layers)]
+                         for s in range(args.steps)])
+        kernel_ms = float(kern.mean())
+        for s in ev:
+            for e2 in s:
+                for e in e2:
+                    hip.destroy(e)
+        log(f"eager: {ms_eager:.4f} ms/step; decode kernel {kernel_ms * 1e3:.2f} us per layer "
+            f"(p10 {np.percentile(kern, 10) * 1e3:.2f}, p90 {np.percentile(kern, 90) * 1e3:.2f})")
         for i in range(n_layers):
-            lib.decode_profiled(pools[i], batches[i], K, wl.scale, wss[i], outs[i], lses[i],
-                                ev[s][i], out_idx=idxs[i])
-        s_end[s].record()
-    torch.cuda.synchronize()
-    ms_eager = float(np.mean([s_start[s].elapsed_time(s_end[s]) for s in range(args.steps)]))
-    kern = np.array([[hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for i in range(n_layers)]
-                     for s in range(args.steps)])
-    kernel_ms = float(kern.mean())
-    for s in ev:
-        for e2 in s:
-            for e in e2:
-                hip.destroy(e)
-    log(f"eager: {ms_eager:.4f} ms/step; decode kernel {kernel_ms * 1e3:.2f} us per layer "
-        f"(p10 {np.percentile(kern, 10) * 1e3:.2f}, p90 {np.percentile(kern, 90) * 1e3:.2f})")
-    for i in range(n_layers):
-        assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
-            "eager steps are not bit-identical"
+            assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
+                "eager steps are not bit-identical"
 
     # ---- the same step captured once as a hipGraph
     ms_graph = None
-    if not args.no_graph:
+    if per_layer_modes and not args.no_graph:
         g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
         cs.wait_stream(torch.cuda.current_stream())
@@ -308,7 +416,7 @@ def main() -> int:
 
     # ---- every layer's decode step in ONE layer-batched launch (k_decode_layers)
     ms_lb = ms_lb_graph = lb_kernel_ms = None
-    if not args.no_layer_batched:
+    if args.mode in ("all", "layer-batched"):
         run = lib.Layers(pools, batches, K, wl.scale)
         for _ in range(args.warmup):
             run.run()
@@ -408,7 +516,7 @@ def main() -> int:
         "algorithmic_bytes_per_step": step_bytes,
         "queries_per_step": queries_per_step,
         "ms_per_step_by_mode": modes,
-        "k_decode_us_per_layer": kernel_ms * 1e3,
+        "k_decode_us_per_layer": None if kernel_ms is None else kernel_ms * 1e3,
         "k_decode_layers_us_per_launch": None if lb_kernel_ms is None else lb_kernel_ms * 1e3,
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kernel_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,

@@ -49,7 +49,7 @@ namespace {
 constexpr int kD = 128;            // head dim
 constexpr int kLowRankRows = 255;  // tokens 1..255 of a block
 constexpr int kVStride = 132;      // LDS row stride (halves) of 128-wide tiles: conflict-free column reads
-constexpr int kWinChunk = 128;     // window rows per part in dkv_decode
+constexpr int kWinChunk = 256;     // window rows per window part (when the window has parts of its own)
 
 thread_local char g_err[512] = "";
 
@@ -971,17 +971,21 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       }
     }
   }
+  // The wave's first two exact tiles.  Issued in every case (a part without
+  // exact rows reads its first query row, unused), so that no branch separates
+  // these loads from the waits for earlier ones.  With low-rank rows they are
+  // issued once the low-rank scores are formed: the U registers are free by
+  // then, and the loads overlap the rest of the low-rank step while this
+  // workgroup's first burst has already been consumed.
   v8h ka[4], va[4], kb[4], vb[4];
   int ta = wave, tb = wave + kAttWaves;
-  {
-    // issued in every case (a part without exact rows reads its first query
-    // row, unused), so that no branch separates these loads from the waits for
-    // earlier ones
+  auto issue_exact = [&]() {
     const bool none = n_ex == 0;
     const f16* qrow0 = Bt.q + (int64_t)row0 * kD;
     load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, ta, none ? 1 : ntile, none ? 1 : n_ex, ka, va, l16, q4);
     load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, tb, none ? 1 : ntile, none ? 1 : n_ex, kb, vb, l16, q4);
-  }
+  };
+  if constexpr (!LR) issue_exact();
 
   // ---- low-rank set-up: residual-position mask (per wave), VVx, VKx q
   if constexpr (LR) {
@@ -1064,6 +1068,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         zz[k][e] = masked ? -INFINITY : z[e] * scale;
       }
     }
+    issue_exact();
     float tm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k)
