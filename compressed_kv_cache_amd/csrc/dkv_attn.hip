@@ -716,11 +716,17 @@ __device__ __forceinline__ void stage_v_tile(f16* Vt, const v8h (&vx)[4], int l1
 // One softmax step over two 16-row exact tiles (b optional): scores, a common
 // maximum, the rescale of the state and of the low-rank accumulator, and PV.
 // rows_a / rows_b: valid rows of each tile (the rest are masked out).
-template <int NQ>
+struct NoNext {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// next(): issued once the pair's K and V registers are consumed (V staged in
+// LDS), to load the following pair into them while this one finishes.
+template <int NQ, class Next = NoNext>
 __device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h (&ka)[4], const v8h (&va)[4],
                                            const v8h (&kb)[4], const v8h (&vb)[4], int rows_a, int rows_b,
                                            bool has_b, const v4h (&qf)[4][2], float scale, f16* Va, f16* Vb,
-                                           int l16, int q4) {
+                                           int l16, int q4, Next&& next = Next()) {
   const v4f Sa = exact_scores(ka, qf);
   const v4f Sb = exact_scores(kb, qf);
   float za[4], zb[4];
@@ -757,6 +763,7 @@ __device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h
   }
   stage_v_tile(Va, va, l16, q4);
   if (has_b) stage_v_tile(Vb, vb, l16, q4);
+  next();
   wave_sync_lds();
   exact_pv(st, Va, pa, l16, q4);
   if (has_b) exact_pv(st, Vb, pb, l16, q4);
@@ -1115,11 +1122,14 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     f16* Vb = Va + 16 * kVStride;
     while (ta < ntile) {
       const bool has_b = tb < ntile;  // uniform over the wave
-      exact_pair<NQ>(st, Wt, ka, va, kb, vb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, scale, Va, Vb, l16, q4);
-      ta += 2 * kAttWaves;
-      tb += 2 * kAttWaves;
-      if (ta < ntile) load_exact_tile(exk, exv, ta, ntile, n_ex, ka, va, l16, q4);
-      if (tb < ntile) load_exact_tile(exk, exv, tb, ntile, n_ex, kb, vb, l16, q4);
+      const int ta_n = ta + 2 * kAttWaves, tb_n = tb + 2 * kAttWaves;
+      exact_pair<NQ>(st, Wt, ka, va, kb, vb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, scale, Va, Vb, l16, q4,
+                     [&]() {
+                       if (ta_n < ntile) load_exact_tile(exk, exv, ta_n, ntile, n_ex, ka, va, l16, q4);
+                       if (tb_n < ntile) load_exact_tile(exk, exv, tb_n, ntile, n_ex, kb, vb, l16, q4);
+                     });
+      ta = ta_n;
+      tb = tb_n;
     }
   }
 
@@ -1641,7 +1651,17 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArg
   // the item and its layer are the same in every lane: keep them, and the
   // layer's arguments, in scalar registers
   const int t = __builtin_amdgcn_readfirstlane(sh_item);
-  const LayerArgs la = table[__builtin_amdgcn_readfirstlane(sh_layer)];
+  // read through the constant address space (scalar loads, scalar registers)
+  static_assert(sizeof(LayerArgs) % 4 == 0, "LayerArgs is copied as 32-bit words");
+  constexpr int kArgWords = (int)(sizeof(LayerArgs) / 4);
+  typedef const __attribute__((address_space(4))) uint32_t ConstWord;
+  uint32_t words[kArgWords];
+  {
+    ConstWord* src = (ConstWord*)table + (int64_t)__builtin_amdgcn_readfirstlane(sh_layer) * kArgWords;
+#pragma unroll
+    for (int k = 0; k < kArgWords; ++k) words[k] = src[k];
+  }
+  const LayerArgs la = __builtin_bit_cast(LayerArgs, words);
   if (t >= 0) {
     if (la.nrq <= 0 || NMAX == 0)
       decode_item<0>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
