@@ -30,6 +30,16 @@ window rows ~ N(0, 1); U[:, j] ~ N(0, sigma_j^2) with sigma_j = s0 * decay^j;
 V_K and V_V have orthonormal rows (transposed Q factor of a d x r Gaussian).
 All values are drawn in float32 and rounded once to fp16 (round to nearest
 even).
+
+Quantised residual formats (README "Physical 4-Bit Group-Quantized Residual
+Buffers", "Tunable Quantization Dials": groups of 64 dimensions, 8 or 4 bits,
+an fp16 scale and bias per group).  The stored bytes are drawn directly:
+  resid_k, resid_v        uint8 [S][Hkv][R][d] codes (8 bits), or
+                          uint8 [S][Hkv][R][d/2], two 4-bit codes per byte
+  resid_k_sb, resid_v_sb  fp16 [S][Hkv][R][d/64][2] = (scale, bias)
+Codes are uniform; scales uniform in [0.012, 0.020] (8 bits) or [0.20, 0.30]
+(4 bits) and biases ~ N(-2.0, 0.3) or N(-1.9, 0.2), so that the rows they
+stand for span roughly [-2, 2].
 """
 from __future__ import annotations
 
@@ -43,6 +53,8 @@ import numpy as np
 HEAD_DIM = 128
 BLOCK_SIZE = 256
 LOWRANK_ROWS = BLOCK_SIZE - 1
+QUANT_GROUP = 64
+RESID_FP16, RESID_INT8, RESID_INT4 = 0, 1, 2
 
 
 @dataclasses.dataclass
@@ -59,11 +71,19 @@ class Layer:
     q: np.ndarray
     win_k: np.ndarray
     win_v: np.ndarray
+    resid_format: int = RESID_FP16
+    resid_k_sb: Optional[np.ndarray] = None
+    resid_v_sb: Optional[np.ndarray] = None
 
     def pool(self) -> dict:
         """The block-store arrays as a plain dict (the oracle's input form)."""
-        return {k: getattr(self, k) for k in
-                ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+        d = {k: getattr(self, k) for k in
+             ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+        if self.resid_format != RESID_FP16:
+            d["resid_format"] = self.resid_format
+            d["resid_k_sb"] = self.resid_k_sb
+            d["resid_v_sb"] = self.resid_v_sb
+        return d
 
 
 @dataclasses.dataclass
@@ -171,10 +191,25 @@ def _positions(rng: np.random.Generator, lead: tuple, n_resid: int) -> np.ndarra
     return np.sort(pos, axis=-1).astype(np.uint8)
 
 
+def _quantised_residuals(rng: np.random.Generator, lead: tuple, n_resid: int, d: int, fmt: int):
+    """Codes and (scale, bias) pairs of the K and V residual rows, drawn directly."""
+    kids = rng.spawn(6)
+    width = d if fmt == RESID_INT8 else d // 2
+    lo, hi, mu, sd = (0.012, 0.020, -2.0, 0.3) if fmt == RESID_INT8 else (0.20, 0.30, -1.9, 0.2)
+    out = []
+    for i in range(2):
+        codes = kids[3 * i].integers(0, 256, size=lead + (n_resid, width), dtype=np.uint8)
+        sb = np.empty(lead + (n_resid, d // QUANT_GROUP, 2), dtype=np.float32)
+        sb[..., 0] = kids[3 * i + 1].uniform(lo, hi, size=sb.shape[:-1])
+        sb[..., 1] = kids[3 * i + 2].normal(mu, sd, size=sb.shape[:-1])
+        out.append((np.ascontiguousarray(codes), _f16(sb)))
+    return out
+
+
 def make_layer(rng: np.random.Generator, *, n_slots: int, batch: int, n_q_heads: int,
                n_kv_heads: int, window: int, rank: int, n_resid: int,
                sigma0: float = 0.5, decay: float = 0.9, zero_anchor: bool = False,
-               head_dim: int = HEAD_DIM) -> Layer:
+               head_dim: int = HEAD_DIM, resid_format: int = RESID_FP16) -> Layer:
     """Draw one layer's pool, query and window with child streams in a fixed order."""
     d = head_dim
     streams = rng.spawn(9)
@@ -188,15 +223,20 @@ def make_layer(rng: np.random.Generator, *, n_slots: int, batch: int, n_q_heads:
     u = _normal(streams[2], lead + (LOWRANK_ROWS, rank)) * sig
     vk = _orthonormal_rows(streams[3], lead, rank, d)
     vv = _orthonormal_rows(streams[4], lead, rank, d)
-    rk = _normal(streams[5], lead + (n_resid, d))
-    rv = _normal(streams[5], lead + (n_resid, d))
+    ksb = vsb = None
+    if resid_format == RESID_FP16:
+        rk = _f16(_normal(streams[5], lead + (n_resid, d)))
+        rv = _f16(_normal(streams[5], lead + (n_resid, d)))
+    else:
+        (rk, ksb), (rv, vsb) = _quantised_residuals(rng.spawn(1)[0], lead, n_resid, d, resid_format)
     pos = _positions(streams[6], lead, n_resid)
     q = _normal(streams[7], (batch, n_q_heads, d))
     wk = _normal(streams[8], (batch, n_kv_heads, window, d))
     wv = _normal(streams[8], (batch, n_kv_heads, window, d))
     return Layer(rank=rank, anchor_k=_f16(ak), anchor_v=_f16(av), u=_f16(u), vk=_f16(vk),
-                 vv=_f16(vv), resid_k=_f16(rk), resid_v=_f16(rv), resid_pos=pos,
-                 q=_f16(q), win_k=_f16(wk), win_v=_f16(wv))
+                 vv=_f16(vv), resid_k=rk, resid_v=rv, resid_pos=pos,
+                 q=_f16(q), win_k=_f16(wk), win_v=_f16(wv), resid_format=resid_format,
+                 resid_k_sb=ksb, resid_v_sb=vsb)
 
 
 def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_heads: int,
@@ -205,7 +245,7 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
                   permute_slots: bool = False, zero_anchor: bool = False,
                   win_len: Optional[Sequence[int]] = None, max_blocks: Optional[int] = None,
                   head_dim: int = HEAD_DIM, only_layers: Optional[Sequence[int]] = None,
-                  notes: str = "") -> Workload:
+                  notes: str = "", resid_format: int = RESID_FP16) -> Workload:
     """Generic seeded workload: one Layer per entry of `ranks`.
 
     Sequence b owns n_blocks[b] logical blocks; their pool slots are
@@ -237,7 +277,8 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
         layers.append(make_layer(lrng, n_slots=max(total, 1), batch=batch, n_q_heads=n_q_heads,
                                  n_kv_heads=n_kv_heads, window=window, rank=int(ranks[li]),
                                  n_resid=n_resid, sigma0=sigma0, decay=decay,
-                                 zero_anchor=zero_anchor, head_dim=head_dim))
+                                 zero_anchor=zero_anchor, head_dim=head_dim,
+                                 resid_format=resid_format))
     return Workload(name=name, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                     head_dim=head_dim, window=window, n_resid=n_resid, top_k=top_k,
                     scale=float(1.0 / np.sqrt(head_dim)), block_table=table, n_blocks=nb,
@@ -289,8 +330,19 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
                 variant: str = "") -> Workload:
     """Build configuration `cfg` (0..4).  `layers` selects a subset of the
     28-layer stack (config 2) to bound host memory; `variant` is one of
-    "", "S1" (sigma_j = 4 * 0.9^j) or "S2" (zero anchors) for config 0."""
+    "", "S1" (sigma_j = 4 * 0.9^j) or "S2" (zero anchors) for config 0, or
+    "Q8" / "Q4" (residual rows in the 8- or 4-bit group-quantised format) for
+    configs 0, 1 and 2."""
     seed = 1000 + cfg if seed is None else seed
+    if variant in ("Q8", "Q4"):
+        fmt = RESID_INT8 if variant == "Q8" else RESID_INT4
+        base = {0: dict(batch=1, n_q_heads=1, n_kv_heads=1, window=512, n_blocks=[14], ranks=[32],
+                        n_resid=40, top_k=14),
+                1: dict(batch=1, n_q_heads=12, n_kv_heads=2, window=1024, n_blocks=[60], ranks=[32],
+                        n_resid=128, top_k=16),
+                2: dict(batch=4, n_q_heads=12, n_kv_heads=2, window=1024, n_blocks=[252] * 4,
+                        ranks=STACK_RANKS, n_resid=128, top_k=32, only_layers=layers)}[cfg]
+        return make_workload(CONFIG_NAMES[cfg] + "_" + variant, seed=seed, resid_format=fmt, **base)
     if cfg == 0:
         sigma0 = 4.0 if variant == "S1" else 0.5
         return make_workload(CONFIG_NAMES[0] + (("_" + variant) if variant else ""), seed=seed,

@@ -28,12 +28,21 @@ What it computes (sources are the pages on DKV, cited by title and section):
   (the pages keep per-block decode-router metadata, README "Per-Block Memory
   Breakdown"); ties go to the lowest logical block index.
 
+* Residual storage formats -- README "Physical 4-Bit Group-Quantized Residual
+  Buffers" and its "Tunable Quantization Dials": residual keys and values may
+  be stored with asymmetric group quantisation, groups of 64 dimensions, 8 or
+  4 bits, with a half-precision scale and bias per group; the decode attends
+  the dequantised rows x = scale * code + bias.
+
 Readings where the pages are silent (listed in the design notes):
   the anchor is attended as its own row at position 0; the delta is relative to
   the anchor with the singular values folded into U; the LSE is the natural log
   of the sum of exp of scaled scores z = scale * q.k; a sequence with no rows
   at all gives o = 0 and lse = -inf; routing scores are unscaled (scale does not
-  change the order).
+  change the order); quantised codes are unsigned (0 .. 2^bits - 1), 4-bit
+  codes are packed two per byte with the even dimension in the low nibble (the
+  little-endian order of the pages' uint32 words), and each row stores
+  (scale, bias) for dimensions 0..63 then for 64..127.
 
 Every function is plain numpy in float64: inputs are upcast exactly from fp16.
 Pins against things other than this code live in tests/test_oracle_pins.py.
@@ -50,6 +59,50 @@ LOWRANK_ROWS = BLOCK_SIZE - 1
 
 def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Residual storage formats (README "Physical 4-Bit Group-Quantized Residual
+# Buffers", "Tunable Quantization Dials")
+# ---------------------------------------------------------------------------
+
+RESID_FP16, RESID_INT8, RESID_INT4 = 0, 1, 2
+QUANT_GROUP = 64
+RESID_BITS = {RESID_INT8: 8, RESID_INT4: 4}
+
+
+def dequantize_rows(codes, scale_bias, bits: int) -> np.ndarray:
+    """Rows stored with asymmetric group quantisation: x[d] = scale[g] * code[d] +
+    bias[g] with g = d // 64 and unsigned codes.  codes: uint8 [R][d] (8 bits)
+    or [R][d / 2] (4 bits, dimension 2j in the low nibble of byte j and 2j + 1
+    in the high nibble); scale_bias: fp16 [R][d / 64][2] holding (scale, bias).
+    Returns float64 [R][d]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        q = c.astype(np.float64)
+    elif bits == 4:
+        q = np.empty(c.shape[:-1] + (2 * c.shape[-1],))
+        q[..., 0::2] = (c & 0x0F).astype(np.float64)
+        q[..., 1::2] = (c >> 4).astype(np.float64)
+    else:
+        raise ValueError(f"bits {bits}")
+    sb = _f64(scale_bias)
+    n_groups = sb.shape[-2]
+    assert q.shape[-1] == n_groups * QUANT_GROUP
+    scale = np.repeat(sb[..., 0], QUANT_GROUP, axis=-1)
+    bias = np.repeat(sb[..., 1], QUANT_GROUP, axis=-1)
+    return scale * q + bias
+
+
+def residual_rows(pool: Dict[str, np.ndarray], slot: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Residual K and V rows of one block and KV head as float64 [R][d], in any
+    of the storage formats."""
+    fmt = int(pool.get("resid_format", RESID_FP16))
+    if fmt == RESID_FP16:
+        return _f64(pool["resid_k"][slot, h]), _f64(pool["resid_v"][slot, h])
+    bits = RESID_BITS[fmt]
+    return (dequantize_rows(pool["resid_k"][slot, h], pool["resid_k_sb"][slot, h], bits),
+            dequantize_rows(pool["resid_v"][slot, h], pool["resid_v_sb"][slot, h], bits))
 
 
 # ---------------------------------------------------------------------------
@@ -163,8 +216,9 @@ def route(q_group, keys, top_k: int) -> Tuple[np.ndarray, np.ndarray]:
 # ---------------------------------------------------------------------------
 
 def _slot_entry(pool: Dict[str, np.ndarray], slot: int, h: int) -> Dict[str, np.ndarray]:
-    return {k: pool[k][slot, h] for k in
-            ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")}
+    e = {k: pool[k][slot, h] for k in ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_pos")}
+    e["resid_k"], e["resid_v"] = residual_rows(pool, slot, h)
+    return e
 
 
 def route_batch(pool, q, block_table, n_blocks, n_kv_heads: int, top_k: int):
@@ -256,9 +310,14 @@ def window_partials(win_k, win_v, win_len, q, n_kv_heads: int, splits: int, scal
     return o, l
 
 
-def bytes_per_block(rank: int, n_resid: int, head_dim: int = 128, elem: int = 2) -> int:
+def bytes_per_block(rank: int, n_resid: int, head_dim: int = 128, elem: int = 2,
+                    resid_format: int = RESID_FP16) -> int:
     """Algorithmic bytes one routed block of one KV head streams at decode:
-    anchors (2d), U (255 r), V_K and V_V (2 r d) and residual K, V (2 R d) in
-    fp16, plus one byte per residual position."""
-    return elem * (2 * head_dim + LOWRANK_ROWS * rank + 2 * rank * head_dim
-                   + 2 * n_resid * head_dim) + n_resid
+    anchors (2d), U (255 r), V_K and V_V (2 r d) in fp16, residual K and V rows
+    (fp16, or codes plus an fp16 scale and bias per 64-dimension group), and one
+    byte per residual position."""
+    if resid_format == RESID_FP16:
+        row = elem * head_dim
+    else:
+        row = head_dim * RESID_BITS[resid_format] // 8 + 4 * (head_dim // QUANT_GROUP)
+    return elem * (2 * head_dim + LOWRANK_ROWS * rank + 2 * rank * head_dim) + 2 * n_resid * row + n_resid

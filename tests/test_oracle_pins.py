@@ -447,3 +447,72 @@ def test_block_byte_accounting_matches_pages():
     assert H * (oracle.bytes_per_block(r, 64) - lowrank_only - 64) == rows["exact_residuals_R64"]["bytes"]
     assert H * 2 * 256 * 128 * 2 == rows["dense_block"]["bytes"]
     assert lowrank_only == u_bytes + 2 * 2 * 128 + 2 * 2 * r * 128
+
+
+# ---------------------------------------------------------------------------
+# Quantised residual rows (README "Physical 4-Bit Group-Quantized Residual
+# Buffers", "Tunable Quantization Dials")
+# ---------------------------------------------------------------------------
+
+def test_quantised_row_bytes_match_pages():
+    g = json.load(open(os.path.join(HERE, "golden", "dkv_resid_quant.json")))
+    d = 128
+    fp16_row = 2 * d
+    # per-row bytes from the byte accounting: codes + scale/bias
+    int8_row = (oracle.bytes_per_block(32, 1, resid_format=oracle.RESID_INT8)
+                - oracle.bytes_per_block(32, 0) - 1) // 2
+    int4_row = (oracle.bytes_per_block(32, 1, resid_format=oracle.RESID_INT4)
+                - oracle.bytes_per_block(32, 0) - 1) // 2
+    assert int4_row - g["scale_bias_bytes_per_row"] == 4 * g["int4_words_per_row_d128"]
+    assert round(fp16_row / int8_row, 1) == g["compression_vs_fp16"]["int8"]
+    assert round(fp16_row / int4_row, 2) == g["compression_vs_fp16"]["int4"]
+    assert oracle.QUANT_GROUP == g["group_size"]
+
+
+def test_int4_nibble_order_and_groups():
+    # byte j holds dimension 2j in its low nibble and 2j + 1 in its high nibble
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, 0] = 0x21          # dims 0, 1 -> 1, 2
+    codes[0, 1] = 0x43          # dims 2, 3 -> 3, 4
+    codes[0, 32] = 0xF0         # dims 64, 65 -> 0, 15 (second group)
+    sb = np.array([[[1.0, 0.0], [0.5, -3.0]]], dtype=np.float16)
+    x = oracle.dequantize_rows(codes, sb, 4)
+    assert x.shape == (1, 128)
+    assert list(x[0, :5]) == [1.0, 2.0, 3.0, 4.0, 0.0]
+    assert list(x[0, 64:67]) == [-3.0, 4.5, -3.0]
+    assert x[0, 63] == 0.0 and x[0, 127] == -3.0
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_quantised_pool_equals_fp16_pool_special_case(fmt):
+    """Codes with per-group scale and bias chosen so that the rows they stand for
+    are exact fp16 values: the quantised pool must decode exactly like an fp16
+    pool holding those rows (built here by slicing, group by group)."""
+    wl = synth.make_workload("qx", seed=55 + fmt, batch=2, n_q_heads=4, n_kv_heads=2, window=20,
+                             n_blocks=[3, 2], ranks=[6], n_resid=9, top_k=2, resid_format=fmt)
+    L = wl.layers[0]
+    qpool = L.pool()
+    S, H, R = qpool["resid_k"].shape[:3]
+    rng = np.random.default_rng(9)
+    top = 256 if fmt == 1 else 16
+    fpool = dict(qpool)
+    del fpool["resid_format"], fpool["resid_k_sb"], fpool["resid_v_sb"]
+    for name in ("resid_k", "resid_v"):
+        codes = rng.integers(0, top, size=(S, H, R, 128))
+        sb = np.zeros((S, H, R, 2, 2), dtype=np.float16)
+        sb[..., 0, 0], sb[..., 0, 1] = 0.5, -2.0          # group 0: x = 0.5 c - 2
+        sb[..., 1, 0], sb[..., 1, 1] = 0.25, 1.0          # group 1: x = 0.25 c + 1
+        rows = np.empty((S, H, R, 128), dtype=np.float16)
+        rows[..., :64] = 0.5 * codes[..., :64] - 2.0
+        rows[..., 64:] = 0.25 * codes[..., 64:] + 1.0
+        if fmt == 1:
+            stored = codes.astype(np.uint8)
+        else:
+            stored = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+        qpool[name], qpool[name + "_sb"], fpool[name] = stored, sb, rows
+    args = (L.q, L.win_k, L.win_v, wl.block_table, wl.n_blocks, wl.win_len, wl.n_kv_heads, wl.top_k,
+            wl.scale)
+    oq, lq, iq = oracle.decode(qpool, *args)
+    of, lf, i_f = oracle.decode(fpool, *args)
+    assert np.array_equal(iq, i_f)
+    assert np.array_equal(oq, of) and np.array_equal(lq, lf)
