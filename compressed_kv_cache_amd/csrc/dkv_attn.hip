@@ -39,6 +39,7 @@
 #include <type_traits>
 
 typedef _Float16 f16;
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -76,6 +77,11 @@ struct PoolArgs {
   const uint8_t* rp; int64_t rp_s, rp_h;
   float* key; int64_t key_s, key_h;
   int rank, n_resid, n_kv, n_slots;
+  int rfmt;                                   // residual rows: 0 fp16 (rk, rv), 1 / 2 8- / 4-bit codes
+  const uint8_t* rkq; int64_t rkq_s, rkq_h;   // codes [R][128] or [R][64] (bytes)
+  const uint8_t* rvq; int64_t rvq_s, rvq_h;
+  const f16* rks; int64_t rks_s, rks_h;       // (scale, bias) per 64-dimension group [R][2][2]
+  const f16* rvs; int64_t rvs_s, rvs_h;
 };
 
 struct BatchArgs {
@@ -783,6 +789,200 @@ __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, in
   }
 }
 
+// ---- residual rows in the 8- / 4-bit group-quantised formats -------------
+// Row x[d] = scale_g code[d] + bias_g, g = d / 64, unsigned codes; 4-bit codes
+// two per byte, dimension 2j in the low nibble of byte j.  Codes enter the MFMA
+// as exact fp16 integers; the per-row scales and biases are applied in fp32:
+//   q.x = s_0 (q.code)_{0..63} + s_1 (q.code)_{64..127} + b_0 sum(q_{0..63}) + b_1 sum(q_{64..127})
+//   sum_t p_t x_t[d] = sum_t code_t[d] (s_g p_t) + sum_t b_g p_t
+// with s_g p_t as an fp16 hi + lo pair.
+
+template <int BITS>
+struct QTile {
+  // per lane: row l16 of the tile, dimensions 32 s + 8 q4 .. + 7 (8 or 4 bytes)
+  typename std::conditional<BITS == 8, uint2, uint32_t>::type kc[4], vc[4];
+  // per lane: (s0, b0, s1, b1) of rows 4 q4 .. 4 q4 + 3 of the tile
+  uint2 ksb[4], vsb[4];
+};
+
+// rows past n_ex read row n_ex - 1 (finite, weight 0); n_ex >= 1
+template <int BITS>
+__device__ __forceinline__ void load_qtile(const uint8_t* kq, const uint8_t* vq, const f16* ks, const f16* vs,
+                                           int tile, int ntile, int n_ex, QTile<BITS>& T, int l16, int q4) {
+  constexpr int RB = BITS == 8 ? kD : kD / 2;  // code bytes per row
+  const int t = tile * 16 + l16;
+  const int tc = (tile < ntile && t < n_ex) ? t : n_ex - 1;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t off = (int64_t)tc * RB + (BITS == 8 ? 32 * s + 8 * q4 : 16 * s + 4 * q4);
+    if constexpr (BITS == 8) {
+      T.kc[s] = *reinterpret_cast<const uint2*>(kq + off);
+      T.vc[s] = *reinterpret_cast<const uint2*>(vq + off);
+    } else {
+      T.kc[s] = *reinterpret_cast<const uint32_t*>(kq + off);
+      T.vc[s] = *reinterpret_cast<const uint32_t*>(vq + off);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = tile * 16 + 4 * q4 + e;
+    const int rc = (tile < ntile && r < n_ex) ? r : n_ex - 1;
+    T.ksb[e] = *reinterpret_cast<const uint2*>(ks + (int64_t)rc * 4);
+    T.vsb[e] = *reinterpret_cast<const uint2*>(vs + (int64_t)rc * 4);
+  }
+}
+
+// two bytes (low halves of each 16-bit half of w) -> two exact fp16 integers
+__device__ __forceinline__ uint32_t bytes2_to_h2(uint32_t w) {
+  // 0x6400 | b is the fp16 1024 + b; subtracting 1024 is exact
+  const uint32_t m = (w & 0x00FF00FFu) | 0x64006400u;
+  const v2h x = __builtin_bit_cast(v2h, m) - (v2h){(f16)1024.0f, (f16)1024.0f};
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// 8 codes of a lane -> v8h of exact fp16 integers (dimension order)
+template <int BITS>
+__device__ __forceinline__ v8h codes_to_h8(typename std::conditional<BITS == 8, uint2, uint32_t>::type c) {
+  uint32_t w[4];
+  if constexpr (BITS == 8) {
+    // bytes b0..b3 of c.x: pairs (b0, b1) and (b2, b3)
+    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c010c00u));
+    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c030c02u));
+    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c010c00u));
+    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c030c02u));
+  } else {
+    // nibbles: dimension 2j = low nibble of byte j, 2j + 1 = high nibble
+    const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+    // lo byte j -> low half, hi byte j -> high half
+    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c040c00u));
+    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c050c01u));
+    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c060c02u));
+    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c070c03u));
+  }
+  return __builtin_bit_cast(v8h, w);
+}
+
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
+
+// One softmax step over two quantised 16-row tiles (b optional).  Q0, Q1: this
+// lane's head's query sums over dimensions 0..63 and 64..127.
+template <int NQ, int BITS, class Next = NoNext>
+__device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const QTile<BITS>& A, const QTile<BITS>& Bq,
+                                             int rows_a, int rows_b, bool has_b, const v4h (&qf)[4][2], float Q0,
+                                             float Q1, float scale, f16* Va, f16* Vb, int l16, int q4,
+                                             Next&& next = Next()) {
+  // scores per group: rows of the S layout are 4 q4 + e, heads l16
+  auto scores = [&](const QTile<BITS>& T, float (&z)[4], int rows) {
+    v4f S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const v8h k = codes_to_h8<BITS>(T.kc[s]);
+      if (s < 2) {
+        S0 = mfma16(lo4(k), qf[s][0], S0);
+        S0 = mfma16(hi4(k), qf[s][1], S0);
+      } else {
+        S1 = mfma16(lo4(k), qf[s][0], S1);
+        S1 = mfma16(hi4(k), qf[s][1], S1);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float s0 = h_lo(T.ksb[e].x), b0 = h_hi(T.ksb[e].x), s1 = h_lo(T.ksb[e].y), b1 = h_hi(T.ksb[e].y);
+      const float v = (s0 * S0[e] + s1 * S1[e]) + (b0 * Q0 + b1 * Q1);
+      z[e] = (4 * q4 + e < rows) ? v * scale : -INFINITY;
+    }
+  };
+  float za[4], zb[4];
+  scores(A, za, rows_a);
+  if (has_b) {
+    scores(Bq, zb, rows_b);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) zb[e] = -INFINITY;
+  }
+  float tm = fmaxf(fmaxf(fmaxf(za[0], za[1]), fmaxf(za[2], za[3])),
+                   fmaxf(fmaxf(zb[0], zb[1]), fmaxf(zb[2], zb[3])));
+  tm = q4_max(tm);
+  const float mn = fmaxf(st.m, tm);
+  const bool none = (mn == -INFINITY);
+  const float alpha = none ? 1.f : __expf(st.m - mn);
+  float pa[4], pb[4];
+  float ps_ = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pa[e] = none ? 0.f : __expf(za[e] - mn);
+    pb[e] = none ? 0.f : __expf(zb[e] - mn);
+    ps_ += pa[e] + pb[e];
+  }
+  st.l = st.l * alpha + q4_sum(ps_);
+  st.m = mn;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.Ot[n][e] *= alpha;
+  }
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Wt[n][e] *= alpha;
+  }
+  // the codes of V, staged as exact fp16 integers
+  {
+    v8h vx[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) vx[s2] = codes_to_h8<BITS>(A.vc[s2]);
+    stage_v_tile(Va, vx, l16, q4);
+    if (has_b) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) vx[s2] = codes_to_h8<BITS>(Bq.vc[s2]);
+      stage_v_tile(Vb, vx, l16, q4);
+    }
+  }
+  wave_sync_lds();
+  // per tile: the weights s_g p_t of each group as an fp16 hi + lo pair, the
+  // codes of V from LDS, and the bias sums beta_g = sum_t b_g p_t
+  float beta0 = 0.f, beta1 = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (tt == 1 && !has_b) break;
+    // one tile's LDS reads at a time: keeps the registers they fill few
+    __builtin_amdgcn_sched_barrier(0);
+    const QTile<BITS>& T = tt == 0 ? A : Bq;
+    const float(&pp)[4] = tt == 0 ? pa : pb;
+    const f16* Vt = tt == 0 ? Va : Vb;
+    v4h wh[2], wl[2];
+    split_hl(h_lo(T.vsb[0].x) * pp[0], h_lo(T.vsb[1].x) * pp[1], h_lo(T.vsb[2].x) * pp[2],
+             h_lo(T.vsb[3].x) * pp[3], wh[0], wl[0]);
+    split_hl(h_lo(T.vsb[0].y) * pp[0], h_lo(T.vsb[1].y) * pp[1], h_lo(T.vsb[2].y) * pp[2],
+             h_lo(T.vsb[3].y) * pp[3], wh[1], wl[1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      beta0 += h_hi(T.vsb[e].x) * pp[e];
+      beta1 += h_hi(T.vsb[e].y) * pp[e];
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      v4h av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
+      st.Ot[n] = mfma16(av, wh[n >> 2], st.Ot[n]);
+      st.Ot[n] = mfma16(av, wl[n >> 2], st.Ot[n]);
+    }
+  }
+  beta0 = q4_sum(beta0);
+  beta1 = q4_sum(beta1);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const float bb = n < 4 ? beta0 : beta1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.Ot[n][e] += bb;
+  }
+  // the tiles' registers are free: load the next pair
+  next();
+  wave_sync_lds();
+}
+
 // NRQ = number of 16-wide column tiles of the augmented rank r + 1 (0 without
 // low-rank rows), a template parameter so that every loop over them is static.
 // Pool slot of routed block p of unit u from the routed indices and the block
@@ -800,7 +1000,9 @@ __device__ __forceinline__ int lookup_slot(const BatchArgs& Bt, const AttnArgs& 
 // residual rows, and, when win_tile_stride > 0, the window's 16-row tiles p,
 // p + stride, ..., which are attended first, before get_slot() (which may wait
 // for the routing) is called.  Other parts are window chunks of win_chunk rows.
-template <int NRQ, class SlotFn>
+// QK: 0 for pools whose residual rows are fp16, 1 for the quantised formats
+// (separate instances, so that the fp16 kernels hold none of that code).
+template <int NRQ, int QK, class SlotFn>
 __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& Bt, const AttnArgs& A, int u, int p,
                                             SlotFn&& get_slot, unsigned char* smem) {
   constexpr int NQ = NRQ > 0 ? NRQ : 1;
@@ -876,6 +1078,12 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   int n_ex = 0;
   const f16* exk = nullptr;
   const f16* exv = nullptr;
+  // residual rows in a quantised format: codes and (scale, bias) pairs
+  int qbits = 0;
+  const uint8_t* exkq = nullptr;
+  const uint8_t* exvq = nullptr;
+  const f16* exks = nullptr;
+  const f16* exvs = nullptr;
   int slot = -1;
   if (p < A.n_block_parts) {
     slot = get_slot();  // routed pool slot, or -1
@@ -884,8 +1092,16 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       lr = (A.block_mode & 1) != 0;
       if ((A.block_mode & 2) && P.n_resid > 0) {
         n_ex = P.n_resid;
-        exk = P.rk + slot * P.rk_s + h * P.rk_h;
-        exv = P.rv + slot * P.rv_s + h * P.rv_h;
+        if (P.rfmt == 0) {
+          exk = P.rk + slot * P.rk_s + h * P.rk_h;
+          exv = P.rv + slot * P.rv_s + h * P.rv_h;
+        } else {
+          qbits = P.rfmt == 1 ? 8 : 4;
+          exkq = P.rkq + slot * P.rkq_s + h * P.rkq_h;
+          exvq = P.rvq + slot * P.rvq_s + h * P.rvq_h;
+          exks = P.rks + slot * P.rks_s + h * P.rks_h;
+          exvs = P.rvs + slot * P.rvs_s + h * P.rvs_h;
+        }
       }
     }
   } else {
@@ -912,8 +1128,9 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   // their uses (with or without the low-rank rows, chosen once), so that the
   // compiler's wait counts let the first data be used while the rest is still
   // in flight.
-  auto body = [&](auto lr_tag) {
+  auto body = [&](auto lr_tag, auto bits_tag) {
   constexpr bool LR = decltype(lr_tag)::value && NRQ > 0;
+  constexpr int QB = decltype(bits_tag)::value;  // 0: fp16 exact rows; 8 / 4: quantised residual rows
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
 
@@ -985,12 +1202,20 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   // then, and the loads overlap the rest of the low-rank step while this
   // workgroup's first burst has already been consumed.
   v8h ka[4], va[4], kb[4], vb[4];
+  QTile<QB == 4 ? 4 : 8> qta, qtb;  // quantised residual tiles (QB != 0; n_ex > 0 there)
   int ta = wave, tb = wave + kAttWaves;
   auto issue_exact = [&]() {
-    const bool none = n_ex == 0;
-    const f16* qrow0 = Bt.q + (int64_t)row0 * kD;
-    load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, ta, none ? 1 : ntile, none ? 1 : n_ex, ka, va, l16, q4);
-    load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, tb, none ? 1 : ntile, none ? 1 : n_ex, kb, vb, l16, q4);
+    if constexpr (QB == 0) {
+      const bool none = n_ex == 0;
+      const f16* qrow0 = Bt.q + (int64_t)row0 * kD;
+      load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, ta, none ? 1 : ntile, none ? 1 : n_ex, ka, va, l16,
+                      q4);
+      load_exact_tile(none ? qrow0 : exk, none ? qrow0 : exv, tb, none ? 1 : ntile, none ? 1 : n_ex, kb, vb, l16,
+                      q4);
+    } else {
+      load_qtile<QB>(exkq, exvq, exks, exvs, ta, ntile, n_ex, qta, l16, q4);
+      load_qtile<QB>(exkq, exvq, exks, exvs, tb, ntile, n_ex, qtb, l16, q4);
+    }
   };
   if constexpr (!LR) issue_exact();
 
@@ -1117,7 +1342,34 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
 
   // ---- exact rows: two 16-row tiles per softmax step
-  if (n_ex > 0) {
+  if (QB != 0 && n_ex > 0) {
+    f16* Va = reinterpret_cast<f16*>(my);
+    f16* Vb = Va + 16 * kVStride;
+    // this lane's head's query sums over dimensions 0..63 and 64..127
+    float Q0 = 0.f, Q1 = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (float)qf[s2][0][e] + (float)qf[s2][1][e];
+        if (s2 < 2) Q0 += x; else Q1 += x;
+      }
+    }
+    Q0 = q4_sum(Q0);
+    Q1 = q4_sum(Q1);
+    while (ta < ntile) {
+      const bool has_b = tb < ntile;  // uniform over the wave
+      const int ta_n = ta + 2 * kAttWaves, tb_n = tb + 2 * kAttWaves;
+      exact_pair_q<NQ, (QB == 4 ? 4 : 8)>(st, Wt, qta, qtb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, Q0, Q1,
+                                          scale, Va, Vb, l16, q4, [&]() {
+        if (ta_n < ntile) load_qtile<(QB == 4 ? 4 : 8)>(exkq, exvq, exks, exvs, ta_n, ntile, n_ex, qta, l16, q4);
+        if (tb_n < ntile) load_qtile<(QB == 4 ? 4 : 8)>(exkq, exvq, exks, exvs, tb_n, ntile, n_ex, qtb, l16, q4);
+      });
+      ta = ta_n;
+      tb = tb_n;
+    }
+  }
+  if (QB == 0 && n_ex > 0) {
     f16* Va = reinterpret_cast<f16*>(my);
     f16* Vb = Va + 16 * kVStride;
     while (ta < ntile) {
@@ -1220,18 +1472,39 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     if (c4 == 0) st_dev(&A.part_lse[(int64_t)(row0 + g) * A.n_parts + part], (Lg > 0.f) ? Mg + __logf(Lg) : -INFINITY);
   }
   };
-  if (NRQ > 0 && lr)
-    body(std::true_type{});
-  else
-    body(std::false_type{});
+  using I0 = std::integral_constant<int, 0>;
+  using I8 = std::integral_constant<int, 8>;
+  using I4 = std::integral_constant<int, 4>;
+  if constexpr (QK == 0) {
+    if (NRQ > 0 && lr)
+      body(std::true_type{}, I0{});
+    else
+      body(std::false_type{}, I0{});
+  } else {
+    if (NRQ > 0 && lr) {
+      if (qbits == 8)
+        body(std::true_type{}, I8{});
+      else if (qbits == 4)
+        body(std::true_type{}, I4{});
+      else
+        body(std::true_type{}, I0{});
+    } else {
+      if (qbits == 8)
+        body(std::false_type{}, I8{});
+      else if (qbits == 4)
+        body(std::false_type{}, I4{});
+      else
+        body(std::false_type{}, I0{});
+    }
+  }
 }
 
-template <int NRQ>
+template <int NRQ, int QK>
 __global__ __launch_bounds__(kAttThreads, 2) void k_attend(PoolArgs P, BatchArgs Bt, AttnArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int item = blockIdx.x;
   const int u = item / A.items_per_unit, p = item % A.items_per_unit;
-  attend_part<NRQ>(P, Bt, A, u, p, [&]() { return lookup_slot(Bt, A, u, p); }, smem);
+  attend_part<NRQ, QK>(P, Bt, A, u, p, [&]() { return lookup_slot(Bt, A, u, p); }, smem);
 }
 
 // ----------------------------------------------------------------------------
@@ -1420,7 +1693,7 @@ constexpr int kCtrlHeaderBytes = 4096;          // control words: [0..63] misc, 
 // One work item of a fused decode step: t < n_route routes unit t; then
 // the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merges
 // (u, g).  sh_slot: a shared word of the calling workgroup.
-template <int NRQ>
+template <int NRQ, int QK>
 __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& Bt, const DecodeArgs& D, int t,
                                             unsigned char* smem, RouteShared<kAttWaves>& rsh, int32_t& sh_slot) {
   const int tid = threadIdx.x;
@@ -1453,7 +1726,7 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
       lds_barrier();
       return (int)sh_slot;
     };
-    attend_part<NRQ>(P, Bt, D.att, u, p, get_slot, smem);
+    attend_part<NRQ, QK>(P, Bt, D.att, u, p, get_slot, smem);
     // count this part once its partial is stored
     stores_done();
     __syncthreads();
@@ -1480,7 +1753,7 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
   }
 }
 
-template <int NRQ>
+template <int NRQ, int QK>
 __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ RouteShared<kAttWaves> rsh;
@@ -1520,7 +1793,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   }
   lds_barrier();
   const int t = (int)sh_ticket;
-  decode_item<NRQ>(P, Bt, D, t, smem, rsh, sh_slot);
+  decode_item<NRQ, QK>(P, Bt, D, t, smem, rsh, sh_slot);
   // The last merge to finish zeroes the control words for the next launch:
   // merges start only after all of their unit's parts are stored, and every
   // part only after its routing, so no other item still uses them.
@@ -1618,7 +1891,7 @@ __device__ __forceinline__ void layers_item(int i, int x, int nx, const LayersAr
 // Work items of every layer from the per-XCD queues (see layers_item).
 // NMAX: the largest low-rank tile count of any layer (instances hold only the
 // attention variants up to it, which keeps register use down).
-template <int NMAX>
+template <int NMAX, int QK>
 __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArgs* __restrict__ table, LayersArgs L) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ RouteShared<kAttWaves> rsh;
@@ -1664,17 +1937,17 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArg
   const LayerArgs la = __builtin_bit_cast(LayerArgs, words);
   if (t >= 0) {
     if (la.nrq <= 0 || NMAX == 0)
-      decode_item<0>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<0, QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
     else if (la.nrq == 1 || NMAX == 1)
-      decode_item<(NMAX < 1 ? NMAX : 1)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<(NMAX < 1 ? NMAX : 1), QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
     else if (la.nrq == 2 || NMAX == 2)
-      decode_item<(NMAX < 2 ? NMAX : 2)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<(NMAX < 2 ? NMAX : 2), QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
     else if (la.nrq == 3 || NMAX == 3)
-      decode_item<(NMAX < 3 ? NMAX : 3)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<(NMAX < 3 ? NMAX : 3), QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
     else if (la.nrq == 4 || NMAX == 4)
-      decode_item<(NMAX < 4 ? NMAX : 4)>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<(NMAX < 4 ? NMAX : 4), QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
     else
-      decode_item<NMAX>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
+      decode_item<NMAX, QK>(la.P, la.Bt, la.D, t, smem, rsh, sh_slot);
   }
   // The last merge of the launch zeroes every layer's control words and the
   // queue counters: it finishes after every part, and every part after its
@@ -1723,6 +1996,8 @@ dkv_status check_pool_shape(const dkv_pool* P) {
   if (P->n_resid > DKV_MAX_RESID) return fail(DKV_ERR_UNSUPPORTED, "n_resid %d > 255", P->n_resid);
   if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
   if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
+  if (P->resid_format != DKV_RESID_FP16 && P->resid_format != DKV_RESID_INT8 && P->resid_format != DKV_RESID_INT4)
+    return fail(DKV_ERR_INVALID_ARG, "resid_format %d unknown", P->resid_format);
   return DKV_OK;
 }
 
@@ -1742,8 +2017,15 @@ dkv_status check_pool_arrays(const dkv_pool* P, int which) {
       if ((s = check_view(P->resid_pos, "resid_pos", 1, 1))) return s;
   }
   if ((which & 2) && P->n_resid > 0) {
-    if ((s = check_view(P->resid_k, "resid_k", 2, 16))) return s;
-    if ((s = check_view(P->resid_v, "resid_v", 2, 16))) return s;
+    if (P->resid_format == DKV_RESID_FP16) {
+      if ((s = check_view(P->resid_k, "resid_k", 2, 16))) return s;
+      if ((s = check_view(P->resid_v, "resid_v", 2, 16))) return s;
+    } else {
+      if ((s = check_view(P->resid_k, "resid_k", 1, 16))) return s;
+      if ((s = check_view(P->resid_v, "resid_v", 1, 16))) return s;
+      if ((s = check_view(P->resid_k_sb, "resid_k_sb", 2, 16))) return s;
+      if ((s = check_view(P->resid_v_sb, "resid_v_sb", 2, 16))) return s;
+    }
   }
   if (which & 4)
     if ((s = check_view(P->route_key, "route_key", 4, 16))) return s;
@@ -1792,6 +2074,17 @@ PoolArgs make_pool_args(const dkv_pool* P) {
   a.n_resid = P->n_resid;
   a.n_kv = P->n_kv_heads;
   a.n_slots = P->n_slots;
+  a.rfmt = P->resid_format;
+  a.rkq = a.rvq = nullptr;
+  a.rks = a.rvs = nullptr;
+  a.rkq_s = a.rkq_h = a.rvq_s = a.rvq_h = a.rks_s = a.rks_h = a.rvs_s = a.rvs_h = 0;
+  if (P->resid_format != DKV_RESID_FP16) {
+    a.rk = a.rv = nullptr;
+    a.rkq = (const uint8_t*)P->resid_k.ptr; a.rkq_s = P->resid_k.slot_stride; a.rkq_h = P->resid_k.head_stride;
+    a.rvq = (const uint8_t*)P->resid_v.ptr; a.rvq_s = P->resid_v.slot_stride; a.rvq_h = P->resid_v.head_stride;
+    a.rks = (const f16*)P->resid_k_sb.ptr; a.rks_s = P->resid_k_sb.slot_stride; a.rks_h = P->resid_k_sb.head_stride;
+    a.rvs = (const f16*)P->resid_v_sb.ptr; a.rvs_s = P->resid_v_sb.slot_stride; a.rvs_h = P->resid_v_sb.head_stride;
+  }
   return a;
 }
 
@@ -1843,34 +2136,48 @@ dkv_status launch_route(const dkv_pool* P, const dkv_batch* B, int top_k, int32_
   return launched("k_route_topk");
 }
 
-template <int NRQ>
-dkv_status launch_decode_nrq(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B, const DecodeArgs& D) {
+template <int NRQ, int QK>
+dkv_status launch_decode_nrq_q(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
+                               const DecodeArgs& D) {
   static bool attr_set = false;
   if (!attr_set) {
     // 160 KB of LDS per workgroup on gfx950, less this kernel's static shared memory
-    if (hipFuncSetAttribute((const void*)k_decode<NRQ>, hipFuncAttributeMaxDynamicSharedMemorySize, 158 * 1024) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_decode<NRQ, QK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            158 * 1024) != hipSuccess)
       return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_decode) failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_decode<NRQ>, dim3((unsigned)D.n_items), dim3(kAttThreads), shm, st, make_pool_args(P),
+  hipLaunchKernelGGL((k_decode<NRQ, QK>), dim3((unsigned)D.n_items), dim3(kAttThreads), shm, st, make_pool_args(P),
                      make_batch_args(P, B), D);
   return launched("k_decode");
 }
 
 template <int NRQ>
-dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
-                             const AttnArgs& a) {
+dkv_status launch_decode_nrq(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B, const DecodeArgs& D) {
+  return P->resid_format == DKV_RESID_FP16 ? launch_decode_nrq_q<NRQ, 0>(shm, st, P, B, D)
+                                           : launch_decode_nrq_q<NRQ, 1>(shm, st, P, B, D);
+}
+
+template <int NRQ, int QK>
+dkv_status launch_attend_nrq_q(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
+                               const AttnArgs& a) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_attend<NRQ>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-        hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_attend<NRQ, QK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
       return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_attend) failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_attend<NRQ>, dim3((unsigned)items), dim3(kAttThreads), shm, st, make_pool_args(P),
+  hipLaunchKernelGGL((k_attend<NRQ, QK>), dim3((unsigned)items), dim3(kAttThreads), shm, st, make_pool_args(P),
                      make_batch_args(P, B), a);
   return launched("k_attend");
+}
+
+template <int NRQ>
+dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
+                             const AttnArgs& a) {
+  return P->resid_format == DKV_RESID_FP16 ? launch_attend_nrq_q<NRQ, 0>(items, shm, st, P, B, a)
+                                           : launch_attend_nrq_q<NRQ, 1>(items, shm, st, P, B, a);
 }
 
 dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* idx, const int32_t* slots,
@@ -2002,18 +2309,23 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
 // C ABI
 // ----------------------------------------------------------------------------
 
-template <int NMAX>
-static dkv_status launch_layers(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
+template <int NMAX, int QK>
+static dkv_status launch_layers_q(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_decode_layers<NMAX>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    if (hipFuncSetAttribute((const void*)k_decode_layers<NMAX, QK>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             158 * 1024) != hipSuccess)
       return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_decode_layers) failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_decode_layers<NMAX>, dim3((unsigned)plan->n_items), dim3(kAttThreads),
+  hipLaunchKernelGGL((k_decode_layers<NMAX, QK>), dim3((unsigned)plan->n_items), dim3(kAttThreads),
                      (size_t)plan->lds_bytes, st, (const LayerArgs*)plan->table, L);
   return launched("k_decode_layers");
+}
+
+template <int NMAX>
+static dkv_status launch_layers(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
+  return plan->quantised ? launch_layers_q<NMAX, 1>(plan, L, st) : launch_layers_q<NMAX, 0>(plan, L, st);
 }
 
 extern "C" {
@@ -2315,6 +2627,10 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     int nmax = 0;
     for (int l = 0; l < n_layers; ++l) nmax = host[l].nrq > nmax ? host[l].nrq : nmax;
     plan->max_tiles = nmax;
+    int quant = 0;
+    for (int l = 0; l < n_layers; ++l) quant |= pools[l].resid_format != DKV_RESID_FP16 ? 1 : 0;
+    plan->quantised = quant;
+    plan->reserved1 = 0;
     plan->table = table;
     plan->workspace = workspace;
   }

@@ -51,7 +51,11 @@ class PoolC(ctypes.Structure):
                 ("rank", ctypes.c_int32), ("n_resid", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("n_slots", ctypes.c_int32),
                 ("anchor_k", View), ("anchor_v", View), ("u", View), ("vk", View), ("vv", View),
-                ("resid_k", View), ("resid_v", View), ("resid_pos", View), ("route_key", View)]
+                ("resid_k", View), ("resid_v", View), ("resid_pos", View), ("route_key", View),
+                ("resid_format", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("resid_k_sb", View), ("resid_v_sb", View)]
+
+RESID_FP16, RESID_INT8, RESID_INT4 = 0, 1, 2
 
 
 class BatchC(ctypes.Structure):
@@ -67,7 +71,8 @@ class LayersPlanC(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_units", ctypes.c_int32), ("routes", ctypes.c_int32),
                 ("parts", ctypes.c_int32), ("win_parts", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("table", ctypes.c_void_p),
+                ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("quantised", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+                ("table", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p)]
 
 
@@ -169,26 +174,33 @@ class Pool:
     """One layer's block pool on the device (torch tensors kept alive here).
 
     anchor_k, anchor_v fp16 [S][Hkv][128]; u fp16 [S][Hkv][255][r];
-    vk, vv fp16 [S][Hkv][r][128]; resid_k, resid_v fp16 [S][Hkv][R][128];
-    resid_pos uint8 [S][Hkv][R]; route_key fp32 [S][Hkv][128].
+    vk, vv fp16 [S][Hkv][r][128]; resid_k, resid_v fp16 [S][Hkv][R][128], or
+    uint8 codes [S][Hkv][R][128] (8-bit) / [S][Hkv][R][64] (4-bit) with
+    resid_k_sb, resid_v_sb fp16 [S][Hkv][R][2][2]; resid_pos uint8 [S][Hkv][R];
+    route_key fp32 [S][Hkv][128].
     Inner dimensions must be packed; outer (slot, head) strides are free."""
 
-    def __init__(self, anchor_k, anchor_v, u, vk, vv, resid_k, resid_v, resid_pos, route_key):
+    def __init__(self, anchor_k, anchor_v, u, vk, vv, resid_k, resid_v, resid_pos, route_key,
+                 resid_format: int = RESID_FP16, resid_k_sb=None, resid_v_sb=None):
         self.tensors = dict(anchor_k=anchor_k, anchor_v=anchor_v, u=u, vk=vk, vv=vv,
                             resid_k=resid_k, resid_v=resid_v, resid_pos=resid_pos,
-                            route_key=route_key)
+                            route_key=route_key, resid_k_sb=resid_k_sb, resid_v_sb=resid_v_sb)
         S, Hkv = anchor_k.shape[0], anchor_k.shape[1]
         self.rank = int(u.shape[-1])
         self.n_resid = int(resid_k.shape[2])
         self.n_kv_heads = int(Hkv)
         self.n_slots = int(S)
+        self.resid_format = int(resid_format)
         self.c = PoolC(HEAD_DIM, BLOCK_SIZE, self.rank, self.n_resid, self.n_kv_heads, self.n_slots,
                        _view(anchor_k, 1), _view(anchor_v, 1), _view(u, 2), _view(vk, 2),
                        _view(vv, 2), _view(resid_k, 2), _view(resid_v, 2), _view(resid_pos, 1),
-                       _view(route_key, 1))
+                       _view(route_key, 1), self.resid_format, 0, _view(resid_k_sb, 3),
+                       _view(resid_v_sb, 3))
 
     # per-(slot, head) record order: what a block's attention reads first comes first
     RECORD_ORDER = ("resid_pos", "vv", "anchor_v", "vk", "anchor_k", "u", "resid_k", "resid_v")
+    RECORD_ORDER_Q = ("resid_pos", "vv", "anchor_v", "vk", "anchor_k", "u", "resid_k_sb", "resid_k",
+                      "resid_v_sb", "resid_v")
 
     @classmethod
     def from_numpy(cls, arrays: dict, device="cuda", layout: str = "records"):
@@ -203,18 +215,23 @@ class Pool:
         import torch
         S, Hkv, d = arrays["anchor_k"].shape
         rk = torch.zeros((S, Hkv, d), dtype=torch.float32, device=device)
+        fmt = int(arrays.get("resid_format", RESID_FP16))
         names = ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos")
+        order = cls.RECORD_ORDER
+        if fmt != RESID_FP16:
+            names = names + ("resid_k_sb", "resid_v_sb")
+            order = cls.RECORD_ORDER_Q
         if layout == "arrays":
             t = {k: torch.from_numpy(arrays[k]).to(device) for k in names}
         elif layout == "records":
             offs, rec = {}, 0
-            for k in cls.RECORD_ORDER:
+            for k in order:
                 offs[k] = rec
                 nbytes = arrays[k][0, 0].nbytes if arrays[k].size else 0
                 rec += (nbytes + 255) // 256 * 256
             rec = max(rec, 256)
             host = np.zeros((S, Hkv, rec), dtype=np.uint8)
-            for k in cls.RECORD_ORDER:
+            for k in order:
                 a = np.ascontiguousarray(arrays[k])
                 nb = a[0, 0].nbytes if a.size else 0
                 if nb:
@@ -233,7 +250,7 @@ class Pool:
         else:
             raise ValueError(f"unknown pool layout {layout!r}")
         pool = cls(t["anchor_k"], t["anchor_v"], t["u"], t["vk"], t["vv"], t["resid_k"],
-                   t["resid_v"], t["resid_pos"], rk)
+                   t["resid_v"], t["resid_pos"], rk, fmt, t.get("resid_k_sb"), t.get("resid_v_sb"))
         if "_record" in t:
             pool.tensors["_record"] = t["_record"]
         return pool

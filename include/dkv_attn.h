@@ -43,7 +43,8 @@
  *     [0, n_blocks[b]) are treated as empty blocks (no rows), never read.
  *   - Alignment: every fp16 / fp32 array base and every slot / head stride
  *     (in bytes) must be a multiple of 16, except `u` (a multiple of 8 bytes
- *     when r is a multiple of 4, else of 2) and `resid_pos` (any alignment).
+ *     when r is a multiple of 4, else of 2) and `resid_pos` (any alignment);
+ *     quantised residual codes and their scale/bias arrays also take 16.
  *   - Deterministic: identical inputs give bit-identical outputs (fixed
  *     reduction orders, no floating-point atomics).
  *   - lse values are natural logarithms of sums of exp of SCALED scores.
@@ -60,13 +61,24 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 3
+#define DKV_ABI_VERSION 4
 #define DKV_HEAD_DIM 128
 #define DKV_BLOCK_SIZE 256
 #define DKV_MAX_RANK 64
 #define DKV_MAX_RESID 255
 #define DKV_MAX_GROUP 16
 #define DKV_MAX_ROUTE_BLOCKS 12288
+
+/* Storage format of the residual rows (README "Physical 4-Bit Group-Quantized
+ * Residual Buffers" and its "Tunable Quantization Dials"): fp16 rows, or
+ * asymmetric group quantisation in groups of 64 of the 128 dimensions with an
+ * fp16 scale and bias per group: x[d] = scale_g * code[d] + bias_g, g = d / 64,
+ * unsigned codes (0..255 or 0..15).  4-bit codes are packed two per byte,
+ * dimension 2j in the low nibble of byte j (the little-endian order of the
+ * pages' packed uint32 words). */
+#define DKV_RESID_FP16 0
+#define DKV_RESID_INT8 1
+#define DKV_RESID_INT4 2
 
 typedef int32_t dkv_status;
 #define DKV_OK 0
@@ -97,10 +109,14 @@ typedef struct dkv_pool {
   dkv_view u;          /* fp16 [255][r] */
   dkv_view vk;         /* fp16 [r][d]   */
   dkv_view vv;         /* fp16 [r][d]   */
-  dkv_view resid_k;    /* fp16 [R][d]   */
-  dkv_view resid_v;    /* fp16 [R][d]   */
+  dkv_view resid_k;    /* fp16 [R][d]; or uint8 codes [R][d] (INT8) / [R][d/2] (INT4) */
+  dkv_view resid_v;    /* same as resid_k */
   dkv_view resid_pos;  /* uint8 [R], distinct values in 1..255 */
   dkv_view route_key;  /* fp32 [d]; written by dkv_route_keys, read by routing */
+  int32_t resid_format;   /* DKV_RESID_FP16 (0, what zero-initialised structs hold), _INT8 or _INT4 */
+  int32_t reserved0;
+  dkv_view resid_k_sb;    /* quantised formats only: fp16 [R][2][2], (scale, bias) of dims 0..63, 64..127 */
+  dkv_view resid_v_sb;    /* same for the V rows */
 } dkv_pool;
 
 /* One decode step's batch: one new query token per sequence. */
@@ -276,6 +292,8 @@ typedef struct dkv_layers_plan {
   int32_t n_items;        /* work items of one launch */
   int32_t lds_bytes;      /* dynamic LDS per workgroup */
   int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */
+  int32_t quantised;      /* 1 if any layer's residual rows are quantised */
+  int32_t reserved1;
   const void* table;
   void* workspace;
 } dkv_layers_plan;

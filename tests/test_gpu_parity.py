@@ -184,7 +184,8 @@ def _all_blocks_idx(wl):
     return idx
 
 
-@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (1, "")])
+@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (1, ""), (0, "Q8"), (0, "Q4"),
+                                         (1, "Q8")])
 def test_block_partials(lib, cfg, variant):
     wl = config(cfg, variant)
     say(f"[block partials] {wl.name} {variant}")
@@ -255,7 +256,8 @@ def test_lse_merge(lib):
 # Fused decode on the five workloads and the sensitivity variants
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (3, ""), (4, "")])
+@pytest.mark.parametrize("cfg,variant", [(0, ""), (0, "S1"), (0, "S2"), (3, ""), (4, ""),
+                                         (0, "Q8"), (0, "Q4"), (1, "Q8"), (1, "Q4")])
 def test_decode_configs(lib, cfg, variant):
     check_decode(lib, config(cfg, variant), label=variant)
 
@@ -577,3 +579,64 @@ def test_decode_layers_graph_replays(lib):
         torch.cuda.synchronize()
         assert torch.equal(run.outs[0], ref[0][0])
     assert run.timeout_flag() == 0
+
+
+
+# ---------------------------------------------------------------------------
+# Residual rows in the 8- and 4-bit group-quantised formats
+# ---------------------------------------------------------------------------
+
+QEDGE = {
+    "q8_R255_rank15": dict(ranks=[15], n_resid=255, resid_format=1),
+    "q4_R255_rank7": dict(ranks=[7], n_resid=255, resid_format=2),
+    "q8_no_residuals": dict(n_resid=0, resid_format=1),
+    "q4_rank64_ragged": dict(ranks=[64], resid_format=2, window=37, win_len=[37, 5, 0, 36]),
+    "q8_group16": dict(n_q_heads=16, n_kv_heads=1, resid_format=1),
+}
+
+
+@pytest.mark.parametrize("case", sorted(QEDGE))
+def test_decode_quantised_edge_cases(lib, case):
+    kw = dict(seed=500 + len(case), batch=4, n_q_heads=6, n_kv_heads=2, window=64,
+              n_blocks=[5, 3, 6, 4], ranks=[12], n_resid=20, top_k=3, sigma0=2.0)
+    kw.update(QEDGE[case])
+    wl = synth.make_workload(case, **kw)
+    check_decode(lib, wl, label=case)
+
+
+@pytest.mark.parametrize("variant", ["Q8", "Q4"])
+def test_decode_quantised_pool_layouts(lib, variant):
+    """Records and dense per-array tensors give the same bits for quantised pools."""
+    wl = config(1, variant)
+    lay = wl.layers[0]
+    res = {}
+    for layout in ("arrays", "records"):
+        pool = lib.Pool.from_numpy(lay.pool(), DEV, layout=layout)
+        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                                     wl.win_len, device=DEV)
+        lib.route_keys(pool)
+        out, lse, idx = lib.decode(pool, batch, wl.top_k, wl.scale)
+        torch.cuda.synchronize()
+        res[layout] = (out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy())
+    for a, b in zip(res["arrays"], res["records"]):
+        assert np.array_equal(a, b)
+
+
+def test_decode_layers_mixed_formats(lib):
+    """fp16, 8-bit and 4-bit layers in one layer-batched launch, each against the oracle."""
+    base = dict(batch=4, n_q_heads=6, n_kv_heads=2, window=48, n_blocks=[5, 2, 6, 3],
+                win_len=[48, 9, 17, 30], top_k=3, sigma0=2.0, n_resid=24)
+    specs = [dict(ranks=[24], resid_format=0), dict(ranks=[48], resid_format=1),
+             dict(ranks=[16], resid_format=2), dict(ranks=[9], resid_format=1)]
+    wls = [synth.make_workload(f"fmt{i}", seed=610 + i, **base, **sp) for i, sp in enumerate(specs)]
+    pools, batches = [], []
+    for w in wls:
+        p, b = upload(lib, w)
+        pools.append(p)
+        batches.append(b)
+    run = lib.Layers(pools, batches, 3, wls[0].scale)
+    assert run.plan.quantised == 1
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        say(f"[layers mixed formats] layer {l} format {specs[l]['resid_format']}")
+        _oracle_check(w, w.layers[0], *res[l], 3)
