@@ -47,16 +47,20 @@ METRIC = "decode attention queries/sec + achieved HBM GB/s over compressed KV at
 D = 128
 
 
-def bytes_per_block(rank: int, n_resid: int) -> int:
-    """Algorithmic bytes of one routed block of one KV head (fp16, + u8 positions)."""
-    return 2 * (2 * D + 255 * rank + 2 * rank * D + 2 * n_resid * D) + n_resid
+RESID_ROW_BYTES = {0: 2 * D, 1: D + 8, 2: D // 2 + 8}   # fp16; 8- / 4-bit codes + fp16 scale, bias per 64
 
 
-def layer_bytes(batch, hkv, hq, top_k_eff, rank, n_resid, window, n_blocks):
+def bytes_per_block(rank: int, n_resid: int, resid_format: int = 0) -> int:
+    """Algorithmic bytes of one routed block of one KV head (fp16 low-rank state,
+    residual rows in their storage format, u8 positions)."""
+    return 2 * (2 * D + 255 * rank + 2 * rank * D) + 2 * n_resid * RESID_ROW_BYTES[resid_format] + n_resid
+
+
+def layer_bytes(batch, hkv, hq, top_k_eff, rank, n_resid, window, n_blocks, resid_format: int = 0):
     """Per-layer algorithmic bytes by stage: route keys + q (routing), routed
     blocks + window + q (attention), output (merge)."""
     route = batch * hkv * n_blocks * D * 4 + batch * hq * D * 2
-    attend = batch * hkv * (top_k_eff * bytes_per_block(rank, n_resid) + 2 * 2 * window * D) \
+    attend = batch * hkv * (top_k_eff * bytes_per_block(rank, n_resid, resid_format) + 2 * 2 * window * D) \
         + batch * hq * D * 2
     merge = batch * hq * (D * 2 + 4) + batch * hkv * top_k_eff * 4
     return route, attend, merge
@@ -112,11 +116,77 @@ def measured_traffic(kernel: str, digest: str):
     return t.get("bytes_per_launch")
 
 
-def step_algorithmic_bytes(n_layers: int) -> int:
+def step_algorithmic_bytes(n_layers: int, resid_format: int = 0) -> int:
     """Algorithmic bytes of one step over the first n_layers layers of the stack."""
     from compressed_kv_cache_amd import synth
     B, Hq, Hkv, K, R, W, N = 4, 12, 2, 32, 128, 1024, 252
-    return sum(sum(layer_bytes(B, Hkv, Hq, min(K, N), synth.STACK_RANKS[i], R, W, N)) for i in range(n_layers))
+    return sum(sum(layer_bytes(B, Hkv, Hq, min(K, N), synth.STACK_RANKS[i], R, W, N, resid_format))
+               for i in range(n_layers))
+
+
+def measure_quantised(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
+    """The same 64k batch-4 stack with its residual rows stored in the 8- or
+    4-bit group-quantised format (variant "Q8" / "Q4"): one layer-batched launch
+    per step, timed eagerly with events and as a graph replay."""
+    dev = torch.device("cuda:0")
+    pools, batches = [], []
+    for li in range(n_layers):
+        wl = synth.make_config(2, layers=[li], variant=variant)
+        lay = wl.layers[0]
+        pool = lib.Pool.from_numpy(lay.pool(), dev)
+        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                                     wl.win_len, device=dev)
+        lib.route_keys(pool)
+        lib.gather_route_keys(pool, batch)
+        pools.append(pool)
+        batches.append(batch)
+        del wl, lay
+    run = lib.Layers(pools, batches, 32, float(1.0 / np.sqrt(D)))
+    for _ in range(warmup):
+        run.run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in run.outs]
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda._sleep(int(2e-3 * 2.4e9))
+    for s in range(steps):
+        e0[s].record()
+        run.run()
+        e1[s].record()
+    torch.cuda.synchronize()
+    kern = float(np.mean([e0[s].elapsed_time(e1[s]) for s in range(steps)]))
+    assert run.timeout_flag() == 0 and all(torch.equal(a, b) for a, b in zip(ref, run.outs))
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        run.run(cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run.run(torch.cuda.current_stream())
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
+    fmt = 1 if variant == "Q8" else 2
+    alg = step_algorithmic_bytes(n_layers, fmt)
+    log(f"{variant} residuals, layer-batched: {ms:.4f} ms/step (graph); kernel {kern * 1e3:.1f} us; "
+        f"{alg / 1e6:.1f} MB per step")
+    res = {"resid_format": {"Q8": "int8", "Q4": "int4"}[variant], "ms_per_step": ms,
+           "queries_per_s": 4 * n_layers / (ms * 1e-3), "algorithmic_bytes_per_step": alg,
+           "kernel_us_per_launch": kern * 1e3, "achieved_GBps": alg / (kern * 1e-3) / 1e9}
+    del run, pools, batches
+    torch.cuda.empty_cache()
+    return res
 
 
 def pmc_summary(args) -> int:
@@ -242,6 +312,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--quantised", choices=("none", "int8", "int4", "both"), default="both",
+                    help="also time the stack with its residual rows in the 8- / 4-bit format "
+                         "(layer-batched launch; reported beside the fp16 value)")
     ap.add_argument("--mode", choices=("all", "per-layer", "layer-batched"), default="all",
                     help="which launch modes to time (default: all)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -525,6 +598,11 @@ def main() -> int:
         "resident_cache_GB": resident / 1e9,
         "kernel_source_sha256_16": digest,
     }
+    if args.quantised != "none" and args.mode != "per-layer":
+        # free the fp16 stack first: the quantised stacks are built the same way
+        variants = {"int8": ["Q8"], "int4": ["Q4"], "both": ["Q8", "Q4"]}[args.quantised]
+        res["quantised_residuals"] = [measure_quantised(lib, synth, torch, np, v, n_layers, args.steps,
+                                                        args.warmup, log) for v in variants]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cpu_sample or {layer_ids[0]: meta}, args.cpu_seconds, log)
     print(json.dumps(res))

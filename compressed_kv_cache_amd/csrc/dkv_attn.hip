@@ -795,7 +795,7 @@ __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, in
 // as exact fp16 integers; the per-row scales and biases are applied in fp32:
 //   q.x = s_0 (q.code)_{0..63} + s_1 (q.code)_{64..127} + b_0 sum(q_{0..63}) + b_1 sum(q_{64..127})
 //   sum_t p_t x_t[d] = sum_t code_t[d] (s_g p_t) + sum_t b_g p_t
-// with s_g p_t as an fp16 hi + lo pair.
+// with s_g p_t rounded to fp16, as the softmax weights of fp16 rows are.
 
 template <int BITS>
 struct QTile {
@@ -951,11 +951,11 @@ __device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const Q
     const QTile<BITS>& T = tt == 0 ? A : Bq;
     const float(&pp)[4] = tt == 0 ? pa : pb;
     const f16* Vt = tt == 0 ? Va : Vb;
-    v4h wh[2], wl[2];
-    split_hl(h_lo(T.vsb[0].x) * pp[0], h_lo(T.vsb[1].x) * pp[1], h_lo(T.vsb[2].x) * pp[2],
-             h_lo(T.vsb[3].x) * pp[3], wh[0], wl[0]);
-    split_hl(h_lo(T.vsb[0].y) * pp[0], h_lo(T.vsb[1].y) * pp[1], h_lo(T.vsb[2].y) * pp[2],
-             h_lo(T.vsb[3].y) * pp[3], wh[1], wl[1]);
+    const float w0[4] = {h_lo(T.vsb[0].x) * pp[0], h_lo(T.vsb[1].x) * pp[1], h_lo(T.vsb[2].x) * pp[2],
+                         h_lo(T.vsb[3].x) * pp[3]};
+    const float w1[4] = {h_lo(T.vsb[0].y) * pp[0], h_lo(T.vsb[1].y) * pp[1], h_lo(T.vsb[2].y) * pp[2],
+                         h_lo(T.vsb[3].y) * pp[3]};
+    const v4h wh[2] = {to_h4(w0), to_h4(w1)};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       beta0 += h_hi(T.vsb[e].x) * pp[e];
@@ -967,7 +967,6 @@ __device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const Q
 #pragma unroll
       for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
       st.Ot[n] = mfma16(av, wh[n >> 2], st.Ot[n]);
-      st.Ot[n] = mfma16(av, wl[n >> 2], st.Ot[n]);
     }
   }
   beta0 = q4_sum(beta0);
