@@ -642,13 +642,18 @@ constexpr int kRedStride = 132;  // floats per row of the reduction buffer (conf
 __host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
 
 
-// per-wave scratch: the V tile of an exact tile, or the Ux transpose of a
-// low-rank tile, followed by that wave's residual-position bit mask
-// per-wave scratch: the wave's four transposed U tiles (low-rank phase) or two
-// V tiles (exact phase), then the 256-bit residual-position mask
+// Staged MFMA A operands are stored transposed, so that a lane's four
+// elements (four consecutive rows of one column) are one 8-byte LDS read:
+//   V^T of a 16-row exact tile: Vt[d][row], d-rows of kVTStride halves;
+//   Ux^T of a wave's 64 low-rank positions: T[j][position], j-rows of kTTStride halves.
+constexpr int kVTStride = 20;                       // 16 rows + pad (8-byte aligned rows)
+constexpr int kTTStride = 4 * 16 + 4;               // 64 positions + pad
+
+// per-wave scratch: the wave's transposed U tiles (low-rank phase) or two
+// transposed V tiles (exact phase), then the 256-bit residual-position mask
 __host__ __device__ inline int att_scratch_bytes(int rq) {
-  const int a = kLRTilesPerWave * 16 * (rq + 4) * 2;
-  const int b = 2 * 16 * kVStride * 2;
+  const int a = rq * kTTStride * 2;
+  const int b = 2 * kD * kVTStride * 2;
   return round16((a > b ? a : b) + 32);
 }
 
@@ -699,23 +704,25 @@ __device__ __forceinline__ v4f exact_scores(const v8h (&kx)[4], const v4h (&qf)[
   return S;
 }
 
-// O^T += V^T p for one 16-row tile whose V rows sit in LDS at Vt[row][kVStride]
+// the A operand of O^T += V^T p for output tile n: V rows 4 q4 .. 4 q4 + 3 of
+// column d = 16 n + l16, from the transposed staging
+__device__ __forceinline__ v4h vt_operand(const f16* Vt, int n, int l16, int q4) {
+  return *reinterpret_cast<const v4h*>(Vt + (16 * n + l16) * kVTStride + 4 * q4);
+}
+
+// O^T += V^T p for one 16-row tile staged transposed at Vt[d][row]
 __device__ __forceinline__ void exact_pv(ExState& st, const f16* Vt, const float (&pe)[4], int l16, int q4) {
   const v4h ph = to_h4(pe);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    v4h av;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
-    st.Ot[n] = mfma16(av, ph, st.Ot[n]);
-  }
+  for (int n = 0; n < 8; ++n) st.Ot[n] = mfma16(vt_operand(Vt, n, l16, q4), ph, st.Ot[n]);
 }
 
+// lane (row l16, q4) holds V[l16][32 s + 8 q4 + j]: store it transposed
 __device__ __forceinline__ void stage_v_tile(f16* Vt, const v8h (&vx)[4], int l16, int q4) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4) = lo4(vx[s]);
-    *reinterpret_cast<v4h*>(Vt + l16 * kVStride + 32 * s + 8 * q4 + 4) = hi4(vx[s]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Vt[(32 * s + 8 * q4 + j) * kVTStride + l16] = vx[s][j];
   }
 }
 
@@ -962,12 +969,7 @@ __device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const Q
       beta1 += h_hi(T.vsb[e].y) * pp[e];
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      v4h av;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) av[e] = Vt[(4 * q4 + e) * kVStride + 16 * n + l16];
-      st.Ot[n] = mfma16(av, wh[n >> 2], st.Ot[n]);
-    }
+    for (int n = 0; n < 8; ++n) st.Ot[n] = mfma16(vt_operand(Vt, n, l16, q4), wh[n >> 2], st.Ot[n]);
   }
   beta0 = q4_sum(beta0);
   beta1 = q4_sum(beta1);
@@ -1032,7 +1034,6 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   f16* vvx = reinterpret_cast<f16*>(qt + 16 * RQ);                // [RQ][kVStride]  [V_V ; a_v ; *]
   float* wstat = reinterpret_cast<float*>(vvx + RQ * kVStride);   // m [4][16], l [4][16]
   unsigned char* region = reinterpret_cast<unsigned char*>(wstat + 2 * kAttWaves * 16);
-  constexpr int TS = RQ + 4;
   unsigned char* my = region + wave * att_scratch_bytes(RQ);
   uint32_t* wmask = reinterpret_cast<uint32_t*>(my + att_scratch_bytes(RQ) - 32);
   const float scale = A.scale;
@@ -1057,7 +1058,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     const int n_wt = (wl + 15) >> 4;
     any = p < n_wt;  // uniform
     f16* Va = reinterpret_cast<f16*>(my);
-    f16* Vb = Va + 16 * kVStride;
+    f16* Vb = Va + kD * kVTStride;
     v8h ka[4], va[4], kb[4], vb[4];
     for (int i = wave; p + A.win_tile_stride * i < n_wt; i += 2 * kAttWaves) {
       const int wa = p + A.win_tile_stride * i, wb = p + A.win_tile_stride * (i + kAttWaves);
@@ -1257,7 +1258,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
       split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
     }
-    f16* T = reinterpret_cast<f16*>(my);  // [kLRTilesPerWave][16][TS]
+    f16* T = reinterpret_cast<f16*>(my);  // Ux^T [RQ][kTTStride]: column j of the wave's 64 positions
     float zz[kLRTilesPerWave][4];
     // Ux = [U | 1 | 0]; the anchor row has U = 0.  Per lane and 16-column
     // tile: a 64-bit mask keeping the columns below r and the fp16 1.0 at
@@ -1284,7 +1285,8 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         uint64_t w = __builtin_bit_cast(uint64_t, ua[k][s]) >> (16 * back);
         w = (w & (i > 0 ? keep[s] : 0ull)) | one[s];
         ua[k][s] = __builtin_bit_cast(v4h, w);
-        *reinterpret_cast<v4h*>(T + (k * 16 + l16) * TS + 16 * s + 4 * q4) = ua[k][s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) T[(16 * s + 4 * q4 + e) * kTTStride + k * 16 + l16] = ua[k][s][e];
       }
       v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1331,9 +1333,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       const v4h ph = to_h4(pe[k]);
 #pragma unroll
       for (int n = 0; n < NQ; ++n) {
-        v4h au;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) au[e] = T[(k * 16 + 4 * q4 + e) * TS + 16 * n + l16];
+        const v4h au = *reinterpret_cast<const v4h*>(T + (16 * n + l16) * kTTStride + k * 16 + 4 * q4);
         Wt[n] = mfma16(au, ph, Wt[n]);
       }
     }
@@ -1343,7 +1343,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   // ---- exact rows: two 16-row tiles per softmax step
   if (QB != 0 && n_ex > 0) {
     f16* Va = reinterpret_cast<f16*>(my);
-    f16* Vb = Va + 16 * kVStride;
+    f16* Vb = Va + kD * kVTStride;
     // this lane's head's query sums over dimensions 0..63 and 64..127
     float Q0 = 0.f, Q1 = 0.f;
 #pragma unroll
@@ -1370,7 +1370,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
   if (QB == 0 && n_ex > 0) {
     f16* Va = reinterpret_cast<f16*>(my);
-    f16* Vb = Va + 16 * kVStride;
+    f16* Vb = Va + kD * kVTStride;
     while (ta < ntile) {
       const bool has_b = tb < ntile;  // uniform over the wave
       const int ta_n = ta + 2 * kAttWaves, tb_n = tb + 2 * kAttWaves;
