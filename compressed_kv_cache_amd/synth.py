@@ -368,3 +368,47 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
                              window=2048, n_blocks=[504] * 8, ranks=[32], n_resid=128, top_k=64,
                              decay=0.93)
     raise ValueError(f"unknown config {cfg}")
+
+
+# ---------------------------------------------------------------------------
+# Blocks to seal (the write side of the cache): the raw keys and values of
+# 256-token blocks, and the Gaussian test matrix of the randomised SVD.
+#
+# Each (block, KV head) holds X = [K | V] (256 x 256): a per-block offset row
+# ~ N(0, 1), plus a planted rank-`true_rank` part C W with C[:, j] ~
+# N(0, sigma_j^2), sigma_j = s0 * decay^j, and W with orthonormal rows, plus
+# N(0, noise^2) noise, plus N(0, outlier_std^2) added to `n_outliers`
+# distinct rows among 1..255: tokens the low-rank part cannot hold (with the
+# defaults a planted row carries less energy, 256 * 0.35^2 = 31, than the
+# 32nd planted component, about 46, so a rank-32 basis does not spend a
+# component on it, while its key error, about 4, is far above the others').  The
+# test matrix is N(0, 1) in float32, [256][width].  Keys and values are
+# rounded once to fp16.
+
+@dataclasses.dataclass
+class SealInput:
+    k: np.ndarray          # fp16 [n_blocks][Hkv][256][128]
+    v: np.ndarray          # fp16 [n_blocks][Hkv][256][128]
+    omega: np.ndarray      # float32 [256][width]
+    outliers: np.ndarray   # uint8 [n_blocks][Hkv][n_outliers], the planted rows
+
+
+def make_seal_input(seed: int, n_blocks: int, n_kv_heads: int, *, width: int, true_rank: int = 48,
+                    s0: float = 4.0, decay: float = 0.93, noise: float = 0.05, n_outliers: int = 8,
+                    outlier_std: float = 0.35) -> SealInput:
+    rng = np.random.default_rng(seed)
+    streams = rng.spawn(6)
+    lead = (n_blocks, n_kv_heads)
+    two_d = 2 * HEAD_DIM
+    x = _normal(streams[0], lead + (1, two_d)) + np.zeros(lead + (BLOCK_SIZE, two_d), np.float32)
+    sig = (s0 * decay ** np.arange(true_rank)).astype(np.float32)
+    c = _normal(streams[1], lead + (BLOCK_SIZE, true_rank)) * sig
+    w = _orthonormal_rows(streams[2], lead, true_rank, two_d)
+    x += np.matmul(c, w)
+    x += _normal(streams[3], lead + (BLOCK_SIZE, two_d), noise)
+    pos = _positions(streams[4], lead, n_outliers)
+    bump = _normal(streams[5], lead + (n_outliers, two_d), outlier_std)
+    for idx in np.ndindex(*lead):
+        x[idx][pos[idx].astype(np.int64)] += bump[idx]
+    omega = np.random.default_rng([seed, 1]).standard_normal((two_d, width), dtype=np.float32)
+    return SealInput(k=_f16(x[..., :HEAD_DIM]), v=_f16(x[..., HEAD_DIM:]), omega=omega, outliers=pos)

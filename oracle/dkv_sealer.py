@@ -1,0 +1,140 @@
+"""fp64 CPU oracle for sealing a DKV block (the write side of the compressed cache).
+
+TEST INFRASTRUCTURE ONLY.  Only tests, the package's smoke() check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library and never sees its outputs.
+
+What it computes (sources are the pages on DKV, cited by title and section):
+
+* Block layout -- "DKV: Anchor + Low-Rank Differential KV-Cache Compression for
+  Scalable Long-Context Inference" (Zenodo record, abstract) and the
+  Differential-KV README, "Core Architecture & Paper Overview", items 1-3: the
+  first token of a 256-token block is the anchor (a_k, a_v), kept exact; the
+  other 255 tokens are represented by a rank-r truncated SVD of the joint K|V
+  delta, U in R^{255 x r} and V_K, V_V in R^{r x d}; a budget of R tokens is
+  kept exact as residual rows.
+* Residual selection -- README "Content-Aware / Rarity-Aware Residual
+  Selection": plain DKV picks the residual tokens by the L2 reconstruction
+  error of their key, the largest errors first (the content-aware boosts
+  need token text and are not built).
+* The SVD is randomised and seeded -- README "Key Environment Knobs"
+  (DKV_SVD_SEED, the random state of the SVD) and the note on A/B method
+  (the randomised SVD's seed is the axis to vary).  The steps are those of a
+  randomised subspace iteration (Halko, Martinsson and Tropp, "Finding
+  structure with randomness", the range finder with power iterations followed
+  by the SVD of the small projected matrix).  The Gaussian test matrix is an
+  input: the caller draws it from its seeded generator.
+
+Readings where the pages are silent (listed in the design notes):
+  the delta is taken relative to the anchor, A = [K[1:] - a_k | V[1:] - a_v]
+  (255 x 256), and the singular values are folded into U; the oversampling p
+  (test-matrix width r + p) and the number of power iterations q are
+  arguments, with defaults p = 8 and q = 2; each orthonormalisation is a QR
+  factorisation (any orthonormal basis of the same range gives the same
+  result); the factors are stored as fp16 (round to nearest even) and the
+  residual errors are measured against the reconstruction from those stored
+  factors; equal errors go to the lower position; positions are stored in
+  ascending order.
+
+Every function is plain numpy in float64: inputs are upcast exactly from fp16.
+Pins against things other than this code live in tests/test_oracle_sealer.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 256
+D = 128
+ROWS = BLOCK - 1
+
+DEFAULT_OVERSAMPLE = 8
+DEFAULT_POWER_ITERS = 2
+
+
+def joint_delta(k: np.ndarray, v: np.ndarray):
+    """Anchor and joint delta of one block: a_k = k[0], a_v = v[0] and
+    A = [k[1:] - a_k | v[1:] - a_v] (README "Core Architecture", items 1-2)."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    assert k.shape == (BLOCK, D) and v.shape == (BLOCK, D)
+    a_k, a_v = k[0].copy(), v[0].copy()
+    return a_k, a_v, np.hstack([k[1:] - a_k, v[1:] - a_v])
+
+
+def _orth(x: np.ndarray) -> np.ndarray:
+    q, _ = np.linalg.qr(x)
+    return q
+
+
+def randomized_svd(a: np.ndarray, rank: int, omega: np.ndarray, power_iters: int = DEFAULT_POWER_ITERS):
+    """Rank-`rank` factors of `a` by randomised subspace iteration with the
+    test matrix `omega` (n x l): Y = A omega, Q = orth(Y); q times Z =
+    orth(A^T Q), Q = orth(A Z); then B = Q^T A = Ub S W^T (a small exact SVD)
+    and A ~ (Q Ub_r) S_r W_r^T.  Returns (U S, singular values, W^T rows)."""
+    a = np.asarray(a, np.float64)
+    omega = np.asarray(omega, np.float64)
+    assert omega.shape[0] == a.shape[1] and omega.shape[1] >= rank
+    q = _orth(a @ omega)
+    for _ in range(power_iters):
+        z = _orth(a.T @ q)
+        q = _orth(a @ z)
+    b = q.T @ a
+    ub, s, wt = np.linalg.svd(b, full_matrices=False)
+    us = (q @ ub[:, :rank]) * s[:rank]
+    return us, s[:rank], wt[:rank]
+
+
+def _f16(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, np.float64).astype(np.float16)
+
+
+def residual_errors(k: np.ndarray, a_k: np.ndarray, u: np.ndarray, vk: np.ndarray) -> np.ndarray:
+    """L2 error of each reconstructed key, e_i = |k_i - (a_k + U_{i-1} V_K)|
+    for positions i = 1..255 (README, residual selection by reconstruction
+    error), from the given (stored) factors."""
+    k = np.asarray(k, np.float64)
+    rec = np.asarray(a_k, np.float64) + np.asarray(u, np.float64) @ np.asarray(vk, np.float64)
+    return np.sqrt(np.sum((k[1:] - rec) ** 2, axis=1))
+
+
+def select_residuals(err: np.ndarray, n_resid: int) -> np.ndarray:
+    """The n_resid positions (1-based in-block, 1..255) with the largest error,
+    equal errors to the lower position, in ascending order."""
+    err = np.asarray(err, np.float64)
+    order = sorted(range(err.shape[0]), key=lambda i: (-err[i], i))
+    return np.sort(np.array(order[:n_resid], dtype=np.int64) + 1)
+
+
+def seal_block(k: np.ndarray, v: np.ndarray, rank: int, n_resid: int, omega: np.ndarray,
+               power_iters: int = DEFAULT_POWER_ITERS) -> dict:
+    """One block (256 x 128 keys and values, fp16 values) sealed into the pool
+    arrays of one slot and KV head: anchors, U (255 x r), V_K, V_V (r x 128),
+    residual positions and rows.  Stored factors are fp16; `fp64` holds the
+    unrounded factors and the singular values."""
+    assert 1 <= rank <= min(ROWS, 2 * D) and 0 <= n_resid <= ROWS
+    a_k, a_v, a = joint_delta(k, v)
+    us, s, wt = randomized_svd(a, rank, omega, power_iters)
+    u16, vk16, vv16 = _f16(us), _f16(wt[:, :D]), _f16(wt[:, D:])
+    err = residual_errors(k, a_k, u16, vk16)
+    pos = select_residuals(err, n_resid)
+    k16, v16 = np.asarray(k, np.float16), np.asarray(v, np.float16)
+    return {
+        "anchor_k": k16[0].copy(), "anchor_v": v16[0].copy(),
+        "u": u16, "vk": vk16, "vv": vv16,
+        "resid_pos": pos.astype(np.uint8),
+        "resid_k": k16[pos].copy(), "resid_v": v16[pos].copy(),
+        "err": err,
+        "fp64": {"us": us, "s": s, "wt": wt},
+    }
+
+
+def reconstruct(sealed: dict):
+    """Keys and values a sealed block stands for: the anchor, a + U V for the
+    other positions, and the residual rows in place of their twins."""
+    u = np.asarray(sealed["u"], np.float64)
+    k = np.vstack([sealed["anchor_k"], np.asarray(sealed["anchor_k"], np.float64) + u @ np.asarray(sealed["vk"], np.float64)])
+    v = np.vstack([sealed["anchor_v"], np.asarray(sealed["anchor_v"], np.float64) + u @ np.asarray(sealed["vv"], np.float64)])
+    pos = np.asarray(sealed["resid_pos"], np.int64)
+    k[pos] = np.asarray(sealed["resid_k"], np.float64)
+    v[pos] = np.asarray(sealed["resid_v"], np.float64)
+    return k, v
