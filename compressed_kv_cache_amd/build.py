@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "dkv_attn.hip")
+SRCS = [os.path.join(HERE, "csrc", "dkv_attn.hip"), os.path.join(HERE, "csrc", "dkv_seal.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libdkv_attn.so")
 
@@ -26,7 +26,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-o", tmp] + SRCS
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)

@@ -2304,6 +2304,13 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
 
 }  // namespace
 
+// Error reporting for the library's other translation unit (the block sealer):
+// the same thread-local message that dkv_last_error() returns.
+__attribute__((visibility("hidden"))) dkv_status dkv_fail_message(dkv_status s, const char* msg) {
+  return fail(s, "%s", msg);
+}
+__attribute__((visibility("hidden"))) void dkv_clear_error_message() { g_err[0] = 0; }
+
 // ----------------------------------------------------------------------------
 // C ABI
 // ----------------------------------------------------------------------------

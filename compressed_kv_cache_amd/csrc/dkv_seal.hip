@@ -1,0 +1,598 @@
+// Block sealer of the DKV compressed KV cache on gfx950: the write side.
+//
+// A 256-token block of one KV head is reduced to its anchor (the first token,
+// exact), a rank-r joint K|V delta U (255 x r, singular values folded in),
+// V_K, V_V (r x 128), and the R tokens the delta reconstructs worst, kept
+// exact (pages: "DKV: Anchor + Low-Rank Differential KV-Cache Compression for
+// Scalable Long-Context Inference", Zenodo abstract; Differential-KV README,
+// "Core Architecture & Paper Overview" items 1-3, "Content-Aware /
+// Rarity-Aware Residual Selection" for the plain L2 selection, "Key
+// Environment Knobs" for the seeded randomised SVD).
+//
+// One workgroup (256 threads) per (block, KV head).  With A = [K[1:] - K[0] |
+// V[1:] - V[0]] (255 x 256), the steps of a randomised subspace iteration:
+//   Y = A omega, Q = orth(Y); power_iters times Z = orth(A^T Q), Q = orth(A Z);
+//   B^T = A^T Q; C = B B^T (width x width) = Z_B^T Z_B; C = E diag(l) E^T by
+//   cyclic Jacobi; U S = Q E_r S_r, W_r = B^T E_r S_r^-1, [V_K | V_V] = W_r^T.
+// Thread mapping: a row product (Y = A F) gives thread t row t of the result,
+// a column product (Z = A^T F) thread c row c; the factor F sits in LDS and
+// every thread reads the same row of it at a time (LDS broadcast).  orth() is
+// Cholesky QR, twice: the Gram matrix in LDS (4 x 4 register blocks), its
+// Cholesky factor by one wave, the triangular solve on each thread's row in
+// registers; pivots below 1e-5 of the largest diagonal drop their column (a
+// rank-deficient Y spans fewer directions).  All arithmetic is fp32; the
+// factors are stored as fp16 (round to nearest even), and the residual errors
+// are measured against the reconstruction from those stored factors.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "dkv_attn.h"
+
+__attribute__((visibility("hidden"))) dkv_status dkv_fail_message(dkv_status s, const char* msg);
+__attribute__((visibility("hidden"))) void dkv_clear_error_message();
+
+typedef _Float16 f16;
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRows = 255;          // delta rows: tokens 1..255
+constexpr int kThreads = 256;
+constexpr int kMaxWidth = 80;       // columns of the test matrix
+constexpr int kMaxPowerIters = 8;
+constexpr int kMaxSweeps = 24;      // Jacobi sweeps (they stop once no rotation is needed)
+constexpr int kOrthPasses = 2;      // Cholesky QR passes per orthonormalisation
+constexpr float kDropPivot = 1e-5f; // relative pivot below which a column is dropped
+constexpr float kJacobiSkip = 1e-7f;
+
+struct SealArgs {
+  const f16* sk; int64_t sk_s, sk_h;
+  const f16* sv; int64_t sv_s, sv_h;
+  const int32_t* slots;
+  int n_heads, n_slots;
+  const float* omega; int width;
+  int rank, n_resid, power_iters;
+  f16* ak; int64_t ak_s, ak_h;
+  f16* av; int64_t av_s, av_h;
+  f16* u; int64_t u_s, u_h;
+  f16* vk; int64_t vk_s, vk_h;
+  f16* vv; int64_t vv_s, vv_h;
+  f16* rk; int64_t rk_s, rk_h;
+  f16* rv; int64_t rv_s, rv_h;
+  uint8_t* rp; int64_t rp_s, rp_h;
+};
+
+// LDS layout (in 4-byte words) for a padded width LP (a multiple of 16)
+template <int LP>
+struct Lay {
+  static constexpr int SS = LP + 4;  // row stride of S, G, E: 16-byte aligned rows
+  static constexpr int S = 0;                    // [256][SS] the factor of a product / rows for a Gram
+  static constexpr int G = S + 256 * SS;         // [LP][SS] Gram, Cholesky factor, Jacobi matrix
+  static constexpr int E = G + LP * SS;          // [LP][SS] Jacobi eigenvectors
+  static constexpr int ANC = E + LP * SS;        // [256] anchor row (fp32)
+  static constexpr int ERR = ANC + 256;          // [256] squared key errors
+  static constexpr int SEL = ERR + 256;          // [256] selected flags
+  static constexpr int INV = SEL + 256;          // [LP] inverse Cholesky pivots
+  static constexpr int SIG = INV + LP;           // [LP] singular values, descending
+  static constexpr int PERM = SIG + LP;          // [LP] eigenvalue order
+  static constexpr int RC = PERM + LP;           // [LP / 2] rotation cosines
+  static constexpr int RS = RC + LP / 2;         // [LP / 2] rotation sines
+  static constexpr int RP = RS + LP / 2;         // [LP / 2] rotation pairs (p)
+  static constexpr int RQ = RP + LP / 2;         // [LP / 2] rotation pairs (q)
+  static constexpr int FLAG = RQ + LP / 2;       // [4] rotation counters of the sweeps
+  static constexpr int WORDS = FLAG + 4;
+  static constexpr size_t bytes = (size_t)WORDS * 4;
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS operations are done
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// v = A[t] F for row t of A (thread t; row 255 does not exist and gives 0)
+template <int LP>
+__device__ __forceinline__ void row_product(const f16* xk, const f16* xv, const float* anc, const float* F, int t,
+                                            float (&v)[LP]) {
+  constexpr int SS = Lay<LP>::SS;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) v[j] = 0.f;
+  if (t >= kRows) return;
+  const f16* kr = xk + (int64_t)(t + 1) * kD;
+  const f16* vr = xv + (int64_t)(t + 1) * kD;
+  for (int c8 = 0; c8 < 2 * kD / 8; ++c8) {
+    const v8h x = *reinterpret_cast<const v8h*>(c8 < kD / 8 ? kr + 8 * c8 : vr + 8 * (c8 - kD / 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 8 * c8 + e;
+      const float a = (float)x[e] - anc[c];
+      const float4* fr = reinterpret_cast<const float4*>(F + c * SS);
+#pragma unroll
+      for (int j4 = 0; j4 < LP / 4; ++j4) {
+        const float4 f = fr[j4];
+        v[4 * j4 + 0] = fmaf(a, f.x, v[4 * j4 + 0]);
+        v[4 * j4 + 1] = fmaf(a, f.y, v[4 * j4 + 1]);
+        v[4 * j4 + 2] = fmaf(a, f.z, v[4 * j4 + 2]);
+        v[4 * j4 + 3] = fmaf(a, f.w, v[4 * j4 + 3]);
+      }
+    }
+  }
+}
+
+// v = (A^T F)[c] = sum_t A[t][c] F[t] for column c of A (thread c)
+template <int LP>
+__device__ __forceinline__ void col_product(const f16* xk, const f16* xv, const float* anc, const float* F, int c,
+                                            float (&v)[LP]) {
+  constexpr int SS = Lay<LP>::SS;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) v[j] = 0.f;
+  const f16* col = (c < kD ? xk + c : xv + (c - kD)) + kD;  // row 1 of column c
+  const float ac = anc[c];
+  for (int t = 0; t < kRows; ++t) {
+    const float a = (float)col[(int64_t)t * kD] - ac;
+    const float4* fr = reinterpret_cast<const float4*>(F + t * SS);
+#pragma unroll
+    for (int j4 = 0; j4 < LP / 4; ++j4) {
+      const float4 f = fr[j4];
+      v[4 * j4 + 0] = fmaf(a, f.x, v[4 * j4 + 0]);
+      v[4 * j4 + 1] = fmaf(a, f.y, v[4 * j4 + 1]);
+      v[4 * j4 + 2] = fmaf(a, f.z, v[4 * j4 + 2]);
+      v[4 * j4 + 3] = fmaf(a, f.w, v[4 * j4 + 3]);
+    }
+  }
+}
+
+template <int LP>
+__device__ __forceinline__ void store_row(float* S, int t, const float (&v)[LP]) {
+  float4* d = reinterpret_cast<float4*>(S + t * Lay<LP>::SS);
+#pragma unroll
+  for (int j4 = 0; j4 < LP / 4; ++j4) d[j4] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+}
+
+// G = S^T S over the 256 rows of S (both triangles), in 4 x 4 blocks
+template <int LP>
+__device__ __forceinline__ void gram(const float* S, float* G, int tid) {
+  constexpr int SS = Lay<LP>::SS, NB = LP / 4, NP = NB * (NB + 1) / 2;
+  for (int e = tid; e < NP; e += kThreads) {
+    int bi = 0;
+    while ((bi + 1) * (bi + 2) / 2 <= e) ++bi;
+    const int bj = e - bi * (bi + 1) / 2;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+    for (int t = 0; t < 256; ++t) {
+      const float4 x = *reinterpret_cast<const float4*>(S + t * SS + 4 * bi);
+      const float4 y = *reinterpret_cast<const float4*>(S + t * SS + 4 * bj);
+      const float xa[4] = {x.x, x.y, x.z, x.w}, yb[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(xa[a], yb[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        G[(4 * bi + a) * SS + 4 * bj + b] = acc[a][b];
+        G[(4 * bj + b) * SS + 4 * bi + a] = acc[a][b];
+      }
+  }
+}
+
+// Cholesky factor of G (one wave): L in G's lower triangle, inv[k] = 1 / L[k][k],
+// or 0 for a pivot below kDropPivot of the largest diagonal (its column dropped)
+template <int LP>
+__device__ __forceinline__ void cholesky(float* G, float* inv, int lane) {
+  constexpr int SS = Lay<LP>::SS, R2 = (LP + 63) / 64;
+  float mx = 0.f;
+  for (int i = lane; i < LP; i += 64) mx = fmaxf(mx, G[i * SS + i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float tol = kDropPivot * mx;
+  for (int k = 0; k < LP; ++k) {
+    float s[R2];
+#pragma unroll
+    for (int r2 = 0; r2 < R2; ++r2) {
+      const int i = lane + 64 * r2;
+      s[r2] = 0.f;
+      if (i >= k && i < LP) {
+        float acc = G[i * SS + k];
+        for (int m = 0; m < k; ++m) acc = fmaf(-G[i * SS + m], G[k * SS + m], acc);
+        s[r2] = acc;
+      }
+    }
+    const float d = __shfl(k < 64 ? s[0] : s[R2 - 1], k & 63);
+    const float lkk = d > tol ? sqrtf(d) : 0.f;
+    const float ik = lkk > 0.f ? 1.f / lkk : 0.f;
+#pragma unroll
+    for (int r2 = 0; r2 < R2; ++r2) {
+      const int i = lane + 64 * r2;
+      if (i > k && i < LP) G[i * SS + k] = s[r2] * ik;
+    }
+    if (lane == (k & 63)) {
+      G[k * SS + k] = lkk;
+      inv[k] = ik;
+    }
+    wave_sync();
+  }
+}
+
+// v <- v L^-T (row v of Y becomes row of Q = Y L^-T); dropped columns give 0
+template <int LP>
+__device__ __forceinline__ void solve_row(const float* G, const float* inv, float (&v)[LP]) {
+  constexpr int SS = Lay<LP>::SS;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    float acc = v[j];
+#pragma unroll
+    for (int m = 0; m < j; ++m) acc = fmaf(-v[m], G[j * SS + m], acc);
+    v[j] = acc * inv[j];
+  }
+}
+
+// player in a slot of round k of the circle method (n players, n even)
+__device__ __forceinline__ int player(int slot, int k, int n) { return slot == 0 ? 0 : 1 + (slot - 1 + k) % (n - 1); }
+
+// C (in G, symmetric LP x LP) = E diag(C) E^T by cyclic Jacobi with the
+// rotations of each round (LP / 2 disjoint pairs) applied together
+template <int LP>
+__device__ __forceinline__ void jacobi(float* G, float* E, float* rc, float* rs, int* rp, int* rq, int* flag,
+                                       int tid) {
+  constexpr int SS = Lay<LP>::SS, NP = LP / 2;
+  for (int e = tid; e < LP * LP; e += kThreads) E[(e / LP) * SS + e % LP] = (e / LP == e % LP) ? 1.f : 0.f;
+  if (tid < 4) flag[tid] = 0;
+  __syncthreads();
+  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    if (tid == 0) flag[(sweep + 1) % 3] = 0;  // the counter of the next sweep (last read two sweeps ago)
+    for (int round = 0; round < LP - 1; ++round) {
+      if (tid < NP) {
+        const int a = player(tid, round, LP), b = player(LP - 1 - tid, round, LP);
+        const int p = a < b ? a : b, q = a < b ? b : a;
+        const float app = G[p * SS + p], aqq = G[q * SS + q], apq = G[p * SS + q];
+        float c = 1.f, s = 0.f;
+        if (fabsf(apq) > kJacobiSkip * sqrtf(fabsf(app * aqq)) + 1e-30f) {
+          const float tau = (aqq - app) / (2.f * apq);
+          const float t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
+          c = 1.f / sqrtf(1.f + t * t);
+          s = t * c;
+          atomicAdd(&flag[sweep % 3], 1);
+        }
+        rc[tid] = c;
+        rs[tid] = s;
+        rp[tid] = p;
+        rq[tid] = q;
+      }
+      __syncthreads();
+      // C[P][Q] <- J_P^T C[P][Q] J_Q, with J = [[c, s], [-s, c]] on (p, q)
+      for (int e = tid; e < NP * NP; e += kThreads) {
+        const int P = e / NP, Q = e % NP;
+        const int p1 = rp[P], p2 = rq[P], q1 = rp[Q], q2 = rq[Q];
+        const float cp = rc[P], sp = rs[P], cq = rc[Q], sq = rs[Q];
+        const float m11 = G[p1 * SS + q1], m12 = G[p1 * SS + q2], m21 = G[p2 * SS + q1], m22 = G[p2 * SS + q2];
+        const float t11 = cp * m11 - sp * m21, t12 = cp * m12 - sp * m22;
+        const float t21 = sp * m11 + cp * m21, t22 = sp * m12 + cp * m22;
+        G[p1 * SS + q1] = cq * t11 - sq * t12;
+        G[p1 * SS + q2] = sq * t11 + cq * t12;
+        G[p2 * SS + q1] = cq * t21 - sq * t22;
+        G[p2 * SS + q2] = sq * t21 + cq * t22;
+      }
+      // E <- E J
+      for (int e = tid; e < LP * NP; e += kThreads) {
+        const int i = e / NP, P = e % NP;
+        const int p = rp[P], q = rq[P];
+        const float c = rc[P], s = rs[P];
+        const float ep = E[i * SS + p], eq = E[i * SS + q];
+        E[i * SS + p] = c * ep - s * eq;
+        E[i * SS + q] = s * ep + c * eq;
+      }
+      __syncthreads();
+    }
+    if (flag[sweep % 3] == 0) break;  // uniform: read after the sweep's last barrier
+  }
+}
+
+template <int LP>
+__global__ __launch_bounds__(kThreads) void k_seal(SealArgs A) {
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+  typedef Lay<LP> L;
+  constexpr int SS = L::SS;
+  float* S = lds + L::S;
+  float* G = lds + L::G;
+  float* E = lds + L::E;
+  float* anc = lds + L::ANC;
+  float* errv = lds + L::ERR;
+  int* sel = reinterpret_cast<int*>(lds + L::SEL);
+  float* inv = lds + L::INV;
+  float* sig = lds + L::SIG;
+  int* perm = reinterpret_cast<int*>(lds + L::PERM);
+  float* rc = lds + L::RC;
+  float* rs = lds + L::RS;
+  int* rp = reinterpret_cast<int*>(lds + L::RP);
+  int* rq = reinterpret_cast<int*>(lds + L::RQ);
+  int* flag = reinterpret_cast<int*>(lds + L::FLAG);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / A.n_heads, h = blockIdx.x % A.n_heads;
+  const int slot = A.slots[b];
+  if (slot < 0 || slot >= A.n_slots) return;  // the same in every thread
+  const f16* xk = A.sk + b * A.sk_s + h * A.sk_h;  // [256][128]
+  const f16* xv = A.sv + b * A.sv_s + h * A.sv_h;
+
+  // anchor row, and the test matrix (zero-padded to LP columns)
+  anc[tid] = (float)(tid < kD ? xk[tid] : xv[tid - kD]);
+  for (int i = tid; i < 256 * LP; i += kThreads) {
+    const int c = i / LP, j = i % LP;
+    S[c * SS + j] = j < A.width ? A.omega[(int64_t)c * A.width + j] : 0.f;
+  }
+  __syncthreads();
+
+  // ---- range finder: v holds this thread's row of Y, Z or Q.  Step 0 is
+  //      Y = A omega; then odd steps Z = A^T Q, even steps Y = A Z; each
+  //      result is orthonormalised.
+  float v[LP];
+  const int n_steps = 1 + 2 * A.power_iters;
+  for (int step = 0; step < n_steps; ++step) {
+    if (step > 0) {
+      store_row<LP>(S, tid, v);  // the factor of this step's product
+      __syncthreads();
+    }
+    if (step & 1)
+      col_product<LP>(xk, xv, anc, S, tid, v);
+    else
+      row_product<LP>(xk, xv, anc, S, tid, v);
+    __syncthreads();  // every thread is done reading S
+    for (int pass = 0; pass < kOrthPasses; ++pass) {
+      store_row<LP>(S, tid, v);
+      __syncthreads();
+      gram<LP>(S, G, tid);
+      __syncthreads();
+      if (wave == 0) cholesky<LP>(G, inv, lane);
+      __syncthreads();
+      solve_row<LP>(G, inv, v);
+      __syncthreads();  // G and S are rewritten next
+    }
+  }
+  // ---- B^T = A^T Q (thread c: row c), C = B B^T
+  float z[LP];
+  store_row<LP>(S, tid, v);
+  __syncthreads();
+  col_product<LP>(xk, xv, anc, S, tid, z);
+  __syncthreads();
+  store_row<LP>(S, tid, z);
+  __syncthreads();
+  gram<LP>(S, G, tid);
+  __syncthreads();
+  if (tid < LP) perm[tid] = tid;  // (every entry is rewritten below; never left unset)
+  jacobi<LP>(G, E, rc, rs, rp, rq, flag, tid);
+  // ---- singular values in descending order (equal ones by index)
+  if (tid < LP) {
+    const float lt = G[tid * SS + tid];
+    int r = 0;
+    for (int i = 0; i < LP; ++i) {
+      const float li = G[i * SS + i];
+      r += (li > lt || (li == lt && i < tid)) ? 1 : 0;
+    }
+    r = r < LP ? r : LP - 1;
+    perm[r] = tid;
+    sig[r] = sqrtf(fmaxf(lt, 0.f));
+  }
+  __syncthreads();
+  // ---- right factors: W_k = B^T E_k / sigma_k (thread c: entry c), stored
+  //      as fp16 and kept (rounded) in S for the residual errors
+  const int rank = A.rank;
+  {
+    const int c = tid;
+    f16* dst = c < kD ? A.vk + slot * A.vk_s + h * A.vk_h + c : A.vv + slot * A.vv_s + h * A.vv_h + (c - kD);
+    for (int k = 0; k < rank; ++k) {
+      const int pk = min(max(perm[k], 0), LP - 1);
+      float w = 0.f;
+#pragma unroll
+      for (int j = 0; j < LP; ++j) w = fmaf(z[j], E[j * SS + pk], w);
+      const float sk = sig[k];
+      const f16 w16 = (f16)(sk > 0.f ? w / sk : 0.f);
+      dst[(int64_t)k * kD] = w16;
+      if (c < kD) S[k * kD + c] = (float)w16;  // V_K [rank][128]: rank * 128 <= LP * 128 < 256 * SS
+    }
+  }
+  __syncthreads();
+  // ---- left factors U S = Q E_k sigma_k (thread t: row t), the reconstruction
+  //      of its key from the stored factors, and its squared error
+  const int t = tid;
+  if (t < kRows) {
+    float rec[kD];
+#pragma unroll
+    for (int c = 0; c < kD; ++c) rec[c] = anc[c];
+    f16* urow = A.u + slot * A.u_s + h * A.u_h + (int64_t)t * rank;
+    for (int k = 0; k < rank; ++k) {
+      const int pk = min(max(perm[k], 0), LP - 1);
+      float uk = 0.f;
+#pragma unroll
+      for (int j = 0; j < LP; ++j) uk = fmaf(v[j], E[j * SS + pk], uk);
+      const f16 u16 = (f16)(uk * sig[k]);
+      urow[k] = u16;
+      const float uf = (float)u16;
+      const float4* vkr = reinterpret_cast<const float4*>(S + k * kD);
+#pragma unroll
+      for (int c4 = 0; c4 < kD / 4; ++c4) {
+        const float4 w = vkr[c4];
+        rec[4 * c4 + 0] = fmaf(uf, w.x, rec[4 * c4 + 0]);
+        rec[4 * c4 + 1] = fmaf(uf, w.y, rec[4 * c4 + 1]);
+        rec[4 * c4 + 2] = fmaf(uf, w.z, rec[4 * c4 + 2]);
+        rec[4 * c4 + 3] = fmaf(uf, w.w, rec[4 * c4 + 3]);
+      }
+    }
+    const f16* kr = xk + (int64_t)(t + 1) * kD;
+    float e2 = 0.f;
+#pragma unroll
+    for (int c8 = 0; c8 < kD / 8; ++c8) {
+      const v8h x = *reinterpret_cast<const v8h*>(kr + 8 * c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = (float)x[e] - rec[8 * c8 + e];
+        e2 = fmaf(d, d, e2);
+      }
+    }
+    errv[t] = e2;
+  }
+  // ---- anchors (exact copies)
+  {
+    const int c = tid;
+    if (c < kD)
+      A.ak[slot * A.ak_s + h * A.ak_h + c] = xk[c];
+    else
+      A.av[slot * A.av_s + h * A.av_h + (c - kD)] = xv[c - kD];
+  }
+  __syncthreads();
+  // ---- residual rows: the n_resid largest errors (equal errors: lower
+  //      position first), stored in ascending position order
+  if (A.n_resid > 0) {
+    if (t < kRows) {
+      const float et = errv[t];
+      int r = 0;
+      for (int i = 0; i < kRows; ++i) {
+        const float ei = errv[i];
+        r += (ei > et || (ei == et && i < t)) ? 1 : 0;
+      }
+      sel[t] = r < A.n_resid ? 1 : 0;
+    }
+    __syncthreads();
+    if (t < kRows && sel[t]) {
+      int o = 0;
+      for (int i = 0; i < t; ++i) o += sel[i];
+      if (o >= A.n_resid) return;  // only with non-finite errors (ranks then tie): never write past R rows
+      A.rp[slot * A.rp_s + h * A.rp_h + o] = (uint8_t)(t + 1);
+      const v8h* ks = reinterpret_cast<const v8h*>(xk + (int64_t)(t + 1) * kD);
+      const v8h* vs = reinterpret_cast<const v8h*>(xv + (int64_t)(t + 1) * kD);
+      v8h* kd = reinterpret_cast<v8h*>(A.rk + slot * A.rk_s + h * A.rk_h + (int64_t)o * kD);
+      v8h* vd = reinterpret_cast<v8h*>(A.rv + slot * A.rv_s + h * A.rv_h + (int64_t)o * kD);
+#pragma unroll
+      for (int c8 = 0; c8 < kD / 8; ++c8) {
+        kd[c8] = ks[c8];
+        vd[c8] = vs[c8];
+      }
+    }
+  }
+}
+
+dkv_status fail(dkv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dkv_status fail(dkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  return dkv_fail_message(s, buf);
+}
+
+bool al(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
+
+dkv_status check_out(const dkv_view& v, const char* name, int esz, int align) {
+  if (!v.ptr) return fail(DKV_ERR_INVALID_ARG, "pool->%s.ptr is NULL", name);
+  if (!al(v.ptr, align) || (v.slot_stride * esz) % align != 0 || (v.head_stride * esz) % align != 0)
+    return fail(DKV_ERR_UNSUPPORTED, "pool->%s must be %d-byte aligned (pointer and strides)", name, align);
+  return DKV_OK;
+}
+
+template <int LP>
+dkv_status launch_seal(const SealArgs& a, unsigned grid, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_seal<LP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)Lay<LP>::bytes) != hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_seal) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_seal<LP>), dim3(grid), dim3(kThreads), Lay<LP>::bytes, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_seal launch failed: %s", hipGetErrorString(e));
+  return DKV_OK;
+}
+
+static_assert(Lay<kMaxWidth>::bytes <= 160 * 1024, "sealer LDS exceeds 160 KB");
+static_assert(Lay<16>::SS >= 1, "padded width");
+
+}  // namespace
+
+extern "C" {
+
+dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v, const int32_t* slots,
+                           int32_t n_blocks, const float* omega, int32_t width, int32_t power_iters, void* stream) {
+  dkv_clear_error_message();
+  const dkv_pool* P = pool;
+  if (!P) return fail(DKV_ERR_INVALID_ARG, "pool is NULL");
+  if (P->head_dim != DKV_HEAD_DIM) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d != 128", P->head_dim);
+  if (P->block_size != DKV_BLOCK_SIZE) return fail(DKV_ERR_UNSUPPORTED, "block_size %d != 256", P->block_size);
+  if (P->rank < 1) return fail(DKV_ERR_INVALID_ARG, "rank %d < 1", P->rank);
+  if (P->rank > DKV_MAX_RANK) return fail(DKV_ERR_UNSUPPORTED, "rank %d > 64", P->rank);
+  if (P->n_resid < 0) return fail(DKV_ERR_INVALID_ARG, "n_resid %d < 0", P->n_resid);
+  if (P->n_resid > DKV_MAX_RESID) return fail(DKV_ERR_UNSUPPORTED, "n_resid %d > 255", P->n_resid);
+  if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
+  if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
+  if (P->resid_format != DKV_RESID_FP16)
+    return fail(DKV_ERR_UNSUPPORTED, "sealing writes fp16 residual rows only (resid_format %d)", P->resid_format);
+  if (width < P->rank) return fail(DKV_ERR_INVALID_ARG, "width %d < rank %d", width, P->rank);
+  if (width > kMaxWidth) return fail(DKV_ERR_UNSUPPORTED, "width %d > %d", width, kMaxWidth);
+  if (power_iters < 0 || power_iters > kMaxPowerIters)
+    return fail(DKV_ERR_INVALID_ARG, "power_iters %d not in 0..%d", power_iters, kMaxPowerIters);
+  if (n_blocks < 0) return fail(DKV_ERR_INVALID_ARG, "n_blocks %d < 0", n_blocks);
+  if (n_blocks == 0) return DKV_OK;
+  if (!slots || !omega) return fail(DKV_ERR_INVALID_ARG, "slots / omega is NULL");
+  if (!al(omega, 4)) return fail(DKV_ERR_UNSUPPORTED, "omega must be 4-byte aligned");
+  if (!src_k.ptr || !src_v.ptr) return fail(DKV_ERR_INVALID_ARG, "src_k / src_v is NULL");
+  if (!al(src_k.ptr, 16) || !al(src_v.ptr, 16) || (src_k.slot_stride * 2) % 16 || (src_k.head_stride * 2) % 16 ||
+      (src_v.slot_stride * 2) % 16 || (src_v.head_stride * 2) % 16)
+    return fail(DKV_ERR_UNSUPPORTED, "src_k / src_v must be 16-byte aligned (pointers and strides)");
+  dkv_status s;
+  if ((s = check_out(P->anchor_k, "anchor_k", 2, 2)) || (s = check_out(P->anchor_v, "anchor_v", 2, 2)) ||
+      (s = check_out(P->u, "u", 2, 2)) || (s = check_out(P->vk, "vk", 2, 2)) || (s = check_out(P->vv, "vv", 2, 2)))
+    return s;
+  if (P->n_resid > 0 && ((s = check_out(P->resid_k, "resid_k", 2, 16)) ||
+                         (s = check_out(P->resid_v, "resid_v", 2, 16)) ||
+                         (s = check_out(P->resid_pos, "resid_pos", 1, 1))))
+    return s;
+  const int64_t grid = (int64_t)n_blocks * P->n_kv_heads;
+  if (grid > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many blocks");
+  SealArgs a;
+  a.sk = (const f16*)src_k.ptr; a.sk_s = src_k.slot_stride; a.sk_h = src_k.head_stride;
+  a.sv = (const f16*)src_v.ptr; a.sv_s = src_v.slot_stride; a.sv_h = src_v.head_stride;
+  a.slots = slots;
+  a.n_heads = P->n_kv_heads;
+  a.n_slots = P->n_slots;
+  a.omega = omega;
+  a.width = width;
+  a.rank = P->rank;
+  a.n_resid = P->n_resid;
+  a.power_iters = power_iters;
+  a.ak = (f16*)P->anchor_k.ptr; a.ak_s = P->anchor_k.slot_stride; a.ak_h = P->anchor_k.head_stride;
+  a.av = (f16*)P->anchor_v.ptr; a.av_s = P->anchor_v.slot_stride; a.av_h = P->anchor_v.head_stride;
+  a.u = (f16*)P->u.ptr; a.u_s = P->u.slot_stride; a.u_h = P->u.head_stride;
+  a.vk = (f16*)P->vk.ptr; a.vk_s = P->vk.slot_stride; a.vk_h = P->vk.head_stride;
+  a.vv = (f16*)P->vv.ptr; a.vv_s = P->vv.slot_stride; a.vv_h = P->vv.head_stride;
+  a.rk = (f16*)P->resid_k.ptr; a.rk_s = P->resid_k.slot_stride; a.rk_h = P->resid_k.head_stride;
+  a.rv = (f16*)P->resid_v.ptr; a.rv_s = P->resid_v.slot_stride; a.rv_h = P->resid_v.head_stride;
+  a.rp = (uint8_t*)P->resid_pos.ptr; a.rp_s = P->resid_pos.slot_stride; a.rp_h = P->resid_pos.head_stride;
+  hipStream_t st = (hipStream_t)stream;
+  const unsigned g = (unsigned)grid;
+  if (width <= 16)
+    s = launch_seal<16>(a, g, st);
+  else if (width <= 32)
+    s = launch_seal<32>(a, g, st);
+  else if (width <= 48)
+    s = launch_seal<48>(a, g, st);
+  else if (width <= 64)
+    s = launch_seal<64>(a, g, st);
+  else
+    s = launch_seal<80>(a, g, st);
+  if (s != DKV_OK) return s;
+  if (P->route_key.ptr) return dkv_route_keys(P, slots, n_blocks, stream);
+  return DKV_OK;
+}
+
+}  // extern "C"

@@ -32,7 +32,8 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_route_topk", "dkv_lowrank_attn", "dkv_exact_attn", "dkv_lse_merge",
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
-            "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers")
+            "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
+            "dkv_seal_blocks")
 
 
 class DKVError(RuntimeError):
@@ -109,6 +110,8 @@ def load(path: str = LIB_PATH):
     lib.dkv_decode_layers_prepare.restype = i32
     lib.dkv_decode_layers.argtypes = [ctypes.POINTER(LayersPlanC), vp]
     lib.dkv_decode_layers.restype = i32
+    lib.dkv_seal_blocks.argtypes = [P, View, View, vp, i32, vp, i32, i32, vp]
+    lib.dkv_seal_blocks.restype = i32
     lib.dkv_gather_route_keys.restype = i32
     lib.dkv_route_topk.restype = i32
     lib.dkv_lowrank_attn.argtypes = [P, Bp, vp, i32, f32, vp, vp, i32, i32, vp]
@@ -255,6 +258,19 @@ class Pool:
             pool.tensors["_record"] = t["_record"]
         return pool
 
+    @classmethod
+    def empty(cls, n_slots: int, n_kv_heads: int, rank: int, n_resid: int, device="cuda",
+              layout: str = "records"):
+        """A zero-filled fp16-residual pool for dkv_seal_blocks to write into."""
+        S, H, d = n_slots, n_kv_heads, HEAD_DIM
+        arrays = dict(anchor_k=np.zeros((S, H, d), np.float16), anchor_v=np.zeros((S, H, d), np.float16),
+                      u=np.zeros((S, H, BLOCK_SIZE - 1, rank), np.float16),
+                      vk=np.zeros((S, H, rank, d), np.float16), vv=np.zeros((S, H, rank, d), np.float16),
+                      resid_k=np.zeros((S, H, n_resid, d), np.float16),
+                      resid_v=np.zeros((S, H, n_resid, d), np.float16),
+                      resid_pos=np.zeros((S, H, n_resid), np.uint8))
+        return cls.from_numpy(arrays, device, layout)
+
     @property
     def route_key(self):
         return self.tensors["route_key"]
@@ -314,6 +330,22 @@ def gather_route_keys(pool: Pool, batch: Batch, out=None, attach: bool = True, s
     if attach:
         batch.set_route_keys(out)
     return out
+
+
+def seal_blocks(pool: Pool, k, v, slots, omega, power_iters: int = 2, stream=None) -> None:
+    """Seal blocks into pool slots (dkv_seal_blocks).  k, v: fp16 [n_blocks][Hkv][256][128]
+    with contiguous rows; slots: int32 [n_blocks] on the device; omega: fp32 [256][width]."""
+    import torch
+    lib = load()
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.float16 or t.dim() != 4 or tuple(t.shape[2:]) != (BLOCK_SIZE, HEAD_DIM) \
+                or t.stride(3) != 1 or t.stride(2) != HEAD_DIM:
+            raise ValueError(f"{name} must be fp16 [n_blocks][Hkv][256][128] with contiguous rows")
+    if slots.dtype != torch.int32 or omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("slots must be int32, omega contiguous fp32 [256][width]")
+    n = int(k.shape[0])
+    _check(lib.dkv_seal_blocks(ctypes.byref(pool.c), _view(k, 2), _view(v, 2), _ptr(slots), n, _ptr(omega),
+                               int(omega.shape[1]), int(power_iters), _stream(stream)), "dkv_seal_blocks")
 
 
 def route_keys(pool: Pool, slots=None, stream=None) -> None:

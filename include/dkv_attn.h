@@ -307,6 +307,37 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
                                      void* workspace, size_t workspace_bytes, dkv_layers_plan* plan);
 dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream);
 
+/* Block sealing, the write side of the cache (README "Core Architecture &
+ * Paper Overview", items 1-3; "Content-Aware / Rarity-Aware Residual
+ * Selection", the plain L2 selection; "Key Environment Knobs", DKV_SVD_SEED:
+ * the SVD is randomised and seeded).
+ * Block b (0 <= b < n_blocks), KV head h: its 256 keys and values, fp16 rows of
+ * 128 (row stride 128), start at src_k.ptr + b * src_k.slot_stride +
+ * h * src_k.head_stride (elements), likewise src_v.  The block is written into
+ * pool slot slots[b] (device array; a slot outside [0, n_slots) skips it):
+ *   anchor_k, anchor_v  row 0, exact;
+ *   u, vk, vv           rank-r factors of A = [K[1:] - K[0] | V[1:] - V[0]]
+ *                       (255 x 256): U = Q E_r S_r (singular values folded
+ *                       in), [V_K | V_V] = W_r^T, fp16 (round to nearest even),
+ *                       from the randomised subspace iteration Y = A omega,
+ *                       Q = orth(Y), power_iters times Z = orth(A^T Q),
+ *                       Q = orth(A Z), and the exact SVD B = Q^T A = E S W^T;
+ *   resid_pos/k/v       the n_resid positions in 1..255 whose key is worst
+ *                       reconstructed, |k_i - (a_k + U_{i-1} V_K)| from the
+ *                       stored fp16 factors (fp32 arithmetic; equal errors to
+ *                       the lower position), ascending, and their exact rows;
+ *   route_key           as dkv_route_keys, if pool->route_key.ptr is set.
+ *   omega: fp32 [256][width], the Gaussian test matrix (the caller's seeded
+ *          draw); rank <= width <= 80 (DKV_ERR_UNSUPPORTED above 80);
+ *   power_iters: 0..8.
+ * Only the fp16 residual format is written (DKV_ERR_UNSUPPORTED otherwise).
+ * Sources: 16-byte aligned pointers and strides; residual rows likewise.
+ * Source rows and the pool slots written must not overlap, nor two entries of
+ * slots name the same slot.  Asynchronous on `stream`. */
+dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v, const int32_t* slots,
+                           int32_t n_blocks, const float* omega, int32_t width, int32_t power_iters,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -203,3 +203,26 @@ def test_layer_batched_entry_points_validate(clib):
     assert clib.dkv_decode_layers_prepare(PA, BB, 2, 4, 0.1, outs, outs, None, FAKE, tsz, FAKE, need2,
                                           ctypes.byref(plan)) == L.DKV_ERR_INVALID_ARG
     assert clib.dkv_decode_layers(None, None) == L.DKV_ERR_INVALID_ARG
+
+
+def test_seal_blocks_validates(clib):
+    p = _pool()
+    src = L.View(FAKE, 2 * 256 * 128, 256 * 128)
+    omega = FAKE
+
+    def seal(pool=p, width=40, iters=2, n=2, slots=FAKE, om=omega, sk=src):
+        return clib.dkv_seal_blocks(ctypes.byref(pool) if pool is not None else None, sk, src, slots, n, om,
+                                    width, iters, None)
+    assert seal(pool=None) == L.DKV_ERR_INVALID_ARG
+    assert seal(width=31) == L.DKV_ERR_INVALID_ARG          # width below the rank (32)
+    assert seal(width=81) == L.DKV_ERR_UNSUPPORTED          # test matrix wider than 80 columns
+    assert seal(iters=-1) == L.DKV_ERR_INVALID_ARG
+    assert seal(iters=9) == L.DKV_ERR_INVALID_ARG
+    assert seal(n=-1) == L.DKV_ERR_INVALID_ARG
+    assert seal(n=0) == L.DKV_OK                            # nothing to do, nothing enqueued
+    assert seal(slots=None) == L.DKV_ERR_INVALID_ARG
+    assert seal(om=None) == L.DKV_ERR_INVALID_ARG
+    assert seal(sk=L.View(FAKE + 2, 0, 0)) == L.DKV_ERR_UNSUPPORTED   # source rows not 16-byte aligned
+    assert seal(pool=_pool(resid_format=L.RESID_INT8)) == L.DKV_ERR_UNSUPPORTED
+    assert seal(pool=_pool(head_dim=64)) == L.DKV_ERR_UNSUPPORTED
+    assert seal(width=81) == L.DKV_ERR_UNSUPPORTED and b"width" in clib.dkv_last_error()
