@@ -28,6 +28,12 @@ indices; divided by that kernel's duration measured with events around it in
 the timed eager steps (kernels back to back behind a spin kernel, as in a
 replay).  `traffic` is the committed rocprofv3 PMC summary for that kernel
 (`--pmc-summary` writes it), null when the kernel source changed since.
+
+Beside the decode (not part of `value`): the same stack with its residual rows
+in the 8- and 4-bit formats (`quantised_residuals`), and the write side,
+dkv_seal_blocks sealing one layer's 1008 blocks x 2 KV heads at each of the
+stack's ranks (`sealing`: block-heads per second and the fp32 arithmetic rate
+of its main products).
 """
 from __future__ import annotations
 
@@ -122,6 +128,63 @@ def step_algorithmic_bytes(n_layers: int, resid_format: int = 0) -> int:
     B, Hq, Hkv, K, R, W, N = 4, 12, 2, 32, 128, 1024, 252
     return sum(sum(layer_bytes(B, Hkv, Hq, min(K, N), synth.STACK_RANKS[i], R, W, N, resid_format))
                for i in range(n_layers))
+
+
+def seal_flops(width: int, rank: int, power_iters: int, passes: int = 2) -> int:
+    """Main arithmetic of sealing one (block, KV head), an FMA counted as 2:
+    the 2 + 2q products of A (255 x 256) with a 256 x w or 255 x w factor, the
+    Gram matrices and triangular solves of the (1 + 2q) x passes Cholesky QR
+    steps and the final Gram of B^T, the factors U S and W, and the residual
+    errors.  The Jacobi sweeps (data-dependent count) are not counted."""
+    w, q = width, power_iters
+    products = (2 + 2 * q) * 255 * 256 * w * 2
+    orth = (1 + 2 * q) * passes * (256 * w * w + 256 * w * w)
+    final = 256 * w * w + (255 + 256) * rank * w * 2 + 255 * rank * 128 * 2
+    return products + orth + final
+
+
+def measure_sealing(lib, synth, torch, np, log, repeats: int = 3, power_iters: int = 2):
+    """dkv_seal_blocks over the blocks of one layer of the 64k batch-4 stack
+    (4 sequences x 252 blocks x 2 KV heads, R = 128) at each of the stack's
+    ranks, test-matrix width r + 8; timed with events, checked repeat-equal."""
+    dev = torch.device("cuda:0")
+    nb, H, R = 4 * 252, 2, 128
+    inp = synth.make_seal_input(3000, nb, H, width=max(synth.STACK_RANKS) + 8)
+    k = torch.from_numpy(inp.k).to(dev)
+    v = torch.from_numpy(inp.v).to(dev)
+    slots = torch.arange(nb, dtype=torch.int32, device=dev)
+    out = []
+    for rank in sorted(set(synth.STACK_RANKS)):
+        w = rank + 8
+        om = torch.from_numpy(np.ascontiguousarray(inp.omega[:, :w])).to(dev)
+        pool = lib.Pool.empty(nb, H, rank, R, dev)
+        lib.seal_blocks(pool, k, v, slots, om, power_iters)
+        torch.cuda.synchronize()
+        ref = pool.tensors["_record"].clone()
+        ts = []
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.seal_blocks(pool, k, v, slots, om, power_iters)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        assert torch.equal(ref, pool.tensors["_record"])
+        ms = float(np.median(ts))
+        items = nb * H
+        in_bytes = items * 2 * 256 * 128 * 2
+        fl = items * seal_flops(w, rank, power_iters)
+        log(f"sealing rank {rank}: {ms:.2f} ms for {items} block-heads ({items / ms * 1e3:.0f} per s), "
+            f"{fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        out.append({"rank": rank, "width": w, "power_iters": power_iters, "block_heads": items,
+                    "ms": ms, "block_heads_per_s": items / (ms * 1e-3),
+                    "input_GBps": in_bytes / (ms * 1e-3) / 1e9, "flops_per_block_head": seal_flops(w, rank, power_iters),
+                    "achieved_TFLOPs": fl / (ms * 1e-3) / 1e12})
+        del pool
+    del k, v
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_quantised(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
@@ -312,6 +375,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-sealing", action="store_true",
+                    help="skip the block-sealing measurement (dkv_seal_blocks, reported beside the decode)")
     ap.add_argument("--quantised", choices=("none", "int8", "int4", "both"), default="both",
                     help="also time the stack with its residual rows in the 8- / 4-bit format "
                          "(layer-batched launch; reported beside the fp16 value)")
@@ -603,6 +668,8 @@ def main() -> int:
         variants = {"int8": ["Q8"], "int4": ["Q4"], "both": ["Q8", "Q4"]}[args.quantised]
         res["quantised_residuals"] = [measure_quantised(lib, synth, torch, np, v, n_layers, args.steps,
                                                         args.warmup, log) for v in variants]
+    if not args.no_sealing and args.mode != "per-layer":
+        res["sealing"] = measure_sealing(lib, synth, torch, np, log)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cpu_sample or {layer_ids[0]: meta}, args.cpu_seconds, log)
     print(json.dumps(res))
