@@ -281,7 +281,7 @@ def pmc_summary(args) -> int:
     for key, path, counter in (("fetch", args.pmc_summary[0], "FETCH_SIZE"),
                                ("write", args.pmc_summary[1], "WRITE_SIZE")):
         vals, names = per_dispatch(path, counter)
-        probe = [v for d, v in vals.items() if "elementwise" in names[d] or "mul" in names[d]]
+        probe = [v for d, v in vals.items() if "MulFunctor" in names[d]]  # the torch.mul copy probe only
         kern = [v for d, v in vals.items() if args.pmc_kernel + "<" in names[d] or
                 names[d].split("(")[0].endswith(args.pmc_kernel)]
         if not probe or not kern:
