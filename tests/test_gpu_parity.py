@@ -515,6 +515,38 @@ def test_decode_layers_stack_matches_oracle(lib):
         say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
 
 
+def test_decode_layers_full_stack_sampled(lib):
+    """The benchmark's launch: all 28 layers of the 64k batch-4 stack in one
+    layer-batched launch.  Every layer routes exactly as its per-layer launch
+    does, two launches give the same bits, and sampled layers (one of each
+    rank) match the oracle."""
+    layers = list(range(28))
+    sampled = {3: None, 12: None, 22: None}
+    say(f"[decode layers] stack64k, all {len(layers)} layers, oracle on layers {sorted(sampled)}")
+    pools, batches = [], []
+    scale = top_k = None
+    for l in layers:
+        w = synth.make_config(2, layers=[l])
+        scale, top_k = w.scale, w.top_k
+        pool, batch = upload(lib, w)
+        lib.gather_route_keys(pool, batch)
+        pools.append(pool)
+        batches.append(batch)
+        if l in sampled:
+            sampled[l] = w
+        del w
+    run = lib.Layers(pools, batches, top_k, scale)
+    res = _run_layers(lib, run, reps=2)
+    assert run.timeout_flag() == 0
+    for l in layers:
+        _, _, i1 = lib.decode(pools[l], batches[l], top_k, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1), l
+    for l, w in sorted(sampled.items()):
+        c = _oracle_check(w, w.layers[0], *res[l], w.top_k)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
 def test_decode_layers_mixed_ranks_and_edges(lib):
     """Layers of every low-rank tile count (ranks 1..64, 0..255 residual rows),
     ragged windows and an empty sequence, in one launch."""

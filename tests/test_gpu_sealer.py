@@ -208,3 +208,22 @@ def test_sealed_blocks_decode_like_the_oracle(lib):
     d_l = np.max(np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref))
     say(f"[seal]   decode max |d out| {d_o:.2e}, max |d lse| {d_l:.2e}")
     assert d_o <= 1e-2 and d_l <= 1e-3
+
+
+def test_seal_full_layer_sampled(lib):
+    # the benchmark's sealing launch: one layer's 1008 blocks x 2 KV heads of
+    # the 64k batch-4 stack at rank 48 (R = 128, q = 2); sampled blocks against
+    # the oracle, every block's anchor and residual rows checked as copies
+    say("[seal] one layer of the 64k stack (2016 block-heads), sampled against the oracle")
+    nb, H, rank, R = 4 * 252, 2, 48, 128
+    inp = synth.make_seal_input(3000, nb, H, width=rank + 8)
+    out, om = _seal_gpu(lib, inp, rank, R, 2)
+    assert np.array_equal(out["anchor_k"], inp.k[:, :, 0]) and np.array_equal(out["anchor_v"], inp.v[:, :, 0])
+    pos = out["resid_pos"].astype(np.int64)
+    assert np.all(np.diff(pos, axis=-1) > 0) and pos.min() >= 1 and pos.max() <= 255
+    rows = np.take_along_axis(inp.k, pos[..., None], axis=2)
+    assert np.array_equal(out["resid_k"], rows)
+    for b in (0, 333, 777, nb - 1):
+        for h in range(H):
+            ref = S.seal_block(inp.k[b, h], inp.v[b, h], rank, R, om, 2)
+            _compare_block(out, b, h, inp.k[b, h], inp.v[b, h], ref, rank, R)
