@@ -233,8 +233,8 @@ dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batc
  * combine (the Zenodo abstract's decode path).  top_k = 0 attends the window
  * only.  Work is handed out in ticket order from a counter in the workspace:
  * the routing of each (sequence, KV head) first, then its blocks (which wait
- * for that routing) and window chunks; the workgroup completing a unit's last
- * part merges it.
+ * for that routing) and window chunks, then one merge per unit (which waits
+ * until the unit's parts are stored) combining the partials of its G rows.
  *   workspace: device memory of >= dkv_decode_workspace_size() bytes, 256-byte
  *              aligned, owned by the caller, whose control area is zero (fresh
  *              zero-filled memory, dkv_decode_workspace_init, or a previous
