@@ -105,20 +105,29 @@ __device__ __forceinline__ void row_product(const f16* xk, const f16* xv, const 
   if (t >= kRows) return;
   const f16* kr = xk + (int64_t)(t + 1) * kD;
   const f16* vr = xv + (int64_t)(t + 1) * kD;
-  for (int c8 = 0; c8 < 2 * kD / 8; ++c8) {
-    const v8h x = *reinterpret_cast<const v8h*>(c8 < kD / 8 ? kr + 8 * c8 : vr + 8 * (c8 - kD / 8));
+  constexpr int kAhead = 4;  // 16-byte chunks of the row loaded together
+  for (int c0 = 0; c0 < 2 * kD / 8; c0 += kAhead) {
+    v8h x[kAhead];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 8 * c8 + e;
-      const float a = (float)x[e] - anc[c];
-      const float4* fr = reinterpret_cast<const float4*>(F + c * SS);
+    for (int q = 0; q < kAhead; ++q) {
+      const int c8 = c0 + q;
+      x[q] = *reinterpret_cast<const v8h*>(c8 < kD / 8 ? kr + 8 * c8 : vr + 8 * (c8 - kD / 8));
+    }
 #pragma unroll
-      for (int j4 = 0; j4 < LP / 4; ++j4) {
-        const float4 f = fr[j4];
-        v[4 * j4 + 0] = fmaf(a, f.x, v[4 * j4 + 0]);
-        v[4 * j4 + 1] = fmaf(a, f.y, v[4 * j4 + 1]);
-        v[4 * j4 + 2] = fmaf(a, f.z, v[4 * j4 + 2]);
-        v[4 * j4 + 3] = fmaf(a, f.w, v[4 * j4 + 3]);
+    for (int q = 0; q < kAhead; ++q) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * (c0 + q) + e;
+        const float a = (float)x[q][e] - anc[c];
+        const float4* fr = reinterpret_cast<const float4*>(F + c * SS);
+#pragma unroll
+        for (int j4 = 0; j4 < LP / 4; ++j4) {
+          const float4 f = fr[j4];
+          v[4 * j4 + 0] = fmaf(a, f.x, v[4 * j4 + 0]);
+          v[4 * j4 + 1] = fmaf(a, f.y, v[4 * j4 + 1]);
+          v[4 * j4 + 2] = fmaf(a, f.z, v[4 * j4 + 2]);
+          v[4 * j4 + 3] = fmaf(a, f.w, v[4 * j4 + 3]);
+        }
       }
     }
   }
@@ -133,16 +142,25 @@ __device__ __forceinline__ void col_product(const f16* xk, const f16* xv, const 
   for (int j = 0; j < LP; ++j) v[j] = 0.f;
   const f16* col = (c < kD ? xk + c : xv + (c - kD)) + kD;  // row 1 of column c
   const float ac = anc[c];
-  for (int t = 0; t < kRows; ++t) {
-    const float a = (float)col[(int64_t)t * kD] - ac;
-    const float4* fr = reinterpret_cast<const float4*>(F + t * SS);
+  constexpr int kAhead = 8;  // rows of the column loaded together
+  for (int t0 = 0; t0 < 256; t0 += kAhead) {
+    float a[kAhead];
 #pragma unroll
-    for (int j4 = 0; j4 < LP / 4; ++j4) {
-      const float4 f = fr[j4];
-      v[4 * j4 + 0] = fmaf(a, f.x, v[4 * j4 + 0]);
-      v[4 * j4 + 1] = fmaf(a, f.y, v[4 * j4 + 1]);
-      v[4 * j4 + 2] = fmaf(a, f.z, v[4 * j4 + 2]);
-      v[4 * j4 + 3] = fmaf(a, f.w, v[4 * j4 + 3]);
+    for (int q = 0; q < kAhead; ++q) {
+      const int t = t0 + q < kRows ? t0 + q : kRows - 1;  // row 256 does not exist: read row 255, weight 0
+      a[q] = t0 + q < kRows ? (float)col[(int64_t)t * kD] - ac : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kAhead; ++q) {
+      const float4* fr = reinterpret_cast<const float4*>(F + (t0 + q) * SS);  // F has 256 rows
+#pragma unroll
+      for (int j4 = 0; j4 < LP / 4; ++j4) {
+        const float4 f = fr[j4];
+        v[4 * j4 + 0] = fmaf(a[q], f.x, v[4 * j4 + 0]);
+        v[4 * j4 + 1] = fmaf(a[q], f.y, v[4 * j4 + 1]);
+        v[4 * j4 + 2] = fmaf(a[q], f.z, v[4 * j4 + 2]);
+        v[4 * j4 + 3] = fmaf(a[q], f.w, v[4 * j4 + 3]);
+      }
     }
   }
 }
@@ -203,9 +221,22 @@ __device__ __forceinline__ void cholesky(float* G, float* inv, int lane) {
       const int i = lane + 64 * r2;
       s[r2] = 0.f;
       if (i >= k && i < LP) {
-        float acc = G[i * SS + k];
-        for (int m = 0; m < k; ++m) acc = fmaf(-G[i * SS + m], G[k * SS + m], acc);
-        s[r2] = acc;
+        // sum over m < k of L[i][m] L[k][m]: 16-byte reads, four partial sums
+        const float* li = G + i * SS;
+        const float* lk = G + k * SS;
+        float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        int m = 0;
+        for (; m + 4 <= k; m += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(li + m);
+          const float4 b = *reinterpret_cast<const float4*>(lk + m);
+          acc4.x = fmaf(a.x, b.x, acc4.x);
+          acc4.y = fmaf(a.y, b.y, acc4.y);
+          acc4.z = fmaf(a.z, b.z, acc4.z);
+          acc4.w = fmaf(a.w, b.w, acc4.w);
+        }
+        float acc = (acc4.x + acc4.y) + (acc4.z + acc4.w);
+        for (; m < k; ++m) acc = fmaf(li[m], lk[m], acc);
+        s[r2] = G[i * SS + k] - acc;
       }
     }
     const float d = __shfl(k < 64 ? s[0] : s[R2 - 1], k & 63);
