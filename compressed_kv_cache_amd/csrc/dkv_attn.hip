@@ -1574,8 +1574,87 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
 // ----------------------------------------------------------------------------
 
 
-constexpr int kMergeSlots = kAttThreads / 32;  // 32-lane slots of a merge workgroup
-constexpr int kMergeRowChunk = 8;              // partials loaded at once per lane
+// Log-sum-exp combine of one query row's n_parts partials by one workgroup:
+// kMergeSlots slots of 32 lanes (4 columns per lane), slot s taking parts s,
+// s + kMergeSlots, ..., every load of a round issued at once; the row maximum
+// comes first so the slots' weighted sums add without rescaling, in a fixed
+// order.  lds: kMergeSlots * (kD + 1) + kAttWaves floats.
+constexpr int kMergeSlots = kAttThreads / 32;
+constexpr int kMergeRowChunk = 8;  // parts per slot per round
+__device__ __forceinline__ void merge_row(const float* part_o, const float* part_lse, int n_parts, int row,
+                                          f16* out, float* out_lse, float* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c4 = tid & 31, sl = tid >> 5;
+  float* red = lds;                           // [kMergeSlots][kD]
+  float* redS = lds + kMergeSlots * kD;       // [kMergeSlots]
+  float* redM = redS + kMergeSlots;           // [kAttWaves]
+  const int np = n_parts > 0 ? n_parts : 1;
+  const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row * n_parts * kD, (uint32_t)n_parts * kD * 4);
+  const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row * n_parts, (uint32_t)n_parts * 4);
+  // first round's partials, then the row maximum over every part
+  float4 o[kMergeRowChunk];
+  float l[kMergeRowChunk];
+#pragma unroll
+  for (int k = 0; k < kMergeRowChunk; ++k) {
+    const int pp = sl + kMergeSlots * k;
+    const int pc = pp < np ? pp : np - 1;
+    o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
+    l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
+  }
+  float m = -INFINITY;
+  for (int pp = tid; pp < n_parts; pp += kAttThreads) m = fmaxf(m, ld_coherent(Lb, (uint32_t)pp * 4u));
+  m = wave_minmax<true>(m);
+  if (lane == 0) redM[wave] = m;
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < kAttWaves; ++w) m = fmaxf(m, redM[w]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float S = 0.f;
+  for (int p0 = 0; p0 < n_parts; p0 += kMergeSlots * kMergeRowChunk) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int k = 0; k < kMergeRowChunk; ++k) {
+        const int pp = p0 + sl + kMergeSlots * k;
+        const int pc = pp < np ? pp : np - 1;
+        o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
+        l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeRowChunk; ++k) {
+      const int pp = p0 + sl + kMergeSlots * k;
+      const float w = (pp < n_parts && l[k] != -INFINITY) ? __expf(l[k] - m) : 0.f;
+      S += w;
+      acc.x += w * o[k].x;
+      acc.y += w * o[k].y;
+      acc.z += w * o[k].z;
+      acc.w += w * o[k].w;
+    }
+  }
+  *reinterpret_cast<float4*>(red + sl * kD + 4 * c4) = acc;
+  if (c4 == 0) redS[sl] = S;
+  lds_barrier();
+  if (tid < 32) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float St = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMergeSlots; ++s2) {
+      const float4 v = *reinterpret_cast<const float4*>(red + s2 * kD + 4 * c4);
+      t.x += v.x;
+      t.y += v.y;
+      t.z += v.z;
+      t.w += v.w;
+      St += redS[s2];
+    }
+    const bool any = St > 0.f;
+    v4h h4;
+    h4[0] = (f16)(any ? t.x / St : 0.f);
+    h4[1] = (f16)(any ? t.y / St : 0.f);
+    h4[2] = (f16)(any ? t.z / St : 0.f);
+    h4[3] = (f16)(any ? t.w / St : 0.f);
+    *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * c4) = h4;
+    if (tid == 0) out_lse[row] = any ? m + __logf(St) : -INFINITY;
+  }
+}
 
 // Log-sum-exp combine of the partials of one unit's G query rows (rows row0 ..
 // row0 + G - 1) by one workgroup: each 32-lane slot takes a row (slot s: rows
@@ -1654,7 +1733,8 @@ struct DecodeArgs {
   int n_units;
   int n_route;           // units routed in this launch (0 when top_k == 0)
   int n_part_end;        // n_route + n_units * att.items_per_unit: first merge item
-  int n_items;           // n_part_end + n_units merge items (one per unit): the grid size
+  int merges;            // merge items per unit: G (one per query row) or 1 (one per unit)
+  int n_items;           // n_part_end + n_units * merges: the grid size
 };
 
 constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
@@ -1664,8 +1744,9 @@ constexpr int kCtrlQueue = 64;                  // first queue counter
 constexpr int kCtrlHeaderBytes = 4096;          // control words: [0..63] misc, then the queue counters
 
 // One work item of a fused decode step: t < n_route routes unit t; then
-// the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merge of
-// unit t - n_part_end.  sh_slot: a shared word of the calling workgroup.
+// the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merges,
+// per query row (u, g) or per unit u.  sh_slot: a shared word of the calling
+// workgroup.
 template <int NRQ, int QK>
 __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& Bt, const DecodeArgs& D, int t,
                                             unsigned char* smem, RouteShared<kAttWaves>& rsh, int32_t& sh_slot) {
@@ -1705,8 +1786,10 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     __syncthreads();
     if (tid == 0) atomicAdd(&D.unit_done[u], 1u);
   } else if (t < D.n_items) {
-    // merge item: the G query rows of a unit, once all of the unit's parts are stored
-    const int u = t - D.n_part_end;
+    // merge item: one query row of a unit, or all G of them, once all of the
+    // unit's parts are stored
+    const int it = t - D.n_part_end;
+    const int u = it / D.merges, g = it % D.merges;
     if (tid == 0) {
       const uint32_t want = (uint32_t)D.att.items_per_unit;
       unsigned n = 0;
@@ -1720,7 +1803,11 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     }
     lds_barrier();
     const int b = u / Bt.Hkv, h = u % Bt.Hkv;
-    merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse);
+    if (D.merges == 1)
+      merge_unit(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G, Bt.G, D.out, D.out_lse);
+    else
+      merge_row(D.att.part_o, D.att.part_lse, D.att.n_parts, b * Bt.Hq + h * Bt.G + g, D.out, D.out_lse,
+                reinterpret_cast<float*>(smem));
   }
 }
 
@@ -1740,7 +1827,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
   // running workgroup.
   if (tid == 0) {
     const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
-    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = 1;  // one merge per unit
+    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = D.merges;
     uint32_t item = 0xFFFFFFFFu;
     for (int k = 0; k < kQueues && item == 0xFFFFFFFFu; ++k) {
       const int x = (x0 + k) & (kQueues - 1);
@@ -2232,7 +2319,7 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
                              uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
-                             bool fold = true) {
+                             bool fold = true, bool row_merges = true) {
   const WsLayout w = decode_layout(pool, batch, top_k, fold);
   // folded, each routed-block part also takes its share of the window;
   // otherwise the window comes in chunks of kWinChunk rows
@@ -2264,7 +2351,11 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   D.n_units = units;
   D.n_route = top_k > 0 ? units : 0;
   const int64_t part_end = (int64_t)D.n_route + (int64_t)units * n_parts;
-  const int64_t items = part_end + (int64_t)units;  // one merge per unit
+  // row_merges (one launch per layer, whose merges end the launch): a merge
+  // workgroup per query row; otherwise (several layers in one launch, where
+  // merges overlap other layers' parts) one per unit
+  D.merges = row_merges ? batch->n_q_heads / pool->n_kv_heads : 1;
+  const int64_t items = part_end + (int64_t)units * D.merges;
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
   D.n_part_end = (int)part_end;
   D.n_items = (int)items;
@@ -2576,7 +2667,8 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     if (top_k > 0 && b0.batch > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) break;
     size_t shm_l = 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
-                               out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow)))
+                               out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
+                               /*row_merges=*/false)))
       break;
     host[l].P = make_pool_args(pool);
     host[l].Bt = make_batch_args(pool, batch);
