@@ -50,7 +50,7 @@ namespace {
 constexpr int kD = 128;            // head dim
 constexpr int kLowRankRows = 255;  // tokens 1..255 of a block
 constexpr int kVStride = 132;      // LDS row stride (halves) of 128-wide tiles: conflict-free column reads
-constexpr int kWinChunk = 256;     // window rows per window part (when the window has parts of its own)
+constexpr int kWinChunk = 512;     // window rows per window part (when the window has parts of its own)
 
 thread_local char g_err[512] = "";
 
