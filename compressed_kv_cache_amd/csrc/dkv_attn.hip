@@ -1894,9 +1894,11 @@ struct LayersArgs {
 // the routings of every layer, then the window parts of every layer (they wait
 // on nothing, and run while the routings finish), then the routed-block parts
 // of layer 0, 1, ..., with the merges of layer l placed after the block parts
-// of layer l + kMergeLag, when its parts are most likely done.  Every wait is
-// on an item earlier in the same queue.  Uniform (scalar) arithmetic.
-constexpr int kMergeLag = 2;
+// of layer l + kMergeLag (as measured, no lag beats placing every merge after
+// all block parts: the merges then never wait, and fill the launch's tail).
+// Every wait is on an item earlier in the same queue.  Uniform (scalar)
+// arithmetic.
+constexpr int kMergeLag = 1 << 16;
 
 __device__ __forceinline__ void layers_item(int i, int x, int nx, const LayersArgs& L, int& layer, int& item) {
   const int NL = L.n_layers, NP = L.block_parts, NW = L.win_parts, G = L.group;
