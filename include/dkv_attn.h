@@ -233,8 +233,9 @@ dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batc
  * combine (the Zenodo abstract's decode path).  top_k = 0 attends the window
  * only.  Work is handed out in ticket order from a counter in the workspace:
  * the routing of each (sequence, KV head) first, then its blocks (which wait
- * for that routing) and window chunks, then one merge per unit (which waits
- * until the unit's parts are stored) combining the partials of its G rows.
+ * for that routing) and window chunks, then one merge per query row (which
+ * waits until its unit's parts are stored), so that the G rows of a unit are
+ * combined by G workgroups at once.
  *   workspace: device memory of >= dkv_decode_workspace_size() bytes, 256-byte
  *              aligned, owned by the caller, whose control area is zero (fresh
  *              zero-filled memory, dkv_decode_workspace_init, or a previous
@@ -269,6 +270,8 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
  * calls; the window rows are split into parts of their own (rather than shared
  * out over the routed-block parts), so outputs equal dkv_decode's up to the
  * rounding of that other split, and repeat bit for bit from launch to launch.
+ * Each unit's G query rows are combined by one merge item (the merges of the
+ * other layers keep the chip busy), so plan->group is 1.
  *
  * dkv_decode_layers_prepare (once; synchronous, not capturable in a graph)
  * validates every layer, writes the per-layer argument table into `table`
@@ -288,7 +291,7 @@ typedef struct dkv_layers_plan {
   int32_t routes;         /* routing items per unit (0 or 1) */
   int32_t parts;          /* routed-block parts per unit */
   int32_t win_parts;      /* window parts per unit */
-  int32_t group;          /* merges per unit */
+  int32_t group;          /* merge items per unit (1: one per unit) */
   int32_t n_items;        /* work items of one launch */
   int32_t lds_bytes;      /* dynamic LDS per workgroup */
   int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */

@@ -104,7 +104,8 @@ def check_outputs(out, lse, ref_out, ref_lse, tol_out: float = TOL_OUT,
     if not np.all(np.isfinite(o)):
         return OutCheck(False, np.inf, np.inf, np.inf, "non-finite output")
     same_inf = (l == rl) & ~np.isfinite(rl)
-    dl = np.where(same_inf, 0.0, np.abs(l - rl))
+    with np.errstate(invalid="ignore"):        # -inf - -inf is masked by same_inf
+        dl = np.where(same_inf, 0.0, np.abs(l - rl))
     dl = np.where(np.isnan(dl), np.inf, dl)
     mo = float(np.abs(o - r).max()) if o.size else 0.0
     ml = float(dl.max()) if dl.size else 0.0

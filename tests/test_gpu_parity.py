@@ -570,6 +570,31 @@ def test_decode_layers_mixed_ranks_and_edges(lib):
         _oracle_check(w, w.layers[0], *res[l], 3)
 
 
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (10, 2), (16, 1)])
+def test_decode_layers_query_groups(lib, hq, hkv):
+    """One merge per unit combines G = 1, 5 and 16 query rows (16 takes two
+    passes of the eight 32-lane slots), in a two-layer launch."""
+    base = dict(batch=3, n_q_heads=hq, n_kv_heads=hkv, window=40, n_blocks=[4, 6, 2], win_len=[40, 7, 33],
+                top_k=3, sigma0=2.0)
+    wls = [synth.make_workload(f"group{hq // hkv}_{i}", seed=700 + 10 * i + hq, **base, ranks=[r], n_resid=n)
+           for i, (r, n) in enumerate(((20, 16), (33, 40)))]
+    say(f"[decode layers] G = {hq // hkv}")
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, 3, wls[0].scale)
+    res = _run_layers(lib, run, reps=2)
+    assert run.timeout_flag() == 0
+    for l, w in enumerate(wls):
+        _, _, i1 = lib.decode(pools[l], batches[l], 3, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        c = _oracle_check(w, w.layers[0], *res[l], 3)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
 def test_decode_layers_window_only(lib):
     base = dict(batch=3, n_q_heads=8, n_kv_heads=2, window=300, n_blocks=[2, 1, 2],
                 win_len=[300, 129, 1], top_k=0, ranks=[8], n_resid=4)
