@@ -74,6 +74,9 @@ class Layer:
     resid_format: int = RESID_FP16
     resid_k_sb: Optional[np.ndarray] = None
     resid_v_sb: Optional[np.ndarray] = None
+    # un-rotated pools: the rotary base and each slot's absolute position
+    rope_base: Optional[float] = None
+    slot_pos: Optional[np.ndarray] = None
 
     def pool(self) -> dict:
         """The block-store arrays as a plain dict (the oracle's input form)."""
@@ -83,6 +86,9 @@ class Layer:
             d["resid_format"] = self.resid_format
             d["resid_k_sb"] = self.resid_k_sb
             d["resid_v_sb"] = self.resid_v_sb
+        if self.rope_base is not None:
+            d["rope_base"] = self.rope_base
+            d["slot_pos"] = self.slot_pos
         return d
 
 
@@ -245,8 +251,14 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
                   permute_slots: bool = False, zero_anchor: bool = False,
                   win_len: Optional[Sequence[int]] = None, max_blocks: Optional[int] = None,
                   head_dim: int = HEAD_DIM, only_layers: Optional[Sequence[int]] = None,
-                  notes: str = "", resid_format: int = RESID_FP16) -> Workload:
+                  notes: str = "", resid_format: int = RESID_FP16,
+                  rope_base: Optional[float] = None) -> Workload:
     """Generic seeded workload: one Layer per entry of `ranks`.
+
+    With `rope_base`, every layer's pool is an un-rotated one: its keys are
+    read as pre-rotation keys, and slot_pos holds the absolute position of
+    token 0 of each slot's block, BLOCK_SIZE times its logical index (the
+    arrays drawn are the same either way).
 
     Sequence b owns n_blocks[b] logical blocks; their pool slots are
     consecutive (b-major) or a seeded permutation of all slots.  Every layer
@@ -279,10 +291,26 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
                                  n_resid=n_resid, sigma0=sigma0, decay=decay,
                                  zero_anchor=zero_anchor, head_dim=head_dim,
                                  resid_format=resid_format))
-    return Workload(name=name, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
-                    head_dim=head_dim, window=window, n_resid=n_resid, top_k=top_k,
-                    scale=float(1.0 / np.sqrt(head_dim)), block_table=table, n_blocks=nb,
-                    win_len=wl, layers=layers, seed=seed, notes=notes)
+    out = Workload(name=name, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
+                   head_dim=head_dim, window=window, n_resid=n_resid, top_k=top_k,
+                   scale=float(1.0 / np.sqrt(head_dim)), block_table=table, n_blocks=nb,
+                   win_len=wl, layers=layers, seed=seed, notes=notes)
+    if rope_base is not None:
+        set_unrotated(out, rope_base)
+    return out
+
+
+def set_unrotated(wl: Workload, rope_base: float) -> Workload:
+    """Read the workload's pools as un-rotated ones: record the rotary base and
+    each slot's absolute position (BLOCK_SIZE times its logical block index)."""
+    pos = np.zeros(max(wl.n_slots, 1), dtype=np.int32)
+    for b in range(wl.batch):
+        nb = int(wl.n_blocks[b])
+        pos[wl.block_table[b, :nb]] = BLOCK_SIZE * np.arange(nb, dtype=np.int32)
+    for lay in wl.layers:
+        lay.rope_base = float(rope_base)
+        lay.slot_pos = pos
+    return wl
 
 
 def plant_outlier_rows(wl: Workload, logical_block: int, n_rows: int = 8, rms: float = 4.0,
@@ -316,6 +344,9 @@ CONFIG_NAMES = {
     4: "llama3-8b_layer_ctx128k_b8",
 }
 
+# Rotary base of the un-rotated variants (the Qwen2.5 models' value).
+ROPE_BASE = 1_000_000.0
+
 # Layer-adaptive rank of the 28-layer stack: 0.75r early, 1.5r mid, 0.5r late (r = 32).
 STACK_RANKS = [24] * 9 + [48] * 10 + [16] * 9
 
@@ -332,8 +363,13 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
     28-layer stack (config 2) to bound host memory; `variant` is one of
     "", "S1" (sigma_j = 4 * 0.9^j) or "S2" (zero anchors) for config 0, or
     "Q8" / "Q4" (residual rows in the 8- or 4-bit group-quantised format) for
-    configs 0, 1 and 2."""
+    configs 0, 1 and 2, or "U" (the same arrays read as an un-rotated pool with
+    rotary base ROPE_BASE) for any configuration."""
     seed = 1000 + cfg if seed is None else seed
+    if variant == "U":
+        wl = make_config(cfg, seed, layers)
+        wl.name += "_U"
+        return set_unrotated(wl, ROPE_BASE)
     if variant in ("Q8", "Q4"):
         fmt = RESID_INT8 if variant == "Q8" else RESID_INT4
         base = {0: dict(batch=1, n_q_heads=1, n_kv_heads=1, window=512, n_blocks=[14], ranks=[32],

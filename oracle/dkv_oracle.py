@@ -34,6 +34,14 @@ What it computes (sources are the pages on DKV, cited by title and section):
   4 bits, with a half-precision scale and bias per group; the decode attends
   the dequantised rows x = scale * code + bias.
 
+* Un-rotated pools -- README "Key Environment Knobs" (DKV_ROTATED_POOL) and
+  the preset ladder ("keys stored" column): a pool may hold the keys as they
+  were before the rotary position embedding and rotate them to their absolute
+  positions when they are read; values are never rotated, and the query and
+  the dense window arrive rotated as usual.  A pool dict that carries
+  "rope_base" and "slot_pos" (absolute position of token 0 of the block held
+  in each slot) is such a pool.
+
 Readings where the pages are silent (listed in the design notes):
   the anchor is attended as its own row at position 0; the delta is relative to
   the anchor with the singular values folded into U; the LSE is the natural log
@@ -42,7 +50,12 @@ Readings where the pages are silent (listed in the design notes):
   change the order); quantised codes are unsigned (0 .. 2^bits - 1), 4-bit
   codes are packed two per byte with the even dimension in the low nibble (the
   little-endian order of the pages' uint32 words), and each row stores
-  (scale, bias) for dimensions 0..63 then for 64..127.
+  (scale, bias) for dimensions 0..63 then for 64..127; the rotary embedding
+  pairs dimension j with j + d/2 (the half-split pairing of the Qwen and Llama
+  models the pages run) at angular frequency base^(-2j/d); in an un-rotated
+  pool the anchor sits at the block's position, row i at position + i, and a
+  residual row at position + its in-block position, and the routing key is the
+  mean of the 255 reconstructed keys each rotated to its own position.
 
 Every function is plain numpy in float64: inputs are upcast exactly from fp16.
 Pins against things other than this code live in tests/test_oracle_pins.py.
@@ -113,6 +126,30 @@ def route_key(anchor_k, u, vk) -> np.ndarray:
     """Routing key of one block and KV head: c = a_k + mean over the 255 rows of U,
     times V_K.  Shapes: a_k [d], U [255, r], V_K [r, d] -> [d]."""
     return _f64(anchor_k) + _f64(u).mean(axis=0) @ _f64(vk)
+
+
+def rope_theta(base: float, d: int) -> np.ndarray:
+    """Angular frequencies theta_j = base^(-2j/d) of the rotary embedding, j < d/2."""
+    return float(base) ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+
+
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rows x [n, d] rotated to absolute positions pos [n]: each pair
+    (x_j, x_{j+d/2}) is turned by the angle pos * theta_j,
+    x'_j = x_j cos - x_{j+d/2} sin and x'_{j+d/2} = x_{j+d/2} cos + x_j sin."""
+    X = np.atleast_2d(_f64(x))
+    h = X.shape[1] // 2
+    ang = np.asarray(pos, dtype=np.float64).reshape(-1)[:, None] * rope_theta(base, X.shape[1])[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = X[:, :h], X[:, h:]
+    return np.hstack([a * c - b * s, b * c + a * s])
+
+
+def route_key_unrotated(anchor_k, u, vk, block_pos: int, base: float) -> np.ndarray:
+    """Routing key of a block of an un-rotated pool: the mean over positions
+    i = 1..255 of the reconstructed key a_k + U_i V_K rotated to block_pos + i."""
+    K = _f64(anchor_k)[None, :] + _f64(u) @ _f64(vk)
+    return rope(K, int(block_pos) + np.arange(1, BLOCK_SIZE), base).mean(axis=0)
 
 
 def reconstruct_block(anchor_k, anchor_v, u, vk, vv, resid_k, resid_v, resid_pos
@@ -221,6 +258,27 @@ def _slot_entry(pool: Dict[str, np.ndarray], slot: int, h: int) -> Dict[str, np.
     return e
 
 
+def is_unrotated(pool: Dict[str, np.ndarray]) -> bool:
+    return pool.get("rope_base") is not None
+
+
+def block_route_key(pool: Dict[str, np.ndarray], slot: int, h: int) -> np.ndarray:
+    """Routing key of the block in `slot`, KV head h, for either kind of pool."""
+    if is_unrotated(pool):
+        return route_key_unrotated(pool["anchor_k"][slot, h], pool["u"][slot, h], pool["vk"][slot, h],
+                                   int(pool["slot_pos"][slot]), float(pool["rope_base"]))
+    return route_key(pool["anchor_k"][slot, h], pool["u"][slot, h], pool["vk"][slot, h])
+
+
+def block_rows(pool: Dict[str, np.ndarray], slot: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Explicit K, V rows [256, d] of a block as attention sees them: in an
+    un-rotated pool the keys are rotated to their absolute positions."""
+    K, V = reconstruct_block(**_slot_entry(pool, slot, h))
+    if is_unrotated(pool):
+        K = rope(K, int(pool["slot_pos"][slot]) + np.arange(BLOCK_SIZE), float(pool["rope_base"]))
+    return K, V
+
+
 def route_batch(pool, q, block_table, n_blocks, n_kv_heads: int, top_k: int):
     """Routing of every (sequence, KV head).  Returns (idx [B][Hkv][top_k] padded
     with -1, list of per-(b, h) score vectors, list of per-(b, h) key matrices)."""
@@ -231,9 +289,7 @@ def route_batch(pool, q, block_table, n_blocks, n_kv_heads: int, top_k: int):
     for b in range(B):
         for h in range(n_kv_heads):
             nb = int(n_blocks[b])
-            keys = np.stack([route_key(pool["anchor_k"][block_table[b, j], h],
-                                       pool["u"][block_table[b, j], h],
-                                       pool["vk"][block_table[b, j], h]) for j in range(nb)]) \
+            keys = np.stack([block_route_key(pool, int(block_table[b, j]), h) for j in range(nb)]) \
                 if nb else np.zeros((0, q.shape[-1]))
             sel, s = route(q[b, h * G:(h + 1) * G], keys, top_k)
             idx[b, h, :sel.size] = sel
@@ -263,7 +319,7 @@ def decode(pool, q, win_k, win_v, block_table, n_blocks, win_len, n_kv_heads: in
             for j in idx[b, h]:
                 if j < 0:
                     continue
-                K, V = reconstruct_block(**_slot_entry(pool, int(block_table[b, j]), h))
+                K, V = block_rows(pool, int(block_table[b, j]), h)
                 Ks.append(K)
                 Vs.append(V)
             w = int(win_len[b])
@@ -284,8 +340,15 @@ def block_partials(pool, slot: int, h: int, q_group, scale: float):
     and of its residual rows, for the query rows q_group [G, d]."""
     e = _slot_entry(pool, slot, h)
     Klr, Vlr = lowrank_rows(e["anchor_k"], e["anchor_v"], e["u"], e["vk"], e["vv"], e["resid_pos"])
+    Kex = e["resid_k"]
+    if is_unrotated(pool):
+        base, p0 = float(pool["rope_base"]), int(pool["slot_pos"][slot])
+        keep = np.ones(BLOCK_SIZE, dtype=bool)
+        keep[np.asarray(e["resid_pos"], dtype=np.int64)] = False
+        Klr = rope(Klr, p0 + np.flatnonzero(keep), base)
+        Kex = rope(Kex, p0 + np.asarray(e["resid_pos"], dtype=np.int64), base)
     lr = attend(q_group, Klr, Vlr, scale)
-    ex = attend(q_group, e["resid_k"], e["resid_v"], scale)
+    ex = attend(q_group, Kex, e["resid_v"], scale)
     return lr, ex
 
 
