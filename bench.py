@@ -30,7 +30,9 @@ replay).  `traffic` is the committed rocprofv3 PMC summary for that kernel
 (`--pmc-summary` writes it), null when the kernel source changed since.
 
 Beside the decode (not part of `value`): the same stack with its residual rows
-in the 8- and 4-bit formats (`quantised_residuals`), and the write side,
+in the 8- and 4-bit formats (`quantised_residuals`), the same stack read as
+un-rotated pools whose keys are rotated to their absolute positions at read
+(`unrotated_pool`), and the write side,
 dkv_seal_blocks sealing one layer's 1008 blocks x 2 KV heads at each of the
 stack's ranks (`sealing`: block-heads per second and the fp32 arithmetic rate
 of its main products).
@@ -187,10 +189,12 @@ def measure_sealing(lib, synth, torch, np, log, repeats: int = 3, power_iters: i
     return out
 
 
-def measure_quantised(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
+def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
     """The same 64k batch-4 stack with its residual rows stored in the 8- or
-    4-bit group-quantised format (variant "Q8" / "Q4"): one layer-batched launch
-    per step, timed eagerly with events and as a graph replay."""
+    4-bit group-quantised format (variant "Q8" / "Q4"), or read as un-rotated
+    pools whose keys are rotated to their positions at read (variant "U"): one
+    layer-batched launch per step, timed eagerly with events and as a graph
+    replay."""
     dev = torch.device("cuda:0")
     pools, batches = [], []
     for li in range(n_layers):
@@ -240,11 +244,12 @@ def measure_quantised(lib, synth, torch, np, variant: str, n_layers: int, steps:
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
-    fmt = 1 if variant == "Q8" else 2
+    fmt = {"Q8": 1, "Q4": 2, "U": 0}[variant]
     alg = step_algorithmic_bytes(n_layers, fmt)
-    log(f"{variant} residuals, layer-batched: {ms:.4f} ms/step (graph); kernel {kern * 1e3:.1f} us; "
+    log(f"{variant} variant, layer-batched: {ms:.4f} ms/step (graph); kernel {kern * 1e3:.1f} us; "
         f"{alg / 1e6:.1f} MB per step")
-    res = {"resid_format": {"Q8": "int8", "Q4": "int4"}[variant], "ms_per_step": ms,
+    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16"}[variant],
+           "keys": "unrotated, rotated at read" if variant == "U" else "rotated", "ms_per_step": ms,
            "queries_per_s": 4 * n_layers / (ms * 1e-3), "algorithmic_bytes_per_step": alg,
            "kernel_us_per_launch": kern * 1e3, "achieved_GBps": alg / (kern * 1e-3) / 1e9}
     del run, pools, batches
@@ -375,6 +380,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-unrotated", action="store_true",
+                    help="skip the stack read as un-rotated pools (keys rotated at read)")
     ap.add_argument("--no-sealing", action="store_true",
                     help="skip the block-sealing measurement (dkv_seal_blocks, reported beside the decode)")
     ap.add_argument("--quantised", choices=("none", "int8", "int4", "both"), default="both",
@@ -666,8 +673,11 @@ def main() -> int:
     if args.quantised != "none" and args.mode != "per-layer":
         # free the fp16 stack first: the quantised stacks are built the same way
         variants = {"int8": ["Q8"], "int4": ["Q4"], "both": ["Q8", "Q4"]}[args.quantised]
-        res["quantised_residuals"] = [measure_quantised(lib, synth, torch, np, v, n_layers, args.steps,
-                                                        args.warmup, log) for v in variants]
+        res["quantised_residuals"] = [measure_variant(lib, synth, torch, np, v, n_layers, args.steps,
+                                                      args.warmup, log) for v in variants]
+    if not args.no_unrotated and args.mode != "per-layer":
+        res["unrotated_pool"] = measure_variant(lib, synth, torch, np, "U", n_layers, args.steps, args.warmup,
+                                                log)
     if not args.no_sealing and args.mode != "per-layer":
         res["sealing"] = measure_sealing(lib, synth, torch, np, log)
     if not args.no_cpu_baseline:

@@ -82,6 +82,10 @@ struct PoolArgs {
   const uint8_t* rvq; int64_t rvq_s, rvq_h;
   const f16* rks; int64_t rks_s, rks_h;       // (scale, bias) per 64-dimension group [R][2][2]
   const f16* rvs; int64_t rvs_s, rvs_h;
+  // un-rotated pools: theta_j / (2 pi) as hi[64] then lo[64], and each slot's
+  // absolute position; rope == nullptr for pools of rotated keys
+  const float* rope;
+  const int32_t* spos;
 };
 
 struct BatchArgs {
@@ -308,6 +312,61 @@ __global__ __launch_bounds__(128) void k_route_keys(PoolArgs P, const int32_t* s
   float c = 0.f;
   for (int j = 0; j < r; ++j) c += ubar[j] * (float)VK[j * kD + t];
   P.key[slot * P.key_s + h * P.key_h + t] = (float)AK[t] + c;
+}
+
+// cos and sin of the rotary angle pos * theta_j, with theta_j / (2 pi) given as
+// the unevaluated sum fh + fl: the product pos * fh is split exactly into
+// a + e (fma), its whole turns dropped from a, and the remaining fraction of a
+// turn fed to the hardware sine and cosine, which take their argument in turns.
+// pos < 2^24 is exact in fp32.
+__device__ __forceinline__ void rope_cs(float pf, float fh, float fl, float& c, float& s) {
+  const float a = pf * fh;
+  const float e = __builtin_fmaf(pf, fh, -a);
+  const float t = __builtin_amdgcn_fractf(a) + __builtin_fmaf(pf, fl, e);
+  c = __builtin_amdgcn_cosf(t);
+  s = __builtin_amdgcn_sinf(t);
+}
+
+// Routing keys of an un-rotated pool: the mean over positions i = 1..255 of
+// the reconstructed key a_k + U_i V_K rotated to slot_pos + i.  One workgroup
+// per (slot, KV head); thread t takes the dimension pair (j, j + 64) with
+// j = t % 64 and the positions of one half of the block, in fp32.
+__global__ __launch_bounds__(128) void k_route_keys_rot(PoolArgs P, const int32_t* slots) {
+  const int item = blockIdx.x;
+  const int si = item / P.n_kv, h = item % P.n_kv;
+  const int slot = slots ? slots[si] : si;
+  if (slot < 0 || slot >= P.n_slots) return;
+  __shared__ float part[2][kD];
+  __shared__ float vks[DKV_MAX_RANK * kD];
+  const int r = P.rank;
+  const int t = threadIdx.x, j = t & 63, half = t >> 6;
+  const f16* U = P.u + slot * P.u_s + h * P.u_h;
+  const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
+  const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
+  for (int c = 0; c < r; ++c) vks[c * kD + t] = (float)VK[c * kD + t];
+  lds_barrier();
+  const float a0 = (float)AK[j], a1 = (float)AK[j + 64];
+  const float fh = P.rope[j], fl = P.rope[64 + j];
+  const int p0 = P.spos[slot];
+  float s0 = 0.f, s1 = 0.f;
+  const int i_lo = half == 0 ? 1 : 128, i_hi = half == 0 ? 128 : 256;
+  for (int i = i_lo; i < i_hi; ++i) {
+    const f16* Ui = U + (int64_t)(i - 1) * r;
+    float x = a0, y = a1;
+    for (int c = 0; c < r; ++c) {
+      const float uc = (float)Ui[c];
+      x = __builtin_fmaf(uc, vks[c * kD + j], x);
+      y = __builtin_fmaf(uc, vks[c * kD + j + 64], y);
+    }
+    float cs, sn;
+    rope_cs((float)(p0 + i), fh, fl, cs, sn);
+    s0 += x * cs - y * sn;
+    s1 += y * cs + x * sn;
+  }
+  part[half][j] = s0;
+  part[half][j + 64] = s1;
+  lds_barrier();
+  P.key[slot * P.key_s + h * P.key_h + t] = (part[0][t] + part[1][t]) / (float)kLowRankRows;
 }
 
 // Per-sequence routing-key table: one thread per 16 bytes of out.
@@ -733,15 +792,23 @@ struct NoNext {
   __device__ __forceinline__ void operator()() const {}
 };
 
+// scores of the tiles as stored (which: 0 for tile a, 1 for tile b)
+struct PlainScore {
+  const v4h (&qf)[4][2];
+  __device__ __forceinline__ v4f operator()(const v8h (&kx)[4], int) const { return exact_scores(kx, qf); }
+};
+
 // next(): issued once the pair's K and V registers are consumed (V staged in
 // LDS), to load the following pair into them while this one finishes.
-template <int NQ, class Next = NoNext>
-__device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h (&ka)[4], const v8h (&va)[4],
-                                           const v8h (&kb)[4], const v8h (&vb)[4], int rows_a, int rows_b,
-                                           bool has_b, const v4h (&qf)[4][2], float scale, f16* Va, f16* Vb,
-                                           int l16, int q4, Next&& next = Next()) {
-  const v4f Sa = exact_scores(ka, qf);
-  const v4f Sb = exact_scores(kb, qf);
+// score(kx, which): the tile's scores, exact_scores of the rows as stored
+// unless the rows are rotated first.
+template <int NQ, class Next, class Score>
+__device__ __forceinline__ void exact_pair_scored(ExState& st, v4f (&Wt)[NQ], const v8h (&ka)[4],
+                                                  const v8h (&va)[4], const v8h (&kb)[4], const v8h (&vb)[4],
+                                                  int rows_a, int rows_b, bool has_b, float scale, f16* Va, f16* Vb,
+                                                  int l16, int q4, Next&& next, Score&& score) {
+  const v4f Sa = score(ka, 0);
+  const v4f Sb = score(kb, 1);
   float za[4], zb[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -781,6 +848,15 @@ __device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h
   exact_pv(st, Va, pa, l16, q4);
   if (has_b) exact_pv(st, Vb, pb, l16, q4);
   wave_sync_lds();
+}
+
+template <int NQ, class Next = NoNext>
+__device__ __forceinline__ void exact_pair(ExState& st, v4f (&Wt)[NQ], const v8h (&ka)[4], const v8h (&va)[4],
+                                           const v8h (&kb)[4], const v8h (&vb)[4], int rows_a, int rows_b,
+                                           bool has_b, const v4h (&qf)[4][2], float scale, f16* Va, f16* Vb,
+                                           int l16, int q4, Next&& next = Next()) {
+  exact_pair_scored<NQ>(st, Wt, ka, va, kb, vb, rows_a, rows_b, has_b, scale, Va, Vb, l16, q4,
+                        static_cast<Next&&>(next), PlainScore{qf});
 }
 
 __device__ __forceinline__ void load_exact_tile(const f16* kb, const f16* vb, int tile, int ntile, int n_ex,
@@ -1085,10 +1161,12 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   const f16* exks = nullptr;
   const f16* exvs = nullptr;
   int slot = -1;
+  int bpos = 0;  // un-rotated pools: absolute position of the block's token 0
   if (p < A.n_block_parts) {
     slot = get_slot();  // routed pool slot, or -1
     if (slot >= P.n_slots) slot = -1;
     if (slot >= 0) {
+      if constexpr (QK == 2) bpos = P.spos[slot];
       lr = (A.block_mode & 1) != 0;
       if ((A.block_mode & 2) && P.n_resid > 0) {
         n_ex = P.n_resid;
@@ -1131,8 +1209,17 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   auto body = [&](auto lr_tag, auto bits_tag) {
   constexpr bool LR = decltype(lr_tag)::value && NRQ > 0;
   constexpr int QB = decltype(bits_tag)::value;  // 0: fp16 exact rows; 8 / 4: quantised residual rows
+  // QK == 2: an un-rotated pool, whose block keys are rotated to their
+  // absolute positions here; the frequency table sits in the statistics area
+  // until the final phase
+  constexpr bool ROT = QK == 2;
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
+  float* fq = wstat;  // ROT: theta_j / (2 pi) as hi[64], lo[64]
+  if constexpr (ROT) {
+    if (tid < 128) fq[tid] = P.rope[tid];
+    if constexpr (!LR) lds_barrier();
+  }
 
   // ---- issue the loads, in the order of use
   v4h ua[kLRTilesPerWave][NQ];
@@ -1159,13 +1246,16 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       }
     }
     // VVx rows: V_V rows j < r, a_v at j = r.  Padding rows j > r read V_V row 0:
-    // their weight in (p^T Ux) is exactly 0 because Ux is zero there.
+    // their weight in (p^T Ux) is exactly 0 because Ux is zero there.  (An
+    // un-rotated pool loads them once its scores are formed.)
+    if constexpr (!ROT) {
 #pragma unroll
-    for (int k = 0; k < kVVChunks; ++k) {
-      const int c = tid + kAttThreads * k;
-      const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
-      const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
-      vvl[k] = ld8(src + col);
+      for (int k = 0; k < kVVChunks; ++k) {
+        const int c = tid + kAttThreads * k;
+        const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
+        const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
+        vvl[k] = ld8(src + col);
+      }
     }
     // VKx rows: V_K rows j < r, a_k at j = r; padding rows read V_K row 0
     // (they only meet zero columns of Ux)
@@ -1226,37 +1316,56 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (ps[k] >= 1 && ps[k] <= kLowRankRows) atomicOr(&wmask[ps[k] >> 5], 1u << (ps[k] & 31));
+    if constexpr (!ROT) {
 #pragma unroll
-    for (int k = 0; k < kVVChunks; ++k) {
-      const int c = tid + kAttThreads * k;
-      if (c < RQ * 16) {
-        const int j = c >> 4, col = (c & 15) * 8;
-        *reinterpret_cast<v4h*>(vvx + j * kVStride + col) = lo4(vvl[k]);
-        *reinterpret_cast<v4h*>(vvx + j * kVStride + col + 4) = hi4(vvl[k]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int jt = wave + kAttWaves * k;
-      if (jt < NRQ) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          acc = mfma16(lo4(vkx[k][s]), qf[s][0], acc);
-          acc = mfma16(hi4(vkx[k][s]), qf[s][1], acc);
+      for (int k = 0; k < kVVChunks; ++k) {
+        const int c = tid + kAttThreads * k;
+        if (c < RQ * 16) {
+          const int j = c >> 4, col = (c & 15) * 8;
+          *reinterpret_cast<v4h*>(vvx + j * kVStride + col) = lo4(vvl[k]);
+          *reinterpret_cast<v4h*>(vvx + j * kVStride + col + 4) = hi4(vvl[k]);
         }
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qt[l16 * RQ + jt * 16 + 4 * q4 + e] = acc[e];
+      for (int k = 0; k < 2; ++k) {
+        const int jt = wave + kAttWaves * k;
+        if (jt < NRQ) {
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            acc = mfma16(lo4(vkx[k][s]), qf[s][0], acc);
+            acc = mfma16(hi4(vkx[k][s]), qf[s][1], acc);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qt[l16 * RQ + jt * 16 + 4 * q4 + e] = acc[e];
+        }
+      }
+    } else {
+      // VKx^T [d][j] (rows of RQ + 4 halves) over the V_K q and VVx areas,
+      // which it fits for RQ >= 16; VVx is staged after the scores
+      f16* vkt = reinterpret_cast<f16*>(qt);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int jt = wave + kAttWaves * k;
+        if (jt < NRQ) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) vkt[(32 * s + 8 * q4 + jj) * (RQ + 4) + jt * 16 + l16] = vkx[k][s][jj];
+          }
+        }
       }
     }
-    lds_barrier();  // V_K q and VVx complete (uniform: lr is uniform)
+    lds_barrier();  // V_K q (or VKx^T) and VVx complete (uniform: lr is uniform)
 
     // ---- the wave's four 16-position tiles as one softmax step (position 0 is the anchor)
     v4h qth[NQ], qtl[NQ];
+    if constexpr (!ROT) {
 #pragma unroll
-    for (int s = 0; s < NQ; ++s) {
-      const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
-      split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
+      for (int s = 0; s < NQ; ++s) {
+        const float4 x = *reinterpret_cast<const float4*>(qt + l16 * RQ + 16 * s + 4 * q4);
+        split_hl(x.x, x.y, x.z, x.w, qth[s], qtl[s]);
+      }
     }
     f16* T = reinterpret_cast<f16*>(my);  // Ux^T [RQ][kTTStride]: column j of the wave's 64 positions
     float zz[kLRTilesPerWave][4];
@@ -1289,10 +1398,57 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         for (int e = 0; e < 4; ++e) T[(16 * s + 4 * q4 + e) * kTTStride + k * 16 + l16] = ua[k][s][e];
       }
       v4f z = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!ROT) {
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) {
-        z = mfma16(ua[k][s], qth[s], z);
-        z = mfma16(ua[k][s], qtl[s], z);
+        for (int s = 0; s < NQ; ++s) {
+          z = mfma16(ua[k][s], qth[s], z);
+          z = mfma16(ua[k][s], qtl[s], z);
+        }
+      } else {
+        // the 16 keys themselves, K^T = VKx^T Ux^T in fp32: kt[2 s + hh] holds
+        // dimensions 32 s + 8 q4 + 4 hh + e of position i0 + l16 (the order of
+        // the query fragments), rotated in fp32 and split into fp16 hi + lo
+        // Two halves: dimension groups s = hf and s = hf + 2 (the rotation's
+        // pairs), m = 2 (s >> 1) + hh.
+        const f16* vkt = reinterpret_cast<const f16*>(qt);
+        const float pf = (float)(bpos + i);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          v4f kt[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) kt[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int dim = 32 * (hf + 2 * (m >> 1)) + 8 * (l16 >> 2) + 4 * (m & 1) + (l16 & 3);
+              const v4h a = *reinterpret_cast<const v4h*>(vkt + dim * (RQ + 4) + 16 * t + 4 * q4);
+              kt[m] = mfma16(a, ua[k][t], kt[m]);
+            }
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int f0 = 32 * hf + 8 * q4 + 4 * hh;
+            const float4 fh = *reinterpret_cast<const float4*>(fq + f0);
+            const float4 fl = *reinterpret_cast<const float4*>(fq + 64 + f0);
+            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, fls[4] = {fl.x, fl.y, fl.z, fl.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float cs, sn;
+              rope_cs(pf, fhs[e], fls[e], cs, sn);
+              const float x = kt[hh][e], y = kt[2 + hh][e];
+              kt[hh][e] = x * cs - y * sn;
+              kt[2 + hh][e] = y * cs + x * sn;
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v4h kh, kl;
+            split_hl(kt[m][0], kt[m][1], kt[m][2], kt[m][3], kh, kl);
+            z = mfma16(kh, qf[hf + 2 * (m >> 1)][m & 1], z);
+            z = mfma16(kl, qf[hf + 2 * (m >> 1)][m & 1], z);
+          }
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1302,6 +1458,17 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       }
     }
     issue_exact();
+    if constexpr (ROT) {
+      const f16* AV = P.av + slot * P.av_s + h * P.av_h;
+      const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
+#pragma unroll
+      for (int k = 0; k < kVVChunks; ++k) {
+        const int c = tid + kAttThreads * k;
+        const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
+        const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
+        vvl[k] = ld8(src + col);
+      }
+    }
     float tm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k)
@@ -1368,7 +1535,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       tb = tb_n;
     }
   }
-  if (QB == 0 && n_ex > 0) {
+  if (QB == 0 && n_ex > 0 && !(ROT && p < A.n_block_parts)) {
     f16* Va = reinterpret_cast<f16*>(my);
     f16* Vb = Va + kD * kVTStride;
     while (ta < ntile) {
@@ -1381,6 +1548,72 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
                      });
       ta = ta_n;
       tb = tb_n;
+    }
+  }
+  if constexpr (ROT && QB == 0) {
+    // residual rows of an un-rotated block: row t of the pool is rotated to
+    // the block's position + resid_pos[t] (in fp32, split into fp16 hi + lo)
+    if (n_ex > 0 && p < A.n_block_parts) {
+      f16* Va = reinterpret_cast<f16*>(my);
+      f16* Vb = Va + kD * kVTStride;
+      const uint8_t* rpb = P.rp + slot * P.rp_s + h * P.rp_h;
+      auto rot_score = [&](const v8h (&kx)[4], int which) -> v4f {
+        const int row = 16 * (which == 0 ? ta : tb) + l16;
+        const float pf = (float)(bpos + (row < n_ex ? (int)rpb[row] : 0));
+        v4f S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {  // dimension groups s2 and s2 + 2 (the rotation's pairs)
+#pragma unroll
+          for (int h4 = 0; h4 < 2; ++h4) {
+            const int f0 = 32 * s2 + 8 * q4 + 4 * h4;
+            const float4 fh = *reinterpret_cast<const float4*>(fq + f0);
+            const float4 fl = *reinterpret_cast<const float4*>(fq + 64 + f0);
+            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, fls[4] = {fl.x, fl.y, fl.z, fl.w};
+            float xa[4], xb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float cs, sn;
+              rope_cs(pf, fhs[e], fls[e], cs, sn);
+              const float a0 = (float)kx[s2][4 * h4 + e], b0 = (float)kx[s2 + 2][4 * h4 + e];
+              xa[e] = a0 * cs - b0 * sn;
+              xb[e] = b0 * cs + a0 * sn;
+            }
+            v4h kh, kl;
+            split_hl(xa[0], xa[1], xa[2], xa[3], kh, kl);
+            S = mfma16(kh, qf[s2][h4], S);
+            S = mfma16(kl, qf[s2][h4], S);
+            split_hl(xb[0], xb[1], xb[2], xb[3], kh, kl);
+            S = mfma16(kh, qf[s2 + 2][h4], S);
+            S = mfma16(kl, qf[s2 + 2][h4], S);
+          }
+        }
+        return S;
+      };
+      while (ta < ntile) {
+        const bool has_b = tb < ntile;  // uniform over the wave
+        const int ta_n = ta + 2 * kAttWaves, tb_n = tb + 2 * kAttWaves;
+        exact_pair_scored<NQ>(st, Wt, ka, va, kb, vb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, scale, Va, Vb, l16,
+                              q4, [&]() {
+                                if (ta_n < ntile) load_exact_tile(exk, exv, ta_n, ntile, n_ex, ka, va, l16, q4);
+                                if (tb_n < ntile) load_exact_tile(exk, exv, tb_n, ntile, n_ex, kb, vb, l16, q4);
+                              }, rot_score);
+        ta = ta_n;
+        tb = tb_n;
+      }
+    }
+  }
+  if constexpr (ROT) {
+    lds_barrier();  // every wave is done with the frequency table (and VKx^T)
+    if constexpr (LR) {
+#pragma unroll
+      for (int k = 0; k < kVVChunks; ++k) {
+        const int c = tid + kAttThreads * k;
+        if (c < RQ * 16) {
+          const int j = c >> 4, col = (c & 15) * 8;
+          *reinterpret_cast<v4h*>(vvx + j * kVStride + col) = lo4(vvl[k]);
+          *reinterpret_cast<v4h*>(vvx + j * kVStride + col + 4) = hi4(vvl[k]);
+        }
+      }
     }
   }
 
@@ -1474,7 +1707,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   using I0 = std::integral_constant<int, 0>;
   using I8 = std::integral_constant<int, 8>;
   using I4 = std::integral_constant<int, 4>;
-  if constexpr (QK == 0) {
+  if constexpr (QK == 0 || QK == 2) {
     if (NRQ > 0 && lr)
       body(std::true_type{}, I0{});
     else
@@ -2058,6 +2291,13 @@ dkv_status check_pool_shape(const dkv_pool* P) {
   if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
   if (P->resid_format != DKV_RESID_FP16 && P->resid_format != DKV_RESID_INT8 && P->resid_format != DKV_RESID_INT4)
     return fail(DKV_ERR_INVALID_ARG, "resid_format %d unknown", P->resid_format);
+  if (P->rope_freq) {
+    if (!P->slot_pos) return fail(DKV_ERR_INVALID_ARG, "un-rotated pool (rope_freq set) without slot_pos");
+    if (!al(P->rope_freq, 16) || !al(P->slot_pos, 4))
+      return fail(DKV_ERR_UNSUPPORTED, "rope_freq must be 16-byte and slot_pos 4-byte aligned");
+    if (P->resid_format != DKV_RESID_FP16)
+      return fail(DKV_ERR_UNSUPPORTED, "un-rotated pools need fp16 residual rows");
+  }
   return DKV_OK;
 }
 
@@ -2073,7 +2313,8 @@ dkv_status check_pool_arrays(const dkv_pool* P, int which) {
     if ((s = check_view(P->vv, "vv", 2, 16))) return s;
   }
   if ((which & 1) || (which & 2)) {
-    if (P->n_resid > 0 && (which & 1))
+    // exact residual rows of an un-rotated pool are rotated by their position
+    if (P->n_resid > 0 && ((which & 1) || P->rope_freq))
       if ((s = check_view(P->resid_pos, "resid_pos", 1, 1))) return s;
   }
   if ((which & 2) && P->n_resid > 0) {
@@ -2145,6 +2386,8 @@ PoolArgs make_pool_args(const dkv_pool* P) {
     a.rks = (const f16*)P->resid_k_sb.ptr; a.rks_s = P->resid_k_sb.slot_stride; a.rks_h = P->resid_k_sb.head_stride;
     a.rvs = (const f16*)P->resid_v_sb.ptr; a.rvs_s = P->resid_v_sb.slot_stride; a.rvs_h = P->resid_v_sb.head_stride;
   }
+  a.rope = P->rope_freq;
+  a.spos = P->rope_freq ? P->slot_pos : nullptr;
   return a;
 }
 
@@ -2214,6 +2457,7 @@ dkv_status launch_decode_nrq_q(size_t shm, hipStream_t st, const dkv_pool* P, co
 
 template <int NRQ>
 dkv_status launch_decode_nrq(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B, const DecodeArgs& D) {
+  if (P->rope_freq) return launch_decode_nrq_q<NRQ, 2>(shm, st, P, B, D);
   return P->resid_format == DKV_RESID_FP16 ? launch_decode_nrq_q<NRQ, 0>(shm, st, P, B, D)
                                            : launch_decode_nrq_q<NRQ, 1>(shm, st, P, B, D);
 }
@@ -2236,6 +2480,7 @@ dkv_status launch_attend_nrq_q(int64_t items, size_t shm, hipStream_t st, const 
 template <int NRQ>
 dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
                              const AttnArgs& a) {
+  if (P->rope_freq) return launch_attend_nrq_q<NRQ, 2>(items, shm, st, P, B, a);
   return P->resid_format == DKV_RESID_FP16 ? launch_attend_nrq_q<NRQ, 0>(items, shm, st, P, B, a)
                                            : launch_attend_nrq_q<NRQ, 1>(items, shm, st, P, B, a);
 }
@@ -2396,6 +2641,7 @@ static dkv_status launch_layers_q(const dkv_layers_plan* plan, const LayersArgs&
 
 template <int NMAX>
 static dkv_status launch_layers(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
+  if (plan->unrotated) return launch_layers_q<NMAX, 2>(plan, L, st);
   return plan->quantised ? launch_layers_q<NMAX, 1>(plan, L, st) : launch_layers_q<NMAX, 0>(plan, L, st);
 }
 
@@ -2425,9 +2671,30 @@ dkv_status dkv_route_keys(const dkv_pool* pool, const int32_t* slots, int32_t n_
   const int64_t n = (int64_t)(slots ? n_list : pool->n_slots) * pool->n_kv_heads;
   if (n == 0) return DKV_OK;
   if (n > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many slots");
+  if (pool->rope_freq) {
+    hipLaunchKernelGGL(k_route_keys_rot, dim3((unsigned)n), dim3(128), 0, (hipStream_t)stream,
+                       make_pool_args(pool), slots);
+    return launched("k_route_keys_rot");
+  }
   hipLaunchKernelGGL(k_route_keys, dim3((unsigned)n), dim3(128), 0, (hipStream_t)stream,
                      make_pool_args(pool), slots);
   return launched("k_route_keys");
+}
+
+dkv_status dkv_rope_freqs(double base, int32_t head_dim, float* out) {
+  g_err[0] = 0;
+  if (!out) return fail(DKV_ERR_INVALID_ARG, "out is NULL");
+  if (head_dim != DKV_HEAD_DIM) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d != 128", head_dim);
+  if (!(base > 1.0) || !isfinite(base)) return fail(DKV_ERR_INVALID_ARG, "rope base must be finite and > 1");
+  const int half = head_dim / 2;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int j = 0; j < half; ++j) {
+    const double f = pow(base, -2.0 * j / head_dim) / two_pi;
+    const float hi = (float)f;
+    out[j] = hi;
+    out[half + j] = (float)(f - (double)hi);
+  }
+  return DKV_OK;
 }
 
 dkv_status dkv_gather_route_keys(const dkv_pool* pool, const dkv_batch* batch, float* out, void* stream) {
@@ -2667,6 +2934,10 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
       break;
     }
     if (top_k > 0 && b0.batch > 0 && (s = check_pool_arrays(pool, 1 | 2 | (batch->route_keys ? 0 : 4)))) break;
+    if ((pool->rope_freq != nullptr) != (p0.rope_freq != nullptr)) {
+      s = fail(DKV_ERR_UNSUPPORTED, "layer %d: pools must be all rotated or all un-rotated", l);
+      break;
+    }
     size_t shm_l = 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
                                out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
@@ -2702,7 +2973,7 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     int quant = 0;
     for (int l = 0; l < n_layers; ++l) quant |= pools[l].resid_format != DKV_RESID_FP16 ? 1 : 0;
     plan->quantised = quant;
-    plan->reserved1 = 0;
+    plan->unrotated = p0.rope_freq ? 1 : 0;
     plan->table = table;
     plan->workspace = workspace;
   }

@@ -33,7 +33,7 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
             "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
-            "dkv_seal_blocks")
+            "dkv_seal_blocks", "dkv_rope_freqs")
 
 
 class DKVError(RuntimeError):
@@ -54,7 +54,8 @@ class PoolC(ctypes.Structure):
                 ("anchor_k", View), ("anchor_v", View), ("u", View), ("vk", View), ("vv", View),
                 ("resid_k", View), ("resid_v", View), ("resid_pos", View), ("route_key", View),
                 ("resid_format", ctypes.c_int32), ("reserved0", ctypes.c_int32),
-                ("resid_k_sb", View), ("resid_v_sb", View)]
+                ("resid_k_sb", View), ("resid_v_sb", View),
+                ("rope_freq", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p)]
 
 RESID_FP16, RESID_INT8, RESID_INT4 = 0, 1, 2
 
@@ -72,7 +73,7 @@ class LayersPlanC(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_units", ctypes.c_int32), ("routes", ctypes.c_int32),
                 ("parts", ctypes.c_int32), ("win_parts", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
-                ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("quantised", ctypes.c_int32), ("reserved1", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("quantised", ctypes.c_int32), ("unrotated", ctypes.c_int32),
                 ("table", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p)]
 
@@ -99,6 +100,8 @@ def load(path: str = LIB_PATH):
     lib.dkv_abi_version.restype = i32
     lib.dkv_route_keys.argtypes = [P, vp, i32, vp]
     lib.dkv_route_keys.restype = i32
+    lib.dkv_rope_freqs.argtypes = [ctypes.c_double, i32, vp]
+    lib.dkv_rope_freqs.restype = i32
     lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
     lib.dkv_gather_route_keys.argtypes = [P, Bp, vp, vp]
     lib.dkv_decode_layers_table_size.argtypes = [i32]
@@ -256,7 +259,26 @@ class Pool:
                    t["resid_v"], t["resid_pos"], rk, fmt, t.get("resid_k_sb"), t.get("resid_v_sb"))
         if "_record" in t:
             pool.tensors["_record"] = t["_record"]
+        if arrays.get("rope_base") is not None:
+            pool.set_unrotated(float(arrays["rope_base"]), arrays["slot_pos"])
         return pool
+
+    def set_unrotated(self, rope_base: float, slot_pos) -> None:
+        """Read this pool as an un-rotated one: keys are rotated at read to the
+        absolute positions slot_pos[s] (+ in-block position), with the rotary
+        frequencies of `rope_base` (table from dkv_rope_freqs).  slot_pos:
+        int32 [n_slots], numpy or a device tensor."""
+        import torch
+        table = np.zeros(HEAD_DIM, dtype=np.float32)
+        _check(load().dkv_rope_freqs(float(rope_base), HEAD_DIM, table.ctypes.data), "dkv_rope_freqs")
+        dev = self.tensors["anchor_k"].device
+        freq = torch.from_numpy(table).to(dev)
+        pos = slot_pos if isinstance(slot_pos, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(slot_pos, dtype=np.int32))
+        pos = pos.to(device=dev, dtype=torch.int32).contiguous()
+        if pos.numel() < self.n_slots:
+            raise ValueError(f"slot_pos has {pos.numel()} entries for {self.n_slots} slots")
+        self.tensors["rope_freq"], self.tensors["slot_pos"] = freq, pos
+        self.c.rope_freq, self.c.slot_pos = freq.data_ptr(), pos.data_ptr()
 
     @classmethod
     def empty(cls, n_slots: int, n_kv_heads: int, rank: int, n_resid: int, device="cuda",

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DKV_ABI_VERSION 4
+#define DKV_ABI_VERSION 5
 #define DKV_HEAD_DIM 128
 #define DKV_BLOCK_SIZE 256
 #define DKV_MAX_RANK 64
@@ -117,6 +117,22 @@ typedef struct dkv_pool {
   int32_t reserved0;
   dkv_view resid_k_sb;    /* quantised formats only: fp16 [R][2][2], (scale, bias) of dims 0..63, 64..127 */
   dkv_view resid_v_sb;    /* same for the V rows */
+  /* Un-rotated pools (README "Key Environment Knobs", DKV_ROTATED_POOL = 0, and
+   * the preset ladder's "keys stored" column): the anchors, V_K and residual
+   * keys hold keys from before the rotary position embedding, and every read
+   * rotates a key to its absolute position: the anchor of the block in slot s
+   * to slot_pos[s], low-rank row i to slot_pos[s] + i, a residual row to
+   * slot_pos[s] + its resid_pos.  Rotation pairs dimension j with j + 64 and
+   * turns the pair by the angle position * theta_j:
+   *   x'_j = x_j cos - x_{j+64} sin,   x'_{j+64} = x_{j+64} cos + x_j sin.
+   * Values, the queries and the dense window are never rotated by the library
+   * (the queries and window keys arrive rotated).  NULL rope_freq: the pool
+   * holds rotated keys (the default).  Un-rotated pools need fp16 residual rows.
+   *   rope_freq: fp32 [2][64] device, theta_j / (2 pi) as an unevaluated sum
+   *              row0[j] + row1[j] of two floats (dkv_rope_freqs fills it);
+   *   slot_pos:  int32 [n_slots] device, positions in [0, 2^24 - 256]. */
+  const float* rope_freq;
+  const int32_t* slot_pos;
 } dkv_pool;
 
 /* One decode step's batch: one new query token per sequence. */
@@ -148,13 +164,23 @@ const char* dkv_last_error(void);
 /* DKV_ABI_VERSION of the built library. */
 int32_t dkv_abi_version(void);
 
+/* The rotary frequency table of an un-rotated pool, on the host: for
+ * j < head_dim / 2, theta_j = base^(-2 j / head_dim) (the rotary embedding's
+ * frequencies, computed in double precision) and f_j = theta_j / (2 pi), stored
+ * as out[j] = (float) f_j and out[head_dim / 2 + j] = (float) (f_j - out[j]).
+ * The caller copies the 2 * 64 floats to device memory for pool->rope_freq.
+ *   base > 1; head_dim must be 128.  out: host float [2][head_dim / 2]. */
+dkv_status dkv_rope_freqs(double base, int32_t head_dim, float* out);
+
 /* Routing-key precompute, once per sealed block (off the per-query path).
  * Computes c = a_k + (1/255) sum_{i=1..255} U_i V_K in fp32 for every KV head of
  * the listed slots and stores it through pool->route_key (which must point to
  * writable memory).  The routing key is the block's centroid key, the mean of
  * its anchor-relative reconstructed rows 1..255 (all of them, residual
  * positions included); the pages keep such per-block router metadata (README,
- * "Per-Block Memory Breakdown", the decode-router row).
+ * "Per-Block Memory Breakdown", the decode-router row).  In an un-rotated
+ * pool the key is the mean of those rows each rotated to its own position,
+ * c = (1/255) sum_{i=1..255} rot(a_k + U_i V_K, slot_pos[s] + i).
  *   slots:   int32 [n_list] pool slots to process, or NULL for every slot
  *            (then n_list is ignored).  Out-of-range slots are skipped. */
 dkv_status dkv_route_keys(const dkv_pool* pool, const int32_t* slots, int32_t n_list,
@@ -296,7 +322,7 @@ typedef struct dkv_layers_plan {
   int32_t lds_bytes;      /* dynamic LDS per workgroup */
   int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */
   int32_t quantised;      /* 1 if any layer's residual rows are quantised */
-  int32_t reserved1;
+  int32_t unrotated;      /* 1 if the layers' pools are un-rotated (all of them or none) */
   const void* table;
   void* workspace;
 } dkv_layers_plan;

@@ -123,7 +123,8 @@ def check_partials(o, lse, ref_o, ref_lse, tol_rel: float = TOL_PART_REL,
     l = np.asarray(lse, dtype=np.float64)
     rl = np.asarray(ref_lse, dtype=np.float64)
     same_inf = (l == rl) & ~np.isfinite(rl)
-    dl = np.where(same_inf, 0.0, np.abs(l - rl))
+    with np.errstate(invalid="ignore"):        # -inf - -inf is masked by same_inf
+        dl = np.where(same_inf, 0.0, np.abs(l - rl))
     dl = np.where(np.isnan(dl), np.inf, dl)
     num = np.linalg.norm(o - r, axis=-1)
     den = np.maximum(np.linalg.norm(r, axis=-1), 1e-30)

@@ -1,0 +1,150 @@
+"""GPU parity of un-rotated pools (keys stored before the rotary embedding and
+rotated to their absolute positions at read) against the fp64 oracle, through
+the C ABI: routing keys, routing, per-part partials, the fused decode, and the
+layer-batched launch.  Same bars as the rotated pools."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from compressed_kv_cache_amd import synth
+import oracle
+import parity
+from test_gpu_parity import (DEV, _all_blocks_idx, _oracle_check, _run_layers, check_decode, lib,  # noqa: F401
+                             say, upload)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _u(cfg, layers=None):
+    return synth.make_config(cfg, layers=layers, variant="U")
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_route_keys_unrotated(lib, cfg):
+    wl = _u(cfg)
+    say(f"[route_keys U] {wl.name}")
+    pool, _ = upload(lib, wl)
+    got = pool.route_key.cpu().numpy().astype(np.float64)
+    P = wl.layers[0].pool()
+    worst = 0.0
+    for s in range(got.shape[0]):
+        for h in range(got.shape[1]):
+            ref = oracle.block_route_key(P, s, h)
+            worst = max(worst, float(np.abs(got[s, h] - ref).max() / (np.abs(ref).max() + 1.0)))
+    say(f"   max rel err {worst:.2e}")
+    assert worst < 1e-5
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_route_topk_unrotated(lib, cfg):
+    wl = _u(cfg)
+    say(f"[route_topk U] {wl.name}")
+    pool, batch = upload(lib, wl)
+    idx = lib.route_topk(pool, batch, wl.top_k)
+    torch.cuda.synchronize()
+    _, scores, keys = oracle.route_batch(wl.layers[0].pool(), wl.layers[0].q, wl.block_table, wl.n_blocks,
+                                         wl.n_kv_heads, wl.top_k)
+    rc = parity.check_routing(idx.cpu().numpy(), scores, keys, wl.layers[0].q, wl.n_kv_heads, wl.top_k)
+    say(f"   near-ties {rc.near_ties}")
+    assert rc.ok, rc.message
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_block_partials_unrotated(lib, cfg):
+    wl = _u(cfg)
+    say(f"[block partials U] {wl.name}")
+    pool, batch = upload(lib, wl)
+    idx = _all_blocks_idx(wl)
+    K = idx.shape[-1]
+    gi = torch.from_numpy(idx).to(DEV)
+    lo, ll = lib.lowrank_attn(pool, batch, gi, K, wl.scale)
+    eo, el = lib.exact_attn(pool, batch, gi, K, 0, wl.scale)
+    torch.cuda.synchronize()
+    lo, ll, eo, el = (t.cpu().numpy() for t in (lo, ll, eo, el))
+    lay = wl.layers[0]
+    G = wl.group
+    ref = [np.zeros_like(x, dtype=np.float64) for x in (lo, ll, eo, el)]
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            for k in range(K):
+                slot = int(wl.block_table[b, idx[b, h, k]])
+                (o1, l1), (o2, l2) = oracle.block_partials(lay.pool(), slot, h, lay.q[b, h * G:(h + 1) * G],
+                                                          wl.scale)
+                rows = slice(b * wl.n_q_heads + h * G, b * wl.n_q_heads + (h + 1) * G)
+                ref[0][rows, k], ref[1][rows, k], ref[2][rows, k], ref[3][rows, k] = o1, l1, o2, l2
+    c1 = parity.check_partials(lo, ll, ref[0], ref[1])
+    c2 = parity.check_partials(eo, el, ref[2], ref[3])
+    say(f"   low-rank: rel {c1.rel_l2:.2e} lse {c1.max_lse:.2e}; residual: rel {c2.rel_l2:.2e} "
+        f"lse {c2.max_lse:.2e}")
+    assert c1.ok, c1.message
+    assert c2.ok, c2.message
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_decode_unrotated(lib, cfg):
+    check_decode(lib, _u(cfg), label="U")
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_decode_unrotated_stack_layers(lib, layer):
+    """The 64k batch-4 stack read as un-rotated pools (positions up to 64511),
+    one layer of each rank and the last layer, in the per-layer launch."""
+    wl = _u(2, layers=[0, 9, 19, 27])
+    check_decode(lib, wl, layer=layer, label=f"U rank {wl.layers[layer].rank}")
+
+
+EDGE_U = {
+    "rank1_R0": dict(ranks=[1], n_resid=0),
+    "rank7": dict(ranks=[7]),
+    "rank64": dict(ranks=[64], n_resid=4),
+    "rank15_R255": dict(ranks=[15], n_resid=255),
+    "group16": dict(n_q_heads=16, n_kv_heads=1),
+    "window_only": dict(top_k=0),
+    "permuted_pool": dict(permute_slots=True),
+    "empty_sequence": dict(n_blocks=[3, 0, 5, 2], win_len=[64, 0, 64, 64]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_U))
+def test_decode_unrotated_edge_cases(lib, case):
+    kw = dict(seed=500 + len(case), batch=4, n_q_heads=6, n_kv_heads=2, window=64,
+              n_blocks=[5, 3, 6, 4], ranks=[12], n_resid=20, top_k=3, sigma0=2.0)
+    kw.update(EDGE_U[case])
+    wl = synth.make_workload("U_" + case, rope_base=synth.ROPE_BASE, **kw)
+    check_decode(lib, wl, label=case)
+
+
+def test_decode_unrotated_far_positions(lib):
+    """Blocks placed near the largest supported positions (2^24 - 256): the
+    angle reduction keeps the rotation exact to fp32 rounding there too."""
+    wl = synth.make_workload("U_far", seed=520, batch=2, n_q_heads=4, n_kv_heads=2, window=32,
+                             n_blocks=[4, 6], ranks=[20], n_resid=16, top_k=3, sigma0=2.0,
+                             rope_base=10000.0)
+    for lay in wl.layers:
+        lay.slot_pos = lay.slot_pos + np.int32((1 << 24) - 256 * 8)
+    check_decode(lib, wl, label="far")
+
+
+def test_decode_layers_unrotated(lib):
+    """Four layers of the un-rotated 64k batch-4 stack in one layer-batched
+    launch: routing equals the per-layer launch's and outputs match the oracle."""
+    wl = _u(2, layers=[0, 9, 19, 27])
+    say("[decode layers U] stack64k layers 0, 9, 19, 27")
+    pools, batches = [], []
+    for l in range(4):
+        p_, b_ = upload(lib, wl, l)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    assert run.plan.unrotated == 1
+    res = _run_layers(lib, run, reps=2)
+    for l in range(4):
+        _, _, i1 = lib.decode(pools[l], batches[l], wl.top_k, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        c = _oracle_check(wl, wl.layers[l], *res[l], wl.top_k)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")

@@ -91,6 +91,9 @@ def _decode(clib, pool, batch, top_k=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
     ({"vk": L.View(FAKE, 4100, 1024)}, {}, 4, L.DKV_ERR_UNSUPPORTED),
     ({"u": L.View(None, 0, 0)}, {}, 4, L.DKV_ERR_INVALID_ARG),
     ({}, {}, -1, L.DKV_ERR_INVALID_ARG),
+    ({"rope_freq": FAKE}, {}, 4, L.DKV_ERR_INVALID_ARG),                    # no slot_pos
+    ({"rope_freq": FAKE + 4, "slot_pos": FAKE}, {}, 4, L.DKV_ERR_UNSUPPORTED),
+    ({"rope_freq": FAKE, "slot_pos": FAKE, "resid_format": L.RESID_INT8}, {}, 4, L.DKV_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments(clib, pool_kw, batch_kw, top_k, code):
     st = _decode(clib, _pool(**pool_kw), _batch(**batch_kw), top_k=top_k)
@@ -226,3 +229,31 @@ def test_seal_blocks_validates(clib):
     assert seal(pool=_pool(resid_format=L.RESID_INT8)) == L.DKV_ERR_UNSUPPORTED
     assert seal(pool=_pool(head_dim=64)) == L.DKV_ERR_UNSUPPORTED
     assert seal(width=81) == L.DKV_ERR_UNSUPPORTED and b"width" in clib.dkv_last_error()
+
+
+def test_rope_freqs_table(clib):
+    # host-only: theta_j / (2 pi) = base^(-j/64) / (2 pi) as hi + lo floats
+    import numpy as np
+    out = np.zeros(128, dtype=np.float32)
+    assert clib.dkv_rope_freqs(1e6, 128, out.ctypes.data) == L.DKV_OK
+    hi, lo = out[:64].astype(np.float64), out[64:].astype(np.float64)
+    assert hi[0] == np.float32(1 / (2 * np.pi))                 # theta_0 = 1
+    assert abs(hi[32] + lo[32] - 1e-3 / (2 * np.pi)) < 1e-18     # theta_32 = base^(-1/2)
+    want = np.array([1e6 ** (-j / 64) for j in range(64)]) / (2 * np.pi)
+    assert np.all(np.abs(hi + lo - want) <= 1e-14 * want)
+    assert np.all(np.abs(lo) <= np.spacing(out[:64]).astype(np.float64))
+    assert clib.dkv_rope_freqs(1e6, 64, out.ctypes.data) == L.DKV_ERR_UNSUPPORTED
+    assert clib.dkv_rope_freqs(1.0, 128, out.ctypes.data) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_rope_freqs(1e4, 128, None) == L.DKV_ERR_INVALID_ARG
+
+
+def test_layer_batched_rejects_mixed_rotation(clib):
+    p, q, b = _pool(), _pool(rope_freq=FAKE, slot_pos=FAKE), _batch()
+    PA, BA = (L.PoolC * 2)(p, q), (L.BatchC * 2)(b, b)
+    plan = L.LayersPlanC()
+    outs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    tsz = clib.dkv_decode_layers_table_size(2)
+    need = clib.dkv_decode_layers_workspace_size(PA, BA, 2, 4)
+    st = clib.dkv_decode_layers_prepare(PA, BA, 2, 4, 0.088, outs, outs, None, FAKE, tsz, FAKE, need,
+                                        ctypes.byref(plan))
+    assert st == L.DKV_ERR_UNSUPPORTED and "rotated" in clib.dkv_last_error().decode()
