@@ -727,6 +727,24 @@ __host__ __device__ inline int att_lds_bytes(int rq) {
   return 16 * rq * 4 + rq * kVStride * 2 + 2 * kAttWaves * 16 * 4 + att_region_bytes(rq);
 }
 
+// VKx^T of an un-rotated pool's block, staged [d][j] over the V_K q and VVx
+// areas: row stride vkt_stride(RQ) halves and the 4-half chunks of a row
+// permuted by chunk ^ vkt_swz(RQ, d), so that the 16 lanes of a row group,
+// which read one chunk from 16 different rows, hit 32 different banks.  Sizes
+// fit the areas (128 * stride * 2 <= 328 * RQ bytes).
+__host__ __device__ constexpr int vkt_stride(int rq) { return rq == 64 ? 80 : rq; }
+__device__ __forceinline__ constexpr int vkt_swz(int rq, int d) {
+  return rq == 32 ? (((d >> 1) ^ (d >> 2)) & 7) : ((d >> 3) & 3);
+}
+__device__ __forceinline__ constexpr int vkt_at(int rq, int d, int j) {
+  return d * vkt_stride(rq) + 4 * ((j >> 2) ^ vkt_swz(rq, d)) + (j & 3);
+}
+static_assert(128 * vkt_stride(16) * 2 <= 328 * 16 && 128 * vkt_stride(32) * 2 <= 328 * 32 &&
+                  128 * vkt_stride(48) * 2 <= 328 * 48 && 128 * vkt_stride(64) * 2 <= 328 * 64 &&
+                  128 * vkt_stride(80) * 2 <= 328 * 80,
+              "VKx^T must fit the V_K q and VVx areas");
+
+
 // Reductions over the four lanes l16, l16 + 16, l16 + 32, l16 + 48 (the four
 // row groups of an MFMA accumulator), with gfx950 lane-swap moves; every lane
 // gets the same bits.
@@ -1130,7 +1148,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   // ---- window tiles owned by a routed-block part: exact rows that do not
   //      depend on the routing, attended while it may still be running
   bool any = false;
-  if (p < A.n_block_parts && A.win_tile_stride > 0) {
+  if (QK != 2 && p < A.n_block_parts && A.win_tile_stride > 0) {
     const int n_wt = (wl + 15) >> 4;
     any = p < n_wt;  // uniform
     f16* Va = reinterpret_cast<f16*>(my);
@@ -1341,8 +1359,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         }
       }
     } else {
-      // VKx^T [d][j] (rows of RQ + 4 halves) over the V_K q and VVx areas,
-      // which it fits for RQ >= 16; VVx is staged after the scores
+      // VKx^T [d][j] over the V_K q and VVx areas (VVx is staged after the scores)
       f16* vkt = reinterpret_cast<f16*>(qt);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -1351,7 +1368,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) vkt[(32 * s + 8 * q4 + jj) * (RQ + 4) + jt * 16 + l16] = vkx[k][s][jj];
+            for (int jj = 0; jj < 8; ++jj) vkt[vkt_at(RQ, 32 * s + 8 * q4 + jj, jt * 16 + l16)] = vkx[k][s][jj];
           }
         }
       }
@@ -1422,7 +1439,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
               const int dim = 32 * (hf + 2 * (m >> 1)) + 8 * (l16 >> 2) + 4 * (m & 1) + (l16 & 3);
-              const v4h a = *reinterpret_cast<const v4h*>(vkt + dim * (RQ + 4) + 16 * t + 4 * q4);
+              const v4h a = *reinterpret_cast<const v4h*>(vkt + vkt_at(RQ, dim, 16 * t + 4 * q4));
               kt[m] = mfma16(a, ua[k][t], kt[m]);
             }
           }
@@ -2544,9 +2561,12 @@ struct WsLayout {
 };
 
 // fold: the window's tiles are shared out over the routed-block parts (else
-// the window has parts of its own, of kWinChunk rows)
+// the window has parts of its own, of kWinChunk rows).  Un-rotated pools never
+// fold: their block parts then start with empty output accumulators, which
+// keeps the registers the rotation needs free.
 WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold = true) {
   WsLayout w;
+  fold = fold && !pool->rope_freq;
   const size_t B = (size_t)batch->batch;
   const size_t units = B * (size_t)pool->n_kv_heads;
   const size_t n_parts = (top_k > 0 && fold) ? (size_t)top_k
@@ -2570,7 +2590,7 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   const WsLayout w = decode_layout(pool, batch, top_k, fold);
   // folded, each routed-block part also takes its share of the window;
   // otherwise the window comes in chunks of kWinChunk rows
-  fold = fold && top_k > 0;
+  fold = fold && top_k > 0 && !pool->rope_freq;
   const int n_win = fold ? 0 : decode_win_parts(batch->window);
   const int n_parts = top_k + n_win;
   const int units = batch->batch * pool->n_kv_heads;
