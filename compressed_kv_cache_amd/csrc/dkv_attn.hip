@@ -1265,7 +1265,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
     // VVx rows: V_V rows j < r, a_v at j = r.  Padding rows j > r read V_V row 0:
     // their weight in (p^T Ux) is exactly 0 because Ux is zero there.  (An
-    // un-rotated pool loads them once its scores are formed.)
+    // un-rotated pool loads them half-way through its scores.)
     if constexpr (!ROT) {
 #pragma unroll
       for (int k = 0; k < kVVChunks; ++k) {
@@ -1473,19 +1473,23 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         const bool masked = (ii > 0) & (((wmask[ii >> 5] >> (ii & 31)) & 1u) != 0u);
         zz[k][e] = masked ? -INFINITY : z[e] * scale;
       }
-    }
-    issue_exact();
-    if constexpr (ROT) {
-      const f16* AV = P.av + slot * P.av_s + h * P.av_h;
-      const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
+      if constexpr (ROT) {
+        // V_V and a_v, into the registers of the U tiles already used: after
+        // the second tile, or (the largest ranks, short of registers) the last
+        if (k == (NRQ >= 5 ? kLRTilesPerWave - 1 : 1)) {
+          const f16* AV = P.av + slot * P.av_s + h * P.av_h;
+          const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
 #pragma unroll
-      for (int k = 0; k < kVVChunks; ++k) {
-        const int c = tid + kAttThreads * k;
-        const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
-        const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
-        vvl[k] = ld8(src + col);
+          for (int c2 = 0; c2 < kVVChunks; ++c2) {
+            const int c = tid + kAttThreads * c2;
+            const int j = (c < RQ * 16) ? (c >> 4) : 0, col = (c & 15) * 8;
+            const f16* src = (j < r) ? VV + (int64_t)j * kD : ((j == r) ? AV : VV);
+            vvl[c2] = ld8(src + col);
+          }
+        }
       }
     }
+    issue_exact();
     float tm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kLRTilesPerWave; ++k)
