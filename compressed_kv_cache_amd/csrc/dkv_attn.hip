@@ -327,6 +327,16 @@ __device__ __forceinline__ void rope_cs(float pf, float fh, float fl, float& c, 
   s = __builtin_amdgcn_sinf(t);
 }
 
+// cos and sin of the rotary angle of a row at in-block offset `off` (0..255):
+// t0 = the block's own angle in turns, reduced exactly once per block (fract of
+// slot_pos * theta / 2 pi), plus off * theta / 2 pi, < 41 turns.  The rounding
+// of that sum (< 4e-6 turns) is far below the fp16 rounding of the rotated key.
+__device__ __forceinline__ void rope_cs_off(float off, float fh, float t0, float& c, float& s) {
+  const float t = __builtin_fmaf(off, fh, t0);
+  c = __builtin_amdgcn_cosf(t);
+  s = __builtin_amdgcn_sinf(t);
+}
+
 // Routing keys of an un-rotated pool: the mean over positions i = 1..255 of
 // the reconstructed key a_k + U_i V_K rotated to slot_pos + i.  One workgroup
 // per (slot, KV head); thread t takes the dimension pair (j, j + 64) with
@@ -1233,9 +1243,17 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   constexpr bool ROT = QK == 2;
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
-  float* fq = wstat;  // ROT: theta_j / (2 pi) as hi[64], lo[64]
+  float* fq = wstat;  // ROT: theta_j / (2 pi) [64], then the block's angles in turns [64]
   if constexpr (ROT) {
-    if (tid < 128) fq[tid] = P.rope[tid];
+    if (tid < 64) {
+      fq[tid] = P.rope[tid];
+    } else if (tid < 128) {
+      const int j = tid - 64;
+      const float fh = P.rope[j], fl = P.rope[64 + j], pf = (float)bpos;
+      const float a = pf * fh;
+      const float e = __builtin_fmaf(pf, fh, -a);
+      fq[tid] = __builtin_amdgcn_fractf(__builtin_amdgcn_fractf(a) + __builtin_fmaf(pf, fl, e));
+    }
     if constexpr (!LR) lds_barrier();
   }
 
@@ -1422,13 +1440,14 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
           z = mfma16(ua[k][s], qtl[s], z);
         }
       } else {
-        // the 16 keys themselves, K^T = VKx^T Ux^T in fp32: kt[2 s + hh] holds
+        // the 16 keys themselves, K^T = VKx^T Ux^T in fp32: kt holds
         // dimensions 32 s + 8 q4 + 4 hh + e of position i0 + l16 (the order of
-        // the query fragments), rotated in fp32 and split into fp16 hi + lo
+        // the query fragments), rotated in fp32 and rounded once to fp16, the
+        // precision of the rotated keys a rotated pool stores
         // Two halves: dimension groups s = hf and s = hf + 2 (the rotation's
         // pairs), m = 2 (s >> 1) + hh.
         const f16* vkt = reinterpret_cast<const f16*>(qt);
-        const float pf = (float)(bpos + i);
+        const float off = (float)i;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           v4f kt[4];
@@ -1447,12 +1466,12 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
           for (int hh = 0; hh < 2; ++hh) {
             const int f0 = 32 * hf + 8 * q4 + 4 * hh;
             const float4 fh = *reinterpret_cast<const float4*>(fq + f0);
-            const float4 fl = *reinterpret_cast<const float4*>(fq + 64 + f0);
-            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, fls[4] = {fl.x, fl.y, fl.z, fl.w};
+            const float4 t0 = *reinterpret_cast<const float4*>(fq + 64 + f0);
+            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, t0s[4] = {t0.x, t0.y, t0.z, t0.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float cs, sn;
-              rope_cs(pf, fhs[e], fls[e], cs, sn);
+              rope_cs_off(off, fhs[e], t0s[e], cs, sn);
               const float x = kt[hh][e], y = kt[2 + hh][e];
               kt[hh][e] = x * cs - y * sn;
               kt[2 + hh][e] = y * cs + x * sn;
@@ -1460,10 +1479,8 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
           }
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            v4h kh, kl;
-            split_hl(kt[m][0], kt[m][1], kt[m][2], kt[m][3], kh, kl);
-            z = mfma16(kh, qf[hf + 2 * (m >> 1)][m & 1], z);
-            z = mfma16(kl, qf[hf + 2 * (m >> 1)][m & 1], z);
+            const float km[4] = {kt[m][0], kt[m][1], kt[m][2], kt[m][3]};
+            z = mfma16(to_h4(km), qf[hf + 2 * (m >> 1)][m & 1], z);
           }
         }
       }
@@ -1573,14 +1590,25 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   }
   if constexpr (ROT && QB == 0) {
     // residual rows of an un-rotated block: row t of the pool is rotated to
-    // the block's position + resid_pos[t] (in fp32, split into fp16 hi + lo)
+    // the block's position + resid_pos[t] (in fp32, rounded once to fp16)
     if (n_ex > 0 && p < A.n_block_parts) {
       f16* Va = reinterpret_cast<f16*>(my);
       f16* Vb = Va + kD * kVTStride;
       const uint8_t* rpb = P.rp + slot * P.rp_s + h * P.rp_h;
       auto rot_score = [&](const v8h (&kx)[4], int which) -> v4f {
-        const int row = 16 * (which == 0 ? ta : tb) + l16;
-        const float pf = (float)(bpos + (row < n_ex ? (int)rpb[row] : 0));
+        const int tile = which == 0 ? ta : tb;
+        const int row = 16 * tile + l16;
+        int rpos;
+        if constexpr (LR) {
+          // the low-rank pass holds every residual position in registers
+          // (position t in lane t % 64 of ps[t / 64]): a cross-lane read
+          const int k4 = tile >> 2;
+          const int src = k4 == 0 ? ps[0] : (k4 == 1 ? ps[1] : (k4 == 2 ? ps[2] : ps[3]));
+          rpos = __shfl(src, 16 * (tile & 3) + l16);
+        } else {
+          rpos = row < n_ex ? (int)rpb[row] : 0;
+        }
+        const float off = (float)(row < n_ex ? rpos : 0);
         v4f S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {  // dimension groups s2 and s2 + 2 (the rotation's pairs)
@@ -1588,24 +1616,19 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
           for (int h4 = 0; h4 < 2; ++h4) {
             const int f0 = 32 * s2 + 8 * q4 + 4 * h4;
             const float4 fh = *reinterpret_cast<const float4*>(fq + f0);
-            const float4 fl = *reinterpret_cast<const float4*>(fq + 64 + f0);
-            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, fls[4] = {fl.x, fl.y, fl.z, fl.w};
+            const float4 t0 = *reinterpret_cast<const float4*>(fq + 64 + f0);
+            const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, t0s[4] = {t0.x, t0.y, t0.z, t0.w};
             float xa[4], xb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float cs, sn;
-              rope_cs(pf, fhs[e], fls[e], cs, sn);
+              rope_cs_off(off, fhs[e], t0s[e], cs, sn);
               const float a0 = (float)kx[s2][4 * h4 + e], b0 = (float)kx[s2 + 2][4 * h4 + e];
               xa[e] = a0 * cs - b0 * sn;
               xb[e] = b0 * cs + a0 * sn;
             }
-            v4h kh, kl;
-            split_hl(xa[0], xa[1], xa[2], xa[3], kh, kl);
-            S = mfma16(kh, qf[s2][h4], S);
-            S = mfma16(kl, qf[s2][h4], S);
-            split_hl(xb[0], xb[1], xb[2], xb[3], kh, kl);
-            S = mfma16(kh, qf[s2 + 2][h4], S);
-            S = mfma16(kl, qf[s2 + 2][h4], S);
+            S = mfma16(to_h4(xa), qf[s2][h4], S);
+            S = mfma16(to_h4(xb), qf[s2 + 2][h4], S);
           }
         }
         return S;
