@@ -77,6 +77,8 @@ class Layer:
     # un-rotated pools: the rotary base and each slot's absolute position
     rope_base: Optional[float] = None
     slot_pos: Optional[np.ndarray] = None
+    # shared basis: the vk / vv entry each slot reads (vk, vv then hold the bases)
+    basis_of: Optional[np.ndarray] = None
 
     def pool(self) -> dict:
         """The block-store arrays as a plain dict (the oracle's input form)."""
@@ -89,6 +91,8 @@ class Layer:
         if self.rope_base is not None:
             d["rope_base"] = self.rope_base
             d["slot_pos"] = self.slot_pos
+        if self.basis_of is not None:
+            d["basis_of"] = self.basis_of
         return d
 
 
@@ -298,6 +302,26 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
     if rope_base is not None:
         set_unrotated(out, rope_base)
     return out
+
+
+def set_shared_basis(wl: Workload, group: int, seed: int = 0) -> Workload:
+    """Let runs of `group` consecutive logical blocks of each sequence read one
+    basis: the first block's V_K, V_V entry serves the run (the others' entries
+    stay in the arrays, unread), so about 1/group of the entries are read, the
+    pages' sharing fraction.  A seeded shuffle of the entries' order keeps a
+    run's entry away from its own slots."""
+    pos = np.arange(max(wl.n_slots, 1), dtype=np.int32)
+    for b in range(wl.batch):
+        nb = int(wl.n_blocks[b])
+        for j in range(nb):
+            pos[wl.block_table[b, j]] = wl.block_table[b, (j // group) * group]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 91, seed])))
+    perm = rng.permutation(max(wl.n_slots, 1)).astype(np.int32)
+    for lay in wl.layers:
+        lay.vk = np.ascontiguousarray(lay.vk[np.argsort(perm)])
+        lay.vv = np.ascontiguousarray(lay.vv[np.argsort(perm)])
+        lay.basis_of = perm[pos]
+    return wl
 
 
 def set_unrotated(wl: Workload, rope_base: float) -> Workload:

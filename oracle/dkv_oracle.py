@@ -41,6 +41,12 @@ What it computes (sources are the pages on DKV, cited by title and section):
   the dense window arrive rotated as usual.  A pool dict that carries
   "rope_base" and "slot_pos" (absolute position of token 0 of the block held
   in each slot) is such a pool.
+* Shared basis -- README "Key Environment Knobs" (DKV_SHARED_BASIS and
+  DKV_SHARED_BASIS_FRAC): blocks whose delta subspaces agree read one basis
+  row instead of each storing its own V, and the pool refuses the combination
+  with rotated keys.  A pool dict that carries "basis_of" (per slot, the entry
+  of vk / vv that holds the block's V_K and V_V) is such a pool; the block's
+  own anchor, U and residual rows stay per slot.
 
 Readings where the pages are silent (listed in the design notes):
   the anchor is attended as its own row at position 0; the delta is relative to
@@ -252,8 +258,17 @@ def route(q_group, keys, top_k: int) -> Tuple[np.ndarray, np.ndarray]:
 # Whole decode step for one layer
 # ---------------------------------------------------------------------------
 
+def basis_entry(pool: Dict[str, np.ndarray], slot: int) -> int:
+    """Entry of vk / vv holding the basis of the block in `slot` (the slot itself
+    unless the pool shares bases)."""
+    b = pool.get("basis_of")
+    return int(slot) if b is None else int(b[slot])
+
+
 def _slot_entry(pool: Dict[str, np.ndarray], slot: int, h: int) -> Dict[str, np.ndarray]:
-    e = {k: pool[k][slot, h] for k in ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_pos")}
+    e = {k: pool[k][slot, h] for k in ("anchor_k", "anchor_v", "u", "resid_pos")}
+    g = basis_entry(pool, slot)
+    e["vk"], e["vv"] = pool["vk"][g, h], pool["vv"][g, h]
     e["resid_k"], e["resid_v"] = residual_rows(pool, slot, h)
     return e
 
@@ -264,10 +279,11 @@ def is_unrotated(pool: Dict[str, np.ndarray]) -> bool:
 
 def block_route_key(pool: Dict[str, np.ndarray], slot: int, h: int) -> np.ndarray:
     """Routing key of the block in `slot`, KV head h, for either kind of pool."""
+    vk = pool["vk"][basis_entry(pool, slot), h]
     if is_unrotated(pool):
-        return route_key_unrotated(pool["anchor_k"][slot, h], pool["u"][slot, h], pool["vk"][slot, h],
+        return route_key_unrotated(pool["anchor_k"][slot, h], pool["u"][slot, h], vk,
                                    int(pool["slot_pos"][slot]), float(pool["rope_base"]))
-    return route_key(pool["anchor_k"][slot, h], pool["u"][slot, h], pool["vk"][slot, h])
+    return route_key(pool["anchor_k"][slot, h], pool["u"][slot, h], vk)
 
 
 def block_rows(pool: Dict[str, np.ndarray], slot: int, h: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -1,0 +1,67 @@
+"""Pins of the oracle's shared-basis pools (several blocks read one V_K, V_V
+basis entry) against the plain pool definition: the same blocks with their
+basis copied into their own slots decode and route identically, and an
+identity sharing map changes nothing.  CPU only."""
+import numpy as np
+
+import oracle
+from compressed_kv_cache_amd import synth
+
+
+def _wl(seed, group=2):
+    wl = synth.make_workload("sb", seed=seed, batch=2, n_q_heads=4, n_kv_heads=2, window=24,
+                             n_blocks=[5, 4], ranks=[10], n_resid=12, top_k=3, sigma0=2.0,
+                             rope_base=1e6, permute_slots=True)
+    return synth.set_shared_basis(wl, group)
+
+
+def _materialised(pool):
+    p = {k: v for k, v in pool.items() if k != "basis_of"}
+    g = np.asarray(pool["basis_of"], dtype=np.int64)
+    p["vk"], p["vv"] = pool["vk"][g], pool["vv"][g]
+    return p
+
+
+def _decode(wl, pool, idx=None):
+    lay = wl.layers[0]
+    return oracle.decode(pool, lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks, wl.win_len,
+                         wl.n_kv_heads, wl.top_k, wl.scale, idx=idx)
+
+
+def test_runs_share_one_entry():
+    wl = _wl(31, group=2)
+    b = wl.layers[0].basis_of
+    for s in range(2):
+        t = wl.block_table[s, :wl.n_blocks[s]]
+        for j in range(0, len(t) - 1, 2):
+            assert b[t[j]] == b[t[j + 1]]
+        assert len({int(b[x]) for x in t}) == (len(t) + 1) // 2
+
+
+def test_shared_basis_equals_materialised_pool():
+    wl = _wl(32)
+    pool = wl.layers[0].pool()
+    mat = _materialised(pool)
+    for s in range(wl.n_slots):
+        for h in range(2):
+            np.testing.assert_array_equal(oracle.block_route_key(pool, s, h), oracle.block_route_key(mat, s, h))
+    o1, l1, i1 = _decode(wl, pool)
+    o2, l2, i2 = _decode(wl, mat)
+    assert np.array_equal(i1, i2)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    # the sharing map matters: reading each slot's own entry gives other keys
+    own = {k: v for k, v in pool.items() if k != "basis_of"}
+    o3, _, _ = _decode(wl, own, idx=i1)
+    assert np.abs(o3 - o1).max() > 1e-3
+
+
+def test_identity_map_changes_nothing():
+    wl = _wl(33)
+    pool = wl.layers[0].pool()
+    own = {k: v for k, v in pool.items() if k != "basis_of"}
+    ident = dict(own, basis_of=np.arange(wl.n_slots, dtype=np.int32))
+    o1, l1, _ = _decode(wl, own)
+    o2, l2, _ = _decode(wl, ident)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
