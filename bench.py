@@ -32,7 +32,8 @@ replay).  `traffic` is the committed rocprofv3 PMC summary for that kernel
 Beside the decode (not part of `value`): the same stack with its residual rows
 in the 8- and 4-bit formats (`quantised_residuals`), the same stack read as
 un-rotated pools whose keys are rotated to their absolute positions at read
-(`unrotated_pool`), and the write side,
+(`unrotated_pool`) and with pairs of blocks sharing one basis (`shared_basis`),
+and the write side,
 dkv_seal_blocks sealing one layer's 1008 blocks x 2 KV heads at each of the
 stack's ranks (`sealing`: block-heads per second and the fp32 arithmetic rate
 of its main products).
@@ -244,12 +245,13 @@ def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: i
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
-    fmt = {"Q8": 1, "Q4": 2, "U": 0}[variant]
+    fmt = {"Q8": 1, "Q4": 2, "U": 0, "UB": 0}[variant]
     alg = step_algorithmic_bytes(n_layers, fmt)
     log(f"{variant} variant, layer-batched: {ms:.4f} ms/step (graph); kernel {kern * 1e3:.1f} us; "
         f"{alg / 1e6:.1f} MB per step")
-    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16"}[variant],
-           "keys": "unrotated, rotated at read" if variant == "U" else "rotated", "ms_per_step": ms,
+    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16", "UB": "fp16"}[variant],
+           "keys": "unrotated, rotated at read" if variant in ("U", "UB") else "rotated",
+           "shared_basis": "pairs of consecutive blocks" if variant == "UB" else None, "ms_per_step": ms,
            "queries_per_s": 4 * n_layers / (ms * 1e-3), "algorithmic_bytes_per_step": alg,
            "kernel_us_per_launch": kern * 1e3, "achieved_GBps": alg / (kern * 1e-3) / 1e9}
     del run, pools, batches
@@ -678,6 +680,7 @@ def main() -> int:
     if not args.no_unrotated and args.mode != "per-layer":
         res["unrotated_pool"] = measure_variant(lib, synth, torch, np, "U", n_layers, args.steps, args.warmup,
                                                 log)
+        res["shared_basis"] = measure_variant(lib, synth, torch, np, "UB", n_layers, args.steps, args.warmup, log)
     if not args.no_sealing and args.mode != "per-layer":
         res["sealing"] = measure_sealing(lib, synth, torch, np, log)
     if not args.no_cpu_baseline:

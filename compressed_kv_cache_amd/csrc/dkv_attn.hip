@@ -86,6 +86,9 @@ struct PoolArgs {
   // absolute position; rope == nullptr for pools of rotated keys
   const float* rope;
   const int32_t* spos;
+  // shared basis (un-rotated pools only): the vk / vv entry of each slot, or nullptr
+  const int32_t* basis;
+  int n_basis;
 };
 
 struct BatchArgs {
@@ -350,8 +353,13 @@ __global__ __launch_bounds__(128) void k_route_keys_rot(PoolArgs P, const int32_
   __shared__ float vks[DKV_MAX_RANK * kD];
   const int r = P.rank;
   const int t = threadIdx.x, j = t & 63, half = t >> 6;
+  int g = slot;  // the entry holding the block's V_K
+  if (P.basis) {
+    g = P.basis[slot];
+    if (g < 0 || g >= P.n_basis) return;  // uniform over the workgroup
+  }
   const f16* U = P.u + slot * P.u_s + h * P.u_h;
-  const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
+  const f16* VK = P.vk + g * P.vk_s + h * P.vk_h;
   const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
   for (int c = 0; c < r; ++c) vks[c * kD + t] = (float)VK[c * kD + t];
   lds_barrier();
@@ -1190,9 +1198,18 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   const f16* exvs = nullptr;
   int slot = -1;
   int bpos = 0;  // un-rotated pools: absolute position of the block's token 0
+  int bslot = 0; // the vk / vv entry of the block (its slot unless the basis is shared)
   if (p < A.n_block_parts) {
     slot = get_slot();  // routed pool slot, or -1
     if (slot >= P.n_slots) slot = -1;
+    bslot = slot;
+    if constexpr (QK == 2) {
+      if (slot >= 0 && P.basis) {
+        const int g = P.basis[slot];
+        if (g < 0 || g >= P.n_basis) slot = -1;  // no basis: no rows
+        bslot = g;
+      }
+    }
     if (slot >= 0) {
       if constexpr (QK == 2) bpos = P.spos[slot];
       lr = (A.block_mode & 1) != 0;
@@ -1266,8 +1283,8 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   if constexpr (LR) {
     const f16* AK = P.ak + slot * P.ak_s + h * P.ak_h;
     const f16* AV = P.av + slot * P.av_s + h * P.av_h;
-    const f16* VK = P.vk + slot * P.vk_s + h * P.vk_h;
-    const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
+    const f16* VK = P.vk + bslot * P.vk_s + h * P.vk_h;
+    const f16* VV = P.vv + bslot * P.vv_s + h * P.vv_h;
     U = P.u + slot * P.u_s + h * P.u_h;
     {
       // positions 0 (none) for lanes past n_resid; a pool without residual rows
@@ -1495,7 +1512,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
         // the second tile, or (the largest ranks, short of registers) the last
         if (k == (NRQ >= 5 ? kLRTilesPerWave - 1 : 1)) {
           const f16* AV = P.av + slot * P.av_s + h * P.av_h;
-          const f16* VV = P.vv + slot * P.vv_s + h * P.vv_h;
+          const f16* VV = P.vv + bslot * P.vv_s + h * P.vv_h;
 #pragma unroll
           for (int c2 = 0; c2 < kVVChunks; ++c2) {
             const int c = tid + kAttThreads * c2;
@@ -2342,6 +2359,11 @@ dkv_status check_pool_shape(const dkv_pool* P) {
     if (P->resid_format != DKV_RESID_FP16)
       return fail(DKV_ERR_UNSUPPORTED, "un-rotated pools need fp16 residual rows");
   }
+  if (P->basis_of) {
+    if (!P->rope_freq) return fail(DKV_ERR_UNSUPPORTED, "a shared basis needs an un-rotated pool (rope_freq)");
+    if (P->n_basis < 1) return fail(DKV_ERR_INVALID_ARG, "n_basis %d < 1 with basis_of set", P->n_basis);
+    if (!al(P->basis_of, 4)) return fail(DKV_ERR_UNSUPPORTED, "basis_of must be 4-byte aligned");
+  }
   return DKV_OK;
 }
 
@@ -2432,6 +2454,8 @@ PoolArgs make_pool_args(const dkv_pool* P) {
   }
   a.rope = P->rope_freq;
   a.spos = P->rope_freq ? P->slot_pos : nullptr;
+  a.basis = P->rope_freq ? P->basis_of : nullptr;
+  a.n_basis = P->n_basis;
   return a;
 }
 

@@ -55,7 +55,8 @@ class PoolC(ctypes.Structure):
                 ("resid_k", View), ("resid_v", View), ("resid_pos", View), ("route_key", View),
                 ("resid_format", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("resid_k_sb", View), ("resid_v_sb", View),
-                ("rope_freq", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p)]
+                ("rope_freq", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p),
+                ("basis_of", ctypes.c_void_p), ("n_basis", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 RESID_FP16, RESID_INT8, RESID_INT4 = 0, 1, 2
 
@@ -261,7 +262,21 @@ class Pool:
             pool.tensors["_record"] = t["_record"]
         if arrays.get("rope_base") is not None:
             pool.set_unrotated(float(arrays["rope_base"]), arrays["slot_pos"])
+        if arrays.get("basis_of") is not None:
+            pool.set_shared_basis(arrays["basis_of"], int(arrays["vk"].shape[0]))
         return pool
+
+    def set_shared_basis(self, basis_of, n_basis: int) -> None:
+        """Let slot s read its V_K, V_V from entry basis_of[s] of vk / vv (an
+        un-rotated pool only).  basis_of: int32 [n_slots], numpy or a device tensor."""
+        import torch
+        dev = self.tensors["anchor_k"].device
+        b = basis_of if isinstance(basis_of, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(basis_of, dtype=np.int32))
+        b = b.to(device=dev, dtype=torch.int32).contiguous()
+        if b.numel() < self.n_slots:
+            raise ValueError(f"basis_of has {b.numel()} entries for {self.n_slots} slots")
+        self.tensors["basis_of"] = b
+        self.c.basis_of, self.c.n_basis = b.data_ptr(), int(n_basis)
 
     def set_unrotated(self, rope_base: float, slot_pos) -> None:
         """Read this pool as an un-rotated one: keys are rotated at read to the

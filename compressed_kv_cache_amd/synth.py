@@ -388,12 +388,17 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
     "", "S1" (sigma_j = 4 * 0.9^j) or "S2" (zero anchors) for config 0, or
     "Q8" / "Q4" (residual rows in the 8- or 4-bit group-quantised format) for
     configs 0, 1 and 2, or "U" (the same arrays read as an un-rotated pool with
-    rotary base ROPE_BASE) for any configuration."""
+    rotary base ROPE_BASE) for any configuration, or "UB" (the U variant with
+    pairs of consecutive blocks sharing one basis, a sharing fraction of 0.5)."""
     seed = 1000 + cfg if seed is None else seed
     if variant == "U":
         wl = make_config(cfg, seed, layers)
         wl.name += "_U"
         return set_unrotated(wl, ROPE_BASE)
+    if variant == "UB":
+        wl = make_config(cfg, seed, layers, "U")
+        wl.name += "B"
+        return set_shared_basis(wl, 2)
     if variant in ("Q8", "Q4"):
         fmt = RESID_INT8 if variant == "Q8" else RESID_INT4
         base = {0: dict(batch=1, n_q_heads=1, n_kv_heads=1, window=512, n_blocks=[14], ranks=[32],

@@ -133,6 +133,16 @@ typedef struct dkv_pool {
    *   slot_pos:  int32 [n_slots] device, positions in [0, 2^24 - 256]. */
   const float* rope_freq;
   const int32_t* slot_pos;
+  /* Shared basis (README "Key Environment Knobs", DKV_SHARED_BASIS and
+   * DKV_SHARED_BASIS_FRAC: blocks whose delta subspaces agree read one basis).
+   * NULL, or int32 [n_slots] device: the block in slot s reads its V_K and V_V
+   * from entry basis_of[s] of vk and vv (at their slot stride), n_basis entries;
+   * its anchors, U and residual rows stay in slot s.  Needs an un-rotated pool
+   * (the pages refuse sharing with rotated keys).  A block whose entry lies
+   * outside [0, n_basis) contributes no rows and its routing key is not written. */
+  const int32_t* basis_of;
+  int32_t n_basis;
+  int32_t reserved2;
 } dkv_pool;
 
 /* One decode step's batch: one new query token per sequence. */

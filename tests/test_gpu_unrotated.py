@@ -148,3 +148,41 @@ def test_decode_layers_unrotated(lib):
         assert torch.equal(res[l][2], i1)
         c = _oracle_check(wl, wl.layers[l], *res[l], wl.top_k)
         say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# Shared basis (blocks of an un-rotated pool reading one V_K, V_V entry)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,group", [(0, 2), (1, 2), (1, 4), (3, 3)])
+def test_decode_shared_basis(lib, cfg, group):
+    wl = synth.set_shared_basis(_u(cfg), group)
+    pool, _ = upload(lib, wl)
+    got = pool.route_key.cpu().numpy().astype(np.float64)
+    P = wl.layers[0].pool()
+    for s in range(0, got.shape[0], 7):
+        for h in range(got.shape[1]):
+            ref = oracle.block_route_key(P, s, h)
+            assert np.abs(got[s, h] - ref).max() <= 1e-5 * (np.abs(ref).max() + 1.0)
+    check_decode(lib, wl, label=f"shared basis, runs of {group}")
+
+
+def test_decode_layers_shared_basis(lib):
+    """Four layers of the un-rotated 64k batch-4 stack with pairs of blocks
+    sharing a basis, in one layer-batched launch."""
+    wl = synth.make_config(2, layers=[0, 9, 19, 27], variant="UB")
+    say("[decode layers UB] stack64k layers 0, 9, 19, 27")
+    pools, batches = [], []
+    for l in range(4):
+        p_, b_ = upload(lib, wl, l)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    res = _run_layers(lib, run, reps=2)
+    for l in range(4):
+        _, _, i1 = lib.decode(pools[l], batches[l], wl.top_k, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        c = _oracle_check(wl, wl.layers[l], *res[l], wl.top_k)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
