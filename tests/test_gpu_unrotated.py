@@ -186,3 +186,64 @@ def test_decode_layers_shared_basis(lib):
         assert torch.equal(res[l][2], i1)
         c = _oracle_check(wl, wl.layers[l], *res[l], wl.top_k)
         say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
+def test_decode_layers_unrotated_mixed_ranks(lib):
+    """Un-rotated layers of every low-rank tile count (ranks 1..64, 0..255
+    residual rows), ragged windows, an empty sequence and a shared basis in one
+    layer-batched launch."""
+    base = dict(batch=4, n_q_heads=6, n_kv_heads=2, window=48, n_blocks=[5, 0, 6, 3],
+                win_len=[48, 0, 17, 30], top_k=3, sigma0=2.0, rope_base=synth.ROPE_BASE)
+    specs = [dict(ranks=[1], n_resid=0), dict(ranks=[7], n_resid=20), dict(ranks=[24], n_resid=8),
+             dict(ranks=[40], n_resid=33), dict(ranks=[64], n_resid=4), dict(ranks=[15], n_resid=255)]
+    wls = [synth.make_workload(f"umix{i}", seed=600 + i, **base, **s) for i, s in enumerate(specs)]
+    synth.set_shared_basis(wls[2], 2)
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, 3, wls[0].scale)
+    assert run.plan.max_tiles >= 5 and run.plan.unrotated == 1
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        _, _, i1 = lib.decode(pools[l], batches[l], 3, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        _oracle_check(w, w.layers[0], *res[l], 3)
+
+
+def test_decode_layers_unrotated_graph_replays(lib):
+    """The un-rotated layer-batched launch captured in a graph replays to the
+    eager bits, with eager launches and synchronisations between replays."""
+    wl = synth.make_config(0, variant="UB")
+    pools, batches = [], []
+    for _ in range(3):
+        p_, b_ = upload(lib, wl)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    run.run()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), s.clone(), i.clone()) for o, s, i in zip(run.outs, run.lses, run.idxs)]
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        run.run(cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run.run(torch.cuda.current_stream())
+    for _ in range(3):
+        for o in run.outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (o, s, i) in enumerate(ref):
+            assert torch.equal(run.outs[l], o) and torch.equal(run.lses[l], s) and torch.equal(run.idxs[l], i)
+        run.run()
+        torch.cuda.synchronize()
+        assert torch.equal(run.outs[0], ref[0][0])
+    assert run.timeout_flag() == 0
+    _oracle_check(wl, wl.layers[0], *ref[0], wl.top_k)
