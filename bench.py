@@ -409,7 +409,7 @@ def main() -> int:
         return pmc_summary(args)
 
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print(f"bench.py runs on exactly one GPU: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         return 2
 
