@@ -138,3 +138,21 @@ def reconstruct(sealed: dict):
     k[pos] = np.asarray(sealed["resid_k"], np.float64)
     v[pos] = np.asarray(sealed["resid_v"], np.float64)
     return k, v
+
+
+def join_basis(u, vk, vv, vk_g, vv_g):
+    """Join a block to a shared basis (README "Key Environment Knobs",
+    DKV_SHARED_BASIS: blocks read one basis row instead of each storing its own
+    V; a join keeps the part of the block's delta that lies in the shared
+    subspace).  With V = [V_K | V_V] and V_g = [V_K,g | V_V,g] (r x 256, rows
+    orthonormal for a basis written by the sealer): M = V V_g^T, U' = U M, so
+    that U' V_g is the projection of the block's delta U V onto the rows of V_g.
+    The retained energy is |U' V_g|^2 / |U V|^2 (1 when the subspaces agree).
+    Returns (U' [255 x r], retained energy), float64."""
+    U = np.asarray(u, np.float64)
+    V = np.hstack([np.asarray(vk, np.float64), np.asarray(vv, np.float64)])
+    Vg = np.hstack([np.asarray(vk_g, np.float64), np.asarray(vv_g, np.float64)])
+    up = U @ (V @ Vg.T)
+    num = np.sum((up @ Vg) ** 2)
+    den = np.sum((U @ V) ** 2)
+    return up, (num / den if den > 0 else 1.0)

@@ -137,3 +137,37 @@ def test_reconstruction_error_matches_the_truncation(rank):
     err = np.sum((x - np.hstack([rk, rv])) ** 2)
     opt = np.sum(sig[rank:] ** 2)
     assert opt <= err <= 1.02 * opt + 1e-3 * np.sum(a ** 2) * 1e-3
+
+
+def _orth_rows(rng, r, n=256):
+    q, _ = np.linalg.qr(rng.standard_normal((n, r)))
+    return q.T
+
+
+def test_join_to_own_or_rotated_basis_keeps_everything():
+    rng = np.random.default_rng(21)
+    V = _orth_rows(rng, 12)
+    U = rng.standard_normal((255, 12))
+    up, e = S.join_basis(U, V[:, :128], V[:, 128:], V[:, :128], V[:, 128:])
+    np.testing.assert_allclose(up, U, atol=1e-12)
+    assert abs(e - 1.0) < 1e-12
+    Q, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    Vg = Q @ V                                    # another basis of the same subspace
+    up, e = S.join_basis(U, V[:, :128], V[:, 128:], Vg[:, :128], Vg[:, 128:])
+    np.testing.assert_allclose(up @ Vg, U @ V, atol=1e-11)
+    assert abs(e - 1.0) < 1e-12
+
+
+def test_join_is_the_least_squares_projection():
+    rng = np.random.default_rng(22)
+    V, Vg = _orth_rows(rng, 10), _orth_rows(rng, 10)
+    U = rng.standard_normal((255, 10))
+    up, e = S.join_basis(U, V[:, :128], V[:, 128:], Vg[:, :128], Vg[:, 128:])
+    # the best X with X Vg ~ U V in the least-squares sense (numpy's solver)
+    X = np.linalg.lstsq(Vg.T, (U @ V).T, rcond=None)[0].T
+    np.testing.assert_allclose(up, X, atol=1e-10)
+    # orthogonal subspaces keep nothing; random ones about r / 256 of the energy
+    W = _orth_rows(rng, 20)
+    up0, e0 = S.join_basis(U, W[:10, :128], W[:10, 128:], W[10:, :128], W[10:, 128:])
+    assert np.abs(up0).max() < 1e-12 and e0 < 1e-24
+    assert 0.0 < e < 0.2
