@@ -546,7 +546,117 @@ dkv_status launch_seal(const SealArgs& a, unsigned grid, hipStream_t st) {
   return DKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Joining blocks to a shared basis: for block slot s (current basis entry
+// cur) and target entry g, with V = [V_K | V_V] rows of the entries,
+//   M = V_cur V_g^T (r x r),  U' = U M,
+//   retained energy = |U' V_g|^2 / |U V_cur|^2 = tr(C M G_g M^T) / tr(C G_cur),
+// C = U^T U, G = V V^T.  One workgroup per (item, KV head); all products fp32
+// from the fp16 arrays staged in LDS; U' is written back to slot s as fp16.
+// ---------------------------------------------------------------------------
+
+struct JoinArgs {
+  f16* u; int64_t u_s, u_h;
+  const f16* vk; int64_t vk_s, vk_h;
+  const f16* vv; int64_t vv_s, vv_h;
+  const int32_t* slots;
+  const int32_t* entries;
+  const int32_t* basis_of;
+  int n_heads, n_slots, n_entries, rank, write;
+  float* energy;
+};
+
+constexpr int kJoinThreads = 256;
+constexpr int kJoinR = DKV_MAX_RANK;
+// Vc, Vg [64][256] f16; Us [255][64] f16 (later T [64][64] fp32); M, C, Gg [64][64] fp32; 8 partial sums
+constexpr int kJoinLds = 2 * kJoinR * 256 * 2 + 255 * kJoinR * 2 + 3 * kJoinR * kJoinR * 4 + 64;
+static_assert(255 * kJoinR * 2 >= kJoinR * kJoinR * 4, "T must fit the U area");
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int k = 0; k < kJoinThreads / 64; ++k) t += red[k];
+  return t;
+}
+
+__global__ __launch_bounds__(kJoinThreads) void k_join(JoinArgs a) {
+  extern __shared__ __align__(16) unsigned char jsm[];
+  f16* Vc = reinterpret_cast<f16*>(jsm);
+  f16* Vg = Vc + kJoinR * 256;
+  f16* Us = Vg + kJoinR * 256;
+  float* M = reinterpret_cast<float*>(Us + 255 * kJoinR);
+  float* C = M + kJoinR * kJoinR;
+  float* Gg = C + kJoinR * kJoinR;
+  float* red = Gg + kJoinR * kJoinR;
+  float* T = reinterpret_cast<float*>(Us);
+  const int item = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
+  const int t = threadIdx.x, r = a.rank;
+  const int s = a.slots[item], g = a.entries[item];
+  const int cur = (s >= 0 && s < a.n_slots) ? (a.basis_of ? a.basis_of[s] : s) : -1;
+  if (s < 0 || s >= a.n_slots || g < 0 || g >= a.n_entries || cur < 0 || cur >= a.n_entries) {
+    if (t == 0) a.energy[blockIdx.x] = -1.f;  // uniform: nothing joined
+    return;
+  }
+  for (int e = t; e < r * 256; e += kJoinThreads) {
+    const int j = e >> 8, c = e & 255;
+    Vc[j * 256 + c] = c < 128 ? a.vk[cur * a.vk_s + h * a.vk_h + j * 128 + c]
+                              : a.vv[cur * a.vv_s + h * a.vv_h + j * 128 + (c - 128)];
+    Vg[j * 256 + c] = c < 128 ? a.vk[g * a.vk_s + h * a.vk_h + j * 128 + c]
+                              : a.vv[g * a.vv_s + h * a.vv_h + j * 128 + (c - 128)];
+  }
+  f16* U = a.u + s * a.u_s + h * a.u_h;
+  for (int e = t; e < 255 * r; e += kJoinThreads) Us[e] = U[e];
+  __syncthreads();
+  float eo = 0.f;
+  for (int e = t; e < r * r; e += kJoinThreads) {
+    const int i = e / r, j = e % r;
+    float c = 0.f, m = 0.f, gc = 0.f, gg = 0.f;
+    for (int k = 0; k < 255; ++k) c = __builtin_fmaf((float)Us[k * r + i], (float)Us[k * r + j], c);
+    for (int k = 0; k < 256; ++k) {
+      const float vi = (float)Vc[i * 256 + k], gi = (float)Vg[i * 256 + k];
+      m = __builtin_fmaf(vi, (float)Vg[j * 256 + k], m);
+      gc = __builtin_fmaf(vi, (float)Vc[j * 256 + k], gc);
+      gg = __builtin_fmaf(gi, (float)Vg[j * 256 + k], gg);
+    }
+    C[e] = c;
+    M[e] = m;
+    Gg[e] = gg;
+    eo = __builtin_fmaf(c, gc, eo);
+  }
+  __syncthreads();
+  if (t < 255) {
+    for (int j = 0; j < r; ++j) {
+      float acc = 0.f;
+      for (int i = 0; i < r; ++i) acc = __builtin_fmaf((float)Us[t * r + i], M[i * r + j], acc);
+      if (a.write) U[t * r + j] = (f16)acc;
+    }
+  }
+  __syncthreads();  // every thread is done with Us: T takes its place
+  for (int e = t; e < r * r; e += kJoinThreads) {
+    const int i = e / r, j = e % r;
+    float acc = 0.f;
+    for (int k = 0; k < r; ++k) acc = __builtin_fmaf(M[i * r + k], Gg[k * r + j], acc);
+    T[e] = acc;
+  }
+  __syncthreads();
+  float en = 0.f;
+  for (int e = t; e < r * r; e += kJoinThreads) {
+    const int i = e / r, j = e % r;
+    float q = 0.f;
+    for (int k = 0; k < r; ++k) q = __builtin_fmaf(T[i * r + k], M[j * r + k], q);
+    en = __builtin_fmaf(C[e], q, en);
+  }
+  const float so = block_sum(eo, red);
+  const float sn = block_sum(en, red + 4);
+  if (t == 0) a.energy[blockIdx.x] = so > 0.f ? sn / so : 1.f;
+}
+
 static_assert(Lay<kMaxWidth>::bytes <= 160 * 1024, "sealer LDS exceeds 160 KB");
+static_assert(kJoinLds <= 160 * 1024, "join LDS exceeds 160 KB");
 static_assert(Lay<16>::SS >= 1, "padded width");
 
 }  // namespace
@@ -623,6 +733,52 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
     s = launch_seal<80>(a, g, st);
   if (s != DKV_OK) return s;
   if (P->route_key.ptr) return dkv_route_keys(P, slots, n_blocks, stream);
+  return DKV_OK;
+}
+
+dkv_status dkv_join_basis(const dkv_pool* pool, const int32_t* slots, const int32_t* entries, int32_t n,
+                          int32_t write, float* energy, void* stream) {
+  dkv_clear_error_message();
+  const dkv_pool* P = pool;
+  if (!P) return fail(DKV_ERR_INVALID_ARG, "pool is NULL");
+  if (P->head_dim != DKV_HEAD_DIM) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d != 128", P->head_dim);
+  if (P->rank < 1) return fail(DKV_ERR_INVALID_ARG, "rank %d < 1", P->rank);
+  if (P->rank > DKV_MAX_RANK) return fail(DKV_ERR_UNSUPPORTED, "rank %d > 64", P->rank);
+  if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
+  if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
+  if (P->basis_of && P->n_basis < 1) return fail(DKV_ERR_INVALID_ARG, "n_basis %d < 1 with basis_of set", P->n_basis);
+  if (n < 0) return fail(DKV_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n == 0) return DKV_OK;
+  if (!slots || !entries || !energy) return fail(DKV_ERR_INVALID_ARG, "slots / entries / energy is NULL");
+  if (!al(slots, 4) || !al(entries, 4) || !al(energy, 4) || (P->basis_of && !al(P->basis_of, 4)))
+    return fail(DKV_ERR_UNSUPPORTED, "slots, entries, energy and basis_of must be 4-byte aligned");
+  dkv_status s;
+  if ((s = check_out(P->u, "u", 2, 2)) || (s = check_out(P->vk, "vk", 2, 2)) || (s = check_out(P->vv, "vv", 2, 2)))
+    return s;
+  const int64_t grid = (int64_t)n * P->n_kv_heads;
+  if (grid > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many blocks");
+  JoinArgs a;
+  a.u = (f16*)P->u.ptr; a.u_s = P->u.slot_stride; a.u_h = P->u.head_stride;
+  a.vk = (const f16*)P->vk.ptr; a.vk_s = P->vk.slot_stride; a.vk_h = P->vk.head_stride;
+  a.vv = (const f16*)P->vv.ptr; a.vv_s = P->vv.slot_stride; a.vv_h = P->vv.head_stride;
+  a.slots = slots;
+  a.entries = entries;
+  a.basis_of = P->basis_of;
+  a.n_heads = P->n_kv_heads;
+  a.n_slots = P->n_slots;
+  a.n_entries = P->basis_of ? P->n_basis : P->n_slots;
+  a.rank = P->rank;
+  a.write = write ? 1 : 0;
+  a.energy = energy;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_join, hipFuncAttributeMaxDynamicSharedMemorySize, kJoinLds) != hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_join) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_join, dim3((unsigned)grid), dim3(kJoinThreads), kJoinLds, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_join launch failed: %s", hipGetErrorString(e));
   return DKV_OK;
 }
 

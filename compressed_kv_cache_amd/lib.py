@@ -33,7 +33,7 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
             "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
-            "dkv_seal_blocks", "dkv_rope_freqs")
+            "dkv_seal_blocks", "dkv_rope_freqs", "dkv_join_basis")
 
 
 class DKVError(RuntimeError):
@@ -103,6 +103,8 @@ def load(path: str = LIB_PATH):
     lib.dkv_route_keys.restype = i32
     lib.dkv_rope_freqs.argtypes = [ctypes.c_double, i32, vp]
     lib.dkv_rope_freqs.restype = i32
+    lib.dkv_join_basis.argtypes = [P, vp, vp, i32, i32, vp, vp]
+    lib.dkv_join_basis.restype = i32
     lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
     lib.dkv_gather_route_keys.argtypes = [P, Bp, vp, vp]
     lib.dkv_decode_layers_table_size.argtypes = [i32]
@@ -383,6 +385,22 @@ def seal_blocks(pool: Pool, k, v, slots, omega, power_iters: int = 2, stream=Non
     n = int(k.shape[0])
     _check(lib.dkv_seal_blocks(ctypes.byref(pool.c), _view(k, 2), _view(v, 2), _ptr(slots), n, _ptr(omega),
                                int(omega.shape[1]), int(power_iters), _stream(stream)), "dkv_seal_blocks")
+
+
+def join_basis(pool: Pool, slots, entries, write: bool = True, stream=None):
+    """Join the blocks in `slots` to the basis entries `entries` (dkv_join_basis):
+    U' = U V V_g^T written in place when `write`; returns the retained energies,
+    fp32 [n][Hkv] on the device.  slots, entries: int32 [n] device tensors."""
+    import torch
+    lib = load()
+    if slots.dtype != torch.int32 or entries.dtype != torch.int32 or slots.numel() != entries.numel() \
+            or not slots.is_contiguous() or not entries.is_contiguous():
+        raise ValueError("slots and entries must be contiguous int32 tensors of one length")
+    n = int(slots.numel())
+    energy = torch.empty((n, pool.n_kv_heads), dtype=torch.float32, device=slots.device)
+    _check(lib.dkv_join_basis(ctypes.byref(pool.c), _ptr(slots), _ptr(entries), n,
+                              1 if write else 0, _ptr(energy), _stream(stream)), "dkv_join_basis")
+    return energy
 
 
 def route_keys(pool: Pool, slots=None, stream=None) -> None:

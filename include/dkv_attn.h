@@ -377,6 +377,24 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
                            int32_t n_blocks, const float* omega, int32_t width, int32_t power_iters,
                            void* stream);
 
+/* Join blocks to a shared basis: the write side of DKV_SHARED_BASIS (README
+ * "Key Environment Knobs": blocks whose delta subspaces agree read one basis;
+ * joins report the retained delta energy).  For item i, block slot s =
+ * slots[i] (current basis entry cur = basis_of[s], or s without sharing) and
+ * target entry g = entries[i], per KV head h, with V = [V_K | V_V]:
+ *   M = V_cur V_g^T (r x r),  U' = U M  (U' V_g is the least-squares
+ *   projection of the block's delta U V_cur onto the rows of V_g),
+ *   energy[i * n_kv_heads + h] = |U' V_g|^2 / |U V_cur|^2,
+ * fp32 from the fp16 arrays.  write != 0 stores U' into slot s's U (fp16, round
+ * to nearest even); write = 0 only scores the candidate.  The caller then sets
+ * basis_of[s] = g (its own array) and recomputes the routing key
+ * (dkv_route_keys).  Entries index vk / vv: [0, n_basis) with basis_of set,
+ * else [0, n_slots).  An item with a slot or entry out of range writes energy
+ * -1 and changes nothing.  Slots of one call must be distinct.
+ *   slots, entries: int32 [n] device;  energy: fp32 [n][n_kv_heads] device out. */
+dkv_status dkv_join_basis(const dkv_pool* pool, const int32_t* slots, const int32_t* entries, int32_t n,
+                          int32_t write, float* energy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -227,3 +227,40 @@ def test_seal_full_layer_sampled(lib):
         for h in range(H):
             ref = S.seal_block(inp.k[b, h], inp.v[b, h], rank, R, om, 2)
             _compare_block(out, b, h, inp.k[b, h], inp.v[b, h], ref, rank, R)
+
+
+@pytest.mark.parametrize("variant", ["U", "UB"])
+def test_join_basis(lib, variant):
+    """dkv_join_basis against the oracle's join: U' = U V_cur V_g^T and the
+    retained energy, scored first without writing, then written; an item out of
+    range changes nothing."""
+    from compressed_kv_cache_amd import synth
+    wl = synth.make_config(1, variant=variant)
+    lay = wl.layers[0]
+    P = lay.pool()
+    pool = lib.Pool.from_numpy(P, DEV)
+    n_entries = P["vk"].shape[0]
+    slots = np.array([0, 1, 2, 3, 4, 5, 6], dtype=np.int32)
+    entries = np.array([7, 9, 2, 11, 13, 20, n_entries], dtype=np.int32)   # the last one is out of range
+    ts, te = torch.from_numpy(slots).to(DEV), torch.from_numpy(entries).to(DEV)
+    u0 = pool.tensors["u"].clone()
+    e0 = lib.join_basis(pool, ts, te, write=False)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.tensors["u"], u0)
+    e1 = lib.join_basis(pool, ts, te, write=True)
+    torch.cuda.synchronize()
+    assert torch.equal(e0, e1)
+    e1 = e1.cpu().numpy()
+    u1 = pool.tensors["u"].cpu().numpy()
+    for i, (s, g) in enumerate(zip(slots, entries)):
+        for h in range(wl.n_kv_heads):
+            if g >= n_entries:
+                assert e1[i, h] == -1.0
+                assert np.array_equal(u1[s, h], u0[s, h].cpu().numpy())
+                continue
+            cur = int(P["basis_of"][s]) if "basis_of" in P else int(s)
+            ref_u, ref_e = S.join_basis(P["u"][s, h], P["vk"][cur, h], P["vv"][cur, h], P["vk"][g, h],
+                                                 P["vv"][g, h])
+            got = u1[s, h].astype(np.float64)
+            assert np.all(np.abs(got - ref_u) <= 1e-3 * np.abs(ref_u) + 1e-5 * np.abs(ref_u).max()), (i, h)
+            assert abs(e1[i, h] - ref_e) <= 1e-4, (i, h, e1[i, h], ref_e)

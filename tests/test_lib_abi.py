@@ -260,3 +260,18 @@ def test_layer_batched_rejects_mixed_rotation(clib):
     st = clib.dkv_decode_layers_prepare(PA, BA, 2, 4, 0.088, outs, outs, None, FAKE, tsz, FAKE, need,
                                         ctypes.byref(plan))
     assert st == L.DKV_ERR_UNSUPPORTED and "rotated" in clib.dkv_last_error().decode()
+
+
+def test_join_basis_validates(clib):
+    p = _pool()
+    P = ctypes.byref(p)
+    assert clib.dkv_join_basis(None, FAKE, FAKE, 1, 1, FAKE, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_join_basis(P, FAKE, FAKE, -1, 1, FAKE, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_join_basis(P, FAKE, FAKE, 0, 1, FAKE, None) == L.DKV_OK          # nothing to do
+    assert clib.dkv_join_basis(P, None, FAKE, 2, 1, FAKE, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_join_basis(P, FAKE, FAKE, 2, 1, None, None) == L.DKV_ERR_INVALID_ARG
+    assert clib.dkv_join_basis(P, FAKE + 2, FAKE, 2, 1, FAKE, None) == L.DKV_ERR_UNSUPPORTED
+    q = _pool(rank=65)
+    assert clib.dkv_join_basis(ctypes.byref(q), FAKE, FAKE, 2, 1, FAKE, None) == L.DKV_ERR_UNSUPPORTED
+    q = _pool(basis_of=FAKE, n_basis=0)
+    assert clib.dkv_join_basis(ctypes.byref(q), FAKE, FAKE, 2, 1, FAKE, None) == L.DKV_ERR_INVALID_ARG
