@@ -190,6 +190,35 @@ def measure_sealing(lib, synth, torch, np, log, repeats: int = 3, power_iters: i
     return out
 
 
+def measure_joins(lib, synth, torch, np, log, repeats: int = 3):
+    """dkv_join_basis scoring every block of one un-rotated layer of the 64k
+    batch-4 stack (rank 48, 1008 blocks x 2 KV heads) against the basis of its
+    neighbour (the candidate evaluation of a join; no write), timed with events."""
+    dev = torch.device("cuda:0")
+    wl = synth.make_config(2, layers=[9], variant="U")
+    pool = lib.Pool.from_numpy(wl.layers[0].pool(), dev)
+    n = wl.n_slots
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    entries = (slots ^ 1).clamp(max=n - 1).contiguous()
+    lib.join_basis(pool, slots, entries, write=False)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(repeats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.join_basis(pool, slots, entries, write=False)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    items = n * wl.n_kv_heads
+    log(f"joins (scored) rank {wl.layers[0].rank}: {ms:.3f} ms for {items} block-heads")
+    del pool
+    torch.cuda.empty_cache()
+    return {"rank": wl.layers[0].rank, "block_heads": items, "ms": ms, "block_heads_per_s": items / (ms * 1e-3)}
+
+
 def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
     """The same 64k batch-4 stack with its residual rows stored in the 8- or
     4-bit group-quantised format (variant "Q8" / "Q4"), or read as un-rotated
@@ -681,6 +710,7 @@ def main() -> int:
         res["unrotated_pool"] = measure_variant(lib, synth, torch, np, "U", n_layers, args.steps, args.warmup,
                                                 log)
         res["shared_basis"] = measure_variant(lib, synth, torch, np, "UB", n_layers, args.steps, args.warmup, log)
+        res["shared_basis"]["joins"] = measure_joins(lib, synth, torch, np, log)
     if not args.no_sealing and args.mode != "per-layer":
         res["sealing"] = measure_sealing(lib, synth, torch, np, log)
     if not args.no_cpu_baseline:
