@@ -986,11 +986,56 @@ __device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_
 
 // One softmax step over two quantised 16-row tiles (b optional).  Q0, Q1: this
 // lane's head's query sums over dimensions 0..63 and 64..127.
-template <int NQ, int BITS, class Next = NoNext>
+// ROTK (un-rotated pools): each lane's own key row is dequantised, rotated to
+// the block's angle t0 (fq + 64) plus its in-block offset (off_a / off_b) times
+// theta_j / 2 pi (fq), rounded once to fp16 and scored; values are as below.
+template <int NQ, int BITS, bool ROTK = false, class Next = NoNext>
 __device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const QTile<BITS>& A, const QTile<BITS>& Bq,
                                              int rows_a, int rows_b, bool has_b, const v4h (&qf)[4][2], float Q0,
                                              float Q1, float scale, f16* Va, f16* Vb, int l16, int q4,
-                                             Next&& next = Next()) {
+                                             Next&& next = Next(), const float* fq = nullptr, float off_a = 0.f,
+                                             float off_b = 0.f) {
+  // the lane's own row l16: its (scale, bias) pairs are held, as row 4 q4' + e',
+  // by the lanes of q4' = l16 / 4
+  auto rot_scores = [&](const QTile<BITS>& T, float (&z)[4], int rows, float off) {
+    uint32_t sx[4], sy[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sx[e] = (uint32_t)__shfl((int)T.ksb[e].x, 16 * (l16 >> 2));
+      sy[e] = (uint32_t)__shfl((int)T.ksb[e].y, 16 * (l16 >> 2));
+    }
+    const int ee = l16 & 3;
+    const uint32_t mx = ee == 0 ? sx[0] : (ee == 1 ? sx[1] : (ee == 2 ? sx[2] : sx[3]));
+    const uint32_t my = ee == 0 ? sy[0] : (ee == 1 ? sy[1] : (ee == 2 ? sy[2] : sy[3]));
+    const float s0 = h_lo(mx), b0 = h_hi(mx), s1 = h_lo(my), b1 = h_hi(my);
+    v4f S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {  // dimension groups s2 (< 64) and s2 + 2 (>= 64), the rotation's pairs
+      const v8h ka = codes_to_h8<BITS>(T.kc[s2]);
+      const v8h kb = codes_to_h8<BITS>(T.kc[s2 + 2]);
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const int f0 = 32 * s2 + 8 * q4 + 4 * h4;
+        const float4 fh = *reinterpret_cast<const float4*>(fq + f0);
+        const float4 t0 = *reinterpret_cast<const float4*>(fq + 64 + f0);
+        const float fhs[4] = {fh.x, fh.y, fh.z, fh.w}, t0s[4] = {t0.x, t0.y, t0.z, t0.w};
+        float xa[4], xb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float cs, sn;
+          rope_cs_off(off, fhs[e], t0s[e], cs, sn);
+          const float a0 = __builtin_fmaf(s0, (float)ka[4 * h4 + e], b0);
+          const float c0 = __builtin_fmaf(s1, (float)kb[4 * h4 + e], b1);
+          xa[e] = a0 * cs - c0 * sn;
+          xb[e] = c0 * cs + a0 * sn;
+        }
+        S = mfma16(to_h4(xa), qf[s2][h4], S);
+        S = mfma16(to_h4(xb), qf[s2 + 2][h4], S);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = (4 * q4 + e < rows) ? S[e] * scale : -INFINITY;
+  };
   // scores per group: rows of the S layout are 4 q4 + e, heads l16
   auto scores = [&](const QTile<BITS>& T, float (&z)[4], int rows) {
     v4f S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
@@ -1013,9 +1058,9 @@ __device__ __forceinline__ void exact_pair_q(ExState& st, v4f (&Wt)[NQ], const Q
     }
   };
   float za[4], zb[4];
-  scores(A, za, rows_a);
+  if constexpr (ROTK) rot_scores(A, za, rows_a, off_a); else scores(A, za, rows_a);
   if (has_b) {
-    scores(Bq, zb, rows_b);
+    if constexpr (ROTK) rot_scores(Bq, zb, rows_b, off_b); else scores(Bq, zb, rows_b);
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) zb[e] = -INFINITY;
@@ -1166,7 +1211,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   // ---- window tiles owned by a routed-block part: exact rows that do not
   //      depend on the routing, attended while it may still be running
   bool any = false;
-  if (QK != 2 && p < A.n_block_parts && A.win_tile_stride > 0) {
+  if (QK < 2 && p < A.n_block_parts && A.win_tile_stride > 0) {
     const int n_wt = (wl + 15) >> 4;
     any = p < n_wt;  // uniform
     f16* Va = reinterpret_cast<f16*>(my);
@@ -1203,7 +1248,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     slot = get_slot();  // routed pool slot, or -1
     if (slot >= P.n_slots) slot = -1;
     bslot = slot;
-    if constexpr (QK == 2) {
+    if constexpr (QK >= 2) {
       if (slot >= 0 && P.basis) {
         const int g = P.basis[slot];
         if (g < 0 || g >= P.n_basis) slot = -1;  // no basis: no rows
@@ -1211,7 +1256,7 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
       }
     }
     if (slot >= 0) {
-      if constexpr (QK == 2) bpos = P.spos[slot];
+      if constexpr (QK >= 2) bpos = P.spos[slot];
       lr = (A.block_mode & 1) != 0;
       if ((A.block_mode & 2) && P.n_resid > 0) {
         n_ex = P.n_resid;
@@ -1254,10 +1299,10 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
   auto body = [&](auto lr_tag, auto bits_tag) {
   constexpr bool LR = decltype(lr_tag)::value && NRQ > 0;
   constexpr int QB = decltype(bits_tag)::value;  // 0: fp16 exact rows; 8 / 4: quantised residual rows
-  // QK == 2: an un-rotated pool, whose block keys are rotated to their
+  // QK == 2 / 3: an un-rotated pool (fp16 / quantised residual rows), whose block keys are rotated to their
   // absolute positions here; the frequency table sits in the statistics area
   // until the final phase
-  constexpr bool ROT = QK == 2;
+  constexpr bool ROT = QK == 2 || QK == 3;
   const int ntile = (n_ex + 15) >> 4;
   const int r = P.rank;
   float* fq = wstat;  // ROT: theta_j / (2 pi) [64], then the block's angles in turns [64]
@@ -1578,14 +1623,31 @@ __device__ __forceinline__ void attend_part(const PoolArgs& P, const BatchArgs& 
     }
     Q0 = q4_sum(Q0);
     Q1 = q4_sum(Q1);
+    // un-rotated pools: the in-block position of the lane's residual row
+    auto row_off = [&](int tile) -> float {
+      if constexpr (ROT) {
+        const int row = 16 * tile + l16;
+        int rpos;
+        if constexpr (LR) {
+          const int k4 = tile >> 2;
+          const int src = k4 == 0 ? ps[0] : (k4 == 1 ? ps[1] : (k4 == 2 ? ps[2] : ps[3]));
+          rpos = __shfl(src, 16 * (tile & 3) + l16);
+        } else {
+          rpos = row < n_ex ? (int)P.rp[slot * P.rp_s + h * P.rp_h + row] : 0;
+        }
+        return (float)(row < n_ex ? rpos : 0);
+      } else {
+        return 0.f;
+      }
+    };
     while (ta < ntile) {
       const bool has_b = tb < ntile;  // uniform over the wave
       const int ta_n = ta + 2 * kAttWaves, tb_n = tb + 2 * kAttWaves;
-      exact_pair_q<NQ, (QB == 4 ? 4 : 8)>(st, Wt, qta, qtb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, Q0, Q1,
-                                          scale, Va, Vb, l16, q4, [&]() {
+      exact_pair_q<NQ, (QB == 4 ? 4 : 8), ROT>(st, Wt, qta, qtb, n_ex - 16 * ta, n_ex - 16 * tb, has_b, qf, Q0, Q1,
+                                               scale, Va, Vb, l16, q4, [&]() {
         if (ta_n < ntile) load_qtile<(QB == 4 ? 4 : 8)>(exkq, exvq, exks, exvs, ta_n, ntile, n_ex, qta, l16, q4);
         if (tb_n < ntile) load_qtile<(QB == 4 ? 4 : 8)>(exkq, exvq, exks, exvs, tb_n, ntile, n_ex, qtb, l16, q4);
-      });
+      }, fq, row_off(ta), row_off(tb));
       ta = ta_n;
       tb = tb_n;
     }
@@ -2356,8 +2418,6 @@ dkv_status check_pool_shape(const dkv_pool* P) {
     if (!P->slot_pos) return fail(DKV_ERR_INVALID_ARG, "un-rotated pool (rope_freq set) without slot_pos");
     if (!al(P->rope_freq, 16) || !al(P->slot_pos, 4))
       return fail(DKV_ERR_UNSUPPORTED, "rope_freq must be 16-byte and slot_pos 4-byte aligned");
-    if (P->resid_format != DKV_RESID_FP16)
-      return fail(DKV_ERR_UNSUPPORTED, "un-rotated pools need fp16 residual rows");
   }
   if (P->basis_of) {
     if (!P->rope_freq) return fail(DKV_ERR_UNSUPPORTED, "a shared basis needs an un-rotated pool (rope_freq)");
@@ -2525,7 +2585,9 @@ dkv_status launch_decode_nrq_q(size_t shm, hipStream_t st, const dkv_pool* P, co
 
 template <int NRQ>
 dkv_status launch_decode_nrq(size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B, const DecodeArgs& D) {
-  if (P->rope_freq) return launch_decode_nrq_q<NRQ, 2>(shm, st, P, B, D);
+  if (P->rope_freq)
+    return P->resid_format == DKV_RESID_FP16 ? launch_decode_nrq_q<NRQ, 2>(shm, st, P, B, D)
+                                             : launch_decode_nrq_q<NRQ, 3>(shm, st, P, B, D);
   return P->resid_format == DKV_RESID_FP16 ? launch_decode_nrq_q<NRQ, 0>(shm, st, P, B, D)
                                            : launch_decode_nrq_q<NRQ, 1>(shm, st, P, B, D);
 }
@@ -2548,7 +2610,9 @@ dkv_status launch_attend_nrq_q(int64_t items, size_t shm, hipStream_t st, const 
 template <int NRQ>
 dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dkv_pool* P, const dkv_batch* B,
                              const AttnArgs& a) {
-  if (P->rope_freq) return launch_attend_nrq_q<NRQ, 2>(items, shm, st, P, B, a);
+  if (P->rope_freq)
+    return P->resid_format == DKV_RESID_FP16 ? launch_attend_nrq_q<NRQ, 2>(items, shm, st, P, B, a)
+                                             : launch_attend_nrq_q<NRQ, 3>(items, shm, st, P, B, a);
   return P->resid_format == DKV_RESID_FP16 ? launch_attend_nrq_q<NRQ, 0>(items, shm, st, P, B, a)
                                            : launch_attend_nrq_q<NRQ, 1>(items, shm, st, P, B, a);
 }
@@ -2712,7 +2776,7 @@ static dkv_status launch_layers_q(const dkv_layers_plan* plan, const LayersArgs&
 
 template <int NMAX>
 static dkv_status launch_layers(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
-  if (plan->unrotated) return launch_layers_q<NMAX, 2>(plan, L, st);
+  if (plan->unrotated) return plan->quantised ? launch_layers_q<NMAX, 3>(plan, L, st) : launch_layers_q<NMAX, 2>(plan, L, st);
   return plan->quantised ? launch_layers_q<NMAX, 1>(plan, L, st) : launch_layers_q<NMAX, 0>(plan, L, st);
 }
 

@@ -127,7 +127,7 @@ typedef struct dkv_pool {
    *   x'_j = x_j cos - x_{j+64} sin,   x'_{j+64} = x_{j+64} cos + x_j sin.
    * Values, the queries and the dense window are never rotated by the library
    * (the queries and window keys arrive rotated).  NULL rope_freq: the pool
-   * holds rotated keys (the default).  Un-rotated pools need fp16 residual rows.
+   * holds rotated keys (the default).  Residual rows may be fp16 or quantised.
    *   rope_freq: fp32 [2][64] device, theta_j / (2 pi) as an unevaluated sum
    *              row0[j] + row1[j] of two floats (dkv_rope_freqs fills it);
    *   slot_pos:  int32 [n_slots] device, positions in [0, 2^24 - 256]. */

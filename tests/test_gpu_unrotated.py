@@ -247,3 +247,45 @@ def test_decode_layers_unrotated_graph_replays(lib):
         assert torch.equal(run.outs[0], ref[0][0])
     assert run.timeout_flag() == 0
     _oracle_check(wl, wl.layers[0], *ref[0], wl.top_k)
+
+
+# ---------------------------------------------------------------------------
+# Un-rotated pools with 8- and 4-bit residual rows (the pages' default preset
+# stores keys un-rotated with 4-bit residual rows)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,variant", [(0, "Q8"), (0, "Q4"), (1, "Q4"), (1, "Q8")])
+def test_decode_unrotated_quantised(lib, cfg, variant):
+    wl = synth.set_unrotated(synth.make_config(cfg, variant=variant), synth.ROPE_BASE)
+    check_decode(lib, wl, label=f"U {variant}")
+
+
+@pytest.mark.parametrize("fmt,kw", [(2, dict(ranks=[7], n_resid=255)), (1, dict(ranks=[64], n_resid=4)),
+                                    (2, dict(n_q_heads=16, n_kv_heads=1)), (1, dict(n_resid=0))])
+def test_decode_unrotated_quantised_edges(lib, fmt, kw):
+    base = dict(seed=540 + fmt, batch=4, n_q_heads=6, n_kv_heads=2, window=64, n_blocks=[5, 3, 6, 4],
+                ranks=[12], n_resid=20, top_k=3, sigma0=2.0)
+    base.update(kw)
+    wl = synth.make_workload(f"UQ{fmt}", resid_format=fmt, rope_base=synth.ROPE_BASE, **base)
+    check_decode(lib, wl, label=f"U fmt {fmt} {kw}")
+
+
+def test_decode_layers_unrotated_mixed_formats(lib):
+    """Un-rotated layers with fp16, 8-bit and 4-bit residual rows in one launch."""
+    base = dict(batch=3, n_q_heads=6, n_kv_heads=2, window=40, n_blocks=[4, 6, 2], win_len=[40, 7, 33],
+                top_k=3, sigma0=2.0, rope_base=synth.ROPE_BASE)
+    wls = [synth.make_workload(f"umf{f}", seed=560 + f, ranks=[20 + 10 * f], n_resid=24, resid_format=f, **base)
+           for f in (0, 1, 2)]
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, 3, wls[0].scale)
+    assert run.plan.unrotated == 1 and run.plan.quantised == 1
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        _, _, i1 = lib.decode(pools[l], batches[l], 3, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        _oracle_check(w, w.layers[0], *res[l], 3)

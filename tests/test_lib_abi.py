@@ -93,7 +93,6 @@ def _decode(clib, pool, batch, top_k=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
     ({}, {}, -1, L.DKV_ERR_INVALID_ARG),
     ({"rope_freq": FAKE}, {}, 4, L.DKV_ERR_INVALID_ARG),                    # no slot_pos
     ({"rope_freq": FAKE + 4, "slot_pos": FAKE}, {}, 4, L.DKV_ERR_UNSUPPORTED),
-    ({"rope_freq": FAKE, "slot_pos": FAKE, "resid_format": L.RESID_INT8}, {}, 4, L.DKV_ERR_UNSUPPORTED),
     ({"basis_of": FAKE, "n_basis": 4}, {}, 4, L.DKV_ERR_UNSUPPORTED),       # shared basis, rotated pool
     ({"rope_freq": FAKE, "slot_pos": FAKE, "basis_of": FAKE, "n_basis": 0}, {}, 4, L.DKV_ERR_INVALID_ARG),
     ({"rope_freq": FAKE, "slot_pos": FAKE, "basis_of": FAKE + 2, "n_basis": 4}, {}, 4, L.DKV_ERR_UNSUPPORTED),
