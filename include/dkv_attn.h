@@ -23,7 +23,11 @@
  * dense recency window, with scores z = scale * q_g . k.  The library never
  * materialises reconstructed K or V; scores of reconstructed rows are taken
  * in the rank-r space, q.a_k + U_i.(V_K q), and their values gathered as
- * (sum p) a_v + (p^T U) V_V.
+ * (sum p) a_v + (p^T U) V_V.  Pools that hold keys from before the rotary
+ * embedding (dkv_pool.rope_freq) rotate every key to its absolute position
+ * at read: their kernels rebuild each block's keys 16 at a time in registers
+ * (a_k + U_i V_K on matrix cores), rotate them and score them; values are the
+ * same.  Such pools may also share bases between blocks (dkv_pool.basis_of).
  *
  * Conventions shared by every entry point
  *   - head_dim d = 128 and block size 256 are fixed (DKV_ERR_UNSUPPORTED
