@@ -289,3 +289,28 @@ def test_decode_layers_unrotated_mixed_formats(lib):
         torch.cuda.synchronize()
         assert torch.equal(res[l][2], i1)
         _oracle_check(w, w.layers[0], *res[l], 3)
+
+
+def test_shared_basis_entry_out_of_range_is_empty(lib):
+    """A block whose basis entry lies outside [0, n_basis) contributes no rows
+    (its routing key is left as it was, zero here); every other block decodes
+    as usual."""
+    wl = synth.set_shared_basis(_u(0), 2)
+    lay = wl.layers[0]
+    bad_slot = int(wl.block_table[0, 3])
+    lay.basis_of = lay.basis_of.copy()
+    lay.basis_of[bad_slot] = lay.vk.shape[0] + 5
+    pool, batch = upload(lib, wl)
+    assert torch.all(pool.route_key[bad_slot] == 0)
+    out, lse, idx = lib.decode(pool, batch, wl.top_k, wl.scale)
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy().astype(np.int64)
+    keep = g.copy()
+    keep[0][keep[0] == 3] = -1
+    P = lay.pool()
+    P["basis_of"] = P["basis_of"].copy()
+    P["basis_of"][bad_slot] = bad_slot            # never read: the block is dropped from the oracle's set
+    ro, rl, _ = oracle.decode(P, lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks, wl.win_len,
+                              wl.n_kv_heads, wl.top_k, wl.scale, idx=keep)
+    c = parity.check_outputs(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+    assert c.ok, c.message
