@@ -209,55 +209,8 @@ __device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 
 
-// Loads are always issued from an in-bounds address and masked afterwards: a
-// guarded load would compile to its own branch, and the branch merge to a full
-// wait for every outstanding load.
-__device__ __forceinline__ v8h ld8_mask(const f16* p, bool keep) {
-  uint4 x = *reinterpret_cast<const uint4*>(p);
-  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
-  x.x &= m;
-  x.y &= m;
-  x.z &= m;
-  x.w &= m;
-  return __builtin_bit_cast(v8h, x);
-}
-
-__device__ __forceinline__ v4h ld4_mask(const f16* p, bool keep) {
-  uint2 x = *reinterpret_cast<const uint2*>(p);
-  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
-  x.x &= m;
-  x.y &= m;
-  return __builtin_bit_cast(v4h, x);
-}
-
 __device__ __forceinline__ v4h lo4(v8h x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
 __device__ __forceinline__ v4h hi4(v8h x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
-
-// Online softmax over one 16-row tile for the query head g = lane % 16.  The
-// lane holds 4 of the 16 scores; lanes lane ^ 16 and lane ^ 32 hold the rest.
-__device__ __forceinline__ void softmax_tile(const float z[4], float& m_run, float& l_run,
-                                             float& alpha, float p[4]) {
-  float tm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-  tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-  tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-  const float mn = fmaxf(m_run, tm);
-  const bool none = (mn == -INFINITY);
-  alpha = none ? 1.f : __expf(m_run - mn);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = none ? 0.f : __expf(z[e] - mn);
-  float ps = (p[0] + p[1]) + (p[2] + p[3]);
-  ps += __shfl_xor(ps, 16, 64);
-  ps += __shfl_xor(ps, 32, 64);
-  l_run = l_run * alpha + ps;
-  m_run = mn;
-}
-
-// Per-row factor of the accumulator C layout (row g = 4 * (lane / 16) + e) from a
-// per-head value held by every lane with lane % 16 == g.
-__device__ __forceinline__ void rows_of(float v, int q4, float out[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = __shfl(v, 4 * q4 + e, 64);
-}
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -1871,7 +1824,7 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeUnroll = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, const float* part_lse,
-                                                        int n_parts, int n_rows, f16* out, float* out_lse) {
+                                                        int n_parts, f16* out, float* out_lse) {
   __shared__ float red[4][kD];
   __shared__ float redS[4];
   __shared__ float redM[4];
@@ -2617,7 +2570,7 @@ dkv_status launch_attend_nrq(int64_t items, size_t shm, hipStream_t st, const dk
                                            : launch_attend_nrq_q<NRQ, 1>(items, shm, st, P, B, a);
 }
 
-dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* idx, const int32_t* slots,
+dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* idx,
                          int top_k, int n_block_parts, int block_mode, int n_win_parts, int win_chunk,
                          float scale, float* part_o, float* part_lse, int n_parts, int part_offset,
                          hipStream_t st) {
@@ -2655,7 +2608,7 @@ dkv_status launch_attend(const dkv_pool* P, const dkv_batch* B, const int32_t* i
 dkv_status launch_merge(const float* part_o, const float* part_lse, int n_parts, int n_rows, void* out,
                         float* out_lse, hipStream_t st) {
   if (n_rows == 0) return DKV_OK;
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, st, part_o, part_lse, n_parts, n_rows,
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, st, part_o, part_lse, n_parts,
                      (f16*)out, out_lse);
   return launched("k_merge");
 }
@@ -2876,7 +2829,7 @@ dkv_status dkv_lowrank_attn(const dkv_pool* pool, const dkv_batch* batch, const 
   if (batch->batch == 0) return DKV_OK;
   if (!idx || !part_o || !part_lse) return fail(DKV_ERR_INVALID_ARG, "idx / part_o / part_lse is NULL");
   if ((s = check_pool_arrays(pool, 1))) return s;
-  return launch_attend(pool, batch, idx, nullptr, top_k, top_k, 1, 0, kWinChunk, scale, part_o, part_lse,
+  return launch_attend(pool, batch, idx, top_k, top_k, 1, 0, kWinChunk, scale, part_o, part_lse,
                        n_parts, part_offset, (hipStream_t)stream);
 }
 
@@ -2897,7 +2850,7 @@ dkv_status dkv_exact_attn(const dkv_pool* pool, const dkv_batch* batch, const in
   if (!part_o || !part_lse) return fail(DKV_ERR_INVALID_ARG, "part_o / part_lse is NULL");
   if (top_k > 0 && (s = check_pool_arrays(pool, 2))) return s;
   const int chunk = window_splits > 0 ? (batch->window + window_splits - 1) / window_splits : 1;
-  return launch_attend(pool, batch, idx, nullptr, top_k, top_k, 2, window_splits, chunk > 0 ? chunk : 1, scale,
+  return launch_attend(pool, batch, idx, top_k, top_k, 2, window_splits, chunk > 0 ? chunk : 1, scale,
                        part_o, part_lse, n_parts, part_offset, (hipStream_t)stream);
 }
 
