@@ -26,31 +26,14 @@
 //   k_merge       log-sum-exp combine of the parts of each query row.
 // All reductions run in a fixed order; there are no floating-point atomics.
 
-#include <hip/hip_runtime.h>
+#include "dkv_common.h"
 
-#include <math.h>
-#include <stdarg.h>
-#include <stdint.h>
-#include <stdio.h>
-#include <string.h>
-
-#include "dkv_attn.h"
-
-#include <type_traits>
-
-typedef _Float16 f16;
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+// The streaming launch (dkv_stream.hip).
+size_t dkv_stream_lds_bytes();
+hipError_t dkv_stream_launch(const void* table, const void* one, const void* layers, int n_items, size_t lds,
+                             hipStream_t st);
 
 namespace {
-
-constexpr int kD = 128;            // head dim
-constexpr int kLowRankRows = 255;  // tokens 1..255 of a block
-constexpr int kVStride = 132;      // LDS row stride (halves) of 128-wide tiles: conflict-free column reads
-constexpr int kWinChunk = 512;     // window rows per window part (when the window has parts of its own)
 
 thread_local char g_err[512] = "";
 
@@ -62,187 +45,6 @@ dkv_status fail(dkv_status s, const char* fmt, ...) {
   return s;
 }
 
-// ----------------------------------------------------------------------------
-// Kernel arguments (plain structs passed by value)
-// ----------------------------------------------------------------------------
-
-struct PoolArgs {
-  const f16* ak; int64_t ak_s, ak_h;
-  const f16* av; int64_t av_s, av_h;
-  const f16* u;  int64_t u_s, u_h;
-  const f16* vk; int64_t vk_s, vk_h;
-  const f16* vv; int64_t vv_s, vv_h;
-  const f16* rk; int64_t rk_s, rk_h;
-  const f16* rv; int64_t rv_s, rv_h;
-  const uint8_t* rp; int64_t rp_s, rp_h;
-  float* key; int64_t key_s, key_h;
-  int rank, n_resid, n_kv, n_slots;
-  int rfmt;                                   // residual rows: 0 fp16 (rk, rv), 1 / 2 8- / 4-bit codes
-  const uint8_t* rkq; int64_t rkq_s, rkq_h;   // codes [R][128] or [R][64] (bytes)
-  const uint8_t* rvq; int64_t rvq_s, rvq_h;
-  const f16* rks; int64_t rks_s, rks_h;       // (scale, bias) per 64-dimension group [R][2][2]
-  const f16* rvs; int64_t rvs_s, rvs_h;
-  // un-rotated pools: theta_j / (2 pi) as hi[64] then lo[64], and each slot's
-  // absolute position; rope == nullptr for pools of rotated keys
-  const float* rope;
-  const int32_t* spos;
-  // shared basis (un-rotated pools only): the vk / vv entry of each slot, or nullptr
-  const int32_t* basis;
-  int n_basis;
-};
-
-struct BatchArgs {
-  int B, Hq, Hkv, G, W, mb;
-  const int32_t* table;
-  const int32_t* nblk;
-  const int32_t* wlen;
-  const f16* q;
-  const f16* wk;
-  const f16* wv;
-  const float* rkeys;  // [B][Hkv][mb][kD] per-sequence routing keys, or NULL
-};
-
-struct AttnArgs {
-  const int32_t* idx;
-  int top_k;           // row stride of idx
-  int n_block_parts;   // parts per unit that are routed blocks (top_k or 0)
-  int block_mode;      // bit 0: low-rank rows of a block, bit 1: its residual rows
-  int n_win_parts;
-  int win_chunk;
-  int win_tile_stride; // > 0: block part p also attends window tiles p, p + stride, ... (16 rows each)
-  int items_per_unit;
-  int rq;              // augmented rank rounded up to 16 (0 without low-rank rows)
-  float scale;
-  float* part_o;
-  float* part_lse;
-  int n_parts;
-  int part_offset;
-};
-
-// ----------------------------------------------------------------------------
-// Device helpers
-// ----------------------------------------------------------------------------
-
-__device__ __forceinline__ v4f mfma16(v4h a, v4h b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void split_hl(float x0, float x1, float x2, float x3, v4h& hi, v4h& lo) {
-  const float x[4] = {x0, x1, x2, x3};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const f16 h = (f16)x[e];
-    hi[e] = h;
-    lo[e] = (f16)(x[e] - (float)h);
-  }
-}
-
-// Four softmax weights in [0, 1] as an fp16 MFMA operand (round to nearest
-// even: relative error at most 2^-11 per weight; the row sums stay fp32)
-__device__ __forceinline__ v4h to_h4(const float (&x)[4]) {
-  v4h h;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) h[e] = (f16)x[e];
-  return h;
-}
-
-// LDS hand-off between lanes of one wave: LDS operations of a wave complete in
-// order, so waiting for this wave's outstanding LDS operations (lgkmcnt = 0)
-// before reading what other lanes wrote is enough; the empty asm and the wave
-// barrier keep the compiler from moving LDS accesses across this point.
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt = 63 (no wait), expcnt = 7, lgkmcnt = 0
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Workgroup barrier for LDS hand-offs: each wave waits for its own LDS (and
-// scalar) operations, then all waves meet.  Unlike __syncthreads() it does not
-// drain the waves' outstanding global loads, so data requested before it keeps
-// streaming in while the workgroup moves on.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt = 0 only
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ v8h ld8(const f16* p) { return *reinterpret_cast<const v8h*>(p); }
-
-// Values handed from one workgroup to another inside a launch are written and
-// read with device-scope (agent) relaxed atomics: these go to the device-wide
-// coherence point, so no L2 write-back fence is needed on the hot path.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until this thread's stores have completed
-__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Buffer loads at device scope (cache policy sc1): they read the device-coherent
-// copy, so they observe data that other workgroups of the same launch wrote with
-// device-scope stores and then published through a counter, without an
-// invalidation of the whole cache.  Reads outside [base, base + bytes) return 0.
-constexpr int kLoadDeviceScope = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kLoadDeviceScope);  // 4 x 32 raw bits
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-}
-__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float4 v) {
-  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-  const v4u bits = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(bits, r, (int)byte_off, 0, kLoadDeviceScope);
-}
-__device__ __forceinline__ float ld_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kLoadDeviceScope));
-}
-
-
-__device__ __forceinline__ v4h lo4(v8h x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
-__device__ __forceinline__ v4h hi4(v8h x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
-
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 and +0 compare equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(u);
-}
-
-// Exclusive count of `flag` over the workgroup (NW waves) in thread order, and the total.
-template <int NW>
-__device__ __forceinline__ void block_count(bool flag, int& excl, int& total, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-  const int in_wave = __popcll(m & lt);
-  if (lane == 0) wsum[w] = (uint32_t)__popcll(m);
-  lds_barrier();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int c = (int)wsum[i];
-    off += (i < w) ? c : 0;
-    tot += c;
-  }
-  lds_barrier();
-  excl = off + in_wave;
-  total = tot;
-}
 
 // ----------------------------------------------------------------------------
 // Routing key precompute
@@ -360,288 +162,6 @@ __global__ void k_gather_route_keys(PoolArgs P, BatchArgs Bt, float* out) {
   *reinterpret_cast<float4*>(out + row * kD + 4 * c4) = v;
 }
 
-// ----------------------------------------------------------------------------
-// Wave-wide reductions and scans with DPP lane moves (no LDS round trips)
-// ----------------------------------------------------------------------------
-
-template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, true);
-}
-
-// max (MAX = true) or min over the 64 lanes, returned to every lane
-template <bool MAX>
-__device__ __forceinline__ float wave_minmax(float v) {
-  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
-  uint32_t u = __float_as_uint(v);
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0xB1>(u, u))));   // quad_perm 1,0,3,2
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x4E>(u, u))));   // quad_perm 2,3,0,1
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x141>(u, u))));  // row_half_mirror
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x140>(u, u))));  // row_mirror
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x142, 0xa>(u, u))));  // row_bcast:15
-  u = __float_as_uint(op(__uint_as_float(u), __uint_as_float(dpp_u32<0x143, 0xc>(u, u))));  // row_bcast:31
-  return __uint_as_float(__builtin_amdgcn_readlane(u, 63));
-}
-
-// inclusive prefix sum over the 64 lanes in lane order
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  uint32_t s = v + dpp_u32<0x111>(0u, v);  // row_shr:1
-  s += dpp_u32<0x112>(0u, v);              // row_shr:2
-  s += dpp_u32<0x113>(0u, v);              // row_shr:3
-  s += dpp_u32<0x114, 0xf, 0xe>(0u, s);    // row_shr:4 into lanes 4..15 of each row
-  s += dpp_u32<0x118, 0xf, 0xc>(0u, s);    // row_shr:8 into lanes 8..15
-  s += dpp_u32<0x142, 0xa>(0u, s);         // row_bcast:15 into rows 1 and 3
-  s += dpp_u32<0x143, 0xc>(0u, s);         // row_bcast:31 into rows 2 and 3
-  return s;
-}
-
-// ----------------------------------------------------------------------------
-// Top-K routing: one workgroup of 4 waves per (sequence, KV head)
-// ----------------------------------------------------------------------------
-
-constexpr int kRouteThreads = 256;
-constexpr int kRedRow = 36;          // floats per row of the per-wave transpose area (conflict-free float4 reads)
-
-template <int NW>
-struct RouteShared {
-  uint32_t hist[256];
-  uint32_t wsum[NW];
-  float wlo[NW], whi[NW];
-  uint32_t digit, above;
-};
-
-// LDS words route_unit needs for max_blocks blocks and NW waves.
-__host__ __device__ constexpr size_t route_lds_words(int max_blocks, int nw) {
-  return (size_t)2 * (size_t)(((max_blocks > 0 ? max_blocks : 1) + 3) & ~3) + (size_t)nw * 64 * kRedRow;
-}
-
-// Routed-slot words of the fused kernel hold pool slot + kSlotCode (1: no block),
-// so that 0, the state of zero-filled memory, means "routing not written yet".
-constexpr int32_t kSlotPending = 0;
-constexpr int32_t kSlotCode = 2;
-
-// Route one (sequence, KV head) unit u with a workgroup of NT threads.
-// lds: route_lds_words(max_blocks, NT / 64) words: ordered score keys [mb],
-// pool slots [mb] (both rounded up to 4), then a 64 x kRedRow float area per wave.
-//
-// Scores: lane l of a wave holds columns 4 (l % 32) .. +3 of the GQA-mean query;
-// a 512-byte routing key is read by 32 lanes, 16 bytes each, two keys per load
-// instruction (fully coalesced), and the 32 lane partials of a key are summed
-// through LDS.  Selection: block j is routed iff fewer than K blocks beat it
-// (a larger score, or an equal score at a smaller index: the lowest-index-first
-// tie rule), found with a 256-bin histogram of the scores and an exact ranking
-// inside the boundary bin only.  Routed blocks are emitted in ascending block
-// order.
-template <int NT>
-__device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
-                                           float* scores, int32_t* slots_out, uint32_t* lds,
-                                           RouteShared<NT / 64>& sh) {
-  constexpr int NW = NT / 64;
-  static_assert(NT == 256 || NT == 512, "route_unit: 256 histogram bins over the first 4 waves");
-  constexpr int kBinWaves = 256 / 64;
-  uint32_t* wsum = sh.wsum;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = u / Bt.Hkv, h = u % Bt.Hkv;
-  int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
-  N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
-  const int keff = top_k < N ? top_k : N;
-  const int mbp = ((Bt.mb > 0 ? Bt.mb : 1) + 3) & ~3;
-  uint32_t* keys = lds;
-  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + mbp);
-  float* red = reinterpret_cast<float*>(lds + 2 * mbp) + wave * 64 * kRedRow;
-
-  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
-  const int c4 = lane & 31, half = lane >> 5;
-  float4 qb = make_float4(0.f, 0.f, 0.f, 0.f);
-  {
-    const f16* q0 = Bt.q + ((int64_t)b * Bt.Hq + h * Bt.G) * kD + 4 * c4;
-    v4h qh[DKV_MAX_GROUP];
-#pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) qh[g] = *reinterpret_cast<const v4h*>(q0 + (g < Bt.G ? g : Bt.G - 1) * kD);
-#pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) {
-      if (g < Bt.G) {
-        qb.x += (float)qh[g][0];
-        qb.y += (float)qh[g][1];
-        qb.z += (float)qh[g][2];
-        qb.w += (float)qh[g][3];
-      }
-    }
-    const float inv = 1.f / (float)Bt.G;
-    qb.x *= inv;
-    qb.y *= inv;
-    qb.z *= inv;
-    qb.w *= inv;
-  }
-
-  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
-  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
-  const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
-  float4 kv[32];
-  auto load_group = [&](int g0) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      int r = g0 + 2 * i + half;
-      r = r < N ? r : N - 1;
-      const float* src;
-      if (seq_keys) {
-        src = seq_keys + (int64_t)r * kD;
-      } else {
-        const int sr = slot_of[r];
-        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
-      }
-      kv[i] = *reinterpret_cast<const float4*>(src);
-    }
-  };
-  // with per-sequence keys the first group does not wait for the block table
-  if (seq_keys && wave * 64 < N) load_group(wave * 64);
-
-  // ---- pool slots of the unit's blocks (coalesced block-table reads)
-  for (int j = tid; j < N; j += NT) {
-    const int sr = Bt.table[(int64_t)b * Bt.mb + j];
-    slot_of[j] = (sr >= 0 && sr < P.n_slots) ? sr : -1;
-  }
-  lds_barrier();
-
-  // ---- scores of 64-block groups, one group per wave at a time
-  for (int g0 = wave * 64; g0 < N; g0 += NT) {
-    if (!seq_keys || g0 != wave * 64) load_group(g0);
-    float part[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) part[i] = (kv[i].x * qb.x + kv[i].y * qb.y) + (kv[i].z * qb.z + kv[i].w * qb.w);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) red[(2 * i + half) * kRedRow + c4] = part[i];
-    wave_sync_lds();
-    const float4* rr = reinterpret_cast<const float4*>(red + lane * kRedRow);
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float4 v = rr[m];
-      acc += (v.x + v.y) + (v.z + v.w);
-    }
-    const int j = g0 + lane;
-    if (j < N) keys[j] = ordered_key(slot_of[j] >= 0 ? acc : -INFINITY);
-    wave_sync_lds();  // the next group reuses the transpose area
-  }
-  lds_barrier();
-
-  auto emit = [&](int pos, int j, uint32_t k) {
-    st_dev(&idx[(int64_t)u * top_k + pos], j);
-    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)slot_of[j] + kSlotCode);
-  };
-
-  if (keff > 0) {
-    // ---- histogram select.  Finite scores are binned linearly between their
-    // minimum and maximum into bins 1..255 (-inf and below into bin 0); the
-    // bin map is monotone, so every block in a bin above the boundary bin b* is
-    // routed and none below it.  Inside b* the blocks are ranked exactly by
-    // (score, lower index first) against the other members of b*.
-    uint32_t* hist = sh.hist;
-    constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // ordered key of -inf
-    float lo = INFINITY, hi = -INFINITY;
-    for (int jj = tid; jj < N; jj += NT) {
-      const float sc = from_ordered(keys[jj]);
-      if (isfinite(sc)) {
-        lo = fminf(lo, sc);
-        hi = fmaxf(hi, sc);
-      }
-    }
-    if (tid < 256) hist[tid] = 0u;
-    lo = wave_minmax<false>(lo);
-    hi = wave_minmax<true>(hi);
-    if (lane == 0) {
-      sh.wlo[wave] = lo;
-      sh.whi[wave] = hi;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lo = fminf(lo, sh.wlo[w]);
-      hi = fmaxf(hi, sh.whi[w]);
-    }
-    const float inv = (hi > lo) ? 254.99f / (hi - lo) : 0.f;
-    auto bin_of = [&](uint32_t k) -> uint32_t {
-      if (k <= kNegInfKey) return 0u;
-      const float sc = from_ordered(k);
-      if (!(sc <= INFINITY)) return 255u;  // +NaN keys order above +inf
-      const float t = (sc - lo) * inv;
-      return 1u + (uint32_t)fminf(fmaxf(t, 0.f), 254.f);
-    };
-    if (tid == 0) {
-      sh.digit = 0u;
-      sh.above = 0u;
-    }
-    for (int jj = tid; jj < N; jj += NT) atomicAdd(&hist[bin_of(keys[jj])], 1u);
-    lds_barrier();
-    // counts of bins >= 255 - tid (a scan of the bins in descending order)
-    const uint32_t hb = tid < 256 ? hist[255 - tid] : 0u;
-    uint32_t incl = wave_incl_scan(hb);
-    if (lane == 63 && wave < kBinWaves) wsum[wave] = incl;
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < kBinWaves; ++w) incl += (w < wave) ? wsum[w] : 0u;
-    const uint32_t excl = incl - hb;
-    if (tid < 256 && excl < (uint32_t)keff && incl >= (uint32_t)keff) {
-      sh.digit = 255u - (uint32_t)tid;
-      sh.above = excl;
-    }
-    lds_barrier();
-    const uint32_t bstar = sh.digit & 255u, need = (uint32_t)keff - sh.above, m = hist[bstar];
-    // members of b* that are routed: all of them, or the `need` best by rank
-    uint64_t* cand = reinterpret_cast<uint64_t*>(lds + 2 * mbp);  // the score transpose area, now free
-    const uint32_t cap = (uint32_t)(NW * 64 * kRedRow / 2 - 2);
-    uint32_t* n_cand = reinterpret_cast<uint32_t*>(cand + cap);
-    const bool rank_members = m > need;
-    const bool listed = m <= cap;
-    if (rank_members && listed) {
-      if (tid == 0) *n_cand = 0u;
-      lds_barrier();
-      for (int jj = tid; jj < N; jj += NT) {
-        const uint32_t k = keys[jj];
-        if (bin_of(k) == bstar) cand[atomicAdd(n_cand, 1u)] = ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)jj);
-      }
-      lds_barrier();
-    }
-    int sel_base = 0;
-    for (int b0 = 0; b0 < N; b0 += NT) {
-      const int jj = b0 + tid;
-      bool sel = false;
-      uint32_t kj = 0u;
-      if (jj < N) {
-        kj = keys[jj];
-        const uint32_t bj = bin_of(kj);
-        sel = bj > bstar;
-        if (bj == bstar) {
-          if (!rank_members) {
-            sel = true;
-          } else {
-            const uint64_t cj = ((uint64_t)kj << 32) | (uint64_t)(~(uint32_t)jj);
-            uint32_t beat = 0u;
-            if (listed) {
-              for (uint32_t t2 = 0; t2 < m; ++t2) beat += (uint32_t)(cand[t2] > cj);
-            } else {
-              for (int t2 = 0; t2 < N; ++t2) {
-                const uint32_t k2 = keys[t2];
-                beat += (uint32_t)(bin_of(k2) == bstar && (((uint64_t)k2 << 32) | (uint64_t)(~(uint32_t)t2)) > cj);
-              }
-            }
-            sel = beat < need;
-          }
-        }
-      }
-      int sel_rank, sel_tot;
-      block_count<NW>(sel, sel_rank, sel_tot, wsum);
-      if (sel) emit(sel_base + sel_rank, jj, kj);
-      sel_base += sel_tot;
-    }
-  }
-  for (int pos = keff + tid; pos < top_k; pos += NT) {
-    st_dev(&idx[(int64_t)u * top_k + pos], -1);
-    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], -INFINITY);
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], -1 + kSlotCode);
-  }
-}
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_topk(PoolArgs P, BatchArgs Bt, int top_k,
                                                               int32_t* idx, float* scores, int32_t* slots_out) {
@@ -664,12 +184,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_topk(PoolArgs P, BatchA
 // columns 16 w .. 16 w + 15 and 64 + 16 w .. 64 + 16 w + 15.
 // ----------------------------------------------------------------------------
 
-constexpr int kAttThreads = 256;
-constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kLRTilesPerWave = 16 / kAttWaves;
 constexpr int kRedStride = 132;  // floats per row of the reduction buffer (conflict-free C-layout access)
 
-__host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
 
 
 // Staged MFMA A operands are stored transposed, so that a lane's four
@@ -1877,181 +1394,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
     if (lane == 0) out_lse[row] = any ? M + __logf(St) : -INFINITY;
   }
 }
-
-// ----------------------------------------------------------------------------
-// Log-sum-exp merge of the partials of one decode step, inside the launch
-// ----------------------------------------------------------------------------
-
-
-// Log-sum-exp combine of one query row's n_parts partials by one workgroup:
-// kMergeSlots slots of 32 lanes (4 columns per lane), slot s taking parts s,
-// s + kMergeSlots, ..., every load of a round issued at once; the row maximum
-// comes first so the slots' weighted sums add without rescaling, in a fixed
-// order.  lds: kMergeSlots * (kD + 1) + kAttWaves floats.
-constexpr int kMergeSlots = kAttThreads / 32;
-constexpr int kMergeRowChunk = 8;  // parts per slot per round
-__device__ __forceinline__ void merge_row(const float* part_o, const float* part_lse, int n_parts, int row,
-                                          f16* out, float* out_lse, float* lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c4 = tid & 31, sl = tid >> 5;
-  float* red = lds;                           // [kMergeSlots][kD]
-  float* redS = lds + kMergeSlots * kD;       // [kMergeSlots]
-  float* redM = redS + kMergeSlots;           // [kAttWaves]
-  const int np = n_parts > 0 ? n_parts : 1;
-  const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row * n_parts * kD, (uint32_t)n_parts * kD * 4);
-  const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row * n_parts, (uint32_t)n_parts * 4);
-  // first round's partials, then the row maximum over every part
-  float4 o[kMergeRowChunk];
-  float l[kMergeRowChunk];
-#pragma unroll
-  for (int k = 0; k < kMergeRowChunk; ++k) {
-    const int pp = sl + kMergeSlots * k;
-    const int pc = pp < np ? pp : np - 1;
-    o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
-    l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
-  }
-  float m = -INFINITY;
-  for (int pp = tid; pp < n_parts; pp += kAttThreads) m = fmaxf(m, ld_coherent(Lb, (uint32_t)pp * 4u));
-  m = wave_minmax<true>(m);
-  if (lane == 0) redM[wave] = m;
-  lds_barrier();
-#pragma unroll
-  for (int w = 0; w < kAttWaves; ++w) m = fmaxf(m, redM[w]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float S = 0.f;
-  for (int p0 = 0; p0 < n_parts; p0 += kMergeSlots * kMergeRowChunk) {
-    if (p0 > 0) {
-#pragma unroll
-      for (int k = 0; k < kMergeRowChunk; ++k) {
-        const int pp = p0 + sl + kMergeSlots * k;
-        const int pc = pp < np ? pp : np - 1;
-        o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
-        l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kMergeRowChunk; ++k) {
-      const int pp = p0 + sl + kMergeSlots * k;
-      const float w = (pp < n_parts && l[k] != -INFINITY) ? __expf(l[k] - m) : 0.f;
-      S += w;
-      acc.x += w * o[k].x;
-      acc.y += w * o[k].y;
-      acc.z += w * o[k].z;
-      acc.w += w * o[k].w;
-    }
-  }
-  *reinterpret_cast<float4*>(red + sl * kD + 4 * c4) = acc;
-  if (c4 == 0) redS[sl] = S;
-  lds_barrier();
-  if (tid < 32) {
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-    float St = 0.f;
-#pragma unroll
-    for (int s2 = 0; s2 < kMergeSlots; ++s2) {
-      const float4 v = *reinterpret_cast<const float4*>(red + s2 * kD + 4 * c4);
-      t.x += v.x;
-      t.y += v.y;
-      t.z += v.z;
-      t.w += v.w;
-      St += redS[s2];
-    }
-    const bool any = St > 0.f;
-    v4h h4;
-    h4[0] = (f16)(any ? t.x / St : 0.f);
-    h4[1] = (f16)(any ? t.y / St : 0.f);
-    h4[2] = (f16)(any ? t.z / St : 0.f);
-    h4[3] = (f16)(any ? t.w / St : 0.f);
-    *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * c4) = h4;
-    if (tid == 0) out_lse[row] = any ? m + __logf(St) : -INFINITY;
-  }
-}
-
-// Log-sum-exp combine of the partials of one unit's G query rows (rows row0 ..
-// row0 + G - 1) by one workgroup: each 32-lane slot takes a row (slot s: rows
-// s, s + 8, ...), with its lanes on 4 columns each.  The row maximum comes
-// first, then the partials are combined in part order, so the result does not
-// depend on timing.
-__device__ __forceinline__ void merge_unit(const float* part_o, const float* part_lse, int n_parts, int row0, int G,
-                                           f16* out, float* out_lse) {
-  const int c4 = threadIdx.x & 31, sl = threadIdx.x >> 5;
-  const int np = n_parts > 0 ? n_parts : 1;
-  for (int g = sl; g < G; g += kMergeSlots) {
-    const int row = row0 + g;
-    const __amdgpu_buffer_rsrc_t Ob = coherent_rsrc(part_o + (int64_t)row * n_parts * kD, (uint32_t)n_parts * kD * 4);
-    const __amdgpu_buffer_rsrc_t Lb = coherent_rsrc(part_lse + (int64_t)row * n_parts, (uint32_t)n_parts * 4);
-    float m = -INFINITY;
-    for (int p0 = 0; p0 < n_parts; p0 += kMergeRowChunk) {
-      float l[kMergeRowChunk];
-#pragma unroll
-      for (int k = 0; k < kMergeRowChunk; ++k) l[k] = ld_coherent(Lb, (uint32_t)(p0 + k < np ? p0 + k : np - 1) * 4u);
-#pragma unroll
-      for (int k = 0; k < kMergeRowChunk; ++k) m = fmaxf(m, l[k]);
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float S = 0.f;
-    for (int p0 = 0; p0 < n_parts; p0 += kMergeRowChunk) {
-      float4 o[kMergeRowChunk];
-      float l[kMergeRowChunk];
-#pragma unroll
-      for (int k = 0; k < kMergeRowChunk; ++k) {
-        const int pc = p0 + k < np ? p0 + k : np - 1;
-        o[k] = ld_coherent4(Ob, (uint32_t)(pc * kD + 4 * c4) * 4u);
-        l[k] = ld_coherent(Lb, (uint32_t)pc * 4u);
-      }
-#pragma unroll
-      for (int k = 0; k < kMergeRowChunk; ++k) {
-        const float w = (p0 + k < n_parts && l[k] != -INFINITY) ? __expf(l[k] - m) : 0.f;
-        S += w;
-        acc.x += w * o[k].x;
-        acc.y += w * o[k].y;
-        acc.z += w * o[k].z;
-        acc.w += w * o[k].w;
-      }
-    }
-    const bool any = S > 0.f;
-    v4h h4;
-    h4[0] = (f16)(any ? acc.x / S : 0.f);
-    h4[1] = (f16)(any ? acc.y / S : 0.f);
-    h4[2] = (f16)(any ? acc.z / S : 0.f);
-    h4[3] = (f16)(any ? acc.w / S : 0.f);
-    *reinterpret_cast<v4h*>(out + (int64_t)row * kD + 4 * c4) = h4;
-    if (c4 == 0) out_lse[row] = any ? m + __logf(S) : -INFINITY;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// One decode step of one layer in a single launch.
-//
-// Work items, handed out in ticket order (an atomic counter, so an item is
-// only ever taken by a workgroup that is already running): first the routing
-// of every (sequence, KV head) unit, then per unit its routed blocks and its
-// window chunks, then one merge per unit.  A block item waits (bounded) until
-// its routed slot is published, a merge until its unit's parts are counted;
-// what they wait for precedes them in ticket order and is held by running
-// workgroups, so every wait ends.  The last merge leaves the control words
-// zeroed for the next launch.
-// ----------------------------------------------------------------------------
-
-struct DecodeArgs {
-  AttnArgs att;
-  int32_t* idx;          // [units][top_k] routed logical blocks
-  int32_t* slots;        // [units][top_k] routed pool slots (-1: none); kSlotPending until routed
-  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, queue counters
-  uint32_t* unit_done;   // [units] parts finished
-  f16* out;
-  float* out_lse;
-  int n_units;
-  int n_route;           // units routed in this launch (0 when top_k == 0)
-  int n_part_end;        // n_route + n_units * att.items_per_unit: first merge item
-  int merges;            // merge items per unit: G (one per query row) or 1 (one per unit)
-  int n_items;           // n_part_end + n_units * merges: the grid size
-};
-
-constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
-constexpr int kQueues = 8;                      // one work queue per XCD
-constexpr int kQueueStride = 64;                // words between queue counters (separate 256-byte lines)
-constexpr int kCtrlQueue = 64;                  // first queue counter
-constexpr int kCtrlHeaderBytes = 4096;          // control words: [0..63] misc, then the queue counters
-
 // One work item of a fused decode step: t < n_route routes unit t; then
 // the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merges,
 // per query row (u, g) or per unit u.  sh_slot: a shared word of the calling
@@ -2176,89 +1518,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
     }
   }
 }
-
-// ----------------------------------------------------------------------------
-// Layer-batched decode: the fused steps of several layers in one launch
-// ----------------------------------------------------------------------------
-
-struct LayerArgs {
-  PoolArgs P;
-  BatchArgs Bt;
-  DecodeArgs D;  // the layer's workspace region; D.ctrl is the launch-wide control header
-  int nrq;
-};
-
-struct LayersArgs {
-  uint32_t* ctrl;  // [1] merges finished, [2] sticky wait-timeout flag, queue counters
-  int n_layers;
-  int n_units;     // units per layer (the same in every layer)
-  int routes;       // routing items per unit (0 or 1)
-  int block_parts;  // routed-block parts per unit
-  int win_parts;    // window parts per unit
-  int group;        // merges per unit (query heads per KV head)
-};
-
-// Position i of XCD queue x (which holds the nx units u = x + 8 j of every
-// layer) -> (layer, item index within that layer's launch).  The queue holds
-// the routings of every layer, then the window parts of every layer (they wait
-// on nothing, and run while the routings finish), then the routed-block parts
-// of layer 0, 1, ..., with the merges of layer l placed after the block parts
-// of layer l + kMergeLag (as measured, no lag beats placing every merge after
-// all block parts: the merges then never wait, and fill the launch's tail).
-// Every wait is on an item earlier in the same queue.  Uniform (scalar)
-// arithmetic.
-constexpr int kMergeLag = 1 << 16;
-
-__device__ __forceinline__ void layers_item(int i, int x, int nx, const LayersArgs& L, int& layer, int& item) {
-  const int NL = L.n_layers, NP = L.block_parts, NW = L.win_parts, G = L.group;
-  const int per_unit = NP + NW;
-  const int n_route = L.routes * L.n_units;
-  const int n_part_end = n_route + L.n_units * per_unit;
-  const int nR = nx * L.routes, nW = nx * NW, nP = nx * NP, nM = nx * G;
-  if (i < NL * nR) {
-    layer = i / nR;
-    item = x + kQueues * (i % nR);
-    return;
-  }
-  i -= NL * nR;
-  if (i < NL * nW) {
-    layer = i / nW;
-    const int r = i % nW;
-    item = n_route + (x + kQueues * (r / NW)) * per_unit + NP + r % NW;
-    return;
-  }
-  i -= NL * nW;
-  const int a = NL < kMergeLag ? NL : kMergeLag;
-  int kind = 0, r = 0;  // kind 0: block part of `layer`, 1: merge of `layer`
-  if (i < a * nP) {
-    layer = i / nP;
-    r = i % nP;
-  } else {
-    i -= a * nP;
-    const int pair = nP + nM;
-    if (i < (NL - a) * pair) {
-      const int c = i / pair;
-      r = i % pair;
-      if (r < nP) {
-        layer = a + c;
-      } else {
-        layer = c;
-        r -= nP;
-        kind = 1;
-      }
-    } else {
-      i -= (NL - a) * pair;
-      layer = NL - a + i / nM;
-      r = i % nM;
-      kind = 1;
-    }
-  }
-  item = kind == 0 ? n_route + (x + kQueues * (r / NP)) * per_unit + r % NP
-                   : n_part_end + (x + kQueues * (r / G)) * G + r % G;
-}
-
-// Work items of every layer from the per-XCD queues (see layers_item).
-// NMAX: the largest low-rank tile count of any layer (instances hold only the
 // attention variants up to it, which keeps register use down).
 template <int NMAX, int QK>
 __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArgs* __restrict__ table, LayersArgs L) {
@@ -2632,13 +1891,56 @@ struct WsLayout {
 // the window has parts of its own, of kWinChunk rows).  Un-rotated pools never
 // fold: their block parts then start with empty output accumulators, which
 // keeps the registers the rotation needs free.
+// Window rows per window part of the streaming launch: 256 with one launch
+// per layer (more, shorter parts), kWinChunk with several layers.
+constexpr int kStreamWinChunk = 256;
+// Routed blocks per block part of the streaming launch with several layers
+// (one with one layer per launch, where parallelism matters most).
+constexpr int kStreamLayerBlocks = 4;
+
+int stream_win_parts(int window, int chunk) {
+  const int n = (window + chunk - 1) / chunk;
+  return n > 0 ? n : 1;
+}
+
+// Parts per unit reserved in a decode workspace: enough for the classic
+// launches (window folded or not) and for the streaming launch.
+size_t reserved_parts(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold) {
+  fold = fold && !pool->rope_freq;
+  const size_t classic = (top_k > 0 && fold) ? (size_t)top_k
+                                             : (size_t)top_k + (size_t)decode_win_parts(batch->window);
+  const size_t stream = (size_t)top_k + (size_t)stream_win_parts(batch->window, kStreamWinChunk);
+  return classic > stream ? classic : stream;
+}
+
+bool al_view(const dkv_view& v, int esz, int a) {
+  return al(v.ptr, a) && (v.slot_stride * esz) % a == 0 && (v.head_stride * esz) % a == 0;
+}
+
+// The streaming launch (dkv_stream.hip) takes pools of rotated keys with fp16
+// residual rows, ranks that are multiples of 8 up to 56, residual counts that
+// are multiples of 4, 16-byte aligned fp16 arrays and 4-byte aligned
+// positions.  It is used when DKV_STREAM=1 is set in the environment.
+bool stream_eligible(const dkv_pool* P, const dkv_batch* B) {
+  static const int enabled = [] {
+    const char* e = getenv("DKV_STREAM");
+    return (e && e[0] == '1') ? 1 : 0;
+  }();
+  if (!enabled || P->rope_freq || P->basis_of || P->resid_format != DKV_RESID_FP16) return false;
+  if (P->rank % 8 != 0 || P->rank > 56 || P->n_resid % 4 != 0) return false;
+  if (!al_view(P->anchor_k, 2, 16) || !al_view(P->anchor_v, 2, 16) || !al_view(P->u, 2, 16) ||
+      !al_view(P->vk, 2, 16) || !al_view(P->vv, 2, 16))
+    return false;
+  if (P->n_resid > 0 && (!al_view(P->resid_k, 2, 16) || !al_view(P->resid_v, 2, 16) || !al_view(P->resid_pos, 1, 4)))
+    return false;
+  return al(B->q, 16) && al(B->win_k, 16) && al(B->win_v, 16);
+}
+
 WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold = true) {
   WsLayout w;
-  fold = fold && !pool->rope_freq;
   const size_t B = (size_t)batch->batch;
   const size_t units = B * (size_t)pool->n_kv_heads;
-  const size_t n_parts = (top_k > 0 && fold) ? (size_t)top_k
-                                             : (size_t)top_k + (size_t)decode_win_parts(batch->window);
+  const size_t n_parts = reserved_parts(pool, batch, top_k, fold);
   const size_t rows = B * (size_t)batch->n_q_heads;
   w.unit_done = kCtrlHeaderBytes;
   w.slots = w.unit_done + align256(units * 4);
@@ -2654,21 +1956,26 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
                              uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
-                             bool fold = true, bool row_merges = true) {
+                             bool fold = true, bool row_merges = true, int stream_blocks = 0, int stream_chunk = 0) {
   const WsLayout w = decode_layout(pool, batch, top_k, fold);
   // folded, each routed-block part also takes its share of the window;
-  // otherwise the window comes in chunks of kWinChunk rows
-  fold = fold && top_k > 0 && !pool->rope_freq;
-  const int n_win = fold ? 0 : decode_win_parts(batch->window);
-  const int n_parts = top_k + n_win;
+  // otherwise the window comes in chunks of kWinChunk rows.  The streaming
+  // launch has parts of stream_blocks routed blocks and window parts of
+  // stream_chunk rows.
+  fold = fold && top_k > 0 && !pool->rope_freq && stream_blocks == 0;
+  const int n_block = stream_blocks > 0 ? (top_k + stream_blocks - 1) / stream_blocks : top_k;
+  const int n_win = stream_blocks > 0 ? stream_win_parts(batch->window, stream_chunk)
+                                      : (fold ? 0 : decode_win_parts(batch->window));
+  const int n_parts = n_block + n_win;
   const int units = batch->batch * pool->n_kv_heads;
   AttnArgs& a = D.att;
   a.idx = nullptr;
   a.top_k = top_k;
-  a.n_block_parts = top_k;
+  a.n_block_parts = n_block;
   a.block_mode = 3;
   a.n_win_parts = n_win;
-  a.win_chunk = kWinChunk;
+  a.win_chunk = stream_blocks > 0 ? stream_chunk : kWinChunk;
+  a.blocks_per_item = stream_blocks;
   a.win_tile_stride = fold ? top_k : 0;
   a.items_per_unit = n_parts;
   a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
@@ -2694,7 +2001,7 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
   D.n_part_end = (int)part_end;
   D.n_items = (int)items;
-  shm = (size_t)att_lds_bytes(a.rq);
+  shm = stream_blocks > 0 ? dkv_stream_lds_bytes() : (size_t)att_lds_bytes(a.rq);
   const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
   if (top_k > 0 && route_shm > shm) shm = route_shm;
   return DKV_OK;
@@ -2914,13 +2221,35 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   const hipStream_t st = (hipStream_t)stream;
   DecodeArgs D;
   size_t shm = 0;
+  const bool streaming = stream_eligible(pool, batch);
   if ((s = build_decode_args(pool, batch, top_k, scale, (unsigned char*)workspace, (uint32_t*)workspace, out, out_lse,
-                             out_idx, D, shm)))
+                             out_idx, D, shm, true, true, streaming ? 1 : 0, kStreamWinChunk)))
     return s;
   const AttnArgs& a = D.att;
 
   if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)
     return fail(DKV_ERR_HIP, "hipEventRecord failed");
+  if (streaming) {
+    LayerArgs one;
+    memset(&one, 0, sizeof(one));
+    one.P = make_pool_args(pool);
+    one.Bt = make_batch_args(pool, batch);
+    one.D = D;
+    one.nrq = a.rq / 16;
+    LayersArgs L;
+    L.ctrl = (uint32_t*)workspace;
+    L.n_layers = 1;
+    L.n_units = D.n_units;
+    L.routes = D.n_route > 0 ? 1 : 0;
+    L.block_parts = a.n_block_parts;
+    L.win_parts = a.n_win_parts;
+    L.group = D.merges;
+    const hipError_t e = dkv_stream_launch(nullptr, &one, &L, D.n_items, shm, st);
+    if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_stream launch failed: %s", hipGetErrorString(e));
+    if (events && hipEventRecord((hipEvent_t)events[1], st) != hipSuccess)
+      return fail(DKV_ERR_HIP, "hipEventRecord failed");
+    return DKV_OK;
+  }
   switch (a.rq / 16) {
     case 0: s = launch_decode_nrq<0>(shm, st, pool, batch, D); break;
     case 1: s = launch_decode_nrq<1>(shm, st, pool, batch, D); break;
@@ -2999,6 +2328,9 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
   dkv_status s = DKV_OK;
   size_t shm = 0, off = kCtrlHeaderBytes;
   unsigned char* ws = (unsigned char*)workspace;
+  bool streaming = true;
+  for (int l = 0; l < n_layers; ++l) streaming = streaming && stream_eligible(&pools[l], &batches[l]);
+  const int sblocks = streaming ? (top_k < kStreamLayerBlocks ? (top_k > 0 ? top_k : 1) : kStreamLayerBlocks) : 0;
   for (int l = 0; l < n_layers && s == DKV_OK; ++l) {
     const dkv_pool* pool = &pools[l];
     const dkv_batch* batch = &batches[l];
@@ -3029,7 +2361,7 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     size_t shm_l = 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
                                out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
-                               /*row_merges=*/false)))
+                               /*row_merges=*/false, sblocks, kWinChunk)))
       break;
     host[l].P = make_pool_args(pool);
     host[l].Bt = make_batch_args(pool, batch);
@@ -3062,6 +2394,8 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     for (int l = 0; l < n_layers; ++l) quant |= pools[l].resid_format != DKV_RESID_FP16 ? 1 : 0;
     plan->quantised = quant;
     plan->unrotated = p0.rope_freq ? 1 : 0;
+    plan->stream = streaming ? 1 : 0;
+    plan->stream_blocks = sblocks;
     plan->table = table;
     plan->workspace = workspace;
   }
@@ -3081,6 +2415,14 @@ dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
   L.block_parts = plan->parts;
   L.win_parts = plan->win_parts;
   L.group = plan->group;
+  if (plan->stream) {
+    LayerArgs unused;
+    memset(&unused, 0, sizeof(unused));
+    const hipError_t e =
+        dkv_stream_launch(plan->table, &unused, &L, plan->n_items, (size_t)plan->lds_bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_stream launch failed: %s", hipGetErrorString(e));
+    return DKV_OK;
+  }
   switch (plan->max_tiles) {  // the largest low-rank tile count of the layers
     case 0: return launch_layers<0>(plan, L, (hipStream_t)stream);
     case 1: return launch_layers<1>(plan, L, (hipStream_t)stream);

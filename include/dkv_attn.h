@@ -337,6 +337,8 @@ typedef struct dkv_layers_plan {
   int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */
   int32_t quantised;      /* 1 if any layer's residual rows are quantised */
   int32_t unrotated;      /* 1 if the layers' pools are un-rotated (all of them or none) */
+  int32_t stream;         /* 1: the streaming launch (every layer qualifies, see dkv_decode) */
+  int32_t stream_blocks;  /* streaming launch: routed blocks per block part */
   const void* table;
   void* workspace;
 } dkv_layers_plan;
