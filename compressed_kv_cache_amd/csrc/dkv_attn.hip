@@ -1920,11 +1920,11 @@ bool al_view(const dkv_view& v, int esz, int a) {
 // The streaming launch (dkv_stream.hip) takes pools of rotated keys with fp16
 // residual rows, ranks that are multiples of 8 up to 56, residual counts that
 // are multiples of 4, 16-byte aligned fp16 arrays and 4-byte aligned
-// positions.  It is used when DKV_STREAM=1 is set in the environment.
+// positions.  DKV_STREAM=0 in the environment selects the classic launch.
 bool stream_eligible(const dkv_pool* P, const dkv_batch* B) {
   static const int enabled = [] {
     const char* e = getenv("DKV_STREAM");
-    return (e && e[0] == '1') ? 1 : 0;
+    return (e && e[0] == '0') ? 0 : 1;
   }();
   if (!enabled || P->rope_freq || P->basis_of || P->resid_format != DKV_RESID_FP16) return false;
   if (P->rank % 8 != 0 || P->rank > 56 || P->n_resid % 4 != 0) return false;
@@ -2221,7 +2221,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   const hipStream_t st = (hipStream_t)stream;
   DecodeArgs D;
   size_t shm = 0;
-  const bool streaming = stream_eligible(pool, batch);
+  const bool streaming = false;  // one launch per layer: the classic launch (streaming parts hold four blocks)
   if ((s = build_decode_args(pool, batch, top_k, scale, (unsigned char*)workspace, (uint32_t*)workspace, out, out_lse,
                              out_idx, D, shm, true, true, streaming ? 1 : 0, kStreamWinChunk)))
     return s;

@@ -31,20 +31,22 @@
 
 namespace {
 
-constexpr int kSRowB = 272;                      // bytes per 128-wide fp16 row in LDS: 256 + one 16-byte pad
-constexpr int kSPage = 64 * kSRowB;              // bytes per ring slot: 64 such rows
-constexpr int kSSlots = 4;                       // ring depth
-constexpr int kSRing = kSPage * kSSlots;
-constexpr int kSQOff = kSRing;                   // the unit's query rows [16][128] fp16 (4 KB)
-constexpr int kSQtOff = kSQOff + 16 * kD * 2;    // V_K q exchange [64][16] fp32 (4 KB)
-constexpr int kSMaskOff = kSQtOff + 64 * 16 * 4; // residual-position masks [2][8] u32
-constexpr int kSMaxBlocks = 32;                  // routed blocks per part at most
-constexpr int kSSlotOff = kSMaskOff + 64;        // the part's routed pool slots [kSMaxBlocks]
-constexpr int kSNvOff = kSSlotOff + 4 * kSMaxBlocks;
-constexpr int kSLds = kSNvOff + 16;
-constexpr int kSRows = 64;                       // K / V rows per page
-
-static_assert(kSLds % 16 == 0, "LDS areas are 16-byte aligned");
+constexpr int kSRowB = 272;                 // bytes per 128-wide fp16 row in LDS: 256 + one 16-byte pad
+constexpr int kWRows = 16;                  // rows per page
+constexpr int kWPage = kWRows * kSRowB;     // bytes per ring slot (a U page of 32 positions also fits)
+constexpr int kWSlots = 4;                  // ring depth per wave
+constexpr int kWRing = kWPage * kWSlots;    // one wave's ring
+constexpr int kSMaxBlocks = 32;             // routed blocks per part at most
+constexpr int kWQOff = kAttWaves * kWRing;  // the unit's query rows [16][128] fp16 (4 KB)
+constexpr int kWPosOff = kWQOff + 16 * kD * 2;        // residual positions, per wave [4][128] bytes
+constexpr int kWMaskOff = kWPosOff + kAttWaves * 128;  // residual-position masks, per wave [4][8] u32
+constexpr int kWSlotOff = kWMaskOff + kAttWaves * 32; // the part's routed pool slots [kSMaxBlocks]
+constexpr int kWNvOff = kWSlotOff + 4 * kSMaxBlocks;
+constexpr int kWBaseOff = kWNvOff + 16;                 // per-block source addresses [kSMaxBlocks][kBases] u64
+enum { kBaseAK = 0, kBaseAV, kBaseU, kBaseVK, kBaseVV, kBaseRK, kBaseRV, kBaseRP, kBases };
+constexpr int kWLds = kWBaseOff + kSMaxBlocks * kBases * 8;
+static_assert(kWLds % 16 == 0, "LDS areas are 16-byte aligned");
+static_assert(32 * 2 * 56 + 16 <= kWPage, "a U page of 32 positions fits a slot");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -117,64 +119,6 @@ __device__ __forceinline__ v4f mfma32(v8h a, v8h b, v4f c) {
 // 16 different bank groups
 __device__ __forceinline__ int swz(int row, int c) { return row * kSRowB + (c << 4); }
 
-// Page layout of a part.  A block has 4 + 2 nt pages: 0 V_K rows and a_k (row
-// r) plus the residual positions (dwords at kPosOff); 1 U positions 0..127 (a
-// zero row, then U rows 0..126); 2 U positions 128..255 (U rows 127..254);
-// then K and V pages of 64 residual rows each; last V_V rows and a_v (row r).
-// A window part has 2 nt pages, K and V of 64 rows each.
-enum PageKind { kPageVK = 0, kPageU0 = 1, kPageU1 = 2, kPageK = 3, kPageV = 4, kPageVV = 5 };
-
-struct StreamGeom {
-  int r, nq;       // rank and round16(r) / 16
-  int R, nt;       // residual rows, and their 64-row tiles
-  int ppb;         // pages per block
-  bool window;     // a window part
-  int nrows;       // window part: its rows
-  int total;       // pages of the part
-};
-
-// A page cursor: block `blk` of the part and page `k` of that block (for a
-// window part, blk = 0 and k counts its pages), advanced one page at a time.
-struct PageCursor {
-  int blk, k;
-  __device__ __forceinline__ void next(const StreamGeom& g) {
-    if (++k == g.ppb && !g.window) {
-      k = 0;
-      ++blk;
-    }
-  }
-  // kind of the page and its K / V tile
-  __device__ __forceinline__ void kind(const StreamGeom& g, int& kd, int& t) const {
-    if (g.window) {
-      kd = kPageK + (k & 1);
-      t = k >> 1;
-    } else if (k < 3) {
-      kd = k;
-      t = 0;
-    } else if (k == g.ppb - 1) {
-      kd = kPageVV;
-      t = 0;
-    } else {
-      kd = kPageK + ((k - 3) & 1);
-      t = (k - 3) >> 1;
-    }
-  }
-};
-
-__device__ __forceinline__ int rows_of_tile(const StreamGeom& g, int t) {
-  const int n = g.window ? g.nrows : g.R;
-  const int rem = n - kSRows * t;
-  return rem < kSRows ? rem : kSRows;
-}
-
-constexpr int kPosOff = 57 * kSRowB;  // residual positions (bytes) in a V_K page: after at most 57 rows
-
-// Per-block source addresses, gathered once per part into LDS (bytes):
-// a_k, a_v, U, V_K, V_V, K rows, V rows, positions.
-enum { kBaseAK = 0, kBaseAV, kBaseU, kBaseVK, kBaseVV, kBaseRK, kBaseRV, kBaseRP, kBases };
-constexpr int kSBaseOff = kSLds;                        // [kSMaxBlocks][kBases] u64
-constexpr int kSLdsTotal = kSBaseOff + kSMaxBlocks * kBases * 8;
-
 __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, uint32_t off, unsigned char* lds_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, off, 0, 0, 0);
 }
@@ -187,73 +131,100 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint
 
 constexpr uint32_t kOutside = 0xFFFFFFF0u;  // a buffer offset past every resource: the load returns zeros
 
-// Issue this wave's loads of the page at cursor `cur` into ring slot `dst`;
-// returns how many vector-memory instructions this wave issued for it.  The
-// loads are buffer loads straight into LDS: each source array is a buffer
-// resource sized to its data, and every 16-byte chunk of the page whose
-// offset falls outside it (row pads, rows past the data, U's leading zero row)
-// is written as zeros by the range check.  A 128-wide row page maps chunk p to
-// row p / 17, chunk p % 17 (chunk 16 is the row's pad); a U page maps p
-// linearly.  The extra row r of a V_K / V_V page (a_k / a_v) comes from a load
-// of its own.
-__device__ __forceinline__ int issue_page(const StreamGeom& g, const PageCursor& cur, unsigned char* dst,
-                                          const uint64_t* bases, const char* wk_rows, const char* wv_rows) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int kind, t;
-  cur.kind(g, kind, t);
+// The pages one wave streams.  A block: V_K tiles (16 rows of [V_K ; a_k] each,
+// a_k at row r), 8 U pages of 32 positions, K and V tiles of 16 residual rows,
+// V_V tiles (16 rows of [V_V ; a_v]).  A window share: K and V tiles of 16 rows.
+enum PageKind { kPageVK = 0, kPageU = 1, kPageK = 2, kPageV = 3, kPageVV = 4 };
+
+struct WaveGeom {
+  int r, nq, nqv;  // rank, round16(r) / 16, round16(r + 1) / 16 (V_K / V_V tiles)
+  int R, nt;       // residual rows (or the wave's window rows) and their 16-row tiles
+  int ppb;         // pages of the wave's block (or window share)
+  bool window;
+};
+
+__device__ __forceinline__ void page_kind(const WaveGeom& g, int k, int& kind, int& i) {
+  if (g.window) {
+    kind = kPageK + (k & 1);
+    i = k >> 1;
+    return;
+  }
+  if (k < g.nqv) {
+    kind = kPageVK;
+    i = k;
+  } else if ((k -= g.nqv) < 8) {
+    kind = kPageU;
+    i = k;
+  } else if ((k -= 8) < 2 * g.nt) {
+    kind = kPageK + (k & 1);
+    i = k >> 1;
+  } else {
+    kind = kPageVV;
+    i = k - 2 * g.nt;
+  }
+}
+
+// Issue the loads of page k of this wave's stream into its ring slot `dst`;
+// returns the number of vector-memory instructions issued.  The loads are
+// buffer loads straight into LDS: each source array is a buffer resource
+// sized to its data, and every 16-byte chunk of the page whose offset falls
+// outside it (row pads, rows past the data, U's leading zero row, the end of
+// U) is written as zeros by the range check.  A 128-wide row page maps chunk p
+// to row p / 17, chunk p % 17 (chunk 16 is the row's pad); a U page maps p
+// linearly.  Row r of [V_K ; a_k] and [V_V ; a_v] comes from a load of its own.
+__device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned char* dst, const uint64_t* bb,
+                                          const char* wk_rows, const char* wv_rows, unsigned char* posdst) {
+  const int lane = threadIdx.x & 63;
+  int kind, i;
+  page_kind(g, k, kind, i);
   const int r = g.r;
-  const uint64_t* bb = bases + cur.blk * kBases;
   int ops = 0;
-  if (kind == kPageU0 || kind == kPageU1) {
-    // U positions 0..127: a zero row (offsets below the data), U rows 0..126;
-    // positions 128..255: U rows 127..254; then a zero chunk past the data
-    const bool first = kind == kPageU0;
-    const __amdgpu_buffer_rsrc_t rs =
-        rsrc_of((const char*)bb[kBaseU] + (first ? 0 : 254 * r), (uint32_t)(first ? 254 * r : 256 * r));
-    const int ni = (16 * r + 1 + 63) >> 6;
-    const int p_off = first ? (r >> 3) : 0;
-    for (int i = wave; i < ni; i += kAttWaves) {
-      dma16b(rs, (uint32_t)(16 * (64 * i + lane - p_off)), dst + 1024 * i);
+  if (kind == kPageU) {
+    // positions 32 i .. 32 i + 31: U rows 32 i - 1 .. 32 i + 30 (row -1 reads
+    // as zeros: the anchor), and 16 bytes more for the last row's column overrun
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of((const char*)bb[kBaseU], (uint32_t)(510 * r));
+    const int nch = 4 * r + 1;
+    const int start = (32 * i - 1) * 2 * r;
+    for (int q = 0; q < nch; q += 64) {
+      dma16b(rs, (uint32_t)(start + 16 * (q + lane)), dst + 16 * q);
       ++ops;
     }
     return ops;
   }
-  const char* base0;
-  int nvalid, special = -1, rows;
+  const char* base;
+  int nvalid, special = -1;
   if (kind == kPageVK || kind == kPageVV) {
-    base0 = (const char*)bb[kind == kPageVK ? kBaseVK : kBaseVV];
-    nvalid = r;
-    special = r;
-    rows = kind == kPageVK ? r + 1 : round16(r + 1);  // the fold reads round16(r + 1) rows
+    base = (const char*)bb[kind == kPageVK ? kBaseVK : kBaseVV] + 16 * i * 256;
+    nvalid = r - 16 * i;
+    nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+    special = r - 16 * i;
+    if (special > 15) special = -1;
   } else {
-    nvalid = rows_of_tile(g, t);
+    const int rem = g.R - 16 * i;
+    nvalid = rem < 16 ? rem : 16;
     if (g.window)
-      base0 = (kind == kPageK ? wk_rows : wv_rows) + (int64_t)kSRows * t * 256;
+      base = (kind == kPageK ? wk_rows : wv_rows) + 16 * i * 256;
     else
-      base0 = (const char*)bb[kind == kPageK ? kBaseRK : kBaseRV] + (int64_t)kSRows * t * 256;
-    rows = round16(nvalid);
+      base = (const char*)bb[kind == kPageK ? kBaseRK : kBaseRV] + 16 * i * 256;
   }
-  const __amdgpu_buffer_rsrc_t rs = rsrc_of(base0, (uint32_t)nvalid * 256u);
-  const int nch = 17 * rows;
-  const int ni = (nch + 63) >> 6;
-  for (int i = wave; i < ni; i += kAttWaves) {
-    const int p = 64 * i + lane;
-    const int row = (p * 3856) >> 16;  // p / 17 for p < 4097
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)nvalid * 256u);
+  for (int q = 0; q < 17 * 16; q += 64) {
+    const int p = q + lane;
+    const int row = (p * 3856) >> 16;  // p / 17
     const int c = p - 17 * row;
     const uint32_t off = c < 16 ? (uint32_t)(row * 256 + 16 * c) : kOutside;
-    if (p < nch && row != special) dma16b(rs, off, dst + 1024 * i);
+    if (p < 17 * 16 && row != special) dma16b(rs, off, dst + 16 * q);
     ++ops;
   }
-  if (special >= 0 && wave == kAttWaves - 1) {
-    // row r: a_k or a_v (16 chunks) and its pad
+  if (special >= 0) {
     const __amdgpu_buffer_rsrc_t rs1 = rsrc_of((const char*)bb[kind == kPageVK ? kBaseAK : kBaseAV], 256u);
     if (lane < 17) dma16b(rs1, lane < 16 ? (uint32_t)(16 * lane) : kOutside, dst + kSRowB * special);
     ++ops;
   }
-  if (kind == kPageVK && wave == 0 && g.R > 0) {
-    // residual positions: R bytes as R / 4 dwords (R % 4 == 0)
+  if (kind == kPageVK && i == 0 && g.R > 0) {
+    // the block's residual positions: R bytes as R / 4 dwords (R % 4 == 0)
     const __amdgpu_buffer_rsrc_t rp = rsrc_of((const char*)bb[kBaseRP], (uint32_t)g.R);
-    if (4 * lane < g.R) dma4b(rp, (uint32_t)(4 * lane), dst + kPosOff);
+    if (4 * lane < g.R) dma4b(rp, (uint32_t)(4 * lane), posdst);
     ++ops;
   }
   return ops;
@@ -337,31 +308,36 @@ __device__ __forceinline__ void store_empty(const AttnArgs& A, int row0, int G, 
   if (tid < G) st_dev(&A.part_lse[(int64_t)(row0 + tid) * A.n_parts + part], -INFINITY);
 }
 
+// q~ (or W^T) tile number i of a four-tile register array, i uniform
+template <class T>
+__device__ __forceinline__ T pick4(const T (&a)[4], int i) {
+  return i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
+}
+
 // One attention part of unit u: part p < n_block_parts holds routed ranks
-// [p * bpi, min((p + 1) * bpi, top_k)); the others are window chunks of
-// win_chunk rows.
+// [p * bpi, min((p + 1) * bpi, top_k)), at most four: wave w streams block w.
+// The other parts are window chunks of win_chunk rows: wave w streams rows
+// [w c / 4, (w + 1) c / 4) of the chunk.  Each wave keeps its own softmax state
+// over its rows; the four states are combined at the end into the part's
+// partial.
 __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& Bt, const AttnArgs& A,
-                                         const int32_t* slots, uint32_t* ctrl, int u, int p, unsigned char* smem) {
+                                            const int32_t* slots, uint32_t* ctrl, int u, int p, unsigned char* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
   const int G = Bt.G;
   const int row0 = b * Bt.Hq + h * G;
   const int part = A.part_offset + p;
-  int32_t* slist = reinterpret_cast<int32_t*>(smem + kSSlotOff);
-  int32_t* shn = reinterpret_cast<int32_t*>(smem + kSNvOff);
-  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + kSMaskOff);
+  int32_t* slist = reinterpret_cast<int32_t*>(smem + kWSlotOff);
+  int32_t* shn = reinterpret_cast<int32_t*>(smem + kWNvOff);
+  uint64_t* bases = reinterpret_cast<uint64_t*>(smem + kWBaseOff);
 
-  StreamGeom g;
+  WaveGeom g;
   g.r = P.rank;
   g.nq = round16(P.rank) >> 4;
-  g.R = P.n_resid;
-  g.nt = (P.n_resid + kSRows - 1) / kSRows;
-  g.ppb = 4 + 2 * g.nt;
+  g.nqv = round16(P.rank + 1) >> 4;
   g.window = p >= A.n_block_parts;
-  g.nrows = 0;
-  int wrow0 = 0;
-  int nv = 0;
+  int nv = 0, wrow0 = 0, wrows = 0;
   if (!g.window) {
     // the part's routed slots, waited for (bounded) until the routing wrote them
     const int k0 = p * A.blocks_per_item;
@@ -392,27 +368,35 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
     }
     lds_barrier();
     nv = shn[0];
-    g.total = nv * g.ppb;
+    g.R = P.n_resid;
   } else {
     const int s = p - A.n_block_parts;
     int wl = Bt.wlen ? Bt.wlen[b] : Bt.W;
     wl = wl < 0 ? 0 : (wl > Bt.W ? Bt.W : wl);
     const int start = s * A.win_chunk;
     const int end = (start + A.win_chunk < wl) ? start + A.win_chunk : wl;
-    g.nrows = end > start ? end - start : 0;
-    wrow0 = start;
-    g.total = 2 * ((g.nrows + kSRows - 1) / kSRows);
+    const int rows = end > start ? end - start : 0;
+    // wave w: a quarter of the chunk, in whole 16-row tiles
+    const int per = (((A.win_chunk + kAttWaves - 1) / kAttWaves) + 15) & ~15;
+    wrow0 = start + per * wave;
+    const int lim = rows - per * wave;
+    wrows = lim < 0 ? 0 : (lim > per ? per : lim);
+    g.R = wrows;
+    nv = rows > 0 ? 1 : 0;
   }
-  if (g.total == 0) {
+  g.nt = (g.R + 15) >> 4;
+  if (nv == 0) {
     store_empty(A, row0, G, part);
     return;
   }
+  g.ppb = g.window ? 2 * g.nt : 2 * g.nqv + 8 + 2 * g.nt;
+  const bool mine = g.window ? wrows > 0 : wave < nv;   // uniform over the wave
+  const int total = mine ? g.ppb : 0;
   const int64_t win_base = (((int64_t)b * Bt.Hkv + h) * Bt.W) * kD;
   const char* wk_rows = (const char*)(Bt.wk + win_base + (int64_t)wrow0 * kD);
   const char* wv_rows = (const char*)(Bt.wv + win_base + (int64_t)wrow0 * kD);
 
-  // ---- the source addresses of the part's blocks, once
-  uint64_t* bases = reinterpret_cast<uint64_t*>(smem + kSBaseOff);
+  // ---- the blocks' source addresses and the query rows, once per part
   if (!g.window && tid < nv * kBases) {
     const int blk = tid / kBases, which = tid % kBases;
     const int64_t slot = slist[blk];
@@ -429,27 +413,19 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
     }
     bases[tid] = (uint64_t)a;
   }
-  if (tid < 16) masks[tid] = 0u;
-  lds_barrier();
-
-  // ---- prologue: the query rows (heads past G read the zero chunk), the first pages.
-  // in_flight: this wave's load-instruction counts of the pages issued and not
-  // yet waited for, one byte each, the oldest in the low byte.
-  unsigned char* qrows = smem + kSQOff;
+  unsigned char* qrows = smem + kWQOff;
   {
     const int hh = tid >> 4, c = tid & 15;
     const void* src = hh < G ? (const void*)(Bt.q + (int64_t)(row0 + hh) * kD + 8 * c) : (const void*)kZeroChunk;
     dma16(src, qrows + 1024 * wave);
   }
-  PageCursor ic = {0, 0};   // next page to issue
-  int n_issued = 0;
-  uint32_t in_flight = 0u;
-  for (; n_issued < kSSlots - 1 && n_issued < g.total; ++n_issued) {
-    const int ops = issue_page(g, ic, smem + kSPage * n_issued, bases, wk_rows, wv_rows) + (n_issued == 0 ? 1 : 0);
-    in_flight |= (uint32_t)ops << (8 * n_issued);
-    ic.next(g);
-  }
+  lds_barrier();  // the source addresses are in place (the query rows are still in flight)
 
+  // ---- this wave's stream: pages through its own ring, kWSlots - 1 ahead
+  unsigned char* ring = smem + wave * kWRing;
+  unsigned char* posb = smem + kWPosOff + 128 * wave;
+  uint32_t* mask = reinterpret_cast<uint32_t*>(smem + kWMaskOff + 32 * wave);
+  const uint64_t* bb = bases + (g.window ? 0 : wave) * kBases;
   SState st;
 #pragma unroll
   for (int n = 0; n < 8; ++n) st.Ot[n] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -459,184 +435,162 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
   st.l = 0.f;
   st.llr = 0.f;
   const float scale = A.scale;
-  v8h qf[4];          // q[head = l16][32 s + 8 q4 + 0..7], the B operand of the d-contractions
-  v4h qth[4], qtl[4];  // V_K q of the current block (hi + lo fp16), rows 16 k + 4 q4 + e, head l16
-  float qa = 0.f;     // scale * q . a_k of the current block
-  uint32_t mbits = 0u; // residual-position bits of the lane's positions in the current block
-  v4h pv;             // weights of the wave's rows of the current K page (fp16), for its V page
-  PageCursor cc = {0, 0};   // page being used
+  // the first pages, then the query rows (loaded before them) once every wave has its share
+  int n_issued = 0;
+  uint32_t in_flight = 0u;  // this wave's load counts of the pages issued and not yet waited for (bytes, oldest low)
+  for (; n_issued < kWSlots - 1 && n_issued < total; ++n_issued)
+    in_flight |= (uint32_t)issue_page(g, n_issued, ring + kWPage * n_issued, bb, wk_rows, wv_rows, posb)
+                 << (8 * n_issued);
+  wait_vm((int)((in_flight & 0xFFu) + ((in_flight >> 8) & 0xFFu) + (in_flight >> 16)));
+  lds_barrier();
+  v8h qf[4];  // q[head = l16][32 s + 8 q4 + 0..7], the B operand of the d-contractions
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const v8h*>(qrows + l16 * 256 + 64 * s + 16 * q4);
 
-  for (int n = 0; n < g.total; ++n, cc.next(g)) {
-    // this wave's loads of the pages issued after page n may stay in flight
-    const uint32_t after = in_flight >> 8;
-    wait_vm((int)((after & 0xFFu) + ((after >> 8) & 0xFFu) + (after >> 16)));
-    lds_barrier();
-    in_flight = after;
-    if (n_issued < g.total) {
-      const int ops = issue_page(g, ic, smem + kSPage * (n_issued % kSSlots), bases, wk_rows, wv_rows);
-      in_flight |= (uint32_t)ops << (8 * (n_issued - n - 1));
-      ic.next(g);
-      ++n_issued;
-    }
-    if (n == 0) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qf[s] = *reinterpret_cast<const v8h*>(qrows + l16 * 256 + 64 * s + 16 * q4);
-    }
-    const unsigned char* pg = smem + kSPage * (n % kSSlots);
-    int kind, t;
-    cc.kind(g, kind, t);
-    const int blk = cc.blk;
+  if (total > 0) {
     const int r = g.r;
-    if (kind == kPageVK) {
-      // V_K q (rows j < r) and q . a_k (row r): wave w takes rows 16 w .. 16 w + 15
-      if (16 * wave < r + 1) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const int j = 16 * wave + l16;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(j, 4 * s + q4)), qf[s], acc);
-        float* qt = reinterpret_cast<float*>(smem + kSQtOff);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qt[(16 * wave + 4 * q4 + e) * 16 + l16] = acc[e];
+    v4h qth[4], qtl[4];  // scaled V_K q of the block (hi + lo fp16): rows 16 k + 4 q4 + e, head l16
+    float qa = 0.f;      // scale * q . a_k
+    float llr_tot = 0.f; // the block's low-rank weight sum per head (at the first V_V tile)
+    v4h pv;              // weights of the current K tile (fp16), for its V tile
+    for (int n = 0; n < total; ++n) {
+      const uint32_t after = in_flight >> 8;
+      wait_vm((int)((after & 0xFFu) + ((after >> 8) & 0xFFu) + (after >> 16)));
+      in_flight = after;
+      if (n_issued < total) {
+        in_flight |= (uint32_t)issue_page(g, n_issued, ring + kWPage * (n_issued % kWSlots), bb, wk_rows, wv_rows,
+                                          posb)
+                     << (8 * (n_issued - n - 1));
+        ++n_issued;
       }
-      // residual-position mask of this block; the other buffer is cleared for the next block
-      uint32_t* mk = masks + 8 * (blk & 1);
-      if (wave == 1 && lane < 8) masks[8 * ((blk + 1) & 1) + lane] = 0u;
-      if (tid < g.R) {
-        const int ps = pg[kPosOff + tid];
-        if (ps >= 1 && ps <= kLowRankRows) atomicOr(&mk[ps >> 5], 1u << (ps & 31));
-      }
-    } else if (kind == kPageU0 || kind == kPageU1) {
-      if (kind == kPageU0) {
-        // this block's scaled V_K q rows (zero beyond r) and q . a_k, and the
-        // residual-position bits of the lane's 16 positions (4 q4 + e of its
-        // two tiles, in both U pages)
-        const float* qt = reinterpret_cast<const float*>(smem + kSQtOff);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (k < g.nq) {
-            v4f x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = 16 * k + 4 * q4 + e;
-              x[e] = j < r ? qt[j * 16 + l16] * scale : 0.f;
-            }
-            split4(x, qth[k], qtl[k]);
-          }
-        }
-        qa = qt[r * 16 + l16] * scale;
-        const uint32_t* mk = masks + 8 * (blk & 1);
-        const uint32_t w0 = mk[wave], w1 = mk[wave + 4];
-        mbits = ((w0 >> (4 * q4)) & 0xFu) | (((w0 >> (16 + 4 * q4)) & 0xFu) << 4) |
-                (((w1 >> (4 * q4)) & 0xFu) << 8) | (((w1 >> (16 + 4 * q4)) & 0xFu) << 12);
-      }
-      const uint32_t pbits = kind == kPageU0 ? (mbits & 0xFFu) : (mbits >> 8);
-      float z[8];
-      v4f zt[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int lrow = 32 * wave + 16 * tt + l16;  // row of the page = position - posbase
+      const unsigned char* pg = ring + kWPage * (n % kWSlots);
+      int kind, i;
+      page_kind(g, n, kind, i);
+      if (kind == kPageVK) {
+        // V_K q rows 16 i .. 16 i + 15 (q . a_k at row r)
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (k < g.nq) {
-            const v4h a = *reinterpret_cast<const v4h*>(pg + 2 * (lrow * r + 16 * k + 4 * q4));
-            acc = mfma16(a, qth[k], acc);
-            acc = mfma16(a, qtl[k], acc);
-          }
-        }
-        zt[tt] = acc;
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(l16, 4 * s + q4)), qf[s], acc);
+        v4f x;
+        float qr = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool masked = ((pbits >> (4 * tt + e)) & 1u) != 0u;
-          z[4 * tt + e] = masked ? -INFINITY : zt[tt][e] + qa;
+          const int j = 16 * i + 4 * q4 + e;
+          x[e] = j < r ? acc[e] * scale : 0.f;
+          qr += j == r ? acc[e] * scale : 0.f;
         }
-      }
-      softmax_step<8>(st, z, true);
-      v8h pf;
+        v4h hi, lo;
+        split4(x, hi, lo);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (f16)z[e];
-      // W^T += Ux^T p over the wave's 32 positions (positions 4 q4 + t of both tiles)
+        for (int k = 0; k < 4; ++k)
+          if (k == i) {
+            qth[k] = hi;
+            qtl[k] = lo;
+          }
+        if (16 * i <= r && r < 16 * i + 16) qa = hq_sum(qr);
+        if (i == 0) {
+          // the block's residual-position mask (this wave's own LDS words)
+          if (lane < 8) mask[lane] = 0u;
+          wave_sync_lds();
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < g.nq) {
-          const int c0 = 16 * k + 4 * (l16 & 3);
-          const int ra = 32 * wave + 4 * q4 + (l16 >> 2);
-          const v4h a0 = ld_tr(pg + 2 * (ra * r + c0));
-          const v4h a1 = ld_tr(pg + 2 * ((ra + 16) * r + c0));
-          const v8h a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          st.Wt[k] = mfma32(a, pf, st.Wt[k]);
+          for (int k = 0; k < 2; ++k) {
+            const int t = lane + 64 * k;
+            if (t < g.R) {
+              const int ps = posb[t];
+              if (ps >= 1 && ps <= kLowRankRows) atomicOr(&mask[ps >> 5], 1u << (ps & 31));
+            }
+          }
+          wave_sync_lds();
         }
-      }
-    } else if (kind == kPageK) {
-      const int nr = rows_of_tile(g, t);
-      if (16 * wave < nr) {
+      } else if (kind == kPageU) {
+        // positions 32 i + 16 tt + row of the page; row 0 of page 0 is the anchor
+        const uint32_t mw = mask[i];
+        float z[8];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int lrow = 16 * tt + l16;
+          v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (k < g.nq) {
+              const v4h a = *reinterpret_cast<const v4h*>(pg + 2 * (lrow * r + 16 * k + 4 * q4));
+              acc = mfma16(a, qth[k], acc);
+              acc = mfma16(a, qtl[k], acc);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool masked = ((mw >> (16 * tt + 4 * q4 + e)) & 1u) != 0u;
+            z[4 * tt + e] = masked ? -INFINITY : acc[e] + qa;
+          }
+        }
+        softmax_step<8>(st, z, true);
+        v8h pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (f16)z[e];
+        // W^T += Ux^T p over the page's 32 positions (positions 4 q4 + t of both tiles)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (k < g.nq) {
+            const int c0 = 16 * k + 4 * (l16 & 3);
+            const int ra = 4 * q4 + (l16 >> 2);
+            const v4h a0 = ld_tr(pg + 2 * (ra * r + c0));
+            const v4h a1 = ld_tr(pg + 2 * ((ra + 16) * r + c0));
+            const v8h a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.Wt[k] = mfma32(a, pf, st.Wt[k]);
+          }
+        }
+      } else if (kind == kPageK) {
+        const int nr = g.R - 16 * i;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const int row = 16 * wave + l16;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(row, 4 * s + q4)), qf[s], acc);
+        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(l16, 4 * s + q4)), qf[s], acc);
         float z[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = (16 * wave + 4 * q4 + e < nr) ? acc[e] * scale : -INFINITY;
+        for (int e = 0; e < 4; ++e) z[e] = (4 * q4 + e < nr) ? acc[e] * scale : -INFINITY;
         softmax_step<4>(st, z, false);
         pv = to_h4v(z[0], z[1], z[2], z[3]);
-      }
-    } else if (kind == kPageV) {
-      const int nr = rows_of_tile(g, t);
-      if (16 * wave < nr) {
+      } else if (kind == kPageV) {
         const int s4 = l16 & 3;
-        const int row = 16 * wave + 4 * q4 + (l16 >> 2);
+        const int row = 4 * q4 + (l16 >> 2);
 #pragma unroll
         for (int nn = 0; nn < 8; ++nn) {
           const v4h a = ld_tr(pg + swz(row, 2 * nn + (s4 >> 1)) + 8 * (s4 & 1));
           st.Ot[nn] = mfma16(a, pv, st.Ot[nn]);
         }
-      }
-    } else {
-      // kPageVV: fold this block's low-rank values, (p^T U) V_V + (sum p) a_v,
-      // as one product: row r of W^T is the block's low-rank weight sum, row r
-      // of the page a_v
-      const int nqv = round16(r + 1) >> 4;
-      const float llr = hq_sum(st.llr);
-      st.llr = 0.f;
-      v4h wh[4], wlo[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (k < nqv) {
-          v4f x = st.Wt[k];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 16 * k + 4 * q4 + e;
-            x[e] = j < r ? x[e] : (j == r ? llr : 0.f);
-          }
-          split4(x, wh[k], wlo[k]);
-          st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+      } else {
+        // V_V tile i: O^T += [V_V ; a_v]^T rows 16 i .. 16 i + 15 times W^T rows
+        // (row r of W^T: the block's low-rank weight sum, for a_v)
+        if (i == 0) {
+          llr_tot = hq_sum(st.llr);
+          st.llr = 0.f;
         }
-      }
-      const int s4 = l16 & 3;
+        v4f x = pick4(st.Wt, i);
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        v4f acc = st.Ot[nn];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (k < nqv) {
-            const int row = 16 * k + 4 * q4 + (l16 >> 2);
-            const v4h a = ld_tr(pg + swz(row, 2 * nn + (s4 >> 1)) + 8 * (s4 & 1));
-            acc = mfma16(a, wh[k], acc);
-            acc = mfma16(a, wlo[k], acc);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * i + 4 * q4 + e;
+          x[e] = j < r ? x[e] : (j == r ? llr_tot : 0.f);
         }
-        st.Ot[nn] = acc;
+        v4h wh, wlo;
+        split4(x, wh, wlo);
+        const int s4 = l16 & 3;
+        const int row = 4 * q4 + (l16 >> 2);
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) {
+          const v4h a = ld_tr(pg + swz(row, 2 * nn + (s4 >> 1)) + 8 * (s4 & 1));
+          st.Ot[nn] = mfma16(a, wlo, mfma16(a, wh, st.Ot[nn]));
+        }
+        if (i == g.nqv - 1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
   }
 
   // ---- the four waves' states at their common maximum, summed in wave order
-  lds_barrier();  // every wave is done with the ring
-  float* red = reinterpret_cast<float*>(smem);            // [4 waves][16 heads][132]
+  lds_barrier();  // every wave is done with its ring
+  float* red = reinterpret_cast<float*>(smem);                    // [4 waves][16 heads][132]
   float* wst = reinterpret_cast<float*>(smem + 4 * 16 * 132 * 4);  // m [4][16], l [4][16]
   const float lt = hq_sum(st.l);
   if (q4 == 0) {
@@ -781,7 +735,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_stream(const LayerArgs* __re
 
 // LDS bytes of the streaming attention parts (the routing and merge items of
 // the launch may need more: the caller takes the maximum).
-__attribute__((visibility("hidden"))) size_t dkv_stream_lds_bytes() { return (size_t)kSLdsTotal; }
+__attribute__((visibility("hidden"))) size_t dkv_stream_lds_bytes() { return (size_t)kWLds; }
 
 // Launch the streaming decode (see k_stream); table == nullptr: one layer, `one`.
 // The argument structs come as bytes: their types are private to each
