@@ -1406,7 +1406,8 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     // no item
   } else if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
-    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
+    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh,
+                            slot_tag(ld_dev(&D.ctrl[3])));
   } else if (t < D.n_part_end) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
@@ -1415,18 +1416,19 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     auto get_slot = [&]() {
       if (tid == 0) {
         const int32_t* sp = &D.slots[(int64_t)u * D.att.top_k + p];
+        const uint32_t tag = slot_tag(ld_dev(&D.ctrl[3]));
         unsigned n = 0;
         int32_t v = ld_dev(sp);
-        while (v == kSlotPending && n < kRouteWaitLimit) {
+        while (!slot_ready(v, tag) && n < kRouteWaitLimit) {
           __builtin_amdgcn_s_sleep(1);
           v = ld_dev(sp);
           ++n;
         }
-        if (v == kSlotPending) {
+        if (!slot_ready(v, tag)) {
           atomicOr(&D.ctrl[2], 1u);
-          v = -1 + kSlotCode;  // give up: an empty part
+          v = (int32_t)(tag | (uint32_t)(-1 + kSlotCode));  // give up: an empty part
         }
-        sh_slot = v - kSlotCode;
+        sh_slot = slot_value(v);
       }
       lds_barrier();
       return (int)sh_slot;
@@ -1512,9 +1514,11 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
     lds_barrier();
     if (sh_flag) {
       for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
-      for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
       if (tid < kQueues) D.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
-      if (tid == 0) D.ctrl[1] = 0u;
+      if (tid == 0) {
+        D.ctrl[1] = 0u;
+        D.ctrl[3] = D.ctrl[3] + 1u;  // the next launch's routed-slot tag
+      }
     }
   }
 }
@@ -1589,10 +1593,12 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArg
       for (int l = 0; l < L.n_layers; ++l) {
         const DecodeArgs& D = table[l].D;
         for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
-        for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
       }
       if (tid < kQueues) L.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
-      if (tid == 0) L.ctrl[1] = 0u;
+      if (tid == 0) {
+        L.ctrl[1] = 0u;
+        L.ctrl[3] = L.ctrl[3] + 1u;  // the next launch's routed-slot tag
+      }
     }
   }
 }
@@ -1624,6 +1630,7 @@ dkv_status check_pool_shape(const dkv_pool* P) {
   if (P->n_resid > DKV_MAX_RESID) return fail(DKV_ERR_UNSUPPORTED, "n_resid %d > 255", P->n_resid);
   if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
   if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
+  if (P->n_slots > DKV_MAX_SLOTS) return fail(DKV_ERR_UNSUPPORTED, "n_slots %d > %d", P->n_slots, DKV_MAX_SLOTS);
   if (P->resid_format != DKV_RESID_FP16 && P->resid_format != DKV_RESID_INT8 && P->resid_format != DKV_RESID_INT4)
     return fail(DKV_ERR_INVALID_ARG, "resid_format %d unknown", P->resid_format);
   if (P->rope_freq) {

@@ -270,10 +270,20 @@ __host__ __device__ constexpr size_t route_lds_words(int max_blocks, int nw) {
   return (size_t)2 * (size_t)(((max_blocks > 0 ? max_blocks : 1) + 3) & ~3) + (size_t)nw * 64 * kRedRow;
 }
 
-// Routed-slot words of the fused kernel hold pool slot + kSlotCode (1: no block),
-// so that 0, the state of zero-filled memory, means "routing not written yet".
+// Routed-slot words of the fused kernels hold the launch's tag in the top byte
+// and pool slot + kSlotCode in the low 24 bits (1: no block), so that a word
+// whose low bits are 0 (zero-filled memory) or whose tag is another launch's
+// means "not routed yet in this launch".  The tag is the low byte of the
+// workspace's launch counter (control word 3), which the last merge of each
+// launch advances: a routing word that arrives after its launch ended can
+// never be taken for the next launch's.
 constexpr int32_t kSlotPending = 0;
 constexpr int32_t kSlotCode = 2;
+__device__ __forceinline__ uint32_t slot_tag(uint32_t epoch) { return (epoch & 0xFFu) << 24; }
+__device__ __forceinline__ bool slot_ready(int32_t w, uint32_t tag) {
+  return ((uint32_t)w & 0xFF000000u) == tag && ((uint32_t)w & 0x00FFFFFFu) != 0u;
+}
+__device__ __forceinline__ int32_t slot_value(int32_t w) { return (int32_t)((uint32_t)w & 0x00FFFFFFu) - kSlotCode; }
 
 // Route one (sequence, KV head) unit u with a workgroup of NT threads.
 // lds: route_lds_words(max_blocks, NT / 64) words: ordered score keys [mb],
@@ -290,7 +300,7 @@ constexpr int32_t kSlotCode = 2;
 template <int NT>
 __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
                                            float* scores, int32_t* slots_out, uint32_t* lds,
-                                           RouteShared<NT / 64>& sh) {
+                                           RouteShared<NT / 64>& sh, uint32_t tag = 0u) {
   constexpr int NW = NT / 64;
   static_assert(NT == 256 || NT == 512, "route_unit: 256 histogram bins over the first 4 waves");
   constexpr int kBinWaves = 256 / 64;
@@ -383,7 +393,7 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
   auto emit = [&](int pos, int j, uint32_t k) {
     st_dev(&idx[(int64_t)u * top_k + pos], j);
     if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)slot_of[j] + kSlotCode);
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)(tag | (uint32_t)(slot_of[j] + kSlotCode)));
   };
 
   if (keff > 0) {
@@ -494,7 +504,7 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
   for (int pos = keff + tid; pos < top_k; pos += NT) {
     st_dev(&idx[(int64_t)u * top_k + pos], -1);
     if (scores) st_dev(&scores[(int64_t)u * top_k + pos], -INFINITY);
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], -1 + kSlotCode);
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)(tag | (uint32_t)(-1 + kSlotCode)));
   }
 }
 
@@ -661,8 +671,8 @@ __device__ __forceinline__ void merge_unit(const float* part_o, const float* par
 struct DecodeArgs {
   AttnArgs att;
   int32_t* idx;          // [units][top_k] routed logical blocks
-  int32_t* slots;        // [units][top_k] routed pool slots (-1: none); kSlotPending until routed
-  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, queue counters
+  int32_t* slots;        // [units][top_k] routed-slot words (launch tag | slot + kSlotCode)
+  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, [3] launch counter, queue counters
   uint32_t* unit_done;   // [units] parts finished
   f16* out;
   float* out_lse;

@@ -592,7 +592,6 @@ __global__ __launch_bounds__(kJoinThreads) void k_join(JoinArgs a) {
   float* C = M + kJoinR * kJoinR;
   float* Gg = C + kJoinR * kJoinR;
   float* red = Gg + kJoinR * kJoinR;
-  float* T = reinterpret_cast<float*>(Us);
   const int item = blockIdx.x / a.n_heads, h = blockIdx.x % a.n_heads;
   const int t = threadIdx.x, r = a.rank;
   const int s = a.slots[item], g = a.entries[item];
@@ -628,26 +627,64 @@ __global__ __launch_bounds__(kJoinThreads) void k_join(JoinArgs a) {
     eo = __builtin_fmaf(c, gc, eo);
   }
   __syncthreads();
+  // X = M Gg^-1 (least squares: U' = U X solves U' V_g = U V_cur best), by a
+  // Cholesky factor Gg = L L^T computed in place; a pivot below 1e-6 of the
+  // largest diagonal drops its direction (rows of V_g are meant to be
+  // independent).  X takes the place of the two bases, now free.
+  float* X = reinterpret_cast<float*>(Vc);
+  __shared__ float piv_floor;
+  if (t == 0) {
+    float mx = 0.f;
+    for (int k = 0; k < r; ++k) mx = fmaxf(mx, Gg[k * r + k]);
+    piv_floor = 1e-6f * mx;
+  }
+  __syncthreads();
+  for (int k = 0; k < r; ++k) {
+    if (t == 0) {
+      const float d = Gg[k * r + k];
+      Gg[k * r + k] = d > piv_floor ? sqrtf(d) : 0.f;
+    }
+    __syncthreads();
+    const float lkk = Gg[k * r + k];
+    for (int i = k + 1 + t; i < r; i += kJoinThreads) Gg[i * r + k] = lkk > 0.f ? Gg[i * r + k] / lkk : 0.f;
+    __syncthreads();
+    const int m = r - k - 1;
+    for (int e = t; e < m * m; e += kJoinThreads) {
+      const int i = k + 1 + e / m, j = k + 1 + e % m;
+      if (j <= i) Gg[i * r + j] -= Gg[i * r + k] * Gg[j * r + k];
+    }
+    __syncthreads();
+  }
+  if (t < r) {
+    // row t of X: x L L^T = m_t; forward L y = m_t^T, then backward L^T x^T = y
+    float* x = X + t * r;
+    for (int i = 0; i < r; ++i) {
+      float acc = M[t * r + i];
+      for (int j = 0; j < i; ++j) acc -= Gg[i * r + j] * x[j];
+      const float lii = Gg[i * r + i];
+      x[i] = lii > 0.f ? acc / lii : 0.f;
+    }
+    for (int i = r - 1; i >= 0; --i) {
+      float acc = x[i];
+      for (int j = i + 1; j < r; ++j) acc -= Gg[j * r + i] * x[j];
+      const float lii = Gg[i * r + i];
+      x[i] = lii > 0.f ? acc / lii : 0.f;
+    }
+  }
+  __syncthreads();
   if (t < 255) {
     for (int j = 0; j < r; ++j) {
       float acc = 0.f;
-      for (int i = 0; i < r; ++i) acc = __builtin_fmaf((float)Us[t * r + i], M[i * r + j], acc);
+      for (int i = 0; i < r; ++i) acc = __builtin_fmaf((float)Us[t * r + i], X[i * r + j], acc);
       if (a.write) U[t * r + j] = (f16)acc;
     }
   }
-  __syncthreads();  // every thread is done with Us: T takes its place
-  for (int e = t; e < r * r; e += kJoinThreads) {
-    const int i = e / r, j = e % r;
-    float acc = 0.f;
-    for (int k = 0; k < r; ++k) acc = __builtin_fmaf(M[i * r + k], Gg[k * r + j], acc);
-    T[e] = acc;
-  }
-  __syncthreads();
+  // retained energy |U X V_g|^2 = tr(C X Gg X^T) = tr(C M X^T), over tr(C G_cur)
   float en = 0.f;
   for (int e = t; e < r * r; e += kJoinThreads) {
     const int i = e / r, j = e % r;
     float q = 0.f;
-    for (int k = 0; k < r; ++k) q = __builtin_fmaf(T[i * r + k], M[j * r + k], q);
+    for (int k = 0; k < r; ++k) q = __builtin_fmaf(M[i * r + k], X[j * r + k], q);
     en = __builtin_fmaf(C[e], q, en);
   }
   const float so = block_sum(eo, red);

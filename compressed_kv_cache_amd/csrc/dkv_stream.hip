@@ -346,18 +346,19 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
       int32_t slot = -1;
       if (lane < kn) {
         const int32_t* sp = &slots[(int64_t)u * A.top_k + k0 + lane];
+        const uint32_t tag = slot_tag(ld_dev(&ctrl[3]));
         unsigned n = 0;
         int32_t v = ld_dev(sp);
-        while (v == kSlotPending && n < kRouteWaitLimit) {
+        while (!slot_ready(v, tag) && n < kRouteWaitLimit) {
           __builtin_amdgcn_s_sleep(1);
           v = ld_dev(sp);
           ++n;
         }
-        if (v == kSlotPending) {
+        if (!slot_ready(v, tag)) {
           atomicOr(&ctrl[2], 1u);
-          v = -1 + kSlotCode;
+          v = (int32_t)(tag | (uint32_t)(-1 + kSlotCode));
         }
-        slot = v - kSlotCode;
+        slot = slot_value(v);
         if (slot >= P.n_slots) slot = -1;
       }
       const bool ok = slot >= 0;
@@ -636,7 +637,8 @@ __device__ __forceinline__ void stream_item(const PoolArgs& P, const BatchArgs& 
     // no item
   } else if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
-    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh);
+    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh,
+                            slot_tag(ld_dev(&D.ctrl[3])));
   } else if (t < D.n_part_end) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
@@ -723,10 +725,12 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_stream(const LayerArgs* __re
       for (int l = 0; l < L.n_layers; ++l) {
         const DecodeArgs& D = table ? table[l].D : la.D;
         for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
-        for (int i = tid; i < D.n_route * D.att.top_k; i += kAttThreads) D.slots[i] = kSlotPending;  // 0
       }
       if (tid < kQueues) L.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
-      if (tid == 0) L.ctrl[1] = 0u;
+      if (tid == 0) {
+        L.ctrl[1] = 0u;
+        L.ctrl[3] = L.ctrl[3] + 1u;  // the next launch's routed-slot tag
+      }
     }
   }
 }

@@ -192,13 +192,16 @@ def _orthonormal_rows(rng: np.random.Generator, lead: tuple, r: int, d: int) -> 
     return out.reshape(lead + (r, d))
 
 
-def _positions(rng: np.random.Generator, lead: tuple, n_resid: int) -> np.ndarray:
-    """n_resid distinct in-block positions from 1..255, ascending, per entry."""
+def _positions(rng: np.random.Generator, lead: tuple, n_resid: int, ascending: bool = False) -> np.ndarray:
+    """n_resid distinct in-block positions from 1..255 per entry, in the seeded
+    random order of the draw (the decode takes them in any order), or ascending."""
     if n_resid == 0:
         return np.zeros(lead + (0,), dtype=np.uint8)
     keys = rng.random(size=lead + (LOWRANK_ROWS,))
     pos = np.argsort(keys, axis=-1, kind="stable")[..., :n_resid] + 1
-    return np.sort(pos, axis=-1).astype(np.uint8)
+    if ascending:
+        pos = np.sort(pos, axis=-1)
+    return pos.astype(np.uint8)
 
 
 def _quantised_residuals(rng: np.random.Generator, lead: tuple, n_resid: int, d: int, fmt: int):
@@ -471,7 +474,7 @@ def make_seal_input(seed: int, n_blocks: int, n_kv_heads: int, *, width: int, tr
     w = _orthonormal_rows(streams[2], lead, true_rank, two_d)
     x += np.matmul(c, w)
     x += _normal(streams[3], lead + (BLOCK_SIZE, two_d), noise)
-    pos = _positions(streams[4], lead, n_outliers)
+    pos = _positions(streams[4], lead, n_outliers, ascending=True)
     bump = _normal(streams[5], lead + (n_outliers, two_d), outlier_std)
     for idx in np.ndindex(*lead):
         x[idx][pos[idx].astype(np.int64)] += bump[idx]

@@ -42,9 +42,10 @@
  *     host before anything is enqueued; on failure the call returns an error
  *     code, enqueues nothing, and dkv_last_error() describes the problem.
  *   - Contents of device arrays are preconditions and are not checked on the
- *     hot path: residual positions distinct in 1..255, finite values.  Block
- *     table entries outside [0, n_slots) and idx entries outside
- *     [0, n_blocks[b]) are treated as empty blocks (no rows), never read.
+ *     hot path: residual positions distinct in 1..255 (in any order), finite
+ *     values.  Block table entries outside [0, n_slots) and idx entries
+ *     outside [0, n_blocks[b]) are treated as empty blocks (no rows), never
+ *     read.
  *   - Alignment: every fp16 / fp32 array base and every slot / head stride
  *     (in bytes) must be a multiple of 16, except `u` (a multiple of 8 bytes
  *     when r is a multiple of 4, else of 2) and `resid_pos` (any alignment);
@@ -72,6 +73,7 @@ extern "C" {
 #define DKV_MAX_RESID 255
 #define DKV_MAX_GROUP 16
 #define DKV_MAX_ROUTE_BLOCKS 12288
+#define DKV_MAX_SLOTS ((1 << 24) - 3)  /* blocks a pool may hold */
 
 /* Storage format of the residual rows (README "Physical 4-Bit Group-Quantized
  * Residual Buffers" and its "Tunable Quantization Dials"): fp16 rows, or
@@ -87,7 +89,7 @@ extern "C" {
 typedef int32_t dkv_status;
 #define DKV_OK 0
 #define DKV_ERR_INVALID_ARG 1  /* null pointer, negative size, bad combination */
-#define DKV_ERR_UNSUPPORTED 2  /* d != 128, block != 256, r > 64, R > 255, G > 16, misalignment */
+#define DKV_ERR_UNSUPPORTED 2  /* d != 128, block != 256, r > 64, R > 255, G > 16, n_slots > DKV_MAX_SLOTS, misalignment */
 #define DKV_ERR_WORKSPACE 3    /* workspace missing or smaller than dkv_decode_workspace_size() */
 #define DKV_ERR_HIP 4          /* a HIP launch failed; see dkv_last_error() */
 
@@ -138,12 +140,16 @@ typedef struct dkv_pool {
   const float* rope_freq;
   const int32_t* slot_pos;
   /* Shared basis (README "Key Environment Knobs", DKV_SHARED_BASIS and
-   * DKV_SHARED_BASIS_FRAC: blocks whose delta subspaces agree read one basis).
+   * DKV_SHARED_BASIS_FRAC; "3. Shared Low-Rank Bases"): several blocks may
+   * use one stored V_K, V_V pair, so the basis store can hold fewer entries
+   * than the pool has slots.
    * NULL, or int32 [n_slots] device: the block in slot s reads its V_K and V_V
-   * from entry basis_of[s] of vk and vv (at their slot stride), n_basis entries;
-   * its anchors, U and residual rows stay in slot s.  Needs an un-rotated pool
-   * (the pages refuse sharing with rotated keys).  A block whose entry lies
-   * outside [0, n_basis) contributes no rows and its routing key is not written. */
+   * from entry basis_of[s] of vk and vv (entry e at vk.ptr + e * vk.slot_stride
+   * + h * vk.head_stride: the basis store may be an array of its own, n_basis
+   * entries); its anchors, U and residual rows stay in slot s.  Needs an
+   * un-rotated pool (the pages refuse sharing with rotated keys).  A block
+   * whose entry lies outside [0, n_basis) contributes no rows and its routing
+   * key is not written. */
   const int32_t* basis_of;
   int32_t n_basis;
   int32_t reserved2;
@@ -282,7 +288,11 @@ dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batc
  *              dkv_decode with the same or a larger-or-equal shape).  Calls
  *              that share a workspace must not overlap.  Word 2 of the
  *              workspace (uint32 at byte 8) is a sticky flag set if a block
- *              ever gave up waiting for its routing (never in a correct run).
+ *              ever gave up waiting for its routing (never in a correct run);
+ *              word 3 counts launches: the routed-slot words a launch writes
+ *              carry its low byte, so that a routing that finishes after its
+ *              launch gave up on it is never read by a later launch (its
+ *              routed indices in out_idx may still be overwritten late).
  *   out:     fp16 [B][Hq][d] out;  out_lse: fp32 [B][Hq] out.
  *   out_idx: int32 [B][Hkv][top_k] out (the routed blocks), or NULL. */
 dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
@@ -384,17 +394,20 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
                            void* stream);
 
 /* Join blocks to a shared basis: the write side of DKV_SHARED_BASIS (README
- * "Key Environment Knobs": blocks whose delta subspaces agree read one basis;
- * joins report the retained delta energy).  For item i, block slot s =
- * slots[i] (current basis entry cur = basis_of[s], or s without sharing) and
- * target entry g = entries[i], per KV head h, with V = [V_K | V_V]:
- *   M = V_cur V_g^T (r x r),  U' = U M  (U' V_g is the least-squares
- *   projection of the block's delta U V_cur onto the rows of V_g),
- *   energy[i * n_kv_heads + h] = |U' V_g|^2 / |U V_cur|^2,
- * fp32 from the fp16 arrays.  write != 0 stores U' into slot s's U (fp16, round
- * to nearest even); write = 0 only scores the candidate.  The caller then sets
- * basis_of[s] = g (its own array) and recomputes the routing key
- * (dkv_route_keys).  Entries index vk / vv: [0, n_basis) with basis_of set,
+ * "Key Environment Knobs" and "3. Shared Low-Rank Bases": a joined block reads
+ * the group's basis, keeping the part of its delta the group's subspace can
+ * express; joins are judged by the retained energy).  For item i, block slot
+ * s = slots[i] (current basis entry cur = basis_of[s], or s without sharing)
+ * and target entry g = entries[i], per KV head h, with V = [V_K | V_V]:
+ *   M = V_cur V_g^T,  U' = U M (V_g V_g^T)^-1  (the least-squares solution of
+ *   U' V_g = U V_cur; U M when the rows of V_g are orthonormal, as the sealer
+ *   writes them),  energy[i * n_kv_heads + h] = |U' V_g|^2 / |U V_cur|^2,
+ * fp32 from the fp16 arrays; V_g V_g^T is factored by Cholesky, and a pivot
+ * below 1e-6 of its largest diagonal drops that direction (rows of V_g are
+ * meant to be linearly independent).  write != 0 stores U' into slot s's U
+ * (fp16, round to nearest even); write = 0 only scores the candidate.  The
+ * caller then sets basis_of[s] = g (its own array) and recomputes the routing
+ * key (dkv_route_keys).  Entries index vk / vv: [0, n_basis) with basis_of set,
  * else [0, n_slots).  An item with a slot or entry out of range writes energy
  * -1 and changes nothing.  Slots of one call must be distinct.
  *   slots, entries: int32 [n] device;  energy: fp32 [n][n_kv_heads] device out. */

@@ -42,9 +42,9 @@ What it computes (sources are the pages on DKV, cited by title and section):
   "rope_base" and "slot_pos" (absolute position of token 0 of the block held
   in each slot) is such a pool.
 * Shared basis -- README "Key Environment Knobs" (DKV_SHARED_BASIS and
-  DKV_SHARED_BASIS_FRAC): blocks whose delta subspaces agree read one basis
-  row instead of each storing its own V, and the pool refuses the combination
-  with rotated keys.  A pool dict that carries "basis_of" (per slot, the entry
+  DKV_SHARED_BASIS_FRAC) and "3. Shared Low-Rank Bases": several blocks may
+  use one stored V_K, V_V pair in place of one each; the pages allow this only
+  for pools of un-rotated keys.  A pool dict that carries "basis_of" (per slot, the entry
   of vk / vv that holds the block's V_K and V_V) is such a pool; the block's
   own anchor, U and residual rows stay per slot.
 

@@ -142,17 +142,24 @@ def reconstruct(sealed: dict):
 
 def join_basis(u, vk, vv, vk_g, vv_g):
     """Join a block to a shared basis (README "Key Environment Knobs",
-    DKV_SHARED_BASIS: blocks read one basis row instead of each storing its own
-    V; a join keeps the part of the block's delta that lies in the shared
-    subspace).  With V = [V_K | V_V] and V_g = [V_K,g | V_V,g] (r x 256, rows
-    orthonormal for a basis written by the sealer): M = V V_g^T, U' = U M, so
-    that U' V_g is the projection of the block's delta U V onto the rows of V_g.
-    The retained energy is |U' V_g|^2 / |U V|^2 (1 when the subspaces agree).
-    Returns (U' [255 x r], retained energy), float64."""
+    DKV_SHARED_BASIS, and "3. Shared Low-Rank Bases": a joined block reads the
+    group's basis instead of its own V, and keeps the part of its delta that
+    the group's subspace can express).  With V = [V_K | V_V] and V_g = [V_K,g |
+    V_V,g] (r x 256, linearly independent rows), U' is the least-squares
+    solution of U' V_g = U V:
+
+        U' = U V V_g^T (V_g V_g^T)^-1,
+
+    which for rows of V_g that are orthonormal (a basis written by the sealer)
+    is the pages' U' = U (V V_g^T).  The retained energy is |U' V_g|^2 /
+    |U V|^2, the pages' tr(G C C^T) / tr(G V V^T) (G = U^T U, C = V V_g^T) for
+    such a V_g; 1 when the subspaces agree.  Returns (U' [255 x r], retained
+    energy), float64."""
     U = np.asarray(u, np.float64)
     V = np.hstack([np.asarray(vk, np.float64), np.asarray(vv, np.float64)])
     Vg = np.hstack([np.asarray(vk_g, np.float64), np.asarray(vv_g, np.float64)])
-    up = U @ (V @ Vg.T)
+    M = V @ Vg.T
+    up = np.linalg.solve(Vg @ Vg.T, (U @ M).T).T
     num = np.sum((up @ Vg) ** 2)
     den = np.sum((U @ V) ** 2)
     return up, (num / den if den > 0 else 1.0)

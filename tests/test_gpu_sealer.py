@@ -264,3 +264,7 @@ def test_join_basis(lib, variant):
             got = u1[s, h].astype(np.float64)
             assert np.all(np.abs(got - ref_u) <= 1e-3 * np.abs(ref_u) + 1e-5 * np.abs(ref_u).max()), (i, h)
             assert abs(e1[i, h] - ref_e) <= 1e-4, (i, h, e1[i, h], ref_e)
+            if g == cur:
+                # its own basis (joint rows of V_K, V_V not orthonormal here: the
+                # synthetic bases are orthonormal in K and in V separately)
+                assert abs(e1[i, h] - 1.0) <= 1e-4, (i, h, e1[i, h])

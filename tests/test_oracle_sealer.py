@@ -171,3 +171,60 @@ def test_join_is_the_least_squares_projection():
     up0, e0 = S.join_basis(U, W[:10, :128], W[:10, 128:], W[10:, :128], W[10:, 128:])
     assert np.abs(up0).max() < 1e-12 and e0 < 1e-24
     assert 0.0 < e < 0.2
+
+
+def test_join_energy_closed_form_at_interior_values():
+    """V_g shares the first k of the block's basis rows and replaces the rest by
+    rows orthogonal to all of V: the join keeps exactly the first k columns of
+    U, so the retained energy is their share of |U|^2 (V orthonormal)."""
+    rng = np.random.default_rng(23)
+    r, k = 12, 5
+    W = _orth_rows(rng, 2 * r)                 # 24 orthonormal rows
+    V = W[:r]
+    Vg = np.vstack([W[:k], W[r:r + (r - k)]])
+    U = rng.standard_normal((255, r)) * (0.9 ** np.arange(r))
+    up, e = S.join_basis(U, V[:, :128], V[:, 128:], Vg[:, :128], Vg[:, 128:])
+    want = np.sum(U[:, :k] ** 2) / np.sum(U ** 2)
+    assert 0.5 < want < 0.9                    # an interior value
+    assert abs(e - want) < 1e-12
+    np.testing.assert_allclose(up[:, :k], U[:, :k], atol=1e-12)
+    np.testing.assert_allclose(up[:, k:], 0.0, atol=1e-12)
+
+
+def test_join_energy_is_the_pages_trace_ratio():
+    """For V_g with orthonormal rows the energy equals tr(G C C^T) / tr(G V V^T)
+    with G = U^T U and C = V V_g^T (README "3. Shared Low-Rank Bases"), at
+    interior values: V_g mixes the block's rows with new directions."""
+    rng = np.random.default_rng(24)
+    r = 10
+    V = _orth_rows(rng, r)
+    for t in (0.2, 0.5, 0.8):
+        N = _orth_rows(rng, r)
+        # rows of V_g: orthonormal rows spanning a mix of V and N
+        Vg = np.linalg.qr((np.sqrt(1 - t) * V + np.sqrt(t) * N).T)[0].T
+        U = rng.standard_normal((255, r)) * (0.8 ** np.arange(r))
+        _, e = S.join_basis(U, V[:, :128], V[:, 128:], Vg[:, :128], Vg[:, 128:])
+        G = U.T @ U
+        C = V @ Vg.T
+        want = np.trace(G @ C @ C.T) / np.trace(G @ V @ V.T)
+        assert 0.05 < want < 0.98
+        assert abs(e - want) < 1e-10
+
+
+def test_join_with_a_basis_whose_rows_are_not_orthonormal():
+    """V_K and V_V orthonormal each (joint Gram 2 I), or V_g any full-rank r x 256
+    matrix: U' is numpy's least-squares solution of X V_g = U V, and joining to
+    the block's own basis keeps U and all of the energy."""
+    rng = np.random.default_rng(25)
+    r = 8
+    vk, vv = _orth_rows(rng, r, 128), _orth_rows(rng, r, 128)
+    U = rng.standard_normal((255, r))
+    up, e = S.join_basis(U, vk, vv, vk, vv)
+    np.testing.assert_allclose(up, U, atol=1e-12)
+    assert abs(e - 1.0) < 1e-12
+    V = np.hstack([vk, vv])
+    Vg = rng.standard_normal((r, 256))
+    up, e = S.join_basis(U, vk, vv, Vg[:, :128], Vg[:, 128:])
+    X = np.linalg.lstsq(Vg.T, (U @ V).T, rcond=None)[0].T
+    np.testing.assert_allclose(up, X, atol=1e-10)
+    assert abs(e - np.sum((X @ Vg) ** 2) / np.sum((U @ V) ** 2)) < 1e-12
