@@ -28,6 +28,8 @@
 
 #include "dkv_common.h"
 
+#include <mutex>
+
 // The streaming launch (dkv_stream.hip).
 size_t dkv_stream_lds_bytes();
 hipError_t dkv_stream_launch(const void* table, const void* one, const void* layers, int n_items, size_t lds,
@@ -2027,6 +2029,33 @@ __attribute__((visibility("hidden"))) void dkv_clear_error_message() { g_err[0] 
 // C ABI
 // ----------------------------------------------------------------------------
 
+// Scratch of dkv_decode_noalloc: the decode workspace of callers that cannot
+// allocate, in a fixed device array (each GPU holds its own copy for the life
+// of the process).  Host code must not use the array's name as a device
+// address: its address on a device comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept here.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+static dkv_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DKV_ERR_HIP, "hipGetDevice failed or device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DKV_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DKV_OK;
+}
+
 template <int NMAX, int QK>
 static dkv_status launch_layers_q(const dkv_layers_plan* plan, const LayersArgs& L, hipStream_t st) {
   static bool attr_set = false;
@@ -2286,6 +2315,31 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
   }
   return decode_impl(pool, batch, top_k, scale, workspace, workspace_bytes, out, out_lse, out_idx, events, stream);
 }
+
+dkv_status dkv_decode_noalloc(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale, void* out,
+                              float* out_lse, int32_t* out_idx, void* stream) {
+  g_err[0] = 0;
+  dkv_status s;
+  if ((s = check_pool_shape(pool))) return s;
+  if (top_k < 0) return fail(DKV_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+  if ((s = check_batch(pool, batch, top_k > 0, true))) return s;
+  const size_t need = dkv_decode_workspace_size(pool, batch, top_k);
+  if (need > kScratchBytes)
+    return fail(DKV_ERR_WORKSPACE, "this decode needs %zu bytes of scratch; dkv_decode_noalloc holds %zu (use dkv_decode "
+                "with a workspace)", need, kScratchBytes);
+  if (batch->batch == 0) return DKV_OK;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws))) return s;
+  // the control area starts at zero for this call, whatever an earlier call left
+  const WsLayout w = decode_layout(pool, batch, top_k);
+  const int words = (int)(w.ctrl_bytes / 4);
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)ws, words);
+  if ((s = launched("k_zero_words"))) return s;
+  return decode_impl(pool, batch, top_k, scale, ws, kScratchBytes, out, out_lse, out_idx, nullptr, stream);
+}
+
+size_t dkv_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 // ---- layer-batched decode -------------------------------------------------
 

@@ -33,7 +33,8 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_decode_workspace_size", "dkv_decode_workspace_init", "dkv_decode",
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
             "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
-            "dkv_seal_blocks", "dkv_rope_freqs", "dkv_join_basis")
+            "dkv_seal_blocks", "dkv_rope_freqs", "dkv_join_basis", "dkv_decode_noalloc",
+            "dkv_decode_noalloc_max_bytes")
 
 
 class DKVError(RuntimeError):
@@ -136,6 +137,10 @@ def load(path: str = LIB_PATH):
     lib.dkv_decode_profiled.argtypes = [P, Bp, i32, f32, vp, ctypes.c_size_t, vp, vp, vp,
                                         ctypes.POINTER(ctypes.c_void_p), vp]
     lib.dkv_decode_profiled.restype = i32
+    lib.dkv_decode_noalloc.argtypes = [P, Bp, i32, f32, vp, vp, vp, vp]
+    lib.dkv_decode_noalloc.restype = i32
+    lib.dkv_decode_noalloc_max_bytes.argtypes = []
+    lib.dkv_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -497,6 +502,24 @@ def decode(pool: Pool, batch: Batch, top_k: int, scale: float, workspace=None, o
     _check(lib.dkv_decode(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, scale,
                           _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                           _ptr(out), _ptr(out_lse), _ptr(out_idx), _stream(stream)), "dkv_decode")
+    return out, out_lse, out_idx
+
+
+def decode_noalloc(pool: Pool, batch: Batch, top_k: int, scale: float, out=None, out_lse=None, out_idx=None,
+                   return_idx: bool = True, stream=None):
+    """dkv_decode_noalloc: one fused decode step with the library's fixed scratch
+    as its workspace.  Returns (out, lse, idx or None)."""
+    import torch
+    lib = load()
+    dev = batch.tensors["q"].device
+    if out is None:
+        out = torch.empty((batch.batch, batch.n_q_heads, HEAD_DIM), dtype=torch.float16, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((batch.batch, batch.n_q_heads), dtype=torch.float32, device=dev)
+    if out_idx is None and return_idx and top_k > 0:
+        out_idx = torch.empty((batch.batch, pool.n_kv_heads, top_k), dtype=torch.int32, device=dev)
+    _check(lib.dkv_decode_noalloc(ctypes.byref(pool.c), ctypes.byref(batch.c), top_k, scale, _ptr(out),
+                                  _ptr(out_lse), _ptr(out_idx), _stream(stream)), "dkv_decode_noalloc")
     return out, out_lse, out_idx
 
 

@@ -308,6 +308,22 @@ dkv_status dkv_decode_profiled(const dkv_pool* pool, const dkv_batch* batch, int
                                float* out_lse, int32_t* out_idx, void* const* events,
                                void* stream);
 
+/* dkv_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same decode, with its workspace in a fixed device array of
+ * dkv_decode_noalloc_max_bytes() bytes (16 MiB) that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates and frees
+ * nothing; it clears the array's control area with a small kernel on
+ * `stream`, then runs dkv_decode on it.  A decode whose
+ * dkv_decode_workspace_size() exceeds the array returns DKV_ERR_WORKSPACE and
+ * enqueues nothing.  All calls on one GPU share that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must not be
+ * made; consecutive calls on one stream are fine.  Arguments and results as
+ * dkv_decode. */
+dkv_status dkv_decode_noalloc(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,
+                              void* out, float* out_lse, int32_t* out_idx, void* stream);
+size_t dkv_decode_noalloc_max_bytes(void);
+
 /* ---- Layer-batched decode -------------------------------------------------
  * The fused decode step (dkv_decode) of n_layers independent layers in ONE
  * launch, so that the routing, block-attention and merge phases of different
