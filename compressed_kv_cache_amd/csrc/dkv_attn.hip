@@ -30,10 +30,16 @@
 
 #include <mutex>
 
-// The streaming launch (dkv_stream.hip).
+// The streaming launches (dkv_stream.hip).
 size_t dkv_stream_lds_bytes();
 hipError_t dkv_stream_launch(const void* table, const void* one, const void* layers, int n_items, size_t lds,
                              hipStream_t st);
+hipError_t dkv_stream_step(const void* table, const void* layers_a, int n_items_a, size_t lds_a, const int32_t* sched,
+                           int n_waves, int n_sched_items, int top_k, int n_layers, int n_units, hipStream_t st);
+
+#include <algorithm>
+#include <queue>
+#include <vector>
 
 namespace {
 
@@ -1903,9 +1909,6 @@ struct WsLayout {
 // Window rows per window part of the streaming launch: 256 with one launch
 // per layer (more, shorter parts), kWinChunk with several layers.
 constexpr int kStreamWinChunk = 256;
-// Routed blocks per block part of the streaming launch with several layers
-// (one with one layer per launch, where parallelism matters most).
-constexpr int kStreamLayerBlocks = 4;
 
 int stream_win_parts(int window, int chunk) {
   const int n = (window + chunk - 1) / chunk;
@@ -1945,11 +1948,14 @@ bool stream_eligible(const dkv_pool* P, const dkv_batch* B) {
   return al(B->q, 16) && al(B->win_k, 16) && al(B->win_v, 16);
 }
 
-WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold = true) {
+// min_parts: at least this many parts per unit (the layer-batched streams' schedule)
+WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold = true,
+                       size_t min_parts = 0) {
   WsLayout w;
   const size_t B = (size_t)batch->batch;
   const size_t units = B * (size_t)pool->n_kv_heads;
-  const size_t n_parts = reserved_parts(pool, batch, top_k, fold);
+  size_t n_parts = reserved_parts(pool, batch, top_k, fold);
+  if (min_parts > n_parts) n_parts = min_parts;
   const size_t rows = B * (size_t)batch->n_q_heads;
   w.unit_done = kCtrlHeaderBytes;
   w.slots = w.unit_done + align256(units * 4);
@@ -1965,8 +1971,9 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
                              uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
-                             bool fold = true, bool row_merges = true, int stream_blocks = 0, int stream_chunk = 0) {
-  const WsLayout w = decode_layout(pool, batch, top_k, fold);
+                             bool fold = true, bool row_merges = true, int stream_blocks = 0, int stream_chunk = 0,
+                             size_t min_parts = 0) {
+  const WsLayout w = decode_layout(pool, batch, top_k, fold, min_parts);
   // folded, each routed-block part also takes its share of the window;
   // otherwise the window comes in chunks of kWinChunk rows.  The streaming
   // launch has parts of stream_blocks routed blocks and window parts of
@@ -2352,15 +2359,55 @@ size_t dkv_decode_layers_table_size(int32_t n_layers) {
 // one load phase rather than two
 constexpr bool kLayersFoldWindow = false;
 
-static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
-  return align256(decode_layout(pool, batch, top_k, kLayersFoldWindow).total);
+// Streams of the layer-batched streaming launches: at most this many one-wave
+// workgroups (eight per CU of the MI355X's 256).
+constexpr int kStreamMaxWaves = 2048;
+// Work items of the streams: window rows and residual rows in items of at most
+// these many rows; each routed block's low-rank part is an item of its own.
+constexpr int kStreamWinRows = 128;
+constexpr int kStreamResRows = 64;
+
+static bool layers_stream(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
+  if (top_k < 1) return false;
+  for (int l = 0; l < n_layers; ++l)
+    if (!stream_eligible(&pools[l], &batches[l])) return false;
+  return true;
+}
+
+// the streams' work items of one unit: its window items, then per routed rank
+// a low-rank item and the residual items
+static int64_t stream_unit_items(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
+  const int64_t nwin = (batch->window + kStreamWinRows - 1) / kStreamWinRows;
+  const int64_t nres = (pool->n_resid + kStreamResRows - 1) / kStreamResRows;
+  return nwin + (int64_t)top_k * (1 + nres);
+}
+
+static int64_t stream_sched_items(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
+  int64_t n = 0;
+  for (int l = 0; l < n_layers; ++l)
+    n += (int64_t)batches[l].batch * pools[l].n_kv_heads * stream_unit_items(&pools[l], &batches[l], top_k);
+  return n;
+}
+
+static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool streams) {
+  const size_t min_parts = streams ? (size_t)stream_unit_items(pool, batch, top_k) : 0;
+  return align256(decode_layout(pool, batch, top_k, kLayersFoldWindow, min_parts).total);
+}
+
+// the streams' schedule: wave offsets, four words per item, a part count per (layer, unit)
+static size_t stream_sched_words(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
+  const int64_t items = stream_sched_items(pools, batches, n_layers, top_k);
+  const int64_t waves = items < kStreamMaxWaves ? items : kStreamMaxWaves;
+  return (size_t)(waves + 1 + 4 * items + (int64_t)n_layers * batches[0].batch * pools[0].n_kv_heads);
 }
 
 size_t dkv_decode_layers_workspace_size(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
                                         int32_t top_k) {
   if (!pools || !batches || n_layers < 1 || top_k < 0) return 0;
+  const bool streams = layers_stream(pools, batches, n_layers, top_k);
   size_t total = kCtrlHeaderBytes;
-  for (int l = 0; l < n_layers; ++l) total += layer_region_bytes(&pools[l], &batches[l], top_k);
+  for (int l = 0; l < n_layers; ++l) total += layer_region_bytes(&pools[l], &batches[l], top_k, streams);
+  if (streams) total += align256(stream_sched_words(pools, batches, n_layers, top_k) * 4);
   return total;
 }
 
@@ -2389,9 +2436,7 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
   dkv_status s = DKV_OK;
   size_t shm = 0, off = kCtrlHeaderBytes;
   unsigned char* ws = (unsigned char*)workspace;
-  bool streaming = true;
-  for (int l = 0; l < n_layers; ++l) streaming = streaming && stream_eligible(&pools[l], &batches[l]);
-  const int sblocks = streaming ? (top_k < kStreamLayerBlocks ? (top_k > 0 ? top_k : 1) : kStreamLayerBlocks) : 0;
+  const bool streams = layers_stream(pools, batches, n_layers, top_k);
   for (int l = 0; l < n_layers && s == DKV_OK; ++l) {
     const dkv_pool* pool = &pools[l];
     const dkv_batch* batch = &batches[l];
@@ -2420,19 +2465,116 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
       break;
     }
     size_t shm_l = 0;
+    const size_t min_parts = streams ? (size_t)stream_unit_items(pool, batch, top_k) : 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
                                out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
-                               /*row_merges=*/false, sblocks, kWinChunk)))
+                               /*row_merges=*/false, 0, kWinChunk, min_parts)))
       break;
     host[l].P = make_pool_args(pool);
     host[l].Bt = make_batch_args(pool, batch);
     host[l].nrq = host[l].D.att.rq / 16;
+    if (streams) {
+      // the first launch of the step holds the routings only; the partials are
+      // the streams' runs' (at most one per item of the unit)
+      DecodeArgs& D = host[l].D;
+      D.att.n_block_parts = 0;
+      D.att.n_win_parts = 0;
+      D.att.items_per_unit = 0;
+      D.att.n_parts = (int)min_parts;
+      D.merges = 0;
+      D.n_part_end = D.n_route;
+      D.n_items = D.n_route;
+    }
     if (shm_l > shm) shm = shm_l;
-    off += layer_region_bytes(pool, batch, top_k);
+    off += layer_region_bytes(pool, batch, top_k, streams);
   }
+  // The streams' schedule: every unit's work items in order (layer, batch row,
+  // kv head; window items, then per routed rank its low-rank item and its
+  // residual items), cut into n_waves contiguous segments of about equal cost
+  // (bytes, plus a fixed cost per page).  A wave's consecutive items of one
+  // unit form a run: one attention state, one partial.
+  std::vector<int32_t> sched;
+  int n_waves = 0;
+  int64_t n_sched = 0;
+  if (s == DKV_OK && streams) {
+    const int units = b0.batch * p0.n_kv_heads;
+    n_sched = stream_sched_items(pools, batches, n_layers, top_k);
+    if (n_sched > 0x3FFFFFFF || n_layers > 0xFFFF || top_k > 0xFFFF || b0.batch > 0xFFFF ||
+        p0.n_kv_heads > 0xFFFF || b0.window > 0x7FFFFFFF - kStreamWinRows) {
+      free(host);
+      return fail(DKV_ERR_INVALID_ARG, "too many stream items (%lld)", (long long)n_sched);
+    }
+    struct Item {
+      uint32_t w[4];
+      int64_t cost;
+      int32_t unit;  // layer * units + unit
+    };
+    const int64_t kPageCost = 1024;  // a page's fixed cost, in bytes
+    std::vector<Item> items;
+    items.reserve((size_t)n_sched);
+    for (int l = 0; l < n_layers; ++l) {
+      const int r = pools[l].rank, R = pools[l].n_resid, W = batches[l].window;
+      const int nqv = (r + 1 + 15) / 16;
+      for (int u = 0; u < units; ++u) {
+        const uint32_t bh = (uint32_t)(u / p0.n_kv_heads) | ((uint32_t)(u % p0.n_kv_heads) << 16);
+        const int32_t ug = l * units + u;
+        for (int r0 = 0; r0 < W; r0 += kStreamWinRows) {
+          const int rows = W - r0 < kStreamWinRows ? W - r0 : kStreamWinRows;
+          items.push_back({{(uint32_t)l | (kItemWin << 16), (uint32_t)r0, bh, (uint32_t)rows << 16},
+                           (int64_t)rows * 512 + 2 * ((rows + 15) / 16) * kPageCost, ug});
+        }
+        for (int k = 0; k < top_k; ++k) {
+          items.push_back({{(uint32_t)l | (kItemLowRank << 16), (uint32_t)k, bh, 0u},
+                           (int64_t)2 * (r + 1) * 256 + 510 * r + R + (2 * nqv + 8) * kPageCost, ug});
+          for (int r0 = 0; r0 < R; r0 += kStreamResRows) {
+            const int rows = R - r0 < kStreamResRows ? R - r0 : kStreamResRows;
+            items.push_back({{(uint32_t)l | (kItemResid << 16), (uint32_t)k | ((uint32_t)r0 << 16), bh,
+                              (uint32_t)rows << 16},
+                             (int64_t)rows * 512 + 2 * ((rows + 15) / 16) * kPageCost, ug});
+          }
+        }
+      }
+    }
+    n_waves = (int)(n_sched < kStreamMaxWaves ? n_sched : kStreamMaxWaves);
+    int64_t total_cost = 0;
+    for (const Item& it : items) total_cost += it.cost;
+    // item i goes to the wave whose share holds the middle of its cost
+    std::vector<int32_t> wave_of(items.size());
+    int64_t cum = 0;
+    for (size_t i = 0; i < items.size(); ++i) {
+      const double mid = (double)cum + 0.5 * (double)items[i].cost;
+      int w = (int)(mid * n_waves / (double)(total_cost > 0 ? total_cost : 1));
+      wave_of[i] = w < n_waves ? w : n_waves - 1;
+      cum += items[i].cost;
+    }
+    // runs: the flags, each run's partial index within its unit, the units' counts
+    std::vector<int32_t> unit_parts((size_t)n_layers * units, 0);
+    for (size_t i = 0; i < items.size(); ++i) {
+      const bool first = i == 0 || wave_of[i - 1] != wave_of[i] || items[i - 1].unit != items[i].unit;
+      const bool last = i + 1 == items.size() || wave_of[i + 1] != wave_of[i] || items[i + 1].unit != items[i].unit;
+      if (first) ++unit_parts[(size_t)items[i].unit];
+      const int part = unit_parts[(size_t)items[i].unit] - 1;
+      items[i].w[0] |= (first ? 1u << 24 : 0u) | (last ? 2u << 24 : 0u);
+      items[i].w[3] |= (uint32_t)part;
+    }
+    sched.reserve(stream_sched_words(pools, batches, n_layers, top_k));
+    size_t i = 0;
+    for (int w = 0; w < n_waves; ++w) {
+      sched.push_back((int32_t)i);
+      while (i < items.size() && wave_of[i] == w) ++i;
+    }
+    sched.push_back((int32_t)i);
+    for (const Item& it : items)
+      for (int k = 0; k < 4; ++k) sched.push_back((int32_t)it.w[k]);
+    sched.insert(sched.end(), unit_parts.begin(), unit_parts.end());
+  }
+  const size_t sched_off = align256(off);
   if (s == DKV_OK) {
     if (hipMemcpy(table, host, (size_t)n_layers * sizeof(LayerArgs), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemset(workspace, 0, need) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        hipMemset(workspace, 0, need) != hipSuccess ||
+        (!sched.empty() && hipMemcpy(ws + sched_off, sched.data(), sched.size() * 4, hipMemcpyHostToDevice) !=
+                               hipSuccess) ||
+        hipDeviceSynchronize() != hipSuccess)
       s = fail(DKV_ERR_HIP, "table upload or workspace clear failed");
   }
   if (s == DKV_OK) {
@@ -2440,11 +2582,11 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     plan->n_layers = n_layers;
     plan->n_units = units;
     plan->routes = top_k > 0 ? 1 : 0;
-    plan->parts = host[0].D.att.n_block_parts;
+    plan->parts = streams ? 0 : host[0].D.att.n_block_parts;
     plan->win_parts = host[0].D.att.n_win_parts;
-    plan->group = 1;  // merges per unit
-    const int64_t items =
-        (int64_t)n_layers * units * (plan->routes + plan->parts + plan->win_parts + plan->group);
+    plan->group = streams ? 0 : 1;  // merges per unit (the streams: a launch of their own)
+    // the launch's work items (with the streams: the first launch's, the routings)
+    const int64_t items = (int64_t)n_layers * units * (plan->routes + plan->parts + plan->win_parts + plan->group);
     if (items > 0x7FFFFFFF) s = fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
     plan->n_items = (int32_t)items;
     plan->lds_bytes = (int32_t)shm;
@@ -2455,8 +2597,11 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     for (int l = 0; l < n_layers; ++l) quant |= pools[l].resid_format != DKV_RESID_FP16 ? 1 : 0;
     plan->quantised = quant;
     plan->unrotated = p0.rope_freq ? 1 : 0;
-    plan->stream = streaming ? 1 : 0;
-    plan->stream_blocks = sblocks;
+    plan->stream = streams ? 1 : 0;
+    plan->stream_top_k = streams ? top_k : 0;
+    plan->stream_items = (int32_t)n_sched;
+    plan->stream_waves = n_waves;
+    plan->stream_sched = (int32_t)(sched_off / 4);
     plan->table = table;
     plan->workspace = workspace;
   }
@@ -2477,11 +2622,11 @@ dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
   L.win_parts = plan->win_parts;
   L.group = plan->group;
   if (plan->stream) {
-    LayerArgs unused;
-    memset(&unused, 0, sizeof(unused));
-    const hipError_t e =
-        dkv_stream_launch(plan->table, &unused, &L, plan->n_items, (size_t)plan->lds_bytes, (hipStream_t)stream);
-    if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_stream launch failed: %s", hipGetErrorString(e));
+    const hipError_t e = dkv_stream_step(plan->table, &L, plan->n_items, (size_t)plan->lds_bytes,
+                                         (const int32_t*)plan->workspace + plan->stream_sched, plan->stream_waves,
+                                         plan->stream_items, plan->stream_top_k, plan->n_layers,
+                                         plan->n_units, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DKV_ERR_HIP, "streaming launches failed: %s", hipGetErrorString(e));
     return DKV_OK;
   }
   switch (plan->max_tiles) {  // the largest low-rank tile count of the layers

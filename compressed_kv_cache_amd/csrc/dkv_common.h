@@ -270,6 +270,16 @@ __host__ __device__ constexpr size_t route_lds_words(int max_blocks, int nw) {
   return (size_t)2 * (size_t)(((max_blocks > 0 ? max_blocks : 1) + 3) & ~3) + (size_t)nw * 64 * kRedRow;
 }
 
+// The layer-batched streams' schedule (written on the host, read by the
+// streams): work items of four words each,
+//   w0: layer | kind << 16 | flags << 24 (flag 1: the item opens a run, 2: it
+//       closes one; a run is a wave's consecutive items of one unit)
+//   w1: window items: the first window row; block items: the routed rank
+//       | the first residual row << 16 (residual items)
+//   w2: batch row | kv head << 16
+//   w3: the run's partial index | rows << 16 (window and residual items)
+enum { kItemWin = 0, kItemLowRank = 1, kItemResid = 2 };
+
 // Routed-slot words of the fused kernels hold the launch's tag in the top byte
 // and pool slot + kSlotCode in the low 24 bits (1: no block), so that a word
 // whose low bits are 0 (zero-filled memory) or whose tag is another launch's

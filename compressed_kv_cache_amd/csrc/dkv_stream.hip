@@ -63,23 +63,74 @@ __device__ __forceinline__ void dma4(const void* src, unsigned char* lds_dst) {
 
 // wait until at most n of this wave's vector-memory operations are outstanding
 __device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+  // n is the same on every lane: branch on a scalar.  The count's low four
+  // bits sit in bits 0..3 of the immediate, its high two in bits 14..15;
+  // expcnt and lgkmcnt are left at their maximum (no wait).
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 0: __builtin_amdgcn_s_waitcnt(0xf70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0xf71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0xf72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0xf73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0xf74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0xf75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0xf76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0xf77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0xf78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0xf79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0xf7a); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0xf7b); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0xf7c); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0xf7d); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0xf7e); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0xf7f); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4f70); break;
+    case 17: __builtin_amdgcn_s_waitcnt(0x4f71); break;
+    case 18: __builtin_amdgcn_s_waitcnt(0x4f72); break;
+    case 19: __builtin_amdgcn_s_waitcnt(0x4f73); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4f74); break;
+    case 21: __builtin_amdgcn_s_waitcnt(0x4f75); break;
+    case 22: __builtin_amdgcn_s_waitcnt(0x4f76); break;
+    case 23: __builtin_amdgcn_s_waitcnt(0x4f77); break;
+    case 24: __builtin_amdgcn_s_waitcnt(0x4f78); break;
+    case 25: __builtin_amdgcn_s_waitcnt(0x4f79); break;
+    case 26: __builtin_amdgcn_s_waitcnt(0x4f7a); break;
+    case 27: __builtin_amdgcn_s_waitcnt(0x4f7b); break;
+    case 28: __builtin_amdgcn_s_waitcnt(0x4f7c); break;
+    case 29: __builtin_amdgcn_s_waitcnt(0x4f7d); break;
+    case 30: __builtin_amdgcn_s_waitcnt(0x4f7e); break;
+    case 31: __builtin_amdgcn_s_waitcnt(0x4f7f); break;
+    case 32: __builtin_amdgcn_s_waitcnt(0x8f70); break;
+    case 33: __builtin_amdgcn_s_waitcnt(0x8f71); break;
+    case 34: __builtin_amdgcn_s_waitcnt(0x8f72); break;
+    case 35: __builtin_amdgcn_s_waitcnt(0x8f73); break;
+    case 36: __builtin_amdgcn_s_waitcnt(0x8f74); break;
+    case 37: __builtin_amdgcn_s_waitcnt(0x8f75); break;
+    case 38: __builtin_amdgcn_s_waitcnt(0x8f76); break;
+    case 39: __builtin_amdgcn_s_waitcnt(0x8f77); break;
+    case 40: __builtin_amdgcn_s_waitcnt(0x8f78); break;
+    case 41: __builtin_amdgcn_s_waitcnt(0x8f79); break;
+    case 42: __builtin_amdgcn_s_waitcnt(0x8f7a); break;
+    case 43: __builtin_amdgcn_s_waitcnt(0x8f7b); break;
+    case 44: __builtin_amdgcn_s_waitcnt(0x8f7c); break;
+    case 45: __builtin_amdgcn_s_waitcnt(0x8f7d); break;
+    case 46: __builtin_amdgcn_s_waitcnt(0x8f7e); break;
+    case 47: __builtin_amdgcn_s_waitcnt(0x8f7f); break;
+    case 48: __builtin_amdgcn_s_waitcnt(0xcf70); break;
+    case 49: __builtin_amdgcn_s_waitcnt(0xcf71); break;
+    case 50: __builtin_amdgcn_s_waitcnt(0xcf72); break;
+    case 51: __builtin_amdgcn_s_waitcnt(0xcf73); break;
+    case 52: __builtin_amdgcn_s_waitcnt(0xcf74); break;
+    case 53: __builtin_amdgcn_s_waitcnt(0xcf75); break;
+    case 54: __builtin_amdgcn_s_waitcnt(0xcf76); break;
+    case 55: __builtin_amdgcn_s_waitcnt(0xcf77); break;
+    case 56: __builtin_amdgcn_s_waitcnt(0xcf78); break;
+    case 57: __builtin_amdgcn_s_waitcnt(0xcf79); break;
+    case 58: __builtin_amdgcn_s_waitcnt(0xcf7a); break;
+    case 59: __builtin_amdgcn_s_waitcnt(0xcf7b); break;
+    case 60: __builtin_amdgcn_s_waitcnt(0xcf7c); break;
+    case 61: __builtin_amdgcn_s_waitcnt(0xcf7d); break;
+    case 62: __builtin_amdgcn_s_waitcnt(0xcf7e); break;
+    default: __builtin_amdgcn_s_waitcnt(0xcf7f); break;
   }
 }
 
@@ -108,6 +159,96 @@ typedef __fp16 v4fp16 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 __device__ __forceinline__ v4h ld_tr(const unsigned char* p) {
   const v4fp16 t = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) v4fp16*)p);
   return __builtin_bit_cast(v4h, t);
+}
+
+// LDS reads of ring pages, written as inline asm that waits for its own
+// reads before it ends (outputs early-clobber: a read that lands must not
+// overwrite the address of the next): the compiler would otherwise wait for every load in
+// flight to LDS (it cannot tell which slot they fill) before each LDS read,
+// and the ring would drain at every page.  Addresses are LDS byte offsets.
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// four 16-byte reads at a, a + 64, a + 128, a + 192
+__device__ __forceinline__ void lds_b128x4(uint32_t a, v8h (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a)
+      : "memory");
+}
+// eight transposed 8-byte reads at a + 32 k (k = 0..7)
+__device__ __forceinline__ void lds_tr8(uint32_t a, v4h (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a)
+      : "memory");
+}
+// transposed 8-byte reads at a + 32 k and b + 32 k (k = 0..3)
+__device__ __forceinline__ void lds_tr44(uint32_t a, uint32_t b, v4h (&o)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %4, %9\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:32\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:64\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a), "v"(b)
+      : "memory");
+}
+// plain 8-byte reads at a + 32 k and b + 32 k (k = 0..3)
+__device__ __forceinline__ void lds_b64x44(uint32_t a, uint32_t b, v4h (&o)[8]) {
+  asm volatile(
+      "ds_read_b64 %0, %8\n\t"
+      "ds_read_b64 %1, %8 offset:32\n\t"
+      "ds_read_b64 %2, %8 offset:64\n\t"
+      "ds_read_b64 %3, %8 offset:96\n\t"
+      "ds_read_b64 %4, %9\n\t"
+      "ds_read_b64 %5, %9 offset:32\n\t"
+      "ds_read_b64 %6, %9 offset:64\n\t"
+      "ds_read_b64 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a), "v"(b)
+      : "memory");
+}
+// two bytes at a and a + 64
+__device__ __forceinline__ void lds_u8x2(uint32_t a, uint32_t& x, uint32_t& y) {
+  asm volatile(
+      "ds_read_u8 %0, %2\n\t"
+      "ds_read_u8 %1, %2 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y)
+      : "v"(a)
+      : "memory");
+}
+
+// OR over the 64 lanes, returned to every lane
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_u32<0xB1>(0u, v);        // quad_perm 1,0,3,2
+  v |= dpp_u32<0x4E>(0u, v);        // quad_perm 2,3,0,1
+  v |= dpp_u32<0x141>(0u, v);       // row_half_mirror
+  v |= dpp_u32<0x140>(0u, v);       // row_mirror
+  v |= dpp_u32<0x142, 0xa>(0u, v);  // row_bcast:15
+  v |= dpp_u32<0x143, 0xc>(0u, v);  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ v4f mfma32(v8h a, v8h b, v4f c) {
@@ -172,8 +313,29 @@ __device__ __forceinline__ void page_kind(const WaveGeom& g, int k, int& kind, i
 // U) is written as zeros by the range check.  A 128-wide row page maps chunk p
 // to row p / 17, chunk p % 17 (chunk 16 is the row's pad); a U page maps p
 // linearly.  Row r of [V_K ; a_k] and [V_V ; a_v] comes from a load of its own.
+// Per lane: the source offset of chunk 64 q + lane (q = 0..4) of a 128-wide
+// row page (row p / 17, chunk p % 17 of the row; chunk 16, the row's pad, is
+// kOutside), the same for every row page.
+struct RowOffs {
+  uint32_t off[5];
+};
+
+__device__ __forceinline__ RowOffs row_offs() {
+  const int lane = threadIdx.x & 63;
+  RowOffs o;
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int p = 64 * q + lane;
+    const int row = (p * 3856) >> 16;  // p / 17 for p < 17 * 16 * 2
+    const int c = p - 17 * row;
+    o.off[q] = c < 16 ? (uint32_t)(row * 256 + 16 * c) : kOutside;
+  }
+  return o;
+}
+
 __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned char* dst, const uint64_t* bb,
-                                          const char* wk_rows, const char* wv_rows, unsigned char* posdst) {
+                                          const char* wk_rows, const char* wv_rows, unsigned char* posdst,
+                                          const RowOffs& ro) {
   const int lane = threadIdx.x & 63;
   int kind, i;
   page_kind(g, k, kind, i);
@@ -208,12 +370,12 @@ __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned cha
       base = (const char*)bb[kind == kPageK ? kBaseRK : kBaseRV] + 16 * i * 256;
   }
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(base, (uint32_t)nvalid * 256u);
-  for (int q = 0; q < 17 * 16; q += 64) {
-    const int p = q + lane;
-    const int row = (p * 3856) >> 16;  // p / 17
-    const int c = p - 17 * row;
-    const uint32_t off = c < 16 ? (uint32_t)(row * 256 + 16 * c) : kOutside;
-    if (p < 17 * 16 && row != special) dma16b(rs, off, dst + 16 * q);
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    // chunks past the page's 17 * 16 (lanes 16.. of the last load) are not loaded;
+    // a pad chunk's offset (kOutside) has no row that equals `special`
+    const uint32_t off = ro.off[q];
+    if ((q < 4 || lane < 16) && (int)(off >> 8) != special) dma16b(rs, off, dst + 1024 * q);
     ++ops;
   }
   if (special >= 0) {
@@ -313,6 +475,177 @@ template <class T>
 __device__ __forceinline__ T pick4(const T (&a)[4], int i) {
   return i == 0 ? a[0] : (i == 1 ? a[1] : (i == 2 ? a[2] : a[3]));
 }
+
+// One page of a wave's stream: the work of page kind `kind`, number i, held in
+// LDS at pg (the wave's own ring slot).  st and the per-block values (q~ as hi +
+// lo, q . a_k, the block's low-rank weight sum, the current K tile's weights)
+// carry over from page to page.
+struct BlockRegs {
+  v4h qth[4], qtl[4];  // scaled V_K q of the block (hi + lo fp16): rows 16 k + 4 q4 + e, head l16
+  float qa;            // scale * q . a_k
+  float llr_tot;       // the block's low-rank weight sum per head (at its first V_V tile)
+  v4h pv;              // weights of the current K tile (fp16), for its V tile
+  uint32_t mw[8];      // the block's residual-position mask (bit p of word p / 32: position p)
+};
+
+// The page kinds' work.  P0: the page's LDS byte address (the wave's own ring
+// slot); i: the page's number within its kind.  st and br carry over from page
+// to page.  With i a compile-time constant every register array index folds.
+
+// V_K q rows 16 i .. 16 i + 15 (q . a_k at row r); page 0 also turns the
+// block's residual positions (bytes at LDS address posb) into the mask words.
+__device__ __forceinline__ void page_vk(const WaveGeom& g, int i, uint32_t P0, const v8h (&qf)[4], BlockRegs& br,
+                                        float scale, uint32_t posb) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int r = g.r;
+  v8h a[4];
+  lds_b128x4(P0 + l16 * kSRowB + 16 * q4, a);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) acc = mfma32(a[s2], qf[s2], acc);
+  v4f x;
+  float qr = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * i + 4 * q4 + e;
+    x[e] = j < r ? acc[e] * scale : 0.f;
+    qr += j == r ? acc[e] * scale : 0.f;
+  }
+  v4h hi, lo;
+  split4(x, hi, lo);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    br.qth[k] = k == i ? hi : br.qth[k];
+    br.qtl[k] = k == i ? lo : br.qtl[k];
+  }
+  if (16 * i <= r && r < 16 * i + 16) br.qa = hq_sum(qr);
+  if (i == 0) {
+    uint32_t p1 = 0u, p2 = 0u;
+    lds_u8x2(posb + lane, p1, p2);
+    p1 = lane < g.R ? p1 : 0u;
+    p2 = lane + 64 < g.R ? p2 : 0u;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t v = ((p1 >> 5) == (uint32_t)w && p1 >= 1u ? 1u << (p1 & 31) : 0u) |
+                         ((p2 >> 5) == (uint32_t)w && p2 >= 1u ? 1u << (p2 & 31) : 0u);
+      br.mw[w] = wave_or(v);
+    }
+  }
+}
+
+// U page i: positions 32 i + 16 tt + row (row 0 of page 0 is the anchor):
+// low-rank scores, then W^T += Ux^T p over the page's 32 positions.
+__device__ __forceinline__ void page_u(const WaveGeom& g, int i, uint32_t P0, SState& st, BlockRegs& br) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4, s4 = l16 & 3;
+  const int r = g.r;
+  const uint32_t mw = i == 0 ? br.mw[0] : i == 1 ? br.mw[1] : i == 2 ? br.mw[2] : i == 3 ? br.mw[3]
+                    : i == 4 ? br.mw[4] : i == 5 ? br.mw[5] : i == 6 ? br.mw[6] : br.mw[7];
+  v4h ua[8];  // [tt * 4 + k]: U rows 16 tt + l16, columns 16 k + 4 q4 .. + 3
+  const uint32_t a0 = P0 + 2 * (l16 * r + 4 * q4);
+  lds_b64x44(a0, a0 + 32 * r, ua);
+  float z[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < g.nq) {
+        acc = mfma16(ua[4 * tt + k], br.qth[k], acc);
+        acc = mfma16(ua[4 * tt + k], br.qtl[k], acc);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool masked = ((mw >> (16 * tt + 4 * q4 + e)) & 1u) != 0u;
+      z[4 * tt + e] = masked ? -INFINITY : acc[e] + br.qa;
+    }
+  }
+  softmax_step<8>(st, z, true);
+  v8h pf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pf[e] = (f16)z[e];
+  v4h ut[8];  // [k], [4 + k]: transposed U of rows 4 q4 .., 16 + 4 q4 .., columns 16 k + l16
+  const uint32_t b0 = P0 + 2 * ((4 * q4 + (l16 >> 2)) * r + 4 * s4);
+  lds_tr44(b0, b0 + 32 * r, ut);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k < g.nq) {
+      const v8h a = __builtin_shufflevector(ut[k], ut[4 + k], 0, 1, 2, 3, 4, 5, 6, 7);
+      st.Wt[k] = mfma32(a, pf, st.Wt[k]);
+    }
+  }
+}
+
+// K page i: scores of residual (or window) rows 16 i .. 16 i + 15.
+__device__ __forceinline__ void page_k(const WaveGeom& g, int i, uint32_t P0, SState& st, const v8h (&qf)[4],
+                                       BlockRegs& br, float scale) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4;
+  const int nr = g.R - 16 * i;
+  v8h a[4];
+  lds_b128x4(P0 + l16 * kSRowB + 16 * q4, a);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) acc = mfma32(a[s2], qf[s2], acc);
+  float z[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = (4 * q4 + e < nr) ? acc[e] * scale : -INFINITY;
+  softmax_step<4>(st, z, false);
+  br.pv = to_h4v(z[0], z[1], z[2], z[3]);
+}
+
+// V page: O^T += V^T p of the K page before it.
+__device__ __forceinline__ void page_v(uint32_t P0, SState& st, const BlockRegs& br) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4, s4 = l16 & 3;
+  v4h a[8];
+  lds_tr8(P0 + (4 * q4 + (l16 >> 2)) * kSRowB + 16 * (s4 >> 1) + 8 * (s4 & 1), a);
+#pragma unroll
+  for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = mfma16(a[nn], br.pv, st.Ot[nn]);
+}
+
+// V_V page i: O^T += [V_V ; a_v]^T rows 16 i .. 16 i + 15 times W^T rows (row
+// r of W^T: the block's low-rank weight sum, for a_v).
+__device__ __forceinline__ void page_vv(const WaveGeom& g, int i, uint32_t P0, SState& st, BlockRegs& br) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, q4 = lane >> 4, s4 = l16 & 3;
+  const int r = g.r;
+  if (i == 0) {
+    br.llr_tot = hq_sum(st.llr);
+    st.llr = 0.f;
+  }
+  v4f x = pick4(st.Wt, i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 16 * i + 4 * q4 + e;
+    x[e] = j < r ? x[e] : (j == r ? br.llr_tot : 0.f);
+  }
+  v4h wh, wlo;
+  split4(x, wh, wlo);
+  v4h a[8];
+  lds_tr8(P0 + (4 * q4 + (l16 >> 2)) * kSRowB + 16 * (s4 >> 1) + 8 * (s4 & 1), a);
+#pragma unroll
+  for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = mfma16(a[nn], wlo, mfma16(a[nn], wh, st.Ot[nn]));
+  if (i == g.nqv - 1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// One page of a wave's stream, of any kind (kind and i at run time).
+__device__ __forceinline__ void compute_page(const WaveGeom& g, int kind, int i, const unsigned char* pg, SState& st,
+                                             const v8h (&qf)[4], BlockRegs& br, float scale,
+                                             const unsigned char* posb) {
+  const uint32_t P0 = lds_off(pg);
+  if (kind == kPageVK)
+    page_vk(g, i, P0, qf, br, scale, lds_off(posb));
+  else if (kind == kPageU)
+    page_u(g, i, P0, st, br);
+  else if (kind == kPageK)
+    page_k(g, i, P0, st, qf, br, scale);
+  else if (kind == kPageV)
+    page_v(P0, st, br);
+  else
+    page_vv(g, i, P0, st, br);
+}
+
 
 // One attention part of unit u: part p < n_block_parts holds routed ranks
 // [p * bpi, min((p + 1) * bpi, top_k)), at most four: wave w streams block w.
@@ -425,7 +758,6 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
   // ---- this wave's stream: pages through its own ring, kWSlots - 1 ahead
   unsigned char* ring = smem + wave * kWRing;
   unsigned char* posb = smem + kWPosOff + 128 * wave;
-  uint32_t* mask = reinterpret_cast<uint32_t*>(smem + kWMaskOff + 32 * wave);
   const uint64_t* bb = bases + (g.window ? 0 : wave) * kBases;
   SState st;
 #pragma unroll
@@ -438,9 +770,10 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
   const float scale = A.scale;
   // the first pages, then the query rows (loaded before them) once every wave has its share
   int n_issued = 0;
+  const RowOffs ro = row_offs();
   uint32_t in_flight = 0u;  // this wave's load counts of the pages issued and not yet waited for (bytes, oldest low)
   for (; n_issued < kWSlots - 1 && n_issued < total; ++n_issued)
-    in_flight |= (uint32_t)issue_page(g, n_issued, ring + kWPage * n_issued, bb, wk_rows, wv_rows, posb)
+    in_flight |= (uint32_t)issue_page(g, n_issued, ring + kWPage * n_issued, bb, wk_rows, wv_rows, posb, ro)
                  << (8 * n_issued);
   wait_vm((int)((in_flight & 0xFFu) + ((in_flight >> 8) & 0xFFu) + (in_flight >> 16)));
   lds_barrier();
@@ -450,142 +783,23 @@ __device__ __forceinline__ void stream_part(const PoolArgs& P, const BatchArgs& 
 
   if (total > 0) {
     const int r = g.r;
-    v4h qth[4], qtl[4];  // scaled V_K q of the block (hi + lo fp16): rows 16 k + 4 q4 + e, head l16
-    float qa = 0.f;      // scale * q . a_k
-    float llr_tot = 0.f; // the block's low-rank weight sum per head (at the first V_V tile)
-    v4h pv;              // weights of the current K tile (fp16), for its V tile
+    BlockRegs br;
+    br.qa = 0.f;
+    br.llr_tot = 0.f;
     for (int n = 0; n < total; ++n) {
       const uint32_t after = in_flight >> 8;
       wait_vm((int)((after & 0xFFu) + ((after >> 8) & 0xFFu) + (after >> 16)));
       in_flight = after;
       if (n_issued < total) {
         in_flight |= (uint32_t)issue_page(g, n_issued, ring + kWPage * (n_issued % kWSlots), bb, wk_rows, wv_rows,
-                                          posb)
+                                          posb, ro)
                      << (8 * (n_issued - n - 1));
         ++n_issued;
       }
       const unsigned char* pg = ring + kWPage * (n % kWSlots);
       int kind, i;
       page_kind(g, n, kind, i);
-      if (kind == kPageVK) {
-        // V_K q rows 16 i .. 16 i + 15 (q . a_k at row r)
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(l16, 4 * s + q4)), qf[s], acc);
-        v4f x;
-        float qr = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * i + 4 * q4 + e;
-          x[e] = j < r ? acc[e] * scale : 0.f;
-          qr += j == r ? acc[e] * scale : 0.f;
-        }
-        v4h hi, lo;
-        split4(x, hi, lo);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k == i) {
-            qth[k] = hi;
-            qtl[k] = lo;
-          }
-        if (16 * i <= r && r < 16 * i + 16) qa = hq_sum(qr);
-        if (i == 0) {
-          // the block's residual-position mask (this wave's own LDS words)
-          if (lane < 8) mask[lane] = 0u;
-          wave_sync_lds();
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int t = lane + 64 * k;
-            if (t < g.R) {
-              const int ps = posb[t];
-              if (ps >= 1 && ps <= kLowRankRows) atomicOr(&mask[ps >> 5], 1u << (ps & 31));
-            }
-          }
-          wave_sync_lds();
-        }
-      } else if (kind == kPageU) {
-        // positions 32 i + 16 tt + row of the page; row 0 of page 0 is the anchor
-        const uint32_t mw = mask[i];
-        float z[8];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int lrow = 16 * tt + l16;
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (k < g.nq) {
-              const v4h a = *reinterpret_cast<const v4h*>(pg + 2 * (lrow * r + 16 * k + 4 * q4));
-              acc = mfma16(a, qth[k], acc);
-              acc = mfma16(a, qtl[k], acc);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool masked = ((mw >> (16 * tt + 4 * q4 + e)) & 1u) != 0u;
-            z[4 * tt + e] = masked ? -INFINITY : acc[e] + qa;
-          }
-        }
-        softmax_step<8>(st, z, true);
-        v8h pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (f16)z[e];
-        // W^T += Ux^T p over the page's 32 positions (positions 4 q4 + t of both tiles)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (k < g.nq) {
-            const int c0 = 16 * k + 4 * (l16 & 3);
-            const int ra = 4 * q4 + (l16 >> 2);
-            const v4h a0 = ld_tr(pg + 2 * (ra * r + c0));
-            const v4h a1 = ld_tr(pg + 2 * ((ra + 16) * r + c0));
-            const v8h a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-            st.Wt[k] = mfma32(a, pf, st.Wt[k]);
-          }
-        }
-      } else if (kind == kPageK) {
-        const int nr = g.R - 16 * i;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma32(*reinterpret_cast<const v8h*>(pg + swz(l16, 4 * s + q4)), qf[s], acc);
-        float z[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = (4 * q4 + e < nr) ? acc[e] * scale : -INFINITY;
-        softmax_step<4>(st, z, false);
-        pv = to_h4v(z[0], z[1], z[2], z[3]);
-      } else if (kind == kPageV) {
-        const int s4 = l16 & 3;
-        const int row = 4 * q4 + (l16 >> 2);
-#pragma unroll
-        for (int nn = 0; nn < 8; ++nn) {
-          const v4h a = ld_tr(pg + swz(row, 2 * nn + (s4 >> 1)) + 8 * (s4 & 1));
-          st.Ot[nn] = mfma16(a, pv, st.Ot[nn]);
-        }
-      } else {
-        // V_V tile i: O^T += [V_V ; a_v]^T rows 16 i .. 16 i + 15 times W^T rows
-        // (row r of W^T: the block's low-rank weight sum, for a_v)
-        if (i == 0) {
-          llr_tot = hq_sum(st.llr);
-          st.llr = 0.f;
-        }
-        v4f x = pick4(st.Wt, i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * i + 4 * q4 + e;
-          x[e] = j < r ? x[e] : (j == r ? llr_tot : 0.f);
-        }
-        v4h wh, wlo;
-        split4(x, wh, wlo);
-        const int s4 = l16 & 3;
-        const int row = 4 * q4 + (l16 >> 2);
-#pragma unroll
-        for (int nn = 0; nn < 8; ++nn) {
-          const v4h a = ld_tr(pg + swz(row, 2 * nn + (s4 >> 1)) + 8 * (s4 & 1));
-          st.Ot[nn] = mfma16(a, wlo, mfma16(a, wh, st.Ot[nn]));
-        }
-        if (i == g.nqv - 1) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
-        }
-      }
+      compute_page(g, kind, i, pg, st, qf, br, scale, posb);
     }
   }
 
@@ -715,11 +929,15 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_stream(const LayerArgs* __re
                       : (CLayer*)((CByte*)__builtin_amdgcn_kernarg_segment_ptr() + kOneArgOffset);
   const LayerArgs& la = *(const LayerArgs*)cla;
   if (t >= 0) stream_item(la.P, la.Bt, la.D, t, smem, rsh);
-  // the last merge of the launch leaves every layer's control words zero
-  if (t >= la.D.n_part_end) {
+  // The last merge of the launch leaves every layer's control words zero; a
+  // launch without merges (routings and window parts only, ahead of the block
+  // streams) counts every item instead.
+  const bool counted = L.group > 0 ? t >= la.D.n_part_end : t >= 0;
+  const uint32_t n_counted = (uint32_t)(L.n_layers * L.n_units *
+                                        (L.group > 0 ? L.group : L.routes + L.block_parts + L.win_parts));
+  if (counted) {
     __syncthreads();
-    if (tid == 0)
-      sh_flag = (atomicAdd(&L.ctrl[1], 1u) == (uint32_t)(L.n_layers * L.n_units * L.group - 1)) ? 1u : 0u;
+    if (tid == 0) sh_flag = (atomicAdd(&L.ctrl[1], 1u) == n_counted - 1u) ? 1u : 0u;
     lds_barrier();
     if (sh_flag) {
       for (int l = 0; l < L.n_layers; ++l) {
@@ -729,10 +947,377 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_stream(const LayerArgs* __re
       if (tid < kQueues) L.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
       if (tid == 0) {
         L.ctrl[1] = 0u;
-        L.ctrl[3] = L.ctrl[3] + 1u;  // the next launch's routed-slot tag
+        // the next launch's routed-slot tag (with block streams, the merge launch
+        // that ends the step advances it)
+        if (L.group > 0) L.ctrl[3] = L.ctrl[3] + 1u;
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Streams: after the routing of a step has run, each one-wave workgroup
+// streams a contiguous segment of the step's work (every unit's window rows
+// and routed blocks, cut on the host into segments of equal bytes) through its
+// LDS ring.  No item waits on another: the routing finished in an earlier
+// launch.
+// ---------------------------------------------------------------------------
+
+struct BlocksArgs {
+  const LayerArgs* table;
+  const int32_t* sched;  // the step's schedule (see k_blocks)
+  const uint32_t* ctrl;  // the step's control header (word 3: the routed-slot tag of this step)
+  int n_waves;
+  int top_k;
+};
+
+constexpr int kBPosOff = kWRing;                 // residual positions [128] bytes
+constexpr int kBBaseOff = kBPosOff + 128;        // the issuing item's source addresses [kBases] u64
+constexpr int kBLds = kBBaseOff + kBases * 8;
+
+typedef const __attribute__((address_space(4))) int32_t CInt;
+typedef const __attribute__((address_space(4))) uint32_t CUint;
+typedef const __attribute__((address_space(4))) LayerArgs CLayerArgs;
+
+// What one side of a stream needs to know about a work item.
+struct SItem {
+  WaveGeom g;
+  int npages;        // pages of the item's stream: the unit's query rows first if it opens a run
+  int kind, first, last;
+  int G, row0, part; // the unit's query rows row0 .. row0 + G - 1; the run's partial index
+  int layer, h;
+  int64_t slot;      // block items: the routed pool slot, or -1 (nothing to stream)
+  const char* rows_k;  // window and residual items: their first key and value rows
+  const char* rows_v;
+};
+
+__device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uint32_t tag) {
+  const uint32_t w0 = ((CUint*)item)[0], w1 = ((CUint*)item)[1], w2 = ((CUint*)item)[2], w3 = ((CUint*)item)[3];
+  SItem it;
+  it.layer = (int)(w0 & 0xFFFFu);
+  it.kind = (int)((w0 >> 16) & 0xFFu);
+  it.first = (int)((w0 >> 24) & 1u);
+  it.last = (int)((w0 >> 25) & 1u);
+  const int b = (int)(w2 & 0xFFFFu), h = (int)(w2 >> 16);
+  it.part = (int)(w3 & 0xFFFFu);
+  const int nrows = (int)(w3 >> 16);
+  const LayerArgs& la = *(const LayerArgs*)((CLayerArgs*)A.table + it.layer);
+  const PoolArgs& P = la.P;
+  const int Hkv = la.Bt.Hkv, G = la.Bt.G;
+  it.h = h;
+  it.G = G;
+  it.row0 = b * la.Bt.Hq + h * G;
+  it.g.r = P.rank;
+  it.g.nq = round16(P.rank) >> 4;
+  it.g.nqv = round16(P.rank + 1) >> 4;
+  it.slot = -1;
+  it.rows_k = nullptr;
+  it.rows_v = nullptr;
+  int pages;
+  if (it.kind == kItemWin) {
+    // window rows row0 .. row0 + nrows - 1, as far as the row's window reaches
+    const int r0 = (int)w1;
+    int wl = la.Bt.wlen ? ((CInt*)la.Bt.wlen)[b] : la.Bt.W;
+    wl = wl < 0 ? 0 : (wl > la.Bt.W ? la.Bt.W : wl);
+    int rows = wl - r0;
+    rows = rows < 0 ? 0 : (rows > nrows ? nrows : rows);
+    const int64_t base = (((int64_t)b * Hkv + h) * la.Bt.W + r0) * kD;
+    it.rows_k = (const char*)(la.Bt.wk + base);
+    it.rows_v = (const char*)(la.Bt.wv + base);
+    it.g.window = true;
+    it.g.R = rows;
+    it.g.nt = (rows + 15) >> 4;
+    pages = 2 * it.g.nt;
+  } else {
+    const int rank = (int)(w1 & 0xFFFFu);
+    const int unit = b * Hkv + h;
+    const int32_t w = ((CInt*)la.D.slots)[(int64_t)unit * A.top_k + rank];  // a scalar load
+    int64_t slot = slot_ready(w, tag) ? slot_value(w) : -1;
+    if (slot >= P.n_slots) slot = -1;
+    it.slot = slot;
+    if (it.kind == kItemLowRank) {
+      it.g.window = false;
+      it.g.R = P.n_resid;
+      it.g.nt = 0;
+      pages = slot >= 0 ? 2 * it.g.nqv + 8 : 0;
+    } else {
+      const int r0 = (int)(w1 >> 16);
+      it.g.window = true;
+      it.g.R = slot >= 0 ? nrows : 0;
+      it.g.nt = (it.g.R + 15) >> 4;
+      if (slot >= 0) {
+        it.rows_k = (const char*)(P.rk + slot * P.rk_s + h * P.rk_h + (int64_t)r0 * kD);
+        it.rows_v = (const char*)(P.rv + slot * P.rv_s + h * P.rv_h + (int64_t)r0 * kD);
+      }
+      pages = 2 * it.g.nt;
+    }
+  }
+  it.g.ppb = pages;
+  it.npages = it.first + pages;
+  return it;
+}
+
+// the source addresses of the low-rank item an issuing stream enters, into its LDS
+__device__ __forceinline__ void item_bases(const BlocksArgs& A, const SItem& it, uint64_t* bases) {
+  const int lane = threadIdx.x & 63;
+  const LayerArgs& la = *(const LayerArgs*)((CLayerArgs*)A.table + it.layer);
+  const PoolArgs& P = la.P;
+  const int h = it.h;
+  const int64_t slot = it.slot;
+  if (lane < kBases) {
+    const void* a;
+    switch (lane) {
+      case kBaseAK: a = P.ak + slot * P.ak_s + h * P.ak_h; break;
+      case kBaseAV: a = P.av + slot * P.av_s + h * P.av_h; break;
+      case kBaseU: a = P.u + slot * P.u_s + h * P.u_h; break;
+      case kBaseVK: a = P.vk + slot * P.vk_s + h * P.vk_h; break;
+      case kBaseVV: a = P.vv + slot * P.vv_s + h * P.vv_h; break;
+      case kBaseRK: a = P.rk + slot * P.rk_s + h * P.rk_h; break;
+      case kBaseRV: a = P.rv + slot * P.rv_s + h * P.rv_h; break;
+      default: a = P.rp + slot * P.rp_s + h * P.rp_h; break;
+    }
+    bases[lane] = (uint64_t)a;
+  }
+  wave_sync_lds();
+}
+
+// Issue page k of item `it` (page 0 of an item that opens a run: the unit's
+// query rows, 16 rows of 256 bytes, rows past G zero).
+__device__ __forceinline__ int issue_item_page(const BlocksArgs& A, const SItem& it, int k, unsigned char* dst,
+                                               const uint64_t* bases, unsigned char* posb, const RowOffs& ro) {
+  if (it.first && k == 0) {
+    const int lane = threadIdx.x & 63;
+    const LayerArgs& la = *(const LayerArgs*)((CLayerArgs*)A.table + it.layer);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(la.Bt.q + (int64_t)it.row0 * kD, (uint32_t)(it.G * 256));
+#pragma unroll
+    for (int q = 0; q < 256; q += 64) dma16b(rs, (uint32_t)(16 * (q + lane)), dst + 16 * q);
+    return 4;
+  }
+  return issue_page(it.g, k - it.first, dst, bases, it.rows_k, it.rows_v, posb, ro);
+}
+
+// The issuing side of a wave's stream: its pages, in order, into the ring's
+// kWSlots slots; in_flight holds the vector-memory operation counts of the
+// pages in flight, one byte each, byte 0 the oldest (the next to be used).
+struct Issuer {
+  SItem it;        // the item being issued
+  int ii, ik;      // its index in the wave's list, its next page
+  int i1;          // the end of the list
+  int n_issued, total;
+  uint32_t in_flight;
+};
+
+// enter item ii of the list (items without pages are passed over)
+__device__ __forceinline__ void issuer_enter(const BlocksArgs& A, CInt* items, uint32_t tag, Issuer& S,
+                                             uint64_t* bases) {
+  for (; S.ii < S.i1; ++S.ii) {
+    S.it = sched_item(A, items + 4 * S.ii, tag);
+    if (S.it.npages > 0) break;
+  }
+  S.ik = 0;
+  if (S.ii < S.i1 && S.it.kind == kItemLowRank && S.it.slot >= 0) item_bases(A, S.it, bases);
+}
+
+// issue the stream's next page, if any; n_next: the oldest page not yet used
+__device__ __forceinline__ void issue_next(const BlocksArgs& A, CInt* items, uint32_t tag, Issuer& S, int n_next,
+                                           unsigned char* ring, uint64_t* bases, unsigned char* posb,
+                                           const RowOffs& ro) {
+  if (S.n_issued >= S.total) return;
+  const int ops = issue_item_page(A, S.it, S.ik, ring + kWPage * (S.n_issued & (kWSlots - 1)), bases, posb, ro);
+  S.in_flight |= (uint32_t)ops << (8 * (S.n_issued - n_next));
+  ++S.n_issued;
+  if (++S.ik == S.it.npages) {
+    ++S.ii;
+    issuer_enter(A, items, tag, S, bases);
+  }
+}
+
+// wait until the oldest page in flight has landed (in-order completion of the
+// counted operations: the newer ones may still be in flight)
+__device__ __forceinline__ void wait_oldest(uint32_t in_flight) {
+  const uint32_t a = in_flight >> 8;
+  wait_vm((int)((a & 0xFFu) + ((a >> 8) & 0xFFu) + (a >> 16)));
+}
+
+// Vector-memory operations of a run's partial store (eight 16-byte stores of
+// o and one of the lse per lane, in inline asm so that the count is exact).
+constexpr int kPartialStoreOps = 9;
+
+// The streams of a decode step: wave w runs the schedule's items sched[w] ..
+// sched[w + 1] - 1 (window rows of a unit, the low-rank part of a routed block,
+// or residual rows of one) as one stream of pages through its ring: the next
+// item's first pages load while the current item's last ones are used.  The
+// wave's consecutive items of one unit (a run) share one attention state and
+// leave one partial; its store joins the count of operations in flight
+// instead of draining it.  An item's pages come in a fixed order, so the work
+// of each page kind runs in a loop of its own.
+//
+// Schedule layout (int32 words): [n_waves + 1] item offsets per wave, then
+// the items (four words each, see kItemWin), then the partial count of each
+// (layer, unit).
+__global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x, l16 = lane & 15, q4 = lane >> 4;
+  CInt* sched = (CInt*)A.sched;  // scalar loads: the schedule is the same for the whole wave
+  const int i0 = sched[blockIdx.x], i1 = sched[blockIdx.x + 1];
+  if (i0 >= i1) return;
+  CInt* items = sched + A.n_waves + 1;
+  const uint32_t tag = slot_tag(((CUint*)A.ctrl)[3]);
+  unsigned char* ring = smem;
+  unsigned char* posb = smem + kBPosOff;
+  uint64_t* bases = reinterpret_cast<uint64_t*>(smem + kBBaseOff);
+  const uint32_t ring0 = lds_off(ring), posb0 = lds_off(posb);
+  const RowOffs ro = row_offs();
+
+  Issuer S;
+  S.total = 0;
+  for (int j = i0; j < i1; ++j) S.total += sched_item(A, items + 4 * j, tag).npages;
+  S.ii = i0;
+  S.i1 = i1;
+  S.n_issued = 0;
+  S.in_flight = 0u;
+  issuer_enter(A, items, tag, S, bases);
+#pragma unroll 1
+  for (int k = 0; k < kWSlots; ++k) issue_next(A, items, tag, S, 0, ring, bases, posb, ro);
+
+  SState st;
+  BlockRegs br;
+  v8h qf[4];
+  int n = 0;  // the next page to use
+  for (int ci = i0; ci < i1; ++ci) {
+    const SItem cur = sched_item(A, items + 4 * ci, tag);
+    const WaveGeom& g = cur.g;
+    const LayerArgs& la = *(const LayerArgs*)((CLayerArgs*)A.table + cur.layer);
+    const float scale = la.D.att.scale;
+    if (cur.first) {
+      // a new run: the unit's query rows, a fresh state
+      wait_oldest(S.in_flight);
+      lds_b128x4(ring0 + kWPage * (n & (kWSlots - 1)) + l16 * 256 + 16 * q4, qf);
+      S.in_flight >>= 8;
+      issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+      st.m = -INFINITY;
+      st.l = 0.f;
+      st.llr = 0.f;
+    }
+    if (cur.kind == kItemLowRank) {
+      if (cur.slot >= 0) {
+        br.qa = 0.f;
+        br.llr_tot = 0.f;
+        for (int i = 0; i < g.nqv; ++i) {
+          wait_oldest(S.in_flight);
+          page_vk(g, i, ring0 + kWPage * (n & (kWSlots - 1)), qf, br, scale, posb0);
+          S.in_flight >>= 8;
+          issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+        }
+        for (int i = 0; i < 8; ++i) {
+          wait_oldest(S.in_flight);
+          page_u(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, br);
+          S.in_flight >>= 8;
+          issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+        }
+        for (int i = 0; i < g.nqv; ++i) {
+          wait_oldest(S.in_flight);
+          page_vv(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, br);
+          S.in_flight >>= 8;
+          issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+        }
+      }
+    } else {
+      for (int i = 0; i < g.nt; ++i) {
+        wait_oldest(S.in_flight);
+        page_k(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, qf, br, scale);
+        S.in_flight >>= 8;
+        issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+        wait_oldest(S.in_flight);
+        page_v(ring0 + kWPage * (n & (kWSlots - 1)), st, br);
+        S.in_flight >>= 8;
+        issue_next(A, items, tag, S, ++n, ring, bases, posb, ro);
+      }
+    }
+    if (cur.last) {
+      // the run's partial: o normalised, lse (every lane of a head writes the
+      // same lse).  G >= 1, so lane 0 always stores and every store issues.
+      const int np = la.D.att.n_parts;
+      const float lt = hq_sum(st.l);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse = lt > 0.f ? st.m + __logf(lt) : -INFINITY;
+      if (l16 < cur.G) {
+        float* po = la.D.att.part_o + ((int64_t)(cur.row0 + l16) * np + cur.part) * kD + 4 * q4;
+        float* pl = la.D.att.part_lse + (int64_t)(cur.row0 + l16) * np + cur.part;
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) {
+          const v4f v = st.Ot[nn] * inv;
+          // (one wait state before the store data registers may be rewritten)
+          asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" : : "v"(po + 16 * nn), "v"(v) : "memory");
+        }
+        asm volatile("global_store_dword %0, %1, off\n\ts_nop 1" : : "v"(pl), "v"(lse) : "memory");
+      }
+      // the stores count as part of the newest page in flight: waiting for an
+      // older page then also allows for them, waiting for that page waits for them
+      if (S.n_issued > n) S.in_flight += (uint32_t)kPartialStoreOps << (8 * (S.n_issued - 1 - n));
+    }
+  }
+}
+
+// The log-sum-exp merges of a step: one workgroup per (layer, unit), a wave
+// per query row (rows w, w + 4, ...), two columns per lane.  The unit's
+// partials are its runs', in run order; n_parts[layer * n_units + unit] of
+// them.  The sum runs in part order, so the result does not depend on timing.
+__global__ __launch_bounds__(kAttThreads) void k_merges(const LayerArgs* __restrict__ table, int n_units,
+                                                        const int32_t* __restrict__ unit_parts, uint32_t* ctrl) {
+  const int layer = blockIdx.x / n_units, u = blockIdx.x - layer * n_units;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const LayerArgs& la = *(const LayerArgs*)((CLayerArgs*)table + layer);
+  const int b = u / la.Bt.Hkv, h = u - b * la.Bt.Hkv;
+  const int G = la.Bt.G, row0 = b * la.Bt.Hq + h * G;
+  const int stride = la.D.att.n_parts;
+  const int np = ((CInt*)unit_parts)[blockIdx.x];
+  for (int g = wave; g < G; g += kAttWaves) {
+    const int row = row0 + g;
+    const float* lse = la.D.att.part_lse + (int64_t)row * stride;
+    const float* po = la.D.att.part_o + (int64_t)row * stride * kD + 2 * lane;
+    float m = -INFINITY;
+    for (int p = lane; p < np; p += 64) m = fmaxf(m, lse[p]);
+    m = wave_minmax<true>(m);
+    float2 acc = make_float2(0.f, 0.f);
+    float S = 0.f;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const int p = p0 + lane;
+      const float lp = p < np ? lse[p] : -INFINITY;
+      const float wl = lp != -INFINITY ? __expf(lp - m) : 0.f;
+      const int cnt = np - p0 < 64 ? np - p0 : 64;
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float2 o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int kk = k0 + k < cnt ? k0 + k : cnt - 1;
+          o[k] = *reinterpret_cast<const float2*>(po + (int64_t)(p0 + kk) * kD);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w = k0 + k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k0 + k)) : 0.f;
+          S += w;
+          acc.x += w * o[k].x;
+          acc.y += w * o[k].y;
+        }
+      }
+    }
+    const bool any = S > 0.f;
+    const float inv = any ? 1.f / S : 0.f;
+    typedef f16 v2h __attribute__((ext_vector_type(2)));
+    v2h r2;
+    r2[0] = (f16)(acc.x * inv);
+    r2[1] = (f16)(acc.y * inv);
+    *reinterpret_cast<v2h*>(la.D.out + (int64_t)row * kD + 2 * lane) = r2;
+    if (lane == 0) la.D.out_lse[row] = any ? m + __logf(S) : -INFINITY;
+  }
+  // the last workgroup advances the step's routed-slot tag (the launch order
+  // makes every earlier reader done with it)
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) ctrl[3] = ctrl[3] + 1u;
 }
 
 }  // namespace
@@ -759,5 +1344,35 @@ __attribute__((visibility("hidden"))) hipError_t dkv_stream_launch(const void* t
     attr_set = true;
   }
   hipLaunchKernelGGL(k_stream, dim3((unsigned)n_items), dim3(kAttThreads), lds, st, (const LayerArgs*)table, one, L);
+  return hipGetLastError();
+}
+
+// One decode step of several layers as three launches on `st`: the routings
+// (k_stream), the streams (k_blocks), the merges (k_merges).  layers_a: the
+// LayersArgs of the first launch; sched: the step's schedule in device memory
+// (see k_blocks), with n_waves streams, over n_layers * n_units units.
+__attribute__((visibility("hidden"))) hipError_t dkv_stream_step(const void* table, const void* layers_a_bytes,
+                                                                 int n_items_a, size_t lds_a, const int32_t* sched,
+                                                                 int n_waves, int n_sched_items, int top_k,
+                                                                 int n_layers, int n_units, hipStream_t st) {
+  LayerArgs none;
+  memset(&none, 0, sizeof(none));
+  hipError_t e = dkv_stream_launch(table, &none, layers_a_bytes, n_items_a, lds_a, st);
+  if (e != hipSuccess) return e;
+  LayersArgs L;
+  memcpy(&L, layers_a_bytes, sizeof(L));
+  BlocksArgs B;
+  B.table = (const LayerArgs*)table;
+  B.sched = sched;
+  B.ctrl = L.ctrl;
+  B.n_waves = n_waves;
+  B.top_k = top_k;
+  if (n_waves > 0) {
+    hipLaunchKernelGGL(k_blocks, dim3((unsigned)n_waves), dim3(64), (size_t)kBLds, st, B);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int32_t* unit_parts = sched + (n_waves + 1) + 4 * (int64_t)n_sched_items;
+  hipLaunchKernelGGL(k_merges, dim3((unsigned)(n_layers * n_units)), dim3(kAttThreads), 0, st,
+                     (const LayerArgs*)table, n_units, unit_parts, L.ctrl);
   return hipGetLastError();
 }

@@ -76,7 +76,9 @@ class LayersPlanC(ctypes.Structure):
                 ("parts", ctypes.c_int32), ("win_parts", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("n_items", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("max_tiles", ctypes.c_int32), ("quantised", ctypes.c_int32), ("unrotated", ctypes.c_int32),
-                ("stream", ctypes.c_int32), ("stream_blocks", ctypes.c_int32),
+                ("stream", ctypes.c_int32), ("stream_top_k", ctypes.c_int32),
+                ("stream_items", ctypes.c_int32), ("stream_waves", ctypes.c_int32),
+                ("stream_sched", ctypes.c_int32),
                 ("table", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p)]
 

@@ -363,8 +363,12 @@ typedef struct dkv_layers_plan {
   int32_t max_tiles;      /* largest 16-column low-rank tile count of the layers */
   int32_t quantised;      /* 1 if any layer's residual rows are quantised */
   int32_t unrotated;      /* 1 if the layers' pools are un-rotated (all of them or none) */
-  int32_t stream;         /* 1: the streaming launch (every layer qualifies, see dkv_decode) */
-  int32_t stream_blocks;  /* streaming launch: routed blocks per block part */
+  int32_t stream;         /* 1: the streaming launches (every layer qualifies): the routings, then one
+                             stream of window rows and routed blocks per wave, then the merges */
+  int32_t stream_top_k;   /* streaming launches: routed blocks per unit */
+  int32_t stream_items;   /* streaming launches: work items of the streams' schedule */
+  int32_t stream_waves;   /* streaming launches: streams (one-wave workgroups) */
+  int32_t stream_sched;   /* streaming launches: 32-bit word offset of the schedule in the workspace */
   const void* table;
   void* workspace;
 } dkv_layers_plan;
