@@ -30,12 +30,10 @@
 
 #include <mutex>
 
-// The streaming launches (dkv_stream.hip).
+// The layer-batched streaming step (dkv_stream.hip).
 size_t dkv_stream_lds_bytes();
-hipError_t dkv_stream_launch(const void* table, const void* one, const void* layers, int n_items, size_t lds,
-                             hipStream_t st);
-hipError_t dkv_stream_step(const void* table, const void* layers_a, int n_items_a, size_t lds_a, const int32_t* sched,
-                           int n_waves, int n_sched_items, int top_k, int n_layers, int n_units, hipStream_t st);
+hipError_t dkv_stream_step(const void* table, uint32_t* ctrl, size_t route_lds, const int32_t* sched, int n_waves,
+                           int n_sched_items, int top_k, int n_layers, int n_units, hipStream_t st);
 
 #include <algorithm>
 #include <queue>
@@ -1906,23 +1904,12 @@ struct WsLayout {
 // the window has parts of its own, of kWinChunk rows).  Un-rotated pools never
 // fold: their block parts then start with empty output accumulators, which
 // keeps the registers the rotation needs free.
-// Window rows per window part of the streaming launch: 256 with one launch
-// per layer (more, shorter parts), kWinChunk with several layers.
-constexpr int kStreamWinChunk = 256;
-
-int stream_win_parts(int window, int chunk) {
-  const int n = (window + chunk - 1) / chunk;
-  return n > 0 ? n : 1;
-}
-
-// Parts per unit reserved in a decode workspace: enough for the classic
-// launches (window folded or not) and for the streaming launch.
+//
+// Parts per unit reserved in a decode workspace: enough for the fused launch
+// with the window folded or not.
 size_t reserved_parts(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool fold) {
   fold = fold && !pool->rope_freq;
-  const size_t classic = (top_k > 0 && fold) ? (size_t)top_k
-                                             : (size_t)top_k + (size_t)decode_win_parts(batch->window);
-  const size_t stream = (size_t)top_k + (size_t)stream_win_parts(batch->window, kStreamWinChunk);
-  return classic > stream ? classic : stream;
+  return (top_k > 0 && fold) ? (size_t)top_k : (size_t)top_k + (size_t)decode_win_parts(batch->window);
 }
 
 bool al_view(const dkv_view& v, int esz, int a) {
@@ -1971,17 +1958,13 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
                              uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
-                             bool fold = true, bool row_merges = true, int stream_blocks = 0, int stream_chunk = 0,
-                             size_t min_parts = 0) {
+                             bool fold = true, bool row_merges = true, size_t min_parts = 0) {
   const WsLayout w = decode_layout(pool, batch, top_k, fold, min_parts);
   // folded, each routed-block part also takes its share of the window;
-  // otherwise the window comes in chunks of kWinChunk rows.  The streaming
-  // launch has parts of stream_blocks routed blocks and window parts of
-  // stream_chunk rows.
-  fold = fold && top_k > 0 && !pool->rope_freq && stream_blocks == 0;
-  const int n_block = stream_blocks > 0 ? (top_k + stream_blocks - 1) / stream_blocks : top_k;
-  const int n_win = stream_blocks > 0 ? stream_win_parts(batch->window, stream_chunk)
-                                      : (fold ? 0 : decode_win_parts(batch->window));
+  // otherwise the window comes in chunks of kWinChunk rows
+  fold = fold && top_k > 0 && !pool->rope_freq;
+  const int n_block = top_k;
+  const int n_win = fold ? 0 : decode_win_parts(batch->window);
   const int n_parts = n_block + n_win;
   const int units = batch->batch * pool->n_kv_heads;
   AttnArgs& a = D.att;
@@ -1990,8 +1973,7 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   a.n_block_parts = n_block;
   a.block_mode = 3;
   a.n_win_parts = n_win;
-  a.win_chunk = stream_blocks > 0 ? stream_chunk : kWinChunk;
-  a.blocks_per_item = stream_blocks;
+  a.win_chunk = kWinChunk;
   a.win_tile_stride = fold ? top_k : 0;
   a.items_per_unit = n_parts;
   a.rq = top_k > 0 ? rq_of(pool->rank) : 0;
@@ -2017,7 +1999,7 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   if (items > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many work items (%lld)", (long long)items);
   D.n_part_end = (int)part_end;
   D.n_items = (int)items;
-  shm = stream_blocks > 0 ? dkv_stream_lds_bytes() : (size_t)att_lds_bytes(a.rq);
+  shm = (size_t)att_lds_bytes(a.rq);
   const size_t route_shm = route_lds_bytes(batch->max_blocks, kAttWaves);
   if (top_k > 0 && route_shm > shm) shm = route_shm;
   return DKV_OK;
@@ -2264,35 +2246,13 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   const hipStream_t st = (hipStream_t)stream;
   DecodeArgs D;
   size_t shm = 0;
-  const bool streaming = false;  // one launch per layer: the classic launch (streaming parts hold four blocks)
   if ((s = build_decode_args(pool, batch, top_k, scale, (unsigned char*)workspace, (uint32_t*)workspace, out, out_lse,
-                             out_idx, D, shm, true, true, streaming ? 1 : 0, kStreamWinChunk)))
+                             out_idx, D, shm)))
     return s;
   const AttnArgs& a = D.att;
 
   if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)
     return fail(DKV_ERR_HIP, "hipEventRecord failed");
-  if (streaming) {
-    LayerArgs one;
-    memset(&one, 0, sizeof(one));
-    one.P = make_pool_args(pool);
-    one.Bt = make_batch_args(pool, batch);
-    one.D = D;
-    one.nrq = a.rq / 16;
-    LayersArgs L;
-    L.ctrl = (uint32_t*)workspace;
-    L.n_layers = 1;
-    L.n_units = D.n_units;
-    L.routes = D.n_route > 0 ? 1 : 0;
-    L.block_parts = a.n_block_parts;
-    L.win_parts = a.n_win_parts;
-    L.group = D.merges;
-    const hipError_t e = dkv_stream_launch(nullptr, &one, &L, D.n_items, shm, st);
-    if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_stream launch failed: %s", hipGetErrorString(e));
-    if (events && hipEventRecord((hipEvent_t)events[1], st) != hipSuccess)
-      return fail(DKV_ERR_HIP, "hipEventRecord failed");
-    return DKV_OK;
-  }
   switch (a.rq / 16) {
     case 0: s = launch_decode_nrq<0>(shm, st, pool, batch, D); break;
     case 1: s = launch_decode_nrq<1>(shm, st, pool, batch, D); break;
@@ -2468,14 +2428,15 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
     const size_t min_parts = streams ? (size_t)stream_unit_items(pool, batch, top_k) : 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
                                out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
-                               /*row_merges=*/false, 0, kWinChunk, min_parts)))
+                               /*row_merges=*/false, min_parts)))
       break;
     host[l].P = make_pool_args(pool);
     host[l].Bt = make_batch_args(pool, batch);
     host[l].nrq = host[l].D.att.rq / 16;
     if (streams) {
-      // the first launch of the step holds the routings only; the partials are
-      // the streams' runs' (at most one per item of the unit)
+      // the routings launch needs only routing LDS; the partials are the
+      // streams' runs' (at most one per item of the unit)
+      shm_l = route_lds_bytes(batch->max_blocks, kAttWaves);
       DecodeArgs& D = host[l].D;
       D.att.n_block_parts = 0;
       D.att.n_win_parts = 0;
@@ -2509,28 +2470,36 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
       int64_t cost;
       int32_t unit;  // layer * units + unit
     };
-    const int64_t kPageCost = 1024;  // a page's fixed cost, in bytes
+    // An item's cost, in stream clock cycles: every page waits about a memory
+    // latency over the ring depth and an issue slot (kPage), plus its own
+    // arithmetic: a K page's scores and softmax, a V page's products, a V_K or
+    // V_V page's tile (the first V_K page also builds the position mask and
+    // q . a_k), and a U page's 32-position groups, each dearer with more
+    // 16-wide rank tiles.  (Measured per page kind on the streams.)
+    const int64_t kPage = 1500, kK = 500, kV = 110, kVK = 650, kVK0 = 700, kVV = 850;
+    const int64_t kUGroup = 900, kUGroupTile = 250, kItemEntry = 1600;
     std::vector<Item> items;
     items.reserve((size_t)n_sched);
     for (int l = 0; l < n_layers; ++l) {
       const int r = pools[l].rank, R = pools[l].n_resid, W = batches[l].window;
-      const int nqv = (r + 1 + 15) / 16;
+      const int nq = (r + 15) / 16, mu = r <= 16 ? 4 : (r <= 32 ? 2 : 1), nu = 8 / mu;
+      const int64_t lowrank = kItemEntry + (2 * nq + nu) * kPage + nq * (kVK + kVV) + kVK0 +
+                              8 * (kUGroup + (nq - 1) * kUGroupTile);
       for (int u = 0; u < units; ++u) {
         const uint32_t bh = (uint32_t)(u / p0.n_kv_heads) | ((uint32_t)(u % p0.n_kv_heads) << 16);
         const int32_t ug = l * units + u;
         for (int r0 = 0; r0 < W; r0 += kStreamWinRows) {
           const int rows = W - r0 < kStreamWinRows ? W - r0 : kStreamWinRows;
           items.push_back({{(uint32_t)l | (kItemWin << 16), (uint32_t)r0, bh, (uint32_t)rows << 16},
-                           (int64_t)rows * 512 + 2 * ((rows + 15) / 16) * kPageCost, ug});
+                           kItemEntry + ((rows + 15) / 16) * (2 * kPage + kK + kV), ug});
         }
         for (int k = 0; k < top_k; ++k) {
-          items.push_back({{(uint32_t)l | (kItemLowRank << 16), (uint32_t)k, bh, 0u},
-                           (int64_t)2 * (r + 1) * 256 + 510 * r + R + (2 * nqv + 8) * kPageCost, ug});
+          items.push_back({{(uint32_t)l | (kItemLowRank << 16), (uint32_t)k, bh, 0u}, lowrank, ug});
           for (int r0 = 0; r0 < R; r0 += kStreamResRows) {
             const int rows = R - r0 < kStreamResRows ? R - r0 : kStreamResRows;
             items.push_back({{(uint32_t)l | (kItemResid << 16), (uint32_t)k | ((uint32_t)r0 << 16), bh,
                               (uint32_t)rows << 16},
-                             (int64_t)rows * 512 + 2 * ((rows + 15) / 16) * kPageCost, ug});
+                             kItemEntry + ((rows + 15) / 16) * (2 * kPage + kK + kV), ug});
           }
         }
       }
@@ -2622,10 +2591,10 @@ dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
   L.win_parts = plan->win_parts;
   L.group = plan->group;
   if (plan->stream) {
-    const hipError_t e = dkv_stream_step(plan->table, &L, plan->n_items, (size_t)plan->lds_bytes,
+    const hipError_t e = dkv_stream_step(plan->table, L.ctrl, (size_t)plan->lds_bytes,
                                          (const int32_t*)plan->workspace + plan->stream_sched, plan->stream_waves,
-                                         plan->stream_items, plan->stream_top_k, plan->n_layers,
-                                         plan->n_units, (hipStream_t)stream);
+                                         plan->stream_items, plan->stream_top_k, plan->n_layers, plan->n_units,
+                                         (hipStream_t)stream);
     if (e != hipSuccess) return fail(DKV_ERR_HIP, "streaming launches failed: %s", hipGetErrorString(e));
     return DKV_OK;
   }

@@ -87,7 +87,6 @@ struct AttnArgs {
   float* part_lse;
   int n_parts;
   int part_offset;
-  int blocks_per_item; // streaming launch: routed blocks per block part
 };
 
 // ----------------------------------------------------------------------------

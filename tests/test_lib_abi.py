@@ -126,11 +126,9 @@ def test_workspace_size_formula(clib):
     for window in (0, 64, 300):
         b = _batch(window=window)
         for top_k in (0, 1, 16, 64):
-            # the larger of the classic launch's parts (routed-block parts each with a
-            # share of the window, or window chunks of 512 rows) and the streaming
-            # launch's (top_k block parts and window parts of 256 rows)
-            classic = top_k if top_k > 0 else max(1, (window + 511) // 512)
-            n_parts = max(classic, top_k + max(1, (window + 255) // 256))
+            # the fused launch's parts: routed-block parts each with a share of the
+            # window, or (no routed blocks) window chunks of 512 rows
+            n_parts = top_k if top_k > 0 else max(1, (window + 511) // 512)
             rows, units = 2 * 12, 2 * 2
             ctrl = 4096 + a256(units * 4) + a256(units * top_k * 4)  # counters/queues, per-unit, routed slots
             want = ctrl + a256(units * top_k * 4) + a256(rows * n_parts * 4) \
