@@ -33,7 +33,9 @@
 // The layer-batched streaming step (dkv_stream.hip).
 size_t dkv_stream_lds_bytes();
 hipError_t dkv_stream_step(const void* table, uint32_t* ctrl, size_t route_lds, const int32_t* sched, int n_waves,
-                           int n_sched_items, int top_k, int n_layers, int n_units, hipStream_t st);
+                           int n_sched_items, int top_k, int n_layers, int n_units, void* const* events,
+                           hipStream_t st);
+hipError_t dkv_stream_read_probe_launch(const void* src, size_t per, int n_waves, uint32_t* sink, hipStream_t st);
 
 #include <algorithm>
 #include <queue>
@@ -2578,10 +2580,39 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
   return s;
 }
 
-dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
+static dkv_status layers_step(const dkv_layers_plan* plan, void* const* events, void* stream);
+
+dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) { return layers_step(plan, nullptr, stream); }
+
+dkv_status dkv_decode_layers_profiled(const dkv_layers_plan* plan, void* const* events, void* stream) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) {
+    g_err[0] = 0;
+    return fail(DKV_ERR_INVALID_ARG, "events must hold four hipEvent_t handles");
+  }
+  return layers_step(plan, events, stream);
+}
+
+dkv_status dkv_stream_read_probe(const void* src, size_t bytes, int32_t n_waves, uint32_t* sink, void* stream) {
+  g_err[0] = 0;
+  if (!src || !sink) return fail(DKV_ERR_INVALID_ARG, "src / sink is NULL");
+  if (n_waves < 1 || n_waves > 65536) return fail(DKV_ERR_INVALID_ARG, "n_waves %d out of [1, 65536]", n_waves);
+  if (!al(src, 16) || bytes % ((size_t)4096 * n_waves) != 0 || bytes / n_waves > 0xFFFFF000u)
+    return fail(DKV_ERR_INVALID_ARG, "bytes %zu must be a multiple of 4096 * n_waves (< 4 GiB per wave), src 16-byte aligned",
+                bytes);
+  if (bytes == 0) return DKV_OK;
+  const hipError_t e = dkv_stream_read_probe_launch(src, bytes / n_waves, n_waves, sink, (hipStream_t)stream);
+  return e == hipSuccess ? DKV_OK : fail(DKV_ERR_HIP, "read probe launch failed: %s", hipGetErrorString(e));
+}
+
+static dkv_status layers_step(const dkv_layers_plan* plan, void* const* events, void* stream) {
   g_err[0] = 0;
   if (!plan || !plan->table || !plan->workspace) return fail(DKV_ERR_INVALID_ARG, "plan is NULL or not prepared");
-  if (plan->n_items == 0) return DKV_OK;
+  if (plan->n_items == 0 && !plan->stream) {
+    for (int k = 0; events && k < 4; ++k)
+      if (hipEventRecord((hipEvent_t)events[k], (hipStream_t)stream) != hipSuccess)
+        return fail(DKV_ERR_HIP, "hipEventRecord failed");
+    return DKV_OK;
+  }
   LayersArgs L;
   L.ctrl = (uint32_t*)plan->workspace;
   L.n_layers = plan->n_layers;
@@ -2590,23 +2621,34 @@ dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream) {
   L.block_parts = plan->parts;
   L.win_parts = plan->win_parts;
   L.group = plan->group;
+  const hipStream_t st = (hipStream_t)stream;
+  if (events && hipEventRecord((hipEvent_t)events[0], st) != hipSuccess)
+    return fail(DKV_ERR_HIP, "hipEventRecord failed");
+  dkv_status s = DKV_OK;
   if (plan->stream) {
     const hipError_t e = dkv_stream_step(plan->table, L.ctrl, (size_t)plan->lds_bytes,
                                          (const int32_t*)plan->workspace + plan->stream_sched, plan->stream_waves,
                                          plan->stream_items, plan->stream_top_k, plan->n_layers, plan->n_units,
-                                         (hipStream_t)stream);
+                                         events, st);
     if (e != hipSuccess) return fail(DKV_ERR_HIP, "streaming launches failed: %s", hipGetErrorString(e));
-    return DKV_OK;
+  } else {
+    switch (plan->max_tiles) {  // the largest low-rank tile count of the layers
+      case 0: s = launch_layers<0>(plan, L, st); break;
+      case 1: s = launch_layers<1>(plan, L, st); break;
+      case 2: s = launch_layers<2>(plan, L, st); break;
+      case 3: s = launch_layers<3>(plan, L, st); break;
+      case 4: s = launch_layers<4>(plan, L, st); break;
+      case 5: s = launch_layers<5>(plan, L, st); break;
+      default: return fail(DKV_ERR_INVALID_ARG, "plan is corrupt (tile count %d)", plan->max_tiles);
+    }
+    if (s) return s;
+    if (events && (hipEventRecord((hipEvent_t)events[1], st) != hipSuccess ||
+                   hipEventRecord((hipEvent_t)events[2], st) != hipSuccess))
+      return fail(DKV_ERR_HIP, "hipEventRecord failed");
   }
-  switch (plan->max_tiles) {  // the largest low-rank tile count of the layers
-    case 0: return launch_layers<0>(plan, L, (hipStream_t)stream);
-    case 1: return launch_layers<1>(plan, L, (hipStream_t)stream);
-    case 2: return launch_layers<2>(plan, L, (hipStream_t)stream);
-    case 3: return launch_layers<3>(plan, L, (hipStream_t)stream);
-    case 4: return launch_layers<4>(plan, L, (hipStream_t)stream);
-    case 5: return launch_layers<5>(plan, L, (hipStream_t)stream);
-    default: return fail(DKV_ERR_INVALID_ARG, "plan is corrupt (tile count %d)", plan->max_tiles);
-  }
+  if (events && hipEventRecord((hipEvent_t)events[3], st) != hipSuccess)
+    return fail(DKV_ERR_HIP, "hipEventRecord failed");
+  return DKV_OK;
 }
 
 }  // extern "C"

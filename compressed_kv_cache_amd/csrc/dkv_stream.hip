@@ -44,8 +44,8 @@ constexpr int kWChunks = kWPage / 16;       // 16-byte chunks per ring slot
 constexpr int kWSlots = 4;                  // ring depth per wave
 constexpr int kWRing = kWPage * kWSlots;    // one wave's ring
 enum { kBaseAK = 0, kBaseAV, kBaseU, kBaseVK, kBaseVV, kBaseRP, kBases };
-constexpr int kBPosOff = kWRing;            // the residual positions of a low-rank item [128] bytes
-constexpr int kBBaseOff = kBPosOff + 128;   // the issuing low-rank item's source addresses [kBases] u64
+constexpr int kBPosOff = kWRing;            // the residual positions of a low-rank item [256] bytes
+constexpr int kBBaseOff = kBPosOff + 256;   // the issuing low-rank item's source addresses [kBases] u64
 constexpr int kBAncOff = kBBaseOff + 64;    // anchor rows a_k, a_v of low-rank items, two buffers [2][512] bytes
 constexpr int kBLds = kBAncOff + 2 * 512;
 
@@ -210,13 +210,15 @@ __device__ __forceinline__ void lds_b64x44(uint32_t a, uint32_t b, v4h (&o)[8]) 
       : "v"(a), "v"(b)
       : "memory");
 }
-// two bytes at a and a + 64
-__device__ __forceinline__ void lds_u8x2(uint32_t a, uint32_t& x, uint32_t& y) {
+// four bytes at a, a + 64, a + 128, a + 192
+__device__ __forceinline__ void lds_u8x4(uint32_t a, uint32_t (&x)[4]) {
   asm volatile(
-      "ds_read_u8 %0, %2\n\t"
-      "ds_read_u8 %1, %2 offset:64\n\t"
+      "ds_read_u8 %0, %4\n\t"
+      "ds_read_u8 %1, %4 offset:64\n\t"
+      "ds_read_u8 %2, %4 offset:128\n\t"
+      "ds_read_u8 %3, %4 offset:192\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x), "=&v"(y)
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
       : "v"(a)
       : "memory");
 }
@@ -383,7 +385,7 @@ __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned cha
     if (lane < 32) dma16(a, ancdst);
     ++ops;
     if (g.R > 0) {
-      // the residual positions: R bytes as R / 4 dwords (R % 4 == 0)
+      // the residual positions: R <= 255 bytes as R / 4 dwords (R % 4 == 0)
       const __amdgpu_buffer_rsrc_t rp = rsrc_of(uniform_ptr(bb[kBaseRP]), (uint32_t)g.R);
       if (4 * lane < g.R) dma4b(rp, (uint32_t)(4 * lane), posdst);
       ++ops;
@@ -507,14 +509,16 @@ __device__ __forceinline__ void page_vk(const WaveGeom& g, int i, uint32_t P0, c
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) aq = mfma32(l16 == 0 ? ak[s2] : zero, qf[s2], aq);
     br.qa = hq_sum(q4 == 0 ? aq[0] * scale : 0.f);
-    uint32_t p1 = 0u, p2 = 0u;
-    lds_u8x2(posb + lane, p1, p2);
-    p1 = lane < g.R ? p1 : 0u;
-    p2 = lane + 64 < g.R ? p2 : 0u;
+    // positions lane + 64 j of the block's R (distinct, in 1..255, any order)
+    uint32_t p[4];
+    lds_u8x4(posb + lane, p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = lane + 64 * j < g.R ? p[j] : 0u;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const uint32_t v = ((p1 >> 5) == (uint32_t)w && p1 >= 1u ? 1u << (p1 & 31) : 0u) |
-                         ((p2 >> 5) == (uint32_t)w && p2 >= 1u ? 1u << (p2 & 31) : 0u);
+      uint32_t v = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v |= (p[j] >> 5) == (uint32_t)w && p[j] >= 1u ? 1u << (p[j] & 31) : 0u;
       br.mw[w] = wave_or(v);
     }
   }
@@ -995,6 +999,47 @@ __global__ __launch_bounds__(kAttThreads) void k_merges(const LayerArgs* __restr
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) ctrl[3] = ctrl[3] + 1u;
 }
 
+// The streams' read ceiling: workgroup w reads bytes [w per, (w + 1) per) of
+// src through its four-page ring with the same 16-byte buffer loads into LDS
+// (four per 4096-byte page, up to four pages ahead), reads each page back
+// once and writes the wrapping sum of its 32-bit words to sink[w].
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(64) void k_read_probe(const unsigned char* __restrict__ src, uint32_t per,
+                                                   uint32_t* __restrict__ sink) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = rsrc_of(src + (size_t)blockIdx.x * per, per);
+  const int npages = (int)(per / 4096u);
+  const uint32_t ring0 = lds_off(smem);
+  uint32_t acc = 0u;
+  for (int n = 0; n < 4 && n < npages; ++n)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma16b(rs, (uint32_t)n * 4096u + 1024u * k + 16u * lane, smem + 4096 * n + 1024 * k);
+  for (int n = 0; n < npages; ++n) {
+    const int newer = npages - n - 1 < 3 ? npages - n - 1 : 3;
+    wait_vm(4 * newer);
+    v4u w[4];  // bytes 16 lane + 1024 k of the page
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+        : "v"(ring0 + 4096u * (uint32_t)(n & 3) + 16u * (uint32_t)lane)
+        : "memory");
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += w[k][0] + w[k][1] + w[k][2] + w[k][3];
+    if (n + 4 < npages)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        dma16b(rs, (uint32_t)(n + 4) * 4096u + 1024u * k + 16u * lane, smem + 4096 * (n & 3) + 1024 * k);
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += (uint32_t)__shfl_xor((int)acc, o);
+  if (lane == 0) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 // LDS bytes of a stream (one-wave workgroup).
@@ -1005,15 +1050,22 @@ __attribute__((visibility("hidden"))) size_t dkv_stream_lds_bytes() { return (si
 // merges (k_merges).  sched: the step's schedule in device memory (see
 // k_blocks), with n_waves streams and n_sched_items items, over n_layers *
 // n_units units; ctrl: the step's control header.
+// events: NULL, or hipEvent_t handles [1] (recorded after the routings) and
+// [2] (after the streams).
 __attribute__((visibility("hidden"))) hipError_t dkv_stream_step(const void* table, uint32_t* ctrl,
                                                                  size_t route_lds, const int32_t* sched,
                                                                  int n_waves, int n_sched_items, int top_k,
-                                                                 int n_layers, int n_units, hipStream_t st) {
+                                                                 int n_layers, int n_units, void* const* events,
+                                                                 hipStream_t st) {
   const LayerArgs* T = (const LayerArgs*)table;
   if (top_k > 0) {
     hipLaunchKernelGGL(k_routes, dim3((unsigned)(n_layers * n_units)), dim3(kAttThreads), route_lds, st, T,
                        n_units, top_k);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (events) {
+    hipError_t e = hipEventRecord((hipEvent_t)events[1], st);
     if (e != hipSuccess) return e;
   }
   BlocksArgs B;
@@ -1027,8 +1079,22 @@ __attribute__((visibility("hidden"))) hipError_t dkv_stream_step(const void* tab
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (events) {
+    hipError_t e = hipEventRecord((hipEvent_t)events[2], st);
+    if (e != hipSuccess) return e;
+  }
   const int32_t* unit_parts = sched + (n_waves + 1) + 4 * (int64_t)n_sched_items;
   hipLaunchKernelGGL(k_merges, dim3((unsigned)(n_layers * n_units)), dim3(kAttThreads), 0, st, T, n_units,
                      unit_parts, ctrl);
+  return hipGetLastError();
+}
+
+// The streams' read ceiling (see k_read_probe): n_waves workgroups of `per`
+// bytes each (a multiple of 4096).
+__attribute__((visibility("hidden"))) hipError_t dkv_stream_read_probe_launch(const void* src, size_t per,
+                                                                              int n_waves, uint32_t* sink,
+                                                                              hipStream_t st) {
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)n_waves), dim3(64), (size_t)(4 * 4096), st,
+                     (const unsigned char*)src, (uint32_t)per, sink);
   return hipGetLastError();
 }

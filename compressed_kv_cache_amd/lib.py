@@ -34,7 +34,7 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
             "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
             "dkv_seal_blocks", "dkv_rope_freqs", "dkv_join_basis", "dkv_decode_noalloc",
-            "dkv_decode_noalloc_max_bytes")
+            "dkv_decode_noalloc_max_bytes", "dkv_decode_layers_profiled", "dkv_stream_read_probe")
 
 
 class DKVError(RuntimeError):
@@ -120,6 +120,10 @@ def load(path: str = LIB_PATH):
     lib.dkv_decode_layers_prepare.restype = i32
     lib.dkv_decode_layers.argtypes = [ctypes.POINTER(LayersPlanC), vp]
     lib.dkv_decode_layers.restype = i32
+    lib.dkv_decode_layers_profiled.argtypes = [ctypes.POINTER(LayersPlanC), vp, vp]
+    lib.dkv_decode_layers_profiled.restype = i32
+    lib.dkv_stream_read_probe.argtypes = [vp, ctypes.c_size_t, i32, vp, vp]
+    lib.dkv_stream_read_probe.restype = i32
     lib.dkv_seal_blocks.argtypes = [P, View, View, vp, i32, vp, i32, i32, vp]
     lib.dkv_seal_blocks.restype = i32
     lib.dkv_gather_route_keys.restype = i32
@@ -536,6 +540,14 @@ def decode_profiled(pool: Pool, batch: Batch, top_k: int, scale: float, workspac
            "dkv_decode_profiled")
 
 
+def read_probe(src, n_waves: int, sink, stream=None) -> None:
+    """dkv_stream_read_probe over the bytes of device tensor `src` (a multiple of
+    4096 * n_waves); sink: int32 or uint32 device tensor of n_waves words."""
+    assert sink.numel() >= n_waves
+    _check(load().dkv_stream_read_probe(_ptr(src), src.numel() * src.element_size(), n_waves, _ptr(sink),
+                                        _stream(stream)), "dkv_stream_read_probe")
+
+
 class Layers:
     """A prepared layer-batched decode (dkv_decode_layers_prepare): the fused
     decode steps of several layers in one launch per run().  Holds the device
@@ -571,6 +583,13 @@ class Layers:
 
     def run(self, stream=None) -> None:
         _check(load().dkv_decode_layers(ctypes.byref(self.plan), _stream(stream)), "dkv_decode_layers")
+
+    def run_profiled(self, events, stream=None) -> None:
+        """run() plus four hipEvent_t records (raw handles as ints): before the
+        step, after the routings, after the streams, after the merges."""
+        arr = (ctypes.c_void_p * 4)(*events)
+        _check(load().dkv_decode_layers_profiled(ctypes.byref(self.plan), arr, _stream(stream)),
+               "dkv_decode_layers_profiled")
 
     def timeout_flag(self) -> int:
         """The workspace's sticky wait-timeout word (0 in every correct run)."""

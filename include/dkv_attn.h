@@ -325,30 +325,40 @@ dkv_status dkv_decode_noalloc(const dkv_pool* pool, const dkv_batch* batch, int3
 size_t dkv_decode_noalloc_max_bytes(void);
 
 /* ---- Layer-batched decode -------------------------------------------------
- * The fused decode step (dkv_decode) of n_layers independent layers in ONE
- * launch, so that the routing, block-attention and merge phases of different
- * layers overlap and the launch streams the cache at full bandwidth.  Use it
- * when several layers' queries are at hand at once: micro-batches in flight at
- * different layers, or a model's layers evaluated on given queries.  All
- * layers share head_dim, block size, n_kv_heads and the batch shape (batch,
- * n_q_heads, window, max_blocks) and top_k; pools may differ in rank, residual
- * count and slot count.  The routed blocks are those of n_layers dkv_decode
- * calls; the window rows are split into parts of their own (rather than shared
- * out over the routed-block parts), so outputs equal dkv_decode's up to the
- * rounding of that other split, and repeat bit for bit from launch to launch.
- * Each unit's G query rows are combined by one merge item (the merges of the
- * other layers keep the chip busy), so plan->group is 1.
+ * The fused decode step (dkv_decode) of n_layers independent layers at once,
+ * so that the layers' work shares the chip and the step streams the cache at
+ * full bandwidth.  Use it when several layers' queries are at hand at once:
+ * micro-batches in flight at different layers, or a model's layers evaluated
+ * on given queries (a single token's layers depend on each other and cannot).
+ * All layers share head_dim, block size, n_kv_heads and the batch shape
+ * (batch, n_q_heads, window, max_blocks) and top_k; pools may differ in rank,
+ * residual count and slot count.  The routed blocks are those of n_layers
+ * dkv_decode calls; outputs equal dkv_decode's up to the rounding of another
+ * split of the rows into partials, and repeat bit for bit from step to step.
+ *
+ * When every layer's pool qualifies (rotated keys, fp16 residual rows, rank a
+ * multiple of 8 up to 56, residual count a multiple of 4, 16-byte aligned
+ * arrays; plan->stream = 1), a step is three launches: the routings; the
+ * streams, one-wave workgroups each running a contiguous segment of the step's
+ * work (window rows, the low-rank parts and the residual rows of the routed
+ * blocks; segments of about equal cost, fixed at prepare) through its own LDS
+ * ring; and the log-sum-exp merges of each unit's partials.  Otherwise a step
+ * is one launch whose routing, block-attention and merge items come from
+ * per-XCD queues (the window in parts of its own; plan->group merge items per
+ * unit).
  *
  * dkv_decode_layers_prepare (once; synchronous, not capturable in a graph)
  * validates every layer, writes the per-layer argument table into `table`
  * (device memory of dkv_decode_layers_table_size bytes, caller-owned), zeroes
  * the control words of `workspace` (device memory of
- * dkv_decode_layers_workspace_size bytes, 256-byte aligned, caller-owned) and
- * fills *plan.  dkv_decode_layers (any number of times; asynchronous, may be
- * captured) runs one step.  The pools, batches, outputs, table and workspace
- * given to prepare must keep their addresses; their contents (e.g. the
- * queries) may change between calls.  Calls sharing a workspace must not
- * overlap.  Word 2 of the workspace is the sticky wait-timeout flag.
+ * dkv_decode_layers_workspace_size bytes, 256-byte aligned, caller-owned),
+ * writes the streams' schedule into it, and fills *plan.  dkv_decode_layers
+ * (any number of times; asynchronous, may be captured) runs one step.  The
+ * pools, batches, outputs, table and workspace given to prepare must keep
+ * their addresses; their contents (e.g. the queries, window lengths, block
+ * tables) may change between calls.  Calls sharing a workspace must not
+ * overlap.  Word 2 of the workspace is the sticky wait-timeout flag (one
+ * launch only).
  *   outs[l]: fp16 [B][Hq][d]; out_lses[l]: fp32 [B][Hq];
  *   out_idxs: NULL, or per layer int32 [B][Hkv][top_k] or NULL. */
 typedef struct dkv_layers_plan {
@@ -381,6 +391,25 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
                                      int32_t* const* out_idxs, void* table, size_t table_bytes,
                                      void* workspace, size_t workspace_bytes, dkv_layers_plan* plan);
 dkv_status dkv_decode_layers(const dkv_layers_plan* plan, void* stream);
+
+/* dkv_decode_layers with timing (the pages' DKV_PROFILE_CB knob, README "Key
+ * Environment Knobs": GPU-kernel latency profiling).  Identical results;
+ * additionally records the four caller-created hipEvent_t handles in `events`
+ * on `stream`: [0] before the step, [1] after the routings, [2] after the
+ * streams, [3] after the merges (a one-launch step: [1] and [2] right before
+ * [3], after its launch). */
+dkv_status dkv_decode_layers_profiled(const dkv_layers_plan* plan, void* const* events, void* stream);
+
+/* The streams' read ceiling: the loads dkv_decode_layers streams with (16-byte
+ * buffer loads straight into a four-page LDS ring, one ring per one-wave
+ * workgroup) over a plain array, as a measure of the box's streaming-read
+ * bandwidth for them.  n_waves workgroups each read a contiguous 1/n_waves of
+ * `src` (device memory, `bytes` a multiple of 4096 * n_waves, 16-byte
+ * aligned) in pages of 4096 bytes, and write the 32-bit wrapping sum of their
+ * share's 32-bit words to sink[w] (uint32, device memory).  Asynchronous on
+ * `stream`.  DKV_ERR_INVALID_ARG for a size, alignment or count it cannot
+ * take. */
+dkv_status dkv_stream_read_probe(const void* src, size_t bytes, int32_t n_waves, uint32_t* sink, void* stream);
 
 /* Block sealing, the write side of the cache (README "Core Architecture &
  * Paper Overview", items 1-3; "Content-Aware / Rarity-Aware Residual

@@ -640,6 +640,141 @@ def test_decode_layers_graph_replays(lib):
 
 
 # ---------------------------------------------------------------------------
+# The layer-batched streams (plan.stream == 1): every pool qualifies
+# ---------------------------------------------------------------------------
+
+SEDGE = {
+    "r8_no_residuals": dict(ranks=[8], n_resid=0),
+    "r16_R252": dict(ranks=[16], n_resid=252),
+    "r24_R68": dict(ranks=[24], n_resid=68),
+    "r40_R4": dict(ranks=[40], n_resid=4),
+    "r56_R128_G16": dict(ranks=[56], n_resid=128, n_q_heads=16, n_kv_heads=1),
+    "r32_topk_over_blocks": dict(ranks=[32], n_resid=20, top_k=9),
+    "r48_G1_long_ragged_window": dict(ranks=[48], n_resid=36, n_q_heads=2, n_kv_heads=2, window=300,
+                                      win_len=[300, 129, 0, 17]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SEDGE))
+def test_streams_edge_cases(lib, case):
+    """Two layers of a shape the streams take (ranks 8..56 in steps of 8, 0..252
+    residual rows, G = 1..16, ragged and empty windows and sequences, top_k above
+    the block count), in one step: the plan streams, both layers match the
+    oracle, route as dkv_decode does and repeat bit for bit."""
+    kw = dict(batch=4, n_q_heads=6, n_kv_heads=2, window=48, n_blocks=[5, 0, 6, 3],
+              win_len=[48, 0, 17, 30], ranks=[16], n_resid=20, top_k=3, sigma0=2.0)
+    kw.update(SEDGE[case])
+    top_k = kw["top_k"]
+    wls = [synth.make_workload(f"{case}_{i}", seed=900 + 7 * i + len(case), **kw) for i in range(2)]
+    say(f"[streams] {case}")
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, top_k, wls[0].scale)
+    assert run.plan.stream == 1 and run.plan.stream_waves > 0
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        _, _, i1 = lib.decode(pools[l], batches[l], top_k, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        c = _oracle_check(w, w.layers[0], *res[l], top_k)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
+def test_streams_mixed_ranks(lib):
+    """Layers of ranks 8, 24, 40 and 56 with 4, 128 and 252 residual rows in one
+    streamed step (each rank's U pages hold a different number of positions)."""
+    base = dict(batch=2, n_q_heads=12, n_kv_heads=2, window=256, n_blocks=[9, 7], win_len=[256, 100],
+                top_k=5, sigma0=2.0)
+    specs = [(8, 4), (24, 128), (40, 252), (56, 128)]
+    wls = [synth.make_workload(f"smix{i}", seed=950 + i, ranks=[r], n_resid=n, **base)
+           for i, (r, n) in enumerate(specs)]
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, 5, wls[0].scale)
+    assert run.plan.stream == 1
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        c = _oracle_check(w, w.layers[0], *res[l], 5)
+        say(f"   rank {specs[l][0]} R {specs[l][1]}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
+class _HipEvents:
+    """Raw hipEvent_t handles (hipEventCreate through the HIP runtime torch loaded)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def make(self):
+        e = self.ct.c_void_p()
+        assert self.h.hipEventCreate(self.ct.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        t = self.ct.c_float()
+        assert self.h.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a), self.ct.c_void_p(b)) == 0
+        return t.value
+
+    def free(self, e):
+        self.h.hipEventDestroy(self.ct.c_void_p(e))
+
+
+def test_decode_layers_profiled(lib):
+    """dkv_decode_layers_profiled gives run()'s bits and four ordered events
+    (before, after the routings, after the streams, after the merges)."""
+    wl = config(1)
+    pools, batches = _upload_layers(lib, wl, [0, 0])
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    assert run.plan.stream == 1
+    run.run()
+    torch.cuda.synchronize()
+    ref = [(o.clone(), s.clone()) for o, s in zip(run.outs, run.lses)]
+    hip = _HipEvents()
+    ev = [hip.make() for _ in range(4)]
+    for o in run.outs:
+        o.zero_()
+    run.run_profiled(ev)
+    torch.cuda.synchronize()
+    for l, (o, s) in enumerate(ref):
+        assert torch.equal(run.outs[l], o) and torch.equal(run.lses[l], s)
+    gaps = [hip.ms(ev[k], ev[k + 1]) for k in range(3)]
+    assert all(g >= 0.0 for g in gaps) and hip.ms(ev[0], ev[3]) > 0.0, gaps
+    with pytest.raises(lib.DKVError):
+        run.run_profiled([ev[0], 0, ev[2], ev[3]])
+    for e in ev:
+        hip.free(e)
+
+
+@pytest.mark.parametrize("pages", [1, 3, 9])
+def test_stream_read_probe(lib, pages):
+    """The read-ceiling probe reads every byte once: each wave's 32-bit wrapping
+    sum equals numpy's over its share; sizes it cannot take are refused."""
+    n_waves = 40
+    n = n_waves * pages * 4096 // 4
+    g = torch.Generator(device="cpu").manual_seed(1234 + pages)
+    x = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, generator=g).to(DEV)
+    sink = torch.zeros(n_waves, dtype=torch.int32, device=DEV)
+    lib.read_probe(x, n_waves, sink)
+    torch.cuda.synchronize()
+    want = x.cpu().numpy().view(np.uint32).reshape(n_waves, -1).astype(np.uint64).sum(axis=1) % (1 << 32)
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want.astype(np.uint32))
+    with pytest.raises(lib.DKVError):
+        lib.read_probe(x[:-4], n_waves, sink)
+
+
+# ---------------------------------------------------------------------------
 # Residual rows in the 8- and 4-bit group-quantised formats
 # ---------------------------------------------------------------------------
 
