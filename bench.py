@@ -1,42 +1,52 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark over a compressed KV cache on one MI355X.
 
-Workload: the Qwen2.5-1.5B-shaped 28-layer stack at 64k context, batch 4
-(12 query heads over 2 KV heads, d = 128, 252 compressed blocks of 256 tokens
-plus a 1024-token exact window per sequence, 128 residual rows per block, top-K
-= 32 routed blocks, layer ranks 24 / 48 / 16).  Synthetic seeded caches of that
-shape stand in for model-derived KV (no weights or datasets are used).
+Headline workload: the Qwen2.5-1.5B-shaped 28-layer stack at 64k context,
+batch 4 (12 query heads over 2 KV heads, d = 128, 252 compressed blocks of 256
+tokens plus a 1024-token exact window per sequence, 128 residual rows per
+block, top-K = 32 routed blocks, layer ranks 24 / 48 / 16).  Synthetic seeded
+caches of that shape stand in for model-derived KV (no weights or datasets
+are used).
 
 One step = one decode query for each of the 4 sequences in each of the 28
-layers (112 queries): routing, block and window attention and the log-sum-exp
-merge of every layer, with every input resident in HBM.  The step is timed in
-three launch modes:
-  per_layer_eager         28 dkv_decode calls, hipEvents around every kernel;
+layers (112 queries): routing, block and window attention and the
+log-sum-exp merge of every layer, with every input resident in HBM.  The step
+is timed in four launch modes:
+  per_layer_eager         28 dkv_decode calls (one fused launch per layer);
   per_layer_hipgraph      the same 28 calls captured once as a hipGraph;
-  layer_batched_eager     one dkv_decode_layers launch for all 28 layers;
-  layer_batched_hipgraph  that launch captured as a hipGraph.
-`value` is the queries/s of the fastest mode (named in config.timed_mode);
-every mode is reported in ms_per_step_by_mode.  The layer-batched launch does
-the same work, on the same inputs, with the same routing (checked in the run).
+  layer_batched_eager     one dkv_decode_layers step for all 28 layers (three
+                          launches: routings, streams, merges);
+  layer_batched_hipgraph  that step captured as a hipGraph.
+The per-layer modes are the schedule one token's decode runs (layer l+1's
+query needs layer l's output); the layer-batched modes need all the layers'
+queries at once (micro-batches in flight at different layers, or layers
+evaluated on given queries).  `value` is the queries/s of the fastest mode,
+named in config.timed_mode; every mode is in ms_per_step_by_mode, with the
+median and p10 / p90 over the timed steps.
 
-Roofline: the kernel of the timed mode (k_decode for the per-layer modes,
-k_decode_layers for the layer-batched ones).  Its algorithmic bytes per launch
-are, for each (sequence, KV head, layer), the fp32 routing keys of all N blocks
-(512 N bytes), K_eff routed blocks of P(r, R) = 2*(2d + 255 r + 2 r d + 2 R d) + R
-bytes and 2*2*W*d window bytes, plus the fp16 queries, outputs, lse and routed
-indices; divided by that kernel's duration measured with events around it in
-the timed eager steps (kernels back to back behind a spin kernel, as in a
-replay).  `traffic` is the committed rocprofv3 PMC summary for that kernel
-(`--pmc-summary` writes it), null when the kernel source changed since.
+Roofline: the dominant kernel of the timed mode.  For the layer-batched modes
+that is k_blocks (the streams): its algorithmic bytes per launch are the K_eff
+routed blocks of P(r, R) = 2*(2d + 255 r + 2 r d) + 2 R (row bytes) + R bytes
+each, the window rows (2 * 2 * d bytes each) and the fp16 queries (each read
+once per unit), and its duration comes from events around that launch alone
+(dkv_decode_layers_profiled) in the timed eager steps.  For the per-layer
+modes it is k_decode, one launch per layer, over the whole layer's bytes
+(routing keys, 512 bytes per block, included).  `traffic` is the committed
+rocprofv3 PMC summary for that kernel, null when the kernel sources changed
+since it was taken.
 
-Beside the decode (not part of `value`): the same stack with its residual rows
-in the 8- and 4-bit formats (`quantised_residuals`), the same stack read as
-un-rotated pools whose keys are rotated to their absolute positions at read
-(`unrotated_pool`) and with pairs of blocks sharing one basis (`shared_basis`),
-and the write side,
-dkv_seal_blocks sealing one layer's 1008 blocks x 2 KV heads at each of the
-stack's ranks (`sealing`: block-heads per second and the fp32 arithmetic rate
-of its main products).
+Beside the headline (not part of `value`):
+  configs         every configuration (4k, 16k, the stack, ragged batch 32,
+                  131k batch 8), each in its per-layer and streamed launch,
+                  graph-replayed, cycling over enough cache copies (>= 512 MB
+                  per cycle) that no step finds its data in the 256 MB
+                  Infinity Cache, with its own CPU oracle baseline;
+  read_ceiling    dkv_stream_read_probe over 2 GiB: the box's streaming-read
+                  bandwidth for the loads the streams use;
+  the stack with 8- / 4-bit residual rows (quantised_residuals), read as
+  un-rotated pools (unrotated_pool), with pairs of blocks sharing one basis
+  (shared_basis), and the write side, dkv_seal_blocks sealing one layer's
+  1008 blocks x 2 KV heads at each of the stack's ranks (sealing).
 """
 from __future__ import annotations
 
@@ -44,7 +54,9 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
+import re
 import sys
 import time
 
@@ -54,7 +66,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 METRIC = "decode attention queries/sec + achieved HBM GB/s over compressed KV at 64k ctx"
 D = 128
-
+CACHE_DEFEAT_BYTES = 512 * 10 ** 6   # >= 2 x the 256 MB Infinity Cache per cycle over copies
+MAX_COPIES = 512
 
 RESID_ROW_BYTES = {0: 2 * D, 1: D + 8, 2: D // 2 + 8}   # fp16; 8- / 4-bit codes + fp16 scale, bias per 64
 
@@ -65,14 +78,93 @@ def bytes_per_block(rank: int, n_resid: int, resid_format: int = 0) -> int:
     return 2 * (2 * D + 255 * rank + 2 * rank * D) + 2 * n_resid * RESID_ROW_BYTES[resid_format] + n_resid
 
 
-def layer_bytes(batch, hkv, hq, top_k_eff, rank, n_resid, window, n_blocks, resid_format: int = 0):
-    """Per-layer algorithmic bytes by stage: route keys + q (routing), routed
-    blocks + window + q (attention), output (merge)."""
-    route = batch * hkv * n_blocks * D * 4 + batch * hq * D * 2
-    attend = batch * hkv * (top_k_eff * bytes_per_block(rank, n_resid, resid_format) + 2 * 2 * window * D) \
-        + batch * hq * D * 2
-    merge = batch * hq * (D * 2 + 4) + batch * hkv * top_k_eff * 4
-    return route, attend, merge
+def step_bytes(batch, hq, hkv, top_k, n_blocks, win_len, layers):
+    """Algorithmic bytes of one decode step by part.  n_blocks, win_len: per
+    sequence; layers: (rank, n_resid, resid_format) per layer.  Parts: route
+    (the routing keys, fp32, every block of every unit), blocks (K_eff routed
+    blocks per unit), window (the unit's window rows), q (fp16 queries, once),
+    merge (fp16 outputs, fp32 lse, int32 routed indices)."""
+    nb = [max(0, int(n)) for n in n_blocks]
+    wl = [max(0, int(w)) for w in win_len]
+    out = dict(route=0, blocks=0, window=0, q=0, merge=0)
+    for rank, n_resid, fmt in layers:
+        out["route"] += hkv * sum(nb) * D * 4
+        out["blocks"] += hkv * sum(min(top_k, n) for n in nb) * bytes_per_block(rank, n_resid, fmt)
+        out["window"] += hkv * sum(wl) * 2 * 2 * D
+        out["q"] += batch * hq * D * 2
+        out["merge"] += batch * hq * (D * 2 + 4) + batch * hkv * top_k * 4
+    out["step"] = sum(out.values())
+    out["streams"] = out["blocks"] + out["window"] + out["q"]
+    return out
+
+
+def workload_bytes(wl, layers=None):
+    lays = wl.layers if layers is None else layers
+    return step_bytes(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.top_k, wl.n_blocks,
+                      [min(int(w), wl.window) for w in wl.win_len],
+                      [(l.rank, wl.n_resid, l.resid_format) for l in lays])
+
+
+def stack_bytes(n_layers: int, resid_format: int = 0):
+    """step_bytes of the first n_layers layers of the 64k batch-4 stack."""
+    from compressed_kv_cache_amd import synth
+    return step_bytes(4, 12, 2, 32, [252] * 4, [1024] * 4,
+                      [(synth.STACK_RANKS[i], 128, resid_format) for i in range(n_layers)])
+
+
+def pct(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
+
+
+def source_digest() -> str:
+    """sha256[:16] over every kernel source of the library and its header."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "compressed_kv_cache_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "dkv_attn.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch of `kernel` (read + written, scaled by the
+    copy-kernel calibration) from the committed rocprofv3 PMC summary, or None
+    when the kernel sources changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic_stack64k_b4.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != digest:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:                                   # pragma: no cover
+        return len(os.sched_getaffinity(0))
 
 
 class Hip:
@@ -103,34 +195,161 @@ class Hip:
         self.h.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def source_digest() -> str:
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "compressed_kv_cache_amd", "csrc", "dkv_attn.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+def graph_steps(torch, np, step, n_steps: int, reps: int, warmup: int):
+    """Capture step(i, stream) for i in range(n_steps) as one hipGraph and replay
+    it warmup + reps times; per-step milliseconds of each timed replay."""
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        for i in range(n_steps):
+            step(i, cs)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n_steps):
+            step(i, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for r in range(reps):
+        e0[r].record()
+        g.replay()
+        e1[r].record()
+    torch.cuda.synchronize()
+    return [e0[r].elapsed_time(e1[r]) / n_steps for r in range(reps)], g
 
 
-def measured_traffic(kernel: str, digest: str):
-    """HBM bytes per launch of `kernel` (read + written, scaled by the
-    copy-kernel calibration) from the committed rocprofv3 PMC summary, or None
-    when the kernel source changed since the counters were taken."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic_stack64k_b4.json")
-    try:
-        with open(p) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha256_16") != digest:
-        return None
-    return t.get("bytes_per_launch")
+def measure_ceiling(lib, torch, np, log, n_waves: int = 2048, per_wave: int = 1 << 20, reps: int = 7):
+    """The streams' read ceiling: dkv_stream_read_probe over n_waves x per_wave bytes."""
+    dev = torch.device("cuda:0")
+    n = n_waves * per_wave
+    x = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(n_waves, dtype=torch.int32, device=dev)
+    lib.read_probe(x, n_waves, sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum().item()) == n // 4, "read probe checksum"
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.read_probe(x, n_waves, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    p = pct(ts)
+    gbps = n / (p["median"] * 1e-3) / 1e9
+    log(f"read ceiling: {gbps:.0f} GB/s ({n_waves} one-wave workgroups x {per_wave >> 10} KiB)")
+    del x, sink
+    torch.cuda.empty_cache()
+    return {"GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS, "bytes": n, "ms": p,
+            "method": f"dkv_stream_read_probe: {n_waves} one-wave workgroups each streaming {per_wave >> 10} KiB "
+                      "through a four-page LDS ring with 16-byte buffer loads into LDS (the streams' loads); "
+                      f"median of {reps} launches"}
 
 
-def step_algorithmic_bytes(n_layers: int, resid_format: int = 0) -> int:
-    """Algorithmic bytes of one step over the first n_layers layers of the stack."""
-    from compressed_kv_cache_amd import synth
-    B, Hq, Hkv, K, R, W, N = 4, 12, 2, 32, 128, 1024, 252
-    return sum(sum(layer_bytes(B, Hkv, Hq, min(K, N), synth.STACK_RANKS[i], R, W, N, resid_format))
-               for i in range(n_layers))
+def oracle_sample(wl, b0: int, b1: int):
+    """The oracle's inputs for sequences b0 .. b1 - 1 of a one-layer workload."""
+    lay = wl.layers[0]
+    return (lay.pool(), lay.q[b0:b1], lay.win_k[b0:b1], lay.win_v[b0:b1], wl.block_table[b0:b1],
+            wl.n_blocks[b0:b1], wl.win_len[b0:b1], wl.n_kv_heads, wl.top_k, wl.scale)
+
+
+def cpu_decode_rate(samples, seconds: float, log, what: str):
+    """Queries/s of the fp64 oracle (as it stands) over `samples` ((args,
+    queries) pairs), cycled until about `seconds` of wall time are spent."""
+    import oracle
+    runs, spent, queries = 0, 0.0, 0
+    while spent < seconds or runs == 0:
+        args, nq = samples[runs % len(samples)]
+        t0 = time.perf_counter()
+        oracle.decode(*args)
+        spent += time.perf_counter() - t0
+        runs += 1
+        queries += nq
+    log(f"cpu baseline ({what}): {runs} decodes, {queries} queries in {spent:.1f} s")
+    return queries / spent, runs, spent
+
+
+def measure_config(cfg: int, lib, synth, torch, np, steps: int, warmup: int, cpu_seconds: float, log,
+                   want_cpu: bool):
+    """One single-layer configuration in its per-layer (dkv_decode) and streamed
+    (dkv_decode_layers over the one layer) launch: enough cache copies that a
+    cycle over them moves >= 512 MB, one graph holding one step per copy,
+    replayed `steps` times; per-step median and p10 / p90."""
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = synth.make_config(cfg)
+    by = workload_bytes(wl)
+    copies = max(1, min(MAX_COPIES, math.ceil(CACHE_DEFEAT_BYTES / by["step"])))
+    lay = wl.layers[0]
+    arrays = lay.pool()
+    pools, batches, runs = [], [], []
+    for c in range(copies):
+        p = lib.Pool.from_numpy(arrays, dev)
+        b = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks, wl.win_len, device=dev)
+        lib.route_keys(p)
+        lib.gather_route_keys(p, b)
+        pools.append(p)
+        batches.append(b)
+    torch.cuda.synchronize()
+    log(f"{wl.name}: {copies} cache copies of {by['step'] / 1e6:.2f} MB per step "
+        f"({time.perf_counter() - t0:.0f} s to build)")
+    queries = wl.batch * wl.n_q_heads
+    ws = lib.alloc_workspace(pools[0], batches[0], wl.top_k)
+    out = torch.empty((wl.batch, wl.n_q_heads, D), dtype=torch.float16, device=dev)
+    lse = torch.empty((wl.batch, wl.n_q_heads), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.batch, wl.n_kv_heads, wl.top_k), dtype=torch.int32, device=dev)
+
+    def per_layer(i, st):
+        c = i % copies
+        lib.decode(pools[c], batches[c], wl.top_k, wl.scale, workspace=ws, out=out, out_lse=lse, out_idx=idx,
+                   stream=st)
+    per_layer(0, None)
+    torch.cuda.synchronize()
+    ref_out, ref_idx = out.clone(), idx.clone()
+    layers = [lib.Layers([pools[c]], [batches[c]], wl.top_k, wl.scale) for c in range(copies)]
+    layers[0].run()
+    torch.cuda.synchronize()
+    assert torch.equal(layers[0].idxs[0], ref_idx), f"{wl.name}: streamed step routes differently"
+    d_out = (layers[0].outs[0].float() - ref_out.float()).abs().max().item()
+    assert d_out <= 2e-3, f"{wl.name}: streamed and per-layer outputs differ by {d_out:.2e}"
+
+    def streamed(i, st):
+        layers[i % copies].run(st)
+    modes = {}
+    for name, fn in (("per_layer_hipgraph", per_layer), ("layer_batched_hipgraph", streamed)):
+        ms, g = graph_steps(torch, np, fn, copies, max(steps, 10), warmup)
+        del g
+        p = pct(ms)
+        modes[name] = {"ms_per_step": p, "queries_per_s": queries / (p["median"] * 1e-3),
+                       "GBps": by["step"] / (p["median"] * 1e-3) / 1e9,
+                       "hbm_frac": by["step"] / (p["median"] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"{wl.name} {name}: {p['median'] * 1e3:.1f} us/step (p10 {p['p10'] * 1e3:.1f}, p90 {p['p90'] * 1e3:.1f}), "
+            f"{modes[name]['GBps']:.0f} GB/s")
+    best = min(modes, key=lambda k: modes[k]["ms_per_step"]["median"])
+    plan = layers[0].plan
+    entry = {"config": wl.name, "queries_per_step": queries, "algorithmic_bytes_per_step": by["step"],
+             "bytes_by_part": {k: by[k] for k in ("route", "blocks", "window", "q", "merge")},
+             "cache_copies": copies, "streamed": bool(plan.stream), "modes": modes, "best_mode": best,
+             "queries_per_s": modes[best]["queries_per_s"], "GBps": modes[best]["GBps"],
+             "hbm_frac": modes[best]["hbm_frac"]}
+    del layers, pools, batches, ws
+    torch.cuda.empty_cache()
+    if want_cpu:
+        # a bounded sample: whole batch for the small configs, a slice for the large ones
+        nb = {0: wl.batch, 1: wl.batch, 3: 2, 4: 1}[cfg]
+        samples = [(oracle_sample(wl, b, b + nb), nb * wl.n_q_heads) for b in range(0, wl.batch, nb)][:4]
+        qps, runs, spent = cpu_decode_rate(samples, cpu_seconds, log, wl.name)
+        entry["cpu_baseline"] = {"value": qps, "unit": "queries/s", "cores": oracle_threads(),
+                                 "cpu_model": cpu_model(), "kind": "oracle",
+                                 "sample": f"{runs} oracle decodes of {nb} sequence(s) each ({spent:.1f} s)"}
+    del wl
+    return entry
 
 
 def seal_flops(width: int, rank: int, power_iters: int, passes: int = 2) -> int:
@@ -219,75 +438,6 @@ def measure_joins(lib, synth, torch, np, log, repeats: int = 3):
     return {"rank": wl.layers[0].rank, "block_heads": items, "ms": ms, "block_heads_per_s": items / (ms * 1e-3)}
 
 
-def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
-    """The same 64k batch-4 stack with its residual rows stored in the 8- or
-    4-bit group-quantised format (variant "Q8" / "Q4"), or read as un-rotated
-    pools whose keys are rotated to their positions at read (variant "U"): one
-    layer-batched launch per step, timed eagerly with events and as a graph
-    replay."""
-    dev = torch.device("cuda:0")
-    pools, batches = [], []
-    for li in range(n_layers):
-        wl = synth.make_config(2, layers=[li], variant=variant)
-        lay = wl.layers[0]
-        pool = lib.Pool.from_numpy(lay.pool(), dev)
-        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
-                                     wl.win_len, device=dev)
-        lib.route_keys(pool)
-        lib.gather_route_keys(pool, batch)
-        pools.append(pool)
-        batches.append(batch)
-        del wl, lay
-    run = lib.Layers(pools, batches, 32, float(1.0 / np.sqrt(D)))
-    for _ in range(warmup):
-        run.run()
-    torch.cuda.synchronize()
-    ref = [o.clone() for o in run.outs]
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda._sleep(int(2e-3 * 2.4e9))
-    for s in range(steps):
-        e0[s].record()
-        run.run()
-        e1[s].record()
-    torch.cuda.synchronize()
-    kern = float(np.mean([e0[s].elapsed_time(e1[s]) for s in range(steps)]))
-    assert run.timeout_flag() == 0 and all(torch.equal(a, b) for a, b in zip(ref, run.outs))
-    g = torch.cuda.CUDAGraph()
-    cs = torch.cuda.Stream()
-    cs.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cs):
-        run.run(cs)
-    torch.cuda.current_stream().wait_stream(cs)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        run.run(torch.cuda.current_stream())
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
-    fmt = {"Q8": 1, "Q4": 2, "U": 0, "UB": 0}[variant]
-    alg = step_algorithmic_bytes(n_layers, fmt)
-    log(f"{variant} variant, layer-batched: {ms:.4f} ms/step (graph); kernel {kern * 1e3:.1f} us; "
-        f"{alg / 1e6:.1f} MB per step")
-    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16", "UB": "fp16"}[variant],
-           "keys": "unrotated, rotated at read" if variant in ("U", "UB") else "rotated",
-           "shared_basis": "pairs of consecutive blocks" if variant == "UB" else None, "ms_per_step": ms,
-           "queries_per_s": 4 * n_layers / (ms * 1e-3), "algorithmic_bytes_per_step": alg,
-           "kernel_us_per_launch": kern * 1e3, "achieved_GBps": alg / (kern * 1e-3) / 1e9}
-    del run, pools, batches
-    torch.cuda.empty_cache()
-    return res
-
-
 def pmc_summary(args) -> int:
     """Per-launch HBM traffic of one kernel from two rocprofv3 --pmc runs of
     this benchmark (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each
@@ -318,8 +468,8 @@ def pmc_summary(args) -> int:
                                ("write", args.pmc_summary[1], "WRITE_SIZE")):
         vals, names = per_dispatch(path, counter)
         probe = [v for d, v in vals.items() if "MulFunctor" in names[d]]  # the torch.mul copy probe only
-        kern = [v for d, v in vals.items() if args.pmc_kernel + "<" in names[d] or
-                names[d].split("(")[0].endswith(args.pmc_kernel)]
+        pat = re.compile(r"(^|[\s:])" + re.escape(args.pmc_kernel) + r"[(<]")
+        kern = [v for d, v in vals.items() if pat.search(names[d])]
         if not probe or not kern:
             print(f"{path}: no copy-probe or {args.pmc_kernel} dispatches", file=sys.stderr)
             return 2
@@ -328,7 +478,8 @@ def pmc_summary(args) -> int:
         out[key] = {"counter": counter, "probe_KiB": probe_kib, "scale": scale, "dispatches": len(kern),
                     "bytes_per_launch": sum(kern) / len(kern) * 1024.0 * scale}
     n_layers = max(1, min(28, args.layers))
-    alg = step_algorithmic_bytes(n_layers)
+    sb = stack_bytes(n_layers)
+    alg = sb["streams"] if args.pmc_kernel == "k_blocks" else sb["step"]
     if args.pmc_kernel == "k_decode":
         alg /= n_layers
     total = out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"]
@@ -369,37 +520,59 @@ def pmc_summary(args) -> int:
     return 0
 
 
-CPU_SAMPLE_LAYERS = (0, 9, 19, 27)      # one layer of each rank (24, 48, 16) and the last
-
-
-def cpu_baseline(sample: dict, seconds: float, log):
-    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
-    decode steps of the sample layers (all 4 sequences each), cycled until about
-    `seconds` of CPU time are spent.  sample: {layer index: Workload}."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:                                   # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    runs, spent = 0, 0.0
-    keys = sorted(sample)
-    while spent < seconds:
-        li = keys[runs % len(keys)]
-        wl = sample[li]
+def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: int, warmup: int, log):
+    """The same 64k batch-4 stack with its residual rows stored in the 8- or
+    4-bit group-quantised format (variant "Q8" / "Q4"), or read as un-rotated
+    pools whose keys are rotated to their positions at read (variant "U"), or
+    those with pairs of blocks sharing one basis ("UB"): one layer-batched step
+    per step, timed eagerly with events and as a graph replay."""
+    dev = torch.device("cuda:0")
+    pools, batches = [], []
+    for li in range(n_layers):
+        wl = synth.make_config(2, layers=[li], variant=variant)
         lay = wl.layers[0]
-        t0 = time.perf_counter()
-        oracle.decode(lay.pool(), lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
-                      wl.win_len, wl.n_kv_heads, wl.top_k, wl.scale)
-        spent += time.perf_counter() - t0
-        runs += 1
-        if runs % len(keys) == 0:
-            log(f"cpu baseline: {runs} layer decodes, {spent:.1f} s")
-    queries = runs * 4
-    return {"value": queries / spent, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} one-layer decode steps (4 sequences each) cycling over layers "
-                      f"{list(keys)} of the stack: routing over all 252 blocks, explicit "
-                      f"decompression of the 32 routed blocks and dense fp64 softmax; {spent:.1f} s"}
+        pool = lib.Pool.from_numpy(lay.pool(), dev)
+        batch = lib.Batch.from_numpy(lay.q, lay.win_k, lay.win_v, wl.block_table, wl.n_blocks,
+                                     wl.win_len, device=dev)
+        lib.route_keys(pool)
+        lib.gather_route_keys(pool, batch)
+        pools.append(pool)
+        batches.append(batch)
+        del wl, lay
+    run = lib.Layers(pools, batches, 32, float(1.0 / np.sqrt(D)))
+    for _ in range(warmup):
+        run.run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in run.outs]
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda._sleep(int(2e-3 * 2.4e9))
+    for s in range(steps):
+        e0[s].record()
+        run.run()
+        e1[s].record()
+    torch.cuda.synchronize()
+    eager = pct([e0[s].elapsed_time(e1[s]) for s in range(steps)])
+    assert run.timeout_flag() == 0 and all(torch.equal(a, b) for a, b in zip(ref, run.outs))
+    ms, g = graph_steps(torch, np, lambda i, st: run.run(st), 1, steps, warmup)
+    assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
+    p = pct(ms)
+    fmt = {"Q8": 1, "Q4": 2, "U": 0, "UB": 0}[variant]
+    alg = stack_bytes(n_layers, fmt)["step"]
+    log(f"{variant} variant, layer-batched: {p['median']:.4f} ms/step (graph); eager {eager['median'] * 1e3:.1f} us; "
+        f"{alg / 1e6:.1f} MB per step; streamed {bool(run.plan.stream)}")
+    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16", "UB": "fp16"}[variant],
+           "keys": "unrotated, rotated at read" if variant in ("U", "UB") else "rotated",
+           "shared_basis": "pairs of consecutive blocks" if variant == "UB" else None,
+           "streamed": bool(run.plan.stream), "ms_per_step": p["median"], "ms_per_step_pct": p,
+           "queries_per_s": 4 * n_layers / (p["median"] * 1e-3), "algorithmic_bytes_per_step": alg,
+           "eager_us_per_step": eager["median"] * 1e3, "achieved_GBps": alg / (p["median"] * 1e-3) / 1e9}
+    del run, pools, batches, g
+    torch.cuda.empty_cache()
+    return res
+
+
+CPU_SAMPLE_LAYERS = (0, 9, 19, 27)      # one layer of each rank (24, 48, 16) and the last
 
 
 def main() -> int:
@@ -409,21 +582,26 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=28, help="layers of the stack to use (default all 28)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="CPU oracle time per configuration of the configs list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--configs", default="0,1,3,4",
+                    help="configurations measured beside the stack (comma list of 0,1,3,4; '' for none)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--no-unrotated", action="store_true",
                     help="skip the stack read as un-rotated pools (keys rotated at read)")
     ap.add_argument("--no-sealing", action="store_true",
                     help="skip the block-sealing measurement (dkv_seal_blocks, reported beside the decode)")
     ap.add_argument("--quantised", choices=("none", "int8", "int4", "both"), default="both",
                     help="also time the stack with its residual rows in the 8- / 4-bit format "
-                         "(layer-batched launch; reported beside the fp16 value)")
+                         "(layer-batched step; reported beside the fp16 value)")
     ap.add_argument("--mode", choices=("all", "per-layer", "layer-batched"), default="all",
-                    help="which launch modes to time (default: all)")
+                    help="which launch modes of the stack to time (default: all)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this benchmark "
                          "into profiles/<kernel>_traffic_stack64k_b4.{json,md} and exit")
-    ap.add_argument("--pmc-kernel", default="k_decode_layers", help="kernel the PMC summary is for")
+    ap.add_argument("--pmc-kernel", default="k_blocks", help="kernel the PMC summary is for")
     ap.add_argument("--pmc-command", default="", help="the rocprofv3 command lines, recorded in the summary")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this size (PMC scaling reference)")
@@ -463,6 +641,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy probe: {n * 4} bytes read and {n * 4} bytes written per dispatch")
         del a, b
+
+    ceiling = None if args.no_ceiling else measure_ceiling(lib, torch, np, log)
 
     hip = Hip()
     n_layers = max(1, min(28, args.layers))
@@ -504,30 +684,24 @@ def main() -> int:
     log(f"resident cache {resident / 1e9:.2f} GB in {time.perf_counter() - t0:.0f} s")
 
     B, Hq, Hkv, K, R, W, N = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.top_k, wl.n_resid, wl.window, 252
-    ranks = [synth.STACK_RANKS[i] for i in layer_ids]
-    per_layer = [layer_bytes(B, Hkv, Hq, min(K, N), r, R, W, N) for r in ranks]
-    step_route = sum(x[0] for x in per_layer)
-    step_attend = sum(x[1] for x in per_layer)
-    step_merge = sum(x[2] for x in per_layer)
-    step_bytes = step_route + step_attend + step_merge
+    by = stack_bytes(n_layers)
     queries_per_step = B * n_layers
 
-    def step_eager():
+    def step_eager(stream=None):
         for i in range(n_layers):
             lib.decode(pools[i], batches[i], K, wl.scale, workspace=wss[i], out=outs[i],
-                       out_lse=lses[i], out_idx=idxs[i])
+                       out_lse=lses[i], out_idx=idxs[i], stream=stream)
 
     per_layer_modes = args.mode in ("all", "per-layer")
-    # ---- eager, with hipEvents around every layer's decode kernel, in the timed steps
+    hold = int(2e-3 * 2.4e9)                              # ~2 ms of shader clock
+    # ---- per-layer: eager, with hipEvents around every layer's decode kernel
     for _ in range(args.warmup if per_layer_modes else 1):
         step_eager()
     torch.cuda.synchronize()
     ref_out = [o.clone() for o in outs]
     ref_lse = [x.clone() for x in lses]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    ms_eager = kernel_ms = None
-    hold = int(2e-3 * 2.4e9)                              # ~2 ms of shader clock
+    modes, kern_by_mode = {}, {}
+    kernel_ms = None
     if per_layer_modes:
         ev = [[[hip.event() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
         s_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -544,128 +718,86 @@ def main() -> int:
                                     ev[s][i], out_idx=idxs[i])
             s_end[s].record()
         torch.cuda.synchronize()
-        ms_eager = float(np.mean([s_start[s].elapsed_time(s_end[s]) for s in range(args.steps)]))
-        kern = np.array([[hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for i in range(n_layers)]
-                         for s in range(args.steps)])
-        kernel_ms = float(kern.mean())
+        modes["per_layer_eager"] = pct([s_start[s].elapsed_time(s_end[s]) for s in range(args.steps)])
+        kern = [hip.elapsed_ms(ev[s][i][0], ev[s][i][1]) for s in range(args.steps) for i in range(n_layers)]
+        kernel_ms = pct(kern)
         for s in ev:
             for e2 in s:
                 for e in e2:
                     hip.destroy(e)
-        log(f"eager: {ms_eager:.4f} ms/step; decode kernel {kernel_ms * 1e3:.2f} us per layer "
-            f"(p10 {np.percentile(kern, 10) * 1e3:.2f}, p90 {np.percentile(kern, 90) * 1e3:.2f})")
+        log(f"per-layer eager: {modes['per_layer_eager']['median']:.4f} ms/step; k_decode "
+            f"{kernel_ms['median'] * 1e3:.2f} us per layer (p10 {kernel_ms['p10'] * 1e3:.2f}, "
+            f"p90 {kernel_ms['p90'] * 1e3:.2f})")
         for i in range(n_layers):
             assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
                 "eager steps are not bit-identical"
-
-    # ---- the same step captured once as a hipGraph
-    ms_graph = None
-    if per_layer_modes and not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cs):
-            step_eager()
-        torch.cuda.current_stream().wait_stream(cs)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            step_eager()
-        torch.cuda.synchronize()
-        for rep in range(3):                              # every replay equals eager
-            for o in outs:
-                o.zero_()
-            g.replay()
-            torch.cuda.synchronize()
+        if not args.no_graph:
+            ms, g = graph_steps(torch, np, lambda i, st: step_eager(st), 1, args.steps, args.warmup)
             for i in range(n_layers):
                 assert torch.equal(outs[i], ref_out[i]) and torch.equal(lses[i], ref_lse[i]), \
-                    f"graph replay {rep} differs from eager"
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t_start.record()
-        for _ in range(args.steps):
-            g.replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        ms_graph = t_start.elapsed_time(t_end) / args.steps
-        log(f"hipGraph: {ms_graph:.4f} ms/step")
+                    "graph replays differ from eager"
+            del g
+            modes["per_layer_hipgraph"] = pct(ms)
+            log(f"per-layer hipGraph: {modes['per_layer_hipgraph']['median']:.4f} ms/step")
 
-    # ---- every layer's decode step in ONE layer-batched launch (k_decode_layers)
-    ms_lb = ms_lb_graph = lb_kernel_ms = None
+    # ---- every layer's decode step at once (dkv_decode_layers)
+    lb_parts = None
+    streamed = False
     if args.mode in ("all", "layer-batched"):
         run = lib.Layers(pools, batches, K, wl.scale)
+        streamed = bool(run.plan.stream)
         for _ in range(args.warmup):
             run.run()
         torch.cuda.synchronize()
         # the same routing; outputs equal the per-layer ones up to the rounding of
-        # another split of the rows (the window has parts of its own here)
+        # another split of the rows into partials
         for i in range(n_layers):
             assert torch.equal(run.idxs[i], idxs[i]), f"layer-batched layer {i} routes differently"
             d_out = (run.outs[i].float() - ref_out[i].float()).abs().max().item()
             d_lse = (run.lses[i] - ref_lse[i]).abs().max().item()
             assert d_out <= 2e-3 and d_lse <= 1e-4, f"layer-batched layer {i}: {d_out:.2e} {d_lse:.2e}"
         lb_ref = [o.clone() for o in run.outs]
-        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev = [[hip.event() for _ in range(4)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         torch.cuda._sleep(hold)
         for s in range(args.steps):
-            e0[s].record()
-            run.run()
-            e1[s].record()
+            run.run_profiled(ev[s])
         torch.cuda.synchronize()
-        lb = np.array([e0[s].elapsed_time(e1[s]) for s in range(args.steps)])
-        lb_kernel_ms = float(lb.mean())
-        ms_lb = float(e0[0].elapsed_time(e1[-1])) / args.steps
-        log(f"layer-batched: {ms_lb:.4f} ms/step; k_decode_layers {lb_kernel_ms * 1e3:.2f} us per launch "
-            f"(p10 {np.percentile(lb, 10) * 1e3:.2f}, p90 {np.percentile(lb, 90) * 1e3:.2f})")
-        assert run.timeout_flag() == 0, "a wait in k_decode_layers timed out"
+        steps_ms = [hip.elapsed_ms(ev[s][0], ev[s][3]) for s in range(args.steps)]
+        part = [[hip.elapsed_ms(ev[s][k], ev[s][k + 1]) for s in range(args.steps)] for k in range(3)]
+        for s in ev:
+            for e in s:
+                hip.destroy(e)
+        modes["layer_batched_eager"] = pct(steps_ms)
+        lb_parts = {"routes": pct(part[0]), "streams": pct(part[1]), "merges": pct(part[2])}
+        log(f"layer-batched eager: {modes['layer_batched_eager']['median']:.4f} ms/step; routings "
+            f"{lb_parts['routes']['median'] * 1e3:.1f} us, streams {lb_parts['streams']['median'] * 1e3:.1f} us "
+            f"(p10 {lb_parts['streams']['p10'] * 1e3:.1f}, p90 {lb_parts['streams']['p90'] * 1e3:.1f}), "
+            f"merges {lb_parts['merges']['median'] * 1e3:.1f} us")
+        assert run.timeout_flag() == 0, "a wait in the layer-batched step timed out"
         for i in range(n_layers):
             assert torch.equal(run.outs[i], lb_ref[i]), "layer-batched steps are not bit-identical"
         if not args.no_graph:
-            g2 = torch.cuda.CUDAGraph()
-            cs = torch.cuda.Stream()
-            cs.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cs):
-                run.run(cs)
-            torch.cuda.current_stream().wait_stream(cs)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g2):
-                run.run(torch.cuda.current_stream())
-            torch.cuda.synchronize()
-            for rep in range(3):
-                for o in run.outs:
-                    o.zero_()
-                g2.replay()
-                torch.cuda.synchronize()
-                for i in range(n_layers):
-                    assert torch.equal(run.outs[i], lb_ref[i]), f"layer-batched replay {rep} differs"
-            for _ in range(args.warmup):
-                g2.replay()
-            torch.cuda.synchronize()
-            t_start.record()
-            for _ in range(args.steps):
-                g2.replay()
-            t_end.record()
-            torch.cuda.synchronize()
-            ms_lb_graph = t_start.elapsed_time(t_end) / args.steps
-            log(f"layer-batched hipGraph: {ms_lb_graph:.4f} ms/step")
+            ms, g = graph_steps(torch, np, lambda i, st: run.run(st), 1, args.steps, args.warmup)
+            for i in range(n_layers):
+                assert torch.equal(run.outs[i], lb_ref[i]), "layer-batched graph replays differ"
+            del g
+            modes["layer_batched_hipgraph"] = pct(ms)
+            log(f"layer-batched hipGraph: {modes['layer_batched_hipgraph']['median']:.4f} ms/step")
+        del run
 
-    modes = {"per_layer_eager": ms_eager, "per_layer_hipgraph": ms_graph,
-             "layer_batched_eager": ms_lb, "layer_batched_hipgraph": ms_lb_graph}
-    mode = min((k for k in modes if modes[k] is not None), key=lambda k: modes[k])
-    best_ms = modes[mode]
+    mode = min(modes, key=lambda k: modes[k]["median"])
+    best_ms = modes[mode]["median"]
     qps = queries_per_step / (best_ms * 1e-3)
-    gbps = step_bytes / (best_ms * 1e-3) / 1e9
+    gbps = by["step"] / (best_ms * 1e-3) / 1e9
     digest = source_digest()
-    if mode.startswith("layer_batched"):
-        # one k_decode_layers launch processes the whole step
-        kernel_name, launch_bytes, kern_ms = "k_decode_layers", step_bytes, lb_kernel_ms
+    if mode.startswith("layer_batched") and streamed:
+        kernel_name, launch_bytes, kern = "k_blocks", by["streams"], lb_parts["streams"]
+    elif mode.startswith("layer_batched"):
+        kernel_name, launch_bytes, kern = "k_decode_layers", by["step"], modes["layer_batched_eager"]
     else:
-        # one k_decode launch per layer; duration from the events around every
-        # decode kernel in the timed eager steps (kernels back to back, as in a replay)
-        kernel_name, launch_bytes, kern_ms = "k_decode", step_bytes / n_layers, kernel_ms
-    kernel_gbps = launch_bytes / (kern_ms * 1e-3) / 1e9
+        kernel_name, launch_bytes, kern = "k_decode", by["step"] / n_layers, kernel_ms
+    kernel_gbps = launch_bytes / (kern["mean"] * 1e-3) / 1e9
     traffic = measured_traffic(kernel_name, digest)
 
     res = {
@@ -686,23 +818,70 @@ def main() -> int:
                    "batch": B, "layers": n_layers, "context": 65536, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "window": W, "blocks_per_seq": N, "block_size": 256, "top_k": K,
                    "resid_rows": R, "ranks": "24 (layers 0-8), 48 (9-18), 16 (19-27)",
-                   "timed_mode": mode, "accumulate": "f32"},
+                   "timed_mode": mode, "accumulate": "f32",
+                   "timed_mode_needs": ("all layers' queries at once (independent layers: micro-batches "
+                                        "in flight at different layers)") if mode.startswith("layer_batched")
+                   else "one layer at a time (one token's decode)"},
         "achieved_GBps": gbps,
         "hbm_frac": gbps / HBM_PEAK_GBPS,
-        "algorithmic_bytes_per_step": step_bytes,
+        "algorithmic_bytes_per_step": by["step"],
+        "bytes_by_part": {k: by[k] for k in ("route", "blocks", "window", "q", "merge")},
         "queries_per_step": queries_per_step,
-        "ms_per_step_by_mode": modes,
-        "k_decode_us_per_layer": None if kernel_ms is None else kernel_ms * 1e3,
-        "k_decode_layers_us_per_launch": None if lb_kernel_ms is None else lb_kernel_ms * 1e3,
+        "ms_per_step_by_mode": {k: v["median"] for k, v in modes.items()},
+        "ms_per_step_pct_by_mode": modes,
+        "per_layer_schedule": None if "per_layer_hipgraph" not in modes else {
+            "ms_per_step": modes["per_layer_hipgraph"]["median"],
+            "queries_per_s": queries_per_step / (modes["per_layer_hipgraph"]["median"] * 1e-3),
+            "GBps": by["step"] / (modes["per_layer_hipgraph"]["median"] * 1e-3) / 1e9,
+            "k_decode_us_per_layer": kernel_ms["median"] * 1e3},
+        "layer_batched_us_by_launch": None if lb_parts is None else
+        {k: {q: v[q] * 1e3 for q in ("median", "p10", "p90")} for k, v in lb_parts.items()},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kernel_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kernel_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": launch_bytes,
-                     "avg_launch_us": kern_ms * 1e3},
+                     "avg_launch_us": kern["mean"] * 1e3, "median_launch_us": kern["median"] * 1e3},
+        "read_ceiling": ceiling,
         "resident_cache_GB": resident / 1e9,
         "kernel_source_sha256_16": digest,
     }
+    if not args.no_cpu_baseline:
+        samples = [((lay.pool(), lay.q, lay.win_k, lay.win_v, w.block_table, w.n_blocks, w.win_len,
+                     w.n_kv_heads, w.top_k, w.scale), w.batch * w.n_q_heads)
+                   for w in [cpu_sample[k] for k in sorted(cpu_sample)] for lay in [w.layers[0]]] or \
+            [((meta.layers[0].pool(), meta.layers[0].q, meta.layers[0].win_k, meta.layers[0].win_v, meta.block_table,
+               meta.n_blocks, meta.win_len, meta.n_kv_heads, meta.top_k, meta.scale), meta.batch * meta.n_q_heads)]
+        cqps, runs, spent = cpu_decode_rate(samples, args.cpu_seconds, log, "stack")
+        res["cpu_baseline"] = {"value": cqps, "unit": "queries/s", "cores": oracle_threads(),
+                               "cpu_model": cpu_model(), "kind": "oracle",
+                               "sample": f"{runs} one-layer decode steps of all 4 sequences (48 queries each), "
+                                         f"cycling over layers {sorted(cpu_sample)} of the stack: routing over "
+                                         f"all 252 blocks, explicit decompression of the 32 routed blocks and "
+                                         f"dense fp64 softmax; {spent:.1f} s"}
+    del pools, batches, wss, outs, lses, idxs, cpu_sample, meta, wl
+    torch.cuda.empty_cache()
+
+    # ---- every configuration
+    cfgs = [int(c) for c in args.configs.split(",") if c.strip()]
+    entries = []
+    for cfg in cfgs:
+        if cfg == 2:
+            continue
+        entries.append(measure_config(cfg, lib, synth, torch, np, args.steps, args.warmup, args.config_cpu_seconds,
+                                      log, not args.no_cpu_baseline))
+    # the stack itself, from the headline's numbers (its 4.5 GB are far beyond the Infinity Cache)
+    stack_entry = {"config": res["config"]["workload"], "queries_per_step": queries_per_step,
+                   "algorithmic_bytes_per_step": by["step"], "cache_copies": 1,
+                   "streamed": streamed, "best_mode": mode, "queries_per_s": qps, "GBps": gbps,
+                   "hbm_frac": gbps / HBM_PEAK_GBPS,
+                   "modes": {k: {"ms_per_step": v, "queries_per_s": queries_per_step / (v["median"] * 1e-3),
+                                 "GBps": by["step"] / (v["median"] * 1e-3) / 1e9}
+                             for k, v in modes.items()}}
+    if "cpu_baseline" in res:
+        stack_entry["cpu_baseline"] = res["cpu_baseline"]
+    entries.insert(min(2, len(entries)), stack_entry)
+    res["configs"] = entries
+
     if args.quantised != "none" and args.mode != "per-layer":
-        # free the fp16 stack first: the quantised stacks are built the same way
         variants = {"int8": ["Q8"], "int4": ["Q4"], "both": ["Q8", "Q4"]}[args.quantised]
         res["quantised_residuals"] = [measure_variant(lib, synth, torch, np, v, n_layers, args.steps,
                                                       args.warmup, log) for v in variants]
@@ -713,8 +892,6 @@ def main() -> int:
         res["shared_basis"]["joins"] = measure_joins(lib, synth, torch, np, log)
     if not args.no_sealing and args.mode != "per-layer":
         res["sealing"] = measure_sealing(lib, synth, torch, np, log)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cpu_sample or {layer_ids[0]: meta}, args.cpu_seconds, log)
     print(json.dumps(res))
     return 0
 
