@@ -44,8 +44,8 @@ Beside the headline (not part of `value`):
   read_ceiling    dkv_stream_read_probe over 2 GiB: the box's streaming-read
                   bandwidth for the loads the streams use;
   the stack with 8- / 4-bit residual rows (quantised_residuals), read as
-  un-rotated pools (unrotated_pool), with pairs of blocks sharing one basis
-  (shared_basis), and the write side, dkv_seal_blocks sealing one layer's
+  un-rotated pools (unrotated_pool), with pairs of blocks sharing one basis in
+  a compact basis store (shared_basis, with its resident bytes), and the write side, dkv_seal_blocks sealing one layer's
   1008 blocks x 2 KV heads at each of the stack's ranks (sealing).
 """
 from __future__ import annotations
@@ -524,7 +524,8 @@ def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: i
     """The same 64k batch-4 stack with its residual rows stored in the 8- or
     4-bit group-quantised format (variant "Q8" / "Q4"), or read as un-rotated
     pools whose keys are rotated to their positions at read (variant "U"), or
-    those with pairs of blocks sharing one basis ("UB"): one layer-batched step
+    those with pairs of blocks sharing one basis in a compact basis store
+    ("UC2"): one layer-batched step
     per step, timed eagerly with events and as a graph replay."""
     dev = torch.device("cuda:0")
     pools, batches = [], []
@@ -539,6 +540,13 @@ def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: i
         pools.append(pool)
         batches.append(batch)
         del wl, lay
+    pool_bytes = {}
+    for p_ in pools:
+        for t in p_.tensors.values():
+            if t is not None:
+                st = t.untyped_storage()
+                pool_bytes[st.data_ptr()] = st.nbytes()
+    resident_pool = sum(pool_bytes.values())
     run = lib.Layers(pools, batches, 32, float(1.0 / np.sqrt(D)))
     for _ in range(warmup):
         run.run()
@@ -557,13 +565,15 @@ def measure_variant(lib, synth, torch, np, variant: str, n_layers: int, steps: i
     ms, g = graph_steps(torch, np, lambda i, st: run.run(st), 1, steps, warmup)
     assert all(torch.equal(a, b) for a, b in zip(ref, run.outs))
     p = pct(ms)
-    fmt = {"Q8": 1, "Q4": 2, "U": 0, "UB": 0}[variant]
+    fmt = {"Q8": 1, "Q4": 2, "U": 0, "UC2": 0}[variant]
     alg = stack_bytes(n_layers, fmt)["step"]
     log(f"{variant} variant, layer-batched: {p['median']:.4f} ms/step (graph); eager {eager['median'] * 1e3:.1f} us; "
         f"{alg / 1e6:.1f} MB per step; streamed {bool(run.plan.stream)}")
-    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16", "UB": "fp16"}[variant],
-           "keys": "unrotated, rotated at read" if variant in ("U", "UB") else "rotated",
-           "shared_basis": "pairs of consecutive blocks" if variant == "UB" else None,
+    res = {"resid_format": {"Q8": "int8", "Q4": "int4", "U": "fp16", "UC2": "fp16"}[variant],
+           "keys": "unrotated, rotated at read" if variant in ("U", "UC2") else "rotated",
+           "shared_basis": ("pairs of consecutive blocks, a compact basis store of about n_slots / 2 entries"
+                            if variant == "UC2" else None),
+           "resident_pool_bytes": resident_pool,
            "streamed": bool(run.plan.stream), "ms_per_step": p["median"], "ms_per_step_pct": p,
            "queries_per_s": 4 * n_layers / (p["median"] * 1e-3), "algorithmic_bytes_per_step": alg,
            "eager_us_per_step": eager["median"] * 1e3, "achieved_GBps": alg / (p["median"] * 1e-3) / 1e9}
@@ -888,7 +898,9 @@ def main() -> int:
     if not args.no_unrotated and args.mode != "per-layer":
         res["unrotated_pool"] = measure_variant(lib, synth, torch, np, "U", n_layers, args.steps, args.warmup,
                                                 log)
-        res["shared_basis"] = measure_variant(lib, synth, torch, np, "UB", n_layers, args.steps, args.warmup, log)
+        res["shared_basis"] = measure_variant(lib, synth, torch, np, "UC2", n_layers, args.steps, args.warmup,
+                                              log)
+        res["shared_basis"]["resident_pool_bytes_unshared"] = res["unrotated_pool"]["resident_pool_bytes"]
         res["shared_basis"]["joins"] = measure_joins(lib, synth, torch, np, log)
     if not args.no_sealing and args.mode != "per-layer":
         res["sealing"] = measure_sealing(lib, synth, torch, np, log)

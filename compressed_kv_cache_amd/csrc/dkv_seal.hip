@@ -32,6 +32,8 @@
 
 #include "dkv_attn.h"
 
+#include <vector>
+
 __attribute__((visibility("hidden"))) dkv_status dkv_fail_message(dkv_status s, const char* msg);
 __attribute__((visibility("hidden"))) void dkv_clear_error_message();
 
@@ -773,6 +775,19 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
   return DKV_OK;
 }
 
+static dkv_status launch_join(const JoinArgs& a, int64_t grid, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_join, hipFuncAttributeMaxDynamicSharedMemorySize, kJoinLds) != hipSuccess)
+      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_join) failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_join, dim3((unsigned)grid), dim3(kJoinThreads), kJoinLds, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_join launch failed: %s", hipGetErrorString(e));
+  return DKV_OK;
+}
+
 dkv_status dkv_join_basis(const dkv_pool* pool, const int32_t* slots, const int32_t* entries, int32_t n,
                           int32_t write, float* energy, void* stream) {
   dkv_clear_error_message();
@@ -807,16 +822,138 @@ dkv_status dkv_join_basis(const dkv_pool* pool, const int32_t* slots, const int3
   a.rank = P->rank;
   a.write = write ? 1 : 0;
   a.energy = energy;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_join, hipFuncAttributeMaxDynamicSharedMemorySize, kJoinLds) != hipSuccess)
-      return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_join) failed");
-    attr_set = true;
+  return launch_join(a, grid, (hipStream_t)stream);
+}
+
+/* Shared bases under a budget: see dkv_attn.h.  Host-driven: block i is
+ * scored against every entry open so far with k_join (write = 0), the energies
+ * come back to the host, the rule picks, and a join writes U' with k_join
+ * (write = 1); at the end the openers' bases are copied into the store. */
+dkv_status dkv_share_bases(const dkv_pool* pool, const int32_t* slots, int32_t n, int32_t capacity, float threshold,
+                           dkv_view store_vk, dkv_view store_vv, int32_t* entry, int32_t* opener, float* energy,
+                           int32_t* kind, int32_t* n_entries, void* stream) {
+  dkv_clear_error_message();
+  const dkv_pool* P = pool;
+  if (!P) return fail(DKV_ERR_INVALID_ARG, "pool is NULL");
+  if (P->head_dim != DKV_HEAD_DIM) return fail(DKV_ERR_UNSUPPORTED, "head_dim %d != 128", P->head_dim);
+  if (P->rank < 1) return fail(DKV_ERR_INVALID_ARG, "rank %d < 1", P->rank);
+  if (P->rank > DKV_MAX_RANK) return fail(DKV_ERR_UNSUPPORTED, "rank %d > 64", P->rank);
+  if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
+  if (P->basis_of) return fail(DKV_ERR_INVALID_ARG, "the pool must hold each block's own basis (basis_of NULL)");
+  if (n < 0 || capacity < 1) return fail(DKV_ERR_INVALID_ARG, "n %d < 0 or capacity %d < 1", n, capacity);
+  if (!slots || !entry || !opener || !energy || !kind || !n_entries)
+    return fail(DKV_ERR_INVALID_ARG, "slots / entry / opener / energy / kind / n_entries is NULL");
+  if (!store_vk.ptr || !store_vv.ptr) return fail(DKV_ERR_INVALID_ARG, "store arrays are NULL");
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0 || slots[i] >= P->n_slots) return fail(DKV_ERR_INVALID_ARG, "slot %d out of range", slots[i]);
+    for (int k = 0; k < i; ++k)
+      if (slots[k] == slots[i]) return fail(DKV_ERR_INVALID_ARG, "slot %d given twice", slots[i]);
   }
-  hipLaunchKernelGGL(k_join, dim3((unsigned)grid), dim3(kJoinThreads), kJoinLds, (hipStream_t)stream, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(DKV_ERR_HIP, "k_join launch failed: %s", hipGetErrorString(e));
-  return DKV_OK;
+  dkv_status s;
+  if ((s = check_out(P->u, "u", 2, 2)) || (s = check_out(P->vk, "vk", 2, 2)) || (s = check_out(P->vv, "vv", 2, 2)) ||
+      (s = check_out(store_vk, "store_vk", 2, 2)) || (s = check_out(store_vv, "store_vv", 2, 2)))
+    return s;
+  *n_entries = 0;
+  if (n == 0) return DKV_OK;
+  const int H = P->n_kv_heads, cap = capacity < n ? capacity : n;
+  const hipStream_t st = (hipStream_t)stream;
+  // device scratch of this call: candidate slots and entries, their energies
+  int32_t* d = nullptr;
+  float* d_e = nullptr;
+  if (hipMalloc((void**)&d, sizeof(int32_t) * 2 * (size_t)cap) != hipSuccess ||
+      hipMalloc((void**)&d_e, sizeof(float) * (size_t)cap * H) != hipSuccess) {
+    (void)hipFree(d);
+    return fail(DKV_ERR_HIP, "hipMalloc failed");
+  }
+  std::vector<int32_t> cand_s((size_t)cap), open_slot;
+  std::vector<float> es((size_t)cap * H);
+  JoinArgs a;
+  a.u = (f16*)P->u.ptr; a.u_s = P->u.slot_stride; a.u_h = P->u.head_stride;
+  a.vk = (const f16*)P->vk.ptr; a.vk_s = P->vk.slot_stride; a.vk_h = P->vk.head_stride;
+  a.vv = (const f16*)P->vv.ptr; a.vv_s = P->vv.slot_stride; a.vv_h = P->vv.head_stride;
+  a.basis_of = nullptr;
+  a.n_heads = H;
+  a.n_slots = P->n_slots;
+  a.n_entries = P->n_slots;
+  a.rank = P->rank;
+  a.slots = d;
+  a.entries = d + cap;
+  a.energy = d_e;
+  for (int i = 0; i < n && s == DKV_OK; ++i) {
+    const int m = (int)open_slot.size();
+    int best = -1;
+    float best_e = -INFINITY;
+    if (m > 0) {
+      for (int j = 0; j < m; ++j) cand_s[(size_t)j] = slots[i];
+      a.write = 0;
+      if (hipMemcpyAsync(d, cand_s.data(), sizeof(int32_t) * m, hipMemcpyHostToDevice, st) != hipSuccess ||
+          hipMemcpyAsync(d + cap, open_slot.data(), sizeof(int32_t) * m, hipMemcpyHostToDevice, st) != hipSuccess) {
+        s = fail(DKV_ERR_HIP, "hipMemcpyAsync failed");
+        break;
+      }
+      if ((s = launch_join(a, (int64_t)m * H, st))) break;
+      if (hipMemcpyAsync(es.data(), d_e, sizeof(float) * m * H, hipMemcpyDeviceToHost, st) != hipSuccess ||
+          hipStreamSynchronize(st) != hipSuccess) {
+        s = fail(DKV_ERR_HIP, "reading the join energies failed");
+        break;
+      }
+      for (int j = 0; j < m; ++j) {
+        float e = 0.f;
+        for (int h = 0; h < H; ++h) e += es[(size_t)j * H + h];
+        e /= (float)H;
+        if (e > best_e) {
+          best_e = e;
+          best = j;
+        }
+      }
+    }
+    if (best >= 0 && best_e >= threshold) {
+      entry[i] = best;
+      energy[i] = best_e;
+      kind[i] = 1;
+    } else if (m < capacity) {
+      entry[i] = m;
+      energy[i] = 1.f;
+      kind[i] = 0;
+      open_slot.push_back(slots[i]);
+      continue;
+    } else {
+      entry[i] = best;
+      energy[i] = best_e;
+      kind[i] = 2;
+    }
+    // the join: U' into the block's U
+    a.write = 1;
+    const int32_t pair[2] = {slots[i], open_slot[(size_t)entry[i]]};
+    if (hipMemcpyAsync(d, &pair[0], sizeof(int32_t), hipMemcpyHostToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(d + cap, &pair[1], sizeof(int32_t), hipMemcpyHostToDevice, st) != hipSuccess) {
+      s = fail(DKV_ERR_HIP, "hipMemcpyAsync failed");
+      break;
+    }
+    if ((s = launch_join(a, H, st))) break;
+    if (hipStreamSynchronize(st) != hipSuccess) s = fail(DKV_ERR_HIP, "join failed");
+  }
+  // the store: entry j holds the basis of the block that opened it
+  const size_t rowb = (size_t)P->rank * DKV_HEAD_DIM * 2;
+  for (size_t j = 0; j < open_slot.size() && s == DKV_OK; ++j) {
+    opener[j] = open_slot[j];
+    for (int h = 0; h < H && s == DKV_OK; ++h) {
+      const int64_t src = (int64_t)open_slot[j] * P->vk.slot_stride + (int64_t)h * P->vk.head_stride;
+      const int64_t srv = (int64_t)open_slot[j] * P->vv.slot_stride + (int64_t)h * P->vv.head_stride;
+      const int64_t dk = (int64_t)j * store_vk.slot_stride + (int64_t)h * store_vk.head_stride;
+      const int64_t dv = (int64_t)j * store_vv.slot_stride + (int64_t)h * store_vv.head_stride;
+      if (hipMemcpyAsync((f16*)store_vk.ptr + dk, (const f16*)P->vk.ptr + src, rowb, hipMemcpyDeviceToDevice, st) !=
+              hipSuccess ||
+          hipMemcpyAsync((f16*)store_vv.ptr + dv, (const f16*)P->vv.ptr + srv, rowb, hipMemcpyDeviceToDevice, st) !=
+              hipSuccess)
+        s = fail(DKV_ERR_HIP, "copying a basis into the store failed");
+    }
+  }
+  if (hipStreamSynchronize(st) != hipSuccess && s == DKV_OK) s = fail(DKV_ERR_HIP, "stream failed");
+  (void)hipFree(d);
+  (void)hipFree(d_e);
+  if (s == DKV_OK) *n_entries = (int32_t)open_slot.size();
+  return s;
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@ EXPORTED = ("dkv_status_string", "dkv_last_error", "dkv_abi_version", "dkv_route
             "dkv_decode_profiled", "dkv_gather_route_keys", "dkv_decode_layers_table_size",
             "dkv_decode_layers_workspace_size", "dkv_decode_layers_prepare", "dkv_decode_layers",
             "dkv_seal_blocks", "dkv_rope_freqs", "dkv_join_basis", "dkv_decode_noalloc",
-            "dkv_decode_noalloc_max_bytes", "dkv_decode_layers_profiled", "dkv_stream_read_probe")
+            "dkv_decode_noalloc_max_bytes", "dkv_decode_layers_profiled", "dkv_stream_read_probe",
+            "dkv_share_bases")
 
 
 class DKVError(RuntimeError):
@@ -109,6 +110,8 @@ def load(path: str = LIB_PATH):
     lib.dkv_rope_freqs.restype = i32
     lib.dkv_join_basis.argtypes = [P, vp, vp, i32, i32, vp, vp]
     lib.dkv_join_basis.restype = i32
+    lib.dkv_share_bases.argtypes = [P, vp, i32, i32, f32, View, View, vp, vp, vp, vp, vp, vp]
+    lib.dkv_share_bases.restype = i32
     lib.dkv_route_topk.argtypes = [P, Bp, i32, vp, vp, vp]
     lib.dkv_gather_route_keys.argtypes = [P, Bp, vp, vp]
     lib.dkv_decode_layers_table_size.argtypes = [i32]
@@ -242,6 +245,12 @@ class Pool:
         if fmt != RESID_FP16:
             names = names + ("resid_k_sb", "resid_v_sb")
             order = cls.RECORD_ORDER_Q
+        # a basis store smaller than the slot count (shared bases): V_K and V_V
+        # live in arrays of their own, [n_basis][Hkv][r][128]; the records hold
+        # the rest
+        store = arrays.get("basis_of") is not None and arrays["vk"].shape[0] != S
+        if store:
+            order = tuple(k for k in order if k not in ("vk", "vv"))
         if layout == "arrays":
             t = {k: torch.from_numpy(arrays[k]).to(device) for k in names}
         elif layout == "records":
@@ -261,6 +270,9 @@ class Pool:
             t = {}
             for k in names:
                 a = arrays[k]
+                if store and k in ("vk", "vv"):
+                    t[k] = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+                    continue
                 dt = _TORCH_DTYPE[a.dtype.str]
                 nb = a[0, 0].nbytes if a.size else 0
                 if nb == 0:
@@ -413,6 +425,32 @@ def join_basis(pool: Pool, slots, entries, write: bool = True, stream=None):
     _check(lib.dkv_join_basis(ctypes.byref(pool.c), _ptr(slots), _ptr(entries), n,
                               1 if write else 0, _ptr(energy), _stream(stream)), "dkv_join_basis")
     return energy
+
+
+def share_bases(pool: Pool, slots, capacity: int, threshold: float, stream=None):
+    """dkv_share_bases: assign the blocks in `slots` (host int sequence, seal
+    order) to a basis store of `capacity` entries.  Returns (store_vk, store_vv
+    device tensors [entries][Hkv][r][128], entry, opener, energy, kind numpy
+    arrays).  The pool's U of joined blocks is rewritten in place."""
+    import torch
+    lib = load()
+    dev = pool.tensors["vk"].device
+    sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+    n = int(sl.size)
+    cap = max(1, min(int(capacity), n))
+    store_vk = torch.empty((cap, pool.n_kv_heads, pool.rank, HEAD_DIM), dtype=torch.float16, device=dev)
+    store_vv = torch.empty_like(store_vk)
+    entry = np.zeros(n, np.int32)
+    opener = np.zeros(cap, np.int32)
+    energy = np.zeros(n, np.float32)
+    kind = np.zeros(n, np.int32)
+    n_entries = ctypes.c_int32(0)
+    _check(lib.dkv_share_bases(ctypes.byref(pool.c), sl.ctypes.data, n, int(capacity), float(threshold),
+                               _view(store_vk, 2), _view(store_vv, 2), entry.ctypes.data, opener.ctypes.data,
+                               energy.ctypes.data, kind.ctypes.data, ctypes.byref(n_entries), _stream(stream)),
+           "dkv_share_bases")
+    m = int(n_entries.value)
+    return store_vk[:m], store_vv[:m], entry, opener[:m], energy, kind
 
 
 def route_keys(pool: Pool, slots=None, stream=None) -> None:

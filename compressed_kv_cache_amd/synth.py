@@ -307,19 +307,33 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
     return out
 
 
-def set_shared_basis(wl: Workload, group: int, seed: int = 0) -> Workload:
+def set_shared_basis(wl: Workload, group: int, seed: int = 0, compact: bool = False) -> Workload:
     """Let runs of `group` consecutive logical blocks of each sequence read one
-    basis: the first block's V_K, V_V entry serves the run (the others' entries
-    stay in the arrays, unread), so about 1/group of the entries are read, the
-    pages' sharing fraction.  A seeded shuffle of the entries' order keeps a
-    run's entry away from its own slots."""
-    pos = np.arange(max(wl.n_slots, 1), dtype=np.int32)
+    basis: the first block's V_K, V_V entry serves the run, so about 1/group of
+    the entries are read, the pages' sharing fraction.  compact=False keeps
+    every slot's entry in the arrays (the others unread); compact=True keeps
+    only the entries that are read, so vk / vv shrink to n_basis entries (a
+    basis store of its own, smaller than the slot count).  A seeded shuffle of
+    the entries' order keeps a run's entry away from its own slots."""
+    S = max(wl.n_slots, 1)
+    pos = np.arange(S, dtype=np.int32)
     for b in range(wl.batch):
         nb = int(wl.n_blocks[b])
         for j in range(nb):
             pos[wl.block_table[b, j]] = wl.block_table[b, (j // group) * group]
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 91, seed])))
-    perm = rng.permutation(max(wl.n_slots, 1)).astype(np.int32)
+    if compact:
+        used = np.unique(pos)                                  # slots whose basis some block reads
+        order = rng.permutation(used.size)
+        keep = used[order]                                     # entry e holds slot keep[e]'s basis
+        entry_of = np.full(S, -1, dtype=np.int64)
+        entry_of[keep] = np.arange(keep.size)
+        for lay in wl.layers:
+            lay.vk = np.ascontiguousarray(lay.vk[keep])
+            lay.vv = np.ascontiguousarray(lay.vv[keep])
+            lay.basis_of = entry_of[pos].astype(np.int32)
+        return wl
+    perm = rng.permutation(S).astype(np.int32)
     for lay in wl.layers:
         lay.vk = np.ascontiguousarray(lay.vk[np.argsort(perm)])
         lay.vv = np.ascontiguousarray(lay.vv[np.argsort(perm)])
@@ -392,7 +406,10 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
     "Q8" / "Q4" (residual rows in the 8- or 4-bit group-quantised format) for
     configs 0, 1 and 2, or "U" (the same arrays read as an un-rotated pool with
     rotary base ROPE_BASE) for any configuration, or "UB" (the U variant with
-    pairs of consecutive blocks sharing one basis, a sharing fraction of 0.5)."""
+    pairs of consecutive blocks sharing one basis, a sharing fraction of 0.5),
+    or "UC2" / "UC4" (the U variant with runs of 2 or 4 blocks sharing one
+    basis, kept in a compact basis store of about n_slots / 2 or n_slots / 4
+    entries)."""
     seed = 1000 + cfg if seed is None else seed
     if variant == "U":
         wl = make_config(cfg, seed, layers)
@@ -402,6 +419,10 @@ def make_config(cfg: int, seed: Optional[int] = None, layers: Optional[Sequence[
         wl = make_config(cfg, seed, layers, "U")
         wl.name += "B"
         return set_shared_basis(wl, 2)
+    if variant in ("UC2", "UC4"):
+        wl = make_config(cfg, seed, layers, "U")
+        wl.name += variant[1:]
+        return set_shared_basis(wl, int(variant[2]), compact=True)
     if variant in ("Q8", "Q4"):
         fmt = RESID_INT8 if variant == "Q8" else RESID_INT4
         base = {0: dict(batch=1, n_q_heads=1, n_kv_heads=1, window=512, n_blocks=[14], ranks=[32],

@@ -458,10 +458,39 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
  * caller then sets basis_of[s] = g (its own array) and recomputes the routing
  * key (dkv_route_keys).  Entries index vk / vv: [0, n_basis) with basis_of set,
  * else [0, n_slots).  An item with a slot or entry out of range writes energy
- * -1 and changes nothing.  Slots of one call must be distinct.
+ * -1 and changes nothing.  With write != 0, slots of one call must be
+ * distinct (scoring one slot against several entries may repeat it).
  *   slots, entries: int32 [n] device;  energy: fp32 [n][n_kv_heads] device out. */
 dkv_status dkv_join_basis(const dkv_pool* pool, const int32_t* slots, const int32_t* entries, int32_t n,
                           int32_t write, float* energy, void* stream);
+
+/* Shared bases under a budget (README "Key Environment Knobs", DKV_SHARED_BASIS
+ * and DKV_SHARED_BASIS_FRAC: a basis store of a capacity fixed as a fraction
+ * of the block slots; "3. Shared Low-Rank Bases": voluntary joins when the
+ * retained energy is high enough, forced joins once the store is full).
+ * `pool` holds each block's own basis (basis_of NULL), e.g. as dkv_seal_blocks
+ * wrote it.  The blocks in slots[0 .. n) (host array, distinct slots) are taken
+ * in that order; block i is scored (dkv_join_basis) against the basis of the
+ * block that opened each entry so far, its energy for an entry being the mean
+ * over the KV heads, and with the best entry (largest energy, ties to the
+ * lower entry):
+ *   - energy >= threshold: a voluntary join (kind 1);
+ *   - else, while fewer than `capacity` entries are open: block i opens a new
+ *     entry with its own basis (kind 0, energy 1);
+ *   - else: a forced join to the best entry (kind 2).
+ * A join writes U' into the block's U (dkv_join_basis, write = 1).  At the
+ * end entry j of the store (store_vk, store_vv: device views like pool's vk,
+ * vv, at least min(capacity, n) entries) holds the basis of the block that
+ * opened it.  Host outputs: entry[n] (the store entry each block reads),
+ * opener[min(capacity, n)] (the slot that opened each entry), energy[n],
+ * kind[n], *n_entries.  The caller then reads the blocks through the store:
+ * basis_of[slots[i]] = entry[i], vk / vv = the store, n_basis = *n_entries, and
+ * recomputes their routing keys (dkv_route_keys).  Synchronous on `stream`
+ * (energies come back to the host after each block; the decisions are made
+ * on the host in fp32); allocates a little device memory for the call. */
+dkv_status dkv_share_bases(const dkv_pool* pool, const int32_t* slots, int32_t n, int32_t capacity, float threshold,
+                           dkv_view store_vk, dkv_view store_vv, int32_t* entry, int32_t* opener, float* energy,
+                           int32_t* kind, int32_t* n_entries, void* stream);
 
 #ifdef __cplusplus
 }

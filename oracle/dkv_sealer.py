@@ -163,3 +163,57 @@ def join_basis(u, vk, vv, vk_g, vv_g):
     num = np.sum((up @ Vg) ** 2)
     den = np.sum((U @ V) ** 2)
     return up, (num / den if den > 0 else 1.0)
+
+
+def assign_bases(blocks, capacity, threshold):
+    """Shared bases under a budget (README "Key Environment Knobs",
+    DKV_SHARED_BASIS and DKV_SHARED_BASIS_FRAC: the basis store is allocated
+    as a fraction of the block slots; "3. Shared Low-Rank Bases": a block
+    joins a basis voluntarily when the retained energy is high enough, and is
+    forced to join once the store is full).  blocks: sealed blocks in seal
+    order, each (u [H][255][r], vk [H][r][128], vv [H][r][128]) for its H KV
+    heads, with its own basis.  Block i is scored against every entry of the
+    store so far: the retained energy of joining entry j is the mean over the
+    KV heads of join_basis's energy against the basis of the block that opened
+    entry j.  With the best entry (largest energy, ties to the lower entry):
+      - energy >= threshold: a voluntary join (block i reads entry j);
+      - else, while the store holds fewer than `capacity` entries: block i
+        opens a new entry holding its own basis;
+      - else: a forced join to the best entry.
+    A joined block's U becomes join_basis's U' (per head).  Returns (entry
+    [n] (the store entry each block reads), opener [m] (the block that opened
+    each entry), U list (per block, [H][255][r], U' for joined blocks),
+    energy [n] (1 for a block that opened an entry), kind [n] (0 opened, 1
+    voluntary, 2 forced))."""
+    if capacity < 1:
+        raise ValueError("capacity must be at least 1")
+    n = len(blocks)
+    entry = np.zeros(n, np.int64)
+    energy = np.ones(n, np.float64)
+    kind = np.zeros(n, np.int64)
+    opener = []
+    us = []
+    for i, (u, vk, vv) in enumerate(blocks):
+        H = len(u)
+        best, best_e, best_u = -1, -np.inf, None
+        for j, o in enumerate(opener):
+            _, vk_g, vv_g = blocks[o]
+            ups, es = [], []
+            for h in range(H):
+                up, e = join_basis(u[h], vk[h], vv[h], vk_g[h], vv_g[h])
+                ups.append(up)
+                es.append(e)
+            e = float(np.mean(es))
+            if e > best_e:
+                best, best_e, best_u = j, e, ups
+        if best >= 0 and best_e >= threshold:
+            entry[i], energy[i], kind[i] = best, best_e, 1
+            us.append(np.stack(best_u))
+        elif len(opener) < capacity:
+            entry[i] = len(opener)
+            opener.append(i)
+            us.append(np.asarray(u, np.float64))
+        else:
+            entry[i], energy[i], kind[i] = best, best_e, 2
+            us.append(np.stack(best_u))
+    return entry, np.asarray(opener, np.int64), us, energy, kind

@@ -268,3 +268,69 @@ def test_join_basis(lib, variant):
                 # its own basis (joint rows of V_K, V_V not orthonormal here: the
                 # synthetic bases are orthonormal in K and in V separately)
                 assert abs(e1[i, h] - 1.0) <= 1e-4, (i, h, e1[i, h])
+
+
+def _related_pool(seed, n, H, r, related):
+    """n blocks of H KV heads with random orthonormal joint bases [V_K | V_V],
+    except that block i in `related` takes block i - 1's subspace (a random
+    rotation of its basis plus a little noise): fp16 pool arrays."""
+    rng = np.random.default_rng(seed)
+    u = (rng.standard_normal((n, H, 255, r)) * np.linspace(2.0, 0.5, r)).astype(np.float16)
+    W = np.zeros((n, H, r, 256))
+    for i in range(n):
+        for h in range(H):
+            if i in related:
+                Qr, _ = np.linalg.qr(rng.standard_normal((r, r)))
+                w = Qr @ W[i - 1, h] + 1e-3 * rng.standard_normal((r, 256))
+            else:
+                w = rng.standard_normal((r, 256))
+            W[i, h] = np.linalg.qr(w.T)[0].T
+    W = W.astype(np.float16)
+    z = np.zeros((n, H, 128), np.float16)
+    return dict(anchor_k=z, anchor_v=z.copy(), u=u, vk=np.ascontiguousarray(W[..., :128]),
+                vv=np.ascontiguousarray(W[..., 128:]), resid_k=np.zeros((n, H, 0, 128), np.float16),
+                resid_v=np.zeros((n, H, 0, 128), np.float16), resid_pos=np.zeros((n, H, 0), np.uint8))
+
+
+@pytest.mark.parametrize("capacity,threshold", [(12, 0.9), (5, 0.9), (3, 0.5), (1, 2.0)])
+def test_share_bases_against_oracle(lib, capacity, threshold):
+    """dkv_share_bases against the oracle's policy (assign_bases) on blocks in a
+    shuffled seal order, some of which can join an earlier block's basis almost
+    losslessly: the same kinds and entries (a forced join may pick another entry
+    only within 1e-4 of the best energy), the energies, the joined U, and the
+    store holding each opener's basis bit for bit."""
+    n, H, r = 12, 2, 16
+    related = {1, 2, 5, 8, 11}
+    P = _related_pool(2024, n, H, r, related)
+    order = np.random.default_rng(7).permutation(n).astype(np.int32)      # seal order (blocks)
+    slot_of = np.random.default_rng(8).permutation(n).astype(np.int32)    # block i lives in slot slot_of[i]
+    arrays = {k: (v[np.argsort(slot_of)] if v.shape[0] == n else v) for k, v in P.items()}
+    pool = lib.Pool.from_numpy(arrays, DEV)
+    slots = slot_of[order]
+    store_vk, store_vv, entry, opener, energy, kind = lib.share_bases(pool, slots, capacity, threshold)
+    torch.cuda.synchronize()
+    blocks = [(P["u"][i].astype(np.float64), P["vk"][i].astype(np.float64), P["vv"][i].astype(np.float64))
+              for i in order]
+    e_ref, op_ref, us_ref, en_ref, kd_ref = S.assign_bases(blocks, capacity, threshold)
+    say(f"[share bases] capacity {capacity} threshold {threshold}: kinds {list(kind)} entries {len(opener)}")
+    assert list(kind) == list(kd_ref)
+    assert list(opener) == list(slots[op_ref])
+    u_gpu = pool.tensors["u"].cpu().numpy()
+    for i in range(n):
+        if kind[i] == 2 and entry[i] != e_ref[i]:
+            _, e_alt = zip(*[S.join_basis(blocks[i][0][h], blocks[i][1][h], blocks[i][2][h],
+                                          blocks[op_ref[entry[i]]][1][h], blocks[op_ref[entry[i]]][2][h])
+                             for h in range(H)])
+            assert abs(np.mean(e_alt) - en_ref[i]) <= 1e-4, (i, entry[i], e_ref[i])
+            continue
+        assert entry[i] == e_ref[i], (i, entry[i], e_ref[i])
+        assert abs(energy[i] - en_ref[i]) <= 1e-4, (i, energy[i], en_ref[i])
+        got = u_gpu[slots[i]].astype(np.float64)
+        ref = us_ref[i]
+        assert np.all(np.abs(got - ref) <= 2e-3 * np.abs(ref) + 2e-3 * np.abs(ref).max()), i
+    # the store: entry j holds its opener's basis, bit for bit
+    svk, svv = store_vk.cpu().numpy(), store_vv.cpu().numpy()
+    for j, s in enumerate(opener):
+        blk = int(np.where(slot_of == s)[0][0])
+        assert np.array_equal(svk[j], P["vk"][blk]) and np.array_equal(svv[j], P["vv"][blk])
+    assert len(opener) <= capacity

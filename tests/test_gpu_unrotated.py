@@ -188,6 +188,51 @@ def test_decode_layers_shared_basis(lib):
         say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
 
 
+@pytest.mark.parametrize("cfg,variant", [(0, "UC2"), (0, "UC4"), (1, "UC2"), (1, "UC4"), (3, "UC2"), (3, "UC4")])
+def test_decode_compact_basis_store(lib, cfg, variant):
+    """A basis store smaller than the pool (V_K, V_V in arrays of their own with
+    about n_slots / 2 or n_slots / 4 entries, records without them): routing
+    keys and the decode against the oracle."""
+    wl = synth.make_config(cfg, variant=variant)
+    lay = wl.layers[0]
+    n_basis = lay.vk.shape[0]
+    assert n_basis <= (wl.n_slots + int(variant[2]) * wl.batch) // int(variant[2])
+    say(f"[compact basis] {wl.name}: {n_basis} entries for {wl.n_slots} slots")
+    pool, _ = upload(lib, wl)
+    assert pool.c.n_basis == n_basis and pool.tensors["vk"].shape[0] == n_basis
+    got = pool.route_key.cpu().numpy().astype(np.float64)
+    P = lay.pool()
+    for s in range(0, got.shape[0], 5):
+        for h in range(got.shape[1]):
+            ref = oracle.block_route_key(P, s, h)
+            assert np.abs(got[s, h] - ref).max() <= 1e-5 * (np.abs(ref).max() + 1.0)
+    check_decode(lib, wl, label=f"compact basis store {variant}")
+
+
+@pytest.mark.parametrize("variant", ["UC2", "UC4"])
+def test_decode_layers_compact_basis_store(lib, variant):
+    """Four layers of the un-rotated 64k batch-4 stack with compact basis
+    stores, in one layer-batched launch and per layer."""
+    wl = synth.make_config(2, layers=[0, 9, 19, 27], variant=variant)
+    say(f"[decode layers {variant}] stack64k layers 0, 9, 19, 27: {wl.layers[0].vk.shape[0]} entries "
+        f"for {wl.n_slots} slots")
+    pools, batches = [], []
+    for l in range(4):
+        p_, b_ = upload(lib, wl, l)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, wl.top_k, wl.scale)
+    res = _run_layers(lib, run, reps=2)
+    for l in range(4):
+        o1, s1, i1 = lib.decode(pools[l], batches[l], wl.top_k, wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1)
+        c = _oracle_check(wl, wl.layers[l], *res[l], wl.top_k)
+        c1 = _oracle_check(wl, wl.layers[l], o1, s1, i1, wl.top_k)
+        say(f"   layer {l}: max|d out| {c.max_out:.3e} (per layer {c1.max_out:.3e})")
+
+
 def test_decode_layers_unrotated_mixed_ranks(lib):
     """Un-rotated layers of every low-rank tile count (ranks 1..64, 0..255
     residual rows), ragged windows, an empty sequence and a shared basis in one

@@ -228,3 +228,97 @@ def test_join_with_a_basis_whose_rows_are_not_orthonormal():
     X = np.linalg.lstsq(Vg.T, (U @ V).T, rcond=None)[0].T
     np.testing.assert_allclose(up, X, atol=1e-10)
     assert abs(e - np.sum((X @ Vg) ** 2) / np.sum((U @ V) ** 2)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Shared bases under a budget (assign_bases)
+# ---------------------------------------------------------------------------
+
+def _blocks(seed, n, H=2, r=6, related=()):
+    """n random blocks (orthonormal joint basis rows); block i in `related`
+    takes block i - 1's subspace (its basis turned by a random rotation, plus
+    a little noise), so that it can join that block's entry almost losslessly."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        u = rng.standard_normal((H, 255, r))
+        if i in related:
+            _, vk0, vv0 = out[i - 1]
+            vk, vv = [], []
+            for h in range(H):
+                Qr, _ = np.linalg.qr(rng.standard_normal((r, r)))
+                W = Qr @ np.hstack([vk0[h], vv0[h]]) + 1e-3 * rng.standard_normal((r, 256))
+                W = np.linalg.qr(W.T)[0].T
+                vk.append(W[:, :128])
+                vv.append(W[:, 128:])
+            vk, vv = np.stack(vk), np.stack(vv)
+        else:
+            W = np.stack([np.linalg.qr(rng.standard_normal((256, r)))[0].T for _ in range(H)])
+            vk, vv = W[:, :, :128], W[:, :, 128:]
+        out.append((u, vk, vv))
+    return out
+
+
+def _energy_lstsq(b, g):
+    """Retained energy of block b on block g's basis, by numpy's least squares
+    (an independent route to join_basis's U'), mean over heads."""
+    u, vk, vv = b
+    _, vkg, vvg = g
+    es = []
+    for h in range(len(u)):
+        V = np.hstack([vk[h], vv[h]])
+        Vg = np.hstack([vkg[h], vvg[h]])
+        X = np.linalg.lstsq(Vg.T, (u[h] @ V).T, rcond=None)[0].T
+        es.append(np.sum((X @ Vg) ** 2) / np.sum((u[h] @ V) ** 2))
+    return float(np.mean(es))
+
+
+def test_assign_bases_brute_force():
+    """Every decision against a brute-force replay: the energies of each block
+    to every entry open at that time by least squares, the best entry, and the
+    rule (voluntary at or above the threshold, a new entry while there is room,
+    else forced); the store never exceeds its capacity."""
+    blocks = _blocks(5, 9, related=(1, 2, 5, 8))
+    for capacity, thr in ((9, 0.9), (3, 0.9), (2, 0.5), (1, 0.99), (4, 1.5)):
+        entry, opener, us, energy, kind = S.assign_bases(blocks, capacity, thr)
+        assert len(opener) <= capacity
+        open_now = []
+        for i, b in enumerate(blocks):
+            es = [_energy_lstsq(b, blocks[o]) for o in open_now]
+            best = int(np.argmax(es)) if es else -1
+            if es and es[best] >= thr:
+                assert kind[i] == 1 and entry[i] == best and abs(energy[i] - es[best]) < 1e-9
+            elif len(open_now) < capacity:
+                assert kind[i] == 0 and entry[i] == len(open_now) and opener[len(open_now)] == i
+                open_now.append(i)
+                assert np.array_equal(us[i], b[0])
+            else:
+                assert kind[i] == 2 and entry[i] == best and abs(energy[i] - es[best]) < 1e-9
+            if kind[i] != 0:
+                # the joined U reproduces the least-squares projection onto the entry's basis
+                _, vkg, vvg = blocks[opener[entry[i]]]
+                for h in range(2):
+                    Vg = np.hstack([vkg[h], vvg[h]])
+                    V = np.hstack([b[1][h], b[2][h]])
+                    X = np.linalg.lstsq(Vg.T, (b[0][h] @ V).T, rcond=None)[0].T
+                    assert np.allclose(us[i][h], X, atol=1e-9)
+
+
+def test_assign_bases_special_cases():
+    blocks = _blocks(11, 6, related=(3,))
+    # room for everyone and a threshold no energy reaches: every block opens an entry
+    entry, opener, _, energy, kind = S.assign_bases(blocks, 6, 1.01)
+    assert list(kind) == [0] * 6 and list(entry) == list(range(6)) and list(opener) == list(range(6))
+    # one entry: every later block joins it (forced unless related enough)
+    entry, opener, _, _, kind = S.assign_bases(blocks, 1, 2.0)
+    assert list(opener) == [0] and list(entry) == [0] * 6 and list(kind) == [0] + [2] * 5
+    # the related block joins its parent voluntarily, keeping almost all its energy
+    entry, opener, _, energy, kind = S.assign_bases(blocks, 6, 0.9)
+    assert kind[3] == 1 and entry[3] == entry[2] and energy[3] > 0.99
+    assert all(kind[i] == 0 for i in (0, 1, 2, 4, 5))
+    # an exact copy of a block keeps all its energy
+    copy = [blocks[0], (blocks[0][0] * 1.5, blocks[0][1], blocks[0][2])]
+    entry, _, us, energy, kind = S.assign_bases(copy, 2, 0.999)
+    assert kind[1] == 1 and abs(energy[1] - 1.0) < 1e-12 and np.allclose(us[1], copy[1][0])
+    with pytest.raises(ValueError):
+        S.assign_bases(blocks, 0, 0.5)

@@ -65,3 +65,44 @@ def test_identity_map_changes_nothing():
     o2, l2, _ = _decode(wl, ident)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def _wl_compact(seed, group):
+    wl = synth.make_workload("sbc", seed=seed, batch=2, n_q_heads=4, n_kv_heads=2, window=24,
+                             n_blocks=[5, 4], ranks=[10], n_resid=12, top_k=3, sigma0=2.0,
+                             rope_base=1e6, permute_slots=True)
+    return synth.set_shared_basis(wl, group, compact=True)
+
+
+def test_compact_store_equals_materialised_pool():
+    """A compact basis store (only the entries read, n_basis < n_slots) decodes
+    and routes exactly like the pool with each block's basis copied into its own
+    slot, and holds one entry per run of blocks."""
+    for group in (2, 4):
+        wl = _wl_compact(41 + group, group)
+        lay = wl.layers[0]
+        runs = sum((int(n) + group - 1) // group for n in wl.n_blocks)
+        assert lay.vk.shape[0] == runs < wl.n_slots
+        P = lay.pool()
+        assert int(P["basis_of"].max()) < P["vk"].shape[0]
+        ref = _decode(wl, _materialised(P))
+        got = _decode(wl, P)
+        for a, b in zip(got[:2], ref[:2]):
+            assert np.array_equal(a, b)
+        assert np.array_equal(got[2], ref[2])
+
+
+def test_compact_and_expanded_stores_agree():
+    """The same sharing kept in a compact store and in the per-slot arrays
+    (entries shuffled differently) reads the same basis for every block."""
+    base = dict(batch=2, n_q_heads=4, n_kv_heads=2, window=24, n_blocks=[5, 4], ranks=[10], n_resid=12,
+                top_k=3, sigma0=2.0, rope_base=1e6, permute_slots=True)
+    a = synth.set_shared_basis(synth.make_workload("sa", seed=77, **base), 2)
+    b = synth.set_shared_basis(synth.make_workload("sb", seed=77, **base), 2, compact=True)
+    pa, pb = a.layers[0].pool(), b.layers[0].pool()
+    used = sorted({int(x) for s in range(2) for x in a.block_table[s, :a.n_blocks[s]]})
+    for s in used:
+        assert np.array_equal(pa["vk"][pa["basis_of"][s]], pb["vk"][pb["basis_of"][s]])
+        assert np.array_equal(pa["vv"][pa["basis_of"][s]], pb["vv"][pb["basis_of"][s]])
+    ra, rb = _decode(a, pa), _decode(b, pb)
+    assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
