@@ -67,7 +67,48 @@ struct SealArgs {
   f16* rk; int64_t rk_s, rk_h;
   f16* rv; int64_t rv_s, rv_h;
   uint8_t* rp; int64_t rp_s, rp_h;
+  int resid_bits;                  // 16 (fp16 rows), or 8 / 4 (codes in rk / rv as bytes, strides in bytes)
+  f16* rks; int64_t rks_s, rks_h;  // quantised: (scale, bias) pairs [R][2][2] of the K rows
+  f16* rvs; int64_t rvs_s, rvs_h;  // the same for the V rows
 };
+
+// One fp16 row (128 dims) into the group-quantised format: per group of 64,
+// bias = the smallest value, scale = (largest - smallest) / L in fp32 rounded
+// up to fp16 (the grid reaches the largest value), code = round((x - bias) /
+// scale) in fp32 with ties to even, clamped to [0, L] (0 for a zero scale).
+// codes: 128 bytes (8 bits) or 64 bytes (4 bits, dimension 2j in the low
+// nibble of byte j); sb: (scale, bias) of dims 0..63, then 64..127.
+__device__ void quantize_row(const f16* x, int bits, uint8_t* codes, f16* sb) {
+  const float L = (float)((1 << bits) - 1);
+  for (int g = 0; g < 2; ++g) {
+    float lo = (float)x[64 * g], hi = lo;
+    for (int d = 1; d < 64; ++d) {
+      const float v = (float)x[64 * g + d];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    const float s32 = __fdiv_rn(hi - lo, L);
+    f16 s16 = (f16)s32;
+    if ((float)s16 < s32) s16 = __builtin_bit_cast(f16, (uint16_t)(__builtin_bit_cast(uint16_t, s16) + 1u));
+    const f16 b16 = (f16)lo;
+    const float sf = (float)s16, bf = (float)b16;
+    sb[2 * g] = s16;
+    sb[2 * g + 1] = b16;
+    for (int d = 0; d < 64; d += 2) {
+      uint32_t c[2];
+      for (int e = 0; e < 2; ++e) {
+        const float q = sf > 0.f ? rintf(__fdiv_rn((float)x[64 * g + d + e] - bf, sf)) : 0.f;
+        c[e] = (uint32_t)fminf(fmaxf(q, 0.f), L);
+      }
+      if (bits == 8) {
+        codes[64 * g + d] = (uint8_t)c[0];
+        codes[64 * g + d + 1] = (uint8_t)c[1];
+      } else {
+        codes[32 * g + d / 2] = (uint8_t)(c[0] | (c[1] << 4));
+      }
+    }
+  }
+}
 
 // LDS layout (in 4-byte words) for a padded width LP (a multiple of 16)
 template <int LP>
@@ -501,6 +542,16 @@ __global__ __launch_bounds__(kThreads) void k_seal(SealArgs A) {
       for (int i = 0; i < t; ++i) o += sel[i];
       if (o >= A.n_resid) return;  // only with non-finite errors (ranks then tie): never write past R rows
       A.rp[slot * A.rp_s + h * A.rp_h + o] = (uint8_t)(t + 1);
+      if (A.resid_bits != 16) {
+        const int rb = A.resid_bits == 8 ? kD : kD / 2;  // code bytes per row
+        quantize_row(xk + (int64_t)(t + 1) * kD, A.resid_bits,
+                     reinterpret_cast<uint8_t*>(A.rk) + slot * A.rk_s + h * A.rk_h + (int64_t)o * rb,
+                     A.rks + slot * A.rks_s + h * A.rks_h + (int64_t)o * 4);
+        quantize_row(xv + (int64_t)(t + 1) * kD, A.resid_bits,
+                     reinterpret_cast<uint8_t*>(A.rv) + slot * A.rv_s + h * A.rv_h + (int64_t)o * rb,
+                     A.rvs + slot * A.rvs_s + h * A.rvs_h + (int64_t)o * 4);
+        return;
+      }
       const v8h* ks = reinterpret_cast<const v8h*>(xk + (int64_t)(t + 1) * kD);
       const v8h* vs = reinterpret_cast<const v8h*>(xv + (int64_t)(t + 1) * kD);
       v8h* kd = reinterpret_cast<v8h*>(A.rk + slot * A.rk_s + h * A.rk_h + (int64_t)o * kD);
@@ -715,8 +766,9 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
   if (P->n_resid > DKV_MAX_RESID) return fail(DKV_ERR_UNSUPPORTED, "n_resid %d > 255", P->n_resid);
   if (P->n_kv_heads < 1) return fail(DKV_ERR_INVALID_ARG, "n_kv_heads %d < 1", P->n_kv_heads);
   if (P->n_slots < 0) return fail(DKV_ERR_INVALID_ARG, "n_slots %d < 0", P->n_slots);
-  if (P->resid_format != DKV_RESID_FP16)
-    return fail(DKV_ERR_UNSUPPORTED, "sealing writes fp16 residual rows only (resid_format %d)", P->resid_format);
+  if (P->resid_format != DKV_RESID_FP16 && P->resid_format != DKV_RESID_INT8 && P->resid_format != DKV_RESID_INT4)
+    return fail(DKV_ERR_INVALID_ARG, "resid_format %d", P->resid_format);
+  const bool quant = P->resid_format != DKV_RESID_FP16;
   if (width < P->rank) return fail(DKV_ERR_INVALID_ARG, "width %d < rank %d", width, P->rank);
   if (width > kMaxWidth) return fail(DKV_ERR_UNSUPPORTED, "width %d > %d", width, kMaxWidth);
   if (power_iters < 0 || power_iters > kMaxPowerIters)
@@ -733,9 +785,14 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
   if ((s = check_out(P->anchor_k, "anchor_k", 2, 2)) || (s = check_out(P->anchor_v, "anchor_v", 2, 2)) ||
       (s = check_out(P->u, "u", 2, 2)) || (s = check_out(P->vk, "vk", 2, 2)) || (s = check_out(P->vv, "vv", 2, 2)))
     return s;
-  if (P->n_resid > 0 && ((s = check_out(P->resid_k, "resid_k", 2, 16)) ||
-                         (s = check_out(P->resid_v, "resid_v", 2, 16)) ||
-                         (s = check_out(P->resid_pos, "resid_pos", 1, 1))))
+  if (P->n_resid > 0 && !quant &&
+      ((s = check_out(P->resid_k, "resid_k", 2, 16)) || (s = check_out(P->resid_v, "resid_v", 2, 16)) ||
+       (s = check_out(P->resid_pos, "resid_pos", 1, 1))))
+    return s;
+  if (P->n_resid > 0 && quant &&
+      ((s = check_out(P->resid_k, "resid_k", 1, 1)) || (s = check_out(P->resid_v, "resid_v", 1, 1)) ||
+       (s = check_out(P->resid_k_sb, "resid_k_sb", 2, 2)) || (s = check_out(P->resid_v_sb, "resid_v_sb", 2, 2)) ||
+       (s = check_out(P->resid_pos, "resid_pos", 1, 1))))
     return s;
   const int64_t grid = (int64_t)n_blocks * P->n_kv_heads;
   if (grid > 0x7FFFFFFF) return fail(DKV_ERR_INVALID_ARG, "too many blocks");
@@ -758,6 +815,9 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
   a.rk = (f16*)P->resid_k.ptr; a.rk_s = P->resid_k.slot_stride; a.rk_h = P->resid_k.head_stride;
   a.rv = (f16*)P->resid_v.ptr; a.rv_s = P->resid_v.slot_stride; a.rv_h = P->resid_v.head_stride;
   a.rp = (uint8_t*)P->resid_pos.ptr; a.rp_s = P->resid_pos.slot_stride; a.rp_h = P->resid_pos.head_stride;
+  a.resid_bits = P->resid_format == DKV_RESID_INT8 ? 8 : (P->resid_format == DKV_RESID_INT4 ? 4 : 16);
+  a.rks = (f16*)P->resid_k_sb.ptr; a.rks_s = P->resid_k_sb.slot_stride; a.rks_h = P->resid_k_sb.head_stride;
+  a.rvs = (f16*)P->resid_v_sb.ptr; a.rvs_s = P->resid_v_sb.slot_stride; a.rvs_h = P->resid_v_sb.head_stride;
   hipStream_t st = (hipStream_t)stream;
   const unsigned g = (unsigned)grid;
   if (width <= 16)

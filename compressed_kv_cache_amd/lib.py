@@ -323,8 +323,9 @@ class Pool:
 
     @classmethod
     def empty(cls, n_slots: int, n_kv_heads: int, rank: int, n_resid: int, device="cuda",
-              layout: str = "records"):
-        """A zero-filled fp16-residual pool for dkv_seal_blocks to write into."""
+              layout: str = "records", resid_format: int = RESID_FP16):
+        """A zero-filled pool for dkv_seal_blocks to write into (residual rows
+        fp16, or 8- / 4-bit codes with their (scale, bias) pairs)."""
         S, H, d = n_slots, n_kv_heads, HEAD_DIM
         arrays = dict(anchor_k=np.zeros((S, H, d), np.float16), anchor_v=np.zeros((S, H, d), np.float16),
                       u=np.zeros((S, H, BLOCK_SIZE - 1, rank), np.float16),
@@ -332,6 +333,11 @@ class Pool:
                       resid_k=np.zeros((S, H, n_resid, d), np.float16),
                       resid_v=np.zeros((S, H, n_resid, d), np.float16),
                       resid_pos=np.zeros((S, H, n_resid), np.uint8))
+        if resid_format != RESID_FP16:
+            w = d if resid_format == RESID_INT8 else d // 2
+            arrays.update(resid_k=np.zeros((S, H, n_resid, w), np.uint8), resid_v=np.zeros((S, H, n_resid, w), np.uint8),
+                          resid_k_sb=np.zeros((S, H, n_resid, 2, 2), np.float16),
+                          resid_v_sb=np.zeros((S, H, n_resid, 2, 2), np.float16), resid_format=resid_format)
         return cls.from_numpy(arrays, device, layout)
 
     @property

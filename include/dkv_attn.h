@@ -429,12 +429,20 @@ dkv_status dkv_stream_read_probe(const void* src, size_t bytes, int32_t n_waves,
  *   resid_pos/k/v       the n_resid positions in 1..255 whose key is worst
  *                       reconstructed, |k_i - (a_k + U_{i-1} V_K)| from the
  *                       stored fp16 factors (fp32 arithmetic; equal errors to
- *                       the lower position), ascending, and their exact rows;
+ *                       the lower position), ascending, and their exact rows:
+ *                       fp16, or in the pool's 8- / 4-bit format (README
+ *                       "2. Physical 4-Bit Group-Quantized Residual Buffers
+ *                       (INT4)", "Tunable Quantization Dials"): per row and
+ *                       group of 64 dims, bias = the smallest value, scale =
+ *                       (largest - smallest) / L in fp32 rounded up to fp16,
+ *                       code = round((x - bias) / scale) in fp32, ties to
+ *                       even, clamped to [0, L] (L = 255 or 15; 0 for a zero
+ *                       scale), into resid_k / resid_v and resid_k_sb /
+ *                       resid_v_sb;
  *   route_key           as dkv_route_keys, if pool->route_key.ptr is set.
  *   omega: fp32 [256][width], the Gaussian test matrix (the caller's seeded
  *          draw); rank <= width <= 80 (DKV_ERR_UNSUPPORTED above 80);
  *   power_iters: 0..8.
- * Only the fp16 residual format is written (DKV_ERR_UNSUPPORTED otherwise).
  * Sources: 16-byte aligned pointers and strides; residual rows likewise.
  * Source rows and the pool slots written must not overlap, nor two entries of
  * slots name the same slot.  Asynchronous on `stream`. */

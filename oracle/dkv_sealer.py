@@ -105,11 +105,57 @@ def select_residuals(err: np.ndarray, n_resid: int) -> np.ndarray:
     return np.sort(np.array(order[:n_resid], dtype=np.int64) + 1)
 
 
+def quantize_rows(rows, bits: int):
+    """Residual rows into the 8- or 4-bit group-quantised format (README "2.
+    Physical 4-Bit Group-Quantized Residual Buffers (INT4)" and "Tunable
+    Quantization Dials": asymmetric groups of 64 dimensions, a half-precision
+    scale and bias per group and row, unsigned codes; the layout
+    dequantize_rows reads).  rows: fp16 [R][128].  Per row and group, with
+    L = 2^bits - 1 and the group's smallest and largest values lo, hi:
+        bias  = lo (an fp16 value already);
+        scale = (hi - lo) / L in fp32, rounded up to fp16 (so the grid reaches
+                hi);
+        code  = round((x - bias) / scale) in fp32 (ties to even), clamped to
+                [0, L]; 0 when the scale is 0 (a constant group).
+    The codes are decided in fp32 (IEEE subtract and divide, as the kernel
+    computes them), so both sides find the same integers.  Returns (codes uint8
+    [R][128] for 8 bits, or [R][64] with dimension 2j in the low nibble of
+    byte j for 4 bits; scale_bias fp16 [R][2][2] holding (scale, bias) per
+    group)."""
+    x = np.asarray(rows, np.float16).astype(np.float32)
+    R = x.shape[0]
+    L = np.float32((1 << bits) - 1)
+    codes = np.zeros((R, D), np.uint8)
+    sb = np.zeros((R, D // 64, 2), np.float16)
+    for g in range(D // 64):
+        xs = x[:, 64 * g:64 * (g + 1)]
+        lo = xs.min(axis=1) if R else np.zeros(0, np.float32)
+        hi = xs.max(axis=1) if R else np.zeros(0, np.float32)
+        s32 = (hi - lo) / L                                   # fp32 subtract and divide
+        s16 = s32.astype(np.float16)                          # nearest even ...
+        up = s16.astype(np.float32) < s32                     # ... then up to the next fp16
+        s16[up] = np.nextafter(s16[up], np.float16(np.inf))
+        b16 = lo.astype(np.float16)
+        sf, bf = s16.astype(np.float32), b16.astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = (xs - bf[:, None]) / sf[:, None]             # fp32
+        c = np.where(sf[:, None] > 0, np.clip(np.rint(q), 0, L), 0)
+        codes[:, 64 * g:64 * (g + 1)] = c.astype(np.uint8)
+        sb[:, g, 0], sb[:, g, 1] = s16, b16
+    if bits == 8:
+        return codes, sb
+    if bits != 4:
+        raise ValueError(f"bits {bits}")
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), sb
+
+
 def seal_block(k: np.ndarray, v: np.ndarray, rank: int, n_resid: int, omega: np.ndarray,
-               power_iters: int = DEFAULT_POWER_ITERS) -> dict:
+               power_iters: int = DEFAULT_POWER_ITERS, resid_bits: int = 16) -> dict:
     """One block (256 x 128 keys and values, fp16 values) sealed into the pool
     arrays of one slot and KV head: anchors, U (255 x r), V_K, V_V (r x 128),
-    residual positions and rows.  Stored factors are fp16; `fp64` holds the
+    residual positions and rows (fp16, or with resid_bits 8 / 4 in the
+    group-quantised format: codes in resid_k / resid_v, (scale, bias) in
+    resid_k_sb / resid_v_sb).  Stored factors are fp16; `fp64` holds the
     unrounded factors and the singular values."""
     assert 1 <= rank <= min(ROWS, 2 * D) and 0 <= n_resid <= ROWS
     a_k, a_v, a = joint_delta(k, v)
@@ -118,7 +164,7 @@ def seal_block(k: np.ndarray, v: np.ndarray, rank: int, n_resid: int, omega: np.
     err = residual_errors(k, a_k, u16, vk16)
     pos = select_residuals(err, n_resid)
     k16, v16 = np.asarray(k, np.float16), np.asarray(v, np.float16)
-    return {
+    out = {
         "anchor_k": k16[0].copy(), "anchor_v": v16[0].copy(),
         "u": u16, "vk": vk16, "vv": vv16,
         "resid_pos": pos.astype(np.uint8),
@@ -126,6 +172,12 @@ def seal_block(k: np.ndarray, v: np.ndarray, rank: int, n_resid: int, omega: np.
         "err": err,
         "fp64": {"us": us, "s": s, "wt": wt},
     }
+    if resid_bits in (8, 4):
+        out["resid_k"], out["resid_k_sb"] = quantize_rows(k16[pos], resid_bits)
+        out["resid_v"], out["resid_v_sb"] = quantize_rows(v16[pos], resid_bits)
+    elif resid_bits != 16:
+        raise ValueError(f"resid_bits {resid_bits}")
+    return out
 
 
 def reconstruct(sealed: dict):
@@ -135,8 +187,14 @@ def reconstruct(sealed: dict):
     k = np.vstack([sealed["anchor_k"], np.asarray(sealed["anchor_k"], np.float64) + u @ np.asarray(sealed["vk"], np.float64)])
     v = np.vstack([sealed["anchor_v"], np.asarray(sealed["anchor_v"], np.float64) + u @ np.asarray(sealed["vv"], np.float64)])
     pos = np.asarray(sealed["resid_pos"], np.int64)
-    k[pos] = np.asarray(sealed["resid_k"], np.float64)
-    v[pos] = np.asarray(sealed["resid_v"], np.float64)
+    if "resid_k_sb" in sealed:
+        from .dkv_oracle import dequantize_rows
+        bits = 8 if np.asarray(sealed["resid_k"]).shape[-1] == D else 4
+        k[pos] = dequantize_rows(sealed["resid_k"], sealed["resid_k_sb"], bits)
+        v[pos] = dequantize_rows(sealed["resid_v"], sealed["resid_v_sb"], bits)
+    else:
+        k[pos] = np.asarray(sealed["resid_k"], np.float64)
+        v[pos] = np.asarray(sealed["resid_v"], np.float64)
     return k, v
 
 

@@ -46,11 +46,11 @@ def lib():
     return L
 
 
-def _seal_gpu(L, inp, rank, n_resid, power_iters, slots=None, n_slots=None, layout="records"):
+def _seal_gpu(L, inp, rank, n_resid, power_iters, slots=None, n_slots=None, layout="records", resid_format=0):
     nb, H = inp.k.shape[:2]
     slots = np.arange(nb, dtype=np.int32) if slots is None else np.asarray(slots, np.int32)
     n_slots = nb if n_slots is None else n_slots
-    pool = L.Pool.empty(n_slots, H, rank, n_resid, DEV, layout)
+    pool = L.Pool.empty(n_slots, H, rank, n_resid, DEV, layout, resid_format)
     k = torch.from_numpy(inp.k).to(DEV)
     v = torch.from_numpy(inp.v).to(DEV)
     om = torch.from_numpy(np.ascontiguousarray(inp.omega)).to(DEV)
@@ -334,3 +334,47 @@ def test_share_bases_against_oracle(lib, capacity, threshold):
         blk = int(np.where(slot_of == s)[0][0])
         assert np.array_equal(svk[j], P["vk"][blk]) and np.array_equal(svv[j], P["vv"][blk])
     assert len(opener) <= capacity
+
+
+@pytest.mark.parametrize("fmt,bits", [(1, 8), (2, 4)])
+def test_seal_quantised_residuals(lib, fmt, bits):
+    """Sealing into a pool of 8- or 4-bit residual rows: the positions are the
+    fp16 sealing's (same kernel path), and the codes and (scale, bias) pairs
+    equal the oracle's quantisation of those rows bit for bit; the sealed blocks
+    then decode like the oracle's."""
+    say(f"[seal] {bits}-bit residual rows")
+    nb, H, G, W = 14, 2, 6, 64
+    inp = synth.make_seal_input(2400 + bits, nb, H, width=40)
+    rank, R = 32, 40
+    ref16, om = _seal_gpu(lib, inp, rank, R, 2)
+    out, _ = _seal_gpu(lib, inp, rank, R, 2, resid_format=fmt)
+    assert np.array_equal(out["resid_pos"], ref16["resid_pos"]) and np.array_equal(out["u"], ref16["u"])
+    for b in range(nb):
+        for h in range(H):
+            pos = out["resid_pos"][b, h].astype(np.int64)
+            for n, src in (("k", inp.k), ("v", inp.v)):
+                codes, sb = S.quantize_rows(src[b, h][pos], bits)
+                assert np.array_equal(out[f"resid_{n}"][b, h], codes), (b, h, n)
+                assert out[f"resid_{n}_sb"][b, h].tobytes() == sb.tobytes(), (b, h, n)
+    # decode the quantised pool against the oracle's decode of the same arrays
+    rng = np.random.default_rng(2401)
+    q = rng.standard_normal((1, H * G, 128)).astype(np.float16)
+    win_k = rng.standard_normal((1, H, W, 128)).astype(np.float16)
+    win_v = rng.standard_normal((1, H, W, 128)).astype(np.float16)
+    table = np.arange(nb, dtype=np.int32)[None]
+    nblk = np.array([nb], np.int32)
+    wlen = np.array([W], np.int32)
+    scale = 128 ** -0.5
+    P = {n: out[n] for n in ("anchor_k", "anchor_v", "u", "vk", "vv", "resid_k", "resid_v", "resid_pos",
+                             "resid_k_sb", "resid_v_sb")}
+    P["resid_format"] = fmt
+    o_ref, lse_ref, _ = oracle.decode(P, q, win_k, win_v, table, nblk, wlen, H, nb, scale)
+    gpu_pool = lib.Pool.from_numpy(P, DEV)
+    batch = lib.Batch.from_numpy(q, win_k, win_v, table, nblk, wlen, device=DEV)
+    lib.route_keys(gpu_pool)
+    o, lse, _ = lib.decode(gpu_pool, batch, nb, scale)
+    torch.cuda.synchronize()
+    d_o = np.max(np.abs(o.cpu().numpy().astype(np.float64) - o_ref))
+    d_l = np.max(np.abs(lse.cpu().numpy().astype(np.float64) - lse_ref))
+    say(f"[seal]   decode max |d out| {d_o:.2e}, max |d lse| {d_l:.2e}")
+    assert d_o <= 1e-2 and d_l <= 1e-3

@@ -322,3 +322,104 @@ def test_assign_bases_special_cases():
     assert kind[1] == 1 and abs(energy[1] - 1.0) < 1e-12 and np.allclose(us[1], copy[1][0])
     with pytest.raises(ValueError):
         S.assign_bases(blocks, 0, 0.5)
+
+
+# ---------------------------------------------------------------------------
+# Writing residual rows in the 8- and 4-bit group-quantised format
+# ---------------------------------------------------------------------------
+
+from oracle.dkv_oracle import dequantize_rows   # noqa: E402  (the read side, pinned in test_oracle_pins)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_round_trip_within_half_step(bits):
+    """Dequantised (by the read side) rows are within half a scale step of the
+    fp16 rows, for rows of every spread and sign; the grid spans each group."""
+    rng = np.random.default_rng(60 + bits)
+    rows = np.vstack([rng.standard_normal((40, 128)) * sc + off
+                      for sc, off in ((1, 0), (0.01, 3), (30, -100), (1e-3, 0))]).astype(np.float16)
+    codes, sb = S.quantize_rows(rows, bits)
+    assert codes.shape == (rows.shape[0], 128 if bits == 8 else 64) and sb.shape == (rows.shape[0], 2, 2)
+    back = dequantize_rows(codes, sb, bits)
+    step = np.repeat(sb[:, :, 0].astype(np.float64), 64, axis=1)
+    assert np.all(np.abs(back - rows.astype(np.float64)) <= step / 2 * (1 + 1e-5) + 1e-12)
+    L = (1 << bits) - 1
+    x = rows.astype(np.float64)
+    for g in range(2):
+        lo, hi = x[:, 64 * g:64 * g + 64].min(1), x[:, 64 * g:64 * g + 64].max(1)
+        assert np.array_equal(sb[:, g, 1].astype(np.float64), lo)               # bias: the group's minimum
+        assert np.all(sb[:, g, 0].astype(np.float64) * L >= hi - lo)            # the grid reaches the maximum
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_codes_are_nearest(bits):
+    """Each code is a nearest grid point: no neighbouring code reconstructs the
+    value better (up to the fp32 rounding the decision is taken in)."""
+    rng = np.random.default_rng(70 + bits)
+    rows = (rng.standard_normal((64, 128)) * 2).astype(np.float16)
+    codes, sb = S.quantize_rows(rows, bits)
+    L = (1 << bits) - 1
+    c = codes.astype(np.int64) if bits == 8 else np.stack([codes & 15, codes >> 4], -1).reshape(64, 128).astype(np.int64)
+    s_ = np.repeat(sb[:, :, 0].astype(np.float64), 64, axis=1)
+    b_ = np.repeat(sb[:, :, 1].astype(np.float64), 64, axis=1)
+    x = rows.astype(np.float64)
+    err = np.abs(x - (b_ + c * s_))
+    for d in (-1, 1):
+        cn = np.clip(c + d, 0, L)
+        assert np.all(err <= np.abs(x - (b_ + cn * s_)) + 1e-6 * s_)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_rows_on_the_grid_are_exact(bits):
+    """Rows that lie on a grid (fp16 bias, a power-of-two scale, codes 0 and L
+    present) come back with that grid's scale, bias and codes exactly, and
+    ties between two grid points go to the even code."""
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(80 + bits)
+    s, b = 2.0 ** -6, -1.0
+    c = rng.integers(0, L + 1, size=(8, 128))
+    c[:, 0], c[:, 1], c[:, 64], c[:, 65] = 0, L, 0, L
+    rows = (b + c * s).astype(np.float16)
+    assert np.array_equal(rows.astype(np.float64), b + c * s)
+    codes, sb = S.quantize_rows(rows, bits)
+    assert np.all(sb[:, :, 0] == np.float16(s)) and np.all(sb[:, :, 1] == np.float16(b))
+    got = codes.astype(np.int64) if bits == 8 else np.stack([codes & 15, codes >> 4], -1).reshape(8, 128)
+    assert np.array_equal(got, c)
+    # ties: halfway values round to the even code
+    t = np.zeros((1, 128))
+    t[0, :64] = b + np.array([0, L] + [2.5, 3.5, 4.5] * 20 + [1.0, 1.5])[:64] * s
+    t[0, 64:] = b
+    codes, sb = S.quantize_rows(t.astype(np.float16), bits)
+    got = codes.astype(np.int64) if bits == 8 else np.stack([codes & 15, codes >> 4], -1).reshape(1, 128)
+    assert list(got[0, 2:5]) == [2, 4, 4] and got[0, 63] == 2 and got[0, 62] == 1
+    assert np.all(got[0, 64:] == 0) and sb[0, 1, 0] == 0                      # a constant group: scale 0
+
+
+def test_quantize_nibble_order():
+    """4-bit codes: dimension 2j in the low nibble of byte j, 2j + 1 in the high
+    one (the read side's order), on a row whose codes are d mod 16."""
+    d = np.arange(128)
+    rows = (-2.0 + (d % 16) * 0.25)[None, :].astype(np.float16)
+    codes, sb = S.quantize_rows(rows, 4)
+    assert np.all(sb[0, :, 0] == np.float16(0.25)) and np.all(sb[0, :, 1] == np.float16(-2.0))
+    want = ((2 * np.arange(64)) % 16) | (((2 * np.arange(64) + 1) % 16) << 4)
+    assert np.array_equal(codes[0], want.astype(np.uint8))
+
+
+def test_seal_block_quantised_residuals():
+    """A block sealed with 8- or 4-bit residual rows stores the quantised fp16
+    residual rows of the fp16 seal (same positions), and reconstructs within
+    half a step of them."""
+    inp = synth.make_seal_input(91, 1, 1, width=40)
+    k, v = inp.k[0, 0], inp.v[0, 0]
+    om = inp.omega[:, :40]
+    ref = S.seal_block(k, v, 32, 24, om)
+    for bits in (8, 4):
+        q = S.seal_block(k, v, 32, 24, om, resid_bits=bits)
+        assert np.array_equal(q["resid_pos"], ref["resid_pos"]) and np.array_equal(q["u"], ref["u"])
+        ck, sk = S.quantize_rows(ref["resid_k"], bits)
+        assert np.array_equal(q["resid_k"], ck) and np.array_equal(q["resid_k_sb"], sk)
+        kk, _ = S.reconstruct(q)
+        pos = ref["resid_pos"].astype(np.int64)
+        step = np.repeat(q["resid_k_sb"][:, :, 0].astype(np.float64), 64, axis=1)
+        assert np.all(np.abs(kk[pos] - ref["resid_k"].astype(np.float64)) <= step / 2 * (1 + 1e-5))
