@@ -229,7 +229,8 @@ def test_seal_blocks_validates(clib):
     assert seal(slots=None) == L.DKV_ERR_INVALID_ARG
     assert seal(om=None) == L.DKV_ERR_INVALID_ARG
     assert seal(sk=L.View(FAKE + 2, 0, 0)) == L.DKV_ERR_UNSUPPORTED   # source rows not 16-byte aligned
-    assert seal(pool=_pool(resid_format=L.RESID_INT8)) == L.DKV_ERR_UNSUPPORTED
+    assert seal(pool=_pool(resid_format=L.RESID_INT8)) == L.DKV_ERR_INVALID_ARG   # codes without (scale, bias)
+    assert seal(pool=_pool(resid_format=7)) == L.DKV_ERR_INVALID_ARG
     assert seal(pool=_pool(head_dim=64)) == L.DKV_ERR_UNSUPPORTED
     assert seal(width=81) == L.DKV_ERR_UNSUPPORTED and b"width" in clib.dkv_last_error()
 
