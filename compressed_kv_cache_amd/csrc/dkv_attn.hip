@@ -429,38 +429,6 @@ __device__ __forceinline__ void load_qtile(const uint8_t* kq, const uint8_t* vq,
   }
 }
 
-// two bytes (low halves of each 16-bit half of w) -> two exact fp16 integers
-__device__ __forceinline__ uint32_t bytes2_to_h2(uint32_t w) {
-  // 0x6400 | b is the fp16 1024 + b; subtracting 1024 is exact
-  const uint32_t m = (w & 0x00FF00FFu) | 0x64006400u;
-  const v2h x = __builtin_bit_cast(v2h, m) - (v2h){(f16)1024.0f, (f16)1024.0f};
-  return __builtin_bit_cast(uint32_t, x);
-}
-
-// 8 codes of a lane -> v8h of exact fp16 integers (dimension order)
-template <int BITS>
-__device__ __forceinline__ v8h codes_to_h8(typename std::conditional<BITS == 8, uint2, uint32_t>::type c) {
-  uint32_t w[4];
-  if constexpr (BITS == 8) {
-    // bytes b0..b3 of c.x: pairs (b0, b1) and (b2, b3)
-    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c010c00u));
-    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c030c02u));
-    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c010c00u));
-    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c030c02u));
-  } else {
-    // nibbles: dimension 2j = low nibble of byte j, 2j + 1 = high nibble
-    const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
-    // lo byte j -> low half, hi byte j -> high half
-    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c040c00u));
-    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c050c01u));
-    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c060c02u));
-    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c070c03u));
-  }
-  return __builtin_bit_cast(v8h, w);
-}
-
-__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
-__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
 
 // One softmax step over two quantised 16-row tiles (b optional).  Q0, Q1: this
 // lane's head's query sums over dimensions 0..63 and 64..127.
@@ -1918,22 +1886,33 @@ bool al_view(const dkv_view& v, int esz, int a) {
   return al(v.ptr, a) && (v.slot_stride * esz) % a == 0 && (v.head_stride * esz) % a == 0;
 }
 
-// The streaming launch (dkv_stream.hip) takes pools of rotated keys with fp16
-// residual rows, ranks that are multiples of 8 up to 56, residual counts that
-// are multiples of 4, 16-byte aligned fp16 arrays and 4-byte aligned
-// positions.  DKV_STREAM=0 in the environment selects the classic launch.
+// The streaming launch (dkv_stream.hip) takes pools of rotated keys with
+// residual rows in any format, ranks that are multiples of 8 up to 56,
+// residual counts that are multiples of 4, 16-byte aligned row, code and
+// (scale, bias) arrays and 4-byte aligned positions.  DKV_STREAM=0 in the
+// environment selects the classic launch.
 bool stream_eligible(const dkv_pool* P, const dkv_batch* B) {
   static const int enabled = [] {
     const char* e = getenv("DKV_STREAM");
     return (e && e[0] == '0') ? 0 : 1;
   }();
-  if (!enabled || P->rope_freq || P->basis_of || P->resid_format != DKV_RESID_FP16) return false;
+  if (!enabled || P->rope_freq || P->basis_of) return false;
   if (P->rank % 8 != 0 || P->rank > 56 || P->n_resid % 4 != 0) return false;
   if (!al_view(P->anchor_k, 2, 16) || !al_view(P->anchor_v, 2, 16) || !al_view(P->u, 2, 16) ||
       !al_view(P->vk, 2, 16) || !al_view(P->vv, 2, 16))
     return false;
-  if (P->n_resid > 0 && (!al_view(P->resid_k, 2, 16) || !al_view(P->resid_v, 2, 16) || !al_view(P->resid_pos, 1, 4)))
-    return false;
+  if (P->n_resid > 0) {
+    if (!al_view(P->resid_pos, 1, 4)) return false;
+    if (P->resid_format == DKV_RESID_FP16) {
+      if (!al_view(P->resid_k, 2, 16) || !al_view(P->resid_v, 2, 16)) return false;
+    } else if (P->resid_format == DKV_RESID_INT8 || P->resid_format == DKV_RESID_INT4) {
+      if (!al_view(P->resid_k, 1, 16) || !al_view(P->resid_v, 1, 16) || !al_view(P->resid_k_sb, 2, 16) ||
+          !al_view(P->resid_v_sb, 2, 16))
+        return false;
+    } else {
+      return false;
+    }
+  }
   return al(B->q, 16) && al(B->win_k, 16) && al(B->win_v, 16);
 }
 
@@ -2324,10 +2303,11 @@ constexpr bool kLayersFoldWindow = false;
 // Streams of the layer-batched streaming launches: at most this many one-wave
 // workgroups (eight per CU of the MI355X's 256).
 constexpr int kStreamMaxWaves = 2048;
-// Work items of the streams: window rows and residual rows in items of at most
-// these many rows; each routed block's low-rank part is an item of its own.
-constexpr int kStreamWinRows = 128;
-constexpr int kStreamResRows = 64;
+// Work items of the streams: a unit's window rows in items of at most
+// kStreamWinRows rows, each routed block's low-rank part, and its residual rows
+// (one item); the schedule splits window and residual items where a wave's
+// share ends (at most once per wave boundary).
+constexpr int kStreamWinRows = 1024;
 
 static bool layers_stream(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
   if (top_k < 1) return false;
@@ -2336,40 +2316,226 @@ static bool layers_stream(const dkv_pool* pools, const dkv_batch* batches, int n
   return true;
 }
 
-// the streams' work items of one unit: its window items, then per routed rank
-// a low-rank item and the residual items
-static int64_t stream_unit_items(const dkv_pool* pool, const dkv_batch* batch, int top_k) {
-  const int64_t nwin = (batch->window + kStreamWinRows - 1) / kStreamWinRows;
-  const int64_t nres = (pool->n_resid + kStreamResRows - 1) / kStreamResRows;
-  return nwin + (int64_t)top_k * (1 + nres);
-}
+// The streams' schedule: every unit's work items in order (layer, batch row,
+// kv head; its window items, then per routed rank the block's low-rank item
+// and its residual item), cut into n_waves contiguous segments of about equal
+// cost.  A window or residual item that a segment's end falls inside is split
+// there, at a page boundary (16 fp16 rows, 32 rows of codes); a low-rank item
+// is not split: when one would straddle the end, the block's residual item
+// goes first and is split instead, else the low-rank item stays with the
+// segment if it holds the item's middle.  Each segment's end is recomputed as
+// the walk goes (the remaining cost over the remaining waves), so that the
+// last segment gets its share.  A wave's consecutive items of one unit form a
+// run: one attention state, one partial.
+struct StreamSchedule {
+  std::vector<int32_t> words;        // [n_waves + 1] item offsets, four words per item, parts per (layer, unit)
+  int n_waves = 0;
+  int64_t n_items = 0;
+  std::vector<int32_t> layer_parts;  // per layer: the most partials a unit of it has
+};
 
-static int64_t stream_sched_items(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
-  int64_t n = 0;
+// fewest cost units per wave (about four K/V page pairs), so that small steps
+// run on fewer, fuller waves
+constexpr int64_t kStreamMinShare = 15000;
+
+// false when the shapes exceed the schedule's word formats (or the layers'
+// unit counts differ)
+static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k,
+                                  StreamSchedule& S) {
+  const dkv_pool& p0 = pools[0];
+  const dkv_batch& b0 = batches[0];
+  const int64_t units = (int64_t)b0.batch * p0.n_kv_heads;
+  if (n_layers > 0xFFFF || top_k > 0xFFFF || b0.batch > 0xFFFF || p0.n_kv_heads > 0xFFFF || units < 0)
+    return false;
+  int64_t n_base = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((int64_t)batches[l].batch * pools[l].n_kv_heads != units || batches[l].window < 0 ||
+        batches[l].window > 0x7FFFFFFF - kStreamWinRows)
+      return false;
+    const int64_t nwin = (batches[l].window + kStreamWinRows - 1) / kStreamWinRows;
+    n_base += units * (nwin + (int64_t)top_k * (1 + (pools[l].n_resid > 0 ? 1 : 0)));
+  }
+  if (n_base > 0x3FFFFFFF - kStreamMaxWaves) return false;
+  struct Item {
+    uint32_t w[4];
+    int64_t cost;   // the whole item's, its entry (and run start) included
+    int32_t unit;   // layer * units + unit
+    int32_t pairs;  // splittable items: their K/V page pairs (0: not splittable)
+    int32_t rpp;    // rows per pair
+    int64_t pair;   // cost per pair
+  };
+  // An item's cost, in stream clock cycles (fitted to the streams' measured
+  // wave durations per page kind): a fixed cost per page (kPage: a memory
+  // latency over the ring depth and an issue slot) plus its own arithmetic --
+  // a K page's scores and softmax, a V page's products, a V_K or V_V page's
+  // tile (the first V_K page also builds the position mask and q . a_k), a U
+  // page by how many 32-position groups it holds (4, 2, 1 for ranks up to 16,
+  // 32, 64) and its 16-wide rank tiles, a quantised K or V page's 32 rows --
+  // plus the entry into each item and the start of each unit's run.
+  const int64_t kPage = 1500, kK = 500, kV = 110, kVK = 650, kVK0 = 700, kVV = 700;
+  const int64_t kU[5] = {0, 833, 1074, 0, 2875}, kUTile = 250;
+  const int64_t kQK8 = 3500, kQV8 = 2554, kQK4 = 2000, kQV4 = 1391;
+  const int64_t kItemEntry = 4700, kRunStart = 4700;
+  std::vector<Item> items;
+  items.reserve((size_t)n_base);
+  for (int l = 0; l < n_layers; ++l) {
+    const int r = pools[l].rank, R = pools[l].n_resid, W = batches[l].window, fmt = pools[l].resid_format;
+    const int nq = (r + 15) / 16, mu = r <= 16 ? 4 : (r <= 32 ? 2 : 1), nu = 8 / mu;
+    const int nq_min = mu == 4 ? 1 : (mu == 2 ? 2 : 3);
+    const int64_t u_page = kPage + kU[mu] + (nq > nq_min ? nq - nq_min : 0) * kUTile;
+    const int64_t lowrank = kItemEntry + nq * (2 * kPage + kVK + kVV) + kVK0 + nu * u_page;
+    const int64_t kv_pair = 2 * kPage + kK + kV;
+    const int64_t res_pair = fmt == DKV_RESID_INT8 ? 2 * kPage + kQK8 + kQV8
+                           : fmt == DKV_RESID_INT4 ? 2 * kPage + kQK4 + kQV4 : kv_pair;
+    const int res_rpp = fmt == DKV_RESID_FP16 ? 16 : 32;
+    for (int64_t u = 0; u < units; ++u) {
+      const uint32_t bh = (uint32_t)(u / p0.n_kv_heads) | ((uint32_t)(u % p0.n_kv_heads) << 16);
+      const int32_t ug = (int32_t)(l * units + u);
+      const size_t first = items.size();
+      for (int r0 = 0; r0 < W; r0 += kStreamWinRows) {
+        const int rows = W - r0 < kStreamWinRows ? W - r0 : kStreamWinRows;
+        const int pairs = (rows + 15) / 16;
+        items.push_back({{(uint32_t)l | (kItemWin << 16), (uint32_t)r0, bh, (uint32_t)rows << 16},
+                         kItemEntry + pairs * kv_pair, ug, pairs, 16, kv_pair});
+      }
+      for (int k = 0; k < top_k; ++k) {
+        items.push_back({{(uint32_t)l | (kItemLowRank << 16), (uint32_t)k, bh, 0u}, lowrank, ug, 0, 0, 0});
+        if (R > 0) {
+          const int pairs = (R + res_rpp - 1) / res_rpp;
+          items.push_back({{(uint32_t)l | (kItemResid << 16), (uint32_t)k, bh, (uint32_t)R << 16},
+                           kItemEntry + pairs * res_pair, ug, pairs, res_rpp, res_pair});
+        }
+      }
+      if (items.size() > first) items[first].cost += kRunStart;
+    }
+  }
+  double base = 0.0;
+  for (const Item& it : items) base += (double)it.cost;
+  const int64_t want = (int64_t)std::ceil(base / (double)kStreamMinShare);
+  const int n_waves = (int)std::max<int64_t>(1, std::min<int64_t>(kStreamMaxWaves, want));
+  // the walk: cum is the cost emitted so far, w the wave being filled, end its
+  // end (the remaining cost, the expected splits' entries included, over the
+  // remaining waves)
+  std::vector<Item> cut;
+  std::vector<int32_t> wave_of;
+  cut.reserve(items.size() + (size_t)n_waves);
+  wave_of.reserve(items.size() + (size_t)n_waves);
+  double cum = 0.0;
+  int w = 0;
+  int64_t splits = 0;
+  auto end_of = [&](int wave, double c) {
+    if (wave + 1 >= n_waves) return (double)INFINITY;
+    const int rem = n_waves - wave;
+    const double rate = wave > 0 ? std::min(1.0, (double)splits / wave) : 0.5;
+    const double est = base + (double)splits * kItemEntry + rate * (rem - 1) * kItemEntry;
+    return c + (est - c) / rem;
+  };
+  double end = end_of(0, 0.0);
+  auto advance = [&]() {
+    if (w + 1 < n_waves) ++w;
+    end = end_of(w, cum);
+  };
+  auto emit = [&](const Item& it) {
+    cut.push_back(it);
+    wave_of.push_back(w);
+    cum += (double)it.cost;
+  };
+  for (size_t i = 0; i < items.size(); ++i) {
+    for (;;) {
+      Item& it = items[i];
+      if (cum + (double)it.cost <= end) {
+        emit(it);
+        break;
+      }
+      if (it.pairs <= 1) {
+        if (i + 1 < items.size() && items[i + 1].pairs > 1 && items[i + 1].unit == it.unit &&
+            cum + (double)items[i + 1].cost > end) {
+          // the block's residual item fills the segment; the low-rank item follows
+          std::swap(items[i], items[i + 1]);
+          continue;
+        }
+        if (cum + 0.5 * (double)it.cost <= end) {
+          emit(it);
+          advance();
+          break;
+        }
+        advance();
+        continue;
+      }
+      // the pairs that fit before the segment's end stay in wave w
+      const int64_t fixed = it.cost - (int64_t)it.pairs * it.pair;  // the entry (and run start)
+      const int m = (int)std::lround((end - cum - (double)fixed) / (double)it.pair);
+      if (m >= it.pairs) {
+        emit(it);
+        break;
+      }
+      if (m <= 0) {
+        advance();
+        continue;
+      }
+      Item a = it;
+      const int rows_a = m * it.rpp;
+      const int rows_all = (int)(it.w[3] >> 16);
+      a.w[3] = (uint32_t)rows_a << 16;
+      a.pairs = m;
+      a.cost = fixed + (int64_t)m * it.pair;
+      emit(a);
+      ++splits;
+      // the rest, from the row after the first part's, in the next wave
+      if ((it.w[0] >> 16) == (uint32_t)kItemWin)
+        it.w[1] += (uint32_t)rows_a;
+      else
+        it.w[1] += (uint32_t)rows_a << 16;
+      it.w[3] = (uint32_t)(rows_all - rows_a) << 16;
+      it.pairs -= m;
+      it.cost = kItemEntry + (int64_t)it.pairs * it.pair;
+      advance();
+    }
+  }
+  // runs: the flags, each run's partial index within its unit, the units' counts
+  std::vector<int32_t> unit_parts((size_t)(n_layers * units), 0);
+  for (size_t i = 0; i < cut.size(); ++i) {
+    const bool first = i == 0 || wave_of[i - 1] != wave_of[i] || cut[i - 1].unit != cut[i].unit;
+    const bool last = i + 1 == cut.size() || wave_of[i + 1] != wave_of[i] || cut[i + 1].unit != cut[i].unit;
+    if (first) ++unit_parts[(size_t)cut[i].unit];
+    const int part = unit_parts[(size_t)cut[i].unit] - 1;
+    cut[i].w[0] |= (first ? 1u << 24 : 0u) | (last ? 2u << 24 : 0u);
+    cut[i].w[3] |= (uint32_t)part;
+  }
+  S.n_waves = n_waves;
+  S.n_items = (int64_t)cut.size();
+  S.layer_parts.assign((size_t)n_layers, 1);
   for (int l = 0; l < n_layers; ++l)
-    n += (int64_t)batches[l].batch * pools[l].n_kv_heads * stream_unit_items(&pools[l], &batches[l], top_k);
-  return n;
+    for (int64_t u = 0; u < units; ++u)
+      S.layer_parts[(size_t)l] = std::max(S.layer_parts[(size_t)l], unit_parts[(size_t)(l * units + u)]);
+  S.words.clear();
+  S.words.reserve((size_t)n_waves + 1 + 4 * cut.size() + unit_parts.size());
+  size_t i = 0;
+  for (int wv = 0; wv < n_waves; ++wv) {
+    S.words.push_back((int32_t)i);
+    while (i < cut.size() && wave_of[i] == wv) ++i;
+  }
+  S.words.push_back((int32_t)i);
+  for (const Item& it : cut)
+    for (int k = 0; k < 4; ++k) S.words.push_back((int32_t)it.w[k]);
+  S.words.insert(S.words.end(), unit_parts.begin(), unit_parts.end());
+  return true;
 }
 
-static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k, bool streams) {
-  const size_t min_parts = streams ? (size_t)stream_unit_items(pool, batch, top_k) : 0;
+static size_t layer_region_bytes(const dkv_pool* pool, const dkv_batch* batch, int top_k, size_t min_parts) {
   return align256(decode_layout(pool, batch, top_k, kLayersFoldWindow, min_parts).total);
-}
-
-// the streams' schedule: wave offsets, four words per item, a part count per (layer, unit)
-static size_t stream_sched_words(const dkv_pool* pools, const dkv_batch* batches, int n_layers, int top_k) {
-  const int64_t items = stream_sched_items(pools, batches, n_layers, top_k);
-  const int64_t waves = items < kStreamMaxWaves ? items : kStreamMaxWaves;
-  return (size_t)(waves + 1 + 4 * items + (int64_t)n_layers * batches[0].batch * pools[0].n_kv_heads);
 }
 
 size_t dkv_decode_layers_workspace_size(const dkv_pool* pools, const dkv_batch* batches, int32_t n_layers,
                                         int32_t top_k) {
   if (!pools || !batches || n_layers < 1 || top_k < 0) return 0;
-  const bool streams = layers_stream(pools, batches, n_layers, top_k);
+  StreamSchedule S;
+  const bool streams = layers_stream(pools, batches, n_layers, top_k) &&
+                       build_stream_schedule(pools, batches, n_layers, top_k, S);
   size_t total = kCtrlHeaderBytes;
-  for (int l = 0; l < n_layers; ++l) total += layer_region_bytes(&pools[l], &batches[l], top_k, streams);
-  if (streams) total += align256(stream_sched_words(pools, batches, n_layers, top_k) * 4);
+  for (int l = 0; l < n_layers; ++l)
+    total += layer_region_bytes(&pools[l], &batches[l], top_k, streams ? (size_t)S.layer_parts[(size_t)l] : 0);
+  if (streams) total += align256(S.words.size() * 4);
   return total;
 }
 
@@ -2399,6 +2565,11 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
   size_t shm = 0, off = kCtrlHeaderBytes;
   unsigned char* ws = (unsigned char*)workspace;
   const bool streams = layers_stream(pools, batches, n_layers, top_k);
+  StreamSchedule S;
+  if (streams && !build_stream_schedule(pools, batches, n_layers, top_k, S)) {
+    free(host);
+    return fail(DKV_ERR_INVALID_ARG, "the layers' shapes exceed the streams' schedule");
+  }
   for (int l = 0; l < n_layers && s == DKV_OK; ++l) {
     const dkv_pool* pool = &pools[l];
     const dkv_batch* batch = &batches[l];
@@ -2427,7 +2598,7 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
       break;
     }
     size_t shm_l = 0;
-    const size_t min_parts = streams ? (size_t)stream_unit_items(pool, batch, top_k) : 0;
+    const size_t min_parts = streams ? (size_t)S.layer_parts[(size_t)l] : 0;
     if ((s = build_decode_args(pool, batch, top_k, scale, ws + off, (uint32_t*)workspace, outs[l], out_lses[l],
                                out_idxs ? out_idxs[l] : nullptr, host[l].D, shm_l, kLayersFoldWindow,
                                /*row_merges=*/false, min_parts)))
@@ -2449,96 +2620,11 @@ dkv_status dkv_decode_layers_prepare(const dkv_pool* pools, const dkv_batch* bat
       D.n_items = D.n_route;
     }
     if (shm_l > shm) shm = shm_l;
-    off += layer_region_bytes(pool, batch, top_k, streams);
+    off += layer_region_bytes(pool, batch, top_k, min_parts);
   }
-  // The streams' schedule: every unit's work items in order (layer, batch row,
-  // kv head; window items, then per routed rank its low-rank item and its
-  // residual items), cut into n_waves contiguous segments of about equal cost
-  // (bytes, plus a fixed cost per page).  A wave's consecutive items of one
-  // unit form a run: one attention state, one partial.
-  std::vector<int32_t> sched;
-  int n_waves = 0;
-  int64_t n_sched = 0;
-  if (s == DKV_OK && streams) {
-    const int units = b0.batch * p0.n_kv_heads;
-    n_sched = stream_sched_items(pools, batches, n_layers, top_k);
-    if (n_sched > 0x3FFFFFFF || n_layers > 0xFFFF || top_k > 0xFFFF || b0.batch > 0xFFFF ||
-        p0.n_kv_heads > 0xFFFF || b0.window > 0x7FFFFFFF - kStreamWinRows) {
-      free(host);
-      return fail(DKV_ERR_INVALID_ARG, "too many stream items (%lld)", (long long)n_sched);
-    }
-    struct Item {
-      uint32_t w[4];
-      int64_t cost;
-      int32_t unit;  // layer * units + unit
-    };
-    // An item's cost, in stream clock cycles: every page waits about a memory
-    // latency over the ring depth and an issue slot (kPage), plus its own
-    // arithmetic: a K page's scores and softmax, a V page's products, a V_K or
-    // V_V page's tile (the first V_K page also builds the position mask and
-    // q . a_k), and a U page's 32-position groups, each dearer with more
-    // 16-wide rank tiles.  (Measured per page kind on the streams.)
-    const int64_t kPage = 1500, kK = 500, kV = 110, kVK = 650, kVK0 = 700, kVV = 850;
-    const int64_t kUGroup = 900, kUGroupTile = 250, kItemEntry = 1600;
-    std::vector<Item> items;
-    items.reserve((size_t)n_sched);
-    for (int l = 0; l < n_layers; ++l) {
-      const int r = pools[l].rank, R = pools[l].n_resid, W = batches[l].window;
-      const int nq = (r + 15) / 16, mu = r <= 16 ? 4 : (r <= 32 ? 2 : 1), nu = 8 / mu;
-      const int64_t lowrank = kItemEntry + (2 * nq + nu) * kPage + nq * (kVK + kVV) + kVK0 +
-                              8 * (kUGroup + (nq - 1) * kUGroupTile);
-      for (int u = 0; u < units; ++u) {
-        const uint32_t bh = (uint32_t)(u / p0.n_kv_heads) | ((uint32_t)(u % p0.n_kv_heads) << 16);
-        const int32_t ug = l * units + u;
-        for (int r0 = 0; r0 < W; r0 += kStreamWinRows) {
-          const int rows = W - r0 < kStreamWinRows ? W - r0 : kStreamWinRows;
-          items.push_back({{(uint32_t)l | (kItemWin << 16), (uint32_t)r0, bh, (uint32_t)rows << 16},
-                           kItemEntry + ((rows + 15) / 16) * (2 * kPage + kK + kV), ug});
-        }
-        for (int k = 0; k < top_k; ++k) {
-          items.push_back({{(uint32_t)l | (kItemLowRank << 16), (uint32_t)k, bh, 0u}, lowrank, ug});
-          for (int r0 = 0; r0 < R; r0 += kStreamResRows) {
-            const int rows = R - r0 < kStreamResRows ? R - r0 : kStreamResRows;
-            items.push_back({{(uint32_t)l | (kItemResid << 16), (uint32_t)k | ((uint32_t)r0 << 16), bh,
-                              (uint32_t)rows << 16},
-                             kItemEntry + ((rows + 15) / 16) * (2 * kPage + kK + kV), ug});
-          }
-        }
-      }
-    }
-    n_waves = (int)(n_sched < kStreamMaxWaves ? n_sched : kStreamMaxWaves);
-    int64_t total_cost = 0;
-    for (const Item& it : items) total_cost += it.cost;
-    // item i goes to the wave whose share holds the middle of its cost
-    std::vector<int32_t> wave_of(items.size());
-    int64_t cum = 0;
-    for (size_t i = 0; i < items.size(); ++i) {
-      const double mid = (double)cum + 0.5 * (double)items[i].cost;
-      int w = (int)(mid * n_waves / (double)(total_cost > 0 ? total_cost : 1));
-      wave_of[i] = w < n_waves ? w : n_waves - 1;
-      cum += items[i].cost;
-    }
-    // runs: the flags, each run's partial index within its unit, the units' counts
-    std::vector<int32_t> unit_parts((size_t)n_layers * units, 0);
-    for (size_t i = 0; i < items.size(); ++i) {
-      const bool first = i == 0 || wave_of[i - 1] != wave_of[i] || items[i - 1].unit != items[i].unit;
-      const bool last = i + 1 == items.size() || wave_of[i + 1] != wave_of[i] || items[i + 1].unit != items[i].unit;
-      if (first) ++unit_parts[(size_t)items[i].unit];
-      const int part = unit_parts[(size_t)items[i].unit] - 1;
-      items[i].w[0] |= (first ? 1u << 24 : 0u) | (last ? 2u << 24 : 0u);
-      items[i].w[3] |= (uint32_t)part;
-    }
-    sched.reserve(stream_sched_words(pools, batches, n_layers, top_k));
-    size_t i = 0;
-    for (int w = 0; w < n_waves; ++w) {
-      sched.push_back((int32_t)i);
-      while (i < items.size() && wave_of[i] == w) ++i;
-    }
-    sched.push_back((int32_t)i);
-    for (const Item& it : items)
-      for (int k = 0; k < 4; ++k) sched.push_back((int32_t)it.w[k]);
-    sched.insert(sched.end(), unit_parts.begin(), unit_parts.end());
-  }
+  const std::vector<int32_t>& sched = S.words;
+  const int n_waves = S.n_waves;
+  const int64_t n_sched = S.n_items;
   const size_t sched_off = align256(off);
   if (s == DKV_OK) {
     if (hipMemcpy(table, host, (size_t)n_layers * sizeof(LayerArgs), hipMemcpyHostToDevice) != hipSuccess ||

@@ -32,6 +32,41 @@ constexpr int kLowRankRows = 255;  // tokens 1..255 of a block
 constexpr int kVStride = 132;      // LDS row stride (halves) of 128-wide tiles: conflict-free column reads
 constexpr int kWinChunk = 512;     // window rows per window part (when the window has parts of its own)
 
+// ---- codes of the 8- / 4-bit residual formats ------------------------------
+
+// two bytes (low halves of each 16-bit half of w) -> two exact fp16 integers
+__device__ __forceinline__ uint32_t bytes2_to_h2(uint32_t w) {
+  // 0x6400 | b is the fp16 1024 + b; subtracting 1024 is exact
+  const uint32_t m = (w & 0x00FF00FFu) | 0x64006400u;
+  const v2h x = __builtin_bit_cast(v2h, m) - (v2h){(f16)1024.0f, (f16)1024.0f};
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// 8 codes of a lane -> v8h of exact fp16 integers (dimension order)
+template <int BITS>
+__device__ __forceinline__ v8h codes_to_h8(typename std::conditional<BITS == 8, uint2, uint32_t>::type c) {
+  uint32_t w[4];
+  if constexpr (BITS == 8) {
+    // bytes b0..b3 of c.x: pairs (b0, b1) and (b2, b3)
+    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c010c00u));
+    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.x, 0x0c030c02u));
+    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c010c00u));
+    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(0u, c.y, 0x0c030c02u));
+  } else {
+    // nibbles: dimension 2j = low nibble of byte j, 2j + 1 = high nibble
+    const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+    // lo byte j -> low half, hi byte j -> high half
+    w[0] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c040c00u));
+    w[1] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c050c01u));
+    w[2] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c060c02u));
+    w[3] = bytes2_to_h2(__builtin_amdgcn_perm(hi, lo, 0x0c070c03u));
+  }
+  return __builtin_bit_cast(v8h, w);
+}
+
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
+
 // ----------------------------------------------------------------------------
 // Kernel arguments (plain structs passed by value)
 // ----------------------------------------------------------------------------

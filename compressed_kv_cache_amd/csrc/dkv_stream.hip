@@ -54,6 +54,7 @@ static_assert(kBLds % 16 == 0, "LDS areas are 16-byte aligned");
 static_assert(32 * 64 * 2 + 16 <= kWPage, "a U page (32 mu positions of rank r, mu r <= 64) fits a slot");
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // wait until at most n of this wave's vector-memory operations are outstanding
 __device__ __forceinline__ void wait_vm(int n) {
@@ -223,6 +224,32 @@ __device__ __forceinline__ void lds_u8x4(uint32_t a, uint32_t (&x)[4]) {
       : "memory");
 }
 
+// Eight reads at eight addresses (8-byte, 4-byte, or the transposing reads of
+// 8-bit and 4-bit elements: in each 16-lane group, ds_read_b64_tr_b8 gives
+// lane i byte column i of the eight rows the group's lanes 2 k, 2 k + 1 name,
+// and ds_read_b64_tr_b4 nibble column i of the sixteen rows its lanes name),
+// and four 16-byte reads at b, b + 16, b + 32, b + 48, in one round trip.
+#define DKV_LDS_X8S(NAME, INSN, T)                                                                     \
+  __device__ __forceinline__ void NAME(const uint32_t(&a)[8], uint32_t b, T(&o)[8], v4u(&sb)[4]) {    \
+    asm volatile(INSN " %0, %12\n\t" INSN " %1, %13\n\t" INSN " %2, %14\n\t" INSN " %3, %15\n\t"    \
+                 INSN " %4, %16\n\t" INSN " %5, %17\n\t" INSN " %6, %18\n\t" INSN " %7, %19\n\t"    \
+                 "ds_read_b128 %8, %20\n\t"                                                          \
+                 "ds_read_b128 %9, %20 offset:16\n\t"                                                \
+                 "ds_read_b128 %10, %20 offset:32\n\t"                                               \
+                 "ds_read_b128 %11, %20 offset:48\n\t"                                               \
+                 "s_waitcnt lgkmcnt(0)"                                                               \
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),      \
+                   "=&v"(o[6]), "=&v"(o[7]), "=&v"(sb[0]), "=&v"(sb[1]), "=&v"(sb[2]), "=&v"(sb[3])   \
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),       \
+                   "v"(a[7]), "v"(b)                                                                  \
+                 : "memory");                                                                         \
+  }
+DKV_LDS_X8S(lds_b64x8s, "ds_read_b64", v2u)
+DKV_LDS_X8S(lds_b32x8s, "ds_read_b32", uint32_t)
+DKV_LDS_X8S(lds_trb8x8s, "ds_read_b64_tr_b8", v2u)
+DKV_LDS_X8S(lds_trb4x8s, "ds_read_b64_tr_b4", v2u)
+#undef DKV_LDS_X8S
+
 // OR over the 64 lanes, returned to every lane
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   v |= dpp_u32<0xB1>(0u, v);        // quad_perm 1,0,3,2
@@ -286,7 +313,8 @@ constexpr uint32_t kOutside = 0xFFFFFFF0u;  // a buffer offset past every resour
 // U row is zero) and nq V_V pages; its anchor rows a_k and a_v load with its
 // first V_K page into one of two anchor buffers (items alternate), its
 // residual positions into the position buffer.  A K/V item (window rows, or
-// residual rows of a block) streams K and V pages of 16 rows, alternating.
+// residual rows of a block) streams K and V pages, alternating: 16 fp16 rows
+// (272-byte LDS rows), or 32 rows of 8- or 4-bit codes.
 // ---------------------------------------------------------------------------
 
 enum PageKind { kPageVK = 0, kPageU = 1, kPageK = 2, kPageV = 3, kPageVV = 4 };
@@ -294,9 +322,21 @@ enum PageKind { kPageVK = 0, kPageU = 1, kPageK = 2, kPageV = 3, kPageVV = 4 };
 struct WaveGeom {
   int r, nq;   // rank; its 16-row tiles (V_K and V_V pages)
   int mu, nu;  // 32-position groups per U page (4, 2 or 1: mu r <= 64); U pages (8 / mu)
-  int R, nt;   // low-rank item: residual rows (the mask); K/V item: its rows and their 16-row tiles
+  int R, nt;   // low-rank item: residual rows (the mask); K/V item: its rows and their pages of each side
   bool kv;     // a K/V item
+  int qb;      // K/V item: 0 fp16 rows, 8 or 4: residual rows of 8- or 4-bit codes
 };
+
+// A page of a quantised residual item holds 32 rows of one side (K or V): the
+// rows' codes (128 or 64 bytes each), 16-byte chunk c of row j at chunk
+// position c ^ swz(j) of the row, a swizzle that spreads the page's row and
+// column reads over the LDS banks; then, at kQSbOff, the rows' (scale, bias)
+// pairs, 8 bytes per row.
+constexpr int kQRows = 32;
+constexpr int kQSbOff = 4096;
+static_assert(kQSbOff + kQRows * 8 <= kWPage && kQRows * kD <= kQSbOff, "a quantised page fits a slot");
+__device__ __forceinline__ int q8_swz(int j) { return (j ^ ((j >> 3) << 1)) & 7; }
+__device__ __forceinline__ int q4_swz(int j) { return (j >> 2) & 3; }
 
 __device__ __forceinline__ int u_groups(int r) { return r <= 16 ? 4 : (r <= 32 ? 2 : 1); }
 
@@ -316,24 +356,24 @@ __device__ __forceinline__ void page_kind(const WaveGeom& g, int k, int& kind, i
   }
 }
 
+// The lane's index, opaque to loop-invariant code motion: address arithmetic
+// built on it is recomputed where it is used, not held in registers across the
+// streams' loops (which need those registers for the pages' work).
+__device__ __forceinline__ int lane_id() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Per lane: the source offset of chunk 64 q + lane (q = 0..4) of a 128-wide
 // row page (row p / 17, chunk p % 17 of the row; chunk 16, the row's pad, is
-// kOutside), the same for every row page.
-struct RowOffs {
-  uint32_t off[5];
-};
-
-__device__ __forceinline__ RowOffs row_offs() {
-  const int lane = threadIdx.x & 63;
-  RowOffs o;
-#pragma unroll
-  for (int q = 0; q < 5; ++q) {
-    const int p = 64 * q + lane;
-    const int row = (p * 3856) >> 16;  // p / 17 for p < 17 * 16 * 2
-    const int c = p - 17 * row;
-    o.off[q] = c < 16 ? (uint32_t)(row * 256 + 16 * c) : kOutside;
-  }
-  return o;
+// kOutside), the same for every row page.  (Recomputed at each issue: kept
+// live, the offsets would take registers the pages need.)
+__device__ __forceinline__ uint32_t row_off(int q) {
+  const int p = 64 * q + lane_id();
+  const int row = (p * 3856) >> 16;  // p / 17 for p < 17 * 16 * 2
+  const int c = p - 17 * row;
+  return c < 16 ? (uint32_t)(row * 256 + 16 * c) : kOutside;
 }
 
 // Issue the loads of page k of an item's stream into the ring slot `dst`;
@@ -341,15 +381,39 @@ __device__ __forceinline__ RowOffs row_offs() {
 // buffer loads straight into LDS: each source is a buffer resource sized to
 // its data, and every 16-byte chunk whose offset falls outside it reads as
 // zeros.  bb: the low-rank item's source addresses; rows_k / rows_v: the K/V
-// item's first rows; posdst / ancdst: the position and anchor buffers.
+// item's first rows (codes, for quantised rows, and rows_ks / rows_vs their
+// scale and bias pairs); posdst / ancdst: the position and anchor buffers.
 __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned char* dst, const uint64_t* bb,
-                                          const char* rows_k, const char* rows_v, unsigned char* posdst,
-                                          unsigned char* ancdst, const RowOffs& ro) {
+                                          const char* rows_k, const char* rows_v, const char* rows_ks,
+                                          const char* rows_vs, unsigned char* posdst, unsigned char* ancdst) {
   const int lane = threadIdx.x & 63;
   int kind, i;
   page_kind(g, k, kind, i);
   const int r = g.r;
   int ops = 0;
+  if (g.qb) {
+    // 32 rows of codes (swizzled chunks), then their scale and bias pairs
+    const int cb = g.qb == 8 ? kD : kD / 2;
+    int nvalid = g.R - kQRows * i;
+    nvalid = nvalid > kQRows ? kQRows : nvalid;
+    const __amdgpu_buffer_rsrc_t rs =
+        rsrc_of((kind == kPageK ? rows_k : rows_v) + kQRows * i * cb, (uint32_t)(nvalid * cb));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < cb / 32) {
+        const int p = 64 * q + lane;
+        const uint32_t off = g.qb == 8 ? (uint32_t)(128 * (p >> 3) + 16 * ((p & 7) ^ q8_swz(p >> 3)))
+                                       : (uint32_t)(64 * (p >> 2) + 16 * ((p & 3) ^ q4_swz(p >> 2)));
+        dma16b(rs, off, dst + 1024 * q);
+        ++ops;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rsb =
+        rsrc_of((kind == kPageK ? rows_ks : rows_vs) + kQRows * i * 8, (uint32_t)(nvalid * 8));
+    if (lane < kQRows / 2) dma16b(rsb, (uint32_t)(16 * lane), dst + kQSbOff);
+    ++ops;
+    return ops;
+  }
   if (kind == kPageU) {
     // U rows 32 mu i - 1 .. (row -1 reads as zeros: the anchor), dense, and 16
     // bytes more: the last row's reads run one chunk past its end
@@ -376,7 +440,7 @@ __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned cha
 #pragma unroll
   for (int q = 0; q < 5; ++q) {
     // chunks past the page's 17 * 16 (lanes 16.. of the last load) are not loaded
-    if (q < 4 || lane < 16) dma16b(rs, ro.off[q], dst + 1024 * q);
+    if (q < 4 || lane < 16) dma16b(rs, row_off(q), dst + 1024 * q);
     ++ops;
   }
   if (kind == kPageVK && i == 0) {
@@ -402,6 +466,7 @@ struct SState {
   float m;     // running maximum of the head's scaled scores
   float l;     // this lane's share of sum p (all rows)
   float llr;   // this lane's share of sum p over the current block's low-rank rows (anchor included)
+  float bq0, bq1;  // this lane's share of the quantised rows' bias terms of columns 0..63 and 64..127
 };
 
 // Reference maximum slack: the weights exp(z - m) stay below 2 (m is raised,
@@ -414,8 +479,8 @@ constexpr float kLn2 = 0.69314718f;
 // head's four lanes) if some score exceeds it by more than ln 2, rescaling the
 // state, and return the weights exp(z - m).  The common case needs no
 // cross-lane step.
-template <int NS>
-__device__ __forceinline__ void softmax_step(SState& st, float (&z)[NS], bool lowrank) {
+template <int NS, bool LOWRANK>
+__device__ __forceinline__ void softmax_step(SState& st, float (&z)[NS]) {
   float tm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NS; ++i) tm = fmaxf(tm, z[i]);
@@ -426,10 +491,15 @@ __device__ __forceinline__ void softmax_step(SState& st, float (&z)[NS], bool lo
       const float alpha = (st.m == -INFINITY) ? 0.f : __expf(st.m - mn);
 #pragma unroll
       for (int n = 0; n < 8; ++n) st.Ot[n] *= alpha;
+      if (LOWRANK) {
+        // (outside a low-rank item W and its weight sum are zero and dead)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) st.Wt[k] *= alpha;
+        for (int k = 0; k < 4; ++k) st.Wt[k] *= alpha;
+        st.llr *= alpha;
+      }
       st.l *= alpha;
-      st.llr *= alpha;
+      st.bq0 *= alpha;
+      st.bq1 *= alpha;
       st.m = mn;
     }
   }
@@ -441,7 +511,7 @@ __device__ __forceinline__ void softmax_step(SState& st, float (&z)[NS], bool lo
     s += z[i];
   }
   st.l += s;
-  if (lowrank) st.llr += s;
+  if (LOWRANK) st.llr += s;
 }
 
 __device__ __forceinline__ v4h to_h4v(float a, float b, float c, float d) {
@@ -551,7 +621,7 @@ __device__ __forceinline__ void u_group(const WaveGeom& g, int w, uint32_t P0, S
       z[4 * tt + e] = masked ? -INFINITY : acc[e] + br.qa;
     }
   }
-  softmax_step<8>(st, z, true);
+  softmax_step<8, true>(st, z);
   v8h pf;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pf[e] = (f16)z[e];
@@ -587,7 +657,7 @@ __device__ __forceinline__ void page_k(const WaveGeom& g, int i, uint32_t P0, SS
   float z[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) z[e] = (4 * q4 + e < nr) ? acc[e] * scale : -INFINITY;
-  softmax_step<4>(st, z, false);
+  softmax_step<4, false>(st, z);
   br.pv = to_h4v(z[0], z[1], z[2], z[3]);
 }
 
@@ -625,9 +695,147 @@ __device__ __forceinline__ void page_vv(const WaveGeom& g, int i, uint32_t P0, S
   lds_tr8(P0 + (4 * q4 + (l16 >> 2)) * kSRowB + 16 * (s4 >> 1) + 8 * (s4 & 1), a);
 #pragma unroll
   for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = mfma16(a[nn], wlo, mfma16(a[nn], wh, st.Ot[nn]));
-  if (i == g.nq - 1) {
+}
+
+// Quantised residual rows (x[d] = scale_g code[d] + bias_g, g = d / 64): the
+// codes enter the MFMAs as the exact fp16 values 1024 + code (0x64 above the
+// code's byte, one byte permute per pair of codes), the scales and biases apply
+// in fp32 and take the offset back out:
+//   q . x_t = s_0 (q . (1024 + code_t))_{0..63} + s_1 (q . (1024 + code_t))_{64..127}
+//             + (b_0 - 1024 s_0) Q_0 + (b_1 - 1024 s_1) Q_1,
+// Q_g the sum of q over group g; for V the scales fold into the weights
+// (rounded to fp16, as the weights of fp16 rows are), and the bias terms
+// sum_t p_t b_g,t - 1024 sum_t w_g,t (w the rounded weights) accumulate in the
+// state (bq0, bq1) and join O at the run's end.  The offset costs a few bits of
+// the fp32 sums' 24 (sums about nine times larger than the codes' own).
+
+// 8 bytes -> v8h of 1024 + byte, in order
+__device__ __forceinline__ v8h bytes8_b1024(v2u c) {
+  uint32_t w[4];
+  w[0] = __builtin_amdgcn_perm(0x64646464u, c[0], 0x04010400u);
+  w[1] = __builtin_amdgcn_perm(0x64646464u, c[0], 0x04030402u);
+  w[2] = __builtin_amdgcn_perm(0x64646464u, c[1], 0x04010400u);
+  w[3] = __builtin_amdgcn_perm(0x64646464u, c[1], 0x04030402u);
+  return __builtin_bit_cast(v8h, w);
+}
+// 8 nibbles (nibble k: bits 4 k .. 4 k + 3) -> v8h of 1024 + nibble, in order
+__device__ __forceinline__ v8h nibbles8_b1024(uint32_t c) {
+  const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // nibbles 0 2 4 6, 1 3 5 7
+  uint32_t w[4];
+  w[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
+  w[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
+  w[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
+  w[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
+  return __builtin_bit_cast(v8h, w);
+}
+// 8 nibbles -> v8h of 1024 + nibble in the order 0 4 1 5 2 6 3 7 (a k order the
+// V pages' weights follow)
+__device__ __forceinline__ v8h nibbles8_b1024_il(uint32_t c) {
+  uint32_t w[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 4; ++m) w[m] = ((c >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+  return __builtin_bit_cast(v8h, w);
+}
+
+// The (scale, bias) pairs of rows 8 q4 .. 8 q4 + 7 of a quantised page come
+// with the codes' reads: row 8 q4 + k in dwords 2 (k & 1), 2 (k & 1) + 1 of
+// sb[k / 2] (s0 | b0 << 16, s1 | b1 << 16).
+
+// K page i of a quantised residual item: the scores of its rows 8 q4 + k
+// (k = 0..7), head l16, through the softmax step, into the weights z[k].
+// Score tile tt takes row 8 (l16 / 4) + 4 tt + l16 % 4 as its MFMA row l16, so
+// that output row 4 q4 + e is row 8 q4 + 4 tt + e: the lane's eight weights are
+// then those of the rows the V page's MFMA takes as its k = 8 q4 + k.
+__device__ __forceinline__ void page_qk(const WaveGeom& g, int i, uint32_t P0, SState& st, const v8h (&qf)[4],
+                                        float Q0, float Q1, float scale, float (&z)[8]) {
+  const int lane = lane_id(), l16 = lane & 15, q4 = lane >> 4;
+  uint32_t a[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int j = 8 * (l16 >> 2) + 4 * tt + (l16 & 3);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)  // dimensions 32 s2 + 8 q4 .. + 7
+      a[4 * tt + s2] = g.qb == 8 ? P0 + 128 * j + 16 * ((2 * s2 + (q4 >> 1)) ^ q8_swz(j)) + 8 * (q4 & 1)
+                                 : P0 + 64 * j + 16 * (s2 ^ q4_swz(j)) + 4 * q4;
+  }
+  const uint32_t b = P0 + kQSbOff + 64 * q4;
+  v8h kc[8];
+  v4u sb[4];
+  if (g.qb == 8) {
+    v2u c[8];
+    lds_b64x8s(a, b, c, sb);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kc[t] = bytes8_b1024(c[t]);
+  } else {
+    uint32_t c[8];
+    lds_b32x8s(a, b, c, sb);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kc[t] = nibbles8_b1024(c[t]);
+  }
+  const int nr = g.R - kQRows * i;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const v4f S0 = mfma32(kc[4 * tt + 1], qf[1], mfma32(kc[4 * tt], qf[0], zero));
+    const v4f S1 = mfma32(kc[4 * tt + 3], qf[3], mfma32(kc[4 * tt + 2], qf[2], zero));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * tt + e;
+      const uint32_t x = sb[k >> 1][2 * (k & 1)], y = sb[k >> 1][2 * (k & 1) + 1];
+      const float s0 = h_lo(x), s1 = h_lo(y);
+      const float v = (s0 * S0[e] + s1 * S1[e]) + ((h_hi(x) - 1024.f * s0) * Q0 + (h_hi(y) - 1024.f * s1) * Q1);
+      z[k] = 8 * q4 + k < nr ? v * scale : -INFINITY;
+    }
+  }
+  softmax_step<8, false>(st, z);
+}
+
+// V page of a quantised residual item: O^T += V^T p, the codes of rows
+// 8 q4 + k read transposed (column d = 16 nn + l16 of them, as the MFMA's
+// k = 8 q4 + k; for 4-bit codes in the k order 0 4 1 5 2 6 3 7, which the
+// weights follow), one MFMA per 16 columns.
+__device__ __forceinline__ void page_qv(const WaveGeom& g, uint32_t P0, SState& st, const float (&z)[8]) {
+  const int lane = lane_id(), l16 = lane & 15, q4 = lane >> 4;
+  // Q8: the group's lanes 2 k, 2 k + 1 name row 8 q4 + k, bytes 16 nn .. + 7 and
+  // + 8 .. + 15.  Q4: the group's lane k names row 16 (q4 / 2) + (k + 8 q4) % 16,
+  // bytes 8 nn .. + 7 (columns 16 nn .. + 15): its first eight rows, the low
+  // word of the result, are then the rows 8 q4 .. + 7 the lane keeps.
+  const int j = g.qb == 8 ? 8 * q4 + (l16 >> 1) : 16 * (q4 >> 1) + ((l16 + 8 * q4) & 15);
+  uint32_t a[8];
+#pragma unroll
+  for (int nn = 0; nn < 8; ++nn)
+    a[nn] = g.qb == 8 ? P0 + 128 * j + 16 * (nn ^ q8_swz(j)) + 8 * (l16 & 1)
+                      : P0 + 64 * j + 16 * ((nn >> 1) ^ q4_swz(j)) + 8 * (nn & 1);
+  const uint32_t b = P0 + kQSbOff + 64 * q4;
+  v2u c[8];
+  v4u sb[4];
+  if (g.qb == 8)
+    lds_trb8x8s(a, b, c, sb);
+  else
+    lds_trb4x8s(a, b, c, sb);
+  v8h w0, w1;
+  float be0 = 0.f, be1 = 0.f, ws0 = 0.f, ws1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t x = sb[k >> 1][2 * (k & 1)], y = sb[k >> 1][2 * (k & 1) + 1];
+    w0[k] = (f16)(z[k] * h_lo(x));
+    w1[k] = (f16)(z[k] * h_lo(y));
+    be0 += z[k] * h_hi(x);
+    be1 += z[k] * h_hi(y);
+    ws0 += (float)w0[k];
+    ws1 += (float)w1[k];
+  }
+  st.bq0 += be0 - 1024.f * ws0;
+  st.bq1 += be1 - 1024.f * ws1;
+  if (g.qb == 8) {
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = mfma32(bytes8_b1024(c[nn]), nn < 4 ? w0 : w1, st.Ot[nn]);
+  } else {
+    w0 = __builtin_shufflevector(w0, w0, 0, 4, 1, 5, 2, 6, 3, 7);
+    w1 = __builtin_shufflevector(w1, w1, 0, 4, 1, 5, 2, 6, 3, 7);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn)
+      st.Ot[nn] = mfma32(nibbles8_b1024_il(c[nn][0]), nn < 4 ? w0 : w1, st.Ot[nn]);
   }
 }
 
@@ -668,8 +876,10 @@ struct SItem {
   int G, row0, part;   // the unit's query rows row0 .. row0 + G - 1; the run's partial index
   int layer, h;
   int64_t slot;        // block items: the routed pool slot, or -1 (nothing to stream)
-  const char* rows_k;  // K/V items: their first key and value rows
+  const char* rows_k;  // K/V items: their first key and value rows (quantised: codes)
   const char* rows_v;
+  const char* rows_ks; // quantised residual items: the first rows' scale and bias pairs
+  const char* rows_vs;
 };
 
 __device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uint32_t tag) {
@@ -692,9 +902,12 @@ __device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uin
   it.g.nq = round16(P.rank) >> 4;
   it.g.mu = u_groups(P.rank);
   it.g.nu = 8 / it.g.mu;
+  it.g.qb = 0;
   it.slot = -1;
   it.rows_k = nullptr;
   it.rows_v = nullptr;
+  it.rows_ks = nullptr;
+  it.rows_vs = nullptr;
   int pages;
   if (it.kind == kItemWin) {
     // window rows r0 .. r0 + nrows - 1, as far as the batch row's window reaches
@@ -727,10 +940,22 @@ __device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uin
       const int r0 = (int)(w1 >> 16);
       it.g.kv = true;
       it.g.R = slot >= 0 ? nrows : 0;
-      it.g.nt = (it.g.R + 15) >> 4;
-      if (slot >= 0) {
-        it.rows_k = (const char*)(P.rk + slot * P.rk_s + h * P.rk_h + (int64_t)r0 * kD);
-        it.rows_v = (const char*)(P.rv + slot * P.rv_s + h * P.rv_h + (int64_t)r0 * kD);
+      if (P.rfmt == 0) {
+        it.g.nt = (it.g.R + 15) >> 4;
+        if (slot >= 0) {
+          it.rows_k = (const char*)(P.rk + slot * P.rk_s + h * P.rk_h + (int64_t)r0 * kD);
+          it.rows_v = (const char*)(P.rv + slot * P.rv_s + h * P.rv_h + (int64_t)r0 * kD);
+        }
+      } else {
+        it.g.qb = P.rfmt == 1 ? 8 : 4;
+        it.g.nt = (it.g.R + kQRows - 1) / kQRows;
+        const int cb = P.rfmt == 1 ? kD : kD / 2;
+        if (slot >= 0) {
+          it.rows_k = (const char*)(P.rkq + slot * P.rkq_s + h * P.rkq_h + (int64_t)r0 * cb);
+          it.rows_v = (const char*)(P.rvq + slot * P.rvq_s + h * P.rvq_h + (int64_t)r0 * cb);
+          it.rows_ks = (const char*)(P.rks + slot * P.rks_s + h * P.rks_h + (int64_t)r0 * 4);
+          it.rows_vs = (const char*)(P.rvs + slot * P.rvs_s + h * P.rvs_h + (int64_t)r0 * 4);
+        }
       }
       pages = 2 * it.g.nt;
     }
@@ -768,7 +993,7 @@ struct Issuer {
   SItem it;        // the item being issued
   int ii, ik;      // its index in the wave's list, its next page
   int i1;          // the end of the list
-  int n_issued, total;
+  int n_issued;        // pages issued
   int n_lowrank;   // low-rank items entered (their anchor buffer alternates)
   uint32_t in_flight;
 };
@@ -789,8 +1014,8 @@ __device__ __forceinline__ void issuer_enter(const BlocksArgs& A, CInt* items, u
 
 // issue the stream's next page, if any; n_next: the oldest page not yet used
 __device__ __forceinline__ void issue_next(const BlocksArgs& A, CInt* items, uint32_t tag, Issuer& S, int n_next,
-                                           unsigned char* smem, uint64_t* bases, const RowOffs& ro) {
-  if (S.n_issued >= S.total) return;
+                                           unsigned char* smem, uint64_t* bases) {
+  if (S.ii >= S.i1) return;  // every item issued
   unsigned char* dst = smem + kWPage * (S.n_issued & (kWSlots - 1));
   int ops;
   if (S.it.first && S.ik == 0) {
@@ -802,8 +1027,8 @@ __device__ __forceinline__ void issue_next(const BlocksArgs& A, CInt* items, uin
     for (int q = 0; q < 256; q += 64) dma16b(rs, (uint32_t)(16 * (q + lane)), dst + 16 * q);
     ops = 4;
   } else {
-    ops = issue_page(S.it.g, S.ik - S.it.first, dst, bases, S.it.rows_k, S.it.rows_v, smem + kBPosOff,
-                     smem + kBAncOff + 512 * (S.n_lowrank & 1), ro);
+    ops = issue_page(S.it.g, S.ik - S.it.first, dst, bases, S.it.rows_k, S.it.rows_v, S.it.rows_ks,
+                     S.it.rows_vs, smem + kBPosOff, smem + kBAncOff + 512 * (S.n_lowrank & 1));
   }
   S.in_flight |= (uint32_t)ops << (8 * (S.n_issued - n_next));
   ++S.n_issued;
@@ -845,11 +1070,8 @@ __global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
   const uint32_t tag = slot_tag(((CUint*)A.ctrl)[3]);
   uint64_t* bases = reinterpret_cast<uint64_t*>(smem + kBBaseOff);
   const uint32_t ring0 = lds_off(smem), posb0 = lds_off(smem + kBPosOff), anc0 = lds_off(smem + kBAncOff);
-  const RowOffs ro = row_offs();
 
   Issuer S;
-  S.total = 0;
-  for (int j = i0; j < i1; ++j) S.total += sched_item(A, items + 4 * j, tag).npages;
   S.ii = i0;
   S.i1 = i1;
   S.n_issued = 0;
@@ -857,11 +1079,12 @@ __global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
   S.in_flight = 0u;
   issuer_enter(A, items, tag, S, bases);
 #pragma unroll 1
-  for (int k = 0; k < kWSlots; ++k) issue_next(A, items, tag, S, 0, smem, bases, ro);
+  for (int k = 0; k < kWSlots; ++k) issue_next(A, items, tag, S, 0, smem, bases);
 
   SState st;
   BlockRegs br;
   v8h qf[4];
+  float Q0 = 0.f, Q1 = 0.f;  // the sums of the query over dimensions 0..63 and 64..127 (head l16)
   int n = 0;         // the next page to use
   int n_lowrank = 0; // low-rank items used
   for (int ci = i0; ci < i1; ++ci) {
@@ -874,53 +1097,84 @@ __global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
       wait_oldest(S.in_flight);
       lds_b128x4(ring0 + kWPage * (n & (kWSlots - 1)) + l16 * 256 + 16 * q4, qf);
       S.in_flight >>= 8;
-      issue_next(A, items, tag, S, ++n, smem, bases, ro);
+      issue_next(A, items, tag, S, ++n, smem, bases);
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s0 += (float)qf[0][e] + (float)qf[1][e];
+        s1 += (float)qf[2][e] + (float)qf[3][e];
+      }
+      Q0 = hq_sum(s0);
+      Q1 = hq_sum(s1);
 #pragma unroll
       for (int nn = 0; nn < 8; ++nn) st.Ot[nn] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
       st.m = -INFINITY;
       st.l = 0.f;
       st.llr = 0.f;
+      st.bq0 = 0.f;
+      st.bq1 = 0.f;
     }
     if (cur.kind == kItemLowRank) {
       if (cur.slot >= 0) {
         const uint32_t anc = anc0 + 512 * (++n_lowrank & 1);
+        // the block's W and q~ start from zero (so that neither is live outside
+        // the low-rank items)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          st.Wt[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+          br.qth[k] = (v4h){};
+          br.qtl[k] = (v4h){};
+        }
         for (int i = 0; i < g.nq; ++i) {
           wait_oldest(S.in_flight);
           page_vk(g, i, ring0 + kWPage * (n & (kWSlots - 1)), qf, br, scale, posb0, anc);
           S.in_flight >>= 8;
-          issue_next(A, items, tag, S, ++n, smem, bases, ro);
+          issue_next(A, items, tag, S, ++n, smem, bases);
         }
         for (int i = 0; i < g.nu; ++i) {
           wait_oldest(S.in_flight);
           page_u(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, br);
           S.in_flight >>= 8;
-          issue_next(A, items, tag, S, ++n, smem, bases, ro);
+          issue_next(A, items, tag, S, ++n, smem, bases);
         }
         for (int i = 0; i < g.nq; ++i) {
           wait_oldest(S.in_flight);
           page_vv(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, anc);
           S.in_flight >>= 8;
-          issue_next(A, items, tag, S, ++n, smem, bases, ro);
+          issue_next(A, items, tag, S, ++n, smem, bases);
         }
+      }
+    } else if (g.qb) {
+      for (int i = 0; i < g.nt; ++i) {
+        float z[8];
+        wait_oldest(S.in_flight);
+        page_qk(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, qf, Q0, Q1, scale, z);
+        S.in_flight >>= 8;
+        issue_next(A, items, tag, S, ++n, smem, bases);
+        wait_oldest(S.in_flight);
+        page_qv(g, ring0 + kWPage * (n & (kWSlots - 1)), st, z);
+        S.in_flight >>= 8;
+        issue_next(A, items, tag, S, ++n, smem, bases);
       }
     } else {
       for (int i = 0; i < g.nt; ++i) {
         wait_oldest(S.in_flight);
         page_k(g, i, ring0 + kWPage * (n & (kWSlots - 1)), st, qf, br, scale);
         S.in_flight >>= 8;
-        issue_next(A, items, tag, S, ++n, smem, bases, ro);
+        issue_next(A, items, tag, S, ++n, smem, bases);
         wait_oldest(S.in_flight);
         page_v(ring0 + kWPage * (n & (kWSlots - 1)), st, br);
         S.in_flight >>= 8;
-        issue_next(A, items, tag, S, ++n, smem, bases, ro);
+        issue_next(A, items, tag, S, ++n, smem, bases);
       }
     }
     if (cur.last) {
       // the run's partial: o normalised, lse (every lane of a head writes the
       // same lse).  G >= 1, so lane 0 always stores and every store issues.
       const int np = la.D.att.n_parts;
+      const float bq0 = hq_sum(st.bq0), bq1 = hq_sum(st.bq1);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) st.Ot[nn] += nn < 4 ? bq0 : bq1;
       const float lt = hq_sum(st.l);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const float lse = lt > 0.f ? st.m + __logf(lt) : -INFINITY;
@@ -1003,7 +1257,6 @@ __global__ __launch_bounds__(kAttThreads) void k_merges(const LayerArgs* __restr
 // src through its four-page ring with the same 16-byte buffer loads into LDS
 // (four per 4096-byte page, up to four pages ahead), reads each page back
 // once and writes the wrapping sum of its 32-bit words to sink[w].
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(64) void k_read_probe(const unsigned char* __restrict__ src, uint32_t per,
                                                    uint32_t* __restrict__ sink) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];

@@ -652,15 +652,25 @@ SEDGE = {
     "r32_topk_over_blocks": dict(ranks=[32], n_resid=20, top_k=9),
     "r48_G1_long_ragged_window": dict(ranks=[48], n_resid=36, n_q_heads=2, n_kv_heads=2, window=300,
                                       win_len=[300, 129, 0, 17]),
+    # residual rows of 8- and 4-bit codes: pages of 32 rows, items of 64 (ragged last pages and items)
+    "q8_r16_R252": dict(ranks=[16], n_resid=252, resid_format=1),
+    "q4_r24_R68": dict(ranks=[24], n_resid=68, resid_format=2),
+    "q8_r40_R4": dict(ranks=[40], n_resid=4, resid_format=1),
+    "q4_r56_R128_G16": dict(ranks=[56], n_resid=128, n_q_heads=16, n_kv_heads=1, resid_format=2),
+    "q8_r8_no_residuals": dict(ranks=[8], n_resid=0, resid_format=1),
+    "q4_r48_R36_G1_ragged": dict(ranks=[48], n_resid=36, n_q_heads=2, n_kv_heads=2, window=300,
+                                 win_len=[300, 129, 0, 17], resid_format=2),
+    "q8_r32_R96_topk_over_blocks": dict(ranks=[32], n_resid=96, top_k=9, resid_format=1),
 }
 
 
 @pytest.mark.parametrize("case", sorted(SEDGE))
 def test_streams_edge_cases(lib, case):
     """Two layers of a shape the streams take (ranks 8..56 in steps of 8, 0..252
-    residual rows, G = 1..16, ragged and empty windows and sequences, top_k above
-    the block count), in one step: the plan streams, both layers match the
-    oracle, route as dkv_decode does and repeat bit for bit."""
+    residual rows in fp16 or 8- / 4-bit codes, G = 1..16, ragged and empty
+    windows and sequences, top_k above the block count), in one step: the plan
+    streams, both layers match the oracle, route as dkv_decode does and repeat
+    bit for bit."""
     kw = dict(batch=4, n_q_heads=6, n_kv_heads=2, window=48, n_blocks=[5, 0, 6, 3],
               win_len=[48, 0, 17, 30], ranks=[16], n_resid=20, top_k=3, sigma0=2.0)
     kw.update(SEDGE[case])
@@ -704,6 +714,29 @@ def test_streams_mixed_ranks(lib):
     for l, w in enumerate(wls):
         c = _oracle_check(w, w.layers[0], *res[l], 5)
         say(f"   rank {specs[l][0]} R {specs[l][1]}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
+def test_streams_mixed_formats(lib):
+    """fp16, 8-bit and 4-bit residual layers of different ranks in one streamed
+    step, each against the oracle."""
+    base = dict(batch=3, n_q_heads=8, n_kv_heads=2, window=160, n_blocks=[7, 2, 9], win_len=[160, 33, 90],
+                top_k=4, sigma0=2.0)
+    specs = [(24, 128, 0), (48, 128, 1), (16, 252, 2), (8, 60, 1), (40, 8, 2)]
+    wls = [synth.make_workload(f"sfmt{i}", seed=970 + i, ranks=[r], n_resid=n, resid_format=f, **base)
+           for i, (r, n, f) in enumerate(specs)]
+    pools, batches = [], []
+    for w in wls:
+        p_, b_ = upload(lib, w)
+        lib.gather_route_keys(p_, b_)
+        pools.append(p_)
+        batches.append(b_)
+    run = lib.Layers(pools, batches, 4, wls[0].scale)
+    assert run.plan.stream == 1
+    res = _run_layers(lib, run, reps=2)
+    for l, w in enumerate(wls):
+        c = _oracle_check(w, w.layers[0], *res[l], 4)
+        say(f"   rank {specs[l][0]} R {specs[l][1]} format {specs[l][2]}: "
+            f"max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
 
 
 class _HipEvents:
