@@ -712,6 +712,7 @@ def main() -> int:
     ref_lse = [x.clone() for x in lses]
     modes, kern_by_mode = {}, {}
     kernel_ms = None
+    streamed_parts = None
     if per_layer_modes:
         ev = [[[hip.event() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
         s_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -749,6 +750,49 @@ def main() -> int:
             del g
             modes["per_layer_hipgraph"] = pct(ms)
             log(f"per-layer hipGraph: {modes['per_layer_hipgraph']['median']:.4f} ms/step")
+        # ---- per layer, streamed: a one-layer dkv_decode_layers step (routings,
+        # streams, merges) per layer, in layer order
+        runs1 = [lib.Layers([pools[i]], [batches[i]], K, wl.scale) for i in range(n_layers)]
+        if all(r.plan.stream for r in runs1):
+            def step_streamed(stream=None):
+                for r in runs1:
+                    r.run(stream)
+            for _ in range(args.warmup):
+                step_streamed()
+            torch.cuda.synchronize()
+            for i in range(n_layers):
+                assert torch.equal(runs1[i].idxs[0], idxs[i]), f"one-layer streamed layer {i} routes differently"
+                d_out = (runs1[i].outs[0].float() - ref_out[i].float()).abs().max().item()
+                assert d_out <= 2e-3, f"one-layer streamed layer {i}: {d_out:.2e}"
+            ev = [[[hip.event() for _ in range(4)] for _ in range(n_layers)] for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for s_ in range(args.steps):
+                torch.cuda._sleep(hold)
+                for i in range(n_layers):
+                    runs1[i].run_profiled(ev[s_][i])
+            torch.cuda.synchronize()
+            modes["per_layer_streamed_eager"] = pct([hip.elapsed_ms(ev[s_][0][0], ev[s_][-1][3])
+                                                     for s_ in range(args.steps)])
+            streamed_parts = {name: pct([hip.elapsed_ms(ev[s_][i][k], ev[s_][i][k + 1])
+                                         for s_ in range(args.steps) for i in range(n_layers)])
+                              for k, name in enumerate(("routes", "streams", "merges"))}
+            per_layer_streamed_us = pct([hip.elapsed_ms(ev[s_][i][0], ev[s_][i][3])
+                                         for s_ in range(args.steps) for i in range(n_layers)])
+            for s_ in ev:
+                for e2 in s_:
+                    for e in e2:
+                        hip.destroy(e)
+            log(f"per-layer streamed eager: {modes['per_layer_streamed_eager']['median']:.4f} ms/step; per layer "
+                f"{per_layer_streamed_us['median'] * 1e3:.2f} us (routings "
+                f"{streamed_parts['routes']['median'] * 1e3:.2f}, streams "
+                f"{streamed_parts['streams']['median'] * 1e3:.2f}, merges "
+                f"{streamed_parts['merges']['median'] * 1e3:.2f})")
+            if not args.no_graph:
+                ms, g = graph_steps(torch, np, lambda i, st: step_streamed(st), 1, args.steps, args.warmup)
+                del g
+                modes["per_layer_streamed_hipgraph"] = pct(ms)
+                log(f"per-layer streamed hipGraph: {modes['per_layer_streamed_hipgraph']['median']:.4f} ms/step")
+        del runs1
 
     # ---- every layer's decode step at once (dkv_decode_layers)
     lb_parts = None
@@ -798,6 +842,8 @@ def main() -> int:
 
     mode = min(modes, key=lambda k: modes[k]["median"])
     best_ms = modes[mode]["median"]
+    pl = [k for k in modes if k.startswith("per_layer")]
+    per_layer_best = min(pl, key=lambda k: modes[k]["median"]) if pl else None
     qps = queries_per_step / (best_ms * 1e-3)
     gbps = by["step"] / (best_ms * 1e-3) / 1e9
     digest = source_digest()
@@ -839,11 +885,15 @@ def main() -> int:
         "queries_per_step": queries_per_step,
         "ms_per_step_by_mode": {k: v["median"] for k, v in modes.items()},
         "ms_per_step_pct_by_mode": modes,
-        "per_layer_schedule": None if "per_layer_hipgraph" not in modes else {
-            "ms_per_step": modes["per_layer_hipgraph"]["median"],
-            "queries_per_s": queries_per_step / (modes["per_layer_hipgraph"]["median"] * 1e-3),
-            "GBps": by["step"] / (modes["per_layer_hipgraph"]["median"] * 1e-3) / 1e9,
-            "k_decode_us_per_layer": kernel_ms["median"] * 1e3},
+        "per_layer_schedule": None if per_layer_best is None else {
+            "mode": per_layer_best,
+            "ms_per_step": modes[per_layer_best]["median"],
+            "us_per_layer": modes[per_layer_best]["median"] * 1e3 / n_layers,
+            "queries_per_s": queries_per_step / (modes[per_layer_best]["median"] * 1e-3),
+            "GBps": by["step"] / (modes[per_layer_best]["median"] * 1e-3) / 1e9,
+            "k_decode_us_per_layer": kernel_ms["median"] * 1e3 if kernel_ms else None,
+            "one_layer_streamed_us_by_launch": None if streamed_parts is None else
+            {k: {q: v[q] * 1e3 for q in ("median", "p10", "p90")} for k, v in streamed_parts.items()}},
         "layer_batched_us_by_launch": None if lb_parts is None else
         {k: {q: v[q] * 1e3 for q in ("median", "p10", "p90")} for k, v in lb_parts.items()},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": kernel_gbps,

@@ -359,8 +359,33 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
   int32_t* slot_of = reinterpret_cast<int32_t*>(lds + mbp);
   float* red = reinterpret_cast<float*>(lds + 2 * mbp) + wave * 64 * kRedRow;
 
-  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
   const int c4 = lane & 31, half = lane >> 5;
+
+  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
+  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
+  const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
+  float4 kv[32];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      int r = g0 + 2 * i + half;
+      r = r < N ? r : N - 1;
+      const float* src;
+      if (seq_keys) {
+        src = seq_keys + (int64_t)r * kD;
+      } else {
+        const int sr = slot_of[r];
+        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
+      }
+      kv[i] = *reinterpret_cast<const float4*>(src);
+    }
+  };
+  // with per-sequence keys the first group does not wait for the block table
+  // (nor for the query); the keys, this thread's block-table entry and the
+  // query rows are all requested before any of them is used
+  if (seq_keys && wave * 64 < N) load_group(wave * 64);
+  const int tab0 = tid < N ? Bt.table[(int64_t)b * Bt.mb + tid] : -1;
+  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
   float4 qb = make_float4(0.f, 0.f, 0.f, 0.f);
   {
     const f16* q0 = Bt.q + ((int64_t)b * Bt.Hq + h * Bt.G) * kD + 4 * c4;
@@ -383,31 +408,10 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
     qb.w *= inv;
   }
 
-  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
-  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
-  const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
-  float4 kv[32];
-  auto load_group = [&](int g0) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      int r = g0 + 2 * i + half;
-      r = r < N ? r : N - 1;
-      const float* src;
-      if (seq_keys) {
-        src = seq_keys + (int64_t)r * kD;
-      } else {
-        const int sr = slot_of[r];
-        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
-      }
-      kv[i] = *reinterpret_cast<const float4*>(src);
-    }
-  };
-  // with per-sequence keys the first group does not wait for the block table
-  if (seq_keys && wave * 64 < N) load_group(wave * 64);
 
   // ---- pool slots of the unit's blocks (coalesced block-table reads)
   for (int j = tid; j < N; j += NT) {
-    const int sr = Bt.table[(int64_t)b * Bt.mb + j];
+    const int sr = j == tid ? tab0 : Bt.table[(int64_t)b * Bt.mb + j];
     slot_of[j] = (sr >= 0 && sr < P.n_slots) ? sr : -1;
   }
   lds_barrier();
