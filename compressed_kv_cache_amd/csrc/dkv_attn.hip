@@ -2373,9 +2373,9 @@ static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batche
   // 32, 64) and its 16-wide rank tiles, a quantised K or V page's 32 rows --
   // plus the entry into each item and the start of each unit's run.
   const int64_t kPage = 1500, kK = 500, kV = 110, kVK = 650, kVK0 = 700, kVV = 700;
-  const int64_t kU[5] = {0, 833, 1074, 0, 2875}, kUTile = 250;
-  const int64_t kQK8 = 3500, kQV8 = 2554, kQK4 = 2000, kQV4 = 1391;
-  const int64_t kItemEntry = 4700, kRunStart = 4700;
+  const int64_t kU[5] = {0, 1311, 1070, 0, 4630}, kUTile = 250;
+  const int64_t kQK8 = 700, kQV8 = 564, kQK4 = 1100, kQV4 = 818;
+  const int64_t kItemEntry = 3790, kRunStart = 1100;
   std::vector<Item> items;
   items.reserve((size_t)n_base);
   for (int l = 0; l < n_layers; ++l) {
@@ -2385,8 +2385,9 @@ static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batche
     const int64_t u_page = kPage + kU[mu] + (nq > nq_min ? nq - nq_min : 0) * kUTile;
     const int64_t lowrank = kItemEntry + nq * (2 * kPage + kVK + kVV) + kVK0 + nu * u_page;
     const int64_t kv_pair = 2 * kPage + kK + kV;
+    // (a 4-bit tile is one page: both sides' codes and pairs)
     const int64_t res_pair = fmt == DKV_RESID_INT8 ? 2 * kPage + kQK8 + kQV8
-                           : fmt == DKV_RESID_INT4 ? 2 * kPage + kQK4 + kQV4 : kv_pair;
+                           : fmt == DKV_RESID_INT4 ? kPage + kQK4 + kQV4 : kv_pair;
     const int res_rpp = fmt == DKV_RESID_FP16 ? 16 : 32;
     for (int64_t u = 0; u < units; ++u) {
       const uint32_t bh = (uint32_t)(u / p0.n_kv_heads) | ((uint32_t)(u % p0.n_kv_heads) << 16);

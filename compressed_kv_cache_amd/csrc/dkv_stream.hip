@@ -39,7 +39,8 @@ namespace {
 
 constexpr int kSRowB = 272;                 // bytes per 128-wide fp16 row in LDS: 256 + one 16-byte pad
 constexpr int kWRows = 16;                  // rows per row page
-constexpr int kWPage = kWRows * kSRowB;     // bytes per ring slot
+constexpr int kWPage = kWRows * kSRowB + 256;  // bytes per ring slot: a row page (16 rows), or the
+                                               // 4608 bytes of a 4-bit residual page
 constexpr int kWChunks = kWPage / 16;       // 16-byte chunks per ring slot
 constexpr int kWSlots = 4;                  // ring depth per wave
 constexpr int kWRing = kWPage * kWSlots;    // one wave's ring
@@ -322,26 +323,34 @@ enum PageKind { kPageVK = 0, kPageU = 1, kPageK = 2, kPageV = 3, kPageVV = 4 };
 struct WaveGeom {
   int r, nq;   // rank; its 16-row tiles (V_K and V_V pages)
   int mu, nu;  // 32-position groups per U page (4, 2 or 1: mu r <= 64); U pages (8 / mu)
-  int R, nt;   // low-rank item: residual rows (the mask); K/V item: its rows and their pages of each side
+  int R, nt;   // low-rank item: residual rows (the mask); K/V item: its rows and their 16- or 32-row tiles
   bool kv;     // a K/V item
   int qb;      // K/V item: 0 fp16 rows, 8 or 4: residual rows of 8- or 4-bit codes
 };
 
-// A page of a quantised residual item holds 32 rows of one side (K or V): the
-// rows' codes (128 or 64 bytes each), 16-byte chunk c of row j at chunk
-// position c ^ swz(j) of the row, a swizzle that spreads the page's row and
-// column reads over the LDS banks; then, at kQSbOff, the rows' (scale, bias)
-// pairs, 8 bytes per row.
+// A page of an 8-bit residual item holds 32 rows of one side (K or V): the
+// rows' codes (128 bytes each), 16-byte chunk c of row j at chunk position
+// c ^ swz(j) of the row, a swizzle that spreads the page's row and column reads
+// over the LDS banks; then, at kQSbOff, the rows' (scale, bias) pairs, 8 bytes
+// per row.  A page of a 4-bit residual item holds both sides of 32 rows: the K
+// codes (64 bytes a row), the V codes at kQ4VOff, the K pairs at kQSbOff and
+// the V pairs at kQ4VSbOff.
 constexpr int kQRows = 32;
 constexpr int kQSbOff = 4096;
-static_assert(kQSbOff + kQRows * 8 <= kWPage && kQRows * kD <= kQSbOff, "a quantised page fits a slot");
+constexpr int kQ4VOff = 2048;
+constexpr int kQ4VSbOff = kQSbOff + kQRows * 8;
+static_assert(kQSbOff + kQRows * 8 <= kWPage && kQRows * kD <= kQSbOff, "an 8-bit page fits a slot");
+static_assert(kQ4VSbOff + kQRows * 8 <= kWPage && kQ4VOff + kQRows * kD / 2 <= kQSbOff, "a 4-bit page fits a slot");
 __device__ __forceinline__ int q8_swz(int j) { return (j ^ ((j >> 3) << 1)) & 7; }
 __device__ __forceinline__ int q4_swz(int j) { return (j >> 2) & 3; }
 
 __device__ __forceinline__ int u_groups(int r) { return r <= 16 ? 4 : (r <= 32 ? 2 : 1); }
 
 __device__ __forceinline__ void page_kind(const WaveGeom& g, int k, int& kind, int& i) {
-  if (g.kv) {
+  if (g.kv && g.qb == 4) {
+    kind = kPageK;  // K and V of the tile's rows
+    i = k;
+  } else if (g.kv) {
     kind = kPageK + (k & 1);
     i = k >> 1;
   } else if (k < g.nq) {
@@ -392,26 +401,40 @@ __device__ __forceinline__ int issue_page(const WaveGeom& g, int k, unsigned cha
   const int r = g.r;
   int ops = 0;
   if (g.qb) {
-    // 32 rows of codes (swizzled chunks), then their scale and bias pairs
-    const int cb = g.qb == 8 ? kD : kD / 2;
+    // 32 rows of codes (swizzled chunks), then their scale and bias pairs; a
+    // 4-bit page takes the V side's as well
     int nvalid = g.R - kQRows * i;
     nvalid = nvalid > kQRows ? kQRows : nvalid;
-    const __amdgpu_buffer_rsrc_t rs =
-        rsrc_of((kind == kPageK ? rows_k : rows_v) + kQRows * i * cb, (uint32_t)(nvalid * cb));
+    if (g.qb == 8) {
+      const __amdgpu_buffer_rsrc_t rs =
+          rsrc_of((kind == kPageK ? rows_k : rows_v) + kQRows * i * kD, (uint32_t)(nvalid * kD));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < cb / 32) {
+      for (int q = 0; q < 4; ++q) {
         const int p = 64 * q + lane;
-        const uint32_t off = g.qb == 8 ? (uint32_t)(128 * (p >> 3) + 16 * ((p & 7) ^ q8_swz(p >> 3)))
-                                       : (uint32_t)(64 * (p >> 2) + 16 * ((p & 3) ^ q4_swz(p >> 2)));
-        dma16b(rs, off, dst + 1024 * q);
+        dma16b(rs, (uint32_t)(128 * (p >> 3) + 16 * ((p & 7) ^ q8_swz(p >> 3))), dst + 1024 * q);
+        ++ops;
+      }
+      const __amdgpu_buffer_rsrc_t rsb =
+          rsrc_of((kind == kPageK ? rows_ks : rows_vs) + kQRows * i * 8, (uint32_t)(nvalid * 8));
+      if (lane < kQRows / 2) dma16b(rsb, (uint32_t)(16 * lane), dst + kQSbOff);
+      ++ops;
+    } else {
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const __amdgpu_buffer_rsrc_t rs =
+            rsrc_of((side == 0 ? rows_k : rows_v) + kQRows * i * (kD / 2), (uint32_t)(nvalid * (kD / 2)));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int p = 64 * q + lane;
+          dma16b(rs, (uint32_t)(64 * (p >> 2) + 16 * ((p & 3) ^ q4_swz(p >> 2))), dst + kQ4VOff * side + 1024 * q);
+          ++ops;
+        }
+        const __amdgpu_buffer_rsrc_t rsb =
+            rsrc_of((side == 0 ? rows_ks : rows_vs) + kQRows * i * 8, (uint32_t)(nvalid * 8));
+        if (lane < kQRows / 2) dma16b(rsb, (uint32_t)(16 * lane), dst + (side == 0 ? kQSbOff : kQ4VSbOff));
         ++ops;
       }
     }
-    const __amdgpu_buffer_rsrc_t rsb =
-        rsrc_of((kind == kPageK ? rows_ks : rows_vs) + kQRows * i * 8, (uint32_t)(nvalid * 8));
-    if (lane < kQRows / 2) dma16b(rsb, (uint32_t)(16 * lane), dst + kQSbOff);
-    ++ops;
     return ops;
   }
   if (kind == kPageU) {
@@ -790,11 +813,12 @@ __device__ __forceinline__ void page_qk(const WaveGeom& g, int i, uint32_t P0, S
   softmax_step<8, false>(st, z);
 }
 
-// V page of a quantised residual item: O^T += V^T p, the codes of rows
+// V side of a quantised residual tile (codes at P0, scale and bias pairs at
+// Psb): O^T += V^T p, the codes of rows
 // 8 q4 + k read transposed (column d = 16 nn + l16 of them, as the MFMA's
 // k = 8 q4 + k; for 4-bit codes in the k order 0 4 1 5 2 6 3 7, which the
 // weights follow), one MFMA per 16 columns.
-__device__ __forceinline__ void page_qv(const WaveGeom& g, uint32_t P0, SState& st, const float (&z)[8]) {
+__device__ __forceinline__ void page_qv(const WaveGeom& g, uint32_t P0, uint32_t Psb, SState& st, const float (&z)[8]) {
   const int lane = lane_id(), l16 = lane & 15, q4 = lane >> 4;
   // Q8: the group's lanes 2 k, 2 k + 1 name row 8 q4 + k, bytes 16 nn .. + 7 and
   // + 8 .. + 15.  Q4: the group's lane k names row 16 (q4 / 2) + (k + 8 q4) % 16,
@@ -806,7 +830,7 @@ __device__ __forceinline__ void page_qv(const WaveGeom& g, uint32_t P0, SState& 
   for (int nn = 0; nn < 8; ++nn)
     a[nn] = g.qb == 8 ? P0 + 128 * j + 16 * (nn ^ q8_swz(j)) + 8 * (l16 & 1)
                       : P0 + 64 * j + 16 * ((nn >> 1) ^ q4_swz(j)) + 8 * (nn & 1);
-  const uint32_t b = P0 + kQSbOff + 64 * q4;
+  const uint32_t b = Psb + 64 * q4;
   v2u c[8];
   v4u sb[4];
   if (g.qb == 8)
@@ -948,7 +972,7 @@ __device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uin
         }
       } else {
         it.g.qb = P.rfmt == 1 ? 8 : 4;
-        it.g.nt = (it.g.R + kQRows - 1) / kQRows;
+        it.g.nt = (it.g.R + kQRows - 1) / kQRows;  // 4-bit: one page a tile, 8-bit: two
         const int cb = P.rfmt == 1 ? kD : kD / 2;
         if (slot >= 0) {
           it.rows_k = (const char*)(P.rkq + slot * P.rkq_s + h * P.rkq_h + (int64_t)r0 * cb);
@@ -957,7 +981,7 @@ __device__ __forceinline__ SItem sched_item(const BlocksArgs& A, CInt* item, uin
           it.rows_vs = (const char*)(P.rvs + slot * P.rvs_s + h * P.rvs_h + (int64_t)r0 * 4);
         }
       }
-      pages = 2 * it.g.nt;
+      pages = it.g.qb == 4 ? it.g.nt : 2 * it.g.nt;
     }
   }
   it.npages = it.first + pages;
@@ -1144,7 +1168,7 @@ __global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
           issue_next(A, items, tag, S, ++n, smem, bases);
         }
       }
-    } else if (g.qb) {
+    } else if (g.qb == 8) {
       for (int i = 0; i < g.nt; ++i) {
         float z[8];
         wait_oldest(S.in_flight);
@@ -1152,7 +1176,18 @@ __global__ __launch_bounds__(64, 2) void k_blocks(BlocksArgs A) {
         S.in_flight >>= 8;
         issue_next(A, items, tag, S, ++n, smem, bases);
         wait_oldest(S.in_flight);
-        page_qv(g, ring0 + kWPage * (n & (kWSlots - 1)), st, z);
+        const uint32_t P0 = ring0 + kWPage * (n & (kWSlots - 1));
+        page_qv(g, P0, P0 + kQSbOff, st, z);
+        S.in_flight >>= 8;
+        issue_next(A, items, tag, S, ++n, smem, bases);
+      }
+    } else if (g.qb == 4) {
+      for (int i = 0; i < g.nt; ++i) {
+        float z[8];
+        wait_oldest(S.in_flight);
+        const uint32_t P0 = ring0 + kWPage * (n & (kWSlots - 1));
+        page_qk(g, i, P0, st, qf, Q0, Q1, scale, z);
+        page_qv(g, P0 + kQ4VOff, P0 + kQ4VSbOff, st, z);
         S.in_flight >>= 8;
         issue_next(A, items, tag, S, ++n, smem, bases);
       }
