@@ -365,19 +365,15 @@ __device__ __forceinline__ void page_kind(const WaveGeom& g, int k, int& kind, i
   }
 }
 
-// The lane's index, opaque to loop-invariant code motion: address arithmetic
-// built on it is recomputed where it is used, not held in registers across the
-// streams' loops (which need those registers for the pages' work).
-__device__ __forceinline__ int lane_id() {
-  int l = (int)(threadIdx.x & 63);
-  asm volatile("" : "+v"(l));
-  return l;
-}
+// The lane's index.  (Address arithmetic built on it is hoisted out of the
+// streams' loops and held in registers: k_blocks then uses all 256 VGPRs of its
+// two-waves-per-SIMD budget, without spills, and runs its quantised pages ~5%
+// faster than with that arithmetic recomputed per page.)
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // Per lane: the source offset of chunk 64 q + lane (q = 0..4) of a 128-wide
 // row page (row p / 17, chunk p % 17 of the row; chunk 16, the row's pad, is
-// kOutside), the same for every row page.  (Recomputed at each issue: kept
-// live, the offsets would take registers the pages need.)
+// kOutside), the same for every row page.
 __device__ __forceinline__ uint32_t row_off(int q) {
   const int p = 64 * q + lane_id();
   const int row = (p * 3856) >> 16;  // p / 17 for p < 17 * 16 * 2
