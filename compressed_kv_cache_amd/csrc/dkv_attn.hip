@@ -2432,14 +2432,17 @@ static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batche
     return c + (est - c) / rem;
   };
   double end = end_of(0, 0.0);
+  bool empty = true;  // nothing in wave w's segment yet: it takes at least one item (or page pair)
   auto advance = [&]() {
     if (w + 1 < n_waves) ++w;
     end = end_of(w, cum);
+    empty = true;
   };
   auto emit = [&](const Item& it) {
     cut.push_back(it);
     wave_of.push_back(w);
     cum += (double)it.cost;
+    empty = false;
   };
   for (size_t i = 0; i < items.size(); ++i) {
     for (;;) {
@@ -2455,7 +2458,7 @@ static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batche
           std::swap(items[i], items[i + 1]);
           continue;
         }
-        if (cum + 0.5 * (double)it.cost <= end) {
+        if (empty || cum + 0.5 * (double)it.cost <= end) {
           emit(it);
           advance();
           break;
@@ -2465,7 +2468,8 @@ static bool build_stream_schedule(const dkv_pool* pools, const dkv_batch* batche
       }
       // the pairs that fit before the segment's end stay in wave w
       const int64_t fixed = it.cost - (int64_t)it.pairs * it.pair;  // the entry (and run start)
-      const int m = (int)std::lround((end - cum - (double)fixed) / (double)it.pair);
+      int m = (int)std::lround((end - cum - (double)fixed) / (double)it.pair);
+      if (empty && m < 1) m = 1;
       if (m >= it.pairs) {
         emit(it);
         break;

@@ -211,6 +211,39 @@ def test_layer_batched_entry_points_validate(clib):
     assert clib.dkv_decode_layers(None, None) == L.DKV_ERR_INVALID_ARG
 
 
+# Shapes the streams' schedule builder runs on (host code: sizing a workspace
+# builds the whole schedule).  Each must come back at once with a size that
+# covers the classic layout's per-layer regions.
+SCHED_SHAPES = [
+    # (ranks per layer, residual rows, residual format, window, top_k, batch, q heads, kv heads, max_blocks)
+    ([8], 0, 0, 0, 1, 1, 2, 2, 4),
+    ([16], 252, 0, 37, 3, 4, 6, 2, 6),
+    ([24], 68, 2, 300, 9, 4, 2, 2, 5),
+    ([56], 128, 1, 1024, 32, 1, 16, 1, 252),
+    ([40], 4, 2, 4096, 32, 2, 8, 2, 512),
+    ([24] * 9 + [48] * 10 + [16] * 9, 128, 0, 1024, 32, 4, 12, 2, 252),
+    ([24] * 9 + [48] * 10 + [16] * 9, 128, 1, 1024, 32, 4, 12, 2, 252),
+    ([24] * 9 + [48] * 10 + [16] * 9, 128, 2, 1024, 32, 4, 12, 2, 252),
+    ([32] * 4, 40, 0, 4096, 32, 32, 32, 8, 128),
+]
+
+
+@pytest.mark.timeout(60)
+@pytest.mark.parametrize("shape", range(len(SCHED_SHAPES)))
+def test_stream_schedule_sizes(clib, shape):
+    ranks, R, fmt, W, top_k, B, hq, hkv, mb = SCHED_SHAPES[shape]
+    sb = L.View(FAKE, 4096, 2048)
+    pools = [_pool(rank=r, n_resid=R, n_kv_heads=hkv, resid_format=fmt, resid_k_sb=sb, resid_v_sb=sb)
+             for r in ranks]
+    b = _batch(batch=B, n_q_heads=hq, window=W, max_blocks=mb)
+    n = len(ranks)
+    PA = (L.PoolC * n)(*pools)
+    BA = (L.BatchC * n)(*([b] * n))
+    need = clib.dkv_decode_layers_workspace_size(PA, BA, n, top_k)
+    one = sum(clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) for p in pools)
+    assert need > 0 and need >= one // 2
+
+
 def test_seal_blocks_validates(clib):
     p = _pool()
     src = L.View(FAKE, 2 * 256 * 128, 256 * 128)
