@@ -547,6 +547,38 @@ def test_decode_layers_full_stack_sampled(lib):
         say(f"   layer {l}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
 
 
+@pytest.mark.parametrize("variant", ["Q8", "Q4"])
+def test_decode_layers_full_stack_quantised_sampled(lib, variant):
+    """The 64k batch-4 stack with 8- or 4-bit residual rows, all 28 layers in
+    the one streamed launch the benchmark times: every layer routes as its
+    per-layer launch does, two launches give the same bits, and one layer of
+    each rank matches the oracle."""
+    sampled = {3: None, 12: None, 22: None}
+    say(f"[decode layers] stack64k {variant}, 28 layers, oracle on layers {sorted(sampled)}")
+    pools, batches = [], []
+    scale = top_k = None
+    for l in range(28):
+        w = synth.make_config(2, layers=[l], variant=variant)
+        scale, top_k = w.scale, w.top_k
+        pool, batch = upload(lib, w)
+        lib.gather_route_keys(pool, batch)
+        pools.append(pool)
+        batches.append(batch)
+        if l in sampled:
+            sampled[l] = w
+        del w
+    run = lib.Layers(pools, batches, top_k, scale)
+    assert run.plan.stream == 1 and run.plan.quantised == 1
+    res = _run_layers(lib, run, reps=2)
+    for l in range(28):
+        _, _, i1 = lib.decode(pools[l], batches[l], top_k, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(res[l][2], i1), l
+    for l, w in sorted(sampled.items()):
+        c = _oracle_check(w, w.layers[0], *res[l], w.top_k)
+        say(f"   layer {l} rank {w.layers[0].rank}: max|d out| {c.max_out:.3e} max|d lse| {c.max_lse:.3e}")
+
+
 def test_decode_layers_mixed_ranks_and_edges(lib):
     """Layers of every low-rank tile count (ranks 1..64, 0..255 residual rows),
     ragged windows and an empty sequence, in one launch."""
