@@ -1370,11 +1370,77 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(const float* part_o, co
     if (lane == 0) out_lse[row] = any ? M + __logf(St) : -INFINITY;
   }
 }
-// One work item of a fused decode step: t < n_route routes unit t; then
-// the parts (u, p) = ((t - n_route) / P, (t - n_route) % P); then the merges,
-// per query row (u, g) or per unit u.  sh_slot: a shared word of the calling
-// workgroup.
-template <int NRQ, int QK>
+// The routed block of part p of unit u under a split routing: wait (bounded)
+// until the unit's score items have written all of its (slot, score) words,
+// then rank the blocks exactly as route_unit does (the same selection on the
+// same scores) and take the one at position p in ascending block order.  The
+// part also writes that position of the routed indices (-1 past the routed
+// count).  Returns the pool slot, or -1 (no block).
+__device__ __forceinline__ int split_route_slot(const BatchArgs& Bt, const DecodeArgs& D, int u, int p,
+                                                unsigned char* smem, RouteShared<kAttWaves>& rsh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = u / Bt.Hkv;
+  int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
+  N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
+  const int keff = D.att.top_k < N ? D.att.top_k : N;
+  const int mbp = ((Bt.mb > 0 ? Bt.mb : 1) + 3) & ~3;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
+  int32_t* slot_of = reinterpret_cast<int32_t*>(keys + mbp);
+  const uint64_t* src = D.rwords + (int64_t)u * Bt.mb;
+  lds_barrier();  // every wave is past its window tiles, whose LDS scratch is reused here
+  if (tid == 0) {
+    rsh.pick_j = -1;
+    rsh.pick_slot = -1;
+  }
+  bool ready = false;
+  for (unsigned n = 0;; ++n) {
+    bool ok = true;
+    for (int j = tid; j < N; j += kAttThreads) {
+      const uint64_t v = ld_dev(src + j);
+      const uint32_t hi = (uint32_t)(v >> 32);
+      ok = ok && hi != 0u;
+      keys[j] = (uint32_t)v;
+      slot_of[j] = (int32_t)hi - kSlotCode;
+    }
+    const bool wok = __all(ok);
+    if (lane == 0) rsh.ready[n & 1][wave] = wok ? 1u : 0u;
+    lds_barrier();
+    uint32_t all = 1u;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) all &= rsh.ready[n & 1][w];
+    if (all) {
+      ready = true;
+      break;
+    }
+    if (n >= kRouteWaitLimit) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ready) {
+    if (tid == 0) {
+      atomicOr(&D.ctrl[2], 1u);  // give up: an empty part
+      st_dev(&D.idx[(int64_t)u * D.att.top_k + p], -1);
+    }
+    return -1;
+  }
+  route_select<kAttThreads>(keys, N, keff, keys, mbp, rsh, [&](int pos, int j, uint32_t) {
+    if (pos == p) {
+      rsh.pick_j = j;
+      rsh.pick_slot = slot_of[j];
+    }
+  });
+  lds_barrier();
+  const int j = rsh.pick_j, slot = rsh.pick_slot;
+  if (tid == 0) st_dev(&D.idx[(int64_t)u * D.att.top_k + p], j);
+  return slot;
+}
+
+// One work item of a fused decode step: t < n_route routes, unit t /
+// route_items; then the parts (u, p) = ((t - n_route) / P, (t - n_route) % P);
+// then the merges, per query row (u, g) or per unit u.  sh_slot: a shared word
+// of the calling workgroup.  SPLIT: the routing items are score items
+// (score_slice, one per kScoreChunk blocks of a unit) and each block part
+// selects its own block (split_route_slot); otherwise one route_unit per unit.
+template <int NRQ, int QK, bool SPLIT = false>
 __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& Bt, const DecodeArgs& D, int t,
                                             unsigned char* smem, RouteShared<kAttWaves>& rsh, int32_t& sh_slot) {
   const int tid = threadIdx.x;
@@ -1382,32 +1448,47 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     // no item
   } else if (t < D.n_route) {
     __builtin_amdgcn_s_setprio(2);  // every other item of the launch waits on routing
-    route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh,
-                            slot_tag(ld_dev(&D.ctrl[3])));
+    if constexpr (SPLIT) {
+      const int u = t / D.route_items, s = t % D.route_items;
+      score_slice<kAttThreads>(P, Bt, u, s * kScoreChunk, (s + 1) * kScoreChunk, D.rwords + (int64_t)u * Bt.mb,
+                               reinterpret_cast<float*>(smem));
+      // counted once its words are written: the launch's last merge clears
+      // the words only after every score item is counted
+      stores_done();
+      __syncthreads();
+      if (tid == 0) atomicAdd(&D.ctrl[kCtrlScored], 1u);
+    } else {
+      route_unit<kAttThreads>(P, Bt, t, D.att.top_k, D.idx, nullptr, D.slots, reinterpret_cast<uint32_t*>(smem), rsh,
+                              slot_tag(ld_dev(&D.ctrl[3])));
+    }
   } else if (t < D.n_part_end) {
     const int it = t - D.n_route;
     const int u = it / D.att.items_per_unit, p = it % D.att.items_per_unit;
     // the routed slot of a block part: wait (bounded) until the unit's routing
     // has written it; called after the part's window tiles are done
     auto get_slot = [&]() {
-      if (tid == 0) {
-        const int32_t* sp = &D.slots[(int64_t)u * D.att.top_k + p];
-        const uint32_t tag = slot_tag(ld_dev(&D.ctrl[3]));
-        unsigned n = 0;
-        int32_t v = ld_dev(sp);
-        while (!slot_ready(v, tag) && n < kRouteWaitLimit) {
-          __builtin_amdgcn_s_sleep(1);
-          v = ld_dev(sp);
-          ++n;
+      if constexpr (SPLIT) {
+        return split_route_slot(Bt, D, u, p, smem, rsh);
+      } else {
+        if (tid == 0) {
+          const int32_t* sp = &D.slots[(int64_t)u * D.att.top_k + p];
+          const uint32_t tag = slot_tag(ld_dev(&D.ctrl[3]));
+          unsigned n = 0;
+          int32_t v = ld_dev(sp);
+          while (!slot_ready(v, tag) && n < kRouteWaitLimit) {
+            __builtin_amdgcn_s_sleep(1);
+            v = ld_dev(sp);
+            ++n;
+          }
+          if (!slot_ready(v, tag)) {
+            atomicOr(&D.ctrl[2], 1u);
+            v = (int32_t)(tag | (uint32_t)(-1 + kSlotCode));  // give up: an empty part
+          }
+          sh_slot = slot_value(v);
         }
-        if (!slot_ready(v, tag)) {
-          atomicOr(&D.ctrl[2], 1u);
-          v = (int32_t)(tag | (uint32_t)(-1 + kSlotCode));  // give up: an empty part
-        }
-        sh_slot = slot_value(v);
+        lds_barrier();
+        return (int)sh_slot;
       }
-      lds_barrier();
-      return (int)sh_slot;
     };
     attend_part<NRQ, QK>(P, Bt, D.att, u, p, get_slot, smem);
     // count this part once its partial is stored
@@ -1440,59 +1521,74 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
   }
 }
 
+// Work items of a launch, in one list per XCD: the units u with u % 8 == x
+// form list x, holding their routing items, then their parts, then their
+// merges.  Workgroup x + 8 i takes item i of list x (workgroups are handed to
+// the XCDs in turn, so list x runs on XCD x and a unit's hand-offs stay in one
+// XCD's L2).  Every wait is on an item earlier in the same list, which has a
+// smaller workgroup index and so was dispatched first.  Returns the item, or
+// -1 for a workgroup past the end of its list.
+__host__ __device__ inline int decode_item_of(int wg, int n_units, int routes_per_unit, int parts_per_unit,
+                                              int merges_per_unit, int n_route, int n_part_end) {
+  const int x = wg % kQueues, i = wg / kQueues;
+  const int nx = n_units > x ? (n_units - x + kQueues - 1) / kQueues : 0;
+  const int R = routes_per_unit, Pp = parts_per_unit, G = merges_per_unit;
+  if (i >= nx * (R + Pp + G)) return -1;
+  if (i < R * nx) return (x + kQueues * (i / R)) * R + i % R;
+  if (i < (R + Pp) * nx) {
+    const int j = i - R * nx;
+    return n_route + (x + kQueues * (j / Pp)) * Pp + j % Pp;
+  }
+  const int j = i - (R + Pp) * nx;
+  return n_part_end + (x + kQueues * (j / G)) * G + j % G;
+}
+
+// Workgroups of a dkv_decode launch: 8 lists as long as the longest (list 0).
+inline int64_t decode_grid(const DecodeArgs& D) {
+  const int64_t n0 = (D.n_units + kQueues - 1) / kQueues;
+  const int R = D.n_route > 0 ? D.route_items : 0;
+  return (int64_t)kQueues * n0 * (R + D.att.items_per_unit + D.merges);
+}
+
 template <int NRQ, int QK>
 __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs Bt, DecodeArgs D) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ RouteShared<kAttWaves> rsh;
-  __shared__ uint32_t sh_ticket, sh_flag;
+  __shared__ uint32_t sh_flag;
   __shared__ int32_t sh_slot;
   const int tid = threadIdx.x;
-  // Work comes from one queue per XCD (the units u with u % 8 == x go to queue
-  // x), so the queue counters are contended by few workgroups and a unit's
-  // hand-offs tend to stay within one XCD.  A workgroup takes from its own
-  // XCD's queue and, when that is empty, from the next ones.  Each queue holds
-  // its units' routings, then their parts, then their merges: every wait is on
-  // an item that comes earlier in some queue and so is already taken by a
-  // running workgroup.
-  if (tid == 0) {
-    const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kQueues - 1));  // XCC_ID
-    const int R = D.n_route > 0 ? 1 : 0, P = D.att.items_per_unit, G = D.merges;
-    uint32_t item = 0xFFFFFFFFu;
-    for (int k = 0; k < kQueues && item == 0xFFFFFFFFu; ++k) {
-      const int x = (x0 + k) & (kQueues - 1);
-      const int nx = D.n_units > x ? (D.n_units - x + kQueues - 1) / kQueues : 0;
-      const uint32_t size = (uint32_t)(nx * (R + P + G));
-      if (size == 0u) continue;
-      const uint32_t i = atomicAdd(&D.ctrl[kCtrlQueue + x * kQueueStride], 1u);
-      if (i >= size) continue;
-      // queue position -> launch-wide item index: routes, then parts, then merges
-      if (i < (uint32_t)(R * nx)) {
-        item = (uint32_t)(x + kQueues * (int)i);
-      } else if (i < (uint32_t)(R * nx + nx * P)) {
-        const int j = (int)i - R * nx;
-        item = (uint32_t)(D.n_route + (x + kQueues * (j / P)) * P + j % P);
-      } else {
-        const int j = (int)i - R * nx - nx * P;
-        item = (uint32_t)(D.n_part_end + (x + kQueues * (j / G)) * G + j % G);
-      }
-    }
-    sh_ticket = item;
-  }
-  lds_barrier();
-  const int t = (int)sh_ticket;
-  decode_item<NRQ, QK>(P, Bt, D, t, smem, rsh, sh_slot);
-  // The last merge to finish zeroes the control words for the next launch:
+  const int t = decode_item_of((int)blockIdx.x, D.n_units, D.n_route > 0 ? D.route_items : 0, D.att.items_per_unit,
+                               D.merges, D.n_route, D.n_part_end);
+  decode_item<NRQ, QK, true>(P, Bt, D, t, smem, rsh, sh_slot);
+  // The last merge to finish resets the control area for the next launch:
   // merges start only after all of their unit's parts are stored, and every
-  // part only after its routing, so no other item still uses them.
+  // part only after its unit's score words are all written; it waits (bounded)
+  // for the count of finished score items, so that none writes a word after
+  // the words are cleared.
   if (t >= D.n_part_end) {
     __syncthreads();
     if (tid == 0) sh_flag = (atomicAdd(&D.ctrl[1], 1u) == (uint32_t)(D.n_items - D.n_part_end - 1)) ? 1u : 0u;
     lds_barrier();
     if (sh_flag) {
+      if (tid == 0) {
+        unsigned n = 0;
+        while (ld_dev(&D.ctrl[kCtrlScored]) < (uint32_t)D.n_route && n < kRouteWaitLimit) {
+          __builtin_amdgcn_s_sleep(2);
+          ++n;
+        }
+        if (ld_dev(&D.ctrl[kCtrlScored]) < (uint32_t)D.n_route) atomicOr(&D.ctrl[2], 1u);
+      }
+      __syncthreads();
+      if (D.rwords) {
+        uint4* w = reinterpret_cast<uint4*>(D.rwords);
+        const int64_t n16 = (int64_t)D.n_units * Bt.mb / 2;
+        for (int64_t i = tid; i < n16; i += kAttThreads) w[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (tid == 0 && ((int64_t)D.n_units * Bt.mb) & 1) D.rwords[(int64_t)D.n_units * Bt.mb - 1] = 0ull;
+      }
       for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
-      if (tid < kQueues) D.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
       if (tid == 0) {
         D.ctrl[1] = 0u;
+        D.ctrl[kCtrlScored] = 0u;
         D.ctrl[3] = D.ctrl[3] + 1u;  // the next launch's routed-slot tag
       }
     }
@@ -1773,7 +1869,7 @@ dkv_status launch_decode_nrq_q(size_t shm, hipStream_t st, const dkv_pool* P, co
       return fail(DKV_ERR_HIP, "hipFuncSetAttribute(k_decode) failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_decode<NRQ, QK>), dim3((unsigned)D.n_items), dim3(kAttThreads), shm, st, make_pool_args(P),
+  hipLaunchKernelGGL((k_decode<NRQ, QK>), dim3((unsigned)decode_grid(D)), dim3(kAttThreads), shm, st, make_pool_args(P),
                      make_batch_args(P, B), D);
   return launched("k_decode");
 }
@@ -1867,7 +1963,7 @@ int decode_win_parts(int window) {
 // Workspace of dkv_decode: a control area (ticket, counters, per-unit flags;
 // zero between calls), then routed indices and slots, then the partials.
 struct WsLayout {
-  size_t ctrl_bytes, unit_done, slots, idx, part_lse, part_o, total;
+  size_t ctrl_bytes, unit_done, slots, rwords, idx, part_lse, part_o, total;
 };
 
 // fold: the window's tiles are shared out over the routed-block parts (else
@@ -1927,7 +2023,9 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
   const size_t rows = B * (size_t)batch->n_q_heads;
   w.unit_done = kCtrlHeaderBytes;
   w.slots = w.unit_done + align256(units * 4);
-  w.ctrl_bytes = w.slots + align256(units * (size_t)top_k * 4);
+  w.rwords = w.slots + align256(units * (size_t)top_k * 4);
+  const size_t mb = top_k > 0 && batch->max_blocks > 0 ? (size_t)batch->max_blocks : 0;
+  w.ctrl_bytes = w.rwords + align256(units * mb * 8);
   w.idx = w.ctrl_bytes;
   w.part_lse = w.idx + align256(units * (size_t)top_k * 4);
   w.part_o = w.part_lse + align256(rows * n_parts * 4);
@@ -1939,7 +2037,8 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
 // by decode_layout); ctrl: the control header the launch uses.
 dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int top_k, float scale, unsigned char* ws,
                              uint32_t* ctrl, void* out, float* out_lse, int32_t* out_idx, DecodeArgs& D, size_t& shm,
-                             bool fold = true, bool row_merges = true, size_t min_parts = 0) {
+                             bool fold = true, bool row_merges = true, size_t min_parts = 0,
+                             bool split_routing = false) {
   const WsLayout w = decode_layout(pool, batch, top_k, fold, min_parts);
   // folded, each routed-block part also takes its share of the window;
   // otherwise the window comes in chunks of kWinChunk rows
@@ -1970,7 +2069,12 @@ dkv_status build_decode_args(const dkv_pool* pool, const dkv_batch* batch, int t
   D.out = (f16*)out;
   D.out_lse = out_lse;
   D.n_units = units;
-  D.n_route = top_k > 0 ? units : 0;
+  // split routing (dkv_decode): ceil(max_blocks / kScoreChunk) score items per
+  // unit, each scoring kScoreChunk blocks; else one routing item per unit
+  D.rwords = (split_routing && top_k > 0) ? (uint64_t*)(ws + w.rwords) : nullptr;
+  D.route_items = D.rwords ? (batch->max_blocks > kScoreChunk ? (batch->max_blocks + kScoreChunk - 1) / kScoreChunk : 1)
+                           : 1;
+  D.n_route = top_k > 0 ? units * D.route_items : 0;
   const int64_t part_end = (int64_t)D.n_route + (int64_t)units * n_parts;
   // row_merges (one launch per layer, whose merges end the launch): a merge
   // workgroup per query row; otherwise (several layers in one launch, where
@@ -2228,7 +2332,7 @@ static dkv_status decode_impl(const dkv_pool* pool, const dkv_batch* batch, int3
   DecodeArgs D;
   size_t shm = 0;
   if ((s = build_decode_args(pool, batch, top_k, scale, (unsigned char*)workspace, (uint32_t*)workspace, out, out_lse,
-                             out_idx, D, shm)))
+                             out_idx, D, shm, true, true, 0, true)))
     return s;
   const AttnArgs& a = D.att;
 

@@ -189,6 +189,12 @@ __device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // wait until this thread's stores have completed
 __device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -297,6 +303,8 @@ struct RouteShared {
   uint32_t wsum[NW];
   float wlo[NW], whi[NW];
   uint32_t digit, above;
+  uint32_t ready[2][NW];     // a split routing's block part: per-wave "all words present", by poll parity
+  int32_t pick_j, pick_slot; // ... and the routed block it takes, with its pool slot
 };
 
 // LDS words route_unit needs for max_blocks blocks and NW waves.
@@ -329,127 +337,123 @@ __device__ __forceinline__ bool slot_ready(int32_t w, uint32_t tag) {
 }
 __device__ __forceinline__ int32_t slot_value(int32_t w) { return (int32_t)((uint32_t)w & 0x00FFFFFFu) - kSlotCode; }
 
-// Route one (sequence, KV head) unit u with a workgroup of NT threads.
-// lds: route_lds_words(max_blocks, NT / 64) words: ordered score keys [mb],
-// pool slots [mb] (both rounded up to 4), then a 64 x kRedRow float area per wave.
-//
-// Scores: lane l of a wave holds columns 4 (l % 32) .. +3 of the GQA-mean query;
-// a 512-byte routing key is read by 32 lanes, 16 bytes each, two keys per load
-// instruction (fully coalesced), and the 32 lane partials of a key are summed
-// through LDS.  Selection: block j is routed iff fewer than K blocks beat it
-// (a larger score, or an equal score at a smaller index: the lowest-index-first
-// tie rule), found with a 256-bin histogram of the scores and an exact ranking
-// inside the boundary bin only.  Routed blocks are emitted in ascending block
-// order.
+// The GQA-mean query of unit (b, h), columns 4 c4 .. 4 c4 + 3: the group's
+// query rows summed in order, then scaled by 1 / G.
+__device__ __forceinline__ float4 route_query(const BatchArgs& Bt, int b, int h, int c4) {
+  float4 qb = make_float4(0.f, 0.f, 0.f, 0.f);
+  const f16* q0 = Bt.q + ((int64_t)b * Bt.Hq + h * Bt.G) * kD + 4 * c4;
+  v4h qh[DKV_MAX_GROUP];
+#pragma unroll
+  for (int g = 0; g < DKV_MAX_GROUP; ++g) qh[g] = *reinterpret_cast<const v4h*>(q0 + (g < Bt.G ? g : Bt.G - 1) * kD);
+#pragma unroll
+  for (int g = 0; g < DKV_MAX_GROUP; ++g) {
+    if (g < Bt.G) {
+      qb.x += (float)qh[g][0];
+      qb.y += (float)qh[g][1];
+      qb.z += (float)qh[g][2];
+      qb.w += (float)qh[g][3];
+    }
+  }
+  const float inv = 1.f / (float)Bt.G;
+  qb.x *= inv;
+  qb.y *= inv;
+  qb.z *= inv;
+  qb.w *= inv;
+  return qb;
+}
+
+// A routing score is computed in two steps, the same everywhere a score is
+// computed (so every routing path ranks blocks on identical values): each of
+// 32 lanes takes the dot product of 4 of the 128 columns (score_share, with
+// the multiply-adds written out), then the 32 shares, laid out in one LDS
+// row, are added in column order (score_sum).
+__device__ __forceinline__ float score_share(const float4& k, const float4& q) {
+  return __builtin_fmaf(k.x, q.x, k.y * q.y) + __builtin_fmaf(k.z, q.z, k.w * q.w);
+}
+__device__ __forceinline__ float score_sum(const float* row) {
+  const float4* rr = reinterpret_cast<const float4*>(row);
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float4 v = rr[m];
+    acc += (v.x + v.y) + (v.z + v.w);
+  }
+  return acc;
+}
+
+// Blocks one score item covers (a split routing: see score_slice).
+constexpr int kScoreChunk = 64;
+
+// Scores of blocks [j0, j1) of unit u, j1 - j0 <= 16 NT / 64 (clipped to the
+// unit's block count), each written to words[j] with one device-scope 8-byte
+// store: the high word is pool slot + kSlotCode (slot -1 for an invalid
+// block-table entry, whose score is -inf), never 0; the low word is the
+// ordered score.  Wave w takes blocks j0 + 16 w .. + 15; lanes 0-31 read the even and
+// lanes 32-63 the odd ones of each pair, 16 bytes each, and a block's 32
+// shares meet in a 16 x kRedRow float area per wave (red).  No workgroup
+// barrier: waves without blocks return at once.
 template <int NT>
-__device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
-                                           float* scores, int32_t* slots_out, uint32_t* lds,
-                                           RouteShared<NT / 64>& sh, uint32_t tag = 0u) {
-  constexpr int NW = NT / 64;
-  static_assert(NT == 256 || NT == 512, "route_unit: 256 histogram bins over the first 4 waves");
-  constexpr int kBinWaves = 256 / 64;
-  uint32_t* wsum = sh.wsum;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void score_slice(const PoolArgs& P, const BatchArgs& Bt, int u, int j0, int j1,
+                                            uint64_t* words, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = u / Bt.Hkv, h = u % Bt.Hkv;
   int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
   N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
-  const int keff = top_k < N ? top_k : N;
-  const int mbp = ((Bt.mb > 0 ? Bt.mb : 1) + 3) & ~3;
-  uint32_t* keys = lds;
-  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + mbp);
-  float* red = reinterpret_cast<float*>(lds + 2 * mbp) + wave * 64 * kRedRow;
-
+  const int last = (j1 < N ? j1 : N) - 1;
+  const int w0 = j0 + 16 * wave;
+  if (w0 > last) return;
   const int c4 = lane & 31, half = lane >> 5;
-
-  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
-  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
+  // lanes 0..15 look up the slots of blocks w0 .. w0 + 15 (past the end: the last block)
+  const int jt = w0 + (lane & 15) <= last ? w0 + (lane & 15) : last;
   const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
-  float4 kv[32];
-  auto load_group = [&](int g0) {
+  float4 kv[8];
+  if (seq_keys) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      int r = g0 + 2 * i + half;
-      r = r < N ? r : N - 1;
-      const float* src;
-      if (seq_keys) {
-        src = seq_keys + (int64_t)r * kD;
-      } else {
-        const int sr = slot_of[r];
-        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
-      }
-      kv[i] = *reinterpret_cast<const float4*>(src);
+    for (int i = 0; i < 8; ++i) {
+      const int r = w0 + 2 * i + half <= last ? w0 + 2 * i + half : last;
+      kv[i] = *reinterpret_cast<const float4*>(seq_keys + (int64_t)r * kD);
     }
-  };
-  // with per-sequence keys the first group does not wait for the block table
-  // (nor for the query); the keys, this thread's block-table entry and the
-  // query rows are all requested before any of them is used
-  if (seq_keys && wave * 64 < N) load_group(wave * 64);
-  const int tab0 = tid < N ? Bt.table[(int64_t)b * Bt.mb + tid] : -1;
-  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
-  float4 qb = make_float4(0.f, 0.f, 0.f, 0.f);
-  {
-    const f16* q0 = Bt.q + ((int64_t)b * Bt.Hq + h * Bt.G) * kD + 4 * c4;
-    v4h qh[DKV_MAX_GROUP];
+  }
+  const int tab = Bt.table[(int64_t)b * Bt.mb + jt];
+  const int sl = (tab >= 0 && tab < P.n_slots) ? tab : -1;
+  if (!seq_keys) {
 #pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) qh[g] = *reinterpret_cast<const v4h*>(q0 + (g < Bt.G ? g : Bt.G - 1) * kD);
-#pragma unroll
-    for (int g = 0; g < DKV_MAX_GROUP; ++g) {
-      if (g < Bt.G) {
-        qb.x += (float)qh[g][0];
-        qb.y += (float)qh[g][1];
-        qb.z += (float)qh[g][2];
-        qb.w += (float)qh[g][3];
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int s = __shfl(sl, 2 * i + half);  // the slot of block w0 + 2 i + half (clipped alike)
+      kv[i] = *reinterpret_cast<const float4*>(P.key + (int64_t)(s >= 0 ? s : 0) * P.key_s + h * P.key_h + 4 * c4);
     }
-    const float inv = 1.f / (float)Bt.G;
-    qb.x *= inv;
-    qb.y *= inv;
-    qb.z *= inv;
-    qb.w *= inv;
   }
-
-
-  // ---- pool slots of the unit's blocks (coalesced block-table reads)
-  for (int j = tid; j < N; j += NT) {
-    const int sr = j == tid ? tab0 : Bt.table[(int64_t)b * Bt.mb + j];
-    slot_of[j] = (sr >= 0 && sr < P.n_slots) ? sr : -1;
+  const float4 qb = route_query(Bt, b, h, c4);
+  float* rw = red + wave * 16 * kRedRow;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rw[(2 * i + half) * kRedRow + c4] = score_share(kv[i], qb);
+  wave_sync_lds();
+  if (lane < 16 && w0 + lane <= last) {
+    const float acc = score_sum(rw + lane * kRedRow);
+    const uint32_t key = ordered_key(sl >= 0 ? acc : -INFINITY);
+    st_dev(&words[w0 + lane], ((uint64_t)(uint32_t)(sl + kSlotCode) << 32) | (uint64_t)key);
   }
-  lds_barrier();
+}
 
-  // ---- scores of 64-block groups, one group per wave at a time
-  for (int g0 = wave * 64; g0 < N; g0 += NT) {
-    if (!seq_keys || g0 != wave * 64) load_group(g0);
-    float part[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) part[i] = (kv[i].x * qb.x + kv[i].y * qb.y) + (kv[i].z * qb.z + kv[i].w * qb.w);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) red[(2 * i + half) * kRedRow + c4] = part[i];
-    wave_sync_lds();
-    const float4* rr = reinterpret_cast<const float4*>(red + lane * kRedRow);
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float4 v = rr[m];
-      acc += (v.x + v.y) + (v.z + v.w);
-    }
-    const int j = g0 + lane;
-    if (j < N) keys[j] = ordered_key(slot_of[j] >= 0 ? acc : -INFINITY);
-    wave_sync_lds();  // the next group reuses the transpose area
-  }
-  lds_barrier();
-
-  auto emit = [&](int pos, int j, uint32_t k) {
-    st_dev(&idx[(int64_t)u * top_k + pos], j);
-    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
-    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)(tag | (uint32_t)(slot_of[j] + kSlotCode)));
-  };
-
+// The top keff of N blocks by ordered score key (keys[], in LDS; the
+// lowest index first among equal keys), found by the whole workgroup of NT
+// threads: emit(pos, j, key) is called once for each routed block j, pos =
+// its rank in ascending block order.  lds: route_lds_words(mb, NT / 64) words
+// whose first 2 mbp hold keys (and the caller's slots); the rest is scratch.
+//
+// Finite scores are binned linearly between their minimum and maximum into
+// bins 1..255 (-inf and below into bin 0); the bin map is monotone, so every
+// block in a bin above the boundary bin b* is routed and none below it.
+// Inside b* the blocks are ranked exactly by (score, lower index first)
+// against the other members of b*.
+template <int NT, class Emit>
+__device__ __forceinline__ void route_select(const uint32_t* keys, int N, int keff, uint32_t* lds, int mbp,
+                                             RouteShared<NT / 64>& sh, Emit&& emit) {
+  constexpr int NW = NT / 64;
+  constexpr int kBinWaves = 256 / 64;
+  uint32_t* wsum = sh.wsum;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (keff > 0) {
-    // ---- histogram select.  Finite scores are binned linearly between their
-    // minimum and maximum into bins 1..255 (-inf and below into bin 0); the
-    // bin map is monotone, so every block in a bin above the boundary bin b* is
-    // routed and none below it.  Inside b* the blocks are ranked exactly by
-    // (score, lower index first) against the other members of b*.
     uint32_t* hist = sh.hist;
     constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // ordered key of -inf
     float lo = INFINITY, hi = -INFINITY;
@@ -549,6 +553,91 @@ __device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& B
       sel_base += sel_tot;
     }
   }
+}
+
+// Route one (sequence, KV head) unit u with a workgroup of NT threads.
+// lds: route_lds_words(max_blocks, NT / 64) words: ordered score keys [mb],
+// pool slots [mb] (both rounded up to 4), then a 64 x kRedRow float area per wave.
+//
+// Scores: lane l of a wave holds columns 4 (l % 32) .. +3 of the GQA-mean query;
+// a 512-byte routing key is read by 32 lanes, 16 bytes each, two keys per load
+// instruction (fully coalesced), and the 32 lane partials of a key are summed
+// through LDS.  Selection: block j is routed iff fewer than K blocks beat it
+// (a larger score, or an equal score at a smaller index: the lowest-index-first
+// tie rule), found with a 256-bin histogram of the scores and an exact ranking
+// inside the boundary bin only.  Routed blocks are emitted in ascending block
+// order.
+template <int NT>
+__device__ __forceinline__ void route_unit(const PoolArgs& P, const BatchArgs& Bt, int u, int top_k, int32_t* idx,
+                                           float* scores, int32_t* slots_out, uint32_t* lds,
+                                           RouteShared<NT / 64>& sh, uint32_t tag = 0u) {
+  static_assert(NT == 256 || NT == 512, "route_unit: 256 histogram bins over the first 4 waves");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = u / Bt.Hkv, h = u % Bt.Hkv;
+  int N = (Bt.nblk && Bt.mb > 0) ? Bt.nblk[b] : 0;
+  N = N < 0 ? 0 : (N > Bt.mb ? Bt.mb : N);
+  const int keff = top_k < N ? top_k : N;
+  const int mbp = ((Bt.mb > 0 ? Bt.mb : 1) + 3) & ~3;
+  uint32_t* keys = lds;
+  int32_t* slot_of = reinterpret_cast<int32_t*>(lds + mbp);
+  float* red = reinterpret_cast<float*>(lds + 2 * mbp) + wave * 64 * kRedRow;
+
+  const int c4 = lane & 31, half = lane >> 5;
+
+  // ---- routing-key rows of a 64-block group: lanes 0-31 read block g0 + 2 i,
+  //      lanes 32-63 block g0 + 2 i + 1, 16 bytes each (two whole keys per load)
+  const float* seq_keys = Bt.rkeys ? Bt.rkeys + ((int64_t)b * Bt.Hkv + h) * Bt.mb * kD + 4 * c4 : nullptr;
+  float4 kv[32];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      int r = g0 + 2 * i + half;
+      r = r < N ? r : N - 1;
+      const float* src;
+      if (seq_keys) {
+        src = seq_keys + (int64_t)r * kD;
+      } else {
+        const int sr = slot_of[r];
+        src = P.key + (int64_t)(sr >= 0 ? sr : 0) * P.key_s + h * P.key_h + 4 * c4;
+      }
+      kv[i] = *reinterpret_cast<const float4*>(src);
+    }
+  };
+  // with per-sequence keys the first group does not wait for the block table
+  // (nor for the query); the keys, this thread's block-table entry and the
+  // query rows are all requested before any of them is used
+  if (seq_keys && wave * 64 < N) load_group(wave * 64);
+  const int tab0 = tid < N ? Bt.table[(int64_t)b * Bt.mb + tid] : -1;
+  // ---- this lane's 4 columns of the GQA-mean query (no barrier needed)
+  const float4 qb = route_query(Bt, b, h, c4);
+
+  // ---- pool slots of the unit's blocks (coalesced block-table reads)
+  for (int j = tid; j < N; j += NT) {
+    const int sr = j == tid ? tab0 : Bt.table[(int64_t)b * Bt.mb + j];
+    slot_of[j] = (sr >= 0 && sr < P.n_slots) ? sr : -1;
+  }
+  lds_barrier();
+
+  // ---- scores of 64-block groups, one group per wave at a time
+  for (int g0 = wave * 64; g0 < N; g0 += NT) {
+    if (!seq_keys || g0 != wave * 64) load_group(g0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) red[(2 * i + half) * kRedRow + c4] = score_share(kv[i], qb);
+    wave_sync_lds();
+    const float acc = score_sum(red + lane * kRedRow);
+    const int j = g0 + lane;
+    if (j < N) keys[j] = ordered_key(slot_of[j] >= 0 ? acc : -INFINITY);
+    wave_sync_lds();  // the next group reuses the transpose area
+  }
+  lds_barrier();
+
+  auto emit = [&](int pos, int j, uint32_t k) {
+    st_dev(&idx[(int64_t)u * top_k + pos], j);
+    if (scores) st_dev(&scores[(int64_t)u * top_k + pos], from_ordered(k));
+    if (slots_out) st_dev(&slots_out[(int64_t)u * top_k + pos], (int32_t)(tag | (uint32_t)(slot_of[j] + kSlotCode)));
+  };
+
+  route_select<NT>(keys, N, keff, lds, mbp, sh, emit);
   for (int pos = keff + tid; pos < top_k; pos += NT) {
     st_dev(&idx[(int64_t)u * top_k + pos], -1);
     if (scores) st_dev(&scores[(int64_t)u * top_k + pos], -INFINITY);
@@ -720,18 +809,22 @@ struct DecodeArgs {
   AttnArgs att;
   int32_t* idx;          // [units][top_k] routed logical blocks
   int32_t* slots;        // [units][top_k] routed-slot words (launch tag | slot + kSlotCode)
-  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, [3] launch counter, queue counters
+  uint32_t* ctrl;        // [1] finished merges, [2] sticky wait-timeout flag, [3] launch counter,
+                         // [4] finished score items (split routing), queue counters
   uint32_t* unit_done;   // [units] parts finished
   f16* out;
   float* out_lse;
+  uint64_t* rwords;      // split routing: [units][mb] (slot, score) words, zero between launches; else NULL
   int n_units;
-  int n_route;           // units routed in this launch (0 when top_k == 0)
+  int route_items;       // routing items per unit: 1 (route_unit), or the split routing's score items
+  int n_route;           // routing items of this launch: n_units * route_items (0 when top_k == 0)
   int n_part_end;        // n_route + n_units * att.items_per_unit: first merge item
   int merges;            // merge items per unit: G (one per query row) or 1 (one per unit)
   int n_items;           // n_part_end + n_units * merges: the grid size
 };
 
 constexpr unsigned kRouteWaitLimit = 1u << 24;  // polls before giving up
+constexpr int kCtrlScored = 4;                  // control word: score items finished (split routing)
 constexpr int kQueues = 8;                      // one work queue per XCD
 constexpr int kQueueStride = 64;                // words between queue counters (separate 256-byte lines)
 constexpr int kCtrlQueue = 64;                  // first queue counter

@@ -267,7 +267,8 @@ dkv_status dkv_lse_merge(const float* part_o, const float* part_lse, int32_t n_p
 size_t dkv_decode_workspace_size(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k);
 
 /* Prepare a dkv_decode workspace for first use: zeroes its control area (a few
- * KB at its start) with a kernel on `stream` (no memset, so it may be captured
+ * KB at its start, plus 8 bytes per (sequence, KV head, block-table entry)
+ * when top_k > 0) with a kernel on `stream` (no memset, so it may be captured
  * in a graph).  Not needed for memory that is already zero-filled.  Every
  * dkv_decode leaves the control area zeroed again, so a workspace is prepared
  * once and may then be reused by any number of calls (one at a time). */
@@ -277,22 +278,27 @@ dkv_status dkv_decode_workspace_init(const dkv_pool* pool, const dkv_batch* batc
 /* One decode step of one layer in a single kernel launch: routing, low-rank +
  * residual attention of every routed block, window attention and the LSE
  * combine (the Zenodo abstract's decode path).  top_k = 0 attends the window
- * only.  Work is handed out in ticket order from a counter in the workspace:
- * the routing of each (sequence, KV head) first, then its blocks (which wait
- * for that routing) and window chunks, then one merge per query row (which
- * waits until its unit's parts are stored), so that the G rows of a unit are
- * combined by G workgroups at once.
+ * only.  Every (sequence, KV head) unit has its work items: score items, each
+ * scoring 64 of its blocks against the GQA-mean query and writing (slot,
+ * score) words to the workspace; then its parts, each of which attends its
+ * share of the window, waits until all of the unit's words are written, ranks
+ * the blocks itself (top_k by score, the lower block index first among equal
+ * scores; the same ranking dkv_route_topk gives) and attends the routed block
+ * at its own position; then one merge per query row, which waits until the
+ * unit's parts are stored.  Workgroup w takes a fixed item: the units u with
+ * u % 8 == x form list x (their score items, parts, merges, in that order) and
+ * workgroup x + 8 i runs item i of list x, so every wait is on a workgroup of
+ * a smaller index.  The last merge clears the words once every score item is
+ * counted.
  *   workspace: device memory of >= dkv_decode_workspace_size() bytes, 256-byte
  *              aligned, owned by the caller, whose control area is zero (fresh
  *              zero-filled memory, dkv_decode_workspace_init, or a previous
  *              dkv_decode with the same or a larger-or-equal shape).  Calls
  *              that share a workspace must not overlap.  Word 2 of the
- *              workspace (uint32 at byte 8) is a sticky flag set if a block
- *              ever gave up waiting for its routing (never in a correct run);
- *              word 3 counts launches: the routed-slot words a launch writes
- *              carry its low byte, so that a routing that finishes after its
- *              launch gave up on it is never read by a later launch (its
- *              routed indices in out_idx may still be overwritten late).
+ *              workspace (uint32 at byte 8) is a sticky flag set if a part
+ *              ever gave up waiting for its unit's scores, or the last merge
+ *              for the score items (never in a correct run); word 3 counts
+ *              launches.
  *   out:     fp16 [B][Hq][d] out;  out_lse: fp32 [B][Hq] out.
  *   out_idx: int32 [B][Hkv][top_k] out (the routed blocks), or NULL. */
 dkv_status dkv_decode(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k, float scale,

@@ -161,6 +161,54 @@ def test_route_ties_go_to_lowest_index(lib):
     assert 30 in idx[0, 0] and 30 in idx[0, 1]
 
 
+SPLIT_SHAPES = {
+    # several 64-block score items per unit with a ragged last one, and units of different lengths
+    "ragged_items": dict(batch=4, n_q_heads=6, n_kv_heads=2, n_blocks=[300, 129, 64, 65], top_k=37),
+    # top_k above some units' block counts, an empty unit, one block
+    "topk_over_n": dict(batch=4, n_q_heads=6, n_kv_heads=2, n_blocks=[3, 0, 70, 1], top_k=5),
+    # more units than XCD lists: 9 units, so list 0 holds two
+    "nine_units": dict(batch=9, n_q_heads=2, n_kv_heads=1, n_blocks=[17, 64, 2, 130, 5, 66, 128, 1, 40],
+                       top_k=9),
+}
+
+
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("shape", sorted(SPLIT_SHAPES))
+def test_decode_split_routing(lib, shape, gather):
+    """dkv_decode's routing (score items of 64 blocks, each block part selecting
+    its own block) routes exactly as dkv_route_topk does, from pool keys or a
+    per-sequence key table, attends as the oracle does and never times out."""
+    kw = dict(seed=40 + len(shape), window=40, ranks=[8], n_resid=8, sigma0=2.0, **SPLIT_SHAPES[shape])
+    wl = synth.make_workload(shape, **kw)
+    say(f"[split routing] {shape} gather={gather}")
+    pool, batch = upload(lib, wl)
+    if gather:
+        lib.gather_route_keys(pool, batch)
+    want = lib.route_topk(pool, batch, wl.top_k)
+    ws = lib.alloc_workspace(pool, batch, wl.top_k)
+    for rep in range(2):
+        out, lse, idx = lib.decode(pool, batch, wl.top_k, wl.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, want), rep
+    assert int(ws[8:12].view(torch.int32).item()) == 0  # no part gave up waiting
+    check_decode(lib, wl, label=shape)
+
+
+def test_decode_split_routing_ties(lib):
+    """All scores equal: every part of dkv_decode takes the lowest indices, as
+    dkv_route_topk does."""
+    wl = synth.make_workload("split_ties", seed=7, batch=2, n_q_heads=4, n_kv_heads=2, window=16,
+                             n_blocks=[140, 25], ranks=[16], n_resid=8, top_k=10)
+    lay = wl.layers[0]
+    for name in ("anchor_k", "u", "vk"):
+        arr = getattr(lay, name)
+        arr[:] = arr[0:1]
+    pool, batch = upload(lib, wl)
+    _, _, idx = lib.decode(pool, batch, 10, wl.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), np.broadcast_to(np.arange(10), idx.shape))
+
+
 def test_route_more_blocks_than_topk_and_padding(lib):
     wl = synth.make_workload("pad", seed=6, batch=3, n_q_heads=6, n_kv_heads=2, window=8,
                              n_blocks=[3, 0, 70], ranks=[8], n_resid=4, top_k=5, max_blocks=80)

@@ -129,8 +129,11 @@ def test_workspace_size_formula(clib):
             # the fused launch's parts: routed-block parts each with a share of the
             # window, or (no routed blocks) window chunks of 512 rows
             n_parts = top_k if top_k > 0 else max(1, (window + 511) // 512)
-            rows, units = 2 * 12, 2 * 2
-            ctrl = 4096 + a256(units * 4) + a256(units * top_k * 4)  # counters/queues, per-unit, routed slots
+            rows, units, max_blocks = 2 * 12, 2 * 2, 8
+            # counters/queues, per-unit counts, routed slots, and (top_k > 0) the
+            # 8-byte (slot, score) word of every block-table entry
+            ctrl = 4096 + a256(units * 4) + a256(units * top_k * 4) \
+                + (a256(units * max_blocks * 8) if top_k > 0 else 0)
             want = ctrl + a256(units * top_k * 4) + a256(rows * n_parts * 4) \
                 + a256(rows * n_parts * 128 * 4)
             assert clib.dkv_decode_workspace_size(ctypes.byref(p), ctypes.byref(b), top_k) == want
