@@ -163,7 +163,10 @@ def test_route_ties_go_to_lowest_index(lib):
 
 SPLIT_SHAPES = {
     # several 64-block score items per unit with a ragged last one, and units of different lengths
+    # (up to 256 blocks: a wave holds 4 keys per lane; up to 512: 8; more: the selection in LDS)
     "ragged_items": dict(batch=4, n_q_heads=6, n_kv_heads=2, n_blocks=[300, 129, 64, 65], top_k=37),
+    "long_unit": dict(batch=2, n_q_heads=4, n_kv_heads=2, n_blocks=[600, 37], top_k=12),
+    "within_256": dict(batch=3, n_q_heads=6, n_kv_heads=2, n_blocks=[256, 255, 191], top_k=64),
     # top_k above some units' block counts, an empty unit, one block
     "topk_over_n": dict(batch=4, n_q_heads=6, n_kv_heads=2, n_blocks=[3, 0, 70, 1], top_k=5),
     # more units than XCD lists: 9 units, so list 0 holds two
