@@ -1494,7 +1494,7 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     // count this part once its partial is stored
     stores_done();
     __syncthreads();
-    if (tid == 0) atomicAdd(&D.unit_done[u], 1u);
+    if (tid == 0) atomicAdd(&D.unit_done[u * kDoneStride], 1u);
   } else if (t < D.n_items) {
     // merge item: one query row of a unit, or all G of them, once all of the
     // unit's parts are stored
@@ -1503,10 +1503,10 @@ __device__ __forceinline__ void decode_item(const PoolArgs& P, const BatchArgs& 
     if (tid == 0) {
       const uint32_t want = (uint32_t)D.att.items_per_unit;
       unsigned n = 0;
-      uint32_t v = ld_dev(&D.unit_done[u]);
+      uint32_t v = ld_dev(&D.unit_done[u * kDoneStride]);
       while (v < want && n < kRouteWaitLimit) {
         __builtin_amdgcn_s_sleep(2);
-        v = ld_dev(&D.unit_done[u]);
+        v = ld_dev(&D.unit_done[u * kDoneStride]);
         ++n;
       }
       if (v < want) atomicOr(&D.ctrl[2], 1u);
@@ -1585,7 +1585,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode(PoolArgs P, BatchArgs
         for (int64_t i = tid; i < n16; i += kAttThreads) w[i] = make_uint4(0u, 0u, 0u, 0u);
         if (tid == 0 && ((int64_t)D.n_units * Bt.mb) & 1) D.rwords[(int64_t)D.n_units * Bt.mb - 1] = 0ull;
       }
-      for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
+      for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i * kDoneStride] = 0u;
       if (tid == 0) {
         D.ctrl[1] = 0u;
         D.ctrl[kCtrlScored] = 0u;
@@ -1664,7 +1664,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void k_decode_layers(const LayerArg
     if (sh_flag) {
       for (int l = 0; l < L.n_layers; ++l) {
         const DecodeArgs& D = table[l].D;
-        for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i] = 0u;
+        for (int i = tid; i < D.n_units; i += kAttThreads) D.unit_done[i * kDoneStride] = 0u;
       }
       if (tid < kQueues) L.ctrl[kCtrlQueue + tid * kQueueStride] = 0u;
       if (tid == 0) {
@@ -2022,7 +2022,7 @@ WsLayout decode_layout(const dkv_pool* pool, const dkv_batch* batch, int top_k, 
   if (min_parts > n_parts) n_parts = min_parts;
   const size_t rows = B * (size_t)batch->n_q_heads;
   w.unit_done = kCtrlHeaderBytes;
-  w.slots = w.unit_done + align256(units * 4);
+  w.slots = w.unit_done + align256(units * 4 * kDoneStride);
   w.rwords = w.slots + align256(units * (size_t)top_k * 4);
   const size_t mb = top_k > 0 && batch->max_blocks > 0 ? (size_t)batch->max_blocks : 0;
   w.ctrl_bytes = w.rwords + align256(units * mb * 8);

@@ -266,9 +266,10 @@ dkv_status dkv_lse_merge(const float* part_o, const float* part_lse, int32_t n_p
 /* Bytes of workspace dkv_decode needs for this pool, batch and top_k (>= 0). */
 size_t dkv_decode_workspace_size(const dkv_pool* pool, const dkv_batch* batch, int32_t top_k);
 
-/* Prepare a dkv_decode workspace for first use: zeroes its control area (a few
- * KB at its start, plus 8 bytes per (sequence, KV head, block-table entry)
- * when top_k > 0) with a kernel on `stream` (no memset, so it may be captured
+/* Prepare a dkv_decode workspace for first use: zeroes its control area (at
+ * its start: 4 KB, plus 256 bytes per (sequence, KV head) unit, 4 bytes per
+ * unit and routed block, and, when top_k > 0, 8 bytes per unit and
+ * block-table entry) with a kernel on `stream` (no memset, so it may be captured
  * in a graph).  Not needed for memory that is already zero-filled.  Every
  * dkv_decode leaves the control area zeroed again, so a workspace is prepared
  * once and may then be reused by any number of calls (one at a time). */

@@ -130,9 +130,9 @@ def test_workspace_size_formula(clib):
             # window, or (no routed blocks) window chunks of 512 rows
             n_parts = top_k if top_k > 0 else max(1, (window + 511) // 512)
             rows, units, max_blocks = 2 * 12, 2 * 2, 8
-            # counters/queues, per-unit counts, routed slots, and (top_k > 0) the
+            # counters/queues, per-unit counts (a 256-byte line each), routed slots, and (top_k > 0) the
             # 8-byte (slot, score) word of every block-table entry
-            ctrl = 4096 + a256(units * 4) + a256(units * top_k * 4) \
+            ctrl = 4096 + a256(units * 256) + a256(units * top_k * 4) \
                 + (a256(units * max_blocks * 8) if top_k > 0 else 0)
             want = ctrl + a256(units * top_k * 4) + a256(rows * n_parts * 4) \
                 + a256(rows * n_parts * 128 * 4)
