@@ -110,14 +110,17 @@ __device__ void quantize_row(const f16* x, int bits, uint8_t* codes, f16* sb) {
   }
 }
 
-// LDS layout (in 4-byte words) for a padded width LP (a multiple of 16)
+// LDS layout (in 4-byte words) for a padded width LP (a multiple of 8).  E
+// shares S's area: E is written from the Jacobi step on, when S's rows are no
+// longer read, and it sits at the end of S, past the rounded V_K that the
+// right-factor step writes at S's start while it still reads E.
 template <int LP>
 struct Lay {
   static constexpr int SS = LP + 4;  // row stride of S, G, E: 16-byte aligned rows
   static constexpr int S = 0;                    // [256][SS] the factor of a product / rows for a Gram
+  static constexpr int E = S + (256 - LP) * SS;  // [LP][SS] Jacobi eigenvectors (the end of S's area)
   static constexpr int G = S + 256 * SS;         // [LP][SS] Gram, Cholesky factor, Jacobi matrix
-  static constexpr int E = G + LP * SS;          // [LP][SS] Jacobi eigenvectors
-  static constexpr int ANC = E + LP * SS;        // [256] anchor row (fp32)
+  static constexpr int ANC = G + LP * SS;        // [256] anchor row (fp32)
   static constexpr int ERR = ANC + 256;          // [256] squared key errors
   static constexpr int SEL = ERR + 256;          // [256] selected flags
   static constexpr int INV = SEL + 256;          // [LP] inverse Cholesky pivots
@@ -372,8 +375,10 @@ __device__ __forceinline__ void jacobi(float* G, float* E, float* rc, float* rs,
   }
 }
 
+// Widths up to 56 fit two workgroups per CU (LDS and registers), up to 16 three;
+// wider ones one.
 template <int LP>
-__global__ __launch_bounds__(kThreads) void k_seal(SealArgs A) {
+__global__ __launch_bounds__(kThreads, LP <= 16 ? 3 : (LP <= 56 ? 2 : 1)) void k_seal(SealArgs A) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   typedef Lay<LP> L;
   constexpr int SS = L::SS;
@@ -480,37 +485,43 @@ __global__ __launch_bounds__(kThreads) void k_seal(SealArgs A) {
   //      of its key from the stored factors, and its squared error
   const int t = tid;
   if (t < kRows) {
-    float rec[kD];
-#pragma unroll
-    for (int c = 0; c < kD; ++c) rec[c] = anc[c];
+    // the key's 128 columns in two halves of 64 (fewer live registers); each
+    // column and the squared error are summed in the same order either way
+    constexpr int kHalf = kD / 2;
     f16* urow = A.u + slot * A.u_s + h * A.u_h + (int64_t)t * rank;
-    for (int k = 0; k < rank; ++k) {
-      const int pk = min(max(perm[k], 0), LP - 1);
-      float uk = 0.f;
-#pragma unroll
-      for (int j = 0; j < LP; ++j) uk = fmaf(v[j], E[j * SS + pk], uk);
-      const f16 u16 = (f16)(uk * sig[k]);
-      urow[k] = u16;
-      const float uf = (float)u16;
-      const float4* vkr = reinterpret_cast<const float4*>(S + k * kD);
-#pragma unroll
-      for (int c4 = 0; c4 < kD / 4; ++c4) {
-        const float4 w = vkr[c4];
-        rec[4 * c4 + 0] = fmaf(uf, w.x, rec[4 * c4 + 0]);
-        rec[4 * c4 + 1] = fmaf(uf, w.y, rec[4 * c4 + 1]);
-        rec[4 * c4 + 2] = fmaf(uf, w.z, rec[4 * c4 + 2]);
-        rec[4 * c4 + 3] = fmaf(uf, w.w, rec[4 * c4 + 3]);
-      }
-    }
     const f16* kr = xk + (int64_t)(t + 1) * kD;
     float e2 = 0.f;
+    for (int half = 0; half < 2; ++half) {
+      const int c0 = half * kHalf;
+      float rec[kHalf];
 #pragma unroll
-    for (int c8 = 0; c8 < kD / 8; ++c8) {
-      const v8h x = *reinterpret_cast<const v8h*>(kr + 8 * c8);
+      for (int c = 0; c < kHalf; ++c) rec[c] = anc[c0 + c];
+      for (int k = 0; k < rank; ++k) {
+        const int pk = min(max(perm[k], 0), LP - 1);
+        float uk = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float d = (float)x[e] - rec[8 * c8 + e];
-        e2 = fmaf(d, d, e2);
+        for (int j = 0; j < LP; ++j) uk = fmaf(v[j], E[j * SS + pk], uk);
+        const f16 u16 = (f16)(uk * sig[k]);
+        if (half == 0) urow[k] = u16;
+        const float uf = (float)u16;
+        const float4* vkr = reinterpret_cast<const float4*>(S + k * kD + c0);
+#pragma unroll
+        for (int c4 = 0; c4 < kHalf / 4; ++c4) {
+          const float4 w = vkr[c4];
+          rec[4 * c4 + 0] = fmaf(uf, w.x, rec[4 * c4 + 0]);
+          rec[4 * c4 + 1] = fmaf(uf, w.y, rec[4 * c4 + 1]);
+          rec[4 * c4 + 2] = fmaf(uf, w.z, rec[4 * c4 + 2]);
+          rec[4 * c4 + 3] = fmaf(uf, w.w, rec[4 * c4 + 3]);
+        }
+      }
+#pragma unroll
+      for (int c8 = 0; c8 < kHalf / 8; ++c8) {
+        const v8h x = *reinterpret_cast<const v8h*>(kr + c0 + 8 * c8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = (float)x[e] - rec[8 * c8 + e];
+          e2 = fmaf(d, d, e2);
+        }
       }
     }
     errv[t] = e2;
@@ -748,6 +759,10 @@ __global__ __launch_bounds__(kJoinThreads) void k_join(JoinArgs a) {
 static_assert(Lay<kMaxWidth>::bytes <= 160 * 1024, "sealer LDS exceeds 160 KB");
 static_assert(kJoinLds <= 160 * 1024, "join LDS exceeds 160 KB");
 static_assert(Lay<16>::SS >= 1, "padded width");
+// the rounded V_K ([rank <= LP][128] at S's start) stays clear of E
+static_assert(80 * kD <= Lay<80>::E && 64 * kD <= Lay<64>::E && 56 * kD <= Lay<56>::E && 48 * kD <= Lay<48>::E &&
+                  32 * kD <= Lay<32>::E && 16 * kD <= Lay<16>::E,
+              "V_K overlaps the eigenvectors");
 
 }  // namespace
 
@@ -826,6 +841,8 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
     s = launch_seal<32>(a, g, st);
   else if (width <= 48)
     s = launch_seal<48>(a, g, st);
+  else if (width <= 56)
+    s = launch_seal<56>(a, g, st);  // 79 KB of LDS: two workgroups per CU
   else if (width <= 64)
     s = launch_seal<64>(a, g, st);
   else
