@@ -222,6 +222,54 @@ __device__ __forceinline__ void store_row(float* S, int t, const float (&v)[LP])
 template <int LP>
 __device__ __forceinline__ void gram(const float* S, float* G, int tid) {
   constexpr int SS = Lay<LP>::SS, NB = LP / 4, NP = NB * (NB + 1) / 2;
+  if constexpr (NP <= kThreads / 2) {
+    // two halves of the rows: threads 128.. sum rows 128..255 and leave their
+    // 4 x 4 sum in the block's mirror position; threads 0.. sum rows 0..127,
+    // add it and write both triangles
+    const int half = tid >= kThreads / 2 ? 1 : 0, e = tid - half * (kThreads / 2);
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+    int bi = 0, bj = 0;
+    if (e < NP) {
+      while ((bi + 1) * (bi + 2) / 2 <= e) ++bi;
+      bj = e - bi * (bi + 1) / 2;
+      for (int t = half * 128; t < half * 128 + 128; ++t) {
+        const float4 x = *reinterpret_cast<const float4*>(S + t * SS + 4 * bi);
+        const float4 y = *reinterpret_cast<const float4*>(S + t * SS + 4 * bj);
+        const float xa[4] = {x.x, x.y, x.z, x.w}, yb[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(xa[a], yb[b], acc[a][b]);
+      }
+      if (half) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) G[(4 * bj + b) * SS + 4 * bi + a] = acc[a][b];
+      }
+    }
+    __syncthreads();
+    if (e < NP && !half) {
+      float part[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) part[a][b] = G[(4 * bj + b) * SS + 4 * bi + a];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float g = acc[a][b] + part[a][b];
+          G[(4 * bi + a) * SS + 4 * bj + b] = g;
+          G[(4 * bj + b) * SS + 4 * bi + a] = g;
+        }
+    }
+    return;
+  }
   for (int e = tid; e < NP; e += kThreads) {
     int bi = 0;
     while ((bi + 1) * (bi + 2) / 2 <= e) ++bi;
@@ -347,27 +395,60 @@ __device__ __forceinline__ void jacobi(float* G, float* E, float* rc, float* rs,
         rq[tid] = q;
       }
       __syncthreads();
-      // C[P][Q] <- J_P^T C[P][Q] J_Q, with J = [[c, s], [-s, c]] on (p, q)
-      for (int e = tid; e < NP * NP; e += kThreads) {
-        const int P = e / NP, Q = e % NP;
+      // C[P][Q] <- J_P^T C[P][Q] J_Q, with J = [[c, s], [-s, c]] on (p, q), and
+      // E <- E J.  The blocks of a round are disjoint, so every read of this
+      // thread's blocks is issued before any of its writes.
+      constexpr int NGB = (NP * NP + kThreads - 1) / kThreads, NEB = (LP * NP + kThreads - 1) / kThreads;
+      float m[NGB][4];
+      int gi[NGB][4];
+#pragma unroll
+      for (int k = 0; k < NGB; ++k) {
+        const int e = tid + k * kThreads;
+        const int P = e < NP * NP ? e / NP : 0, Q = e < NP * NP ? e % NP : 0;
         const int p1 = rp[P], p2 = rq[P], q1 = rp[Q], q2 = rq[Q];
-        const float cp = rc[P], sp = rs[P], cq = rc[Q], sq = rs[Q];
-        const float m11 = G[p1 * SS + q1], m12 = G[p1 * SS + q2], m21 = G[p2 * SS + q1], m22 = G[p2 * SS + q2];
-        const float t11 = cp * m11 - sp * m21, t12 = cp * m12 - sp * m22;
-        const float t21 = sp * m11 + cp * m21, t22 = sp * m12 + cp * m22;
-        G[p1 * SS + q1] = cq * t11 - sq * t12;
-        G[p1 * SS + q2] = sq * t11 + cq * t12;
-        G[p2 * SS + q1] = cq * t21 - sq * t22;
-        G[p2 * SS + q2] = sq * t21 + cq * t22;
+        gi[k][0] = p1 * SS + q1;
+        gi[k][1] = p1 * SS + q2;
+        gi[k][2] = p2 * SS + q1;
+        gi[k][3] = p2 * SS + q2;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) m[k][x] = G[gi[k][x]];
       }
-      // E <- E J
-      for (int e = tid; e < LP * NP; e += kThreads) {
-        const int i = e / NP, P = e % NP;
-        const int p = rp[P], q = rq[P];
-        const float c = rc[P], s = rs[P];
-        const float ep = E[i * SS + p], eq = E[i * SS + q];
-        E[i * SS + p] = c * ep - s * eq;
-        E[i * SS + q] = s * ep + c * eq;
+      float ev[NEB][2];
+      int ei[NEB][2];
+#pragma unroll
+      for (int k = 0; k < NEB; ++k) {
+        const int e = tid + k * kThreads;
+        const int i = e < LP * NP ? e / NP : 0, P = e < LP * NP ? e % NP : 0;
+        ei[k][0] = i * SS + rp[P];
+        ei[k][1] = i * SS + rq[P];
+        ev[k][0] = E[ei[k][0]];
+        ev[k][1] = E[ei[k][1]];
+      }
+#pragma unroll
+      for (int k = 0; k < NGB; ++k) {
+        const int e = tid + k * kThreads;
+        if (e < NP * NP) {
+          const int P = e / NP, Q = e % NP;
+          const float cp = rc[P], sp = rs[P], cq = rc[Q], sq = rs[Q];
+          const float m11 = m[k][0], m12 = m[k][1], m21 = m[k][2], m22 = m[k][3];
+          const float t11 = cp * m11 - sp * m21, t12 = cp * m12 - sp * m22;
+          const float t21 = sp * m11 + cp * m21, t22 = sp * m12 + cp * m22;
+          G[gi[k][0]] = cq * t11 - sq * t12;
+          G[gi[k][1]] = sq * t11 + cq * t12;
+          G[gi[k][2]] = cq * t21 - sq * t22;
+          G[gi[k][3]] = sq * t21 + cq * t22;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NEB; ++k) {
+        const int e = tid + k * kThreads;
+        if (e < LP * NP) {
+          const int P = e % NP;
+          const float c = rc[P], s = rs[P];
+          const float ep = ev[k][0], eq = ev[k][1];
+          E[ei[k][0]] = c * ep - s * eq;
+          E[ei[k][1]] = s * ep + c * eq;
+        }
       }
       __syncthreads();
     }
