@@ -737,22 +737,17 @@ __device__ __forceinline__ v8h bytes8_b1024(v2u c) {
   w[3] = __builtin_amdgcn_perm(0x64646464u, c[1], 0x04030402u);
   return __builtin_bit_cast(v8h, w);
 }
-// 8 nibbles (nibble k: bits 4 k .. 4 k + 3) -> v8h of 1024 + nibble, in order
-__device__ __forceinline__ v8h nibbles8_b1024(uint32_t c) {
+// 8 nibbles (nibble k: bits 4 k .. 4 k + 3) -> v8h of 1024 + nibble in the
+// order 0 4 1 5 2 6 3 7 (the k order of the 4-bit pages: the V pages' weights
+// and the K pages' query follow it).  The even and odd nibbles are masked into
+// bytes, and each output word takes two of their bytes beside 0x64 high bytes.
+__device__ __forceinline__ v8h nibbles8_b1024_il(uint32_t c) {
   const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;  // nibbles 0 2 4 6, 1 3 5 7
   uint32_t w[4];
-  w[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-  w[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-  w[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-  w[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
-  return __builtin_bit_cast(v8h, w);
-}
-// 8 nibbles -> v8h of 1024 + nibble in the order 0 4 1 5 2 6 3 7 (a k order the
-// V pages' weights follow)
-__device__ __forceinline__ v8h nibbles8_b1024_il(uint32_t c) {
-  uint32_t w[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) w[m] = ((c >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+  w[0] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04020400u);  // nibbles 0, 4
+  w[1] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04020400u);  // 1, 5
+  w[2] = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030401u);  // 2, 6
+  w[3] = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030401u);  // 3, 7
   return __builtin_bit_cast(v8h, w);
 }
 
@@ -789,14 +784,19 @@ __device__ __forceinline__ void page_qk(const WaveGeom& g, int i, uint32_t P0, S
     uint32_t c[8];
     lds_b32x8s(a, b, c, sb);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) kc[t] = nibbles8_b1024(c[t]);
+    for (int t = 0; t < 8; ++t) kc[t] = nibbles8_b1024_il(c[t]);
   }
+  // 4-bit codes come in the k order 0 4 1 5 2 6 3 7: the query takes the same
+  v8h qk[4];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2)
+    qk[s2] = g.qb == 8 ? qf[s2] : __builtin_shufflevector(qf[s2], qf[s2], 0, 4, 1, 5, 2, 6, 3, 7);
   const int nr = g.R - kQRows * i;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const v4f S0 = mfma32(kc[4 * tt + 1], qf[1], mfma32(kc[4 * tt], qf[0], zero));
-    const v4f S1 = mfma32(kc[4 * tt + 3], qf[3], mfma32(kc[4 * tt + 2], qf[2], zero));
+    const v4f S0 = mfma32(kc[4 * tt + 1], qk[1], mfma32(kc[4 * tt], qk[0], zero));
+    const v4f S1 = mfma32(kc[4 * tt + 3], qk[3], mfma32(kc[4 * tt + 2], qk[2], zero));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int k = 4 * tt + e;
