@@ -842,7 +842,7 @@ static_assert(kJoinLds <= 160 * 1024, "join LDS exceeds 160 KB");
 static_assert(Lay<16>::SS >= 1, "padded width");
 // the rounded V_K ([rank <= LP][128] at S's start) stays clear of E
 static_assert(80 * kD <= Lay<80>::E && 64 * kD <= Lay<64>::E && 56 * kD <= Lay<56>::E && 48 * kD <= Lay<48>::E &&
-                  32 * kD <= Lay<32>::E && 16 * kD <= Lay<16>::E,
+                  32 * kD <= Lay<32>::E && 24 * kD <= Lay<24>::E && 16 * kD <= Lay<16>::E,
               "V_K overlaps the eigenvectors");
 
 }  // namespace
@@ -918,6 +918,8 @@ dkv_status dkv_seal_blocks(const dkv_pool* pool, dkv_view src_k, dkv_view src_v,
   const unsigned g = (unsigned)grid;
   if (width <= 16)
     s = launch_seal<16>(a, g, st);
+  else if (width <= 24)
+    s = launch_seal<24>(a, g, st);
   else if (width <= 32)
     s = launch_seal<32>(a, g, st);
   else if (width <= 48)
