@@ -456,10 +456,12 @@ __device__ __forceinline__ void jacobi(float* G, float* E, float* rc, float* rs,
   }
 }
 
-// Widths up to 56 fit two workgroups per CU (LDS and registers), up to 16 three;
-// wider ones one.
+// Workgroups per CU: four for widths up to 24, three up to 32, two up to 56
+// (LDS and registers), one above.  The work is latency-bound: more workgroups
+// per CU win even where the register limit spills 50-90 VGPRs (rank 16:
+// 2.38 -> 1.77 ms, rank 24: 3.55 -> 2.83 ms for one layer's 2,016 blocks).
 template <int LP>
-__global__ __launch_bounds__(kThreads, LP <= 16 ? 3 : (LP <= 56 ? 2 : 1)) void k_seal(SealArgs A) {
+__global__ __launch_bounds__(kThreads, LP <= 24 ? 4 : (LP <= 32 ? 3 : (LP <= 56 ? 2 : 1))) void k_seal(SealArgs A) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   typedef Lay<LP> L;
   constexpr int SS = L::SS;
